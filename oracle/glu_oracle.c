@@ -1,0 +1,457 @@
+/*
+ * CPU oracle for the fused gated-linear-unit activation with block-scaled
+ * ("microscaling") output.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The only callers are the tests, the smoke check and
+ * the benchmark's CPU-baseline leg.  The GPU library never links, loads or calls
+ * this file, and the two share no code, header, table or constant generator.
+ *
+ * Everything is evaluated in binary64 from the textbook definitions, then encoded
+ * by a nearest-value search over each number format's own value table (ties to
+ * the even code).  Nothing here is blocked, fused or reordered for speed beyond
+ * an OpenMP split over independent rows and blocks.
+ *
+ * Sources, cited by page title and section:
+ *   [MX] "Add swiglu + MXFP8 fused CuTe DSL kernel"
+ *        - Summary: SwiGLU fused with the RCEIL MXFP8 cast; rowwise (1x32),
+ *          colwise (32x1) or both scalings from one pass.
+ *        - API: gated_input packs [gate | up]; backward returns [dGate | dUp].
+ *        - Numerics and tests: the fused result equals the activation followed by
+ *          the standalone quantizers (so the quantizer sees the BF16 activation).
+ *   [NV] "feat(phyai-kernel): add Thor NVFP4 GeGLU kernel for pi0.5"
+ *        - Summary: GeGLU fold followed by a compact NVFP4 store.
+ *        - Supported contract: packed E2M1 values, FP8 E4M3 block scales in the
+ *          CUTLASS/FlashInfer 128x4 layout, global scale 1, pairwise-interleaved
+ *          gate/up columns (gate0, up0, gate1, up1, ...).
+ *   [GE] "perf: tile wide GeGLU rows on SM103"
+ *        - Summary and Testing Done: GeGLU forward and its two gradients da, db.
+ *   [H]  "[WS1] Add batch-invariant h_aggregate kernel"
+ *        - Fixed numerical paths: FP32 (here FP64) math with exactly one
+ *          conversion to BF16 at the final store.
+ *
+ * Readings where the pages leave the arithmetic open (each is repeated at the
+ * function that uses it):
+ *   - the quantizer consumes the BF16-rounded activation, rounded once;
+ *   - GELU is the tanh approximation with sqrt(2/pi) and 0.044715;
+ *   - RCEIL: the scale is the smallest power of two 2^e, e in [-127, 127], with
+ *     448 * 2^e >= amax (an all-zero block takes e = -127);
+ *   - E4M3 saturates to +-448; E2M1 saturates to +-6;
+ *   - NVFP4 scale = E4M3(amax / 6) rounded to nearest; codes = E2M1(x / S);
+ *     S == 0 gives signed-zero codes; even element in the low nibble;
+ *   - a block holding NaN or Inf gets a NaN scale (MX 0xFF, NV 0x7F) and NaN
+ *     codes (MX 0x7F) or zero codes (NV).
+ * Parity unpinned: the NaN/Inf block rule, the nibble order, and the 128x4
+ * scale layout beyond its being a zero-padded permutation.  No page prints a
+ * value for any of them.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#if defined(__FAST_MATH__)
+#error "the oracle must be built without fast-math"
+#endif
+
+enum { ORC_SWIGLU = 0, ORC_GEGLU_TANH = 1 };
+enum { ORC_SPLIT = 0, ORC_PAIRED = 1 };
+enum { ORC_ROWWISE = 1, ORC_COLWISE = 2 };
+enum { ORC_SF_ROWMAJOR = 0, ORC_SF_128x4 = 1 };
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------- */
+/* Number formats: value tables and nearest-value encoders                    */
+/* ------------------------------------------------------------------------- */
+
+/* BF16: 1 sign, 8 exponent (bias 127), 7 mantissa bits.  Magnitude code c
+ * (0 .. 0x7F7F finite) has value m * 2^-133 when the exponent field is zero and
+ * (1 + m/128) * 2^(E-127) otherwise.  Code 0x7F80 is +Inf; for rounding it is
+ * treated as the next step, 2^128, so that overflow follows round-to-nearest-even. */
+static double bf16_mag_def(uint32_t c) {
+  uint32_t E = c >> 7, m = c & 0x7F;
+  if (c == 0x7F80) return ldexp(1.0, 128);
+  if (E == 0) return ldexp((double)m, -133);
+  return ldexp(1.0 + m / 128.0, (int)E - 127);
+}
+/* The definition above, tabulated once when the library loads. */
+static double bf16_table[0x7F81];
+__attribute__((constructor)) static void fill_bf16_table(void) {
+  for (uint32_t c = 0; c <= 0x7F80; c++) bf16_table[c] = bf16_mag_def(c);
+}
+static double bf16_mag(uint32_t c) { return bf16_table[c]; }
+
+double orc_bf16_to_f64(uint16_t b) {
+  uint32_t c = b & 0x7FFF;
+  double s = (b & 0x8000) ? -1.0 : 1.0;
+  if (c > 0x7F80) return NAN;
+  if (c == 0x7F80) return s * INFINITY;
+  return s * bf16_mag(c);
+}
+
+/* Nearest code in [0, top] of a monotone magnitude table, ties to the even code.
+ * mag(top) is the largest value the search may return. */
+static uint32_t nearest_code(double a, double (*mag)(uint32_t), uint32_t top) {
+  if (a >= mag(top)) return top;
+  uint32_t lo = 0, hi = top; /* invariant: mag(lo) <= a < mag(hi) */
+  while (hi - lo > 1) {
+    uint32_t mid = lo + (hi - lo) / 2;
+    if (mag(mid) <= a) lo = mid; else hi = mid;
+  }
+  double midpoint = 0.5 * (mag(lo) + mag(hi)); /* exact: both have few bits */
+  if (a < midpoint) return lo;
+  if (a > midpoint) return hi;
+  return (lo % 2 == 0) ? lo : hi;
+}
+
+/* Round a binary64 value to BF16, nearest, ties to even; overflow to Inf. */
+uint16_t orc_bf16_from_f64(double v) {
+  if (isnan(v)) return 0x7FC0;
+  uint16_t s = signbit(v) ? 0x8000 : 0;
+  return (uint16_t)(s | nearest_code(fabs(v), bf16_mag, 0x7F80));
+}
+
+/* OCP FP8 E4M3 ("FN" flavour): 1 sign, 4 exponent (bias 7), 3 mantissa bits, no
+ * infinities, S.1111.111 is NaN, largest finite 448 (0x7E), subnormals k * 2^-9. */
+static double e4m3_mag(uint32_t c) {
+  uint32_t E = c >> 3, m = c & 7;
+  if (E == 0) return ldexp((double)m, -9);
+  return ldexp(1.0 + m / 8.0, (int)E - 7);
+}
+
+double orc_e4m3_to_f64(uint8_t c) {
+  double s = (c & 0x80) ? -1.0 : 1.0;
+  if ((c & 0x7F) == 0x7F) return NAN;
+  return s * e4m3_mag(c & 0x7F);
+}
+
+/* Nearest E4M3, ties to even, saturating at +-448 (reading: the pages never let a
+ * scaled value exceed 448, and saturation keeps anything larger finite). */
+uint8_t orc_e4m3_from_f64(double y) {
+  if (isnan(y)) return 0x7F;
+  uint8_t s = signbit(y) ? 0x80 : 0;
+  return (uint8_t)(s | nearest_code(fabs(y), e4m3_mag, 0x7E));
+}
+
+/* FP4 E2M1: magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}, sign bit 0x8. */
+static double e2m1_mag(uint32_t c) {
+  if (c < 2) return 0.5 * c;
+  return ldexp(1.0 + (c & 1) / 2.0, (int)(c >> 1) - 1);
+}
+
+double orc_e2m1_to_f64(uint8_t c) {
+  double s = (c & 0x8) ? -1.0 : 1.0;
+  return s * e2m1_mag(c & 7);
+}
+
+/* Nearest E2M1, ties to even, saturating at +-6. */
+uint8_t orc_e2m1_from_f64(double y) {
+  if (isnan(y)) return 0x7; /* never reached: NaN blocks are handled first */
+  uint8_t s = signbit(y) ? 0x8 : 0;
+  return (uint8_t)(s | nearest_code(fabs(y), e2m1_mag, 7));
+}
+
+/* RCEIL E8M0 scale exponent for MXFP8 E4M3 ([MX] Summary names RCEIL; reading):
+ * the smallest e in [-127, 127] with 448 * 2^e >= amax.  The scale byte is e + 127. */
+int orc_mx_scale_exponent(double amax) {
+  int e = -127;
+  if (amax > 0) {
+    e = ilogb(amax) - 9; /* 448 * 2^(k-9) < 2^k <= amax, so this guess is low */
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    while (e > -127 && ldexp(448.0, e - 1) >= amax) e--;
+    while (e < 127 && ldexp(448.0, e) < amax) e++;
+  }
+  return e;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Activations ([MX] Summary: swiglu = silu(gate) * up; [NV] Summary and [GE]     */
+/* Summary: GeGLU = gelu(gate) * up, tanh approximation by reading)            */
+/* ------------------------------------------------------------------------- */
+
+static const double GELU_K0 = 0.79788456080286535588; /* sqrt(2/pi) */
+static const double GELU_K1 = 0.044715;
+
+/* logistic function; 1/(1+exp(-z)) is accurate in both tails in binary64 */
+static double logistic(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* act(x):  silu(x) = x * sigma(x);
+ *          gelu_tanh(x) = x/2 * (1 + tanh(k0 (x + k1 x^3))).
+ * 1 + tanh(u) is evaluated as 2 * sigma(2u), the same quantity written without
+ * the cancellation that 1 + tanh(u) suffers for u << 0. */
+double orc_act(int act, double x) {
+  if (act == ORC_SWIGLU) return x * logistic(x);
+  double u = GELU_K0 * (x + GELU_K1 * x * x * x);
+  double one_plus_t = 2.0 * logistic(2.0 * u);
+  return 0.5 * x * one_plus_t;
+}
+
+/* act'(x):  silu'(x) = sigma(x) (1 + x (1 - sigma(x)));
+ *           gelu_tanh'(x) = (1 + t)/2 + x/2 (1 - t^2) k0 (1 + 3 k1 x^2).
+ * 1 - sigma(x) is sigma(-x); 1 - t^2 = (1 + t)(1 - t) with 1 -+ t = 2 sigma(-+2u)
+ * for the same reason as above. */
+double orc_act_grad(int act, double x) {
+  if (act == ORC_SWIGLU) return logistic(x) * (1.0 + x * logistic(-x));
+  double u = GELU_K0 * (x + GELU_K1 * x * x * x);
+  double one_plus_t = 2.0 * logistic(2.0 * u);
+  double one_minus_t = 2.0 * logistic(-2.0 * u);
+  return 0.5 * one_plus_t +
+         0.5 * x * (one_plus_t * one_minus_t) * GELU_K0 * (1.0 + 3.0 * GELU_K1 * x * x);
+}
+
+/* ------------------------------------------------------------------------- */
+/* GLU forward / backward on BF16 operands, one rounding at the store          */
+/* ------------------------------------------------------------------------- */
+
+/* Operand addressing.  SPLIT: gate and up are two [M, N] matrices with row
+ * stride ld (the concatenated [gate | up] of [MX] API is SPLIT with up = gate + N
+ * and ld = 2N).  PAIRED: one [M, 2N] matrix whose column 2j is gate_j and column
+ * 2j+1 is up_j ([NV] Supported contract, weight layout row). */
+static void load_pair(int layout, const uint16_t* gate, const uint16_t* up, int64_t ld,
+                      int64_t m, int64_t j, double* g, double* u) {
+  if (layout == ORC_PAIRED) {
+    *g = orc_bf16_to_f64(gate[m * ld + 2 * j]);
+    *u = orc_bf16_to_f64(gate[m * ld + 2 * j + 1]);
+  } else {
+    *g = orc_bf16_to_f64(gate[m * ld + j]);
+    *u = orc_bf16_to_f64(up[m * ld + j]);
+  }
+}
+
+/* h[m, j] = BF16(act(g) * u)  ([H] Fixed numerical paths: a single final rounding) */
+void orc_glu_fwd(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                 const uint16_t* up, int64_t ld, uint16_t* h, int64_t ldh) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; m++)
+    for (int64_t j = 0; j < N; j++) {
+      double g, u;
+      load_pair(layout, gate, up, ld, m, j, &g, &u);
+      h[m * ldh + j] = orc_bf16_from_f64(orc_act(act, g) * u);
+    }
+}
+
+/* da = BF16(dh * u * act'(g)),  db = BF16(dh * act(g))  ([GE] Testing Done names
+ * forward, da and db; [MX] API returns [dGate | dUp]).  SPLIT writes da and db as
+ * two [M, N] matrices with row stride ldo; PAIRED writes one [M, 2N] matrix in the
+ * input's interleaved order (da to column 2j, db to column 2j+1), db unused. */
+void orc_glu_bwd(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                 const uint16_t* up, int64_t ld, const uint16_t* dh, int64_t lddh,
+                 uint16_t* da, uint16_t* db, int64_t ldo) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; m++)
+    for (int64_t j = 0; j < N; j++) {
+      double g, u;
+      load_pair(layout, gate, up, ld, m, j, &g, &u);
+      double d = orc_bf16_to_f64(dh[m * lddh + j]);
+      uint16_t ra = orc_bf16_from_f64(d * u * orc_act_grad(act, g));
+      uint16_t rb = orc_bf16_from_f64(d * orc_act(act, g));
+      if (layout == ORC_PAIRED) {
+        da[m * ldo + 2 * j] = ra;
+        da[m * ldo + 2 * j + 1] = rb;
+      } else {
+        da[m * ldo + j] = ra;
+        db[m * ldo + j] = rb;
+      }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* MXFP8 quantizer ([MX] Summary: RCEIL E8M0 scale per 32 elements, E4M3 data)  */
+/* ------------------------------------------------------------------------- */
+
+/* One block of 32 values: scale byte and 32 codes. */
+static void mx_block(const double* v, uint8_t* codes, uint8_t* scale) {
+  int finite = 1;
+  double amax = 0.0;
+  for (int i = 0; i < 32; i++) {
+    if (!isfinite(v[i])) finite = 0;
+    else if (fabs(v[i]) > amax) amax = fabs(v[i]);
+  }
+  if (!finite) { /* reading: NaN scale and NaN codes */
+    *scale = 0xFF;
+    for (int i = 0; i < 32; i++) codes[i] = 0x7F;
+    return;
+  }
+  int e = orc_mx_scale_exponent(amax);
+  *scale = (uint8_t)(e + 127);
+  for (int i = 0; i < 32; i++) codes[i] = orc_e4m3_from_f64(ldexp(v[i], -e)); /* exact */
+}
+
+/* X is a row-major [M, N] matrix of FP32 values (BF16 values widened exactly are
+ * FP32 values).  Rowwise: blocks X[m, 32b .. 32b+31], codes [M, N], scales
+ * [M, N/32].  Colwise: blocks X[32b .. 32b+31, j], codes stored transposed as
+ * [N, M] (row j holds column j of X), scales [N, M/32]. */
+void orc_quant_mxfp8(int64_t M, int64_t N, const float* X, int flags, uint8_t* q_row,
+                     uint8_t* s_row, uint8_t* q_col, uint8_t* s_col) {
+  if (flags & ORC_ROWWISE) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+      for (int64_t b = 0; b < N / 32; b++) {
+        double v[32];
+        uint8_t c[32];
+        for (int i = 0; i < 32; i++) v[i] = X[m * N + 32 * b + i];
+        mx_block(v, c, &s_row[m * (N / 32) + b]);
+        memcpy(&q_row[m * N + 32 * b], c, 32);
+      }
+  }
+  if (flags & ORC_COLWISE) {
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < N; j++)
+      for (int64_t b = 0; b < M / 32; b++) {
+        double v[32];
+        uint8_t c[32];
+        for (int i = 0; i < 32; i++) v[i] = X[(32 * b + i) * N + j];
+        mx_block(v, c, &s_col[j * (M / 32) + b]);
+        memcpy(&q_col[j * M + 32 * b], c, 32);
+      }
+  }
+}
+
+/* ------------------------------------------------------------------------- */
+/* NVFP4 quantizer, global scale 1 ([NV] Supported contract)                   */
+/* ------------------------------------------------------------------------- */
+
+/* Byte offset of scale (r, c) in the 128x4 layout (reading: the public
+ * cuBLAS/CUTLASS block-scale layout that the page names; rows padded to a
+ * multiple of 128, scale columns to a multiple of 4). */
+int64_t orc_sf128x4_offset(int64_t r, int64_t c, int64_t scale_cols_padded) {
+  return ((r / 128) * (scale_cols_padded / 4) + c / 4) * 512 + (r % 32) * 16 +
+         ((r % 128) / 32) * 4 + (c % 4);
+}
+
+/* One block of 16 values: E4M3 scale byte and 16 E2M1 codes (one per byte). */
+static void nv_block(const double* v, uint8_t* codes, uint8_t* scale) {
+  int finite = 1;
+  double amax = 0.0;
+  for (int i = 0; i < 16; i++) {
+    if (!isfinite(v[i])) finite = 0;
+    else if (fabs(v[i]) > amax) amax = fabs(v[i]);
+  }
+  if (!finite) { /* reading: NaN scale, zero codes */
+    *scale = 0x7F;
+    memset(codes, 0, 16);
+    return;
+  }
+  /* Reading: S = E4M3(amax / 6), nearest; then codes = E2M1(x / S).  The binary64
+   * quotients take the same rounding decision as the exact ones for FP32 inputs. */
+  uint8_t sc = orc_e4m3_from_f64(amax / 6.0);
+  double S = orc_e4m3_to_f64(sc);
+  *scale = sc;
+  for (int i = 0; i < 16; i++) {
+    if (S == 0.0) codes[i] = signbit(v[i]) ? 0x8 : 0x0;
+    else codes[i] = orc_e2m1_from_f64(v[i] / S);
+  }
+}
+
+/* X is row-major [M, H] FP32.  q is [M, H/2] bytes, element 2k in the low nibble
+ * of byte k and element 2k+1 in the high nibble.  sf is [M, H/16] row-major, or
+ * the zero-padded 128x4 layout of ceil(M/128)*128 rows x ceil(H/64)*4 columns. */
+void orc_quant_nvfp4(int64_t M, int64_t H, const float* X, uint8_t* q, uint8_t* sf,
+                     int sf_layout) {
+  int64_t nb = H / 16;
+  int64_t cols_padded = (nb + 3) / 4 * 4;
+  int64_t rows_padded = (M + 127) / 128 * 128;
+  if (sf_layout == ORC_SF_128x4) memset(sf, 0, (size_t)(rows_padded * cols_padded));
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; m++)
+    for (int64_t b = 0; b < nb; b++) {
+      double v[16];
+      uint8_t c[16], s;
+      for (int i = 0; i < 16; i++) v[i] = X[m * H + 16 * b + i];
+      nv_block(v, c, &s);
+      for (int k = 0; k < 8; k++)
+        q[m * (H / 2) + 8 * b + k] = (uint8_t)(c[2 * k] | (c[2 * k + 1] << 4));
+      if (sf_layout == ORC_SF_128x4) sf[orc_sf128x4_offset(m, b, cols_padded)] = s;
+      else sf[m * nb + b] = s;
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Fused paths = GLU (one BF16 rounding) followed by the quantizer             */
+/* ([MX] Numerics and tests: equal to the activation then the quantizers)      */
+/* ------------------------------------------------------------------------- */
+
+static float* widen_bf16(const uint16_t* b, int64_t n) {
+  float* f = (float*)malloc((size_t)n * sizeof(float));
+  if (!f) return NULL;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; i++) f[i] = (float)orc_bf16_to_f64(b[i]);
+  return f;
+}
+
+/* Returns 0 on success, -1 if host memory ran out. */
+int orc_glu_fwd_mxfp8(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                      const uint16_t* up, int64_t ld, int flags, uint8_t* q_row,
+                      uint8_t* s_row, uint8_t* q_col, uint8_t* s_col) {
+  uint16_t* h = (uint16_t*)malloc((size_t)(M * N) * sizeof(uint16_t));
+  if (!h) return -1;
+  orc_glu_fwd(act, layout, M, N, gate, up, ld, h, N);
+  float* x = widen_bf16(h, M * N);
+  free(h);
+  if (!x) return -1;
+  orc_quant_mxfp8(M, N, x, flags, q_row, s_row, q_col, s_col);
+  free(x);
+  return 0;
+}
+
+/* Backward: the quantized matrix is [da | db], [M, 2N] ([MX] API). */
+int orc_glu_bwd_mxfp8(int act, int64_t M, int64_t N, const uint16_t* gate,
+                      const uint16_t* up, int64_t ld, const uint16_t* dh, int64_t lddh,
+                      int flags, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                      uint8_t* s_col) {
+  uint16_t* d = (uint16_t*)malloc((size_t)(M * 2 * N) * sizeof(uint16_t));
+  if (!d) return -1;
+  orc_glu_bwd(act, ORC_SPLIT, M, N, gate, up, ld, dh, lddh, d, d + N, 2 * N);
+  float* x = widen_bf16(d, M * 2 * N);
+  free(d);
+  if (!x) return -1;
+  orc_quant_mxfp8(M, 2 * N, x, flags, q_row, s_row, q_col, s_col);
+  free(x);
+  return 0;
+}
+
+int orc_glu_fwd_nvfp4(int act, int layout, int64_t M, int64_t H, const uint16_t* gate,
+                      const uint16_t* up, int64_t ld, uint8_t* q, uint8_t* sf,
+                      int sf_layout) {
+  uint16_t* h = (uint16_t*)malloc((size_t)(M * H) * sizeof(uint16_t));
+  if (!h) return -1;
+  orc_glu_fwd(act, layout, M, H, gate, up, ld, h, H);
+  float* x = widen_bf16(h, M * H);
+  free(h);
+  if (!x) return -1;
+  orc_quant_nvfp4(M, H, x, q, sf, sf_layout);
+  free(x);
+  return 0;
+}
+
+/* Element-wise encoders over arrays, for the format pins. */
+void orc_bf16_from_f64_array(const double* v, int64_t n, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; i++) out[i] = orc_bf16_from_f64(v[i]);
+}
+void orc_e4m3_from_f64_array(const double* v, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; i++) out[i] = orc_e4m3_from_f64(v[i]);
+}
+void orc_e2m1_from_f64_array(const double* v, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; i++) out[i] = orc_e2m1_from_f64(v[i]);
+}
+void orc_act_array(int act, const double* x, int64_t n, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; i++) out[i] = orc_act(act, x[i]);
+}
+void orc_act_grad_array(int act, const double* x, int64_t n, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; i++) out[i] = orc_act_grad(act, x[i]);
+}

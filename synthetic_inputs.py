@@ -1,0 +1,78 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module holds no arithmetic of the method: it only draws random tensors.  Every
+draw uses a CPU torch.Generator, so the same seed gives the same bits on any machine.
+
+Workloads (shapes and value distributions of the pages' benchmarks):
+  * swiglu_small  : gate, up BF16 [128, 128] ~ N(0, 1).
+  * swiglu_mid    : gate, up, dh BF16 [4096, 2048] ~ N(0, 1).
+  * swiglu_large  : gate, up, dh BF16 [16384, 7168] ~ N(0, 1) with 0.1% of the
+                    elements of each tensor multiplied by 1000, and the rowwise-only
+                    forward case [131072, 8192] with the same recipe.
+  * geglu_bf16    : gate, up, dh BF16 [R, W] ~ N(0, 1), R in {1024, 8192},
+                    W in {4096, 11008, 14336, 18944, 29568, 8193}.
+  * geglu_nvfp4   : one BF16 [M, 32768] ~ N(0, 1) matrix, columns interleaved
+                    gate0, up0, gate1, up1, ... for M in {784, 816, 880, 968}.
+Draw order within one call: gate, up, dh (then the outlier masks, in the same order).
+"""
+import numpy as np
+import torch
+
+OUTLIER_FRACTION = 1e-3
+OUTLIER_FACTOR = 1000.0
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    """BF16 tensor -> numpy uint16 bit patterns (a view, no arithmetic)."""
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def normal_bf16(shapes, seed=0, outliers=False):
+    """Draws len(shapes) BF16 tensors ~ N(0,1) in order; with outliers=True each tensor
+    has an independent Bernoulli(OUTLIER_FRACTION) mask of elements scaled by
+    OUTLIER_FACTOR before the BF16 rounding.  Returns torch bfloat16 CPU tensors."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    ts = [torch.randn(s, generator=g, dtype=torch.float32) for s in shapes]
+    if outliers:
+        for t in ts:
+            mask = torch.rand(t.shape, generator=g) < OUTLIER_FRACTION
+            t[mask] *= OUTLIER_FACTOR
+    return [t.to(torch.bfloat16) for t in ts]
+
+
+def glu_operands(M, N, seed=0, outliers=False, with_dh=False):
+    """gate, up (and dh) BF16 [M, N] as torch CPU tensors."""
+    n = 3 if with_dh else 2
+    return normal_bf16([(M, N)] * n, seed=seed, outliers=outliers)
+
+
+def paired_operand(M, H, seed=0):
+    """One BF16 [M, 2H] matrix ~ N(0,1); column 2j is gate_j, column 2j+1 is up_j."""
+    return normal_bf16([(M, 2 * H)], seed=seed)[0]
+
+
+def special_bf16_values():
+    """Every finite BF16 bit pattern (both signs), as a uint16 numpy array."""
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    mag = allb & 0x7FFF
+    return allb[mag < 0x7F80]
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    return _bits(t)
+
+
+def from_bits(b: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16)
+
+
+WORKLOADS = {
+    "swiglu_small": dict(M=128, N=128),
+    "swiglu_mid": dict(M=4096, N=2048),
+    "swiglu_large": dict(M=16384, N=7168),
+    "swiglu_xlarge_fwd_row": dict(M=131072, N=8192),
+    "geglu_rows": (1024, 8192),
+    "geglu_widths": (4096, 11008, 14336, 18944, 29568, 8193),
+    "geglu_nvfp4_rows": (784, 816, 880, 968),
+    "geglu_nvfp4_hidden": 16384,
+}

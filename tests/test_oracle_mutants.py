@@ -1,0 +1,87 @@
+"""The oracle's pins must catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a temporary copy of oracle/glu_oracle.c (a dropped term,
+a wrong sign, a swapped or transposed operand, a wrong tie rule, a wrong constant),
+builds it, routes the oracle module to it and runs a few pin tests.  At least one pin
+must fail for every mutant; the real oracle is untouched.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+import test_oracle_formats as tf
+import test_oracle_glu as tg
+import test_oracle_quant as tq
+
+S, G = oracle.SWIGLU, oracle.GEGLU_TANH
+
+# (name, text to find, replacement, pins that should notice)
+MUTANTS = [
+    ("gelu drops x^3", "GELU_K0 * (x + GELU_K1 * x * x * x)", "GELU_K0 * (x)",
+     [lambda: tg.test_act_against_mpmath(G)]),
+    ("silu' sign", "logistic(x) * (1.0 + x * logistic(-x))", "logistic(x) * (1.0 - x * logistic(-x))",
+     [lambda: tg.test_act_grad_against_mpmath(S)]),
+    ("gelu' drops the 3", "3.0 * GELU_K1", "GELU_K1",
+     [lambda: tg.test_act_grad_against_mpmath(G)]),
+    ("gelu' drops a factor", "0.5 * x * (one_plus_t * one_minus_t)", "0.5 * x * (one_plus_t)",
+     [lambda: tg.test_act_grad_against_autograd(G)]),
+    ("ties away from zero", "return (lo % 2 == 0) ? lo : hi;", "return hi;",
+     [tf.test_e4m3_golden, tf.test_e2m1_golden, tf.test_bf16_overflow_and_specials]),
+    ("RCEIL on equality", "ldexp(448.0, e) < amax", "ldexp(448.0, e) <= amax",
+     [tf.test_rceil_golden]),
+    ("RCEIL rounds down", "while (e < 127 && ldexp(448.0, e) < amax) e++;",
+     "while (e < 127 && ldexp(448.0, e + 1) < amax) e++;", [tf.test_rceil_golden]),
+    ("colwise scales transposed", "&s_col[j * (M / 32) + b]", "&s_col[b * N + j]",
+     [tq.test_mx_colwise_is_rowwise_of_transpose]),
+    ("colwise codes transposed", "memcpy(&q_col[j * M + 32 * b], c, 32);",
+     "for (int i = 0; i < 32; i++) q_col[(32 * b + i) * N + j] = c[i];",
+     [tq.test_mx_golden_blocks_rowwise_and_colwise]),
+    ("nibble order", "(c[2 * k] | (c[2 * k + 1] << 4))", "(c[2 * k + 1] | (c[2 * k] << 4))",
+     [tq.test_nv_golden_blocks]),
+    ("gate and up swapped", "*g = orc_bf16_to_f64(gate[m * ld + j]);\n    *u = orc_bf16_to_f64(up[m * ld + j]);",
+     "*g = orc_bf16_to_f64(up[m * ld + j]);\n    *u = orc_bf16_to_f64(gate[m * ld + j]);",
+     [lambda: tg.test_glu_fwd_matches_float64_reference(S)]),
+    ("da drops up", "d * u * orc_act_grad(act, g)", "d * orc_act_grad(act, g)",
+     [lambda: tg.test_glu_bwd_matches_autograd(S)]),
+    ("paired columns swapped", "*g = orc_bf16_to_f64(gate[m * ld + 2 * j]);", "*g = orc_bf16_to_f64(gate[m * ld + 2 * j + 1]);",
+     [tg.test_layouts_agree]),
+    ("NV scale divisor", "amax / 6.0", "amax / 4.0", [tq.test_nv_golden_blocks]),
+    ("MX scale direction", "ldexp(v[i], -e)", "ldexp(v[i], e)", [tq.test_mx_golden_blocks_rowwise_and_colwise]),
+    ("bf16 subnormal exponent", "ldexp((double)m, -133)", "ldexp((double)m, -134)",
+     [tf.test_bf16_overflow_and_specials]),
+    ("E2M1 saturation", "nearest_code(fabs(y), e2m1_mag, 7)", "nearest_code(fabs(y), e2m1_mag, 6)",
+     [tf.test_e2m1_golden]),
+    ("E4M3 subnormal step", "ldexp((double)m, -9)", "ldexp((double)m, -10)", [tf.test_e4m3_decode_matches_torch]),
+    ("non-finite blocks ignored", "if (!isfinite(v[i])) finite = 0;", "if (0) finite = 0;",
+     [tq.test_mx_nonfinite_block_reading]),
+    ("128x4 row interleave", "(r % 32) * 16 +\n         ((r % 128) / 32) * 4", "(r % 32) * 4 +\n         ((r % 128) / 32) * 16",
+     [tq.test_sf128x4_layout_is_zero_padded_permutation]),
+]
+
+
+def _fails(pin) -> bool:
+    try:
+        pin()
+    except AssertionError:
+        return True
+    return False
+
+
+@pytest.mark.parametrize("name,find,repl,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, find, repl, pins):
+    with open(obuild.SRC) as f:
+        src = f.read()
+    assert src.count(find) >= 1, f"mutation site not found: {name}"
+    with tempfile.TemporaryDirectory() as d:
+        msrc = os.path.join(d, "mutant.c")
+        with open(msrc, "w") as f:
+            f.write(src.replace(find, repl))
+        lib = obuild.build(src=msrc, lib=os.path.join(d, "libmutant.so"))
+        with oracle.use_library(lib):
+            assert any(_fails(p) for p in pins), f"no pin noticed: {name}"
+    # the real oracle still passes the same pins
+    for p in pins:
+        p()

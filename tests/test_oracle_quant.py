@@ -1,0 +1,197 @@
+"""Pins for the oracle's MXFP8 and NVFP4 quantizers (CPU only).
+
+References independent of the oracle's own code: hand-worked blocks under tests/golden/,
+brute-force nearest searches with exact rationals over every code of the target format,
+the transpose identity colwise(X) = rowwise(X^T), and the 128x4 scale layout checked as a
+zero-padded permutation with hand-placed entries.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic_inputs as si
+from conftest import parse_golden
+from test_oracle_formats import E2M1, E4M3, _brute_e2m1, _brute_e4m3, _brute_rceil
+
+
+def _block_rows(name):
+    out = []
+    for row in parse_golden(name):
+        cols = [c.strip() for c in row.split("|")]
+        lead = [float.fromhex(v) for v in cols[1].split(",")]
+        fill = float(cols[4]) if cols[4] != "-0" else -0.0
+        out.append((cols[0], lead, int(cols[2], 16), [int(c, 16) for c in cols[3].split(",")], fill))
+    return out
+
+
+def test_mx_golden_blocks_rowwise_and_colwise():
+    for name, lead, scale, codes, fill in _block_rows("mx_block_hand.txt"):
+        blk = np.full(32, fill, np.float32)
+        blk[: len(lead)] = lead
+        q, s, _, _ = oracle.quant_mxfp8(blk.reshape(1, 32), oracle.ROWWISE)
+        rest = 0x80 if np.signbit(fill) else 0x00
+        want = codes + [rest] * (32 - len(codes))
+        assert int(s[0, 0]) == scale, name
+        assert list(q[0]) == want, name
+        # the same block standing as a column of a [32, 3] matrix
+        X = np.zeros((32, 3), np.float32)
+        X[:, 1] = blk
+        _, _, qc, sc = oracle.quant_mxfp8(X, oracle.COLWISE)
+        assert int(sc[1, 0]) == scale and list(qc[1]) == want, name
+
+
+def test_nv_golden_blocks():
+    for name, lead, scale, packed, fill in _block_rows("nv_block_hand.txt"):
+        blk = np.full(16, fill, np.float32)
+        blk[: len(lead)] = lead
+        q, sf = oracle.quant_nvfp4(blk.reshape(1, 16))
+        assert int(sf[0, 0]) == scale, name
+        assert list(q[0][: len(packed)]) == packed, name
+        assert not np.any(q[0][len(packed):]), name
+
+
+def _random_matrix(M, N, seed):
+    rng = np.random.default_rng(seed)
+    X = rng.normal(0, 1, (M, N))
+    X[rng.random((M, N)) < 0.01] *= 1000
+    X[rng.random((M, N)) < 0.01] *= 1e-30
+    X[:, :32][0] = 0.0  # one all-zero block
+    X[1, 32:64] = -0.0
+    return X.astype(np.float32)
+
+
+def test_mx_rowwise_brute_force():
+    X = _random_matrix(6, 96, 20)
+    q, s, _, _ = oracle.quant_mxfp8(X, oracle.ROWWISE)
+    for m in range(X.shape[0]):
+        for b in range(X.shape[1] // 32):
+            blk = X[m, 32 * b: 32 * b + 32]
+            e = _brute_rceil(float(np.max(np.abs(blk))))
+            assert int(s[m, b]) == e + 127
+            for i, x in enumerate(blk):
+                assert int(q[m, 32 * b + i]) == _brute_e4m3(float(x) * 2.0 ** -e)
+
+
+def test_mx_colwise_is_rowwise_of_transpose():
+    X = _random_matrix(64, 96, 21)
+    qr, sr, qc, sc = oracle.quant_mxfp8(X, oracle.ROWWISE | oracle.COLWISE)
+    tq, ts, _, _ = oracle.quant_mxfp8(np.ascontiguousarray(X.T), oracle.ROWWISE)
+    assert np.array_equal(qc, tq) and np.array_equal(sc, ts)
+    # "both" equals the two single-direction runs
+    q1, s1, _, _ = oracle.quant_mxfp8(X, oracle.ROWWISE)
+    _, _, q2, s2 = oracle.quant_mxfp8(X, oracle.COLWISE)
+    assert np.array_equal(qr, q1) and np.array_equal(sr, s1)
+    assert np.array_equal(qc, q2) and np.array_equal(sc, s2)
+
+
+def test_mx_dequant_error_bound():
+    """Every element dequantizes to within half an E4M3 step at the block scale (the
+    code is the nearest value) and no scaled value exceeds 448."""
+    X = _random_matrix(32, 256, 22)
+    q, s, _, _ = oracle.quant_mxfp8(X, oracle.ROWWISE)
+    dec = oracle.e4m3_to_f64(q) * np.exp2(np.repeat(s.astype(np.int64) - 127, 32, axis=1))
+    scaled = np.abs(X.astype(np.float64)) * np.exp2(-(np.repeat(s.astype(np.int64) - 127, 32, axis=1)))
+    assert np.all(scaled <= 448)
+    err = np.abs(dec - X) * np.exp2(-(np.repeat(s.astype(np.int64) - 127, 32, axis=1)))
+    step = np.where(scaled < 2.0 ** -6, 2.0 ** -9, np.exp2(np.floor(np.log2(np.maximum(scaled, 2.0 ** -6)))) / 8)
+    assert np.all(err <= step / 2 + 1e-30)
+
+
+def test_mx_nonfinite_block_reading():
+    """Reading (parity unpinned): a block with NaN or Inf gets scale 0xFF and codes 0x7F;
+    other blocks of the same row are unaffected."""
+    X = np.ones((1, 96), np.float32)
+    X[0, 5] = np.inf
+    X[0, 40] = np.nan
+    q, s, _, _ = oracle.quant_mxfp8(X, oracle.ROWWISE)
+    assert list(s[0]) == [0xFF, 0xFF, 119]
+    assert np.all(q[0, :64] == 0x7F) and np.all(q[0, 64:] == 0x78)  # 1.0 * 2^8 = 256
+
+
+def test_nv_brute_force():
+    X = _random_matrix(4, 64, 23)
+    X[2, 16:32] = np.linspace(-7, 7, 16)
+    q, sf = oracle.quant_nvfp4(X)
+    for m in range(X.shape[0]):
+        for b in range(X.shape[1] // 16):
+            blk = X[m, 16 * b: 16 * b + 16]
+            amax = Fraction(float(np.max(np.abs(blk))))
+            sc = min(range(0x7F), key=lambda c: (abs(E4M3[c] - amax / 6), c % 2)) if amax / 6 < 448 else 0x7E
+            assert int(sf[m, b]) == sc
+            S = E4M3[sc]
+            for i, x in enumerate(blk):
+                nib = (int(q[m, 8 * b + i // 2]) >> (4 * (i % 2))) & 0xF
+                if S == 0:
+                    want = 0x8 if np.signbit(x) else 0
+                else:
+                    a = Fraction(float(abs(x))) / S
+                    want = (0x8 if np.signbit(x) else 0) | (7 if a >= 6 else min(range(8), key=lambda c: (abs(E2M1[c] - a), c % 2)))
+                assert nib == want, (m, b, i, float(x))
+
+
+def test_nv_nonfinite_block_reading():
+    X = np.ones((1, 32), np.float32)
+    X[0, 3] = -np.inf
+    q, sf = oracle.quant_nvfp4(X)
+    assert int(sf[0, 0]) == 0x7F and not np.any(q[0, :8])
+    # amax 1: 1/6 = 0.1667 lies between E4M3 0.15625 (0x22) and 0.171875 (0x23), nearer 0x23
+    assert int(sf[0, 1]) == 0x23
+
+
+def test_sf128x4_layout_is_zero_padded_permutation():
+    for M, H in [(784, 16384), (968, 1024), (130, 80), (1, 16)]:
+        nb = H // 16
+        cp = (nb + 3) // 4 * 4
+        rp = (M + 127) // 128 * 128
+        offs = np.array([[oracle.sf128x4_offset(r, c, cp) for c in range(nb)] for r in range(min(M, 260))])
+        assert len(set(offs.ravel().tolist())) == offs.size
+        assert offs.min() >= 0 and offs.max() < rp * cp
+    # hand-placed entries: 16 bytes per row within a 32-row group, 4 bytes per 32-row group,
+    # 512 bytes per 128-row x 4-column tile, tiles of one row band laid out along columns.
+    cp = 1024
+    assert oracle.sf128x4_offset(0, 0, cp) == 0
+    assert oracle.sf128x4_offset(0, 1, cp) == 1
+    assert oracle.sf128x4_offset(0, 4, cp) == 512
+    assert oracle.sf128x4_offset(1, 0, cp) == 16
+    assert oracle.sf128x4_offset(32, 0, cp) == 4
+    assert oracle.sf128x4_offset(96, 3, cp) == 15
+    assert oracle.sf128x4_offset(31, 0, cp) == 496
+    assert oracle.sf128x4_offset(128, 0, cp) == (cp // 4) * 512
+
+
+def test_nv_128x4_equals_rowmajor_after_unswizzle():
+    X = _random_matrix(200, 128, 24)
+    q1, s1 = oracle.quant_nvfp4(X, oracle.SF_ROWMAJOR)
+    q2, s2 = oracle.quant_nvfp4(X, oracle.SF_128x4)
+    assert np.array_equal(q1, q2)
+    nb, cp = 8, 8
+    seen = np.zeros(s2.size, bool)
+    for r in range(200):
+        for c in range(nb):
+            o = oracle.sf128x4_offset(r, c, cp)
+            assert s2[o] == s1[r, c]
+            seen[o] = True
+    assert not np.any(s2[~seen])
+
+
+def test_fused_equals_glu_then_quantizer():
+    gate, up, dh = si.glu_operands(64, 64, seed=25, outliers=True, with_dh=True)
+    gb, ub, db_ = si.to_bits(gate), si.to_bits(up), si.to_bits(dh)
+    for kind in (oracle.SWIGLU, oracle.GEGLU_TANH):
+        h = oracle.glu_fwd(kind, gb, ub)
+        hf = si.from_bits(h).float().numpy()
+        a = oracle.glu_fwd_mxfp8(kind, gb, ub, flags=3)
+        b = oracle.quant_mxfp8(hf, 3)
+        assert all(np.array_equal(x, y) for x, y in zip(a, b))
+        da, dbb = oracle.glu_bwd(kind, gb, ub, db_)
+        cat = si.from_bits(np.concatenate([da, dbb], axis=1)).float().numpy()
+        a = oracle.glu_bwd_mxfp8(kind, gb, ub, db_, flags=3)
+        b = oracle.quant_mxfp8(cat, 3)
+        assert all(np.array_equal(x, y) for x, y in zip(a, b))
+        paired = np.empty((64, 128), np.uint16)
+        paired[:, 0::2], paired[:, 1::2] = gb, ub
+        a = oracle.glu_fwd_nvfp4(kind, paired, None)
+        b = oracle.quant_nvfp4(hf)
+        assert all(np.array_equal(x, y) for x, y in zip(a, b))
