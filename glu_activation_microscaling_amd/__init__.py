@@ -1,0 +1,242 @@
+"""Python binding of libglu_mx.so, the MI355X (gfx950) fused GLU + microscaling library.
+
+Argument marshalling only: every function checks dtypes and devices, takes data pointers,
+strides and the current HIP stream from torch tensors, allocates outputs when none are
+given, and calls the C entry point of the same name.  All computation happens in the HIP
+kernels; there is no CPU or PyTorch fallback, and a missing or unloadable library raises.
+
+Entry points (C names in include/glu_mx.h):
+  glu_fwd(gate, up=None, act=..., layout=...)               -> h
+  glu_bwd(gate, up, dh, act=..., layout=...)                -> (da, db) or interleaved d
+  glu_fwd_mxfp8(gate, up=None, rowwise=, colwise=, ...)     -> (q_row, q_col, s_row, s_col)
+  glu_bwd_mxfp8(gate, up, dh, rowwise=, colwise=, ...)      -> (q_row, q_col, s_row, s_col)
+  glu_fwd_nvfp4(x, up=None, layout="paired", sf_layout=...) -> (q, sf)
+  glu_quant_mxfp8_f32(x, rowwise=, colwise=)                -> (q_row, q_col, s_row, s_col)
+  glu_quant_nvfp4_f32(x, sf_layout=)                        -> (q, sf)
+A disabled MXFP8 direction comes back as zero-sized tensors (fixed arity), as in the
+MXFP8 page's API section.  Codes and scales are uint8 tensors; BF16 data is torch.bfloat16.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libglu_mx.so")
+
+ACT = {"swiglu": 0, "geglu": 1, "geglu_tanh": 1}
+LAYOUT = {"split": 0, "paired": 1}
+SF_LAYOUT = {"rowmajor": 0, "128x4": 1}
+ROWWISE, COLWISE = 1, 2
+
+STATUS = {
+    0: "GLU_OK", 1: "GLU_ERR_NULL", 2: "GLU_ERR_SHAPE", 3: "GLU_ERR_ALIGN", 4: "GLU_ERR_STRIDE",
+    5: "GLU_ERR_ARG", 6: "GLU_ERR_OVERLAP", 7: "GLU_ERR_UNSUPPORTED", 8: "GLU_ERR_HIP",
+}
+
+_i64, _int, _p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+_SIGNATURES = {
+    "glu_fwd": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _p],
+    "glu_bwd": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p],
+    "glu_fwd_mxfp8": [_int, _int, _i64, _i64, _p, _p, _i64, _int, _p, _p, _p, _p, _p],
+    "glu_bwd_mxfp8": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _int, _p, _p, _p, _p, _p],
+    "glu_fwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int, _p],
+    "glu_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p, _p],
+    "glu_quant_nvfp4_f32": [_i64, _i64, _p, _i64, _p, _p, _int, _p],
+    "glu_check_fwd": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64],
+    "glu_check_bwd": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _p, _p, _i64],
+    "glu_check_fwd_mxfp8": [_int, _int, _i64, _i64, _p, _p, _i64, _int, _p, _p, _p, _p],
+    "glu_check_bwd_mxfp8": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _int, _p, _p, _p, _p],
+    "glu_check_fwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int],
+    "glu_check_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p],
+    "glu_check_quant_nvfp4_f32": [_i64, _i64, _p, _i64, _p, _p, _int],
+}
+
+_lib = None
+
+
+class GluError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({lib().glu_status_string(status).decode()})")
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "or python glu_activation_microscaling_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.glu_status_string.argtypes = [ctypes.c_int]
+        L.glu_status_string.restype = ctypes.c_char_p
+        L.glu_nvfp4_sf_bytes.argtypes = [_i64, _i64, _int]
+        L.glu_nvfp4_sf_bytes.restype = _i64
+        L.glu_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _call(fn, *args):
+    st = getattr(lib(), fn)(*args)
+    if st != 0:
+        raise GluError(fn, st)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
+
+
+def _rowmajor(t, name, dtype):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride (no silent copies)")
+    return t.size(0), t.size(1), t.stride(0)
+
+
+def _operands(gate, up, layout):
+    M, C, ld = _rowmajor(gate, "gate", torch.bfloat16)
+    if layout == "paired":
+        if up is not None:
+            raise ValueError("the paired layout takes one interleaved matrix")
+        if C % 2:
+            raise ValueError("the paired matrix needs an even number of columns")
+        return M, C // 2, ld
+    if up is None:
+        raise ValueError("the split layout needs gate and up")
+    Mu, Cu, ldu = _rowmajor(up, "up", torch.bfloat16)
+    if (Mu, Cu) != (M, C):
+        raise ValueError("gate and up differ in shape")
+    if ldu != ld and M > 1:
+        raise ValueError("gate and up must share a row stride")
+    return M, C, ld
+
+
+def glu_fwd(gate, up=None, *, act="swiglu", layout="split", out=None):
+    """h = bf16(act(gate) * up), [M, N]."""
+    M, N, ld = _operands(gate, up, layout)
+    h = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=gate.device)
+    _, _, ldh = _rowmajor(h, "out", torch.bfloat16)
+    _call("glu_fwd", ACT[act], LAYOUT[layout], M, N, _ptr(gate), _ptr(up), ld, _ptr(h), ldh,
+          _stream(gate))
+    return h
+
+
+def glu_bwd(gate, up, dh, *, act="swiglu", layout="split", out=None):
+    """Split: (da, db) each [M, N].  Paired: one interleaved [M, 2N] gradient.
+    out: (da, db) for split or a single tensor for paired; may alias (gate, up) in place."""
+    M, N, ld = _operands(gate, up, layout)
+    _, _, lddh = _rowmajor(dh, "dh", torch.bfloat16)
+    dev = gate.device
+    if layout == "paired":
+        d = out if out is not None else torch.empty((M, 2 * N), dtype=torch.bfloat16, device=dev)
+        _, _, ldo = _rowmajor(d, "out", torch.bfloat16)
+        _call("glu_bwd", ACT[act], 1, M, N, _ptr(gate), None, ld, _ptr(dh), lddh, _ptr(d), None,
+              ldo, _stream(gate))
+        return d
+    if out is None:
+        out = (torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+               torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+    da, db = out
+    _, _, ldo = _rowmajor(da, "da", torch.bfloat16)
+    _, _, ldb = _rowmajor(db, "db", torch.bfloat16)
+    if ldb != ldo and M > 1:
+        raise ValueError("da and db must share a row stride")
+    _call("glu_bwd", ACT[act], 0, M, N, _ptr(gate), _ptr(up), ld, _ptr(dh), lddh, _ptr(da),
+          _ptr(db), ldo, _stream(gate))
+    return da, db
+
+
+def _mx_buffers(M, C, rowwise, colwise, dev, out):
+    if out is not None:
+        return out
+    u8 = dict(dtype=torch.uint8, device=dev)
+    z = torch.empty((0,), **u8)
+    q_row = torch.empty((M, C), **u8) if rowwise else z
+    s_row = torch.empty((M, C // 32), **u8) if rowwise else z
+    q_col = torch.empty((C, M), **u8) if colwise else z
+    s_col = torch.empty((C, M // 32), **u8) if colwise else z
+    return q_row, q_col, s_row, s_col
+
+
+def _flags(rowwise, colwise):
+    f = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
+    if f == 0:
+        raise ValueError("enable rowwise, colwise or both")
+    return f
+
+
+def glu_fwd_mxfp8(gate, up=None, *, act="swiglu", layout="split", rowwise=True, colwise=False, out=None):
+    """Fused forward + MXFP8: (q_row [M,N], q_col [N,M], s_row [M,N/32], s_col [N,M/32])."""
+    M, N, ld = _operands(gate, up, layout)
+    f = _flags(rowwise, colwise)
+    q_row, q_col, s_row, s_col = _mx_buffers(M, N, rowwise, colwise, gate.device, out)
+    _call("glu_fwd_mxfp8", ACT[act], LAYOUT[layout], M, N, _ptr(gate), _ptr(up), ld, f,
+          _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(gate))
+    return q_row, q_col, s_row, s_col
+
+
+def glu_bwd_mxfp8(gate, up, dh, *, act="swiglu", rowwise=True, colwise=False, out=None):
+    """Fused backward + MXFP8 of [da | db] ([M, 2N]): (q_row [M,2N], q_col [2N,M],
+    s_row [M,2N/32], s_col [2N,M/32])."""
+    M, N, ld = _operands(gate, up, "split")
+    _, _, lddh = _rowmajor(dh, "dh", torch.bfloat16)
+    f = _flags(rowwise, colwise)
+    q_row, q_col, s_row, s_col = _mx_buffers(M, 2 * N, rowwise, colwise, gate.device, out)
+    _call("glu_bwd_mxfp8", ACT[act], 0, M, N, _ptr(gate), _ptr(up), ld, _ptr(dh), lddh, f,
+          _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(gate))
+    return q_row, q_col, s_row, s_col
+
+
+def nvfp4_sf_bytes(M, H, sf_layout="rowmajor"):
+    return lib().glu_nvfp4_sf_bytes(M, H, SF_LAYOUT[sf_layout])
+
+
+def _nv_buffers(M, H, sf_layout, dev, out):
+    if out is not None:
+        return out
+    q = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
+    if sf_layout == "rowmajor":
+        sf = torch.empty((M, H // 16), dtype=torch.uint8, device=dev)
+    else:
+        sf = torch.empty((nvfp4_sf_bytes(M, H, sf_layout),), dtype=torch.uint8, device=dev)
+    return q, sf
+
+
+def glu_fwd_nvfp4(x, up=None, *, act="geglu", layout="paired", sf_layout="rowmajor", out=None):
+    """Fused forward + NVFP4 (global scale 1): (q [M, H/2] packed E2M1, sf scales)."""
+    M, H, ld = _operands(x, up, layout)
+    q, sf = _nv_buffers(M, H, sf_layout, x.device, out)
+    _call("glu_fwd_nvfp4", ACT[act], LAYOUT[layout], M, H, _ptr(x), _ptr(up), ld, _ptr(q), _ptr(sf),
+          SF_LAYOUT[sf_layout], _stream(x))
+    return q, sf
+
+
+def glu_quant_mxfp8_f32(x, *, rowwise=True, colwise=False, out=None):
+    """The MXFP8 quantizer alone on an FP32 [M, N] matrix."""
+    M, N, ld = _rowmajor(x, "x", torch.float32)
+    f = _flags(rowwise, colwise)
+    q_row, q_col, s_row, s_col = _mx_buffers(M, N, rowwise, colwise, x.device, out)
+    _call("glu_quant_mxfp8_f32", M, N, _ptr(x), ld, f, _ptr(q_row), _ptr(s_row), _ptr(q_col),
+          _ptr(s_col), _stream(x))
+    return q_row, q_col, s_row, s_col
+
+
+def glu_quant_nvfp4_f32(x, *, sf_layout="rowmajor", out=None):
+    """The NVFP4 quantizer alone on an FP32 [M, H] matrix."""
+    M, H, ld = _rowmajor(x, "x", torch.float32)
+    q, sf = _nv_buffers(M, H, sf_layout, x.device, out)
+    _call("glu_quant_nvfp4_f32", M, H, _ptr(x), ld, _ptr(q), _ptr(sf), SF_LAYOUT[sf_layout], _stream(x))
+    return q, sf

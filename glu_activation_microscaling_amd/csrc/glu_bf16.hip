@@ -1,0 +1,215 @@
+// GLU forward / backward with BF16 outputs ("perf: tile wide GeGLU rows on SM103",
+// Summary and Testing Done: forward, da and db; "Add swiglu + MXFP8 fused CuTe DSL
+// kernel", API: [gate | up] input and [dGate | dUp] output).
+//
+// A purely element-wise, HBM-bound pass: each thread moves 16-byte vectors of 8 elements
+// (gate, up and dh loads, h or da/db stores), computes in FP32 and rounds once to BF16.
+// Contiguous operands are processed as a single flat row, so any width (8193 included)
+// runs the vector path everywhere except for the last < 8 elements.
+#include "glu_device.h"
+#include "glu_launch.h"
+
+namespace glu {
+namespace {
+
+constexpr int BF_THREADS = 256;
+constexpr int BF_VEC = 2;                                          // vectors per thread
+constexpr int64_t BF_CHUNK = (int64_t)BF_THREADS * BF_VEC * 8;     // elements per tile
+
+struct Uint4 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Uint4 ld16(const uint16_t* p) {
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  return Uint4{{v.x, v.y, v.z, v.w}};
+}
+__device__ __forceinline__ void st16(uint16_t* p, uint32_t a, uint32_t b, uint32_t c,
+                                     uint32_t d) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(a, b, c, d);
+}
+__device__ __forceinline__ float ld_bf(const uint16_t* p) {
+  return __uint_as_float((uint32_t)*p << 16);
+}
+
+// Eight (gate, up) pairs starting at output column j of a row; `in` points at the row.
+template <int LAYOUT>
+__device__ __forceinline__ void load8(const uint16_t* gate_row, const uint16_t* up_row,
+                                      int64_t j, float g[8], float u[8]) {
+  if constexpr (LAYOUT == SPLIT) {
+    Uint4 G = ld16(gate_row + j), U = ld16(up_row + j);
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      g[2 * k] = bf_lo(G.w[k]);
+      g[2 * k + 1] = bf_hi(G.w[k]);
+      u[2 * k] = bf_lo(U.w[k]);
+      u[2 * k + 1] = bf_hi(U.w[k]);
+    }
+  } else {
+    Uint4 A = ld16(gate_row + 2 * j), B = ld16(gate_row + 2 * j + 8);
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      g[k] = bf_lo(A.w[k]);
+      u[k] = bf_hi(A.w[k]);
+      g[4 + k] = bf_lo(B.w[k]);
+      u[4 + k] = bf_hi(B.w[k]);
+    }
+  }
+}
+
+template <int LAYOUT>
+__device__ __forceinline__ void load1(const uint16_t* gate_row, const uint16_t* up_row,
+                                      int64_t j, float& g, float& u) {
+  if constexpr (LAYOUT == SPLIT) {
+    g = ld_bf(gate_row + j);
+    u = ld_bf(up_row + j);
+  } else {
+    g = ld_bf(gate_row + 2 * j);
+    u = ld_bf(gate_row + 2 * j + 1);
+  }
+}
+
+template <int ACT, int LAYOUT>
+__global__ __launch_bounds__(BF_THREADS) void k_glu_fwd_bf16(BF16Args a, int64_t cols,
+                                                             int64_t tiles_per_row,
+                                                             int64_t ntiles) {
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t row = t / tiles_per_row;
+    const int64_t j0 = (t - row * tiles_per_row) * BF_CHUNK;
+    const uint16_t* grow = a.gate + row * a.ld_in;
+    const uint16_t* urow = (LAYOUT == SPLIT) ? a.up + row * a.ld_in : nullptr;
+    uint16_t* hrow = a.out0 + row * a.ld_out;
+
+    float g[BF_VEC][8], u[BF_VEC][8];
+#pragma unroll
+    for (int v = 0; v < BF_VEC; v++) {
+      const int64_t j = j0 + ((int64_t)v * BF_THREADS + threadIdx.x) * 8;
+      if (j + 8 <= cols) load8<LAYOUT>(grow, urow, j, g[v], u[v]);
+    }
+#pragma unroll
+    for (int v = 0; v < BF_VEC; v++) {
+      const int64_t j = j0 + ((int64_t)v * BF_THREADS + threadIdx.x) * 8;
+      if (j + 8 <= cols) {
+        float h[8], zmin = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; k++) h[k] = glu_fwd_elem<ACT>(g[v][k], u[v][k], zmin);
+        if (zmin < TAIL_ZL2) {
+#pragma unroll
+          for (int k = 0; k < 8; k++)
+            if (zl2<ACT>(g[v][k]) < TAIL_ZL2) h[k] = glu_fwd_tail<ACT>(g[v][k], u[v][k]);
+        }
+        st16(hrow + j, bf16_rne(h[0]) | (bf16_rne(h[1]) << 16),
+             bf16_rne(h[2]) | (bf16_rne(h[3]) << 16), bf16_rne(h[4]) | (bf16_rne(h[5]) << 16),
+             bf16_rne(h[6]) | (bf16_rne(h[7]) << 16));
+      } else if (j < cols) {
+        for (int64_t jj = j; jj < cols; jj++) {
+          float gg, uu, zmin = 0.0f;
+          load1<LAYOUT>(grow, urow, jj, gg, uu);
+          float h = glu_fwd_elem<ACT>(gg, uu, zmin);
+          if (zmin < TAIL_ZL2) h = glu_fwd_tail<ACT>(gg, uu);
+          hrow[jj] = (uint16_t)bf16_rne(h);
+        }
+      }
+    }
+  }
+}
+
+template <int ACT, int LAYOUT>
+__global__ __launch_bounds__(BF_THREADS) void k_glu_bwd_bf16(BF16Args a, int64_t cols,
+                                                             int64_t tiles_per_row,
+                                                             int64_t ntiles) {
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t row = t / tiles_per_row;
+    const int64_t j0 = (t - row * tiles_per_row) * BF_CHUNK;
+    const uint16_t* grow = a.gate + row * a.ld_in;
+    const uint16_t* urow = (LAYOUT == SPLIT) ? a.up + row * a.ld_in : nullptr;
+    const uint16_t* drow = a.dh + row * a.ld_dh;
+    uint16_t* arow = a.out0 + row * a.ld_out;
+    uint16_t* brow = (LAYOUT == SPLIT) ? a.out1 + row * a.ld_out : nullptr;
+
+    float g[BF_VEC][8], u[BF_VEC][8], d[BF_VEC][8];
+#pragma unroll
+    for (int v = 0; v < BF_VEC; v++) {
+      const int64_t j = j0 + ((int64_t)v * BF_THREADS + threadIdx.x) * 8;
+      if (j + 8 <= cols) {
+        load8<LAYOUT>(grow, urow, j, g[v], u[v]);
+        Uint4 D = ld16(drow + j);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          d[v][2 * k] = bf_lo(D.w[k]);
+          d[v][2 * k + 1] = bf_hi(D.w[k]);
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < BF_VEC; v++) {
+      const int64_t j = j0 + ((int64_t)v * BF_THREADS + threadIdx.x) * 8;
+      if (j + 8 <= cols) {
+        float da[8], db[8], zmin = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; k++) glu_bwd_elem<ACT>(g[v][k], u[v][k], d[v][k], da[k], db[k], zmin);
+        if (zmin < TAIL_ZL2) {
+#pragma unroll
+          for (int k = 0; k < 8; k++)
+            if (zl2<ACT>(g[v][k]) < TAIL_ZL2) glu_bwd_tail<ACT>(g[v][k], u[v][k], d[v][k], da[k], db[k]);
+        }
+        uint32_t A[8], B[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          A[k] = bf16_rne(da[k]);
+          B[k] = bf16_rne(db[k]);
+        }
+        if constexpr (LAYOUT == SPLIT) {
+          st16(arow + j, A[0] | (A[1] << 16), A[2] | (A[3] << 16), A[4] | (A[5] << 16), A[6] | (A[7] << 16));
+          st16(brow + j, B[0] | (B[1] << 16), B[2] | (B[3] << 16), B[4] | (B[5] << 16), B[6] | (B[7] << 16));
+        } else {
+          st16(arow + 2 * j, A[0] | (B[0] << 16), A[1] | (B[1] << 16), A[2] | (B[2] << 16), A[3] | (B[3] << 16));
+          st16(arow + 2 * j + 8, A[4] | (B[4] << 16), A[5] | (B[5] << 16), A[6] | (B[6] << 16), A[7] | (B[7] << 16));
+        }
+      } else if (j < cols) {
+        for (int64_t jj = j; jj < cols; jj++) {
+          float gg, uu, zmin = 0.0f, da, db;
+          load1<LAYOUT>(grow, urow, jj, gg, uu);
+          float dd = ld_bf(drow + jj);
+          glu_bwd_elem<ACT>(gg, uu, dd, da, db, zmin);
+          if (zmin < TAIL_ZL2) glu_bwd_tail<ACT>(gg, uu, dd, da, db);
+          if constexpr (LAYOUT == SPLIT) {
+            arow[jj] = (uint16_t)bf16_rne(da);
+            brow[jj] = (uint16_t)bf16_rne(db);
+          } else {
+            arow[2 * jj] = (uint16_t)bf16_rne(da);
+            arow[2 * jj + 1] = (uint16_t)bf16_rne(db);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool BWD, int ACT, int LAYOUT>
+hipError_t launch(const BF16Args& a, hipStream_t s) {
+  const int64_t rows = a.flat ? 1 : a.M;
+  const int64_t cols = a.flat ? a.M * a.N : a.N;
+  const int64_t tpr = (cols + BF_CHUNK - 1) / BF_CHUNK;
+  const int64_t ntiles = rows * tpr;
+  const dim3 grid(grid_for(ntiles, (int64_t)1 << 20)), block(BF_THREADS);
+  if constexpr (BWD)
+    return launch_kernel(k_glu_bwd_bf16<ACT, LAYOUT>, grid, block, s, a, cols, tpr, ntiles);
+  else
+    return launch_kernel(k_glu_fwd_bf16<ACT, LAYOUT>, grid, block, s, a, cols, tpr, ntiles);
+}
+
+template <bool BWD>
+hipError_t dispatch(const BF16Args& a, hipStream_t s) {
+  if (a.act == SWIGLU)
+    return a.layout == SPLIT ? launch<BWD, SWIGLU, SPLIT>(a, s) : launch<BWD, SWIGLU, PAIRED>(a, s);
+  return a.layout == SPLIT ? launch<BWD, GEGLU_TANH, SPLIT>(a, s)
+                           : launch<BWD, GEGLU_TANH, PAIRED>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_glu_fwd_bf16(const BF16Args& a, hipStream_t s) { return dispatch<false>(a, s); }
+hipError_t launch_glu_bwd_bf16(const BF16Args& a, hipStream_t s) { return dispatch<true>(a, s); }
+
+}  // namespace glu

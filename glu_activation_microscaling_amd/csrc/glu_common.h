@@ -1,0 +1,12 @@
+// Enumerations shared by the host layer and the kernels; the values are those of the
+// public C ABI (glu_mx.h).
+#pragma once
+
+namespace glu {
+
+enum { SWIGLU = 0, GEGLU_TANH = 1 };
+enum { SPLIT = 0, PAIRED = 1 };
+enum { ROWWISE = 1, COLWISE = 2 };
+enum { SF_ROWMAJOR = 0, SF_128x4 = 1 };
+
+}  // namespace glu

@@ -1,0 +1,251 @@
+// Device helpers for the fused GLU + microscaling kernels (gfx950, wave64).
+//
+// Numerics, following "Add swiglu + MXFP8 fused CuTe DSL kernel" (Summary; Numerics and
+// tests) and "[WS1] Add batch-invariant h_aggregate kernel" (Fixed numerical paths):
+// the activation is evaluated in FP32 and rounded once to BF16 (nearest even); the
+// quantizers then see exactly that BF16 value.  All quantizer decisions below are exact
+// for every finite FP32 input: the MX scale is a power of two (the scaled value is
+// exact), and the NVFP4 decisions compare against exactly representable thresholds.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "glu_common.h"
+
+#if defined(__FAST_MATH__)
+#error "build without fast-math: the quantizer decisions rely on IEEE FP32 arithmetic"
+#endif
+
+namespace glu {
+
+// ---------------------------------------------------------------------------------
+// BF16 <-> FP32
+// ---------------------------------------------------------------------------------
+
+// The two BF16 halves of a 32-bit word, widened exactly.
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// FP32 -> BF16 bits, round to nearest even; FP32 subnormals round like any other value;
+// NaN becomes a quiet NaN with its sign.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? (((u >> 16) & 0x8000u) | 0x7fc0u) : r;
+}
+
+// Rounds to BF16 and returns the rounded value as FP32 (what the quantizer consumes).
+__device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(bf16_rne(f) << 16); }
+
+// ---------------------------------------------------------------------------------
+// Activations.  act(x) = x * sigma(z(x)) with z = x (SiLU) or z = 2 k0 (x + k1 x^3)
+// (tanh-GELU: x/2 (1 + tanh(u)) = x sigma(2u)).  act'(x) = sigma(z) (1 + x sigma(-z) z'(x)).
+// The fast path uses the hardware exp2 and reciprocal and is accurate while
+// z * log2(e) >= TAIL_ZL2; below that e^z leaves the FP32 normal range and the caller
+// recomputes the element in FP64 (act_tail_f64), which is rare and wave-divergent.
+// ---------------------------------------------------------------------------------
+
+constexpr float LOG2E = 1.44269504088896340736f;
+constexpr double GELU_K0 = 0.79788456080286535588;  // sqrt(2/pi)
+constexpr double GELU_K1 = 0.044715;
+constexpr float GEGLU_C0 = (float)(2.0 * GELU_K0 * 1.44269504088896340736);            // 2 k0 log2 e
+constexpr float GEGLU_C1 = (float)(2.0 * GELU_K0 * GELU_K1 * 1.44269504088896340736);  // 2 k0 k1 log2 e
+constexpr float GEGLU_D0 = (float)(2.0 * GELU_K0);                                     // z'(x) = D0 + D1 x^2
+constexpr float GEGLU_D1 = (float)(6.0 * GELU_K0 * GELU_K1);
+constexpr float TAIL_ZL2 = -125.0f;
+
+// z(x) * log2(e)
+template <int ACT>
+__device__ __forceinline__ float zl2(float x) {
+  if constexpr (ACT == SWIGLU) {
+    return x * LOG2E;
+  } else {
+    return x * __builtin_fmaf(x * x, GEGLU_C1, GEGLU_C0);
+  }
+}
+
+// sigma(z) and sigma(-z) from zl = z log2(e), valid for zl >= TAIL_ZL2.
+__device__ __forceinline__ void sigmoid2(float zl, float& s_pos, float& s_neg) {
+  float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(zl));  // e^-|z|, normal here
+  float r = __builtin_amdgcn_rcpf(1.0f + e);               // sigma(|z|)
+  float er = e * r;                                        // sigma(-|z|)
+  bool pos = zl >= 0.0f;
+  s_pos = pos ? r : er;
+  s_neg = pos ? er : r;
+}
+
+// z'(x); x is clamped so that z' stays finite (where it would not, sigma(-z) is 0).
+template <int ACT>
+__device__ __forceinline__ float dz(float x) {
+  if constexpr (ACT == SWIGLU) {
+    return 1.0f;
+  } else {
+    float xc = __builtin_amdgcn_fmed3f(x, -1.0e15f, 1.0e15f);
+    return __builtin_fmaf(xc * xc, GEGLU_D1, GEGLU_D0);
+  }
+}
+
+// Tail path in FP64: act(x) and act'(x) for z(x) far below zero (returned in registers).
+struct ActF64 {
+  double act, grad;
+};
+
+template <int ACT>
+__device__ __noinline__ ActF64 act_tail_f64(double x) {
+  double z = (ACT == SWIGLU) ? x : 2.0 * GELU_K0 * (x + GELU_K1 * x * x * x);
+  double sp = 1.0 / (1.0 + exp(-z));
+  double sn = 1.0 / (1.0 + exp(z));
+  double d = (ACT == SWIGLU) ? 1.0 : 2.0 * GELU_K0 * (1.0 + 3.0 * GELU_K1 * x * x);
+  return ActF64{x * sp, sp * (1.0 + x * sn * d)};
+}
+
+// Forward: act(g) * u in FP32 (the caller rounds it to BF16).
+template <int ACT>
+__device__ __forceinline__ float glu_fwd_elem(float g, float u, float& zmin) {
+  float zl = zl2<ACT>(g);
+  zmin = __builtin_fminf(zmin, zl);
+  float sp, sn;
+  sigmoid2(zl, sp, sn);
+  return (g * sp) * u;
+}
+
+template <int ACT>
+__device__ __forceinline__ float glu_fwd_tail(float g, float u) {
+  return (float)(act_tail_f64<ACT>((double)g).act * (double)u);
+}
+
+// Backward: da = dh u act'(g), db = dh act(g), FP32 before rounding.
+template <int ACT>
+__device__ __forceinline__ void glu_bwd_elem(float g, float u, float d, float& da, float& db,
+                                             float& zmin) {
+  float zl = zl2<ACT>(g);
+  zmin = __builtin_fminf(zmin, zl);
+  float sp, sn;
+  sigmoid2(zl, sp, sn);
+  float grad = sp * __builtin_fmaf(g * sn, dz<ACT>(g), 1.0f);
+  da = (d * u) * grad;
+  db = d * (g * sp);
+}
+
+template <int ACT>
+__device__ __forceinline__ void glu_bwd_tail(float g, float u, float d, float& da, float& db) {
+  const ActF64 r = act_tail_f64<ACT>((double)g);
+  da = (float)((double)d * (double)u * r.grad);
+  db = (float)((double)d * r.act);
+}
+
+// ---------------------------------------------------------------------------------
+// MXFP8: E8M0 RCEIL scale and E4M3 codes
+// ---------------------------------------------------------------------------------
+
+// Scale byte for a finite block whose largest magnitude has FP32 bit pattern amax_bits:
+// e + 127 for the smallest e >= -127 with 448 * 2^e >= amax.  With amax = 1.f * 2^E,
+// 448 = 1.75 * 2^8, so e = E - 135 + (f > 1.75); finite FP32 never reaches e = 127.
+__device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits) {
+  int code = (int)(amax_bits >> 23) - 8 + ((amax_bits & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return code < 0 ? 0u : (uint32_t)code;
+}
+
+// 2^-e as FP32 for scale byte b = e + 127 (b <= 247).
+__device__ __forceinline__ float mx_inv_scale(uint32_t b) {
+  return __uint_as_float((254u - b) << 23);
+}
+
+// E4M3 code of y, nearest even, for |y| <= 448 (larger magnitudes saturate to 0x7E).
+// Normal range: round the FP32 mantissa to 3 bits and rebias (the carry propagates into
+// the exponent).  Below 2^-6 the E4M3 grid is k * 2^-9: y * 512 is exact and rint rounds
+// it to nearest even.
+__device__ __forceinline__ uint32_t e4m3_sw(float y) {
+  uint32_t u = __float_as_uint(y);
+  uint32_t s = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  uint32_t n = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - 0x3c0u;  // (127 - 7) << 3
+  n = n > 0x7eu ? 0x7eu : n;
+  uint32_t d = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  return s | (a >= 0x3c800000u ? n : d);
+}
+
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  return e4m3_sw(a) | (e4m3_sw(b) << 8) | (e4m3_sw(c) << 16) | (e4m3_sw(d) << 24);
+}
+
+// ---------------------------------------------------------------------------------
+// NVFP4: E4M3 scale of amax / 6 and E2M1 codes
+// ---------------------------------------------------------------------------------
+
+// Value of a non-negative finite E4M3 code.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  uint32_t E = c >> 3, m = c & 7u;
+  return E ? __uint_as_float(((E + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+
+// Nearest E4M3 code to amax / 6 (ties to even, saturating at 448), decided exactly: the
+// candidate from amax * (1/6) is within one code of the answer, and 6 * midpoint is
+// exact in FP32, so comparing amax with it settles the rounding without a division.
+__device__ __forceinline__ uint32_t nv_scale_code(float amax) {
+  uint32_t c = e4m3_sw(amax * (1.0f / 6.0f));
+  if (c < 0x7eu) {
+    float up = 6.0f * (0.5f * (e4m3_value(c) + e4m3_value(c + 1)));
+    if (amax > up || (amax == up && ((c + 1) & 1u) == 0)) return c + 1;
+  }
+  if (c > 0u) {
+    float dn = 6.0f * (0.5f * (e4m3_value(c - 1) + e4m3_value(c)));
+    if (amax < dn || (amax == dn && ((c - 1) & 1u) == 0)) return c - 1;
+  }
+  return c;
+}
+
+// E2M1 decision thresholds at scale S: S * {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5}, each exact
+// in FP32.  S == 0 maps every magnitude to code 0 (thresholds at +Inf).
+struct E2m1Thresholds {
+  float t[7];
+};
+
+__device__ __forceinline__ E2m1Thresholds e2m1_thresholds(float S) {
+  const float k[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  E2m1Thresholds r;
+#pragma unroll
+  for (int i = 0; i < 7; i++) r.t[i] = S > 0.0f ? S * k[i] : __builtin_inff();
+  return r;
+}
+
+// E2M1 code nibble of x / S: three exact comparisons pick the code bit by bit.  Ties go
+// to the even code: 0.75, 1.75 and 3.5 round up (>=), 0.25, 1.25, 2.5 and 5 round down (>).
+__device__ __forceinline__ uint32_t e2m1_code(float x, const E2m1Thresholds& T) {
+  float a = __builtin_fabsf(x);
+  bool b2 = a >= T.t[3];
+  bool b1 = a >= (b2 ? T.t[5] : T.t[1]);
+  float t0 = b2 ? (b1 ? T.t[6] : T.t[4]) : (b1 ? T.t[2] : T.t[0]);
+  bool b0 = a > t0;
+  uint32_t s = (__float_as_uint(x) >> 28) & 8u;
+  return s | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+}
+
+// Byte offset of NVFP4 scale (r, c) in the 128x4 layout; cp = padded scale columns.
+__device__ __forceinline__ int64_t sf128x4_offset(int64_t r, int64_t c, int64_t cp) {
+  return ((r >> 7) * (cp >> 2) + (c >> 2)) * 512 + (r & 31) * 16 + ((r & 127) >> 5) * 4 +
+         (c & 3);
+}
+
+// ---------------------------------------------------------------------------------
+// Wave-level exchanges (wave64).  DPP permutes stay inside a 16-lane row; the xor-16
+// step uses ds_swizzle (within 32 lanes).
+// ---------------------------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+constexpr int DPP_XOR1 = 0xb1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4e;         // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_ROR8 = 0x128;    // rotate by 8 inside a row of 16: lane ^ 8
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7 - i inside each group of 8
+
+__device__ __forceinline__ uint32_t swz_xor16(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401f);  // and 0x1f, xor 0x10
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+}  // namespace glu

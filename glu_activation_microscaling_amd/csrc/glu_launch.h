@@ -1,0 +1,82 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernel translation units.
+// Arguments arrive here already validated; launchers only pick a template instance and
+// a grid, and return the HIP launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+
+#include "glu_common.h"
+
+namespace glu {
+
+struct BF16Args {
+  int act, layout;
+  int64_t M, N;
+  const uint16_t* gate;
+  const uint16_t* up;
+  int64_t ld_in;
+  const uint16_t* dh;  // backward only
+  int64_t ld_dh;
+  uint16_t* out0;      // h (forward) or da (backward)
+  uint16_t* out1;      // db (backward, split layout)
+  int64_t ld_out;
+  bool flat;           // operands contiguous: treat as one row of M*N elements
+};
+
+struct MxArgs {
+  int act, layout, flags;
+  int64_t M, N;              // per-half shape; the quantized matrix is [M, N] (fwd) or [M, 2N] (bwd)
+  const void* src;           // gate (BF16) or x (FP32, quantizer hook)
+  const uint16_t* up;
+  int64_t ld_in;
+  const uint16_t* dh;
+  int64_t ld_dh;
+  uint8_t* q_row;
+  uint8_t* s_row;
+  uint8_t* q_col;
+  uint8_t* s_col;
+};
+
+struct NvArgs {
+  int act, layout, sf_layout;
+  int64_t M, H;
+  const void* src;           // gate (BF16) or x (FP32, quantizer hook)
+  const uint16_t* up;
+  int64_t ld_in;
+  uint8_t* q;
+  uint8_t* sf;
+};
+
+hipError_t launch_glu_fwd_bf16(const BF16Args& a, hipStream_t s);
+hipError_t launch_glu_bwd_bf16(const BF16Args& a, hipStream_t s);
+hipError_t launch_glu_fwd_mxfp8(const MxArgs& a, hipStream_t s);
+hipError_t launch_glu_bwd_mxfp8(const MxArgs& a, hipStream_t s);
+hipError_t launch_quant_mxfp8_f32(const MxArgs& a, hipStream_t s);
+hipError_t launch_glu_fwd_nvfp4(const NvArgs& a, hipStream_t s);
+hipError_t launch_quant_nvfp4_f32(const NvArgs& a, hipStream_t s);
+
+// Launches kernel k and returns the launch status of this call alone (the HIP error
+// state left by earlier, unrelated calls is not consulted).
+template <typename... KArgs, typename... Ts>
+hipError_t launch_kernel(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+                         Ts&&... ts) {
+  std::tuple<KArgs...> args(static_cast<KArgs>(ts)...);
+  return std::apply(
+      [&](auto&... xs) {
+        void* argv[] = {(void*)&xs...};
+        return hipLaunchKernel((const void*)k, grid, block, argv, 0, s);
+      },
+      args);
+}
+
+// Workgroups of a grid-stride launch over `units` work items: enough waves to fill the
+// chip several times over, never more than the work.
+inline unsigned grid_for(int64_t units, int64_t cap) {
+  if (units < 1) return 1;
+  return (unsigned)(units < cap ? units : cap);
+}
+
+}  // namespace glu

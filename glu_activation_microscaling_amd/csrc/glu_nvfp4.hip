@@ -1,0 +1,148 @@
+// Fused GLU + NVFP4 quantization with global scale 1 ("feat(phyai-kernel): add Thor NVFP4
+// GeGLU kernel for pi0.5", Summary: GeGLU fold and compact NVFP4 store; Supported contract:
+// E2M1 values, E4M3 scales in the 128x4 layout, pairwise-interleaved gate/up columns), and
+// the FP32 quantizer hook running the same quantize-and-store stage.
+//
+// Work decomposition (wave64): a workgroup of 4 waves covers 2048 consecutive outputs of one
+// row; each lane computes 8 consecutive outputs (one 32-byte load of interleaved gate/up
+// pairs, or 16 bytes each of gate and up).  A 16-element block is a lane pair, so the block
+// amax is one DPP quad_perm exchange.  Each lane stores its 8 E2M1 codes as one 4-byte word
+// (a wave writes 256 contiguous bytes); the even lane of a pair stores the scale byte.
+// With the 128x4 layout the grid also covers the padding rows up to a multiple of 128, and
+// the lane holding the last block of a row zero-fills the padding scale columns.
+#include "glu_device.h"
+#include "glu_launch.h"
+
+namespace glu {
+namespace {
+
+constexpr int NV_THREADS = 256;
+constexpr int64_t NV_TILE = 2048;  // outputs per workgroup
+
+struct Words4 {
+  uint32_t w[4];
+};
+__device__ __forceinline__ Words4 ld16(const void* p) {
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  return Words4{{v.x, v.y, v.z, v.w}};
+}
+
+template <int ACT, int LAYOUT, int SFL, bool F32>
+__global__ __launch_bounds__(NV_THREADS) void k_nvfp4(NvArgs a, int64_t tiles_per_row,
+                                                      int64_t ntiles, int64_t scale_cols,
+                                                      int64_t scale_cols_padded) {
+  const int lane = threadIdx.x & 63;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t row = t / tiles_per_row;
+    const int64_t j = (t - row * tiles_per_row) * NV_TILE + (int64_t)threadIdx.x * 8;
+    const bool in_row = j < a.H;      // pairs of lanes agree (H % 16 == 0)
+    const bool live = in_row && row < a.M;
+
+    float v[8];
+    if (live) {
+      if constexpr (F32) {
+        const float* p = static_cast<const float*>(a.src) + row * a.ld_in + j;
+        Words4 A = ld16(p), B = ld16(p + 4);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          v[k] = __uint_as_float(A.w[k]);
+          v[4 + k] = __uint_as_float(B.w[k]);
+        }
+      } else {
+        const uint16_t* gate = static_cast<const uint16_t*>(a.src);
+        float g[8], u[8];
+        if constexpr (LAYOUT == PAIRED) {
+          const uint16_t* p = gate + row * a.ld_in + 2 * j;
+          Words4 A = ld16(p), B = ld16(p + 8);
+#pragma unroll
+          for (int k = 0; k < 4; k++) {
+            g[k] = bf_lo(A.w[k]);
+            u[k] = bf_hi(A.w[k]);
+            g[4 + k] = bf_lo(B.w[k]);
+            u[4 + k] = bf_hi(B.w[k]);
+          }
+        } else {
+          Words4 G = ld16(gate + row * a.ld_in + j), U = ld16(a.up + row * a.ld_in + j);
+#pragma unroll
+          for (int k = 0; k < 4; k++) {
+            g[2 * k] = bf_lo(G.w[k]);
+            g[2 * k + 1] = bf_hi(G.w[k]);
+            u[2 * k] = bf_lo(U.w[k]);
+            u[2 * k + 1] = bf_hi(U.w[k]);
+          }
+        }
+        float zmin = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; k++) v[k] = glu_fwd_elem<ACT>(g[k], u[k], zmin);
+        if (zmin < TAIL_ZL2) {
+#pragma unroll
+          for (int k = 0; k < 8; k++)
+            if (zl2<ACT>(g[k]) < TAIL_ZL2) v[k] = glu_fwd_tail<ACT>(g[k], u[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++) v[k] = round_bf16(v[k]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; k++) v[k] = 0.0f;
+    }
+
+    // block amax over the lane pair (all lanes take part in the exchange)
+    uint32_t m = __float_as_uint(v[0]) & 0x7fffffffu;
+#pragma unroll
+    for (int k = 1; k < 8; k++) m = umax(m, __float_as_uint(v[k]) & 0x7fffffffu);
+    m = umax(m, dpp<DPP_XOR1>(m));
+
+    const bool nonfinite = m >= 0x7f800000u;
+    const uint32_t sc = nonfinite ? 0x7fu : nv_scale_code(__uint_as_float(m));
+    const E2m1Thresholds T = e2m1_thresholds(e4m3_value(nonfinite ? 0u : sc));
+
+    if (live) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int k = 0; k < 8; k++) word |= e2m1_code(v[k], T) << (4 * k);
+      if (nonfinite) word = 0;
+      *reinterpret_cast<uint32_t*>(a.q + row * (a.H / 2) + j / 2) = word;
+    }
+    if (in_row && (lane & 1) == 0) {
+      const int64_t blk = j / 16;
+      const uint8_t byte = row < a.M ? (uint8_t)sc : (uint8_t)0;  // padding rows hold 0
+      if constexpr (SFL == SF_ROWMAJOR) {
+        a.sf[row * scale_cols + blk] = byte;
+      } else {
+        a.sf[sf128x4_offset(row, blk, scale_cols_padded)] = byte;
+        if (blk == scale_cols - 1)
+          for (int64_t c = scale_cols; c < scale_cols_padded; c++)
+            a.sf[sf128x4_offset(row, c, scale_cols_padded)] = 0;
+      }
+    }
+  }
+}
+
+template <int ACT, int LAYOUT, bool F32>
+hipError_t launch(const NvArgs& a, hipStream_t s) {
+  const int64_t nb = a.H / 16;
+  const int64_t cp = (nb + 3) / 4 * 4;
+  const int64_t rows = a.sf_layout == SF_128x4 ? (a.M + 127) / 128 * 128 : a.M;
+  const int64_t tpr = (a.H + NV_TILE - 1) / NV_TILE;
+  const int64_t ntiles = rows * tpr;
+  const dim3 grid(grid_for(ntiles, (int64_t)1 << 20)), block(NV_THREADS);
+  if (a.sf_layout == SF_128x4)
+    return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_128x4, F32>, grid, block, s, a, tpr, ntiles, nb, cp);
+  return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_ROWMAJOR, F32>, grid, block, s, a, tpr, ntiles, nb, cp);
+}
+
+}  // namespace
+
+hipError_t launch_glu_fwd_nvfp4(const NvArgs& a, hipStream_t s) {
+  if (a.act == SWIGLU)
+    return a.layout == PAIRED ? launch<SWIGLU, PAIRED, false>(a, s) : launch<SWIGLU, SPLIT, false>(a, s);
+  return a.layout == PAIRED ? launch<GEGLU_TANH, PAIRED, false>(a, s)
+                            : launch<GEGLU_TANH, SPLIT, false>(a, s);
+}
+
+hipError_t launch_quant_nvfp4_f32(const NvArgs& a, hipStream_t s) {
+  return launch<SWIGLU, SPLIT, true>(a, s);
+}
+
+}  // namespace glu

@@ -1,0 +1,201 @@
+/*
+ * glu_mx.h - C ABI of the MI355X (gfx950) fused gated-linear-unit library.
+ *
+ * The library computes a gated linear unit h = act(gate) * up, forward and backward, in
+ * FP32 with one BF16 rounding at the store, and can emit the result directly as
+ * block-scaled ("microscaling") data in one pass over the inputs:
+ *   - MXFP8: E4M3 codes with one E8M0 scale per 32 elements, the scale rounded up
+ *     (RCEIL) from the block maximum; rowwise 1x32 blocks, colwise 32x1 blocks, or both.
+ *   - NVFP4: E2M1 codes packed two per byte with one E4M3 scale per 16 elements and a
+ *     global scale of 1.
+ * Activations: SwiGLU, act = silu(x) = x * sigmoid(x); GeGLU, act = gelu_tanh(x) =
+ * x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3))).
+ *
+ * Sources, cited by page title and section:
+ *   [MX] "Add swiglu + MXFP8 fused CuTe DSL kernel": Summary (swiglu fused with the
+ *        RCEIL MXFP8 cast, gate/up read once, rowwise/colwise/both from one pass), API
+ *        (gated_input packs [gate | up]; backward returns [dGate | dUp]; a disabled
+ *        direction comes back zero-sized), Numerics and tests (the fused result equals
+ *        the activation followed by the standalone quantizers; launcher guards for the
+ *        32-bit bound, pointer alignment and geometry).
+ *   [NV] "feat(phyai-kernel): add Thor NVFP4 GeGLU kernel for pi0.5": Summary (GeGLU fold
+ *        and compact NVFP4 store), Supported contract (E2M1 values, E4M3 scales in the
+ *        CUTLASS/FlashInfer 128x4 layout, global scale 1, pairwise-interleaved gate/up,
+ *        caller-supplied output buffers, unsupported inputs fail before launch).
+ *   [GE] "perf: tile wide GeGLU rows on SM103": Summary and Testing Done (GeGLU forward,
+ *        da and db; ragged widths such as 8193 columns).
+ *   [H]  "[WS1] Add batch-invariant h_aggregate kernel": Fixed numerical paths (one
+ *        FP32-to-BF16 conversion at the final store) and Supported profile and
+ *        fail-closed behavior (no silent copies, unsupported layouts raise).
+ *
+ * Conventions shared by every entry point:
+ *   - BF16 values are passed as uint16_t bit patterns.  Every data pointer is a device
+ *     pointer; the library never dereferences one on the host.
+ *   - Extents and row strides ("ld", in elements) are int64_t.  Matrices are row-major.
+ *   - Caller-owned buffers: the library never allocates, frees or synchronizes, and keeps
+ *     no mutable global state, so calls are thread-safe and can be captured in a HIP
+ *     graph.  `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *   - Fail closed: every argument is validated on the host before any HIP call.  On any
+ *     status other than GLU_OK nothing was launched and nothing was written.  A kernel
+ *     fault surfaces at the caller's next synchronization, not here.
+ *   - M == 0 or N == 0 is a valid no-op (pointers are then not inspected).
+ *   - Every base pointer must be 16-byte aligned (GLU_ERR_ALIGN).
+ *   - Outputs may not overlap inputs or each other (GLU_ERR_OVERLAP), judged on the byte
+ *     range each operand spans; the one exception is the in-place backward of glu_bwd.
+ *   - Results are deterministic and batch invariant: every output byte depends only on
+ *     its own element (BF16 entries) or its own 32- or 16-element block.
+ */
+#ifndef GLU_MX_H
+#define GLU_MX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum glu_status {
+  GLU_OK = 0,
+  GLU_ERR_NULL = 1,        /* a required pointer is NULL */
+  GLU_ERR_SHAPE = 2,       /* negative extent, block divisibility violated, extent overflow */
+  GLU_ERR_ALIGN = 3,       /* a base pointer is not 16-byte aligned */
+  GLU_ERR_STRIDE = 4,      /* a row stride is too small or not a multiple of 8 elements */
+  GLU_ERR_ARG = 5,         /* unknown enum/flag, or a pointer given for a disabled output */
+  GLU_ERR_OVERLAP = 6,     /* an output overlaps an input or another output */
+  GLU_ERR_UNSUPPORTED = 7, /* a well-formed combination this library does not implement */
+  GLU_ERR_HIP = 8          /* the HIP runtime refused the launch */
+} glu_status;
+
+/* Activation. */
+enum { GLU_SWIGLU = 0, GLU_GEGLU_TANH = 1 };
+
+/* Operand layout.
+ *   GLU_SPLIT : gate and up are two [M, N] matrices sharing the row stride ld_in.  The
+ *               concatenated [gate | up] matrix of [MX] API is GLU_SPLIT with
+ *               up = gate + N and ld_in = 2N.
+ *   GLU_PAIRED: one [M, 2N] matrix passed as `gate` (`up` must be NULL) whose column 2j is
+ *               gate_j and column 2j+1 is up_j ([NV] Supported contract, weight layout). */
+enum { GLU_SPLIT = 0, GLU_PAIRED = 1 };
+
+/* MXFP8 direction flags; both = GLU_ROWWISE | GLU_COLWISE. */
+enum { GLU_ROWWISE = 1, GLU_COLWISE = 2 };
+
+/* NVFP4 scale-factor layout.
+ *   GLU_SF_ROWMAJOR: [M, H/16] bytes.
+ *   GLU_SF_128x4   : the 128x4 tiled layout named in [NV] Supported contract (scales row).
+ *                    Rows are padded to Rp = ceil(M/128)*128 and scale columns to
+ *                    Cp = ceil((H/16)/4)*4; scale (r, c) lives at byte
+ *                    ((r/128)*(Cp/4) + c/4)*512 + (r%32)*16 + ((r%128)/32)*4 + c%4,
+ *                    and the library writes zero to every padding byte.  The buffer must
+ *                    hold Rp*Cp bytes. */
+enum { GLU_SF_ROWMAJOR = 0, GLU_SF_128x4 = 1 };
+
+/* ---- GLU forward, BF16 output ([MX] Summary; [GE] Summary; [H] Fixed numerical paths)
+ * h[m, j] = bf16(act(g) * up_j), g = gate_j, computed in FP32 and rounded once to nearest
+ * even.  h is [M, N] with row stride ld_h.
+ * Strides: when the operands are contiguous (GLU_SPLIT with ld_in == N, or GLU_PAIRED with
+ * ld_in == 2N, and ld_h == N) any N is accepted (ragged widths such as 8193, [GE] Testing
+ * Done).  Otherwise ld_in and ld_h must be multiples of 8 (GLU_ERR_STRIDE).
+ * ld_in >= N (split) or >= 2N (paired), ld_h >= N. */
+glu_status glu_fwd(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                   const uint16_t* up, int64_t ld_in, uint16_t* h, int64_t ld_h,
+                   void* stream);
+
+/* ---- GLU backward, BF16 output ([GE] Testing Done: forward, da and db; [MX] API)
+ * da = bf16(dh * up * act'(gate)), db = bf16(dh * act(gate)); dh is [M, N] with stride
+ * ld_dh.  GLU_SPLIT: da and db are two [M, N] matrices with row stride ld_out (for the
+ * concatenated [dGate | dUp] result pass db = da + N, ld_out = 2N).  GLU_PAIRED: da is one
+ * interleaved [M, 2N] matrix (column 2j = dGate_j, 2j+1 = dUp_j), db must be NULL.
+ * In place: da == gate and db == up (split) or da == gate (paired) with ld_out == ld_in is
+ * allowed; each element is read before it is overwritten by the same thread.
+ * Strides as for glu_fwd, with ld_dh and ld_out in place of ld_h. */
+glu_status glu_bwd(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                   const uint16_t* up, int64_t ld_in, const uint16_t* dh, int64_t ld_dh,
+                   uint16_t* da, uint16_t* db, int64_t ld_out, void* stream);
+
+/* ---- Fused forward + MXFP8 ([MX] Summary, API, Numerics and tests)
+ * Quantizes h = bf16(act(gate) * up) without writing h.  Per 32-element block: amax =
+ * max|h|; scale byte e + 127 for the smallest e in [-127, 127] with 448 * 2^e >= amax
+ * (RCEIL); codes = E4M3(h * 2^-e), nearest even.  A block holding NaN or Inf gets scale
+ * 0xFF and codes 0x7F.
+ *   rowwise (flags & GLU_ROWWISE): q_row [M, N] codes, s_row [M, N/32] scales.
+ *   colwise (flags & GLU_COLWISE): q_col [N, M] codes (row j holds column j of h, i.e.
+ *                                  the column-major [M, N]), s_col [N, M/32] scales.
+ * A disabled direction's two pointers must be NULL.  Needs N % 32 == 0, M % 32 == 0 when
+ * colwise, ld_in % 8 == 0.  Output buffers are contiguous. */
+glu_status glu_fwd_mxfp8(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                         const uint16_t* up, int64_t ld_in, int flags, uint8_t* q_row,
+                         uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, void* stream);
+
+/* ---- Fused backward + MXFP8 ([MX] API: backward returns [dGate | dUp] quantized)
+ * The quantized matrix is X = [da | db], [M, 2N] (X[:, j] = da_j, X[:, N + j] = db_j), with
+ * da, db as in glu_bwd and never written.  q_row [M, 2N], s_row [M, 2N/32], q_col [2N, M],
+ * s_col [2N, M/32].  Only GLU_SPLIT is implemented (GLU_PAIRED -> GLU_ERR_UNSUPPORTED).
+ * Needs N % 32 == 0, M % 32 == 0 when colwise, ld_in % 8 == 0, ld_dh % 8 == 0. */
+glu_status glu_bwd_mxfp8(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                         const uint16_t* up, int64_t ld_in, const uint16_t* dh,
+                         int64_t ld_dh, int flags, uint8_t* q_row, uint8_t* s_row,
+                         uint8_t* q_col, uint8_t* s_col, void* stream);
+
+/* ---- Fused forward + NVFP4, global scale 1 ([NV] Summary, Supported contract)
+ * h = bf16(act(gate) * up) is [M, H] and never written.  Per 16-element block of a row:
+ * scale S = E4M3(amax / 6), nearest even; codes E2M1(h / S), nearest even, saturating at
+ * +-6; S == 0 gives signed-zero codes.  A block holding NaN or Inf gets scale 0x7F and
+ * zero codes.  q is [M, H/2] bytes with element 2k in the low nibble of byte k; sf is
+ * GLU_SF_ROWMAJOR [M, H/16] or GLU_SF_128x4 (see above).
+ * Needs H % 16 == 0 and ld_in % 8 == 0. */
+glu_status glu_fwd_nvfp4(int act, int layout, int64_t M, int64_t H, const uint16_t* gate,
+                         const uint16_t* up, int64_t ld_in, uint8_t* q, uint8_t* sf,
+                         int sf_layout, void* stream);
+
+/* ---- Quantizer test hooks: the same device quantizer code, fed FP32 values
+ * x is an FP32 [M, N] matrix with row stride ld_x (a multiple of 4).  Outputs and rules
+ * exactly as glu_fwd_mxfp8 / glu_fwd_nvfp4 with x in place of h; every FP32 input is
+ * quantized exactly (no intermediate rounding). */
+glu_status glu_quant_mxfp8_f32(int64_t M, int64_t N, const float* x, int64_t ld_x, int flags,
+                               uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                               uint8_t* s_col, void* stream);
+glu_status glu_quant_nvfp4_f32(int64_t M, int64_t H, const float* x, int64_t ld_x,
+                               uint8_t* q, uint8_t* sf, int sf_layout, void* stream);
+
+/* ---- Host-only validation: the exact checks the entry point of the same name runs
+ * before launching, with the same arguments minus the stream.  Never calls HIP and never
+ * dereferences a pointer, so it runs on machines without a GPU. */
+glu_status glu_check_fwd(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                         const uint16_t* up, int64_t ld_in, uint16_t* h, int64_t ld_h);
+glu_status glu_check_bwd(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                         const uint16_t* up, int64_t ld_in, const uint16_t* dh,
+                         int64_t ld_dh, uint16_t* da, uint16_t* db, int64_t ld_out);
+glu_status glu_check_fwd_mxfp8(int act, int layout, int64_t M, int64_t N,
+                               const uint16_t* gate, const uint16_t* up, int64_t ld_in,
+                               int flags, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                               uint8_t* s_col);
+glu_status glu_check_bwd_mxfp8(int act, int layout, int64_t M, int64_t N,
+                               const uint16_t* gate, const uint16_t* up, int64_t ld_in,
+                               const uint16_t* dh, int64_t ld_dh, int flags,
+                               uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                               uint8_t* s_col);
+glu_status glu_check_fwd_nvfp4(int act, int layout, int64_t M, int64_t H,
+                               const uint16_t* gate, const uint16_t* up, int64_t ld_in,
+                               uint8_t* q, uint8_t* sf, int sf_layout);
+glu_status glu_check_quant_mxfp8_f32(int64_t M, int64_t N, const float* x, int64_t ld_x,
+                                     int flags, uint8_t* q_row, uint8_t* s_row,
+                                     uint8_t* q_col, uint8_t* s_col);
+glu_status glu_check_quant_nvfp4_f32(int64_t M, int64_t H, const float* x, int64_t ld_x,
+                                     uint8_t* q, uint8_t* sf, int sf_layout);
+
+/* Bytes of the scale buffer glu_fwd_nvfp4 / glu_quant_nvfp4_f32 write for this layout
+ * (M*H/16 row-major, Rp*Cp for 128x4), or -1 for bad arguments. */
+int64_t glu_nvfp4_sf_bytes(int64_t M, int64_t H, int sf_layout);
+
+/* Static text for a status code (never NULL). */
+const char* glu_status_string(glu_status status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int glu_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLU_MX_H */

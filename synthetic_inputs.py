@@ -76,3 +76,19 @@ WORKLOADS = {
     "geglu_nvfp4_rows": (784, 816, 880, 968),
     "geglu_nvfp4_hidden": 16384,
 }
+
+
+def normal_bf16_device(shapes, seed=0, device="cuda", outliers=False):
+    """Like normal_bf16 but drawn on the device with a seeded device generator (for the
+    full-size workloads, where drawing gigabytes on the host would dominate).  The bits
+    differ from the host draw of the same seed but are reproducible on any MI355X."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    out = []
+    for s in shapes:
+        t = torch.randn(s, generator=g, device=device, dtype=torch.float32)
+        if outliers:
+            mask = torch.rand(s, generator=g, device=device) < OUTLIER_FRACTION
+            t = torch.where(mask, t * OUTLIER_FACTOR, t)
+        out.append(t.to(torch.bfloat16))
+        del t
+    return out

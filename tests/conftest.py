@@ -24,3 +24,28 @@ def parse_golden(name):
                 continue
             rows.append(line)
     return rows
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    """The built library on a visible GPU; GPU tests skip on machines without one."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import glu_activation_microscaling_amd as glu
+    if not os.path.exists(glu.LIB_PATH):
+        from glu_activation_microscaling_amd import build
+        build.build()
+    glu.lib()
+    return glu
+
+
+def bits(t):
+    """torch bfloat16 tensor (any device) -> numpy uint16 bit patterns."""
+    import numpy as np
+    import torch
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def u8(t):
+    return t.detach().cpu().contiguous().numpy()

@@ -1,0 +1,205 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function include/glu_mx.h declares, and reject every
+unsupported argument before touching the device.  The glu_check_* exports run the exact
+checks of the entry points; here they get fake, never-dereferenced pointers.  The entry
+points themselves are only called with arguments that fail validation (they return before
+any HIP call) or with M == 0 (a no-op).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import glu_activation_microscaling_amd as glu
+from conftest import ROOT
+
+OK, NULL, SHAPE, ALIGN, STRIDE, ARG, OVERLAP, UNSUP, HIP = range(9)
+L = None
+
+
+def setup_module(module):
+    global L
+    if not os.path.exists(glu.LIB_PATH):
+        from glu_activation_microscaling_amd import build
+        build.build()
+    L = glu.lib()
+
+
+def P(addr):
+    return ctypes.c_void_p(addr)
+
+
+A0 = 0x10000000      # fake, 16-byte aligned device addresses far apart
+B0 = 0x20000000
+C0 = 0x30000000
+D0 = 0x40000000
+E0 = 0x50000000
+F0 = 0x60000000
+
+
+def test_every_declared_symbol_is_exported():
+    with open(os.path.join(ROOT, "include", "glu_mx.h")) as f:
+        text = f.read()
+    names = set(re.findall(r"\b(glu_[a-z0-9_]+)\s*\(", text))
+    names -= {"glu_status"}
+    assert len(names) >= 17
+    for n in sorted(names):
+        assert hasattr(L, n), f"missing export {n}"
+
+
+def test_status_strings_and_version():
+    L.glu_status_string.restype = ctypes.c_char_p
+    for s in range(9):
+        assert L.glu_status_string(s)
+    assert L.glu_version() >= 100
+
+
+def fwd(**kw):
+    a = dict(act=0, layout=0, M=64, N=128, gate=A0, up=B0, ld=128, h=C0, ldh=128)
+    a.update(kw)
+    return L.glu_check_fwd(a["act"], a["layout"], a["M"], a["N"], P(a["gate"]), P(a["up"]), a["ld"],
+                           P(a["h"]), a["ldh"])
+
+
+def test_fwd_checks():
+    assert fwd() == OK
+    assert fwd(act=2) == ARG and fwd(layout=5) == ARG
+    assert fwd(M=-1) == SHAPE and fwd(N=-3) == SHAPE
+    assert fwd(M=0, gate=0, up=0, h=0) == OK and fwd(N=0, gate=0) == OK
+    assert fwd(gate=0) == NULL and fwd(up=0) == NULL and fwd(h=0) == NULL
+    assert fwd(layout=1, up=B0, ld=256) == ARG           # paired takes one matrix
+    assert fwd(layout=1, up=0, ld=256) == OK
+    assert fwd(layout=1, up=0, ld=255) == STRIDE          # ld < 2N
+    assert fwd(ld=127) == STRIDE and fwd(ldh=100) == STRIDE
+    assert fwd(N=8193, ld=8193, ldh=8193) == OK           # contiguous: any width
+    assert fwd(N=8193, ld=8200, ldh=8193) == STRIDE       # strided rows need ld % 8 == 0
+    assert fwd(N=8193, ld=8200, ldh=8200) == OK
+    assert fwd(gate=A0 + 2) == ALIGN and fwd(h=C0 + 8) == ALIGN
+    assert fwd(h=A0 + 64) == OVERLAP                      # h inside gate
+    # [gate | up] halves of one buffer: up = gate + N, ld = 2N
+    assert fwd(gate=A0, up=A0 + 2 * 128, ld=256) == OK
+    # an output placed in the row gaps of a strided input is not an overlap...
+    assert fwd(gate=A0, up=A0 + 2 * 128, ld=384, h=A0 + 2 * 256, ldh=384) == OK
+    # ...but one that lands on input elements is
+    assert fwd(gate=A0, up=A0 + 2 * 128, ld=384, h=A0 + 2 * 200, ldh=384) == OVERLAP
+    assert fwd(M=1 << 62, N=1 << 20, ld=1 << 20, ldh=1 << 20) == SHAPE  # extent overflow
+
+
+def bwd(**kw):
+    a = dict(act=1, layout=0, M=64, N=128, gate=A0, up=B0, ld=128, dh=C0, lddh=128, da=D0, db=E0, ldo=128)
+    a.update(kw)
+    return L.glu_check_bwd(a["act"], a["layout"], a["M"], a["N"], P(a["gate"]), P(a["up"]), a["ld"],
+                           P(a["dh"]), a["lddh"], P(a["da"]), P(a["db"]), a["ldo"])
+
+
+def test_bwd_checks():
+    assert bwd() == OK
+    assert bwd(dh=0) == NULL and bwd(da=0) == NULL and bwd(db=0) == NULL
+    assert bwd(layout=1, up=0, ld=256, db=E0, ldo=256) == ARG
+    assert bwd(layout=1, up=0, ld=256, db=0, ldo=256) == OK
+    assert bwd(layout=1, up=0, ld=256, db=0, ldo=128) == STRIDE
+    assert bwd(da=A0, db=B0) == OK                        # in place
+    assert bwd(da=A0, db=B0, ldo=136) == OVERLAP          # same buffers, other stride: not in place
+    assert bwd(da=C0) == OVERLAP                          # da onto dh
+    assert bwd(da=D0, db=D0 + 64) == OVERLAP              # da and db collide
+    # concatenated [dGate | dUp] output: db = da + N, ld_out = 2N
+    assert bwd(da=D0, db=D0 + 2 * 128, ldo=256) == OK
+    assert bwd(dh=C0 + 4) == ALIGN
+
+
+def mxf(**kw):
+    a = dict(act=0, layout=0, M=64, N=128, gate=A0, up=B0, ld=128, flags=3, qr=C0, sr=D0, qc=E0, sc=F0)
+    a.update(kw)
+    return L.glu_check_fwd_mxfp8(a["act"], a["layout"], a["M"], a["N"], P(a["gate"]), P(a["up"]),
+                                 a["ld"], a["flags"], P(a["qr"]), P(a["sr"]), P(a["qc"]), P(a["sc"]))
+
+
+def test_fwd_mxfp8_checks():
+    assert mxf() == OK
+    assert mxf(flags=0) == ARG and mxf(flags=4) == ARG
+    assert mxf(flags=1, qc=0, sc=0) == OK and mxf(flags=2, qr=0, sr=0) == OK
+    assert mxf(flags=1) == ARG                            # colwise pointers given but disabled
+    assert mxf(flags=2, qr=0) == ARG
+    assert mxf(qr=0) == NULL and mxf(sc=0) == NULL
+    assert mxf(N=96, ld=96) == OK and mxf(N=80, ld=80) == SHAPE
+    assert mxf(M=48) == SHAPE                             # colwise needs M % 32 == 0
+    assert mxf(M=48, flags=1, qc=0, sc=0) == OK           # rowwise accepts ragged M
+    assert mxf(ld=132) == STRIDE
+    assert mxf(sr=D0 + 1) == ALIGN
+    assert mxf(qr=A0) == OVERLAP and mxf(sr=C0 + 16) == OVERLAP
+    assert mxf(layout=1, up=0, ld=256) == OK and mxf(layout=1, up=0, ld=128) == STRIDE
+
+
+def mxb(**kw):
+    a = dict(act=0, layout=0, M=64, N=128, gate=A0, up=B0, ld=128, dh=C0, lddh=128, flags=3,
+             qr=D0, sr=E0, qc=F0, sc=0x70000000)
+    a.update(kw)
+    return L.glu_check_bwd_mxfp8(a["act"], a["layout"], a["M"], a["N"], P(a["gate"]), P(a["up"]),
+                                 a["ld"], P(a["dh"]), a["lddh"], a["flags"], P(a["qr"]), P(a["sr"]),
+                                 P(a["qc"]), P(a["sc"]))
+
+
+def test_bwd_mxfp8_checks():
+    assert mxb() == OK
+    assert mxb(layout=1, up=0) == UNSUP
+    assert mxb(dh=0) == NULL
+    assert mxb(lddh=120) == STRIDE and mxb(lddh=132) == STRIDE
+    assert mxb(qr=C0) == OVERLAP
+    assert mxb(N=40, ld=40, lddh=40) == SHAPE
+
+
+def nv(**kw):
+    a = dict(act=1, layout=1, M=100, H=256, gate=A0, up=0, ld=512, q=C0, sf=D0, sfl=0)
+    a.update(kw)
+    return L.glu_check_fwd_nvfp4(a["act"], a["layout"], a["M"], a["H"], P(a["gate"]), P(a["up"]),
+                                 a["ld"], P(a["q"]), P(a["sf"]), a["sfl"])
+
+
+def test_fwd_nvfp4_checks():
+    assert nv() == OK and nv(sfl=1) == OK
+    assert nv(sfl=2) == ARG
+    assert nv(H=264, ld=528) == SHAPE                     # H % 16
+    assert nv(ld=516) == STRIDE and nv(ld=511) == STRIDE and nv(ld=520) == OK
+    assert nv(q=0) == NULL and nv(sf=0) == NULL
+    assert nv(layout=0, up=B0, ld=256) == OK
+    assert nv(sf=C0 + 32) == OVERLAP
+    assert L.glu_nvfp4_sf_bytes(784, 16384, 0) == 784 * 1024
+    assert L.glu_nvfp4_sf_bytes(784, 16384, 1) == 896 * 1024
+    assert L.glu_nvfp4_sf_bytes(968, 16384, 1) == 1024 * 1024
+    assert L.glu_nvfp4_sf_bytes(1, 80, 1) == 128 * 8
+    assert L.glu_nvfp4_sf_bytes(1, 81, 0) == -1
+
+
+def test_quant_hook_checks():
+    q = L.glu_check_quant_mxfp8_f32
+    assert q(64, 64, P(A0), 64, 3, P(B0), P(C0), P(D0), P(E0)) == OK
+    assert q(64, 64, P(A0), 66, 3, P(B0), P(C0), P(D0), P(E0)) == STRIDE
+    assert q(64, 64, P(A0), 60, 3, P(B0), P(C0), P(D0), P(E0)) == STRIDE
+    assert q(64, 64, P(A0), 64, 1, P(B0), P(C0), P(0), P(0)) == OK
+    n = L.glu_check_quant_nvfp4_f32
+    assert n(64, 64, P(A0), 64, P(B0), P(C0), 0) == OK
+    assert n(64, 72, P(A0), 72, P(B0), P(C0), 0) == SHAPE
+
+
+def test_entry_points_fail_before_any_hip_call():
+    """Rejected arguments and empty problems return without touching HIP, so these calls
+    are safe on a machine with no GPU."""
+    assert L.glu_fwd(0, 0, 4, 4, P(0), P(B0), 4, P(C0), 4, P(0)) == NULL
+    assert L.glu_fwd(0, 0, 0, 4, P(0), P(0), 4, P(0), 4, P(0)) == OK
+    assert L.glu_bwd(0, 0, 4, 8, P(A0), P(B0), 8, P(C0), 8, P(D0), P(E0), 4, P(0)) == STRIDE
+    assert L.glu_fwd_mxfp8(0, 0, 64, 40, P(A0), P(B0), 40, 1, P(C0), P(D0), P(0), P(0), P(0)) == SHAPE
+    assert L.glu_bwd_mxfp8(0, 1, 64, 64, P(A0), P(0), 128, P(C0), 64, 1, P(D0), P(E0), P(0), P(0), P(0)) == UNSUP
+    assert L.glu_fwd_nvfp4(1, 1, 8, 24, P(A0), P(0), 48, P(C0), P(D0), 0, P(0)) == SHAPE
+    assert L.glu_quant_mxfp8_f32(32, 32, P(A0), 32, 7, P(B0), P(C0), P(D0), P(E0), P(0)) == ARG
+    assert L.glu_quant_nvfp4_f32(32, 32, P(A0 + 4), 32, P(B0), P(C0), 0, P(0)) == ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        glu.glu_fwd(x, x)
+    with pytest.raises(TypeError):
+        glu.glu_fwd(x.float(), x.float())

@@ -1,0 +1,232 @@
+"""GPU parity of the fused MXFP8 paths and the MXFP8 quantizer hook against the oracle.
+
+Rule 1 (bit-exact when the quantizer sees identical FP32 values):
+  * glu_quant_mxfp8_f32 on random, outlier, subnormal, tie-dense, all-BF16 and non-finite
+    inputs equals oracle.quant_mxfp8 byte for byte, rowwise, colwise and both;
+  * the fused kernels equal the oracle quantizer applied to the GPU's own BF16 glu_fwd /
+    glu_bwd output (the quantizer isolated end to end).
+Rule 3 (fused GPU vs oracle end to end) on the five workload shapes, full or sampled.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from conftest import bits, u8
+from parity import check_rule3_mx
+
+pytestmark = pytest.mark.gpu
+FLAGS = [(True, False), (False, True), (True, True)]
+ACTS = [("swiglu", oracle.SWIGLU), ("geglu", oracle.GEGLU_TANH)]
+
+
+def _flags(row, col):
+    return (oracle.ROWWISE if row else 0) | (oracle.COLWISE if col else 0)
+
+
+def _hook_matches_oracle(gpu, x):
+    xd = torch.from_numpy(x).cuda()
+    for row, col in FLAGS:
+        qr, qc, sr, sc = gpu.glu_quant_mxfp8_f32(xd, rowwise=row, colwise=col)
+        o = oracle.quant_mxfp8(x, _flags(row, col))
+        if row:
+            assert np.array_equal(u8(sr), o[1]), "row scales"
+            assert np.array_equal(u8(qr), o[0]), "row codes"
+        if col:
+            assert np.array_equal(u8(sc), o[3]), "col scales"
+            assert np.array_equal(u8(qc), o[2]), "col codes"
+
+
+def test_hook_random_fp32(gpu):
+    rng = np.random.default_rng(100)
+    x = rng.normal(0, 1, (256, 512))
+    x[rng.random(x.shape) < 1e-3] *= 1000
+    x[rng.random(x.shape) < 1e-2] *= 2.0 ** -40
+    x[:32, :32] = 0.0
+    x[32:64, 64:96] = -0.0
+    x = x.astype(np.float32)
+    x[100, 3] = np.float32(1e-42)  # FP32 subnormal
+    _hook_matches_oracle(gpu, x)
+
+
+def test_hook_every_bf16_value(gpu):
+    allv = si.special_bf16_values()
+    x = np.zeros(65536, np.float32)
+    x[: allv.size] = si.from_bits(allv).float().numpy()
+    _hook_matches_oracle(gpu, x.reshape(2048, 32))
+    _hook_matches_oracle(gpu, np.ascontiguousarray(x.reshape(2048, 32)[::-1]))
+
+
+def test_hook_ties_and_boundaries(gpu):
+    """Each block: one element 448 * 2^k fixes the scale at 2^k; the others sit on E4M3
+    rounding midpoints at that scale and one FP32 ulp either side."""
+    rng = np.random.default_rng(101)
+    vals = np.unique(np.abs(oracle.e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))))
+    mids = (vals[1:] + vals[:-1]) / 2
+    nblk = 8192
+    k = rng.integers(-120, 100, nblk)
+    pick = rng.choice(mids, (nblk, 31))
+    jitter = rng.integers(-1, 2, (nblk, 31))
+    y = (pick * np.exp2(k)[:, None]).astype(np.float32)
+    y = np.where(jitter > 0, np.nextafter(y, np.float32(np.inf)), np.where(jitter < 0, np.nextafter(y, np.float32(0)), y))
+    y *= rng.choice([-1, 1], y.shape).astype(np.float32)
+    first = (448.0 * np.exp2(k)).astype(np.float32)[:, None]
+    x = np.concatenate([first, y], axis=1).astype(np.float32)
+    _hook_matches_oracle(gpu, x.reshape(1024, 256))
+
+
+def test_hook_nonfinite_blocks(gpu):
+    x = np.ones((64, 128), np.float32)
+    x[0, 5] = np.inf
+    x[7, 40] = -np.inf
+    x[40, 100] = np.nan
+    x[33, 64:96] = 3.0e38
+    _hook_matches_oracle(gpu, x)
+
+
+def _q(h_or_x_bits, flags):
+    return oracle.quant_mxfp8(si.from_bits(h_or_x_bits).float().numpy(), flags)
+
+
+@pytest.mark.parametrize("name,kind", ACTS)
+@pytest.mark.parametrize("layout", ["split", "concat", "paired"])
+def test_fused_fwd_equals_quantized_glu_fwd(gpu, name, kind, layout):
+    M, N = 128, 256
+    gate, up = si.glu_operands(M, N, seed=5, outliers=True)
+    gd, ud = gate.cuda(), up.cuda()
+    if layout == "concat":
+        cat = torch.cat([gd, ud], 1)
+        args, lay = (cat[:, :N], cat[:, N:]), "split"
+    elif layout == "paired":
+        args, lay = (torch.stack([gd, ud], 2).reshape(M, 2 * N).contiguous(), None), "paired"
+    else:
+        args, lay = (gd, ud), "split"
+    h = bits(gpu.glu_fwd(*args, act=name, layout=lay))
+    for row, col in FLAGS:
+        qr, qc, sr, sc = gpu.glu_fwd_mxfp8(*args, act=name, layout=lay, rowwise=row, colwise=col)
+        o = _q(h, _flags(row, col))
+        if row:
+            assert np.array_equal(u8(qr), o[0]) and np.array_equal(u8(sr), o[1])
+        if col:
+            assert np.array_equal(u8(qc), o[2]) and np.array_equal(u8(sc), o[3])
+
+
+@pytest.mark.parametrize("name,kind", ACTS)
+def test_fused_bwd_equals_quantized_glu_bwd(gpu, name, kind):
+    M, N = 96, 160
+    gate, up, dh = si.glu_operands(M, N, seed=6, outliers=True, with_dh=True)
+    gd, ud, dd = gate.cuda(), up.cuda(), dh.cuda()
+    da, db = gpu.glu_bwd(gd, ud, dd, act=name)
+    X = np.concatenate([bits(da), bits(db)], axis=1)
+    for row, col in FLAGS:
+        qr, qc, sr, sc = gpu.glu_bwd_mxfp8(gd, ud, dd, act=name, rowwise=row, colwise=col)
+        o = _q(X, _flags(row, col))
+        if row:
+            assert np.array_equal(u8(qr), o[0]) and np.array_equal(u8(sr), o[1])
+        if col:
+            assert np.array_equal(u8(qc), o[2]) and np.array_equal(u8(sc), o[3])
+
+
+def test_both_equals_row_and_col(gpu):
+    gate, up, dh = si.glu_operands(256, 512, seed=8, outliers=True, with_dh=True)
+    gd, ud, dd = gate.cuda(), up.cuda(), dh.cuda()
+    for fn, args in ((gpu.glu_fwd_mxfp8, (gd, ud)), (gpu.glu_bwd_mxfp8, (gd, ud, dd))):
+        b = fn(*args, rowwise=True, colwise=True)
+        r = fn(*args, rowwise=True, colwise=False)
+        c = fn(*args, rowwise=False, colwise=True)
+        assert torch.equal(b[0], r[0]) and torch.equal(b[2], r[2])
+        assert torch.equal(b[1], c[1]) and torch.equal(b[3], c[3])
+
+
+def test_ragged_rows_rowwise_and_edges(gpu):
+    for M, N in [(100, 96), (1, 32), (33, 64), (7, 4096)]:
+        gate, up = si.glu_operands(M, N, seed=M + N, outliers=True)
+        gd, ud = gate.cuda(), up.cuda()
+        qr, qc, sr, sc = gpu.glu_fwd_mxfp8(gd, ud, rowwise=True)
+        assert qc.numel() == 0 and sc.numel() == 0
+        o = _q(bits(gpu.glu_fwd(gd, ud)), oracle.ROWWISE)
+        assert np.array_equal(u8(qr), o[0]) and np.array_equal(u8(sr), o[1])
+    e = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    out = gpu.glu_fwd_mxfp8(e, e, rowwise=True, colwise=True)
+    assert out[0].shape == (0, 64)
+
+
+def test_row_slices_are_batch_invariant(gpu):
+    gate, up = si.glu_operands(256, 256, seed=9, outliers=True)
+    gd, ud = gate.cuda(), up.cuda()
+    full = gpu.glu_fwd_mxfp8(gd, ud, rowwise=True, colwise=True)
+    part = gpu.glu_fwd_mxfp8(gd[64:160], ud[64:160], rowwise=True, colwise=True)
+    assert torch.equal(full[0][64:160], part[0]) and torch.equal(full[2][64:160], part[2])
+    assert torch.equal(full[1][:, 64:160], part[1]) and torch.equal(full[3][:, 2:5], part[3])
+    again = gpu.glu_fwd_mxfp8(gd, ud, rowwise=True, colwise=True)
+    assert all(torch.equal(a, b) for a, b in zip(full, again))
+
+
+# ---- rule 3 on the workload shapes ---------------------------------------------------
+
+def _rule3_rows(h_bits, out, oref, what):
+    qr, qc, sr, sc = out
+    if qr.numel():
+        check_rule3_mx(h_bits, u8(qr), u8(sr), oref[0], oref[1], what + " rowwise")
+    if qc.numel():
+        check_rule3_mx(np.ascontiguousarray(h_bits.T), u8(qc), u8(sc), oref[2], oref[3], what + " colwise")
+
+
+def test_config_small_swiglu_fwd_rowwise(gpu):
+    gate, up = si.glu_operands(128, 128, seed=0)
+    gb, ub = bits(gate), bits(up)
+    out = gpu.glu_fwd_mxfp8(gate.cuda(), up.cuda(), rowwise=True)
+    _rule3_rows(oracle.glu_fwd(oracle.SWIGLU, gb, ub), out,
+                oracle.glu_fwd_mxfp8(oracle.SWIGLU, gb, ub, flags=1), "128x128")
+
+
+def test_config_mid_swiglu_fwd_bwd_both(gpu):
+    gate, up, dh = si.glu_operands(4096, 2048, seed=0, with_dh=True)
+    gb, ub, db_ = bits(gate), bits(up), bits(dh)
+    gd, ud, dd = gate.cuda(), up.cuda(), dh.cuda()
+    out = gpu.glu_fwd_mxfp8(gd, ud, rowwise=True, colwise=True)
+    _rule3_rows(oracle.glu_fwd(oracle.SWIGLU, gb, ub), out,
+                oracle.glu_fwd_mxfp8(oracle.SWIGLU, gb, ub, flags=3), "4096x2048 fwd")
+    out = gpu.glu_bwd_mxfp8(gd, ud, dd, rowwise=True, colwise=True)
+    oa, ob = oracle.glu_bwd(oracle.SWIGLU, gb, ub, db_)
+    _rule3_rows(np.concatenate([oa, ob], 1), out,
+                oracle.glu_bwd_mxfp8(oracle.SWIGLU, gb, ub, db_, flags=3), "4096x2048 bwd")
+
+
+def _slabs(M, n, seed):
+    rng = np.random.default_rng(seed)
+    return sorted({0, M // 32 - 1, *rng.integers(0, M // 32, n).tolist()})
+
+
+def test_config_large_swiglu_outliers_sampled(gpu):
+    """[16384, 7168] with 0.1% x1000 outliers, fwd and bwd, both scalings: every output of
+    sampled 32-row slabs (whole rows, whole colwise blocks) against the oracle."""
+    M, N = 16384, 7168
+    g, u, d = si.normal_bf16_device([(M, N)] * 3, seed=0, outliers=True)
+    fwd = gpu.glu_fwd_mxfp8(g, u, rowwise=True, colwise=True)
+    bwd = gpu.glu_bwd_mxfp8(g, u, d, rowwise=True, colwise=True)
+    torch.cuda.synchronize()
+    for s in _slabs(M, 6, 1):
+        r = slice(32 * s, 32 * s + 32)
+        gb, ub, db_ = bits(g[r]), bits(u[r]), bits(d[r])
+        o = oracle.glu_fwd_mxfp8(oracle.SWIGLU, gb, ub, flags=3)
+        h = oracle.glu_fwd(oracle.SWIGLU, gb, ub)
+        sl = (fwd[0][r], fwd[1][:, r], fwd[2][r], fwd[3][:, s:s + 1])
+        _rule3_rows(h, sl, o, f"fwd slab {s}")
+        o = oracle.glu_bwd_mxfp8(oracle.SWIGLU, gb, ub, db_, flags=3)
+        oa, ob = oracle.glu_bwd(oracle.SWIGLU, gb, ub, db_)
+        sl = (bwd[0][r], bwd[1][:, r], bwd[2][r], bwd[3][:, s:s + 1])
+        _rule3_rows(np.concatenate([oa, ob], 1), sl, o, f"bwd slab {s}")
+
+
+def test_config_xlarge_swiglu_fwd_rowwise_sampled(gpu):
+    M, N = 131072, 8192
+    g, u = si.normal_bf16_device([(M, N)] * 2, seed=0, outliers=True)
+    qr, _, sr, _ = gpu.glu_fwd_mxfp8(g, u, rowwise=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    rows = torch.tensor(sorted({0, M - 1, *rng.integers(0, M, 30).tolist()}), device="cuda")
+    gb, ub = bits(g[rows]), bits(u[rows])
+    o = oracle.glu_fwd_mxfp8(oracle.SWIGLU, gb, ub, flags=1)
+    check_rule3_mx(oracle.glu_fwd(oracle.SWIGLU, gb, ub), u8(qr[rows]), u8(sr[rows]), o[0], o[1], "131072x8192")

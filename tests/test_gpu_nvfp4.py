@@ -1,0 +1,113 @@
+"""GPU parity of the fused NVFP4 path and the NVFP4 quantizer hook against the oracle.
+
+Rule 1: glu_quant_nvfp4_f32 equals oracle.quant_nvfp4 byte for byte on random, outlier,
+tie-dense, all-BF16 and non-finite inputs, in both scale layouts; the fused kernel equals
+the oracle quantizer applied to the GPU's own BF16 glu_fwd output.
+Rule 3: the GeGLU NVFP4 workload ([M, 32768] interleaved, M in {784, 816, 880, 968}) end to
+end against the oracle, plus the zero padding of the 128x4 scale layout.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from conftest import bits, u8
+from parity import check_rule3_nv
+
+pytestmark = pytest.mark.gpu
+SFL = [("rowmajor", oracle.SF_ROWMAJOR), ("128x4", oracle.SF_128x4)]
+
+
+def _hook(gpu, x):
+    xd = torch.from_numpy(x).cuda()
+    for name, code in SFL:
+        q, sf = gpu.glu_quant_nvfp4_f32(xd, sf_layout=name)
+        oq, osf = oracle.quant_nvfp4(x, code)
+        assert np.array_equal(u8(sf).ravel(), osf.ravel()), f"scales ({name})"
+        assert np.array_equal(u8(q), oq), f"codes ({name})"
+
+
+def test_hook_random_fp32(gpu):
+    rng = np.random.default_rng(200)
+    x = rng.normal(0, 1, (200, 1024))
+    x[rng.random(x.shape) < 1e-3] *= 1000
+    x[rng.random(x.shape) < 1e-2] *= 2.0 ** -30
+    x[3, :16] = 0.0
+    x[4, 16:32] = -0.0
+    _hook(gpu, x.astype(np.float32))
+
+
+def test_hook_every_bf16_value(gpu):
+    allv = si.special_bf16_values()
+    x = np.zeros(65536, np.float32)
+    x[: allv.size] = si.from_bits(allv).float().numpy()
+    _hook(gpu, x.reshape(256, 256))
+    rng = np.random.default_rng(201)
+    _hook(gpu, rng.permutation(x).reshape(512, 128))
+
+
+def test_hook_ties_and_boundaries(gpu):
+    """Blocks whose amax lands on 6 x an E4M3 midpoint (scale ties) and whose elements land
+    on E2M1 midpoints x S (code ties), plus one FP32 ulp either side."""
+    rng = np.random.default_rng(202)
+    e4 = np.unique(np.abs(oracle.e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))))
+    nblk = 16384
+    S = rng.choice(e4[1:], nblk)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    y = (rng.choice(mids, (nblk, 15)) * S[:, None]).astype(np.float32)
+    j = rng.integers(-1, 2, y.shape)
+    y = np.where(j > 0, np.nextafter(y, np.float32(np.inf)), np.where(j < 0, np.nextafter(y, np.float32(0)), y))
+    smid = (e4[1:] + e4[:-1]) / 2
+    amax = (6.0 * rng.choice(smid, nblk)).astype(np.float32)
+    ja = rng.integers(-1, 2, nblk)
+    amax = np.where(ja > 0, np.nextafter(amax, np.float32(np.inf)), np.where(ja < 0, np.nextafter(amax, np.float32(0)), amax))
+    x = np.concatenate([amax[:, None], y], axis=1) * rng.choice([-1, 1], (nblk, 16))
+    _hook(gpu, x.astype(np.float32).reshape(1024, 256))
+
+
+def test_hook_nonfinite_blocks(gpu):
+    x = np.ones((8, 64), np.float32)
+    x[0, 3] = np.inf
+    x[5, 20] = np.nan
+    x[6, 40] = -np.inf
+    _hook(gpu, x)
+
+
+@pytest.mark.parametrize("act,kind", [("geglu", oracle.GEGLU_TANH), ("swiglu", oracle.SWIGLU)])
+@pytest.mark.parametrize("layout", ["paired", "split"])
+def test_fused_equals_quantized_glu_fwd(gpu, act, kind, layout):
+    M, H = 130, 1024
+    gate, up = si.glu_operands(M, H, seed=12, outliers=True)
+    gd, ud = gate.cuda(), up.cuda()
+    args = (torch.stack([gd, ud], 2).reshape(M, 2 * H).contiguous(), None) if layout == "paired" else (gd, ud)
+    h = gpu.glu_fwd(*args, act=act, layout=layout)
+    hf = si.from_bits(bits(h)).float().numpy()
+    for name, code in SFL:
+        q, sf = gpu.glu_fwd_nvfp4(*args, act=act, layout=layout, sf_layout=name)
+        oq, osf = oracle.quant_nvfp4(hf, code)
+        assert np.array_equal(u8(q), oq) and np.array_equal(u8(sf).ravel(), osf.ravel())
+
+
+@pytest.mark.parametrize("M", [784, 816, 880, 968])
+def test_config_geglu_nvfp4(gpu, M):
+    H = 16384
+    x = si.paired_operand(M, H, seed=0)
+    xb = bits(x)
+    xd = x.cuda()
+    h = oracle.glu_fwd(oracle.GEGLU_TANH, xb, None, layout=oracle.PAIRED)
+    for name, code in SFL:
+        q, sf = gpu.glu_fwd_nvfp4(xd, act="geglu", layout="paired", sf_layout=name)
+        oq, osf = oracle.glu_fwd_nvfp4(oracle.GEGLU_TANH, xb, None, sf_layout=code)
+        if code == oracle.SF_ROWMAJOR:
+            check_rule3_nv(h, u8(q), u8(sf), oq, osf, f"M={M}")
+        else:
+            # same scales after unswizzling, and zero padding
+            s = u8(sf)
+            nb, cp = H // 16, (H // 16 + 3) // 4 * 4
+            idx = np.array([[oracle.sf128x4_offset(r, c, cp) for c in range(0, nb, 97)] for r in range(0, M, 13)])
+            assert np.array_equal(s[idx], osf[idx])
+            rp = (M + 127) // 128 * 128
+            pad = np.array([oracle.sf128x4_offset(r, c, cp) for r in range(M, rp) for c in range(0, nb, 31)], dtype=np.int64)
+            if pad.size:
+                assert not np.any(s[pad]), "128x4 padding rows must be zero"
