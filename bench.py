@@ -1,0 +1,257 @@
+"""Benchmark of the fused GLU + MX-quant path on one MI355X.
+
+One step = the whole hot path over one batch of the large SwiGLU workload: the fused
+forward with MXFP8 rowwise + colwise output, then the fused backward with MXFP8 rowwise +
+colwise output of [dGate | dUp], on gate, up, dh BF16 [16384, 7168] ~ N(0, 1) with 0.1% of
+the elements scaled x1000 (the shape the MXFP8 page quotes its fused numbers on).
+Inputs are resident in HBM before the timed region.  `value` is algorithmic GB/s: bytes
+the method must move (BF16 inputs read once, E4M3 codes and E8M0 scales written once,
+GB = 1e9) divided by the time of the K timed steps.
+
+Also reported on the same JSON line:
+  roofline      - the dominant kernel (the fused backward) against the 8 TB/s HBM peak,
+                  its duration measured with HIP events on the launch stream;
+  cpu_baseline  - the CPU oracle on a bounded row sample of the same workload;
+  sweep         - every workload shape of the pages (MXFP8 SwiGLU fwd/bwd per direction,
+                  GeGLU BF16 fwd/bwd, GeGLU NVFP4), median of cold launches.
+Only one GPU is supported; --gpus above 1 exits with a message.
+"""
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused GLU+MX-quant fwd/bwd achieved HBM GB/s and % of peak, M×N sweep"
+PEAK_GBPS = 8000.0  # MI355X HBM3E
+# The MXFP8 page's fused GB200 times for this exact workload (forward both 143.36 us,
+# backward both 219.14 us at (16384, 7168)), combined under the same byte model.
+PAGES_STEP_GBPS = (711_983_104 + 1_189_085_184) / ((143.36 + 219.14) * 1e-6) / 1e9
+
+
+def mx_bytes(M, N, bwd, ndir):
+    E = M * N
+    return (6 * E + ndir * (2 * E + 2 * E // 32)) if bwd else (4 * E + ndir * (E + E // 32))
+
+
+def bf16_bytes(M, N, bwd):
+    return (10 if bwd else 6) * M * N
+
+
+def nv_bytes(M, H):
+    E = M * H
+    return 4 * E + E // 2 + E // 16
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def time_launches(torch, fns, iters):
+    """Median / min / p90 of per-launch durations (us), cycling through fns (one per input
+    set, so repeated launches do not re-read cached inputs)."""
+    for f in fns[: min(3, len(fns))]:
+        f()
+    torch.cuda.synchronize()
+    ev = _events(torch, 2 * iters)
+    for i in range(iters):
+        ev[2 * i].record()
+        fns[i % len(fns)]()
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    us = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(iters))
+    return dict(median_us=statistics.median(us), min_us=us[0], p90_us=us[int(0.9 * (len(us) - 1))])
+
+
+def n_sets(bytes_per_set):
+    """Input sets to rotate through so that one pass over them exceeds 1 GiB (4x the
+    256 MB last-level cache), capped at 32."""
+    return max(1, min(32, math.ceil((1 << 30) / max(1, bytes_per_set))))
+
+
+def sweep(torch, glu, si, iters):
+    res = {}
+
+    def rec(name, b, t):
+        print(f"[bench] {name}: {t['median_us']:.2f} us", file=sys.stderr, flush=True)
+        res[name] = dict(bytes=b, us=round(t["median_us"], 2), gbps=round(b / t["median_us"] / 1e3, 1),
+                         frac=round(b / t["median_us"] / 1e3 / PEAK_GBPS, 4))
+
+    # MXFP8 SwiGLU shapes
+    for M, N, outl, cases in [
+        (128, 128, False, [("fwd", "row")]),
+        (4096, 2048, False, [("fwd", "both"), ("bwd", "both")]),
+        (16384, 7168, True, [("fwd", "row"), ("fwd", "col"), ("fwd", "both"),
+                             ("bwd", "row"), ("bwd", "col"), ("bwd", "both")]),
+        (131072, 8192, True, [("fwd", "row")]),
+    ]:
+        per = 6 * M * N
+        sets = [si.normal_bf16_device([(M, N)] * 3, seed=100 + s, outliers=outl) for s in range(n_sets(per))]
+        for d, mode in cases:
+            row, col = mode in ("row", "both"), mode in ("col", "both")
+            bwd = d == "bwd"
+            out = glu._mx_buffers(M, 2 * N if bwd else N, row, col, "cuda", None)
+            if bwd:
+                fns = [lambda s=s: glu.glu_bwd_mxfp8(s[0], s[1], s[2], rowwise=row, colwise=col, out=out) for s in sets]
+            else:
+                fns = [lambda s=s: glu.glu_fwd_mxfp8(s[0], s[1], rowwise=row, colwise=col, out=out) for s in sets]
+            t = time_launches(torch, fns, iters)
+            rec(f"swiglu_mxfp8_{d}_{mode}_{M}x{N}", mx_bytes(M, N, bwd, 2 if mode == "both" else 1), t)
+            del out, fns
+        del sets
+        torch.cuda.empty_cache()
+    # GeGLU BF16 sweep
+    for R in (1024, 8192):
+        for W in (4096, 11008, 14336, 18944, 29568, 8193):
+            sets = [si.normal_bf16_device([(R, W)] * 3, seed=R + W + s) for s in range(n_sets(6 * R * W))]
+            h = torch.empty(R, W, dtype=torch.bfloat16, device="cuda")
+            da, db = torch.empty_like(h), torch.empty_like(h)
+            t = time_launches(torch, [lambda s=s: glu.glu_fwd(s[0], s[1], act="geglu", out=h) for s in sets], iters)
+            rec(f"geglu_bf16_fwd_{R}x{W}", bf16_bytes(R, W, False), t)
+            t = time_launches(torch, [lambda s=s: glu.glu_bwd(s[0], s[1], s[2], act="geglu", out=(da, db))
+                                      for s in sets], iters)
+            rec(f"geglu_bf16_bwd_{R}x{W}", bf16_bytes(R, W, True), t)
+            del sets, h, da, db
+        torch.cuda.empty_cache()
+    # GeGLU NVFP4
+    H = 16384
+    for M in (784, 816, 880, 968):
+        sets = [si.normal_bf16_device([(M, 2 * H)], seed=M + s)[0] for s in range(n_sets(4 * M * H))]
+        out = glu._nv_buffers(M, H, "128x4", "cuda", None)
+        t = time_launches(torch, [lambda x=x: glu.glu_fwd_nvfp4(x, act="geglu", layout="paired",
+                                                                 sf_layout="128x4", out=out) for x in sets], iters)
+        rec(f"geglu_nvfp4_fwd_{M}x{H}", nv_bytes(M, H), t)
+        del sets, out
+    return res
+
+
+def cpu_baseline(si, budget_s):
+    """The oracle (as it stands) on whole 512-row slabs of the step's workload, until
+    budget_s seconds of CPU time have passed or every row is done."""
+    import oracle
+    M, N, slab = 16384, 7168, 512
+    done, t_used = 0, 0.0
+    while done < M and t_used < budget_s:
+        g, u, d = si.glu_operands(slab, N, seed=1000 + done, outliers=True, with_dh=True)
+        gb, ub, db = si.to_bits(g), si.to_bits(u), si.to_bits(d)
+        t0 = time.perf_counter()
+        oracle.glu_fwd_mxfp8(oracle.SWIGLU, gb, ub, flags=3)
+        oracle.glu_bwd_mxfp8(oracle.SWIGLU, gb, ub, db, flags=3)
+        t_used += time.perf_counter() - t0
+        done += slab
+    b = mx_bytes(done, N, False, 2) + mx_bytes(done, N, True, 2)
+    print(f"[bench] cpu oracle: {done} rows in {t_used:.1f} s", file=sys.stderr, flush=True)
+    return dict(value=round(b / t_used / 1e9, 4), unit="GB/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{done} of 16384 rows x 7168 (fwd + bwd, both scalings), {t_used:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sweep-iters", type=int, default=20)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also launch one 1 GiB device copy (for scaling HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path needs no collective and runs one "
+              "kernel per GPU on its own rows; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import glu_activation_microscaling_amd as glu
+    import synthetic_inputs as si
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    glu.lib()  # fail loudly when the HIP library is missing
+
+    M, N = 16384, 7168
+    sets = [si.normal_bf16_device([(M, N)] * 3, seed=s, outliers=True) for s in range(2)]
+    fo = glu._mx_buffers(M, N, True, True, "cuda", None)
+    bo = glu._mx_buffers(M, 2 * N, True, True, "cuda", None)
+    fwd_b, bwd_b = mx_bytes(M, N, False, 2), mx_bytes(M, N, True, 2)
+
+    def step(i, ev=None):
+        g, u, d = sets[i % 2]
+        if ev: ev[0].record()
+        glu.glu_fwd_mxfp8(g, u, rowwise=True, colwise=True, out=fo)
+        if ev: ev[1].record()
+        glu.glu_bwd_mxfp8(g, u, d, rowwise=True, colwise=True, out=bo)
+        if ev: ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [_events(torch, 3) for _ in range(args.steps)]
+    start, end = _events(torch, 2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(end)
+    ms_per_step = gpu_ms / args.steps
+    fwd_us = statistics.mean(e[0].elapsed_time(e[1]) for e in evs) * 1e3
+    bwd_us = statistics.mean(e[1].elapsed_time(e[2]) for e in evs) * 1e3
+    value = (fwd_b + bwd_b) / (ms_per_step * 1e-3) / 1e9
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGES_STEP_GBPS, 3),
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "swiglu_mxfp8_fwd_bwd_both_16384x7168_outliers",
+            "activation": "swiglu", "M": M, "N": N, "outliers": "0.1% x1000",
+            "outputs": "E4M3 codes + E8M0 RCEIL scales, rowwise 1x32 and colwise 32x1",
+            "bytes_per_step": fwd_b + bwd_b, "pct_of_peak": round(100 * value / PEAK_GBPS, 1),
+            "fwd_us": round(fwd_us, 2), "bwd_us": round(bwd_us, 2), "wall_s": round(wall, 3),
+            "pages_gbps_same_workload_gb200": round(PAGES_STEP_GBPS, 1),
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "k_mxfp8 backward, both scalings",
+            "achieved": round(bwd_b / bwd_us / 1e3, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+            "frac": round(bwd_b / bwd_us / 1e3 / PEAK_GBPS, 4),
+            "traffic": None,
+        },
+    }
+    del sets, fo, bo
+    torch.cuda.empty_cache()
+    if not args.no_sweep:
+        result["sweep"] = sweep(torch, glu, si, args.sweep_iters)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(si, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -98,9 +98,8 @@ __global__ __launch_bounds__(BF_THREADS) void k_glu_fwd_bf16(BF16Args a, int64_t
           for (int k = 0; k < 8; k++)
             if (zl2<ACT>(g[v][k]) < TAIL_ZL2) h[k] = glu_fwd_tail<ACT>(g[v][k], u[v][k]);
         }
-        st16(hrow + j, bf16_rne(h[0]) | (bf16_rne(h[1]) << 16),
-             bf16_rne(h[2]) | (bf16_rne(h[3]) << 16), bf16_rne(h[4]) | (bf16_rne(h[5]) << 16),
-             bf16_rne(h[6]) | (bf16_rne(h[7]) << 16));
+        st16(hrow + j, pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]),
+             pack_bf16(h[6], h[7]));
       } else if (j < cols) {
         for (int64_t jj = j; jj < cols; jj++) {
           float gg, uu, zmin = 0.0f;
@@ -153,18 +152,16 @@ __global__ __launch_bounds__(BF_THREADS) void k_glu_bwd_bf16(BF16Args a, int64_t
           for (int k = 0; k < 8; k++)
             if (zl2<ACT>(g[v][k]) < TAIL_ZL2) glu_bwd_tail<ACT>(g[v][k], u[v][k], d[v][k], da[k], db[k]);
         }
-        uint32_t A[8], B[8];
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-          A[k] = bf16_rne(da[k]);
-          B[k] = bf16_rne(db[k]);
-        }
         if constexpr (LAYOUT == SPLIT) {
-          st16(arow + j, A[0] | (A[1] << 16), A[2] | (A[3] << 16), A[4] | (A[5] << 16), A[6] | (A[7] << 16));
-          st16(brow + j, B[0] | (B[1] << 16), B[2] | (B[3] << 16), B[4] | (B[5] << 16), B[6] | (B[7] << 16));
+          st16(arow + j, pack_bf16(da[0], da[1]), pack_bf16(da[2], da[3]), pack_bf16(da[4], da[5]),
+               pack_bf16(da[6], da[7]));
+          st16(brow + j, pack_bf16(db[0], db[1]), pack_bf16(db[2], db[3]), pack_bf16(db[4], db[5]),
+               pack_bf16(db[6], db[7]));
         } else {
-          st16(arow + 2 * j, A[0] | (B[0] << 16), A[1] | (B[1] << 16), A[2] | (B[2] << 16), A[3] | (B[3] << 16));
-          st16(arow + 2 * j + 8, A[4] | (B[4] << 16), A[5] | (B[5] << 16), A[6] | (B[6] << 16), A[7] | (B[7] << 16));
+          st16(arow + 2 * j, pack_bf16(da[0], db[0]), pack_bf16(da[1], db[1]), pack_bf16(da[2], db[2]),
+               pack_bf16(da[3], db[3]));
+          st16(arow + 2 * j + 8, pack_bf16(da[4], db[4]), pack_bf16(da[5], db[5]),
+               pack_bf16(da[6], db[6]), pack_bf16(da[7], db[7]));
         }
       } else if (j < cols) {
         for (int64_t jj = j; jj < cols; jj++) {

@@ -65,15 +65,11 @@ __device__ __forceinline__ float zl2(float x) {
   }
 }
 
-// sigma(z) and sigma(-z) from zl = z log2(e), valid for zl >= TAIL_ZL2.
-__device__ __forceinline__ void sigmoid2(float zl, float& s_pos, float& s_neg) {
-  float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(zl));  // e^-|z|, normal here
-  float r = __builtin_amdgcn_rcpf(1.0f + e);               // sigma(|z|)
-  float er = e * r;                                        // sigma(-|z|)
-  bool pos = zl >= 0.0f;
-  s_pos = pos ? r : er;
-  s_neg = pos ? er : r;
-}
+// e^-z = 2^-zl and sigma(z) = 1 / (1 + e^-z) from zl = z log2(e); accurate for
+// zl >= TAIL_ZL2 (for zl << 0 the exp overflows towards +Inf and sigma goes to 0, which the
+// FP64 tail path replaces).  sigma(-z) = e^-z sigma(z) is accurate in the same range.
+__device__ __forceinline__ float exp_neg(float zl) { return __builtin_amdgcn_exp2f(-zl); }
+__device__ __forceinline__ float sigmoid_from(float e) { return __builtin_amdgcn_rcpf(1.0f + e); }
 
 // z'(x); x is clamped so that z' stays finite (where it would not, sigma(-z) is 0).
 template <int ACT>
@@ -103,11 +99,9 @@ __device__ __noinline__ ActF64 act_tail_f64(double x) {
 // Forward: act(g) * u in FP32 (the caller rounds it to BF16).
 template <int ACT>
 __device__ __forceinline__ float glu_fwd_elem(float g, float u, float& zmin) {
-  float zl = zl2<ACT>(g);
+  const float zl = zl2<ACT>(g);
   zmin = __builtin_fminf(zmin, zl);
-  float sp, sn;
-  sigmoid2(zl, sp, sn);
-  return (g * sp) * u;
+  return (g * sigmoid_from(exp_neg(zl))) * u;
 }
 
 template <int ACT>
@@ -119,11 +113,12 @@ __device__ __forceinline__ float glu_fwd_tail(float g, float u) {
 template <int ACT>
 __device__ __forceinline__ void glu_bwd_elem(float g, float u, float d, float& da, float& db,
                                              float& zmin) {
-  float zl = zl2<ACT>(g);
+  const float zl = zl2<ACT>(g);
   zmin = __builtin_fminf(zmin, zl);
-  float sp, sn;
-  sigmoid2(zl, sp, sn);
-  float grad = sp * __builtin_fmaf(g * sn, dz<ACT>(g), 1.0f);
+  const float e = exp_neg(zl);
+  const float sp = sigmoid_from(e);  // sigma(z)
+  const float sn = e * sp;           // sigma(-z)
+  const float grad = sp * __builtin_fmaf(g * sn, dz<ACT>(g), 1.0f);
   da = (d * u) * grad;
   db = d * (g * sp);
 }
@@ -133,6 +128,57 @@ __device__ __forceinline__ void glu_bwd_tail(float g, float u, float d, float& d
   const ActF64 r = act_tail_f64<ACT>((double)g);
   da = (float)((double)d * (double)u * r.grad);
   db = (float)((double)d * r.act);
+}
+
+// ---------------------------------------------------------------------------------
+// gfx950 conversion instructions.  Each is used only where it was shown, on the device, to
+// equal the software encoder in this file bit for bit over its whole input domain:
+//   v_cvt_pk_bf16_f32            == bf16_rne on every non-NaN FP32 (NaN stays NaN);
+//   v_cvt_pk_fp8_f32             == e4m3_sw on every FP32 with |y| <= 448;
+//   v_cvt_scalef32_pk_fp8_bf16   == e4m3_sw(x * 2^-e) for every BF16 x and scale 2^e,
+//                                   e in [-127, 120], with |x * 2^-e| <= 448 (the scale
+//                                   operand's exponent alone is used; 2^-127 is passed as
+//                                   the FP32 subnormal 0x00400000);
+//   v_cvt_scalef32_pk_fp4_f32    == nearest-even E2M1 with saturation at scale 1.
+// ---------------------------------------------------------------------------------
+
+typedef short v2i16 __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+typedef float v2f32 __attribute__((ext_vector_type(2)));
+
+// Two FP32 values -> packed BF16 pair (lo in bits 0..15), nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  v2f32 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, v2bf16));
+}
+
+// E4M3 codes of a packed BF16 pair scaled by 2^-e (scale = 2^e as FP32), written into the
+// low (hi_word = false) or high 16 bits of `old`: low byte = lo element, high byte = hi.
+template <bool HI_WORD>
+__device__ __forceinline__ uint32_t fp8x2_scaled(uint32_t old, uint32_t bf16_pair, float scale) {
+  v2i16 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(v2i16, old),
+                                                      __builtin_bit_cast(v2bf16, bf16_pair), scale,
+                                                      HI_WORD);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// E4M3 codes of two FP32 values (|y| <= 448), into the low or high 16 bits of `old`.
+template <bool HI_WORD>
+__device__ __forceinline__ uint32_t fp8x2(uint32_t old, float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI_WORD);
+}
+
+// E2M1 codes (nearest even, saturating at 6) of two FP32 values into nibbles 2*SEL and
+// 2*SEL + 1 of `old` (SEL in 0..3).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// FP32 value of an E8M0 scale byte b (2^(b-127)); byte 0 is the subnormal 2^-127.
+__device__ __forceinline__ float e8m0_value(uint32_t b) {
+  const uint32_t f = b << 23;
+  return __uint_as_float(f > 0x00400000u ? f : 0x00400000u);
 }
 
 // ---------------------------------------------------------------------------------
@@ -220,6 +266,17 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, const E2m1Thresholds& T) 
   bool b0 = a > t0;
   uint32_t s = (__float_as_uint(x) >> 28) & 8u;
   return s | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+}
+
+// E2M1 codes of x / S for inputs with at most 16 significant bits (every BF16 value):
+// y = x * rcp(S) is within 2^-22 of x / S, which for such x either is an E2M1 tie exactly
+// or lies at least 2^-8 (relative) away from every tie; rounding y to 16 significant bits
+// therefore restores the ties without moving any other value across one, and the
+// hardware E2M1 convert (nearest even, saturating at 6) then decides exactly.  R = 0 for
+// S = 0 gives signed zeros.
+__device__ __forceinline__ float e2m1_operand(float x, float R) {
+  const uint32_t b = __float_as_uint(x * R);
+  return __uint_as_float((b + 0x80u) & 0xffffff00u);
 }
 
 // Byte offset of NVFP4 scale (r, c) in the 128x4 layout; cp = padded scale columns.

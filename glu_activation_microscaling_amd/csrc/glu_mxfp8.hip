@@ -1,16 +1,18 @@
 // Fused GLU + MXFP8 quantization, forward and backward, rowwise / colwise / both from one
 // read of the inputs ("Add swiglu + MXFP8 fused CuTe DSL kernel", Summary and API), and
-// the FP32 quantizer hook that runs the same quantize-and-store stage on given values.
+// the FP32 quantizer hook that runs the same block rules on given FP32 values.
 //
 // Work decomposition (wave64):
 //   workgroup = 4 waves = a 64-row x 128-column tile; wave w covers rows 32*(w&1) and
 //   columns 64*(w>>1) of it, i.e. one 32-row colwise block row and two 32-column rowwise
 //   blocks per row.  Lane = lr + 8*lc owns rows 4lr..4lr+3 and columns 8lc..8lc+7 of the
-//   wave tile: 16-byte loads per row and per operand, 32 elements per lane.
+//   wave tile: 16-byte loads per row and per operand, 32 elements per lane, kept after
+//   the activation as 16 packed BF16 pairs.
 //   Rowwise amax of a 32-column block spans the 4 lanes lc = 4b..4b+3 (lane bits 3, 4):
-//   DPP row_ror:8 then ds_swizzle xor 16.  Colwise amax of a 32-row block spans the
-//   8 lanes lr = 0..7 (lane bits 0..2) after an in-lane max over 4 rows: DPP quad_perm
-//   xor 1, xor 2, then row_half_mirror.  No LDS is needed: each lane already holds 4
+//   DPP row_ror:8 then ds_swizzle xor 16.  Colwise amax of a 32-row block spans the 8
+//   lanes lr = 0..7 (lane bits 0..2) after an in-lane max over 4 rows: DPP quad_perm xor 1,
+//   xor 2, then row_half_mirror.  Maxima are taken on packed 16-bit magnitudes (two
+//   columns, or two rows, per instruction).  No LDS is needed: each lane already holds 4
 //   consecutive rows of every column it owns, so colwise codes leave as 4-byte stores into
 //   the transposed [N, M] output and rowwise codes as 8-byte stores.
 //   Tiles are dealt to the 8 XCDs in contiguous runs along M (workgroups go to XCDs
@@ -26,6 +28,25 @@ constexpr int MX_THREADS = 256;
 constexpr int TILE_M = 64, TILE_N = 128;
 enum { MODE_FWD = 0, MODE_BWD = 1, MODE_F32 = 2 };
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t w) { return __builtin_bit_cast(u16x2, w); }
+__device__ __forceinline__ uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ uint32_t pkmax(uint32_t a, uint32_t b) {
+  return as_u32(__builtin_elementwise_max(as_u16x2(a), as_u16x2(b)));
+}
+// Packed E8M0 RCEIL scale bytes from packed BF16 magnitudes A = E << 7 | m of finite block
+// maxima: e + 127 = E - 8 + (m > 0x60), i.e. ((A + 0x1F) >> 7) - 8 saturated at 0.
+__device__ __forceinline__ uint32_t pk_scale_bytes(uint32_t A) {
+  const u16x2 t = (as_u16x2(A) + (u16x2){0x1f, 0x1f}) >> (u16x2){7, 7};
+  return as_u32(__builtin_elementwise_sub_sat(t, (u16x2){8, 8}));
+}
+__device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xffffu; }
+__device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
+// (a.lo, b.lo) and (a.hi, b.hi) as packed pairs
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
 struct MxOut {
   uint8_t* q_row;
   uint8_t* s_row;
@@ -35,12 +56,124 @@ struct MxOut {
   int64_t ldq;  // columns of the quantized matrix (N forward, 2N backward)
 };
 
-// Quantizes the lane's 4x8 values (rows r0 + 4lr + i, columns col + c of the quantized
-// matrix) and stores codes and scales.  All 64 lanes must call it together.
+// Quantizes the lane's 4x8 BF16 values H[i][k] = (columns 2k, 2k+1 of row r0 + 4lr + i),
+// columns starting at `col` of the quantized matrix, and stores codes and scales.  All 64
+// lanes must call it together.
 template <int FLAGS>
-__device__ __forceinline__ void mx_quant_store(const float (&v)[4][8], const MxOut& o,
-                                               int64_t r0, int64_t col, int lr, int lc,
-                                               bool col_ok) {
+__device__ __forceinline__ void mx_store_bf16(const uint32_t (&H)[4][4], const MxOut& o,
+                                              int64_t r0, int64_t col, int lr, int lc,
+                                              bool col_ok) {
+  uint32_t A[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int k = 0; k < 4; k++) A[i][k] = H[i][k] & 0x7fff7fffu;
+
+  uint32_t R01 = 0, R23 = 0;  // row block maxima, rows (0,1) and (2,3) packed
+  uint32_t C[4] = {0, 0, 0, 0};  // column block maxima, columns (2k, 2k+1) packed
+  if constexpr ((FLAGS & ROWWISE) != 0) {
+    uint32_t m[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) m[i] = pkmax(pkmax(A[i][0], A[i][1]), pkmax(A[i][2], A[i][3]));
+    R01 = pkmax(pair_lo(m[0], m[1]), pair_hi(m[0], m[1]));
+    R23 = pkmax(pair_lo(m[2], m[3]), pair_hi(m[2], m[3]));
+    R01 = pkmax(R01, dpp<DPP_ROW_ROR8>(R01));
+    R23 = pkmax(R23, dpp<DPP_ROW_ROR8>(R23));
+    R01 = pkmax(R01, swz_xor16(R01));
+    R23 = pkmax(R23, swz_xor16(R23));
+  }
+  if constexpr ((FLAGS & COLWISE) != 0) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      uint32_t c = pkmax(pkmax(A[0][k], A[1][k]), pkmax(A[2][k], A[3][k]));
+      c = pkmax(c, dpp<DPP_XOR1>(c));
+      c = pkmax(c, dpp<DPP_XOR2>(c));
+      C[k] = pkmax(c, dpp<DPP_HALF_MIRROR>(c));
+    }
+  }
+  // any non-finite block among those this lane touches? (rare: handled after the stores)
+  const uint32_t all = pkmax(pkmax(R01, R23), pkmax(pkmax(C[0], C[1]), pkmax(C[2], C[3])));
+  const bool nonfinite = umax(lo16(all), hi16(all)) >= 0x7f80u;
+
+  if constexpr ((FLAGS & ROWWISE) != 0) {
+    const uint32_t S01 = pk_scale_bytes(R01), S23 = pk_scale_bytes(R23);
+    const uint32_t sb[4] = {lo16(S01), hi16(S01), lo16(S23), hi16(S23)};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t row = r0 + 4 * lr + i;
+      if (col_ok && row < o.M) {
+        const float sc = e8m0_value(sb[i]);
+        uint32_t w0 = fp8x2_scaled<false>(0u, H[i][0], sc);
+        w0 = fp8x2_scaled<true>(w0, H[i][1], sc);
+        uint32_t w1 = fp8x2_scaled<false>(0u, H[i][2], sc);
+        w1 = fp8x2_scaled<true>(w1, H[i][3], sc);
+        *reinterpret_cast<uint2*>(o.q_row + row * o.ldq + col) = make_uint2(w0, w1);
+      }
+    }
+    // lane lc = 4b + i stores the scale of row 4lr + i in block b
+    const int i = lc & 3;
+    const int64_t row = r0 + 4 * lr + i;
+    if (col_ok && row < o.M) {
+      const uint32_t w = i < 2 ? S01 : S23;
+      o.s_row[row * (o.ldq / 32) + (col - 8 * i) / 32] = (uint8_t)((i & 1) ? hi16(w) : lo16(w));
+    }
+  }
+  if constexpr ((FLAGS & COLWISE) != 0) {
+    uint32_t S[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) S[k] = pk_scale_bytes(C[k]);
+    if (col_ok) {
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const float s0 = e8m0_value(lo16(S[k])), s1 = e8m0_value(hi16(S[k]));
+        // column 2k: rows (0,1) from the low halves, rows (2,3) likewise
+        uint32_t w0 = fp8x2_scaled<false>(0u, pair_lo(H[0][k], H[1][k]), s0);
+        w0 = fp8x2_scaled<true>(w0, pair_lo(H[2][k], H[3][k]), s0);
+        uint32_t w1 = fp8x2_scaled<false>(0u, pair_hi(H[0][k], H[1][k]), s1);
+        w1 = fp8x2_scaled<true>(w1, pair_hi(H[2][k], H[3][k]), s1);
+        uint8_t* base = o.q_col + (col + 2 * k) * o.M + r0 + 4 * lr;
+        *reinterpret_cast<uint32_t*>(base) = w0;
+        *reinterpret_cast<uint32_t*>(base + o.M) = w1;
+      }
+      // lane lr stores the scale of column 8lc + lr of this 32-row block
+      const uint32_t w = (lr >> 1) == 0 ? S[0] : (lr >> 1) == 1 ? S[1] : (lr >> 1) == 2 ? S[2] : S[3];
+      o.s_col[(col + lr) * (o.M / 32) + r0 / 32] = (uint8_t)((lr & 1) ? hi16(w) : lo16(w));
+    }
+  }
+
+  if (nonfinite) {
+    // a block holding NaN or Inf: scale 0xFF, every code 0x7F (overwrites the fast path)
+    if constexpr ((FLAGS & ROWWISE) != 0) {
+      const uint32_t rm[4] = {lo16(R01), hi16(R01), lo16(R23), hi16(R23)};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int64_t row = r0 + 4 * lr + i;
+        if (col_ok && row < o.M && rm[i] >= 0x7f80u) {
+          *reinterpret_cast<uint2*>(o.q_row + row * o.ldq + col) = make_uint2(0x7f7f7f7fu, 0x7f7f7f7fu);
+          if ((lc & 3) == i) o.s_row[row * (o.ldq / 32) + (col - 8 * i) / 32] = 0xff;
+        }
+      }
+    }
+    if constexpr ((FLAGS & COLWISE) != 0) {
+      if (col_ok) {
+#pragma unroll
+        for (int c = 0; c < 8; c++) {
+          const uint32_t cm = (c & 1) ? hi16(C[c >> 1]) : lo16(C[c >> 1]);
+          if (cm >= 0x7f80u) {
+            *reinterpret_cast<uint32_t*>(o.q_col + (col + c) * o.M + r0 + 4 * lr) = 0x7f7f7f7fu;
+            if (lr == c) o.s_col[(col + c) * (o.M / 32) + r0 / 32] = 0xff;
+          }
+        }
+      }
+    }
+  }
+}
+
+// The same rules on FP32 values (quantizer hook): magnitudes compared as FP32 bits, the
+// scaled value x * 2^-e computed exactly in FP32, then v_cvt_pk_fp8_f32.
+template <int FLAGS>
+__device__ __forceinline__ void mx_store_f32(const float (&v)[4][8], const MxOut& o, int64_t r0,
+                                             int64_t col, int lr, int lc, bool col_ok) {
   uint32_t ab[4][8];
 #pragma unroll
   for (int i = 0; i < 4; i++)
@@ -62,13 +195,14 @@ __device__ __forceinline__ void mx_quant_store(const float (&v)[4][8], const MxO
       packed |= b << (8 * i);
       const int64_t row = r0 + 4 * lr + i;
       if (col_ok && row < o.M) {
-        uint32_t w0 = e4m3x4(v[i][0] * P, v[i][1] * P, v[i][2] * P, v[i][3] * P);
-        uint32_t w1 = e4m3x4(v[i][4] * P, v[i][5] * P, v[i][6] * P, v[i][7] * P);
+        uint32_t w0 = fp8x2<false>(0u, v[i][0] * P, v[i][1] * P);
+        w0 = fp8x2<true>(w0, v[i][2] * P, v[i][3] * P);
+        uint32_t w1 = fp8x2<false>(0u, v[i][4] * P, v[i][5] * P);
+        w1 = fp8x2<true>(w1, v[i][6] * P, v[i][7] * P);
         if (nonfinite) w0 = w1 = 0x7f7f7f7fu;
         *reinterpret_cast<uint2*>(o.q_row + row * o.ldq + col) = make_uint2(w0, w1);
       }
     }
-    // lane lc = 4b + i stores the scale of row 4lr + i in block b
     const int i = lc & 3;
     const int64_t row = r0 + 4 * lr + i;
     if (col_ok && row < o.M)
@@ -88,12 +222,12 @@ __device__ __forceinline__ void mx_quant_store(const float (&v)[4][8], const MxO
       const float P = mx_inv_scale(nonfinite ? 0u : b);
       if (c < 4) packed0 |= b << (8 * c); else packed1 |= b << (8 * (c - 4));
       if (col_ok) {
-        uint32_t w = e4m3x4(v[0][c] * P, v[1][c] * P, v[2][c] * P, v[3][c] * P);
+        uint32_t w = fp8x2<false>(0u, v[0][c] * P, v[1][c] * P);
+        w = fp8x2<true>(w, v[2][c] * P, v[3][c] * P);
         if (nonfinite) w = 0x7f7f7f7fu;
         *reinterpret_cast<uint32_t*>(o.q_col + (col + c) * o.M + r0 + 4 * lr) = w;
       }
     }
-    // lane lr stores the scale of column 8lc + lr of this 32-row block
     if (col_ok) {
       const uint32_t w = lr < 4 ? packed0 : packed1;
       o.s_col[(col + lr) * (o.M / 32) + r0 / 32] = (uint8_t)(w >> (8 * (lr & 3)));
@@ -109,28 +243,58 @@ __device__ __forceinline__ Words4 ld16(const void* p) {
   return Words4{{v.x, v.y, v.z, v.w}};
 }
 
-// Gate and up of 8 consecutive outputs (BF16 widened exactly).
+// Raw operand words of 8 consecutive outputs: SPLIT gives gate and up words (each a BF16
+// pair of adjacent columns); PAIRED gives 8 words, each a (gate, up) BF16 pair.
 template <int LAYOUT>
-__device__ __forceinline__ void load_gu(const uint16_t* gate, const uint16_t* up, int64_t ld,
-                                        int64_t row, int64_t col, float g[8], float u[8]) {
+struct GU {
+  uint32_t a[LAYOUT == SPLIT ? 4 : 8];
+  uint32_t b[LAYOUT == SPLIT ? 4 : 1];
+};
+
+template <int LAYOUT>
+__device__ __forceinline__ void load_gu(GU<LAYOUT>& r, const uint16_t* gate, const uint16_t* up,
+                                        int64_t ld, int64_t row, int64_t col) {
   if constexpr (LAYOUT == SPLIT) {
     Words4 G = ld16(gate + row * ld + col), U = ld16(up + row * ld + col);
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-      g[2 * k] = bf_lo(G.w[k]);
-      g[2 * k + 1] = bf_hi(G.w[k]);
-      u[2 * k] = bf_lo(U.w[k]);
-      u[2 * k + 1] = bf_hi(U.w[k]);
+      r.a[k] = G.w[k];
+      r.b[k] = U.w[k];
     }
   } else {
     const uint16_t* p = gate + row * ld + 2 * col;
     Words4 A = ld16(p), B = ld16(p + 8);
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-      g[k] = bf_lo(A.w[k]);
-      u[k] = bf_hi(A.w[k]);
-      g[4 + k] = bf_lo(B.w[k]);
-      u[4 + k] = bf_hi(B.w[k]);
+      r.a[k] = A.w[k];
+      r.a[4 + k] = B.w[k];
+    }
+  }
+}
+
+template <int LAYOUT>
+__device__ __forceinline__ void zero_gu(GU<LAYOUT>& r) {
+#pragma unroll
+  for (auto& x : r.a) x = 0;
+#pragma unroll
+  for (auto& x : r.b) x = 0;
+}
+
+template <int LAYOUT>
+__device__ __forceinline__ void unpack_gu(const GU<LAYOUT>& r, float g[8], float u[8]) {
+  if constexpr (LAYOUT == SPLIT) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      g[2 * k] = bf_lo(r.a[k]);
+      g[2 * k + 1] = bf_hi(r.a[k]);
+      u[2 * k] = bf_lo(r.b[k]);
+      u[2 * k + 1] = bf_hi(r.b[k]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      g[k] = bf_lo(r.a[k]);
+      u[k] = bf_hi(r.a[k]);
     }
   }
 }
@@ -150,102 +314,120 @@ __global__ __launch_bounds__(MX_THREADS) void k_mxfp8(MxArgs a, int64_t tiles_m,
   const int64_t col = cw + 8 * lc;
   const bool col_ok = col < a.N;
 
-  if constexpr (MODE == MODE_FWD || MODE == MODE_F32) {
+  if constexpr (MODE == MODE_F32) {
     float v[4][8];
-    if constexpr (MODE == MODE_F32) {
-      const float* x = static_cast<const float*>(a.src);
+    const float* x = static_cast<const float*>(a.src);
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int64_t row = r0 + 4 * lr + i;
-        if (col_ok && row < a.M) {
-          const float* p = x + row * a.ld_in + col;
-          Words4 A = ld16(p), B = ld16(p + 4);
+    for (int i = 0; i < 4; i++) {
+      const int64_t row = r0 + 4 * lr + i;
+      if (col_ok && row < a.M) {
+        const float* p = x + row * a.ld_in + col;
+        Words4 A = ld16(p), B = ld16(p + 4);
 #pragma unroll
-          for (int k = 0; k < 4; k++) {
-            v[i][k] = __uint_as_float(A.w[k]);
-            v[i][4 + k] = __uint_as_float(B.w[k]);
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 8; c++) v[i][c] = 0.0f;
+        for (int k = 0; k < 4; k++) {
+          v[i][k] = __uint_as_float(A.w[k]);
+          v[i][4 + k] = __uint_as_float(B.w[k]);
         }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; c++) v[i][c] = 0.0f;
       }
-    } else {
-      const uint16_t* gate = static_cast<const uint16_t*>(a.src);
-      float g[4][8], u[4][8];
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int64_t row = r0 + 4 * lr + i;
-        if (col_ok && row < a.M) {
-          load_gu<LAYOUT>(gate, a.up, a.ld_in, row, col, g[i], u[i]);
-        } else {
-#pragma unroll
-          for (int c = 0; c < 8; c++) g[i][c] = u[i][c] = 0.0f;
-        }
-      }
-      float zmin = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int c = 0; c < 8; c++) v[i][c] = glu_fwd_elem<ACT>(g[i][c], u[i][c], zmin);
-      if (zmin < TAIL_ZL2) {
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-          for (int c = 0; c < 8; c++)
-            if (zl2<ACT>(g[i][c]) < TAIL_ZL2) v[i][c] = glu_fwd_tail<ACT>(g[i][c], u[i][c]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int c = 0; c < 8; c++) v[i][c] = round_bf16(v[i][c]);
     }
     const MxOut o{a.q_row, a.s_row, a.q_col, a.s_col, a.M, a.N};
-    mx_quant_store<FLAGS>(v, o, r0, col, lr, lc, col_ok);
-  } else {
+    mx_store_f32<FLAGS>(v, o, r0, col, lr, lc, col_ok);
+  } else if constexpr (MODE == MODE_FWD) {
     const uint16_t* gate = static_cast<const uint16_t*>(a.src);
-    float va[4][8], vb[4][8];
-    {
-      float g[4][8], u[4][8], d[4][8];
+    GU<LAYOUT> in[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t row = r0 + 4 * lr + i;
+      if (col_ok && row < a.M) load_gu<LAYOUT>(in[i], gate, a.up, a.ld_in, row, col);
+      else zero_gu<LAYOUT>(in[i]);
+    }
+    uint32_t H[4][4];
+    float zmin = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      float g[8], u[8], h[8];
+      unpack_gu<LAYOUT>(in[i], g, u);
+#pragma unroll
+      for (int c = 0; c < 8; c++) h[c] = glu_fwd_elem<ACT>(g[c], u[c], zmin);
+#pragma unroll
+      for (int k = 0; k < 4; k++) H[i][k] = pack_bf16(h[2 * k], h[2 * k + 1]);
+    }
+    if (zmin < TAIL_ZL2) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const int64_t row = r0 + 4 * lr + i;
-        if (col_ok && row < a.M) {
-          load_gu<SPLIT>(gate, a.up, a.ld_in, row, col, g[i], u[i]);
-          Words4 D = ld16(a.dh + row * a.ld_dh + col);
+        float g[8], u[8];
+        unpack_gu<LAYOUT>(in[i], g, u);
 #pragma unroll
-          for (int k = 0; k < 4; k++) {
-            d[i][2 * k] = bf_lo(D.w[k]);
-            d[i][2 * k + 1] = bf_hi(D.w[k]);
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 8; c++) g[i][c] = u[i][c] = d[i][c] = 0.0f;
+        for (int k = 0; k < 4; k++) {
+          float h0 = bf_lo(H[i][k]), h1 = bf_hi(H[i][k]);
+          if (zl2<ACT>(g[2 * k]) < TAIL_ZL2) h0 = glu_fwd_tail<ACT>(g[2 * k], u[2 * k]);
+          if (zl2<ACT>(g[2 * k + 1]) < TAIL_ZL2) h1 = glu_fwd_tail<ACT>(g[2 * k + 1], u[2 * k + 1]);
+          H[i][k] = pack_bf16(h0, h1);
         }
       }
-      float zmin = 0.0f;
+    }
+    const MxOut o{a.q_row, a.s_row, a.q_col, a.s_col, a.M, a.N};
+    mx_store_bf16<FLAGS>(H, o, r0, col, lr, lc, col_ok);
+  } else {
+    const uint16_t* gate = static_cast<const uint16_t*>(a.src);
+    GU<SPLIT> in[4];
+    uint32_t D[4][4];
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 4; i++) {
+      const int64_t row = r0 + 4 * lr + i;
+      if (col_ok && row < a.M) {
+        load_gu<SPLIT>(in[i], gate, a.up, a.ld_in, row, col);
+        Words4 d = ld16(a.dh + row * a.ld_dh + col);
 #pragma unroll
-        for (int c = 0; c < 8; c++) glu_bwd_elem<ACT>(g[i][c], u[i][c], d[i][c], va[i][c], vb[i][c], zmin);
-      if (zmin < TAIL_ZL2) {
+        for (int k = 0; k < 4; k++) D[i][k] = d.w[k];
+      } else {
+        zero_gu<SPLIT>(in[i]);
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int k = 0; k < 4; k++) D[i][k] = 0;
+      }
+    }
+    uint32_t HA[4][4], HB[4][4];
+    float zmin = 0.0f;
 #pragma unroll
-          for (int c = 0; c < 8; c++)
-            if (zl2<ACT>(g[i][c]) < TAIL_ZL2) glu_bwd_tail<ACT>(g[i][c], u[i][c], d[i][c], va[i][c], vb[i][c]);
+    for (int i = 0; i < 4; i++) {
+      float g[8], u[8], da[8], db[8];
+      unpack_gu<SPLIT>(in[i], g, u);
+#pragma unroll
+      for (int c = 0; c < 8; c++) {
+        const float d = (c & 1) ? bf_hi(D[i][c >> 1]) : bf_lo(D[i][c >> 1]);
+        glu_bwd_elem<ACT>(g[c], u[c], d, da[c], db[c], zmin);
       }
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int k = 0; k < 4; k++) {
+        HA[i][k] = pack_bf16(da[2 * k], da[2 * k + 1]);
+        HB[i][k] = pack_bf16(db[2 * k], db[2 * k + 1]);
+      }
+    }
+    if (zmin < TAIL_ZL2) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        float g[8], u[8];
+        unpack_gu<SPLIT>(in[i], g, u);
 #pragma unroll
         for (int c = 0; c < 8; c++) {
-          va[i][c] = round_bf16(va[i][c]);
-          vb[i][c] = round_bf16(vb[i][c]);
+          if (zl2<ACT>(g[c]) < TAIL_ZL2) {
+            const float d = (c & 1) ? bf_hi(D[i][c >> 1]) : bf_lo(D[i][c >> 1]);
+            float da, db;
+            glu_bwd_tail<ACT>(g[c], u[c], d, da, db);
+            const uint32_t ra = pack_bf16(da, da) & 0xffffu, rb = pack_bf16(db, db) & 0xffffu;
+            const int k = c >> 1, sh = 16 * (c & 1);
+            HA[i][k] = (HA[i][k] & ~(0xffffu << sh)) | (ra << sh);
+            HB[i][k] = (HB[i][k] & ~(0xffffu << sh)) | (rb << sh);
+          }
         }
+      }
     }
     const MxOut o{a.q_row, a.s_row, a.q_col, a.s_col, a.M, 2 * a.N};
-    mx_quant_store<FLAGS>(va, o, r0, col, lr, lc, col_ok);
-    mx_quant_store<FLAGS>(vb, o, r0, a.N + col, lr, lc, col_ok);
+    mx_store_bf16<FLAGS>(HA, o, r0, col, lr, lc, col_ok);
+    mx_store_bf16<FLAGS>(HB, o, r0, a.N + col, lr, lc, col_ok);
   }
 }
 

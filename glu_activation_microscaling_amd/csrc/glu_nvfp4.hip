@@ -80,7 +80,11 @@ __global__ __launch_bounds__(NV_THREADS) void k_nvfp4(NvArgs a, int64_t tiles_pe
             if (zl2<ACT>(g[k]) < TAIL_ZL2) v[k] = glu_fwd_tail<ACT>(g[k], u[k]);
         }
 #pragma unroll
-        for (int k = 0; k < 8; k++) v[k] = round_bf16(v[k]);
+        for (int k = 0; k < 4; k++) {
+          const uint32_t p = pack_bf16(v[2 * k], v[2 * k + 1]);
+          v[2 * k] = bf_lo(p);
+          v[2 * k + 1] = bf_hi(p);
+        }
       }
     } else {
 #pragma unroll
@@ -95,12 +99,23 @@ __global__ __launch_bounds__(NV_THREADS) void k_nvfp4(NvArgs a, int64_t tiles_pe
 
     const bool nonfinite = m >= 0x7f800000u;
     const uint32_t sc = nonfinite ? 0x7fu : nv_scale_code(__uint_as_float(m));
-    const E2m1Thresholds T = e2m1_thresholds(e4m3_value(nonfinite ? 0u : sc));
 
     if (live) {
       uint32_t word = 0;
+      const float S = e4m3_value(nonfinite ? 0u : sc);
+      if constexpr (F32) {
+        // any FP32 value: exact threshold comparisons
+        const E2m1Thresholds T = e2m1_thresholds(S);
 #pragma unroll
-      for (int k = 0; k < 8; k++) word |= e2m1_code(v[k], T) << (4 * k);
+        for (int k = 0; k < 8; k++) word |= e2m1_code(v[k], T) << (4 * k);
+      } else {
+        // BF16 values: scaled operand + hardware convert
+        const float R = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
+        word = fp4x2<0>(word, e2m1_operand(v[0], R), e2m1_operand(v[1], R));
+        word = fp4x2<1>(word, e2m1_operand(v[2], R), e2m1_operand(v[3], R));
+        word = fp4x2<2>(word, e2m1_operand(v[4], R), e2m1_operand(v[5], R));
+        word = fp4x2<3>(word, e2m1_operand(v[6], R), e2m1_operand(v[7], R));
+      }
       if (nonfinite) word = 0;
       *reinterpret_cast<uint32_t*>(a.q + row * (a.H / 2) + j / 2) = word;
     }
