@@ -21,6 +21,8 @@ using glu::BF16Args;
 using glu::MxArgs;
 using glu::NvArgs;
 
+// Upper bound on MXFP8 tiles per launch (counted with the smallest tile, 32 x 64), so the
+// tile index and the workgroup count stay within 32 bits.
 constexpr int64_t kMaxTiles = (int64_t)1 << 30;
 
 // Byte extent of a row-major matrix: ((rows - 1) * ld + cols) * esz, or -1 on overflow.
@@ -216,7 +218,7 @@ glu_status glu_check_fwd_mxfp8(int act, int layout, int64_t M, int64_t N, const 
                 QR = mat(q_row, M, N, N, 1), SR = mat(s_row, M, N / 32, N / 32, 1),
                 QC = mat(q_col, N, M, M, 1), SC = mat(s_col, N, M / 32, M / 32, 1);
   if (any_overflow({G, U, QR, SR, QC, SC})) return GLU_ERR_SHAPE;
-  if (((M + 63) / 64) * ((N + 127) / 128) > kMaxTiles) return GLU_ERR_SHAPE;
+  if (((M + 31) / 32) * ((N + 63) / 64) > kMaxTiles) return GLU_ERR_SHAPE;
   return check_no_overlap({QR, SR, QC, SC}, {G, U});
 }
 
@@ -245,7 +247,7 @@ glu_status glu_check_bwd_mxfp8(int act, int layout, int64_t M, int64_t N, const 
                 SR = mat(s_row, M, N2 / 32, N2 / 32, 1), QC = mat(q_col, N2, M, M, 1),
                 SC = mat(s_col, N2, M / 32, M / 32, 1);
   if (any_overflow({G, U, D, QR, SR, QC, SC})) return GLU_ERR_SHAPE;
-  if (((M + 63) / 64) * ((N + 127) / 128) > kMaxTiles) return GLU_ERR_SHAPE;
+  if (((M + 31) / 32) * ((N + 63) / 64) > kMaxTiles) return GLU_ERR_SHAPE;
   return check_no_overlap({QR, SR, QC, SC}, {G, U, D});
 }
 
@@ -289,7 +291,7 @@ glu_status glu_check_quant_mxfp8_f32(int64_t M, int64_t N, const float* x, int64
                 SR = mat(s_row, M, N / 32, N / 32, 1), QC = mat(q_col, N, M, M, 1),
                 SC = mat(s_col, N, M / 32, M / 32, 1);
   if (any_overflow({X, QR, SR, QC, SC})) return GLU_ERR_SHAPE;
-  if (((M + 63) / 64) * ((N + 127) / 128) > kMaxTiles) return GLU_ERR_SHAPE;
+  if (((M + 31) / 32) * ((N + 63) / 64) > kMaxTiles) return GLU_ERR_SHAPE;
   return check_no_overlap({QR, SR, QC, SC}, {X});
 }
 

@@ -43,7 +43,7 @@ __device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(bf
 // (tanh-GELU: x/2 (1 + tanh(u)) = x sigma(2u)).  act'(x) = sigma(z) (1 + x sigma(-z) z'(x)).
 // The fast path uses the hardware exp2 and reciprocal and is accurate while
 // z * log2(e) >= TAIL_ZL2; below that e^z leaves the FP32 normal range and the caller
-// recomputes the element in FP64 (act_tail_f64), which is rare and wave-divergent.
+// recomputes the element on the tail path, which is rare and wave-divergent.
 // ---------------------------------------------------------------------------------
 
 constexpr float LOG2E = 1.44269504088896340736f;
@@ -82,18 +82,14 @@ __device__ __forceinline__ float dz(float x) {
   }
 }
 
-// Tail path in FP64: act(x) and act'(x) for z(x) far below zero (returned in registers).
-struct ActF64 {
-  double act, grad;
-};
-
-template <int ACT>
-__device__ __noinline__ ActF64 act_tail_f64(double x) {
-  double z = (ACT == SWIGLU) ? x : 2.0 * GELU_K0 * (x + GELU_K1 * x * x * x);
-  double sp = 1.0 / (1.0 + exp(-z));
-  double sn = 1.0 / (1.0 + exp(z));
-  double d = (ACT == SWIGLU) ? 1.0 : 2.0 * GELU_K0 * (1.0 + 3.0 * GELU_K1 * x * x);
-  return ActF64{x * sp, sp * (1.0 + x * sn * d)};
+// Tail path, z log2(e) = zl < TAIL_ZL2: e^z = 2^zl is below the FP32 normal range, so it
+// is formed in FP64 as exp2(f) * 2^n with n = floor(zl), f = zl - n (exact), and the
+// products are taken in FP64 (no intermediate overflow or underflow).  There 1 + e^z == 1,
+// so sigma(z) = e^z and sigma(-z) = 1.  zl is clamped where e^z is 0 in FP64 anyway.
+__device__ __forceinline__ double exp2_tail(float zl) {
+  const float zc = __builtin_fmaxf(zl, -1100.0f);
+  const float n = __builtin_floorf(zc);
+  return __builtin_ldexp((double)__builtin_amdgcn_exp2f(zc - n), (int)n);
 }
 
 // Forward: act(g) * u in FP32 (the caller rounds it to BF16).
@@ -106,7 +102,7 @@ __device__ __forceinline__ float glu_fwd_elem(float g, float u, float& zmin) {
 
 template <int ACT>
 __device__ __forceinline__ float glu_fwd_tail(float g, float u) {
-  return (float)(act_tail_f64<ACT>((double)g).act * (double)u);
+  return (float)((double)g * exp2_tail(zl2<ACT>(g)) * (double)u);
 }
 
 // Backward: da = dh u act'(g), db = dh act(g), FP32 before rounding.
@@ -125,9 +121,10 @@ __device__ __forceinline__ void glu_bwd_elem(float g, float u, float d, float& d
 
 template <int ACT>
 __device__ __forceinline__ void glu_bwd_tail(float g, float u, float d, float& da, float& db) {
-  const ActF64 r = act_tail_f64<ACT>((double)g);
-  da = (float)((double)d * (double)u * r.grad);
-  db = (float)((double)d * r.act);
+  const double t = exp2_tail(zl2<ACT>(g));
+  const double gd = (double)g;
+  da = (float)((double)d * (double)u * t * (1.0 + gd * (double)dz<ACT>(g)));
+  db = (float)((double)d * gd * t);
 }
 
 // ---------------------------------------------------------------------------------

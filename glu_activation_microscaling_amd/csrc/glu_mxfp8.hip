@@ -24,8 +24,43 @@
 namespace glu {
 namespace {
 
-constexpr int MX_THREADS = 256;
-constexpr int TILE_M = 64, TILE_N = 128;
+// Waves per workgroup along M and N (each wave covers 32 rows x 64 columns), chosen per
+// direction from measurements on MI355X at [16384, 7168]: rowwise-only output is fastest
+// with 64 x 128 tiles; whenever transposed colwise codes are written (or two matrices are
+// quantized, in backward), wider 64 x 256 tiles win.
+template <int MODE, int FLAGS>
+struct WgShape {
+  static constexpr int M = 2;
+  static constexpr int N = (MODE == 0 && FLAGS == 1) ? 2 : 4;
+};
+
+// Build-time tuning (fixed defaults; alternatives are compiled only to measure them):
+//   GLU_MX_TILE_ORDER 0: each XCD takes a contiguous run of tiles in M-fastest order;
+//                     1: each XCD takes a contiguous run of tiles in N-fastest order;
+//                     2: tiles in workgroup-id order, N fastest (no XCD remapping).
+//   GLU_MX_NT_LOADS / GLU_MX_NT_STORES: non-temporal (streaming) operand loads / code stores.
+#ifndef GLU_MX_TILE_ORDER
+#define GLU_MX_TILE_ORDER 0
+#endif
+#ifndef GLU_MX_NT_LOADS
+#define GLU_MX_NT_LOADS 1
+#endif
+#ifndef GLU_MX_NT_STORES
+#define GLU_MX_NT_STORES 0
+#endif
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void st_code(uint32_t* p, uint32_t v) {
+  if constexpr (GLU_MX_NT_STORES) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+__device__ __forceinline__ void st_code(uint2* p, uint2 v) {
+  const u32x2 x = {v.x, v.y};
+  if constexpr (GLU_MX_NT_STORES) __builtin_nontemporal_store(x, reinterpret_cast<u32x2*>(p));
+  else *reinterpret_cast<u32x2*>(p) = x;
+}
 enum { MODE_FWD = 0, MODE_BWD = 1, MODE_F32 = 2 };
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -58,8 +93,10 @@ struct MxOut {
 
 // Quantizes the lane's 4x8 BF16 values H[i][k] = (columns 2k, 2k+1 of row r0 + 4lr + i),
 // columns starting at `col` of the quantized matrix, and stores codes and scales.  All 64
-// lanes must call it together.
-template <int FLAGS>
+// lanes must call it together.  FULL: the wave's 32 rows and 64 columns are all in range
+// (no per-row or per-column guards); otherwise rows >= M and columns >= the matrix width
+// are skipped.
+template <int FLAGS, bool FULL>
 __device__ __forceinline__ void mx_store_bf16(const uint32_t (&H)[4][4], const MxOut& o,
                                               int64_t r0, int64_t col, int lr, int lc,
                                               bool col_ok) {
@@ -95,34 +132,38 @@ __device__ __forceinline__ void mx_store_bf16(const uint32_t (&H)[4][4], const M
   const uint32_t all = pkmax(pkmax(R01, R23), pkmax(pkmax(C[0], C[1]), pkmax(C[2], C[3])));
   const bool nonfinite = umax(lo16(all), hi16(all)) >= 0x7f80u;
 
+  const int64_t row0 = r0 + 4 * lr;
+  const int64_t nb_row = o.ldq / 32, nb_col = o.M / 32;
+  const bool lane_ok = FULL || col_ok;
   if constexpr ((FLAGS & ROWWISE) != 0) {
     const uint32_t S01 = pk_scale_bytes(R01), S23 = pk_scale_bytes(R23);
     const uint32_t sb[4] = {lo16(S01), hi16(S01), lo16(S23), hi16(S23)};
+    uint8_t* q = o.q_row + row0 * o.ldq + col;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int64_t row = r0 + 4 * lr + i;
-      if (col_ok && row < o.M) {
+      if (FULL || (col_ok && row0 + i < o.M)) {
         const float sc = e8m0_value(sb[i]);
         uint32_t w0 = fp8x2_scaled<false>(0u, H[i][0], sc);
         w0 = fp8x2_scaled<true>(w0, H[i][1], sc);
         uint32_t w1 = fp8x2_scaled<false>(0u, H[i][2], sc);
         w1 = fp8x2_scaled<true>(w1, H[i][3], sc);
-        *reinterpret_cast<uint2*>(o.q_row + row * o.ldq + col) = make_uint2(w0, w1);
+        st_code(reinterpret_cast<uint2*>(q), make_uint2(w0, w1));
       }
+      q += o.ldq;
     }
     // lane lc = 4b + i stores the scale of row 4lr + i in block b
     const int i = lc & 3;
-    const int64_t row = r0 + 4 * lr + i;
-    if (col_ok && row < o.M) {
+    if (FULL || (col_ok && row0 + i < o.M)) {
       const uint32_t w = i < 2 ? S01 : S23;
-      o.s_row[row * (o.ldq / 32) + (col - 8 * i) / 32] = (uint8_t)((i & 1) ? hi16(w) : lo16(w));
+      o.s_row[(row0 + i) * nb_row + ((col - 8 * i) >> 5)] = (uint8_t)((i & 1) ? hi16(w) : lo16(w));
     }
   }
   if constexpr ((FLAGS & COLWISE) != 0) {
     uint32_t S[4];
 #pragma unroll
     for (int k = 0; k < 4; k++) S[k] = pk_scale_bytes(C[k]);
-    if (col_ok) {
+    if (lane_ok) {
+      uint8_t* q = o.q_col + col * o.M + row0;
 #pragma unroll
       for (int k = 0; k < 4; k++) {
         const float s0 = e8m0_value(lo16(S[k])), s1 = e8m0_value(hi16(S[k]));
@@ -131,13 +172,13 @@ __device__ __forceinline__ void mx_store_bf16(const uint32_t (&H)[4][4], const M
         w0 = fp8x2_scaled<true>(w0, pair_lo(H[2][k], H[3][k]), s0);
         uint32_t w1 = fp8x2_scaled<false>(0u, pair_hi(H[0][k], H[1][k]), s1);
         w1 = fp8x2_scaled<true>(w1, pair_hi(H[2][k], H[3][k]), s1);
-        uint8_t* base = o.q_col + (col + 2 * k) * o.M + r0 + 4 * lr;
-        *reinterpret_cast<uint32_t*>(base) = w0;
-        *reinterpret_cast<uint32_t*>(base + o.M) = w1;
+        st_code(reinterpret_cast<uint32_t*>(q), w0);
+        st_code(reinterpret_cast<uint32_t*>(q + o.M), w1);
+        q += 2 * o.M;
       }
       // lane lr stores the scale of column 8lc + lr of this 32-row block
       const uint32_t w = (lr >> 1) == 0 ? S[0] : (lr >> 1) == 1 ? S[1] : (lr >> 1) == 2 ? S[2] : S[3];
-      o.s_col[(col + lr) * (o.M / 32) + r0 / 32] = (uint8_t)((lr & 1) ? hi16(w) : lo16(w));
+      o.s_col[(col + lr) * nb_col + (r0 >> 5)] = (uint8_t)((lr & 1) ? hi16(w) : lo16(w));
     }
   }
 
@@ -147,10 +188,10 @@ __device__ __forceinline__ void mx_store_bf16(const uint32_t (&H)[4][4], const M
       const uint32_t rm[4] = {lo16(R01), hi16(R01), lo16(R23), hi16(R23)};
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const int64_t row = r0 + 4 * lr + i;
+        const int64_t row = row0 + i;
         if (col_ok && row < o.M && rm[i] >= 0x7f80u) {
           *reinterpret_cast<uint2*>(o.q_row + row * o.ldq + col) = make_uint2(0x7f7f7f7fu, 0x7f7f7f7fu);
-          if ((lc & 3) == i) o.s_row[row * (o.ldq / 32) + (col - 8 * i) / 32] = 0xff;
+          if ((lc & 3) == i) o.s_row[row * nb_row + ((col - 8 * i) >> 5)] = 0xff;
         }
       }
     }
@@ -160,8 +201,8 @@ __device__ __forceinline__ void mx_store_bf16(const uint32_t (&H)[4][4], const M
         for (int c = 0; c < 8; c++) {
           const uint32_t cm = (c & 1) ? hi16(C[c >> 1]) : lo16(C[c >> 1]);
           if (cm >= 0x7f80u) {
-            *reinterpret_cast<uint32_t*>(o.q_col + (col + c) * o.M + r0 + 4 * lr) = 0x7f7f7f7fu;
-            if (lr == c) o.s_col[(col + c) * (o.M / 32) + r0 / 32] = 0xff;
+            *reinterpret_cast<uint32_t*>(o.q_col + (col + c) * o.M + row0) = 0x7f7f7f7fu;
+            if (lr == c) o.s_col[(col + c) * nb_col + (r0 >> 5)] = 0xff;
           }
         }
       }
@@ -235,14 +276,6 @@ __device__ __forceinline__ void mx_store_f32(const float (&v)[4][8], const MxOut
   }
 }
 
-struct Words4 {
-  uint32_t w[4];
-};
-__device__ __forceinline__ Words4 ld16(const void* p) {
-  uint4 v = *reinterpret_cast<const uint4*>(p);
-  return Words4{{v.x, v.y, v.z, v.w}};
-}
-
 // Raw operand words of 8 consecutive outputs: SPLIT gives gate and up words (each a BF16
 // pair of adjacent columns); PAIRED gives 8 words, each a (gate, up) BF16 pair.
 template <int LAYOUT>
@@ -250,35 +283,6 @@ struct GU {
   uint32_t a[LAYOUT == SPLIT ? 4 : 8];
   uint32_t b[LAYOUT == SPLIT ? 4 : 1];
 };
-
-template <int LAYOUT>
-__device__ __forceinline__ void load_gu(GU<LAYOUT>& r, const uint16_t* gate, const uint16_t* up,
-                                        int64_t ld, int64_t row, int64_t col) {
-  if constexpr (LAYOUT == SPLIT) {
-    Words4 G = ld16(gate + row * ld + col), U = ld16(up + row * ld + col);
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      r.a[k] = G.w[k];
-      r.b[k] = U.w[k];
-    }
-  } else {
-    const uint16_t* p = gate + row * ld + 2 * col;
-    Words4 A = ld16(p), B = ld16(p + 8);
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      r.a[k] = A.w[k];
-      r.a[4 + k] = B.w[k];
-    }
-  }
-}
-
-template <int LAYOUT>
-__device__ __forceinline__ void zero_gu(GU<LAYOUT>& r) {
-#pragma unroll
-  for (auto& x : r.a) x = 0;
-#pragma unroll
-  for (auto& x : r.b) x = 0;
-}
 
 template <int LAYOUT>
 __device__ __forceinline__ void unpack_gu(const GU<LAYOUT>& r, float g[8], float u[8]) {
@@ -299,51 +303,66 @@ __device__ __forceinline__ void unpack_gu(const GU<LAYOUT>& r, float g[8], float
   }
 }
 
-template <int ACT, int LAYOUT, int FLAGS, int MODE>
-__global__ __launch_bounds__(MX_THREADS) void k_mxfp8(MxArgs a, int64_t tiles_m, int64_t ntiles,
-                                                      int64_t per_xcd) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int lr = lane & 7, lc = lane >> 3;
-  const int64_t b = blockIdx.x;
-  const int64_t t = (b & 7) * per_xcd + (b >> 3);
-  if (t >= ntiles) return;
-  const int64_t tm = t % tiles_m, tn = t / tiles_m;
-  const int64_t r0 = tm * TILE_M + 32 * (w & 1);
-  const int64_t cw = tn * TILE_N + 64 * (w >> 1);
-  if (r0 >= a.M || cw >= a.N) return;  // wave-uniform
-  const int64_t col = cw + 8 * lc;
-  const bool col_ok = col < a.N;
+// 16 bytes at p, or zeros when !ok (a value select, so the operands stay in registers).
+__device__ __forceinline__ uint4 ld16_if(const void* p, bool ok) {
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (ok) {
+    u32x4 x;
+    if constexpr (GLU_MX_NT_LOADS) x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else x = *reinterpret_cast<const u32x4*>(p);
+    v = make_uint4(x.x, x.y, x.z, x.w);
+  }
+  return v;
+}
 
+// Loads the lane's 4 rows of operands.  FULL: every row and column in range.
+template <int LAYOUT, bool FULL>
+__device__ __forceinline__ void load_rows(GU<LAYOUT> (&in)[4], const uint16_t* gate,
+                                          const uint16_t* up, int64_t ld, int64_t row0,
+                                          int64_t col, int64_t M, bool col_ok) {
+  const int64_t off = row0 * ld + (LAYOUT == PAIRED ? 2 * col : col);
+  const uint16_t* g = gate + off;
+  const uint16_t* u = LAYOUT == SPLIT ? up + off : nullptr;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const bool ok = FULL || (col_ok && row0 + i < M);
+    if constexpr (LAYOUT == SPLIT) {
+      const uint4 G = ld16_if(g, ok), U = ld16_if(u, ok);
+      in[i].a[0] = G.x; in[i].a[1] = G.y; in[i].a[2] = G.z; in[i].a[3] = G.w;
+      in[i].b[0] = U.x; in[i].b[1] = U.y; in[i].b[2] = U.z; in[i].b[3] = U.w;
+      u += ld;
+    } else {
+      const uint4 A = ld16_if(g, ok), B = ld16_if(g + 8, ok);
+      in[i].a[0] = A.x; in[i].a[1] = A.y; in[i].a[2] = A.z; in[i].a[3] = A.w;
+      in[i].a[4] = B.x; in[i].a[5] = B.y; in[i].a[6] = B.z; in[i].a[7] = B.w;
+    }
+    g += ld;
+  }
+}
+
+template <int ACT, int LAYOUT, int FLAGS, int MODE, bool FULL>
+__device__ __forceinline__ void mx_tile(const MxArgs& a, int64_t r0, int64_t col, int lr, int lc,
+                                        bool col_ok) {
+  const int64_t row0 = r0 + 4 * lr;
   if constexpr (MODE == MODE_F32) {
     float v[4][8];
-    const float* x = static_cast<const float*>(a.src);
+    const float* x = static_cast<const float*>(a.src) + row0 * a.ld_in + col;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int64_t row = r0 + 4 * lr + i;
-      if (col_ok && row < a.M) {
-        const float* p = x + row * a.ld_in + col;
-        Words4 A = ld16(p), B = ld16(p + 4);
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-          v[i][k] = __uint_as_float(A.w[k]);
-          v[i][4 + k] = __uint_as_float(B.w[k]);
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; c++) v[i][c] = 0.0f;
-      }
+      const bool ok = FULL || (col_ok && row0 + i < a.M);
+      const uint4 A = ld16_if(x, ok), B = ld16_if(x + 4, ok);
+      v[i][0] = __uint_as_float(A.x); v[i][1] = __uint_as_float(A.y);
+      v[i][2] = __uint_as_float(A.z); v[i][3] = __uint_as_float(A.w);
+      v[i][4] = __uint_as_float(B.x); v[i][5] = __uint_as_float(B.y);
+      v[i][6] = __uint_as_float(B.z); v[i][7] = __uint_as_float(B.w);
+      x += a.ld_in;
     }
     const MxOut o{a.q_row, a.s_row, a.q_col, a.s_col, a.M, a.N};
     mx_store_f32<FLAGS>(v, o, r0, col, lr, lc, col_ok);
   } else if constexpr (MODE == MODE_FWD) {
-    const uint16_t* gate = static_cast<const uint16_t*>(a.src);
     GU<LAYOUT> in[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int64_t row = r0 + 4 * lr + i;
-      if (col_ok && row < a.M) load_gu<LAYOUT>(in[i], gate, a.up, a.ld_in, row, col);
-      else zero_gu<LAYOUT>(in[i]);
-    }
+    load_rows<LAYOUT, FULL>(in, static_cast<const uint16_t*>(a.src), a.up, a.ld_in, row0, col, a.M,
+                            col_ok);
     uint32_t H[4][4];
     float zmin = 0.0f;
 #pragma unroll
@@ -370,24 +389,18 @@ __global__ __launch_bounds__(MX_THREADS) void k_mxfp8(MxArgs a, int64_t tiles_m,
       }
     }
     const MxOut o{a.q_row, a.s_row, a.q_col, a.s_col, a.M, a.N};
-    mx_store_bf16<FLAGS>(H, o, r0, col, lr, lc, col_ok);
+    mx_store_bf16<FLAGS, FULL>(H, o, r0, col, lr, lc, col_ok);
   } else {
-    const uint16_t* gate = static_cast<const uint16_t*>(a.src);
     GU<SPLIT> in[4];
+    load_rows<SPLIT, FULL>(in, static_cast<const uint16_t*>(a.src), a.up, a.ld_in, row0, col, a.M,
+                           col_ok);
     uint32_t D[4][4];
+    const uint16_t* dp = a.dh + row0 * a.ld_dh + col;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int64_t row = r0 + 4 * lr + i;
-      if (col_ok && row < a.M) {
-        load_gu<SPLIT>(in[i], gate, a.up, a.ld_in, row, col);
-        Words4 d = ld16(a.dh + row * a.ld_dh + col);
-#pragma unroll
-        for (int k = 0; k < 4; k++) D[i][k] = d.w[k];
-      } else {
-        zero_gu<SPLIT>(in[i]);
-#pragma unroll
-        for (int k = 0; k < 4; k++) D[i][k] = 0;
-      }
+      const uint4 d = ld16_if(dp, FULL || (col_ok && row0 + i < a.M));
+      D[i][0] = d.x; D[i][1] = d.y; D[i][2] = d.z; D[i][3] = d.w;
+      dp += a.ld_dh;
     }
     uint32_t HA[4][4], HB[4][4];
     float zmin = 0.0f;
@@ -426,20 +439,51 @@ __global__ __launch_bounds__(MX_THREADS) void k_mxfp8(MxArgs a, int64_t tiles_m,
       }
     }
     const MxOut o{a.q_row, a.s_row, a.q_col, a.s_col, a.M, 2 * a.N};
-    mx_store_bf16<FLAGS>(HA, o, r0, col, lr, lc, col_ok);
-    mx_store_bf16<FLAGS>(HB, o, r0, a.N + col, lr, lc, col_ok);
+    mx_store_bf16<FLAGS, FULL>(HA, o, r0, col, lr, lc, col_ok);
+    mx_store_bf16<FLAGS, FULL>(HB, o, r0, a.N + col, lr, lc, col_ok);
   }
+}
+
+template <int ACT, int LAYOUT, int FLAGS, int MODE, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_mxfp8(MxArgs a, uint32_t tiles_m,
+                                                          uint32_t ntiles, uint32_t per_xcd) {
+  constexpr int TILE_M = 32 * WGM, TILE_N = 64 * WGN;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane & 7, lc = lane >> 3;
+  const uint32_t b = blockIdx.x;
+  const uint32_t t = GLU_MX_TILE_ORDER == 2 ? b : (b & 7) * per_xcd + (b >> 3);
+  if (t >= ntiles) return;
+  uint32_t tm, tn;
+  if constexpr (GLU_MX_TILE_ORDER == 0) {
+    tn = t / tiles_m;
+    tm = t - tn * tiles_m;
+  } else {
+    const uint32_t tiles_n = ntiles / tiles_m;
+    tm = t / tiles_n;
+    tn = t - tm * tiles_n;
+  }
+  const int64_t r0 = (int64_t)tm * TILE_M + 32 * (w % WGM);
+  const int64_t cw = (int64_t)tn * TILE_N + 64 * (w / WGM);
+  if (r0 >= a.M || cw >= a.N) return;  // wave-uniform
+  const int64_t col = cw + 8 * lc;
+  const bool col_ok = col < a.N;
+  if (r0 + 32 <= a.M && cw + 64 <= a.N)  // wave-uniform
+    mx_tile<ACT, LAYOUT, FLAGS, MODE, true>(a, r0, col, lr, lc, col_ok);
+  else
+    mx_tile<ACT, LAYOUT, FLAGS, MODE, false>(a, r0, col, lr, lc, col_ok);
 }
 
 template <int ACT, int LAYOUT, int FLAGS, int MODE>
 hipError_t launch(const MxArgs& a, hipStream_t s) {
+  constexpr int WGM = WgShape<MODE, FLAGS>::M, WGN = WgShape<MODE, FLAGS>::N;
+  constexpr int TILE_M = 32 * WGM, TILE_N = 64 * WGN;
   const int64_t tiles_m = (a.M + TILE_M - 1) / TILE_M;
   const int64_t tiles_n = (a.N + TILE_N - 1) / TILE_N;
   const int64_t ntiles = tiles_m * tiles_n;
   const int64_t per_xcd = (ntiles + 7) / 8;
-  const dim3 grid((unsigned)(8 * per_xcd)), block(MX_THREADS);
-  return launch_kernel(k_mxfp8<ACT, LAYOUT, FLAGS, MODE>, grid, block, s, a, tiles_m, ntiles,
-                       per_xcd);
+  const dim3 grid((unsigned)(8 * per_xcd)), block(64 * WGM * WGN);
+  return launch_kernel(k_mxfp8<ACT, LAYOUT, FLAGS, MODE, WGM, WGN>, grid, block, s, a,
+                       (uint32_t)tiles_m, (uint32_t)ntiles, (uint32_t)per_xcd);
 }
 
 template <int ACT, int LAYOUT, int MODE>
