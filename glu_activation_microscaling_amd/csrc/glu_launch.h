@@ -61,15 +61,21 @@ hipError_t launch_quant_nvfp4_f32(const NvArgs& a, hipStream_t s);
 // Launches kernel k and returns the launch status of this call alone (the HIP error
 // state left by earlier, unrelated calls is not consulted).
 template <typename... KArgs, typename... Ts>
-hipError_t launch_kernel(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
-                         Ts&&... ts) {
+hipError_t launch_kernel_shm(void (*k)(KArgs...), dim3 grid, dim3 block, size_t shm,
+                             hipStream_t s, Ts&&... ts) {
   std::tuple<KArgs...> args(static_cast<KArgs>(ts)...);
   return std::apply(
       [&](auto&... xs) {
         void* argv[] = {(void*)&xs...};
-        return hipLaunchKernel((const void*)k, grid, block, argv, 0, s);
+        return hipLaunchKernel((const void*)k, grid, block, argv, shm, s);
       },
       args);
+}
+
+template <typename... KArgs, typename... Ts>
+hipError_t launch_kernel(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+                         Ts&&... ts) {
+  return launch_kernel_shm(k, grid, block, 0, s, static_cast<Ts&&>(ts)...);
 }
 
 // Workgroups of a grid-stride launch over `units` work items: enough waves to fill the

@@ -24,14 +24,25 @@
 namespace glu {
 namespace {
 
-// Waves per workgroup along M and N (each wave covers 32 rows x 64 columns), chosen per
-// direction from measurements on MI355X at [16384, 7168]: rowwise-only output is fastest
-// with 64 x 128 tiles; whenever transposed colwise codes are written (or two matrices are
-// quantized, in backward), wider 64 x 256 tiles win.
+// Launch shape per direction: waves per workgroup along M and N (each wave covers 32 rows x
+// 64 columns) and LDS bytes reserved per workgroup.  The LDS is not used by the kernel; the
+// reservation (more than half of a CU's 160 KiB) keeps one workgroup per CU.  Chosen from
+// interleaved measurements on MI355X at [16384, 7168]: rowwise-only forward output is
+// fastest with 64 x 128 tiles at full occupancy; whenever colwise codes are written or two
+// matrices are quantized (backward), 64 x 256 tiles with one workgroup per CU are fastest
+// (fewer concurrent tile streams: 146 vs 176 us forward both, 258 vs 360 us backward both).
 template <int MODE, int FLAGS>
 struct WgShape {
+#if defined(GLU_MX_WG_M) && defined(GLU_MX_WG_N)  // build-time override, for measurements
+  static constexpr int M = GLU_MX_WG_M;
+  static constexpr int N = GLU_MX_WG_N;
+  static constexpr int LDS = GLU_MX_LDS_BYTES;
+#else
+  static constexpr bool ROW_FWD = MODE == 0 && FLAGS == 1;
   static constexpr int M = 2;
-  static constexpr int N = (MODE == 0 && FLAGS == 1) ? 2 : 4;
+  static constexpr int N = ROW_FWD ? 2 : 4;
+  static constexpr int LDS = ROW_FWD ? 0 : 86016;
+#endif
 };
 
 // Build-time tuning (fixed defaults; alternatives are compiled only to measure them):
@@ -47,6 +58,10 @@ struct WgShape {
 #endif
 #ifndef GLU_MX_NT_STORES
 #define GLU_MX_NT_STORES 0
+#endif
+//   GLU_MX_WG_M, GLU_MX_WG_N, GLU_MX_LDS_BYTES: launch shape for every direction (below).
+#ifndef GLU_MX_LDS_BYTES
+#define GLU_MX_LDS_BYTES 0
 #endif
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -364,29 +379,19 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, int64_t r0, int64_t col
     load_rows<LAYOUT, FULL>(in, static_cast<const uint16_t*>(a.src), a.up, a.ld_in, row0, col, a.M,
                             col_ok);
     uint32_t H[4][4];
-    float zmin = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      float g[8], u[8], h[8];
+      float g[8], u[8], h[8], zmin = 0.0f;
       unpack_gu<LAYOUT>(in[i], g, u);
 #pragma unroll
       for (int c = 0; c < 8; c++) h[c] = glu_fwd_elem<ACT>(g[c], u[c], zmin);
+      if (zmin < TAIL_ZL2) {  // rare: e^z below the FP32 normal range
+#pragma unroll
+        for (int c = 0; c < 8; c++)
+          if (zl2<ACT>(g[c]) < TAIL_ZL2) h[c] = glu_fwd_tail<ACT>(g[c], u[c]);
+      }
 #pragma unroll
       for (int k = 0; k < 4; k++) H[i][k] = pack_bf16(h[2 * k], h[2 * k + 1]);
-    }
-    if (zmin < TAIL_ZL2) {
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        float g[8], u[8];
-        unpack_gu<LAYOUT>(in[i], g, u);
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-          float h0 = bf_lo(H[i][k]), h1 = bf_hi(H[i][k]);
-          if (zl2<ACT>(g[2 * k]) < TAIL_ZL2) h0 = glu_fwd_tail<ACT>(g[2 * k], u[2 * k]);
-          if (zl2<ACT>(g[2 * k + 1]) < TAIL_ZL2) h1 = glu_fwd_tail<ACT>(g[2 * k + 1], u[2 * k + 1]);
-          H[i][k] = pack_bf16(h0, h1);
-        }
-      }
     }
     const MxOut o{a.q_row, a.s_row, a.q_col, a.s_col, a.M, a.N};
     mx_store_bf16<FLAGS, FULL>(H, o, r0, col, lr, lc, col_ok);
@@ -403,39 +408,24 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, int64_t r0, int64_t col
       dp += a.ld_dh;
     }
     uint32_t HA[4][4], HB[4][4];
-    float zmin = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      float g[8], u[8], da[8], db[8];
+      float g[8], u[8], d[8], da[8], db[8], zmin = 0.0f;
       unpack_gu<SPLIT>(in[i], g, u);
 #pragma unroll
       for (int c = 0; c < 8; c++) {
-        const float d = (c & 1) ? bf_hi(D[i][c >> 1]) : bf_lo(D[i][c >> 1]);
-        glu_bwd_elem<ACT>(g[c], u[c], d, da[c], db[c], zmin);
+        d[c] = (c & 1) ? bf_hi(D[i][c >> 1]) : bf_lo(D[i][c >> 1]);
+        glu_bwd_elem<ACT>(g[c], u[c], d[c], da[c], db[c], zmin);
+      }
+      if (zmin < TAIL_ZL2) {  // rare: e^z below the FP32 normal range
+#pragma unroll
+        for (int c = 0; c < 8; c++)
+          if (zl2<ACT>(g[c]) < TAIL_ZL2) glu_bwd_tail<ACT>(g[c], u[c], d[c], da[c], db[c]);
       }
 #pragma unroll
       for (int k = 0; k < 4; k++) {
         HA[i][k] = pack_bf16(da[2 * k], da[2 * k + 1]);
         HB[i][k] = pack_bf16(db[2 * k], db[2 * k + 1]);
-      }
-    }
-    if (zmin < TAIL_ZL2) {
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        float g[8], u[8];
-        unpack_gu<SPLIT>(in[i], g, u);
-#pragma unroll
-        for (int c = 0; c < 8; c++) {
-          if (zl2<ACT>(g[c]) < TAIL_ZL2) {
-            const float d = (c & 1) ? bf_hi(D[i][c >> 1]) : bf_lo(D[i][c >> 1]);
-            float da, db;
-            glu_bwd_tail<ACT>(g[c], u[c], d, da, db);
-            const uint32_t ra = pack_bf16(da, da) & 0xffffu, rb = pack_bf16(db, db) & 0xffffu;
-            const int k = c >> 1, sh = 16 * (c & 1);
-            HA[i][k] = (HA[i][k] & ~(0xffffu << sh)) | (ra << sh);
-            HB[i][k] = (HB[i][k] & ~(0xffffu << sh)) | (rb << sh);
-          }
-        }
       }
     }
     const MxOut o{a.q_row, a.s_row, a.q_col, a.s_col, a.M, 2 * a.N};
@@ -482,8 +472,15 @@ hipError_t launch(const MxArgs& a, hipStream_t s) {
   const int64_t ntiles = tiles_m * tiles_n;
   const int64_t per_xcd = (ntiles + 7) / 8;
   const dim3 grid((unsigned)(8 * per_xcd)), block(64 * WGM * WGN);
-  return launch_kernel(k_mxfp8<ACT, LAYOUT, FLAGS, MODE, WGM, WGN>, grid, block, s, a,
-                       (uint32_t)tiles_m, (uint32_t)ntiles, (uint32_t)per_xcd);
+  constexpr int LDS = WgShape<MODE, FLAGS>::LDS;
+  auto k = k_mxfp8<ACT, LAYOUT, FLAGS, MODE, WGM, WGN>;
+  if constexpr (LDS > 65536) {
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (e != hipSuccess) return e;
+  }
+  return launch_kernel_shm(k, grid, block, LDS, s, a, (uint32_t)tiles_m, (uint32_t)ntiles,
+                           (uint32_t)per_xcd);
 }
 
 template <int ACT, int LAYOUT, int MODE>
