@@ -34,6 +34,42 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E
 PAGES_STEP_GBPS = (711_983_104 + 1_189_085_184) / ((143.36 + 219.14) * 1e-6) / 1e9
 
 
+# HBM traffic of the roofline kernel comes from the rocprofv3 counter summary committed under
+# profiles/; it is reported only while the kernel sources are unchanged since that profile.
+KERNEL_SOURCES = [os.path.join(ROOT, "glu_activation_microscaling_amd", "csrc", f)
+                  for f in ("glu_mxfp8.hip", "glu_device.h", "glu_launch.h", "glu_common.h")]
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_mxfp8_swiglu_16384x7168.md")
+
+
+def kernel_source_sha256():
+    """Hash of the kernel sources with // comments and blank lines removed (comment edits do
+    not change the kernel)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()
+
+
+def traffic_bytes(kernel):
+    """Measured HBM bytes (read + write) per launch of `kernel`, or None when no profile of
+    the current kernel sources exists."""
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    sha = kernel_source_sha256()
+    for line in open(TRAFFIC_PROFILE):
+        if not line.startswith("traffic_record:"):
+            continue
+        kv = dict(f.split("=", 1) for f in line.split()[1:])
+        if kv.get("kernel") == kernel and kv.get("source_sha256") == sha:
+            return int(kv["read_bytes"]) + int(kv["write_bytes"])
+    return None
+
+
 def mx_bytes(M, N, bwd, ndir):
     E = M * N
     return (6 * E + ndir * (2 * E + 2 * E // 32)) if bwd else (4 * E + ndir * (E + E // 32))
@@ -82,6 +118,11 @@ def sweep(torch, glu, si, iters):
         res[name] = dict(bytes=b, us=round(t["median_us"], 2), gbps=round(b / t["median_us"] / 1e3, 1),
                          frac=round(b / t["median_us"] / 1e3 / PEAK_GBPS, 4))
 
+    # practical ceiling: a device-to-device copy of 1 GiB (runtime blit kernel), 2 GiB moved
+    src = [torch.empty(1 << 30, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    rec("device_copy_1GiB", 2 << 30, time_launches(torch, [lambda x=x: dst.copy_(x) for x in src], iters))
+    del src, dst
     # MXFP8 SwiGLU shapes
     for M, N, outl, cases in [
         (128, 128, False, [("fwd", "row")]),
@@ -241,7 +282,7 @@ def main():
             "bound": "hbm", "kernel": "k_mxfp8 backward, both scalings",
             "achieved": round(bwd_b / bwd_us / 1e3, 1), "peak": PEAK_GBPS, "unit": "GB/s",
             "frac": round(bwd_b / bwd_us / 1e3 / PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic_bytes("k_mxfp8<0,0,3,1,2,4>"),
         },
     }
     del sets, fo, bo

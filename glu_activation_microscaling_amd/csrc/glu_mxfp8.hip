@@ -3,11 +3,11 @@
 // the FP32 quantizer hook that runs the same block rules on given FP32 values.
 //
 // Work decomposition (wave64):
-//   workgroup = 4 waves = a 64-row x 128-column tile; wave w covers rows 32*(w&1) and
-//   columns 64*(w>>1) of it, i.e. one 32-row colwise block row and two 32-column rowwise
-//   blocks per row.  Lane = lr + 8*lc owns rows 4lr..4lr+3 and columns 8lc..8lc+7 of the
-//   wave tile: 16-byte loads per row and per operand, 32 elements per lane, kept after
-//   the activation as 16 packed BF16 pairs.
+//   A wave covers 32 rows x 64 columns: one 32-row colwise block row and two 32-column
+//   rowwise blocks per row.  Lane = lr + 8*lc owns rows 4lr..4lr+3 and columns 8lc..8lc+7:
+//   16-byte loads per row and per operand, 32 elements per lane, kept after the activation
+//   as 16 packed BF16 pairs.  A workgroup stacks WGM x WGN waves (the launch shape per
+//   direction is set in WgShape below).
 //   Rowwise amax of a 32-column block spans the 4 lanes lc = 4b..4b+3 (lane bits 3, 4):
 //   DPP row_ror:8 then ds_swizzle xor 16.  Colwise amax of a 32-row block spans the 8
 //   lanes lr = 0..7 (lane bits 0..2) after an in-lane max over 4 rows: DPP quad_perm xor 1,
