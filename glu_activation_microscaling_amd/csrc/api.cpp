@@ -24,6 +24,9 @@ using glu::NvArgs;
 // Upper bound on MXFP8 tiles per launch (counted with the smallest tile, 32 x 64), so the
 // tile index and the workgroup count stay within 32 bits.
 constexpr int64_t kMaxTiles = (int64_t)1 << 30;
+// Largest row pitch, in bytes, of an MXFP8 kernel operand: the kernels address 32 rows from a
+// per-piece base with 32-bit offsets that must stay below 2^31.
+constexpr int64_t kMaxMxPitchBytes = (int64_t)1 << 25;
 
 // Byte extent of a row-major matrix: ((rows - 1) * ld + cols) * esz, or -1 on overflow.
 int64_t extent_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esz) {
@@ -209,7 +212,7 @@ glu_status glu_check_fwd_mxfp8(int act, int layout, int64_t M, int64_t N, const 
   if (st != GLU_OK) return st;
   if ((st = check_mx_outputs(flags, q_row, s_row, q_col, s_col)) != GLU_OK) return st;
   if (N % 32 != 0 || ((flags & glu::COLWISE) && M % 32 != 0)) return GLU_ERR_SHAPE;
-  if (ld_in % 8 != 0) return GLU_ERR_STRIDE;
+  if (ld_in % 8 != 0 || ld_in > kMaxMxPitchBytes / 2) return GLU_ERR_STRIDE;
   if (!aligned16(gate) || !aligned16(up) || !aligned16(q_row) || !aligned16(s_row) ||
       !aligned16(q_col) || !aligned16(s_col))
     return GLU_ERR_ALIGN;
@@ -237,6 +240,7 @@ glu_status glu_check_bwd_mxfp8(int act, int layout, int64_t M, int64_t N, const 
   if (N % 32 != 0 || ((flags & glu::COLWISE) && M % 32 != 0)) return GLU_ERR_SHAPE;
   if (ld_dh < N) return GLU_ERR_STRIDE;
   if (ld_in % 8 != 0 || ld_dh % 8 != 0) return GLU_ERR_STRIDE;
+  if (ld_in > kMaxMxPitchBytes / 2 || ld_dh > kMaxMxPitchBytes / 2) return GLU_ERR_STRIDE;
   if (!aligned16(gate) || !aligned16(up) || !aligned16(dh) || !aligned16(q_row) ||
       !aligned16(s_row) || !aligned16(q_col) || !aligned16(s_col))
     return GLU_ERR_ALIGN;
@@ -283,7 +287,7 @@ glu_status glu_check_quant_mxfp8_f32(int64_t M, int64_t N, const float* x, int64
   glu_status st = check_mx_outputs(flags, q_row, s_row, q_col, s_col);
   if (st != GLU_OK) return st;
   if (N % 32 != 0 || ((flags & glu::COLWISE) && M % 32 != 0)) return GLU_ERR_SHAPE;
-  if (ld_x < N || ld_x % 4 != 0) return GLU_ERR_STRIDE;
+  if (ld_x < N || ld_x % 4 != 0 || ld_x > kMaxMxPitchBytes / 4) return GLU_ERR_STRIDE;
   if (!aligned16(x) || !aligned16(q_row) || !aligned16(s_row) || !aligned16(q_col) ||
       !aligned16(s_col))
     return GLU_ERR_ALIGN;

@@ -3,80 +3,107 @@
 // the FP32 quantizer hook that runs the same block rules on given FP32 values.
 //
 // Work decomposition (wave64):
-//   A wave covers 32 rows x 64 columns: one 32-row colwise block row and two 32-column
-//   rowwise blocks per row.  Lane = lr + 8*lc owns rows 4lr..4lr+3 and columns 8lc..8lc+7:
-//   16-byte loads per row and per operand, 32 elements per lane, kept after the activation
-//   as 16 packed BF16 pairs.  A workgroup stacks WGM x WGN waves (the launch shape per
-//   direction is set in WgShape below).
+//   A workgroup owns a TM x TN = 128 x 128 tile of the quantized matrix (of each of da and db
+//   in the backward) with WGM x WGN = 4 x 2 waves.  A wave covers 32 rows x 64 columns: one
+//   32-row colwise block row and two 32-column rowwise blocks per row.  Lane = lr + 8*lc owns
+//   rows 4lr..4lr+3 and columns 8lc..8lc+7 of the wave's piece: 16-byte loads per row and per
+//   operand, 32 elements per lane, kept after the activation as 16 packed BF16 pairs.
 //   Rowwise amax of a 32-column block spans the 4 lanes lc = 4b..4b+3 (lane bits 3, 4):
 //   DPP row_ror:8 then ds_swizzle xor 16.  Colwise amax of a 32-row block spans the 8
 //   lanes lr = 0..7 (lane bits 0..2) after an in-lane max over 4 rows: DPP quad_perm xor 1,
 //   xor 2, then row_half_mirror.  Maxima are taken on packed 16-bit magnitudes (two
-//   columns, or two rows, per instruction).  No LDS is needed: each lane already holds 4
-//   consecutive rows of every column it owns, so colwise codes leave as 4-byte stores into
-//   the transposed [N, M] output and rowwise codes as 8-byte stores.
+//   columns, or two rows, per instruction).
+//   Codes and scales are staged in LDS and leave, after one workgroup barrier, as 16-byte
+//   stores that fill whole 128-byte lines: a tile row of rowwise codes and a tile column of
+//   colwise codes are 128 bytes each, and the scales of a tile row (column) are one 4-byte
+//   word.  Straight from the registers the same data would leave as 32-byte (colwise) and
+//   64-byte (rowwise) pieces and single scale bytes: several times more L2 write requests,
+//   which measured as the limit once enough tiles run concurrently to keep HBM busy.
 //   Tiles are dealt to the 8 XCDs in contiguous runs along M (workgroups go to XCDs
-//   round-robin by id), so the transposed colwise lines and their scale bytes, which
-//   neighbouring tiles along M share, are assembled in one XCD's L2.
+//   round-robin by id), so neighbouring tiles along M, which share the transposed colwise
+//   output's scale words, run on one XCD at about the same time.
 #include "glu_device.h"
 #include "glu_launch.h"
 
 namespace glu {
 namespace {
 
-// Launch shape per direction: waves per workgroup along M and N (each wave covers 32 rows x
-// 64 columns) and LDS bytes reserved per workgroup.  The LDS is not used by the kernel; the
-// reservation (more than half of a CU's 160 KiB) keeps one workgroup per CU.  Chosen from
-// interleaved measurements on MI355X at [16384, 7168]: rowwise-only forward output is
-// fastest with 64 x 128 tiles at full occupancy; whenever colwise codes are written or two
-// matrices are quantized (backward), 64 x 256 tiles with one workgroup per CU are fastest
-// (fewer concurrent tile streams: 146 vs 176 us forward both, 258 vs 360 us backward both).
-template <int MODE, int FLAGS>
-struct WgShape {
-#if defined(GLU_MX_WG_M) && defined(GLU_MX_WG_N)  // build-time override, for measurements
-  static constexpr int M = GLU_MX_WG_M;
-  static constexpr int N = GLU_MX_WG_N;
-  static constexpr int LDS = GLU_MX_LDS_BYTES;
-#else
-  static constexpr bool ROW_FWD = MODE == 0 && FLAGS == 1;
-  static constexpr int M = 2;
-  static constexpr int N = ROW_FWD ? 2 : 4;
-  static constexpr int LDS = ROW_FWD ? 0 : 86016;
-#endif
-};
-
 // Build-time tuning (fixed defaults; alternatives are compiled only to measure them):
-//   GLU_MX_TILE_ORDER 0: each XCD takes a contiguous run of tiles in M-fastest order;
-//                     1: each XCD takes a contiguous run of tiles in N-fastest order;
-//                     2: tiles in workgroup-id order, N fastest (no XCD remapping).
-//   GLU_MX_NT_LOADS / GLU_MX_NT_STORES: non-temporal (streaming) operand loads / code stores.
-#ifndef GLU_MX_TILE_ORDER
-#define GLU_MX_TILE_ORDER 0
-#endif
+//   GLU_MX_NT_LOADS: non-temporal (streaming) operand loads.
+//   GLU_MX_NT_STORES: -1 per kernel (below); 0 / 1 non-temporal code stores off / on.
 #ifndef GLU_MX_NT_LOADS
 #define GLU_MX_NT_LOADS 1
 #endif
 #ifndef GLU_MX_NT_STORES
-#define GLU_MX_NT_STORES 0
+#define GLU_MX_NT_STORES -1
 #endif
-//   GLU_MX_WG_M, GLU_MX_WG_N, GLU_MX_LDS_BYTES: launch shape for every direction (below).
-#ifndef GLU_MX_LDS_BYTES
-#define GLU_MX_LDS_BYTES 0
+//   GLU_MX_TILE_ORDER: -1 per direction (below), else the order 0, 1 or 2 for every kernel.
+#ifndef GLU_MX_TILE_ORDER
+#define GLU_MX_TILE_ORDER -1
 #endif
+
+enum { MODE_FWD = 0, MODE_BWD = 1, MODE_F32 = 2 };
+
+constexpr int WGM = 4, WGN = 2;                 // waves per workgroup along M and N
+constexpr int TM = 32 * WGM, TN = 64 * WGN;     // quantized tile per workgroup
+constexpr int NTHREADS = 64 * WGM * WGN;
+static_assert(TM == 128 && TN == 128, "the LDS swizzles and 4-byte scale words assume 128 x 128");
+
+// Non-temporal code stores: measured faster only for the backward quantized both ways
+// (234 vs 267 us at [16384, 7168] in the blocked tile order); slower for the forward both
+// ways (138 vs 126 us).
+template <int MODE, int FLAGS>
+constexpr bool nt_stores() {
+  return GLU_MX_NT_STORES < 0 ? MODE == MODE_BWD && FLAGS == (ROWWISE | COLWISE)
+                               : GLU_MX_NT_STORES == 1;
+}
+
+// Order of the tiles; each XCD takes a contiguous run of it.
+//   0 (colwise only): along M first, so consecutive tiles continue the same rows of the
+//     transposed [N, M] output and fill its scale rows word after word.
+//   1 (rowwise only): along N first, so consecutive tiles continue the same input and output
+//     rows and fill the rowwise scale rows word after word (about 3% faster at [16384, 7168]).
+//   2 (both): strips of 8 tile columns; in a strip, blocks of 8 x 8 tiles going down M; in a
+//     block, along M first.  The 8 tiles of a block that share rows (columns) write their
+//     4-byte rowwise (colwise) scale words into one 32-byte sector within the same window of
+//     concurrent tiles, so both scale streams leave L2 as whole sectors (orders 0 and 1 leave
+//     one of them as single words: 6% slower at [16384, 7168]).
+#ifndef GLU_MX_ORDER_BLOCK  // build-time override of the block size, for measurements
+#define GLU_MX_ORDER_BLOCK 8
+#endif
+constexpr int kOrderBlock = GLU_MX_ORDER_BLOCK;  // 4: 252, 8: 234, 16: 238 us backward both
+
+template <int FLAGS>
+constexpr int tile_order() {
+  return GLU_MX_TILE_ORDER >= 0 ? GLU_MX_TILE_ORDER
+                                : FLAGS == ROWWISE ? 1 : FLAGS == COLWISE ? 0 : 2;
+}
+
+template <int ORDER>
+__device__ __forceinline__ void tile_of(uint32_t t, uint32_t tiles_m, uint32_t tiles_n,
+                                        uint32_t& tm, uint32_t& tn) {
+  if constexpr (ORDER == 0) {
+    tn = t / tiles_m;
+    tm = t - tn * tiles_m;
+  } else if constexpr (ORDER == 1) {
+    tm = t / tiles_n;
+    tn = t - tm * tiles_n;
+  } else {
+    constexpr uint32_t B = kOrderBlock;
+    const uint32_t strip = tiles_m * B;  // tiles per full strip
+    const uint32_t bj = t / strip, u = t - bj * strip;
+    const uint32_t w = tiles_n - bj * B < B ? tiles_n - bj * B : B;  // strip width
+    const uint32_t bi = u / (B * w), v = u - bi * B * w;
+    const uint32_t h = tiles_m - bi * B < B ? tiles_m - bi * B : B;  // block height
+    const uint32_t j = v / h;
+    tm = bi * B + (v - j * h);
+    tn = bj * B + j;
+  }
+}
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void st_code(uint32_t* p, uint32_t v) {
-  if constexpr (GLU_MX_NT_STORES) __builtin_nontemporal_store(v, p);
-  else *p = v;
-}
-__device__ __forceinline__ void st_code(uint2* p, uint2 v) {
-  const u32x2 x = {v.x, v.y};
-  if constexpr (GLU_MX_NT_STORES) __builtin_nontemporal_store(x, reinterpret_cast<u32x2*>(p));
-  else *reinterpret_cast<u32x2*>(p) = x;
-}
-enum { MODE_FWD = 0, MODE_BWD = 1, MODE_F32 = 2 };
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -96,200 +123,6 @@ __device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
 // (a.lo, b.lo) and (a.hi, b.hi) as packed pairs
 __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-
-struct MxOut {
-  uint8_t* q_row;
-  uint8_t* s_row;
-  uint8_t* q_col;
-  uint8_t* s_col;
-  int64_t M;    // rows of the quantized matrix
-  int64_t ldq;  // columns of the quantized matrix (N forward, 2N backward)
-};
-
-// Quantizes the lane's 4x8 BF16 values H[i][k] = (columns 2k, 2k+1 of row r0 + 4lr + i),
-// columns starting at `col` of the quantized matrix, and stores codes and scales.  All 64
-// lanes must call it together.  FULL: the wave's 32 rows and 64 columns are all in range
-// (no per-row or per-column guards); otherwise rows >= M and columns >= the matrix width
-// are skipped.
-template <int FLAGS, bool FULL>
-__device__ __forceinline__ void mx_store_bf16(const uint32_t (&H)[4][4], const MxOut& o,
-                                              int64_t r0, int64_t col, int lr, int lc,
-                                              bool col_ok) {
-  uint32_t A[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int k = 0; k < 4; k++) A[i][k] = H[i][k] & 0x7fff7fffu;
-
-  uint32_t R01 = 0, R23 = 0;  // row block maxima, rows (0,1) and (2,3) packed
-  uint32_t C[4] = {0, 0, 0, 0};  // column block maxima, columns (2k, 2k+1) packed
-  if constexpr ((FLAGS & ROWWISE) != 0) {
-    uint32_t m[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) m[i] = pkmax(pkmax(A[i][0], A[i][1]), pkmax(A[i][2], A[i][3]));
-    R01 = pkmax(pair_lo(m[0], m[1]), pair_hi(m[0], m[1]));
-    R23 = pkmax(pair_lo(m[2], m[3]), pair_hi(m[2], m[3]));
-    R01 = pkmax(R01, dpp<DPP_ROW_ROR8>(R01));
-    R23 = pkmax(R23, dpp<DPP_ROW_ROR8>(R23));
-    R01 = pkmax(R01, swz_xor16(R01));
-    R23 = pkmax(R23, swz_xor16(R23));
-  }
-  if constexpr ((FLAGS & COLWISE) != 0) {
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      uint32_t c = pkmax(pkmax(A[0][k], A[1][k]), pkmax(A[2][k], A[3][k]));
-      c = pkmax(c, dpp<DPP_XOR1>(c));
-      c = pkmax(c, dpp<DPP_XOR2>(c));
-      C[k] = pkmax(c, dpp<DPP_HALF_MIRROR>(c));
-    }
-  }
-  // any non-finite block among those this lane touches? (rare: handled after the stores)
-  const uint32_t all = pkmax(pkmax(R01, R23), pkmax(pkmax(C[0], C[1]), pkmax(C[2], C[3])));
-  const bool nonfinite = umax(lo16(all), hi16(all)) >= 0x7f80u;
-
-  const int64_t row0 = r0 + 4 * lr;
-  const int64_t nb_row = o.ldq / 32, nb_col = o.M / 32;
-  const bool lane_ok = FULL || col_ok;
-  if constexpr ((FLAGS & ROWWISE) != 0) {
-    const uint32_t S01 = pk_scale_bytes(R01), S23 = pk_scale_bytes(R23);
-    const uint32_t sb[4] = {lo16(S01), hi16(S01), lo16(S23), hi16(S23)};
-    uint8_t* q = o.q_row + row0 * o.ldq + col;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      if (FULL || (col_ok && row0 + i < o.M)) {
-        const float sc = e8m0_value(sb[i]);
-        uint32_t w0 = fp8x2_scaled<false>(0u, H[i][0], sc);
-        w0 = fp8x2_scaled<true>(w0, H[i][1], sc);
-        uint32_t w1 = fp8x2_scaled<false>(0u, H[i][2], sc);
-        w1 = fp8x2_scaled<true>(w1, H[i][3], sc);
-        st_code(reinterpret_cast<uint2*>(q), make_uint2(w0, w1));
-      }
-      q += o.ldq;
-    }
-    // lane lc = 4b + i stores the scale of row 4lr + i in block b
-    const int i = lc & 3;
-    if (FULL || (col_ok && row0 + i < o.M)) {
-      const uint32_t w = i < 2 ? S01 : S23;
-      o.s_row[(row0 + i) * nb_row + ((col - 8 * i) >> 5)] = (uint8_t)((i & 1) ? hi16(w) : lo16(w));
-    }
-  }
-  if constexpr ((FLAGS & COLWISE) != 0) {
-    uint32_t S[4];
-#pragma unroll
-    for (int k = 0; k < 4; k++) S[k] = pk_scale_bytes(C[k]);
-    if (lane_ok) {
-      uint8_t* q = o.q_col + col * o.M + row0;
-#pragma unroll
-      for (int k = 0; k < 4; k++) {
-        const float s0 = e8m0_value(lo16(S[k])), s1 = e8m0_value(hi16(S[k]));
-        // column 2k: rows (0,1) from the low halves, rows (2,3) likewise
-        uint32_t w0 = fp8x2_scaled<false>(0u, pair_lo(H[0][k], H[1][k]), s0);
-        w0 = fp8x2_scaled<true>(w0, pair_lo(H[2][k], H[3][k]), s0);
-        uint32_t w1 = fp8x2_scaled<false>(0u, pair_hi(H[0][k], H[1][k]), s1);
-        w1 = fp8x2_scaled<true>(w1, pair_hi(H[2][k], H[3][k]), s1);
-        st_code(reinterpret_cast<uint32_t*>(q), w0);
-        st_code(reinterpret_cast<uint32_t*>(q + o.M), w1);
-        q += 2 * o.M;
-      }
-      // lane lr stores the scale of column 8lc + lr of this 32-row block
-      const uint32_t w = (lr >> 1) == 0 ? S[0] : (lr >> 1) == 1 ? S[1] : (lr >> 1) == 2 ? S[2] : S[3];
-      o.s_col[(col + lr) * nb_col + (r0 >> 5)] = (uint8_t)((lr & 1) ? hi16(w) : lo16(w));
-    }
-  }
-
-  if (nonfinite) {
-    // a block holding NaN or Inf: scale 0xFF, every code 0x7F (overwrites the fast path)
-    if constexpr ((FLAGS & ROWWISE) != 0) {
-      const uint32_t rm[4] = {lo16(R01), hi16(R01), lo16(R23), hi16(R23)};
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int64_t row = row0 + i;
-        if (col_ok && row < o.M && rm[i] >= 0x7f80u) {
-          *reinterpret_cast<uint2*>(o.q_row + row * o.ldq + col) = make_uint2(0x7f7f7f7fu, 0x7f7f7f7fu);
-          if ((lc & 3) == i) o.s_row[row * nb_row + ((col - 8 * i) >> 5)] = 0xff;
-        }
-      }
-    }
-    if constexpr ((FLAGS & COLWISE) != 0) {
-      if (col_ok) {
-#pragma unroll
-        for (int c = 0; c < 8; c++) {
-          const uint32_t cm = (c & 1) ? hi16(C[c >> 1]) : lo16(C[c >> 1]);
-          if (cm >= 0x7f80u) {
-            *reinterpret_cast<uint32_t*>(o.q_col + (col + c) * o.M + row0) = 0x7f7f7f7fu;
-            if (lr == c) o.s_col[(col + c) * nb_col + (r0 >> 5)] = 0xff;
-          }
-        }
-      }
-    }
-  }
-}
-
-// The same rules on FP32 values (quantizer hook): magnitudes compared as FP32 bits, the
-// scaled value x * 2^-e computed exactly in FP32, then v_cvt_pk_fp8_f32.
-template <int FLAGS>
-__device__ __forceinline__ void mx_store_f32(const float (&v)[4][8], const MxOut& o, int64_t r0,
-                                             int64_t col, int lr, int lc, bool col_ok) {
-  uint32_t ab[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int c = 0; c < 8; c++) ab[i][c] = __float_as_uint(v[i][c]) & 0x7fffffffu;
-
-  if constexpr ((FLAGS & ROWWISE) != 0) {
-    uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      uint32_t m = ab[i][0];
-#pragma unroll
-      for (int c = 1; c < 8; c++) m = umax(m, ab[i][c]);
-      m = umax(m, dpp<DPP_ROW_ROR8>(m));
-      m = umax(m, swz_xor16(m));
-      const bool nonfinite = m >= 0x7f800000u;
-      const uint32_t b = nonfinite ? 0xffu : mx_scale_byte(m);
-      const float P = mx_inv_scale(nonfinite ? 0u : b);
-      packed |= b << (8 * i);
-      const int64_t row = r0 + 4 * lr + i;
-      if (col_ok && row < o.M) {
-        uint32_t w0 = fp8x2<false>(0u, v[i][0] * P, v[i][1] * P);
-        w0 = fp8x2<true>(w0, v[i][2] * P, v[i][3] * P);
-        uint32_t w1 = fp8x2<false>(0u, v[i][4] * P, v[i][5] * P);
-        w1 = fp8x2<true>(w1, v[i][6] * P, v[i][7] * P);
-        if (nonfinite) w0 = w1 = 0x7f7f7f7fu;
-        *reinterpret_cast<uint2*>(o.q_row + row * o.ldq + col) = make_uint2(w0, w1);
-      }
-    }
-    const int i = lc & 3;
-    const int64_t row = r0 + 4 * lr + i;
-    if (col_ok && row < o.M)
-      o.s_row[row * (o.ldq / 32) + (col - 8 * i) / 32] = (uint8_t)(packed >> (8 * i));
-  }
-
-  if constexpr ((FLAGS & COLWISE) != 0) {
-    uint32_t packed0 = 0, packed1 = 0;
-#pragma unroll
-    for (int c = 0; c < 8; c++) {
-      uint32_t m = umax(umax(ab[0][c], ab[1][c]), umax(ab[2][c], ab[3][c]));
-      m = umax(m, dpp<DPP_XOR1>(m));
-      m = umax(m, dpp<DPP_XOR2>(m));
-      m = umax(m, dpp<DPP_HALF_MIRROR>(m));
-      const bool nonfinite = m >= 0x7f800000u;
-      const uint32_t b = nonfinite ? 0xffu : mx_scale_byte(m);
-      const float P = mx_inv_scale(nonfinite ? 0u : b);
-      if (c < 4) packed0 |= b << (8 * c); else packed1 |= b << (8 * (c - 4));
-      if (col_ok) {
-        uint32_t w = fp8x2<false>(0u, v[0][c] * P, v[1][c] * P);
-        w = fp8x2<true>(w, v[2][c] * P, v[3][c] * P);
-        if (nonfinite) w = 0x7f7f7f7fu;
-        *reinterpret_cast<uint32_t*>(o.q_col + (col + c) * o.M + r0 + 4 * lr) = w;
-      }
-    }
-    if (col_ok) {
-      const uint32_t w = lr < 4 ? packed0 : packed1;
-      o.s_col[(col + lr) * (o.M / 32) + r0 / 32] = (uint8_t)(w >> (8 * (lr & 3)));
-    }
-  }
-}
 
 // Raw operand words of 8 consecutive outputs: SPLIT gives gate and up words (each a BF16
 // pair of adjacent columns); PAIRED gives 8 words, each a (gate, up) BF16 pair.
@@ -318,169 +151,467 @@ __device__ __forceinline__ void unpack_gu(const GU<LAYOUT>& r, float g[8], float
   }
 }
 
-// 16 bytes at p, or zeros when !ok (a value select, so the operands stay in registers).
-__device__ __forceinline__ uint4 ld16_if(const void* p, bool ok) {
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (ok) {
-    u32x4 x;
-    if constexpr (GLU_MX_NT_LOADS) x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    else x = *reinterpret_cast<const u32x4*>(p);
-    v = make_uint4(x.x, x.y, x.z, x.w);
-  }
-  return v;
+// Operands are read with raw buffer loads through a descriptor whose base is the first byte
+// of a wave's piece (a wave-uniform address).  A lane whose element is outside the matrix
+// passes kOob as its offset; the hardware's range check turns that load into zeros, so every
+// path through a tile issues the same loads, with no branch and no select.  Row pitches are
+// limited (by the host checks) so that 32 rows of offsets stay below kOob.
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+  // gfx9 descriptor word 3: 32-bit data format, raw (stride 0) addressing
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(kOob - 1),
+                                           0x00020000);
 }
 
-// Loads the lane's 4 rows of operands.  FULL: every row and column in range.
-template <int LAYOUT, bool FULL>
-__device__ __forceinline__ void load_rows(GU<LAYOUT> (&in)[4], const uint16_t* gate,
-                                          const uint16_t* up, int64_t ld, int64_t row0,
-                                          int64_t col, int64_t M, bool col_ok) {
-  const int64_t off = row0 * ld + (LAYOUT == PAIRED ? 2 * col : col);
-  const uint16_t* g = gate + off;
-  const uint16_t* u = LAYOUT == SPLIT ? up + off : nullptr;
+__device__ __forceinline__ void bld16(uint32_t (&w)[4], __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, GLU_MX_NT_LOADS ? 2 : 0);
+  w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+}
+
+// Raw operands of one lane's 4x8 elements of a tile.
+template <int LAYOUT, int MODE>
+struct TileOps {
+  GU<MODE == MODE_BWD ? SPLIT : LAYOUT> in[4];  // gate/up words (forward, backward)
+  uint32_t d[MODE == MODE_BWD ? 4 : 1][4];      // dh words (backward)
+  uint32_t x[MODE == MODE_F32 ? 4 : 1][8];      // FP32 bits (quantizer hook)
+};
+
+// Where one wave's 32 x 64 piece of a tile lies.
+struct TileGeom {
+  int64_t r0, cw;  // first row and column of the piece (wave-uniform)
+  int64_t col;     // this lane's first column
+  bool col_ok;     // this lane's 8 columns are inside
+};
+
+// Issues the loads of the lane's 4 x 8 operands of a piece (4 consecutive rows, 8 columns).
+template <int LAYOUT, int MODE>
+__device__ __forceinline__ void load_ops(TileOps<LAYOUT, MODE>& o, const MxArgs& a,
+                                         const TileGeom& g, int lr, int lc) {
+  const int64_t left = a.M - g.r0;
+  const int rows = left < 0 ? 0 : (left > 32 ? 32 : (int)left);  // rows of the piece inside
+  bool ok[4];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const bool ok = FULL || (col_ok && row0 + i < M);
-    if constexpr (LAYOUT == SPLIT) {
-      const uint4 G = ld16_if(g, ok), U = ld16_if(u, ok);
-      in[i].a[0] = G.x; in[i].a[1] = G.y; in[i].a[2] = G.z; in[i].a[3] = G.w;
-      in[i].b[0] = U.x; in[i].b[1] = U.y; in[i].b[2] = U.z; in[i].b[3] = U.w;
-      u += ld;
-    } else {
-      const uint4 A = ld16_if(g, ok), B = ld16_if(g + 8, ok);
-      in[i].a[0] = A.x; in[i].a[1] = A.y; in[i].a[2] = A.z; in[i].a[3] = A.w;
-      in[i].a[4] = B.x; in[i].a[5] = B.y; in[i].a[6] = B.z; in[i].a[7] = B.w;
-    }
-    g += ld;
-  }
-}
-
-template <int ACT, int LAYOUT, int FLAGS, int MODE, bool FULL>
-__device__ __forceinline__ void mx_tile(const MxArgs& a, int64_t r0, int64_t col, int lr, int lc,
-                                        bool col_ok) {
-  const int64_t row0 = r0 + 4 * lr;
+  for (int i = 0; i < 4; i++) ok[i] = g.col_ok && 4 * lr + i < rows;
   if constexpr (MODE == MODE_F32) {
-    float v[4][8];
-    const float* x = static_cast<const float*>(a.src) + row0 * a.ld_in + col;
+    const uint32_t ld = (uint32_t)a.ld_in * 4u;
+    const auto r = rsrc(static_cast<const float*>(a.src) + g.r0 * a.ld_in + g.cw);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const bool ok = FULL || (col_ok && row0 + i < a.M);
-      const uint4 A = ld16_if(x, ok), B = ld16_if(x + 4, ok);
-      v[i][0] = __uint_as_float(A.x); v[i][1] = __uint_as_float(A.y);
-      v[i][2] = __uint_as_float(A.z); v[i][3] = __uint_as_float(A.w);
-      v[i][4] = __uint_as_float(B.x); v[i][5] = __uint_as_float(B.y);
-      v[i][6] = __uint_as_float(B.z); v[i][7] = __uint_as_float(B.w);
-      x += a.ld_in;
+      const uint32_t off = (uint32_t)(4 * lr + i) * ld + 32u * lc;
+      uint32_t w0[4], w1[4];
+      bld16(w0, r, ok[i] ? off : kOob);
+      bld16(w1, r, ok[i] ? off + 16u : kOob);
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        o.x[i][k] = w0[k];
+        o.x[i][4 + k] = w1[k];
+      }
     }
-    const MxOut o{a.q_row, a.s_row, a.q_col, a.s_col, a.M, a.N};
-    mx_store_f32<FLAGS>(v, o, r0, col, lr, lc, col_ok);
+  } else {
+    constexpr int L = MODE == MODE_BWD ? SPLIT : LAYOUT;
+    const uint32_t ld = (uint32_t)a.ld_in * 2u;
+    const uint16_t* gate = static_cast<const uint16_t*>(a.src);
+    if constexpr (L == SPLIT) {
+      const int64_t base = g.r0 * a.ld_in + g.cw;
+      const auto rg = rsrc(gate + base), ru = rsrc(a.up + base);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const uint32_t off = ok[i] ? (uint32_t)(4 * lr + i) * ld + 16u * lc : kOob;
+        bld16(o.in[i].a, rg, off);
+        bld16(o.in[i].b, ru, off);
+      }
+    } else {
+      const auto rg = rsrc(gate + g.r0 * a.ld_in + 2 * g.cw);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const uint32_t off = (uint32_t)(4 * lr + i) * ld + 32u * lc;
+        uint32_t w0[4], w1[4];
+        bld16(w0, rg, ok[i] ? off : kOob);
+        bld16(w1, rg, ok[i] ? off + 16u : kOob);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          o.in[i].a[k] = w0[k];
+          o.in[i].a[4 + k] = w1[k];
+        }
+      }
+    }
+    if constexpr (MODE == MODE_BWD) {
+      const uint32_t ldd = (uint32_t)a.ld_dh * 2u;
+      const auto rd = rsrc(a.dh + g.r0 * a.ld_dh + g.cw);
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        bld16(o.d[i], rd, ok[i] ? (uint32_t)(4 * lr + i) * ldd + 16u * lc : kOob);
+    }
+  }
+}
+
+// A tile's results before quantization: BF16 words (forward: h; backward: da, db) or the
+// FP32 input of the quantizer hook.
+template <int MODE>
+struct TileVals {
+  uint32_t h[MODE == MODE_BWD ? 2 : 1][4][4];
+  float v[MODE == MODE_F32 ? 4 : 1][8];
+};
+
+template <int ACT, int LAYOUT, int MODE>
+__device__ __forceinline__ void compute(TileVals<MODE>& r, const TileOps<LAYOUT, MODE>& o) {
+  if constexpr (MODE == MODE_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int c = 0; c < 8; c++) r.v[i][c] = __uint_as_float(o.x[i][c]);
   } else if constexpr (MODE == MODE_FWD) {
-    GU<LAYOUT> in[4];
-    load_rows<LAYOUT, FULL>(in, static_cast<const uint16_t*>(a.src), a.up, a.ld_in, row0, col, a.M,
-                            col_ok);
-    uint32_t H[4][4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      float g[8], u[8], h[8], zmin = 0.0f;
-      unpack_gu<LAYOUT>(in[i], g, u);
+      float gg[8], u[8], h[8], zmin = 0.0f;
+      unpack_gu<LAYOUT>(o.in[i], gg, u);
 #pragma unroll
-      for (int c = 0; c < 8; c++) h[c] = glu_fwd_elem<ACT>(g[c], u[c], zmin);
+      for (int c = 0; c < 8; c++) h[c] = glu_fwd_elem<ACT>(gg[c], u[c], zmin);
       if (zmin < TAIL_ZL2) {  // rare: e^z below the FP32 normal range
 #pragma unroll
         for (int c = 0; c < 8; c++)
-          if (zl2<ACT>(g[c]) < TAIL_ZL2) h[c] = glu_fwd_tail<ACT>(g[c], u[c]);
+          if (zl2<ACT>(gg[c]) < TAIL_ZL2) h[c] = glu_fwd_tail<ACT>(gg[c], u[c]);
       }
 #pragma unroll
-      for (int k = 0; k < 4; k++) H[i][k] = pack_bf16(h[2 * k], h[2 * k + 1]);
+      for (int k = 0; k < 4; k++) r.h[0][i][k] = pack_bf16(h[2 * k], h[2 * k + 1]);
     }
-    const MxOut o{a.q_row, a.s_row, a.q_col, a.s_col, a.M, a.N};
-    mx_store_bf16<FLAGS, FULL>(H, o, r0, col, lr, lc, col_ok);
   } else {
-    GU<SPLIT> in[4];
-    load_rows<SPLIT, FULL>(in, static_cast<const uint16_t*>(a.src), a.up, a.ld_in, row0, col, a.M,
-                           col_ok);
-    uint32_t D[4][4];
-    const uint16_t* dp = a.dh + row0 * a.ld_dh + col;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const uint4 d = ld16_if(dp, FULL || (col_ok && row0 + i < a.M));
-      D[i][0] = d.x; D[i][1] = d.y; D[i][2] = d.z; D[i][3] = d.w;
-      dp += a.ld_dh;
-    }
-    uint32_t HA[4][4], HB[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      float g[8], u[8], d[8], da[8], db[8], zmin = 0.0f;
-      unpack_gu<SPLIT>(in[i], g, u);
+      float gg[8], u[8], d[8], da[8], db[8], zmin = 0.0f;
+      unpack_gu<SPLIT>(o.in[i], gg, u);
 #pragma unroll
       for (int c = 0; c < 8; c++) {
-        d[c] = (c & 1) ? bf_hi(D[i][c >> 1]) : bf_lo(D[i][c >> 1]);
-        glu_bwd_elem<ACT>(g[c], u[c], d[c], da[c], db[c], zmin);
+        d[c] = (c & 1) ? bf_hi(o.d[i][c >> 1]) : bf_lo(o.d[i][c >> 1]);
+        glu_bwd_elem<ACT>(gg[c], u[c], d[c], da[c], db[c], zmin);
       }
       if (zmin < TAIL_ZL2) {  // rare: e^z below the FP32 normal range
 #pragma unroll
         for (int c = 0; c < 8; c++)
-          if (zl2<ACT>(g[c]) < TAIL_ZL2) glu_bwd_tail<ACT>(g[c], u[c], d[c], da[c], db[c]);
+          if (zl2<ACT>(gg[c]) < TAIL_ZL2) glu_bwd_tail<ACT>(gg[c], u[c], d[c], da[c], db[c]);
       }
 #pragma unroll
       for (int k = 0; k < 4; k++) {
-        HA[i][k] = pack_bf16(da[2 * k], da[2 * k + 1]);
-        HB[i][k] = pack_bf16(db[2 * k], db[2 * k + 1]);
+        r.h[0][i][k] = pack_bf16(da[2 * k], da[2 * k + 1]);
+        r.h[1][i][k] = pack_bf16(db[2 * k], db[2 * k + 1]);
       }
     }
-    const MxOut o{a.q_row, a.s_row, a.q_col, a.s_col, a.M, 2 * a.N};
-    mx_store_bf16<FLAGS, FULL>(HA, o, r0, col, lr, lc, col_ok);
-    mx_store_bf16<FLAGS, FULL>(HB, o, r0, a.N + col, lr, lc, col_ok);
   }
 }
 
-template <int ACT, int LAYOUT, int FLAGS, int MODE, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void k_mxfp8(MxArgs a, uint32_t tiles_m,
-                                                          uint32_t ntiles, uint32_t per_xcd) {
-  constexpr int TILE_M = 32 * WGM, TILE_N = 64 * WGN;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int lr = lane & 7, lc = lane >> 3;
-  const uint32_t b = blockIdx.x;
-  const uint32_t t = GLU_MX_TILE_ORDER == 2 ? b : (b & 7) * per_xcd + (b >> 3);
-  if (t >= ntiles) return;
-  uint32_t tm, tn;
-  if constexpr (GLU_MX_TILE_ORDER == 0) {
-    tn = t / tiles_m;
-    tm = t - tn * tiles_m;
-  } else {
-    const uint32_t tiles_n = ntiles / tiles_m;
-    tm = t / tiles_n;
-    tn = t - tm * tiles_n;
+// LDS staging of one quantized part (the tile of h, or of da or db):
+//   rq  rowwise codes [TM][TN], row-major;      rs  rowwise scales [TM][TN/32];
+//   cq  colwise codes [TN][TM], column-major;   cs  colwise scales [TN][TM/32].
+// The 16-byte segments of each code row (rq) and column (cq) are XOR-swizzled, by
+// (row / 4) % 8 and (column / 8) % 8, so that the staging writes of a wave (8 rows 4 apart,
+// or 8 columns 8 apart, at the same offset) and the 16-byte reads of the write-out fall in
+// different banks.
+template <int FLAGS>
+struct Stage {
+  static constexpr int RQ = (FLAGS & ROWWISE) ? TM * TN : 0;
+  static constexpr int CQ = (FLAGS & COLWISE) ? TN * TM : 0;
+  static constexpr int RS = (FLAGS & ROWWISE) ? TM * (TN / 32) : 0;
+  static constexpr int CS = (FLAGS & COLWISE) ? TN * (TM / 32) : 0;
+  static constexpr int BYTES = RQ + CQ + RS + CS;
+  uint8_t* rq;
+  uint8_t* cq;
+  uint8_t* rs;
+  uint8_t* cs;
+  __device__ explicit Stage(uint8_t* base)
+      : rq(base), cq(base + RQ), rs(base + RQ + CQ), cs(base + RQ + CQ + RS) {}
+};
+
+// Byte offsets in rq of (row, col) and in cq of (col, row), within a 16-byte segment.
+__device__ __forceinline__ int rq_at(int row, int col) {
+  return row * TN + 16 * ((col >> 4) ^ ((row >> 2) & 7)) + (col & 15);
+}
+__device__ __forceinline__ int cq_at(int col, int row) {
+  return col * TM + 16 * ((row >> 4) ^ ((col >> 3) & 7)) + (row & 15);
+}
+
+__device__ __forceinline__ void lds_st8(uint8_t* p, uint32_t w0, uint32_t w1) {
+  *reinterpret_cast<u32x2*>(p) = (u32x2){w0, w1};
+}
+__device__ __forceinline__ void lds_st4(uint8_t* p, uint32_t w) { *reinterpret_cast<uint32_t*>(p) = w; }
+
+// Quantizes the lane's 4x8 BF16 values H[i][k] = (columns 2k, 2k+1 of tile row row0 + i),
+// tile columns col..col+7 (row0 = 32wm + 4lr, col = 64wn + 8lc), into the LDS stage.  All
+// 64 lanes of the wave take part (cross-lane maxima).  Elements outside the matrix were
+// loaded as zeros: they form blocks of their own (N and, when colwise, M are multiples of
+// 32), quantize to zero codes and are never written out.
+template <int FLAGS>
+__device__ __forceinline__ void stage_bf16(const uint32_t (&H)[4][4], const Stage<FLAGS>& st,
+                                           int row0, int col, int lr, int lc) {
+  uint32_t A[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int k = 0; k < 4; k++) A[i][k] = H[i][k] & 0x7fff7fffu;
+
+  uint32_t R01 = 0, R23 = 0;  // row block maxima, rows (0,1) and (2,3) packed
+  uint32_t C[4] = {0, 0, 0, 0};  // column block maxima, columns (2k, 2k+1) packed
+  if constexpr ((FLAGS & ROWWISE) != 0) {
+    uint32_t m[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) m[i] = pkmax(pkmax(A[i][0], A[i][1]), pkmax(A[i][2], A[i][3]));
+    R01 = pkmax(pair_lo(m[0], m[1]), pair_hi(m[0], m[1]));
+    R23 = pkmax(pair_lo(m[2], m[3]), pair_hi(m[2], m[3]));
+    R01 = pkmax(R01, dpp<DPP_ROW_ROR8>(R01));
+    R23 = pkmax(R23, dpp<DPP_ROW_ROR8>(R23));
+    R01 = pkmax(R01, swz_xor16(R01));
+    R23 = pkmax(R23, swz_xor16(R23));
   }
-  const int64_t r0 = (int64_t)tm * TILE_M + 32 * (w % WGM);
-  const int64_t cw = (int64_t)tn * TILE_N + 64 * (w / WGM);
-  if (r0 >= a.M || cw >= a.N) return;  // wave-uniform
-  const int64_t col = cw + 8 * lc;
-  const bool col_ok = col < a.N;
-  if (r0 + 32 <= a.M && cw + 64 <= a.N)  // wave-uniform
-    mx_tile<ACT, LAYOUT, FLAGS, MODE, true>(a, r0, col, lr, lc, col_ok);
-  else
-    mx_tile<ACT, LAYOUT, FLAGS, MODE, false>(a, r0, col, lr, lc, col_ok);
+  if constexpr ((FLAGS & COLWISE) != 0) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      uint32_t c = pkmax(pkmax(A[0][k], A[1][k]), pkmax(A[2][k], A[3][k]));
+      c = pkmax(c, dpp<DPP_XOR1>(c));
+      c = pkmax(c, dpp<DPP_XOR2>(c));
+      C[k] = pkmax(c, dpp<DPP_HALF_MIRROR>(c));
+    }
+  }
+  // any non-finite block among those this lane touches? (rare: patched after the fast path)
+  const uint32_t all = pkmax(pkmax(R01, R23), pkmax(pkmax(C[0], C[1]), pkmax(C[2], C[3])));
+  const bool nonfinite = umax(lo16(all), hi16(all)) >= 0x7f80u;
+
+  if constexpr ((FLAGS & ROWWISE) != 0) {
+    const uint32_t S01 = pk_scale_bytes(R01), S23 = pk_scale_bytes(R23);
+    const uint32_t sb[4] = {lo16(S01), hi16(S01), lo16(S23), hi16(S23)};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float sc = e8m0_value(sb[i]);
+      uint32_t w0 = fp8x2_scaled<false>(0u, H[i][0], sc);
+      w0 = fp8x2_scaled<true>(w0, H[i][1], sc);
+      uint32_t w1 = fp8x2_scaled<false>(0u, H[i][2], sc);
+      w1 = fp8x2_scaled<true>(w1, H[i][3], sc);
+      lds_st8(st.rq + rq_at(row0 + i, col), w0, w1);
+    }
+    // lane lc = 4b + i stages the scale of row 4lr + i in the wave's block b
+    const int i = lc & 3;
+    const uint32_t w = i < 2 ? S01 : S23;
+    st.rs[(row0 + i) * (TN / 32) + ((col - 8 * i) >> 5)] = (uint8_t)((i & 1) ? hi16(w) : lo16(w));
+  }
+  if constexpr ((FLAGS & COLWISE) != 0) {
+    uint32_t S[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) S[k] = pk_scale_bytes(C[k]);
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const float s0 = e8m0_value(lo16(S[k])), s1 = e8m0_value(hi16(S[k]));
+      // column 2k: rows (0,1) from the low halves, rows (2,3) likewise
+      uint32_t w0 = fp8x2_scaled<false>(0u, pair_lo(H[0][k], H[1][k]), s0);
+      w0 = fp8x2_scaled<true>(w0, pair_lo(H[2][k], H[3][k]), s0);
+      uint32_t w1 = fp8x2_scaled<false>(0u, pair_hi(H[0][k], H[1][k]), s1);
+      w1 = fp8x2_scaled<true>(w1, pair_hi(H[2][k], H[3][k]), s1);
+      lds_st4(st.cq + cq_at(col + 2 * k, row0), w0);
+      lds_st4(st.cq + cq_at(col + 2 * k + 1, row0), w1);
+    }
+    // lane lr stages the scale of column 8lc + lr of this 32-row block
+    const uint32_t w = (lr >> 1) == 0 ? S[0] : (lr >> 1) == 1 ? S[1] : (lr >> 1) == 2 ? S[2] : S[3];
+    st.cs[(col + lr) * (TM / 32) + (row0 >> 5)] = (uint8_t)((lr & 1) ? hi16(w) : lo16(w));
+  }
+
+  if (nonfinite) {
+    // a block holding NaN or Inf: scale 0xFF, every code 0x7F (overwrites the fast path; each
+    // lane patches only what it staged itself, so program order suffices)
+    if constexpr ((FLAGS & ROWWISE) != 0) {
+      const uint32_t rm[4] = {lo16(R01), hi16(R01), lo16(R23), hi16(R23)};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        if (rm[i] >= 0x7f80u) {
+          lds_st8(st.rq + rq_at(row0 + i, col), 0x7f7f7f7fu, 0x7f7f7f7fu);
+          if ((lc & 3) == i) st.rs[(row0 + i) * (TN / 32) + ((col - 8 * i) >> 5)] = 0xff;
+        }
+      }
+    }
+    if constexpr ((FLAGS & COLWISE) != 0) {
+#pragma unroll
+      for (int c = 0; c < 8; c++) {
+        const uint32_t cm = (c & 1) ? hi16(C[c >> 1]) : lo16(C[c >> 1]);
+        if (cm >= 0x7f80u) {
+          lds_st4(st.cq + cq_at(col + c, row0), 0x7f7f7f7fu);
+          if (lr == c) st.cs[(col + c) * (TM / 32) + (row0 >> 5)] = 0xff;
+        }
+      }
+    }
+  }
+}
+
+// The same rules on FP32 values (quantizer hook): magnitudes compared as FP32 bits, the
+// scaled value x * 2^-e computed exactly in FP32, then v_cvt_pk_fp8_f32.
+template <int FLAGS>
+__device__ __forceinline__ void stage_f32(const float (&v)[4][8], const Stage<FLAGS>& st,
+                                          int row0, int col, int lr, int lc) {
+  uint32_t ab[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int c = 0; c < 8; c++) ab[i][c] = __float_as_uint(v[i][c]) & 0x7fffffffu;
+
+  if constexpr ((FLAGS & ROWWISE) != 0) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      uint32_t m = ab[i][0];
+#pragma unroll
+      for (int c = 1; c < 8; c++) m = umax(m, ab[i][c]);
+      m = umax(m, dpp<DPP_ROW_ROR8>(m));
+      m = umax(m, swz_xor16(m));
+      const bool nonfinite = m >= 0x7f800000u;
+      const uint32_t b = nonfinite ? 0xffu : mx_scale_byte(m);
+      const float P = mx_inv_scale(nonfinite ? 0u : b);
+      packed |= b << (8 * i);
+      uint32_t w0 = fp8x2<false>(0u, v[i][0] * P, v[i][1] * P);
+      w0 = fp8x2<true>(w0, v[i][2] * P, v[i][3] * P);
+      uint32_t w1 = fp8x2<false>(0u, v[i][4] * P, v[i][5] * P);
+      w1 = fp8x2<true>(w1, v[i][6] * P, v[i][7] * P);
+      if (nonfinite) w0 = w1 = 0x7f7f7f7fu;
+      lds_st8(st.rq + rq_at(row0 + i, col), w0, w1);
+    }
+    const int i = lc & 3;
+    st.rs[(row0 + i) * (TN / 32) + ((col - 8 * i) >> 5)] = (uint8_t)(packed >> (8 * i));
+  }
+
+  if constexpr ((FLAGS & COLWISE) != 0) {
+    uint32_t packed0 = 0, packed1 = 0;
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      uint32_t m = umax(umax(ab[0][c], ab[1][c]), umax(ab[2][c], ab[3][c]));
+      m = umax(m, dpp<DPP_XOR1>(m));
+      m = umax(m, dpp<DPP_XOR2>(m));
+      m = umax(m, dpp<DPP_HALF_MIRROR>(m));
+      const bool nonfinite = m >= 0x7f800000u;
+      const uint32_t b = nonfinite ? 0xffu : mx_scale_byte(m);
+      const float P = mx_inv_scale(nonfinite ? 0u : b);
+      if (c < 4) packed0 |= b << (8 * c); else packed1 |= b << (8 * (c - 4));
+      uint32_t w = fp8x2<false>(0u, v[0][c] * P, v[1][c] * P);
+      w = fp8x2<true>(w, v[2][c] * P, v[3][c] * P);
+      if (nonfinite) w = 0x7f7f7f7fu;
+      lds_st4(st.cq + cq_at(col + c, row0), w);
+    }
+    const uint32_t w = lr < 4 ? packed0 : packed1;
+    st.cs[(col + lr) * (TM / 32) + (row0 >> 5)] = (uint8_t)(w >> (8 * (lr & 3)));
+  }
+}
+
+template <bool NT>
+__device__ __forceinline__ void st16(uint8_t* p, u32x4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// Writes a staged part to global memory: the part is the [M, N] matrix at column offset
+// `coloff` of the quantized matrix, whose rows hold ldq codes; the tile starts at (r0, c0).
+// Rows >= M and columns >= N are skipped, in whole 16-byte segments (N and, when colwise,
+// M are multiples of 32).  Scale words are written whole where the 4 bytes are in range and
+// 4-byte aligned, else byte by byte.
+template <int FLAGS, bool NT>
+__device__ __forceinline__ void write_out(const Stage<FLAGS>& st, const MxArgs& a, int64_t r0,
+                                          int64_t c0, int64_t coloff, int64_t ldq, int tid) {
+  const int64_t M = a.M, N = a.N;
+  if constexpr ((FLAGS & ROWWISE) != 0) {
+    constexpr int SEGS = TN / 16;
+#pragma unroll
+    for (int k = tid; k < TM * SEGS; k += NTHREADS) {
+      const int row = k / SEGS, seg = k % SEGS;
+      if (r0 + row < M && c0 + 16 * seg < N) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st.rq + row * TN + 16 * (seg ^ ((row >> 2) & 7)));
+        st16<NT>(a.q_row + (r0 + row) * ldq + coloff + c0 + 16 * seg, v);
+      }
+    }
+    const int64_t nb = ldq / 32;
+    const bool whole = nb % 4 == 0 && (coloff / 32) % 4 == 0 && c0 + TN <= N;
+    for (int row = tid; row < TM; row += NTHREADS) {
+      if (r0 + row < M) {
+        uint8_t* dst = a.s_row + (r0 + row) * nb + (coloff + c0) / 32;
+        const uint8_t* src = st.rs + row * (TN / 32);
+        if (whole) {
+          *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+        } else {
+          for (int b = 0; b < TN / 32; b++)
+            if (c0 + 32 * b < N) dst[b] = src[b];
+        }
+      }
+    }
+  }
+  if constexpr ((FLAGS & COLWISE) != 0) {
+    constexpr int SEGS = TM / 16;
+#pragma unroll
+    for (int k = tid; k < TN * SEGS; k += NTHREADS) {
+      const int col = k / SEGS, seg = k % SEGS;
+      if (c0 + col < N && r0 + 16 * seg < M) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st.cq + col * TM + 16 * (seg ^ ((col >> 3) & 7)));
+        st16<NT>(a.q_col + (coloff + c0 + col) * M + r0 + 16 * seg, v);
+      }
+    }
+    const int64_t nb = M / 32;
+    const bool whole = nb % 4 == 0 && r0 + TM <= M;
+    for (int col = tid; col < TN; col += NTHREADS) {
+      if (c0 + col < N) {
+        uint8_t* dst = a.s_col + (coloff + c0 + col) * nb + r0 / 32;
+        const uint8_t* src = st.cs + col * (TM / 32);
+        if (whole) {
+          *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+        } else {
+          for (int b = 0; b < TM / 32; b++)
+            if (r0 + 32 * b < M) dst[b] = src[b];
+        }
+      }
+    }
+  }
+}
+
+// One workgroup per tile.  Workgroup id b runs on XCD b % 8 (workgroups are dealt to the
+// XCDs round-robin); XCD x takes tiles x * per_xcd + b / 8 of the tile order.
+template <int ACT, int LAYOUT, int FLAGS, int MODE>
+__global__ __launch_bounds__(NTHREADS) void k_mxfp8(MxArgs a, uint32_t tiles_m, uint32_t tiles_n,
+                                                    uint32_t ntiles, uint32_t per_xcd) {
+  constexpr int PARTS = MODE == MODE_BWD ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[PARTS * Stage<FLAGS>::BYTES];
+  const uint32_t t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (t >= ntiles) return;  // the whole workgroup
+  uint32_t tm, tn;
+  tile_of<tile_order<FLAGS>()>(t, tiles_m, tiles_n, tm, tn);
+  const int64_t r0 = (int64_t)tm * TM, c0 = (int64_t)tn * TN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int wm = w % WGM, wn = w / WGM;
+  const int lr = lane & 7, lc = lane >> 3;
+
+  TileGeom g;
+  g.r0 = r0 + 32 * wm;
+  g.cw = c0 + 64 * wn;
+  g.col = g.cw + 8 * lc;
+  g.col_ok = g.col < a.N;
+  TileOps<LAYOUT, MODE> o;
+  load_ops<LAYOUT, MODE>(o, a, g, lr, lc);
+  TileVals<MODE> R;
+  compute<ACT, LAYOUT, MODE>(R, o);
+
+  const int row0 = 32 * wm + 4 * lr, col = 64 * wn + 8 * lc;
+  if constexpr (MODE == MODE_F32) {
+    stage_f32<FLAGS>(R.v, Stage<FLAGS>(lds), row0, col, lr, lc);
+  } else {
+    stage_bf16<FLAGS>(R.h[0], Stage<FLAGS>(lds), row0, col, lr, lc);
+    if constexpr (MODE == MODE_BWD)
+      stage_bf16<FLAGS>(R.h[1], Stage<FLAGS>(lds + Stage<FLAGS>::BYTES), row0, col, lr, lc);
+  }
+  __syncthreads();
+  const int64_t ldq = PARTS * a.N;
+  constexpr bool NT = nt_stores<MODE, FLAGS>();
+  write_out<FLAGS, NT>(Stage<FLAGS>(lds), a, r0, c0, 0, ldq, tid);
+  if constexpr (MODE == MODE_BWD)
+    write_out<FLAGS, NT>(Stage<FLAGS>(lds + Stage<FLAGS>::BYTES), a, r0, c0, a.N, ldq, tid);
 }
 
 template <int ACT, int LAYOUT, int FLAGS, int MODE>
 hipError_t launch(const MxArgs& a, hipStream_t s) {
-  constexpr int WGM = WgShape<MODE, FLAGS>::M, WGN = WgShape<MODE, FLAGS>::N;
-  constexpr int TILE_M = 32 * WGM, TILE_N = 64 * WGN;
-  const int64_t tiles_m = (a.M + TILE_M - 1) / TILE_M;
-  const int64_t tiles_n = (a.N + TILE_N - 1) / TILE_N;
-  const int64_t ntiles = tiles_m * tiles_n;
-  const int64_t per_xcd = (ntiles + 7) / 8;
-  const dim3 grid((unsigned)(8 * per_xcd)), block(64 * WGM * WGN);
-  constexpr int LDS = WgShape<MODE, FLAGS>::LDS;
-  auto k = k_mxfp8<ACT, LAYOUT, FLAGS, MODE, WGM, WGN>;
-  if constexpr (LDS > 65536) {
-    const hipError_t e =
-        hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-    if (e != hipSuccess) return e;
-  }
-  return launch_kernel_shm(k, grid, block, LDS, s, a, (uint32_t)tiles_m, (uint32_t)ntiles,
-                           (uint32_t)per_xcd);
+  const int64_t tiles_m = (a.M + TM - 1) / TM, tiles_n = (a.N + TN - 1) / TN;
+  const int64_t ntiles = tiles_m * tiles_n, per_xcd = (ntiles + 7) / 8;
+  return launch_kernel(k_mxfp8<ACT, LAYOUT, FLAGS, MODE>, dim3((unsigned)(8 * per_xcd)),
+                       dim3(NTHREADS), s, a, (uint32_t)tiles_m, (uint32_t)tiles_n, (uint32_t)ntiles,
+                       (uint32_t)per_xcd);
 }
 
 template <int ACT, int LAYOUT, int MODE>

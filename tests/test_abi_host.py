@@ -130,6 +130,9 @@ def test_fwd_mxfp8_checks():
     assert mxf(sr=D0 + 1) == ALIGN
     assert mxf(qr=A0) == OVERLAP and mxf(sr=C0 + 16) == OVERLAP
     assert mxf(layout=1, up=0, ld=256) == OK and mxf(layout=1, up=0, ld=128) == STRIDE
+    # row pitch limit of the MXFP8 kernels: 2^24 elements
+    row = dict(M=1, flags=1, qc=0, sc=0)
+    assert mxf(ld=1 << 24, **row) == OK and mxf(ld=(1 << 24) + 8, **row) == STRIDE
 
 
 def mxb(**kw):
@@ -146,6 +149,9 @@ def test_bwd_mxfp8_checks():
     assert mxb(layout=1, up=0) == UNSUP
     assert mxb(dh=0) == NULL
     assert mxb(lddh=120) == STRIDE and mxb(lddh=132) == STRIDE
+    row = dict(M=1, flags=1, qc=0, sc=0)
+    assert mxb(ld=1 << 24, lddh=1 << 24, **row) == OK
+    assert mxb(ld=(1 << 24) + 8, **row) == STRIDE and mxb(lddh=(1 << 24) + 8, **row) == STRIDE
     assert mxb(qr=C0) == OVERLAP
     assert mxb(N=40, ld=40, lddh=40) == SHAPE
 
@@ -178,6 +184,8 @@ def test_quant_hook_checks():
     assert q(64, 64, P(A0), 66, 3, P(B0), P(C0), P(D0), P(E0)) == STRIDE
     assert q(64, 64, P(A0), 60, 3, P(B0), P(C0), P(D0), P(E0)) == STRIDE
     assert q(64, 64, P(A0), 64, 1, P(B0), P(C0), P(0), P(0)) == OK
+    assert q(1, 64, P(A0), 1 << 23, 1, P(B0), P(C0), P(0), P(0)) == OK
+    assert q(1, 64, P(A0), (1 << 23) + 4, 1, P(B0), P(C0), P(0), P(0)) == STRIDE
     n = L.glu_check_quant_nvfp4_f32
     assert n(64, 64, P(A0), 64, P(B0), P(C0), 0) == OK
     assert n(64, 72, P(A0), 72, P(B0), P(C0), 0) == SHAPE
