@@ -27,6 +27,17 @@ constexpr int64_t kMaxTiles = (int64_t)1 << 30;
 // Largest row pitch, in bytes, of an MXFP8 kernel operand: the kernels address 32 rows from a
 // per-piece base with 32-bit offsets that must stay below 2^31.
 constexpr int64_t kMaxMxPitchBytes = (int64_t)1 << 25;
+// Largest row pitch, in bytes, of an MXFP8 code output (rowwise: the quantized matrix's
+// width; colwise: M): the kernels address 128 output rows from a per-tile base with 32-bit
+// offsets that must stay below 2^31.
+constexpr int64_t kMaxMxOutPitch = (int64_t)1 << 24;
+
+// Output pitches of an MXFP8 launch whose quantized matrix is [M, width].
+glu_status check_mx_pitch(int flags, int64_t M, int64_t width) {
+  if ((flags & glu::ROWWISE) && width > kMaxMxOutPitch) return GLU_ERR_SHAPE;
+  if ((flags & glu::COLWISE) && M > kMaxMxOutPitch) return GLU_ERR_SHAPE;
+  return GLU_OK;
+}
 
 // Byte extent of a row-major matrix: ((rows - 1) * ld + cols) * esz, or -1 on overflow.
 int64_t extent_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esz) {
@@ -212,6 +223,7 @@ glu_status glu_check_fwd_mxfp8(int act, int layout, int64_t M, int64_t N, const 
   if (st != GLU_OK) return st;
   if ((st = check_mx_outputs(flags, q_row, s_row, q_col, s_col)) != GLU_OK) return st;
   if (N % 32 != 0 || ((flags & glu::COLWISE) && M % 32 != 0)) return GLU_ERR_SHAPE;
+  if ((st = check_mx_pitch(flags, M, N)) != GLU_OK) return st;
   if (ld_in % 8 != 0 || ld_in > kMaxMxPitchBytes / 2) return GLU_ERR_STRIDE;
   if (!aligned16(gate) || !aligned16(up) || !aligned16(q_row) || !aligned16(s_row) ||
       !aligned16(q_col) || !aligned16(s_col))
@@ -238,6 +250,7 @@ glu_status glu_check_bwd_mxfp8(int act, int layout, int64_t M, int64_t N, const 
   if (dh == nullptr) return GLU_ERR_NULL;
   if ((st = check_mx_outputs(flags, q_row, s_row, q_col, s_col)) != GLU_OK) return st;
   if (N % 32 != 0 || ((flags & glu::COLWISE) && M % 32 != 0)) return GLU_ERR_SHAPE;
+  if ((st = check_mx_pitch(flags, M, 2 * N)) != GLU_OK) return st;
   if (ld_dh < N) return GLU_ERR_STRIDE;
   if (ld_in % 8 != 0 || ld_dh % 8 != 0) return GLU_ERR_STRIDE;
   if (ld_in > kMaxMxPitchBytes / 2 || ld_dh > kMaxMxPitchBytes / 2) return GLU_ERR_STRIDE;
@@ -287,6 +300,7 @@ glu_status glu_check_quant_mxfp8_f32(int64_t M, int64_t N, const float* x, int64
   glu_status st = check_mx_outputs(flags, q_row, s_row, q_col, s_col);
   if (st != GLU_OK) return st;
   if (N % 32 != 0 || ((flags & glu::COLWISE) && M % 32 != 0)) return GLU_ERR_SHAPE;
+  if ((st = check_mx_pitch(flags, M, N)) != GLU_OK) return st;
   if (ld_x < N || ld_x % 4 != 0 || ld_x > kMaxMxPitchBytes / 4) return GLU_ERR_STRIDE;
   if (!aligned16(x) || !aligned16(q_row) || !aligned16(s_row) || !aligned16(q_col) ||
       !aligned16(s_col))

@@ -92,12 +92,16 @@ __device__ __forceinline__ double exp2_tail(float zl) {
   return __builtin_ldexp((double)__builtin_amdgcn_exp2f(zc - n), (int)n);
 }
 
-// Forward: act(g) * u in FP32 (the caller rounds it to BF16).
+// Forward: act(g) * u in FP32 (the caller rounds it to BF16).  Accurate for
+// zl2(g) >= TAIL_ZL2; zmin tracks the smallest zl2 so the caller can switch to the tail.
+template <int ACT>
+__device__ __forceinline__ float glu_fwd_fast(float g, float u) {
+  return (g * sigmoid_from(exp_neg(zl2<ACT>(g)))) * u;
+}
 template <int ACT>
 __device__ __forceinline__ float glu_fwd_elem(float g, float u, float& zmin) {
-  const float zl = zl2<ACT>(g);
-  zmin = __builtin_fminf(zmin, zl);
-  return (g * sigmoid_from(exp_neg(zl))) * u;
+  zmin = __builtin_fminf(zmin, zl2<ACT>(g));
+  return glu_fwd_fast<ACT>(g, u);
 }
 
 template <int ACT>
@@ -105,18 +109,34 @@ __device__ __forceinline__ float glu_fwd_tail(float g, float u) {
   return (float)((double)g * exp2_tail(zl2<ACT>(g)) * (double)u);
 }
 
-// Backward: da = dh u act'(g), db = dh act(g), FP32 before rounding.
+// Backward: da = dh u act'(g), db = dh act(g), FP32 before rounding, as
+// q = dh sigma(z), db = q g, da = (q u)(1 + (g sigma(-z)) z'(g)).  g sigma(-z) is taken
+// before z'(g): for large g, z'(g) g overflows while sigma(-z) is 0.
+template <int ACT>
+__device__ __forceinline__ void glu_bwd_fast(float g, float u, float d, float& da, float& db) {
+  const float e = exp_neg(zl2<ACT>(g));
+  const float sp = sigmoid_from(e);  // sigma(z)
+  const float q = d * sp;
+  db = q * g;
+  const float sn = e * sp;           // sigma(-z)
+  const float s = ACT == SWIGLU ? __builtin_fmaf(g, sn, 1.0f) : __builtin_fmaf(g * sn, dz<ACT>(g), 1.0f);
+  da = (q * u) * s;
+}
 template <int ACT>
 __device__ __forceinline__ void glu_bwd_elem(float g, float u, float d, float& da, float& db,
                                              float& zmin) {
-  const float zl = zl2<ACT>(g);
-  zmin = __builtin_fminf(zmin, zl);
-  const float e = exp_neg(zl);
-  const float sp = sigmoid_from(e);  // sigma(z)
-  const float sn = e * sp;           // sigma(-z)
-  const float grad = sp * __builtin_fmaf(g * sn, dz<ACT>(g), 1.0f);
-  da = (d * u) * grad;
-  db = d * (g * sp);
+  zmin = __builtin_fminf(zmin, zl2<ACT>(g));
+  glu_bwd_fast<ACT>(g, u, d, da, db);
+}
+
+// Wave-level trigger of the tail path from raw BF16 gate bit patterns: m16 is their maximum
+// as unsigned 16-bit numbers, under which negative values order by magnitude above 0x8000
+// and non-negative ones stay below.  True when some gate value is below G with
+// zl2(g) >= TAIL_ZL2 for every g >= G: SwiGLU G = -80 (zl2 >= -115.5), GeGLU G = -9.5
+// (zl2 >= -110.2).  Negative NaNs trigger it too (harmless: both paths return NaN).
+template <int ACT>
+__device__ __forceinline__ bool tail_possible(uint32_t m16) {
+  return m16 > (ACT == SWIGLU ? 0xC2A0u : 0xC118u);  // BF16 -80, -9.5
 }
 
 template <int ACT>

@@ -3,11 +3,12 @@
 // the FP32 quantizer hook that runs the same block rules on given FP32 values.
 //
 // Work decomposition (wave64):
-//   A workgroup owns a TM x TN = 128 x 128 tile of the quantized matrix (of each of da and db
-//   in the backward) with WGM x WGN = 4 x 2 waves.  A wave covers 32 rows x 64 columns: one
-//   32-row colwise block row and two 32-column rowwise blocks per row.  Lane = lr + 8*lc owns
-//   rows 4lr..4lr+3 and columns 8lc..8lc+7 of the wave's piece: 16-byte loads per row and per
-//   operand, 32 elements per lane, kept after the activation as 16 packed BF16 pairs.
+//   A workgroup owns a TM x TN tile of the quantized matrix (of each of da and db in the
+//   backward): 128 x 128 with 4 x 2 waves, or 64 x 128 with 2 x 2 waves when only rowwise
+//   codes are written.  A wave covers 32 rows x 64 columns: one 32-row colwise block row and
+//   two 32-column rowwise blocks per row.  Lane = lr + 8*lc owns rows 4lr..4lr+3 and columns
+//   8lc..8lc+7 of the wave's piece: 16-byte loads per row and per operand, 32 elements per
+//   lane, kept after the activation as 16 packed BF16 pairs.
 //   Rowwise amax of a 32-column block spans the 4 lanes lc = 4b..4b+3 (lane bits 3, 4):
 //   DPP row_ror:8 then ds_swizzle xor 16.  Colwise amax of a 32-row block spans the 8
 //   lanes lr = 0..7 (lane bits 0..2) after an in-lane max over 4 rows: DPP quad_perm xor 1,
@@ -15,13 +16,13 @@
 //   columns, or two rows, per instruction).
 //   Codes and scales are staged in LDS and leave, after one workgroup barrier, as 16-byte
 //   stores that fill whole 128-byte lines: a tile row of rowwise codes and a tile column of
-//   colwise codes are 128 bytes each, and the scales of a tile row (column) are one 4-byte
-//   word.  Straight from the registers the same data would leave as 32-byte (colwise) and
-//   64-byte (rowwise) pieces and single scale bytes: several times more L2 write requests,
-//   which measured as the limit once enough tiles run concurrently to keep HBM busy.
-//   Tiles are dealt to the 8 XCDs in contiguous runs along M (workgroups go to XCDs
-//   round-robin by id), so neighbouring tiles along M, which share the transposed colwise
-//   output's scale words, run on one XCD at about the same time.
+//   colwise codes are 128 bytes each (colwise output always uses 128-row tiles), and the
+//   scales of a tile row (column) are one 4-byte word.  Straight from the registers the same
+//   data would leave as 32-byte (colwise) and 64-byte (rowwise) pieces and single scale
+//   bytes: several times more L2 write requests, which measured as the limit once enough
+//   tiles run concurrently to keep HBM busy.
+//   Each XCD takes a contiguous run of a tile order chosen per direction (below), so tiles
+//   that share output lines and scale sectors run on one XCD at about the same time.
 #include "glu_device.h"
 #include "glu_launch.h"
 
@@ -41,13 +42,29 @@ namespace {
 #ifndef GLU_MX_TILE_ORDER
 #define GLU_MX_TILE_ORDER -1
 #endif
+//   GLU_MX_TPW: if set, the tiles per workgroup of every kernel (else per kernel, below).
 
 enum { MODE_FWD = 0, MODE_BWD = 1, MODE_F32 = 2 };
 
-constexpr int WGM = 4, WGN = 2;                 // waves per workgroup along M and N
-constexpr int TM = 32 * WGM, TN = 64 * WGN;     // quantized tile per workgroup
-constexpr int NTHREADS = 64 * WGM * WGN;
-static_assert(TM == 128 && TN == 128, "the LDS swizzles and 4-byte scale words assume 128 x 128");
+// Tile of the quantized matrix per workgroup: WM x WN waves, each covering 32 x 64 elements.
+// Every code line leaves as 128 bytes: rowwise codes need TN = 128, colwise codes TM = 128.
+template <int WM_, int WN_>
+struct Tile {
+  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int TM = 32 * WM, TN = 64 * WN;
+  static constexpr int NTHREADS = 64 * WM * WN;
+  static constexpr int RSEG = TN / 16, CSEG = TM / 16;  // 16-byte segments per code line
+  // order-2 block: the tiles of a block that share rows (columns) fill one 32-byte sector of
+  // rowwise (colwise) scale words, TN / 32 (TM / 32) bytes per tile
+  static constexpr int BM = 32 / (TM / 32), BN = 32 / (TN / 32);
+  static_assert((TM == 64 || TM == 128) && TN == 128, "shapes the swizzles and scale words fit");
+};
+
+// Tile per direction, from interleaved measurements at [16384, 7168]: rowwise only 64 x 128
+// (backward 168 vs 176 us with 128 x 128: smaller workgroups, four per CU), otherwise
+// 128 x 128 (a 128 x 64 tile for colwise only was 2-3% slower).
+template <int FLAGS>
+using TileOf = Tile<FLAGS == ROWWISE ? 2 : 4, 2>;
 
 // Non-temporal code stores: measured faster only for the backward quantized both ways
 // (234 vs 267 us at [16384, 7168] in the blocked tile order); slower for the forward both
@@ -63,15 +80,23 @@ constexpr bool nt_stores() {
 //     transposed [N, M] output and fill its scale rows word after word.
 //   1 (rowwise only): along N first, so consecutive tiles continue the same input and output
 //     rows and fill the rowwise scale rows word after word (about 3% faster at [16384, 7168]).
-//   2 (both): strips of 8 tile columns; in a strip, blocks of 8 x 8 tiles going down M; in a
-//     block, along M first.  The 8 tiles of a block that share rows (columns) write their
-//     4-byte rowwise (colwise) scale words into one 32-byte sector within the same window of
+//   2 (both): strips of BN tile columns; in a strip, blocks of BM x BN tiles going down M; in
+//     a block, along M first.  The tiles of a block that share rows (columns) write their
+//     rowwise (colwise) scale words into one 32-byte sector within the same window of
 //     concurrent tiles, so both scale streams leave L2 as whole sectors (orders 0 and 1 leave
-//     one of them as single words: 6% slower at [16384, 7168]).
-#ifndef GLU_MX_ORDER_BLOCK  // build-time override of the block size, for measurements
-#define GLU_MX_ORDER_BLOCK 8
+//     one of them as single words: 6% slower at [16384, 7168]; blocks of 4 x 4 or 16 x 16
+//     128 x 128 tiles were 8% and 2% slower than 8 x 8).
+// Tiles per workgroup: with more than one, the next tile's loads overlap the current tile's
+// write-out.  One is fastest: the prefetch buffer costs more in occupancy than it gains
+// (backward both 248 vs 234 us at [16384, 7168] with two).
+template <int MODE>
+constexpr int tiles_per_workgroup() {
+#ifdef GLU_MX_TPW
+  return GLU_MX_TPW;
+#else
+  return 1;
 #endif
-constexpr int kOrderBlock = GLU_MX_ORDER_BLOCK;  // 4: 252, 8: 234, 16: 238 us backward both
+}
 
 template <int FLAGS>
 constexpr int tile_order() {
@@ -79,7 +104,7 @@ constexpr int tile_order() {
                                 : FLAGS == ROWWISE ? 1 : FLAGS == COLWISE ? 0 : 2;
 }
 
-template <int ORDER>
+template <class T, int ORDER>
 __device__ __forceinline__ void tile_of(uint32_t t, uint32_t tiles_m, uint32_t tiles_n,
                                         uint32_t& tm, uint32_t& tn) {
   if constexpr (ORDER == 0) {
@@ -89,15 +114,15 @@ __device__ __forceinline__ void tile_of(uint32_t t, uint32_t tiles_m, uint32_t t
     tm = t / tiles_n;
     tn = t - tm * tiles_n;
   } else {
-    constexpr uint32_t B = kOrderBlock;
-    const uint32_t strip = tiles_m * B;  // tiles per full strip
+    constexpr uint32_t BM = T::BM, BN = T::BN;
+    const uint32_t strip = tiles_m * BN;  // tiles per full strip
     const uint32_t bj = t / strip, u = t - bj * strip;
-    const uint32_t w = tiles_n - bj * B < B ? tiles_n - bj * B : B;  // strip width
-    const uint32_t bi = u / (B * w), v = u - bi * B * w;
-    const uint32_t h = tiles_m - bi * B < B ? tiles_m - bi * B : B;  // block height
+    const uint32_t w = tiles_n - bj * BN < BN ? tiles_n - bj * BN : BN;  // strip width
+    const uint32_t bi = u / (BM * w), v = u - bi * BM * w;
+    const uint32_t h = tiles_m - bi * BM < BM ? tiles_m - bi * BM : BM;  // block height
     const uint32_t j = v / h;
-    tm = bi * B + (v - j * h);
-    tn = bj * B + j;
+    tm = bi * BM + (v - j * h);
+    tn = bj * BN + j;
   }
 }
 
@@ -254,6 +279,19 @@ struct TileVals {
   float v[MODE == MODE_F32 ? 4 : 1][8];
 };
 
+// Largest raw gate bit pattern of the lane's operands, as an unsigned 16-bit number (the
+// argument of tail_possible).
+template <int LAYOUT>
+__device__ __forceinline__ uint32_t gate_max16(const GU<LAYOUT> (&in)[4]) {
+  uint32_t m = in[0].a[0];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int k = 0; k < (LAYOUT == SPLIT ? 4 : 8); k++)
+      if (i || k) m = pkmax(m, in[i].a[k]);
+  return LAYOUT == SPLIT ? umax(lo16(m), hi16(m)) : lo16(m);  // paired: gate is the low half
+}
+
 template <int ACT, int LAYOUT, int MODE>
 __device__ __forceinline__ void compute(TileVals<MODE>& r, const TileOps<LAYOUT, MODE>& o) {
   if constexpr (MODE == MODE_F32) {
@@ -262,13 +300,14 @@ __device__ __forceinline__ void compute(TileVals<MODE>& r, const TileOps<LAYOUT,
 #pragma unroll
       for (int c = 0; c < 8; c++) r.v[i][c] = __uint_as_float(o.x[i][c]);
   } else if constexpr (MODE == MODE_FWD) {
+    const bool tail = tail_possible<ACT>(gate_max16<LAYOUT>(o.in));
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      float gg[8], u[8], h[8], zmin = 0.0f;
+      float gg[8], u[8], h[8];
       unpack_gu<LAYOUT>(o.in[i], gg, u);
 #pragma unroll
-      for (int c = 0; c < 8; c++) h[c] = glu_fwd_elem<ACT>(gg[c], u[c], zmin);
-      if (zmin < TAIL_ZL2) {  // rare: e^z below the FP32 normal range
+      for (int c = 0; c < 8; c++) h[c] = glu_fwd_fast<ACT>(gg[c], u[c]);
+      if (tail) {  // rare: some e^z may be below the FP32 normal range
 #pragma unroll
         for (int c = 0; c < 8; c++)
           if (zl2<ACT>(gg[c]) < TAIL_ZL2) h[c] = glu_fwd_tail<ACT>(gg[c], u[c]);
@@ -277,16 +316,17 @@ __device__ __forceinline__ void compute(TileVals<MODE>& r, const TileOps<LAYOUT,
       for (int k = 0; k < 4; k++) r.h[0][i][k] = pack_bf16(h[2 * k], h[2 * k + 1]);
     }
   } else {
+    const bool tail = tail_possible<ACT>(gate_max16<SPLIT>(o.in));
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      float gg[8], u[8], d[8], da[8], db[8], zmin = 0.0f;
+      float gg[8], u[8], d[8], da[8], db[8];
       unpack_gu<SPLIT>(o.in[i], gg, u);
 #pragma unroll
       for (int c = 0; c < 8; c++) {
         d[c] = (c & 1) ? bf_hi(o.d[i][c >> 1]) : bf_lo(o.d[i][c >> 1]);
-        glu_bwd_elem<ACT>(gg[c], u[c], d[c], da[c], db[c], zmin);
+        glu_bwd_fast<ACT>(gg[c], u[c], d[c], da[c], db[c]);
       }
-      if (zmin < TAIL_ZL2) {  // rare: e^z below the FP32 normal range
+      if (tail) {  // rare: some e^z may be below the FP32 normal range
 #pragma unroll
         for (int c = 0; c < 8; c++)
           if (zl2<ACT>(gg[c]) < TAIL_ZL2) glu_bwd_tail<ACT>(gg[c], u[c], d[c], da[c], db[c]);
@@ -303,16 +343,16 @@ __device__ __forceinline__ void compute(TileVals<MODE>& r, const TileOps<LAYOUT,
 // LDS staging of one quantized part (the tile of h, or of da or db):
 //   rq  rowwise codes [TM][TN], row-major;      rs  rowwise scales [TM][TN/32];
 //   cq  colwise codes [TN][TM], column-major;   cs  colwise scales [TN][TM/32].
-// The 16-byte segments of each code row (rq) and column (cq) are XOR-swizzled, by
-// (row / 4) % 8 and (column / 8) % 8, so that the staging writes of a wave (8 rows 4 apart,
+// The 16-byte segments of each code row (rq) and column (cq) are XOR-swizzled, by row / 4
+// and column / 8 modulo the segments per line, so that the staging writes of a wave (8 rows 4 apart,
 // or 8 columns 8 apart, at the same offset) and the 16-byte reads of the write-out fall in
 // different banks.
-template <int FLAGS>
+template <class T, int FLAGS>
 struct Stage {
-  static constexpr int RQ = (FLAGS & ROWWISE) ? TM * TN : 0;
-  static constexpr int CQ = (FLAGS & COLWISE) ? TN * TM : 0;
-  static constexpr int RS = (FLAGS & ROWWISE) ? TM * (TN / 32) : 0;
-  static constexpr int CS = (FLAGS & COLWISE) ? TN * (TM / 32) : 0;
+  static constexpr int RQ = (FLAGS & ROWWISE) ? T::TM * T::TN : 0;
+  static constexpr int CQ = (FLAGS & COLWISE) ? T::TN * T::TM : 0;
+  static constexpr int RS = (FLAGS & ROWWISE) ? T::TM * (T::TN / 32) : 0;
+  static constexpr int CS = (FLAGS & COLWISE) ? T::TN * (T::TM / 32) : 0;
   static constexpr int BYTES = RQ + CQ + RS + CS;
   uint8_t* rq;
   uint8_t* cq;
@@ -323,11 +363,13 @@ struct Stage {
 };
 
 // Byte offsets in rq of (row, col) and in cq of (col, row), within a 16-byte segment.
+template <class T>
 __device__ __forceinline__ int rq_at(int row, int col) {
-  return row * TN + 16 * ((col >> 4) ^ ((row >> 2) & 7)) + (col & 15);
+  return row * T::TN + 16 * ((col >> 4) ^ ((row >> 2) & (T::RSEG - 1))) + (col & 15);
 }
+template <class T>
 __device__ __forceinline__ int cq_at(int col, int row) {
-  return col * TM + 16 * ((row >> 4) ^ ((col >> 3) & 7)) + (row & 15);
+  return col * T::TM + 16 * ((row >> 4) ^ ((col >> 3) & (T::CSEG - 1))) + (row & 15);
 }
 
 __device__ __forceinline__ void lds_st8(uint8_t* p, uint32_t w0, uint32_t w1) {
@@ -340,8 +382,8 @@ __device__ __forceinline__ void lds_st4(uint8_t* p, uint32_t w) { *reinterpret_c
 // 64 lanes of the wave take part (cross-lane maxima).  Elements outside the matrix were
 // loaded as zeros: they form blocks of their own (N and, when colwise, M are multiples of
 // 32), quantize to zero codes and are never written out.
-template <int FLAGS>
-__device__ __forceinline__ void stage_bf16(const uint32_t (&H)[4][4], const Stage<FLAGS>& st,
+template <class T, int FLAGS>
+__device__ __forceinline__ void stage_bf16(const uint32_t (&H)[4][4], const Stage<T, FLAGS>& st,
                                            int row0, int col, int lr, int lc) {
   uint32_t A[4][4];
 #pragma unroll
@@ -385,12 +427,12 @@ __device__ __forceinline__ void stage_bf16(const uint32_t (&H)[4][4], const Stag
       w0 = fp8x2_scaled<true>(w0, H[i][1], sc);
       uint32_t w1 = fp8x2_scaled<false>(0u, H[i][2], sc);
       w1 = fp8x2_scaled<true>(w1, H[i][3], sc);
-      lds_st8(st.rq + rq_at(row0 + i, col), w0, w1);
+      lds_st8(st.rq + rq_at<T>(row0 + i, col), w0, w1);
     }
     // lane lc = 4b + i stages the scale of row 4lr + i in the wave's block b
     const int i = lc & 3;
     const uint32_t w = i < 2 ? S01 : S23;
-    st.rs[(row0 + i) * (TN / 32) + ((col - 8 * i) >> 5)] = (uint8_t)((i & 1) ? hi16(w) : lo16(w));
+    st.rs[(row0 + i) * (T::TN / 32) + ((col - 8 * i) >> 5)] = (uint8_t)((i & 1) ? hi16(w) : lo16(w));
   }
   if constexpr ((FLAGS & COLWISE) != 0) {
     uint32_t S[4];
@@ -404,12 +446,12 @@ __device__ __forceinline__ void stage_bf16(const uint32_t (&H)[4][4], const Stag
       w0 = fp8x2_scaled<true>(w0, pair_lo(H[2][k], H[3][k]), s0);
       uint32_t w1 = fp8x2_scaled<false>(0u, pair_hi(H[0][k], H[1][k]), s1);
       w1 = fp8x2_scaled<true>(w1, pair_hi(H[2][k], H[3][k]), s1);
-      lds_st4(st.cq + cq_at(col + 2 * k, row0), w0);
-      lds_st4(st.cq + cq_at(col + 2 * k + 1, row0), w1);
+      lds_st4(st.cq + cq_at<T>(col + 2 * k, row0), w0);
+      lds_st4(st.cq + cq_at<T>(col + 2 * k + 1, row0), w1);
     }
     // lane lr stages the scale of column 8lc + lr of this 32-row block
     const uint32_t w = (lr >> 1) == 0 ? S[0] : (lr >> 1) == 1 ? S[1] : (lr >> 1) == 2 ? S[2] : S[3];
-    st.cs[(col + lr) * (TM / 32) + (row0 >> 5)] = (uint8_t)((lr & 1) ? hi16(w) : lo16(w));
+    st.cs[(col + lr) * (T::TM / 32) + (row0 >> 5)] = (uint8_t)((lr & 1) ? hi16(w) : lo16(w));
   }
 
   if (nonfinite) {
@@ -420,8 +462,8 @@ __device__ __forceinline__ void stage_bf16(const uint32_t (&H)[4][4], const Stag
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         if (rm[i] >= 0x7f80u) {
-          lds_st8(st.rq + rq_at(row0 + i, col), 0x7f7f7f7fu, 0x7f7f7f7fu);
-          if ((lc & 3) == i) st.rs[(row0 + i) * (TN / 32) + ((col - 8 * i) >> 5)] = 0xff;
+          lds_st8(st.rq + rq_at<T>(row0 + i, col), 0x7f7f7f7fu, 0x7f7f7f7fu);
+          if ((lc & 3) == i) st.rs[(row0 + i) * (T::TN / 32) + ((col - 8 * i) >> 5)] = 0xff;
         }
       }
     }
@@ -430,8 +472,8 @@ __device__ __forceinline__ void stage_bf16(const uint32_t (&H)[4][4], const Stag
       for (int c = 0; c < 8; c++) {
         const uint32_t cm = (c & 1) ? hi16(C[c >> 1]) : lo16(C[c >> 1]);
         if (cm >= 0x7f80u) {
-          lds_st4(st.cq + cq_at(col + c, row0), 0x7f7f7f7fu);
-          if (lr == c) st.cs[(col + c) * (TM / 32) + (row0 >> 5)] = 0xff;
+          lds_st4(st.cq + cq_at<T>(col + c, row0), 0x7f7f7f7fu);
+          if (lr == c) st.cs[(col + c) * (T::TM / 32) + (row0 >> 5)] = 0xff;
         }
       }
     }
@@ -440,8 +482,8 @@ __device__ __forceinline__ void stage_bf16(const uint32_t (&H)[4][4], const Stag
 
 // The same rules on FP32 values (quantizer hook): magnitudes compared as FP32 bits, the
 // scaled value x * 2^-e computed exactly in FP32, then v_cvt_pk_fp8_f32.
-template <int FLAGS>
-__device__ __forceinline__ void stage_f32(const float (&v)[4][8], const Stage<FLAGS>& st,
+template <class T, int FLAGS>
+__device__ __forceinline__ void stage_f32(const float (&v)[4][8], const Stage<T, FLAGS>& st,
                                           int row0, int col, int lr, int lc) {
   uint32_t ab[4][8];
 #pragma unroll
@@ -467,10 +509,10 @@ __device__ __forceinline__ void stage_f32(const float (&v)[4][8], const Stage<FL
       uint32_t w1 = fp8x2<false>(0u, v[i][4] * P, v[i][5] * P);
       w1 = fp8x2<true>(w1, v[i][6] * P, v[i][7] * P);
       if (nonfinite) w0 = w1 = 0x7f7f7f7fu;
-      lds_st8(st.rq + rq_at(row0 + i, col), w0, w1);
+      lds_st8(st.rq + rq_at<T>(row0 + i, col), w0, w1);
     }
     const int i = lc & 3;
-    st.rs[(row0 + i) * (TN / 32) + ((col - 8 * i) >> 5)] = (uint8_t)(packed >> (8 * i));
+    st.rs[(row0 + i) * (T::TN / 32) + ((col - 8 * i) >> 5)] = (uint8_t)(packed >> (8 * i));
   }
 
   if constexpr ((FLAGS & COLWISE) != 0) {
@@ -488,129 +530,188 @@ __device__ __forceinline__ void stage_f32(const float (&v)[4][8], const Stage<FL
       uint32_t w = fp8x2<false>(0u, v[0][c] * P, v[1][c] * P);
       w = fp8x2<true>(w, v[2][c] * P, v[3][c] * P);
       if (nonfinite) w = 0x7f7f7f7fu;
-      lds_st4(st.cq + cq_at(col + c, row0), w);
+      lds_st4(st.cq + cq_at<T>(col + c, row0), w);
     }
     const uint32_t w = lr < 4 ? packed0 : packed1;
-    st.cs[(col + lr) * (TM / 32) + (row0 >> 5)] = (uint8_t)(w >> (8 * (lr & 3)));
+    st.cs[(col + lr) * (T::TM / 32) + (row0 >> 5)] = (uint8_t)(w >> (8 * (lr & 3)));
   }
-}
-
-template <bool NT>
-__device__ __forceinline__ void st16(uint8_t* p, u32x4 v) {
-  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-  else *reinterpret_cast<u32x4*>(p) = v;
 }
 
 // Writes a staged part to global memory: the part is the [M, N] matrix at column offset
 // `coloff` of the quantized matrix, whose rows hold ldq codes; the tile starts at (r0, c0).
-// Rows >= M and columns >= N are skipped, in whole 16-byte segments (N and, when colwise,
-// M are multiples of 32).  Scale words are written whole where the 4 bytes are in range and
-// 4-byte aligned, else byte by byte.
-template <int FLAGS, bool NT>
-__device__ __forceinline__ void write_out(const Stage<FLAGS>& st, const MxArgs& a, int64_t r0,
+// Stores are raw buffer stores through descriptors based at the tile's first byte (scalar
+// address arithmetic), with 32-bit lane offsets; a store outside the matrix gets kOob as its
+// offset and the hardware's range check drops it.  Rows >= M and columns >= N fall out in
+// whole 16-byte segments (N and, when colwise, M are multiples of 32).  The host checks keep
+// 128 rows of either output's pitch below kOob.  Scale words are written whole where they are
+// 4-byte aligned and in range, else byte by byte.
+template <class T, int FLAGS, bool NT>
+__device__ __forceinline__ void write_out(const Stage<T, FLAGS>& st, const MxArgs& a, int64_t r0,
                                           int64_t c0, int64_t coloff, int64_t ldq, int tid) {
+  constexpr int AUX = NT ? 2 : 0;
   const int64_t M = a.M, N = a.N;
+  constexpr int TM = T::TM, TN = T::TN, NTHREADS = T::NTHREADS, RSEG = T::RSEG, CSEG = T::CSEG;
+  const int rows = M - r0 < TM ? (int)(M - r0) : TM;  // rows of the tile inside the part
+  const int cols = N - c0 < TN ? (int)(N - c0) : TN;  // columns of the tile inside the part
+  // thread -> (line, 16-byte segment) of a code line; two lines per thread
+  static_assert(TM * RSEG == 2 * NTHREADS && TN * CSEG == 2 * NTHREADS, "two lines per thread");
   if constexpr ((FLAGS & ROWWISE) != 0) {
-    constexpr int SEGS = TN / 16;
+    const auto out = rsrc(a.q_row + r0 * ldq + coloff + c0);
+    const uint32_t pitch = (uint32_t)ldq;
+    const int line = tid / RSEG, seg = tid % RSEG;
+    const bool seg_ok = 16 * seg < cols;
 #pragma unroll
-    for (int k = tid; k < TM * SEGS; k += NTHREADS) {
-      const int row = k / SEGS, seg = k % SEGS;
-      if (r0 + row < M && c0 + 16 * seg < N) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(st.rq + row * TN + 16 * (seg ^ ((row >> 2) & 7)));
-        st16<NT>(a.q_row + (r0 + row) * ldq + coloff + c0 + 16 * seg, v);
-      }
+    for (int i = 0; i < 2; i++) {
+      const int row = line + (NTHREADS / RSEG) * i;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st.rq + row * TN + 16 * (seg ^ ((row >> 2) & (RSEG - 1))));
+      const uint32_t off = seg_ok && row < rows ? (uint32_t)row * pitch + 16u * seg : kOob;
+      __builtin_amdgcn_raw_buffer_store_b128(v, out, off, 0, AUX);
     }
+    // scale words: thread `row` < TM writes the TN/32 scales of tile row `row`
     const int64_t nb = ldq / 32;
-    const bool whole = nb % 4 == 0 && (coloff / 32) % 4 == 0 && c0 + TN <= N;
-    for (int row = tid; row < TM; row += NTHREADS) {
-      if (r0 + row < M) {
-        uint8_t* dst = a.s_row + (r0 + row) * nb + (coloff + c0) / 32;
-        const uint8_t* src = st.rs + row * (TN / 32);
-        if (whole) {
-          *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
-        } else {
-          for (int b = 0; b < TN / 32; b++)
-            if (c0 + 32 * b < N) dst[b] = src[b];
-        }
-      }
+    const auto sout = rsrc(a.s_row + r0 * nb + (coloff + c0) / 32);
+    const int row = tid < TM ? tid : 0;
+    const bool row_ok = tid < TM && row < rows;
+    const uint32_t base = (uint32_t)row * (uint32_t)nb;
+    const bool whole = nb % 4 == 0 && (coloff / 32) % 4 == 0 && cols == TN;
+    if (whole) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(st.rs + row * (TN / 32));
+      __builtin_amdgcn_raw_buffer_store_b32(w, sout, row_ok ? base : kOob, 0, 0);
+    } else {
+#pragma unroll
+      for (int b = 0; b < TN / 32; b++)
+        __builtin_amdgcn_raw_buffer_store_b8(st.rs[row * (TN / 32) + b], sout,
+                                             row_ok && 32 * b < cols ? base + b : kOob, 0, 0);
     }
   }
   if constexpr ((FLAGS & COLWISE) != 0) {
-    constexpr int SEGS = TM / 16;
+    static_assert(TM == 128, "colwise code lines and scale words are 128 rows long");
+    const auto out = rsrc(a.q_col + (coloff + c0) * M + r0);
+    const uint32_t pitch = (uint32_t)M;
+    const int line = tid / CSEG, seg = tid % CSEG;
+    const bool seg_ok = 16 * seg < rows;
 #pragma unroll
-    for (int k = tid; k < TN * SEGS; k += NTHREADS) {
-      const int col = k / SEGS, seg = k % SEGS;
-      if (c0 + col < N && r0 + 16 * seg < M) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(st.cq + col * TM + 16 * (seg ^ ((col >> 3) & 7)));
-        st16<NT>(a.q_col + (coloff + c0 + col) * M + r0 + 16 * seg, v);
-      }
+    for (int i = 0; i < 2; i++) {
+      const int col = line + (NTHREADS / CSEG) * i;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st.cq + col * TM + 16 * (seg ^ ((col >> 3) & (CSEG - 1))));
+      const uint32_t off = seg_ok && col < cols ? (uint32_t)col * pitch + 16u * seg : kOob;
+      __builtin_amdgcn_raw_buffer_store_b128(v, out, off, 0, AUX);
     }
+    // scale words: thread `col` < TN writes the TM/32 scales of tile column `col`
     const int64_t nb = M / 32;
-    const bool whole = nb % 4 == 0 && r0 + TM <= M;
-    for (int col = tid; col < TN; col += NTHREADS) {
-      if (c0 + col < N) {
-        uint8_t* dst = a.s_col + (coloff + c0 + col) * nb + r0 / 32;
-        const uint8_t* src = st.cs + col * (TM / 32);
-        if (whole) {
-          *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
-        } else {
-          for (int b = 0; b < TM / 32; b++)
-            if (r0 + 32 * b < M) dst[b] = src[b];
-        }
-      }
+    const auto sout = rsrc(a.s_col + (coloff + c0) * nb + r0 / 32);
+    const int col = tid < TN ? tid : 0;
+    const bool col_ok = tid < TN && col < cols;
+    const uint32_t base = (uint32_t)col * (uint32_t)nb;
+    const bool whole = nb % 4 == 0 && rows == TM;
+    if (whole) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(st.cs + col * (TM / 32));
+      __builtin_amdgcn_raw_buffer_store_b32(w, sout, col_ok ? base : kOob, 0, 0);
+    } else {
+#pragma unroll
+      for (int b = 0; b < TM / 32; b++)
+        __builtin_amdgcn_raw_buffer_store_b8(st.cs[col * (TM / 32) + b], sout,
+                                             col_ok && 32 * b < rows ? base + b : kOob, 0, 0);
     }
   }
 }
 
-// One workgroup per tile.  Workgroup id b runs on XCD b % 8 (workgroups are dealt to the
-// XCDs round-robin); XCD x takes tiles x * per_xcd + b / 8 of the tile order.
-template <int ACT, int LAYOUT, int FLAGS, int MODE>
-__global__ __launch_bounds__(NTHREADS) void k_mxfp8(MxArgs a, uint32_t tiles_m, uint32_t tiles_n,
-                                                    uint32_t ntiles, uint32_t per_xcd) {
-  constexpr int PARTS = MODE == MODE_BWD ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[PARTS * Stage<FLAGS>::BYTES];
-  const uint32_t t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (t >= ntiles) return;  // the whole workgroup
-  uint32_t tm, tn;
-  tile_of<tile_order<FLAGS>()>(t, tiles_m, tiles_n, tm, tn);
-  const int64_t r0 = (int64_t)tm * TM, c0 = (int64_t)tn * TN;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const int wm = w % WGM, wn = w / WGM;
-  const int lr = lane & 7, lc = lane >> 3;
-
+// The wave's piece of tile (r0, c0).
+__device__ __forceinline__ TileGeom wave_geom(const MxArgs& a, int64_t r0, int64_t c0, int wm,
+                                              int wn, int lc) {
   TileGeom g;
   g.r0 = r0 + 32 * wm;
   g.cw = c0 + 64 * wn;
   g.col = g.cw + 8 * lc;
   g.col_ok = g.col < a.N;
-  TileOps<LAYOUT, MODE> o;
-  load_ops<LAYOUT, MODE>(o, a, g, lr, lc);
-  TileVals<MODE> R;
-  compute<ACT, LAYOUT, MODE>(R, o);
+  return g;
+}
 
+// A workgroup takes `TPW` consecutive tiles of the tile order.  Workgroup id b runs on XCD
+// b % 8 (workgroups are dealt to the XCDs round-robin); XCD x owns positions
+// [x * per_xcd, (x + 1) * per_xcd) of the order, and workgroup b the TPW positions from
+// x * per_xcd + (b / 8) * TPW.  While a tile is staged and written out, the loads of the next
+// one are already in flight.  The loop is entered with the first tile computed, so the wait
+// for a prefetched tile follows the write-out on every path; the write-out's stores are
+// unconditional (out-of-range ones are dropped by the buffer range check), so that wait
+// counts them and does not drain them.
+#ifdef GLU_MX_WPE  // build-time override, for measurements
+#define GLU_MX_KATTR __attribute__((amdgpu_waves_per_eu(GLU_MX_WPE, 8)))
+#else
+#define GLU_MX_KATTR
+#endif
+template <int ACT, int LAYOUT, int FLAGS, int MODE, int TPW>
+__global__ __launch_bounds__(TileOf<FLAGS>::NTHREADS) GLU_MX_KATTR void k_mxfp8(
+    MxArgs a, uint32_t tiles_m, uint32_t tiles_n, uint32_t ntiles, uint32_t per_xcd) {
+  using T = TileOf<FLAGS>;
+  using St = Stage<T, FLAGS>;
+  constexpr int TM = T::TM, TN = T::TN;
+  constexpr int PARTS = MODE == MODE_BWD ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[PARTS * St::BYTES];
+  const uint32_t xcd = blockIdx.x & 7;
+  const uint32_t beg = xcd * per_xcd + (blockIdx.x >> 3) * TPW;
+  const uint32_t end = xcd * per_xcd + per_xcd < ntiles ? xcd * per_xcd + per_xcd : ntiles;
+  if (beg >= end) return;  // the whole workgroup
+  const uint32_t count = end - beg < (uint32_t)TPW ? end - beg : (uint32_t)TPW;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int wm = w % T::WM, wn = w / T::WM;
+  const int lr = lane & 7, lc = lane >> 3;
   const int row0 = 32 * wm + 4 * lr, col = 64 * wn + 8 * lc;
-  if constexpr (MODE == MODE_F32) {
-    stage_f32<FLAGS>(R.v, Stage<FLAGS>(lds), row0, col, lr, lc);
-  } else {
-    stage_bf16<FLAGS>(R.h[0], Stage<FLAGS>(lds), row0, col, lr, lc);
-    if constexpr (MODE == MODE_BWD)
-      stage_bf16<FLAGS>(R.h[1], Stage<FLAGS>(lds + Stage<FLAGS>::BYTES), row0, col, lr, lc);
-  }
-  __syncthreads();
   const int64_t ldq = PARTS * a.N;
   constexpr bool NT = nt_stores<MODE, FLAGS>();
-  write_out<FLAGS, NT>(Stage<FLAGS>(lds), a, r0, c0, 0, ldq, tid);
-  if constexpr (MODE == MODE_BWD)
-    write_out<FLAGS, NT>(Stage<FLAGS>(lds + Stage<FLAGS>::BYTES), a, r0, c0, a.N, ldq, tid);
+  constexpr int ORDER = tile_order<FLAGS>();
+
+  uint32_t tm, tn;
+  tile_of<T, ORDER>(beg, tiles_m, tiles_n, tm, tn);
+  int64_t r0 = (int64_t)tm * TM, c0 = (int64_t)tn * TN;
+  TileOps<LAYOUT, MODE> o;
+  load_ops<LAYOUT, MODE>(o, a, wave_geom(a, r0, c0, wm, wn, lc), lr, lc);
+  TileVals<MODE> R;
+  compute<ACT, LAYOUT, MODE>(R, o);
+  for (uint32_t k = 1;; k++) {
+    const bool more = k < count;
+    int64_t r1 = 0, c1 = 0;
+    if constexpr (TPW > 1) {  // prefetch the next tile (a tile outside the matrix past the last)
+      TileGeom gn;
+      if (more) {
+        tile_of<T, ORDER>(beg + k, tiles_m, tiles_n, tm, tn);
+        r1 = (int64_t)tm * TM;
+        c1 = (int64_t)tn * TN;
+        gn = wave_geom(a, r1, c1, wm, wn, lc);
+      } else {
+        gn = TileGeom{a.M, 0, 0, false};
+      }
+      load_ops<LAYOUT, MODE>(o, a, gn, lr, lc);
+    }
+    if constexpr (MODE == MODE_F32) {
+      stage_f32<T, FLAGS>(R.v, St(lds), row0, col, lr, lc);
+    } else {
+      stage_bf16<T, FLAGS>(R.h[0], St(lds), row0, col, lr, lc);
+      if constexpr (MODE == MODE_BWD)
+        stage_bf16<T, FLAGS>(R.h[1], St(lds + St::BYTES), row0, col, lr, lc);
+    }
+    __syncthreads();
+    write_out<T, FLAGS, NT>(St(lds), a, r0, c0, 0, ldq, tid);
+    if constexpr (MODE == MODE_BWD)
+      write_out<T, FLAGS, NT>(St(lds + St::BYTES), a, r0, c0, a.N, ldq, tid);
+    if (TPW == 1 || !more) break;
+    __syncthreads();  // the stage is read out before it is refilled
+    compute<ACT, LAYOUT, MODE>(R, o);
+    r0 = r1;
+    c0 = c1;
+  }
 }
 
 template <int ACT, int LAYOUT, int FLAGS, int MODE>
 hipError_t launch(const MxArgs& a, hipStream_t s) {
-  const int64_t tiles_m = (a.M + TM - 1) / TM, tiles_n = (a.N + TN - 1) / TN;
+  constexpr int TPW = tiles_per_workgroup<MODE>();
+  using T = TileOf<FLAGS>;
+  const int64_t tiles_m = (a.M + T::TM - 1) / T::TM, tiles_n = (a.N + T::TN - 1) / T::TN;
   const int64_t ntiles = tiles_m * tiles_n, per_xcd = (ntiles + 7) / 8;
-  return launch_kernel(k_mxfp8<ACT, LAYOUT, FLAGS, MODE>, dim3((unsigned)(8 * per_xcd)),
-                       dim3(NTHREADS), s, a, (uint32_t)tiles_m, (uint32_t)tiles_n, (uint32_t)ntiles,
+  const int64_t wg_per_xcd = (per_xcd + TPW - 1) / TPW;
+  return launch_kernel(k_mxfp8<ACT, LAYOUT, FLAGS, MODE, TPW>, dim3((unsigned)(8 * wg_per_xcd)),
+                       dim3(T::NTHREADS), s, a, (uint32_t)tiles_m, (uint32_t)tiles_n, (uint32_t)ntiles,
                        (uint32_t)per_xcd);
 }
 

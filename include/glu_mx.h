@@ -121,9 +121,10 @@ glu_status glu_bwd(int act, int layout, int64_t M, int64_t N, const uint16_t* ga
  *   rowwise (flags & GLU_ROWWISE): q_row [M, N] codes, s_row [M, N/32] scales.
  *   colwise (flags & GLU_COLWISE): q_col [N, M] codes (row j holds column j of h, i.e.
  *                                  the column-major [M, N]), s_col [N, M/32] scales.
- * A disabled direction's two pointers must be NULL.  Needs N % 32 == 0, M % 32 == 0 when
- * colwise, ld_in % 8 == 0 and ld_in <= 2^24 (GLU_ERR_STRIDE).  Output buffers are
- * contiguous. */
+ * A disabled direction's two pointers must be NULL.  Needs N % 32 == 0, and M % 32 == 0
+ * when colwise (GLU_ERR_SHAPE); ld_in % 8 == 0 and ld_in <= 2^24 (GLU_ERR_STRIDE).  Output
+ * buffers are contiguous; each code output's rows are at most 2^24 bytes (rowwise N,
+ * colwise M; GLU_ERR_SHAPE). */
 glu_status glu_fwd_mxfp8(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
                          const uint16_t* up, int64_t ld_in, int flags, uint8_t* q_row,
                          uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, void* stream);
@@ -132,8 +133,8 @@ glu_status glu_fwd_mxfp8(int act, int layout, int64_t M, int64_t N, const uint16
  * The quantized matrix is X = [da | db], [M, 2N] (X[:, j] = da_j, X[:, N + j] = db_j), with
  * da, db as in glu_bwd and never written.  q_row [M, 2N], s_row [M, 2N/32], q_col [2N, M],
  * s_col [2N, M/32].  Only GLU_SPLIT is implemented (GLU_PAIRED -> GLU_ERR_UNSUPPORTED).
- * Needs N % 32 == 0, M % 32 == 0 when colwise, ld_in and ld_dh multiples of 8 and at
- * most 2^24 (GLU_ERR_STRIDE). */
+ * Needs N % 32 == 0, M % 32 == 0 when colwise, rowwise 2N <= 2^24 and colwise M <= 2^24
+ * (GLU_ERR_SHAPE); ld_in and ld_dh multiples of 8 and at most 2^24 (GLU_ERR_STRIDE). */
 glu_status glu_bwd_mxfp8(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
                          const uint16_t* up, int64_t ld_in, const uint16_t* dh,
                          int64_t ld_dh, int flags, uint8_t* q_row, uint8_t* s_row,
@@ -152,7 +153,7 @@ glu_status glu_fwd_nvfp4(int act, int layout, int64_t M, int64_t H, const uint16
 
 /* ---- Quantizer test hooks: the same device quantizer code, fed FP32 values
  * x is an FP32 [M, N] matrix with row stride ld_x (a multiple of 4; at most 2^23 for the
- * MXFP8 hook).  Outputs and rules
+ * MXFP8 hook, whose output pitches are bounded as for glu_fwd_mxfp8).  Outputs and rules
  * exactly as glu_fwd_mxfp8 / glu_fwd_nvfp4 with x in place of h; every FP32 input is
  * quantized exactly (no intermediate rounding). */
 glu_status glu_quant_mxfp8_f32(int64_t M, int64_t N, const float* x, int64_t ld_x, int flags,

@@ -133,6 +133,9 @@ def test_fwd_mxfp8_checks():
     # row pitch limit of the MXFP8 kernels: 2^24 elements
     row = dict(M=1, flags=1, qc=0, sc=0)
     assert mxf(ld=1 << 24, **row) == OK and mxf(ld=(1 << 24) + 8, **row) == STRIDE
+    # colwise output rows (M codes each) at most 2^24 bytes
+    col = dict(N=32, ld=32, flags=2, qr=0, sr=0, gate=1 << 36, up=2 << 36, qc=3 << 36, sc=4 << 36)
+    assert mxf(M=1 << 24, **col) == OK and mxf(M=(1 << 24) + 32, **col) == SHAPE
 
 
 def mxb(**kw):
@@ -150,6 +153,8 @@ def test_bwd_mxfp8_checks():
     assert mxb(dh=0) == NULL
     assert mxb(lddh=120) == STRIDE and mxb(lddh=132) == STRIDE
     row = dict(M=1, flags=1, qc=0, sc=0)
+    assert mxb(N=1 << 23, ld=1 << 23, lddh=1 << 23, **row) == OK   # [da | db] rows: 2^24 codes
+    assert mxb(N=(1 << 23) + 32, ld=(1 << 23) + 32, lddh=(1 << 23) + 32, **row) == SHAPE
     assert mxb(ld=1 << 24, lddh=1 << 24, **row) == OK
     assert mxb(ld=(1 << 24) + 8, **row) == STRIDE and mxb(lddh=(1 << 24) + 8, **row) == STRIDE
     assert mxb(qr=C0) == OVERLAP
