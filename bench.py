@@ -282,7 +282,7 @@ def main():
             "bound": "hbm", "kernel": "k_mxfp8 backward, both scalings",
             "achieved": round(bwd_b / bwd_us / 1e3, 1), "peak": PEAK_GBPS, "unit": "GB/s",
             "frac": round(bwd_b / bwd_us / 1e3 / PEAK_GBPS, 4),
-            "traffic": traffic_bytes("k_mxfp8<0,0,3,1>"),
+            "traffic": traffic_bytes("k_mxfp8<0,0,3,1,1>"),
         },
     }
     del sets, fo, bo

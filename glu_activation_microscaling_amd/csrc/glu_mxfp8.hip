@@ -670,9 +670,18 @@ __global__ __launch_bounds__(TileOf<FLAGS>::NTHREADS) GLU_MX_KATTR void k_mxfp8(
   TileVals<MODE> R;
   compute<ACT, LAYOUT, MODE>(R, o);
   for (uint32_t k = 1;; k++) {
+    if constexpr (MODE == MODE_F32) {
+      stage_f32<T, FLAGS>(R.v, St(lds), row0, col, lr, lc);
+    } else {
+      stage_bf16<T, FLAGS>(R.h[0], St(lds), row0, col, lr, lc);
+      if constexpr (MODE == MODE_BWD)
+        stage_bf16<T, FLAGS>(R.h[1], St(lds + St::BYTES), row0, col, lr, lc);
+    }
     const bool more = k < count;
     int64_t r1 = 0, c1 = 0;
-    if constexpr (TPW > 1) {  // prefetch the next tile (a tile outside the matrix past the last)
+    if constexpr (TPW > 1) {
+      // prefetch the next tile (past the last one, a tile outside the matrix) once this
+      // tile's results are staged, so the operand registers overlap only the write-out
       TileGeom gn;
       if (more) {
         tile_of<T, ORDER>(beg + k, tiles_m, tiles_n, tm, tn);
@@ -683,13 +692,6 @@ __global__ __launch_bounds__(TileOf<FLAGS>::NTHREADS) GLU_MX_KATTR void k_mxfp8(
         gn = TileGeom{a.M, 0, 0, false};
       }
       load_ops<LAYOUT, MODE>(o, a, gn, lr, lc);
-    }
-    if constexpr (MODE == MODE_F32) {
-      stage_f32<T, FLAGS>(R.v, St(lds), row0, col, lr, lc);
-    } else {
-      stage_bf16<T, FLAGS>(R.h[0], St(lds), row0, col, lr, lc);
-      if constexpr (MODE == MODE_BWD)
-        stage_bf16<T, FLAGS>(R.h[1], St(lds + St::BYTES), row0, col, lr, lc);
     }
     __syncthreads();
     write_out<T, FLAGS, NT>(St(lds), a, r0, c0, 0, ldq, tid);

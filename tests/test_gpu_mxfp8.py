@@ -152,6 +152,33 @@ def test_ragged_rows_rowwise_and_edges(gpu):
     assert out[0].shape == (0, 64)
 
 
+@pytest.mark.parametrize("M,N", [(352, 480), (160, 4128), (4224, 96)])
+def test_partial_tiles_every_direction(gpu, M, N):
+    """Tile edges in M and N with odd scale-row lengths (N/32, M/32 not multiples of 4), so
+    the write-out takes its byte-wise scale path; fused == Q(BF16 GLU output) bit for bit."""
+    gate, up, dh = si.glu_operands(M, N, seed=M * 7 + N, outliers=True, with_dh=True)
+    gd, ud, dd = gate.cuda(), up.cuda(), dh.cuda()
+    h = bits(gpu.glu_fwd(gd, ud, act="geglu"))
+    da, db = gpu.glu_bwd(gd, ud, dd, act="geglu")
+    X = np.concatenate([bits(da), bits(db)], axis=1)
+    paired = torch.stack([gd, ud], 2).reshape(M, 2 * N).contiguous()
+    for row, col in FLAGS:
+        o = _q(h, _flags(row, col))
+        for out in (gpu.glu_fwd_mxfp8(gd, ud, act="geglu", rowwise=row, colwise=col),
+                    gpu.glu_fwd_mxfp8(paired, None, act="geglu", layout="paired", rowwise=row,
+                                      colwise=col)):
+            if row:
+                assert np.array_equal(u8(out[0]), o[0]) and np.array_equal(u8(out[2]), o[1])
+            if col:
+                assert np.array_equal(u8(out[1]), o[2]) and np.array_equal(u8(out[3]), o[3])
+        ob = _q(X, _flags(row, col))
+        out = gpu.glu_bwd_mxfp8(gd, ud, dd, act="geglu", rowwise=row, colwise=col)
+        if row:
+            assert np.array_equal(u8(out[0]), ob[0]) and np.array_equal(u8(out[2]), ob[1])
+        if col:
+            assert np.array_equal(u8(out[1]), ob[2]) and np.array_equal(u8(out[3]), ob[3])
+
+
 def test_row_slices_are_batch_invariant(gpu):
     gate, up = si.glu_operands(256, 256, seed=9, outliers=True)
     gd, ud = gate.cuda(), up.cuda()
