@@ -43,6 +43,11 @@ namespace {
 #define GLU_MX_TILE_ORDER -1
 #endif
 //   GLU_MX_TPW: if set, the tiles per workgroup of every kernel (else per kernel, below).
+//   GLU_MX_PIPE: 0 stages everything, then writes everything out; 1 (the backward) writes da
+//   out while staging db.
+#ifndef GLU_MX_PIPE
+#define GLU_MX_PIPE 1
+#endif
 
 enum { MODE_FWD = 0, MODE_BWD = 1, MODE_F32 = 2 };
 
@@ -377,6 +382,96 @@ __device__ __forceinline__ void lds_st8(uint8_t* p, uint32_t w0, uint32_t w1) {
 }
 __device__ __forceinline__ void lds_st4(uint8_t* p, uint32_t w) { *reinterpret_cast<uint32_t*>(p) = w; }
 
+template <class T, int FLAGS>
+__device__ __forceinline__ void stage_rows(const uint32_t (&H)[4][4], const Stage<T, FLAGS>& st,
+                                          int row0, int col, int lc) {
+  uint32_t m[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    m[i] = pkmax(pkmax(H[i][0] & 0x7fff7fffu, H[i][1] & 0x7fff7fffu),
+                 pkmax(H[i][2] & 0x7fff7fffu, H[i][3] & 0x7fff7fffu));
+  uint32_t R01 = pkmax(pair_lo(m[0], m[1]), pair_hi(m[0], m[1]));  // rows (0,1) packed
+  uint32_t R23 = pkmax(pair_lo(m[2], m[3]), pair_hi(m[2], m[3]));  // rows (2,3) packed
+  R01 = pkmax(R01, dpp<DPP_ROW_ROR8>(R01));
+  R23 = pkmax(R23, dpp<DPP_ROW_ROR8>(R23));
+  R01 = pkmax(R01, swz_xor16(R01));
+  R23 = pkmax(R23, swz_xor16(R23));
+
+  const uint32_t S01 = pk_scale_bytes(R01), S23 = pk_scale_bytes(R23);
+  const uint32_t sb[4] = {lo16(S01), hi16(S01), lo16(S23), hi16(S23)};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const float sc = e8m0_value(sb[i]);
+    uint32_t w0 = fp8x2_scaled<false>(0u, H[i][0], sc);
+    w0 = fp8x2_scaled<true>(w0, H[i][1], sc);
+    uint32_t w1 = fp8x2_scaled<false>(0u, H[i][2], sc);
+    w1 = fp8x2_scaled<true>(w1, H[i][3], sc);
+    lds_st8(st.rq + rq_at<T>(row0 + i, col), w0, w1);
+  }
+  // lane lc = 4b + i stages the scale of row 4lr + i in the wave's block b
+  const int i = lc & 3;
+  const uint32_t w = i < 2 ? S01 : S23;
+  st.rs[(row0 + i) * (T::TN / 32) + ((col - 8 * i) >> 5)] = (uint8_t)((i & 1) ? hi16(w) : lo16(w));
+
+  const uint32_t rm = pkmax(R01, R23);
+  if (umax(lo16(rm), hi16(rm)) >= 0x7f80u) {
+    // a block holding NaN or Inf: scale 0xFF, every code 0x7F (overwrites the fast path; each
+    // lane patches only what it staged itself, so program order suffices)
+    const uint32_t rmax[4] = {lo16(R01), hi16(R01), lo16(R23), hi16(R23)};
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      if (rmax[r] >= 0x7f80u) {
+        lds_st8(st.rq + rq_at<T>(row0 + r, col), 0x7f7f7f7fu, 0x7f7f7f7fu);
+        if ((lc & 3) == r) st.rs[(row0 + r) * (T::TN / 32) + ((col - 8 * r) >> 5)] = 0xff;
+      }
+    }
+  }
+}
+
+template <class T, int FLAGS>
+__device__ __forceinline__ void stage_cols(const uint32_t (&H)[4][4], const Stage<T, FLAGS>& st,
+                                          int row0, int col, int lr) {
+  uint32_t C[4];  // column block maxima, columns (2k, 2k+1) packed
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    uint32_t c = pkmax(pkmax(H[0][k] & 0x7fff7fffu, H[1][k] & 0x7fff7fffu),
+                       pkmax(H[2][k] & 0x7fff7fffu, H[3][k] & 0x7fff7fffu));
+    c = pkmax(c, dpp<DPP_XOR1>(c));
+    c = pkmax(c, dpp<DPP_XOR2>(c));
+    C[k] = pkmax(c, dpp<DPP_HALF_MIRROR>(c));
+  }
+  uint32_t S[4];
+#pragma unroll
+  for (int k = 0; k < 4; k++) S[k] = pk_scale_bytes(C[k]);
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const float s0 = e8m0_value(lo16(S[k])), s1 = e8m0_value(hi16(S[k]));
+    // column 2k: rows (0,1) from the low halves, rows (2,3) likewise
+    uint32_t w0 = fp8x2_scaled<false>(0u, pair_lo(H[0][k], H[1][k]), s0);
+    w0 = fp8x2_scaled<true>(w0, pair_lo(H[2][k], H[3][k]), s0);
+    uint32_t w1 = fp8x2_scaled<false>(0u, pair_hi(H[0][k], H[1][k]), s1);
+    w1 = fp8x2_scaled<true>(w1, pair_hi(H[2][k], H[3][k]), s1);
+    lds_st4(st.cq + cq_at<T>(col + 2 * k, row0), w0);
+    lds_st4(st.cq + cq_at<T>(col + 2 * k + 1, row0), w1);
+  }
+  // lane lr stages the scale of column 8lc + lr of this 32-row block
+  const uint32_t w = (lr >> 1) == 0 ? S[0] : (lr >> 1) == 1 ? S[1] : (lr >> 1) == 2 ? S[2] : S[3];
+  st.cs[(col + lr) * (T::TM / 32) + (row0 >> 5)] = (uint8_t)((lr & 1) ? hi16(w) : lo16(w));
+
+  const uint32_t cm = pkmax(pkmax(C[0], C[1]), pkmax(C[2], C[3]));
+  if (umax(lo16(cm), hi16(cm)) >= 0x7f80u) {
+    // a block holding NaN or Inf: scale 0xFF, every code 0x7F (as for the rows)
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      const uint32_t cmax = (c & 1) ? hi16(C[c >> 1]) : lo16(C[c >> 1]);
+      if (cmax >= 0x7f80u) {
+        lds_st4(st.cq + cq_at<T>(col + c, row0), 0x7f7f7f7fu);
+        if (lr == c) st.cs[(col + c) * (T::TM / 32) + (row0 >> 5)] = 0xff;
+      }
+    }
+  }
+}
+
 // Quantizes the lane's 4x8 BF16 values H[i][k] = (columns 2k, 2k+1 of tile row row0 + i),
 // tile columns col..col+7 (row0 = 32wm + 4lr, col = 64wn + 8lc), into the LDS stage.  All
 // 64 lanes of the wave take part (cross-lane maxima).  Elements outside the matrix were
@@ -385,99 +480,8 @@ __device__ __forceinline__ void lds_st4(uint8_t* p, uint32_t w) { *reinterpret_c
 template <class T, int FLAGS>
 __device__ __forceinline__ void stage_bf16(const uint32_t (&H)[4][4], const Stage<T, FLAGS>& st,
                                            int row0, int col, int lr, int lc) {
-  uint32_t A[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int k = 0; k < 4; k++) A[i][k] = H[i][k] & 0x7fff7fffu;
-
-  uint32_t R01 = 0, R23 = 0;  // row block maxima, rows (0,1) and (2,3) packed
-  uint32_t C[4] = {0, 0, 0, 0};  // column block maxima, columns (2k, 2k+1) packed
-  if constexpr ((FLAGS & ROWWISE) != 0) {
-    uint32_t m[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) m[i] = pkmax(pkmax(A[i][0], A[i][1]), pkmax(A[i][2], A[i][3]));
-    R01 = pkmax(pair_lo(m[0], m[1]), pair_hi(m[0], m[1]));
-    R23 = pkmax(pair_lo(m[2], m[3]), pair_hi(m[2], m[3]));
-    R01 = pkmax(R01, dpp<DPP_ROW_ROR8>(R01));
-    R23 = pkmax(R23, dpp<DPP_ROW_ROR8>(R23));
-    R01 = pkmax(R01, swz_xor16(R01));
-    R23 = pkmax(R23, swz_xor16(R23));
-  }
-  if constexpr ((FLAGS & COLWISE) != 0) {
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      uint32_t c = pkmax(pkmax(A[0][k], A[1][k]), pkmax(A[2][k], A[3][k]));
-      c = pkmax(c, dpp<DPP_XOR1>(c));
-      c = pkmax(c, dpp<DPP_XOR2>(c));
-      C[k] = pkmax(c, dpp<DPP_HALF_MIRROR>(c));
-    }
-  }
-  // any non-finite block among those this lane touches? (rare: patched after the fast path)
-  const uint32_t all = pkmax(pkmax(R01, R23), pkmax(pkmax(C[0], C[1]), pkmax(C[2], C[3])));
-  const bool nonfinite = umax(lo16(all), hi16(all)) >= 0x7f80u;
-
-  if constexpr ((FLAGS & ROWWISE) != 0) {
-    const uint32_t S01 = pk_scale_bytes(R01), S23 = pk_scale_bytes(R23);
-    const uint32_t sb[4] = {lo16(S01), hi16(S01), lo16(S23), hi16(S23)};
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const float sc = e8m0_value(sb[i]);
-      uint32_t w0 = fp8x2_scaled<false>(0u, H[i][0], sc);
-      w0 = fp8x2_scaled<true>(w0, H[i][1], sc);
-      uint32_t w1 = fp8x2_scaled<false>(0u, H[i][2], sc);
-      w1 = fp8x2_scaled<true>(w1, H[i][3], sc);
-      lds_st8(st.rq + rq_at<T>(row0 + i, col), w0, w1);
-    }
-    // lane lc = 4b + i stages the scale of row 4lr + i in the wave's block b
-    const int i = lc & 3;
-    const uint32_t w = i < 2 ? S01 : S23;
-    st.rs[(row0 + i) * (T::TN / 32) + ((col - 8 * i) >> 5)] = (uint8_t)((i & 1) ? hi16(w) : lo16(w));
-  }
-  if constexpr ((FLAGS & COLWISE) != 0) {
-    uint32_t S[4];
-#pragma unroll
-    for (int k = 0; k < 4; k++) S[k] = pk_scale_bytes(C[k]);
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const float s0 = e8m0_value(lo16(S[k])), s1 = e8m0_value(hi16(S[k]));
-      // column 2k: rows (0,1) from the low halves, rows (2,3) likewise
-      uint32_t w0 = fp8x2_scaled<false>(0u, pair_lo(H[0][k], H[1][k]), s0);
-      w0 = fp8x2_scaled<true>(w0, pair_lo(H[2][k], H[3][k]), s0);
-      uint32_t w1 = fp8x2_scaled<false>(0u, pair_hi(H[0][k], H[1][k]), s1);
-      w1 = fp8x2_scaled<true>(w1, pair_hi(H[2][k], H[3][k]), s1);
-      lds_st4(st.cq + cq_at<T>(col + 2 * k, row0), w0);
-      lds_st4(st.cq + cq_at<T>(col + 2 * k + 1, row0), w1);
-    }
-    // lane lr stages the scale of column 8lc + lr of this 32-row block
-    const uint32_t w = (lr >> 1) == 0 ? S[0] : (lr >> 1) == 1 ? S[1] : (lr >> 1) == 2 ? S[2] : S[3];
-    st.cs[(col + lr) * (T::TM / 32) + (row0 >> 5)] = (uint8_t)((lr & 1) ? hi16(w) : lo16(w));
-  }
-
-  if (nonfinite) {
-    // a block holding NaN or Inf: scale 0xFF, every code 0x7F (overwrites the fast path; each
-    // lane patches only what it staged itself, so program order suffices)
-    if constexpr ((FLAGS & ROWWISE) != 0) {
-      const uint32_t rm[4] = {lo16(R01), hi16(R01), lo16(R23), hi16(R23)};
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        if (rm[i] >= 0x7f80u) {
-          lds_st8(st.rq + rq_at<T>(row0 + i, col), 0x7f7f7f7fu, 0x7f7f7f7fu);
-          if ((lc & 3) == i) st.rs[(row0 + i) * (T::TN / 32) + ((col - 8 * i) >> 5)] = 0xff;
-        }
-      }
-    }
-    if constexpr ((FLAGS & COLWISE) != 0) {
-#pragma unroll
-      for (int c = 0; c < 8; c++) {
-        const uint32_t cm = (c & 1) ? hi16(C[c >> 1]) : lo16(C[c >> 1]);
-        if (cm >= 0x7f80u) {
-          lds_st4(st.cq + cq_at<T>(col + c, row0), 0x7f7f7f7fu);
-          if (lr == c) st.cs[(col + c) * (T::TM / 32) + (row0 >> 5)] = 0xff;
-        }
-      }
-    }
-  }
+  if constexpr ((FLAGS & ROWWISE) != 0) stage_rows<T, FLAGS>(H, st, row0, col, lc);
+  if constexpr ((FLAGS & COLWISE) != 0) stage_cols<T, FLAGS>(H, st, row0, col, lr);
 }
 
 // The same rules on FP32 values (quantizer hook): magnitudes compared as FP32 bits, the
@@ -546,7 +550,7 @@ __device__ __forceinline__ void stage_f32(const float (&v)[4][8], const Stage<T,
 // 128 rows of either output's pitch below kOob.  Scale words are written whole where they are
 // 4-byte aligned and in range, else byte by byte.
 template <class T, int FLAGS, bool NT>
-__device__ __forceinline__ void write_out(const Stage<T, FLAGS>& st, const MxArgs& a, int64_t r0,
+__device__ __forceinline__ void write_rows(const Stage<T, FLAGS>& st, const MxArgs& a, int64_t r0,
                                           int64_t c0, int64_t coloff, int64_t ldq, int tid) {
   constexpr int AUX = NT ? 2 : 0;
   const int64_t M = a.M, N = a.N;
@@ -584,6 +588,18 @@ __device__ __forceinline__ void write_out(const Stage<T, FLAGS>& st, const MxArg
                                              row_ok && 32 * b < cols ? base + b : kOob, 0, 0);
     }
   }
+}
+
+template <class T, int FLAGS, bool NT>
+__device__ __forceinline__ void write_cols(const Stage<T, FLAGS>& st, const MxArgs& a, int64_t r0,
+                                          int64_t c0, int64_t coloff, int64_t ldq, int tid) {
+  constexpr int AUX = NT ? 2 : 0;
+  const int64_t M = a.M, N = a.N;
+  constexpr int TM = T::TM, TN = T::TN, NTHREADS = T::NTHREADS, RSEG = T::RSEG, CSEG = T::CSEG;
+  const int rows = M - r0 < TM ? (int)(M - r0) : TM;  // rows of the tile inside the part
+  const int cols = N - c0 < TN ? (int)(N - c0) : TN;  // columns of the tile inside the part
+  // thread -> (line, 16-byte segment) of a code line; two lines per thread
+  static_assert(TM * RSEG == 2 * NTHREADS && TN * CSEG == 2 * NTHREADS, "two lines per thread");
   if constexpr ((FLAGS & COLWISE) != 0) {
     static_assert(TM == 128, "colwise code lines and scale words are 128 rows long");
     const auto out = rsrc(a.q_col + (coloff + c0) * M + r0);
@@ -614,6 +630,13 @@ __device__ __forceinline__ void write_out(const Stage<T, FLAGS>& st, const MxArg
                                              col_ok && 32 * b < rows ? base + b : kOob, 0, 0);
     }
   }
+}
+
+template <class T, int FLAGS, bool NT>
+__device__ __forceinline__ void write_out(const Stage<T, FLAGS>& st, const MxArgs& a, int64_t r0,
+                                          int64_t c0, int64_t coloff, int64_t ldq, int tid) {
+  write_rows<T, FLAGS, NT>(st, a, r0, c0, coloff, ldq, tid);
+  write_cols<T, FLAGS, NT>(st, a, r0, c0, coloff, ldq, tid);
 }
 
 // The wave's piece of tile (r0, c0).
@@ -661,6 +684,7 @@ __global__ __launch_bounds__(TileOf<FLAGS>::NTHREADS) GLU_MX_KATTR void k_mxfp8(
   const int64_t ldq = PARTS * a.N;
   constexpr bool NT = nt_stores<MODE, FLAGS>();
   constexpr int ORDER = tile_order<FLAGS>();
+  constexpr int PIPE = GLU_MX_PIPE;
 
   uint32_t tm, tn;
   tile_of<T, ORDER>(beg, tiles_m, tiles_n, tm, tn);
@@ -670,12 +694,19 @@ __global__ __launch_bounds__(TileOf<FLAGS>::NTHREADS) GLU_MX_KATTR void k_mxfp8(
   TileVals<MODE> R;
   compute<ACT, LAYOUT, MODE>(R, o);
   for (uint32_t k = 1;; k++) {
+    // The backward stages da, and writes it out while db is staged (PIPE 1: 227 vs 234 us
+    // at [16384, 7168]; splitting the rowwise and colwise pieces too gained nothing).
+    const St A(lds), B(lds + St::BYTES);
     if constexpr (MODE == MODE_F32) {
-      stage_f32<T, FLAGS>(R.v, St(lds), row0, col, lr, lc);
+      stage_f32<T, FLAGS>(R.v, A, row0, col, lr, lc);
+    } else if constexpr (PIPE == 1 && MODE == MODE_BWD) {
+      stage_bf16<T, FLAGS>(R.h[0], A, row0, col, lr, lc);
+      __syncthreads();
+      write_out<T, FLAGS, NT>(A, a, r0, c0, 0, ldq, tid);
+      stage_bf16<T, FLAGS>(R.h[1], B, row0, col, lr, lc);
     } else {
-      stage_bf16<T, FLAGS>(R.h[0], St(lds), row0, col, lr, lc);
-      if constexpr (MODE == MODE_BWD)
-        stage_bf16<T, FLAGS>(R.h[1], St(lds + St::BYTES), row0, col, lr, lc);
+      stage_bf16<T, FLAGS>(R.h[0], A, row0, col, lr, lc);
+      if constexpr (MODE == MODE_BWD) stage_bf16<T, FLAGS>(R.h[1], B, row0, col, lr, lc);
     }
     const bool more = k < count;
     int64_t r1 = 0, c1 = 0;
@@ -694,9 +725,12 @@ __global__ __launch_bounds__(TileOf<FLAGS>::NTHREADS) GLU_MX_KATTR void k_mxfp8(
       load_ops<LAYOUT, MODE>(o, a, gn, lr, lc);
     }
     __syncthreads();
-    write_out<T, FLAGS, NT>(St(lds), a, r0, c0, 0, ldq, tid);
-    if constexpr (MODE == MODE_BWD)
-      write_out<T, FLAGS, NT>(St(lds + St::BYTES), a, r0, c0, a.N, ldq, tid);
+    if constexpr (PIPE == 1 && MODE == MODE_BWD) {
+      write_out<T, FLAGS, NT>(B, a, r0, c0, a.N, ldq, tid);
+    } else {
+      write_out<T, FLAGS, NT>(A, a, r0, c0, 0, ldq, tid);
+      if constexpr (MODE == MODE_BWD) write_out<T, FLAGS, NT>(B, a, r0, c0, a.N, ldq, tid);
+    }
     if (TPW == 1 || !more) break;
     __syncthreads();  // the stage is read out before it is refilled
     compute<ACT, LAYOUT, MODE>(R, o);
