@@ -62,14 +62,26 @@ struct Tile {
   // order-2 block: the tiles of a block that share rows (columns) fill one 32-byte sector of
   // rowwise (colwise) scale words, TN / 32 (TM / 32) bytes per tile
   static constexpr int BM = 32 / (TM / 32), BN = 32 / (TN / 32);
-  static_assert((TM == 64 || TM == 128) && TN == 128, "shapes the swizzles and scale words fit");
+  static_assert(TM >= 32 && TM <= 128 && TN >= 128 && TN <= 1024 && NTHREADS <= 1024,
+                "shapes the swizzles and scale words fit");
 };
 
-// Tile per direction, from interleaved measurements at [16384, 7168]: rowwise only 64 x 128
-// (backward 168 vs 176 us with 128 x 128: smaller workgroups, four per CU), otherwise
-// 128 x 128 (a 128 x 64 tile for colwise only was 2-3% slower).
-template <int FLAGS>
-using TileOf = Tile<FLAGS == ROWWISE ? 2 : 4, 2>;
+// Tile per kernel, from interleaved measurements at [16384, 7168].  Rowwise only: a band of
+// 32 rows, 512 columns wide in the forward (102 vs 110 us with 64 x 128; 984 vs 1043 us at
+// [131072, 8192]) and 256 wide in the backward (158 vs 169 us), so each workgroup reads and
+// writes long runs of its rows.  With colwise output, 128 x 128.
+#ifndef GLU_MX_ROW_WM  // build-time override of the rowwise-only tile, for measurements
+#define GLU_MX_ROW_WM 1
+#define GLU_MX_ROW_WN(MODE) ((MODE) == 1 ? 4 : 8)
+#else
+#define GLU_MX_ROW_WN(MODE) GLU_MX_ROW_WN_
+#endif
+#ifndef GLU_MX_COL_WN  // build-time override of the colwise tiles' width, for measurements
+#define GLU_MX_COL_WN 2
+#endif
+template <int FLAGS, int MODE>
+using TileOf = Tile<FLAGS == ROWWISE ? GLU_MX_ROW_WM : 4,
+                    FLAGS == ROWWISE ? GLU_MX_ROW_WN(MODE) : GLU_MX_COL_WN>;
 
 // Non-temporal code stores: measured faster only for the backward quantized both ways
 // (234 vs 267 us at [16384, 7168] in the blocked tile order); slower for the forward both
@@ -577,14 +589,25 @@ __device__ __forceinline__ void write_rows(const Stage<T, FLAGS>& st, const MxAr
     const int row = tid < TM ? tid : 0;
     const bool row_ok = tid < TM && row < rows;
     const uint32_t base = (uint32_t)row * (uint32_t)nb;
-    const bool whole = nb % 4 == 0 && (coloff / 32) % 4 == 0 && cols == TN;
+    constexpr int NB = TN / 32;  // scale bytes per tile row
+    const bool whole = nb % NB == 0 && (coloff / 32) % NB == 0 && cols == TN;
     if (whole) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(st.rs + row * (TN / 32));
-      __builtin_amdgcn_raw_buffer_store_b32(w, sout, row_ok ? base : kOob, 0, 0);
+      const uint8_t* src = st.rs + row * NB;
+      const uint32_t o = row_ok ? base : kOob;
+      if constexpr (NB == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t*>(src), sout, o, 0, 0);
+      } else if constexpr (NB == 8) {
+        __builtin_amdgcn_raw_buffer_store_b64(*reinterpret_cast<const u32x2*>(src), sout, o, 0, 0);
+      } else {
+#pragma unroll
+        for (int h = 0; h < NB / 16; h++)
+          __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(src + 16 * h), sout,
+                                                 row_ok ? base + 16 * h : kOob, 0, 0);
+      }
     } else {
 #pragma unroll
-      for (int b = 0; b < TN / 32; b++)
-        __builtin_amdgcn_raw_buffer_store_b8(st.rs[row * (TN / 32) + b], sout,
+      for (int b = 0; b < NB; b++)
+        __builtin_amdgcn_raw_buffer_store_b8(st.rs[row * NB + b], sout,
                                              row_ok && 32 * b < cols ? base + b : kOob, 0, 0);
     }
   }
@@ -664,9 +687,9 @@ __device__ __forceinline__ TileGeom wave_geom(const MxArgs& a, int64_t r0, int64
 #define GLU_MX_KATTR
 #endif
 template <int ACT, int LAYOUT, int FLAGS, int MODE, int TPW>
-__global__ __launch_bounds__(TileOf<FLAGS>::NTHREADS) GLU_MX_KATTR void k_mxfp8(
+__global__ __launch_bounds__((TileOf<FLAGS, MODE>::NTHREADS)) GLU_MX_KATTR void k_mxfp8(
     MxArgs a, uint32_t tiles_m, uint32_t tiles_n, uint32_t ntiles, uint32_t per_xcd) {
-  using T = TileOf<FLAGS>;
+  using T = TileOf<FLAGS, MODE>;
   using St = Stage<T, FLAGS>;
   constexpr int TM = T::TM, TN = T::TN;
   constexpr int PARTS = MODE == MODE_BWD ? 2 : 1;
@@ -742,7 +765,7 @@ __global__ __launch_bounds__(TileOf<FLAGS>::NTHREADS) GLU_MX_KATTR void k_mxfp8(
 template <int ACT, int LAYOUT, int FLAGS, int MODE>
 hipError_t launch(const MxArgs& a, hipStream_t s) {
   constexpr int TPW = tiles_per_workgroup<MODE>();
-  using T = TileOf<FLAGS>;
+  using T = TileOf<FLAGS, MODE>;
   const int64_t tiles_m = (a.M + T::TM - 1) / T::TM, tiles_n = (a.N + T::TN - 1) / T::TN;
   const int64_t ntiles = tiles_m * tiles_n, per_xcd = (ntiles + 7) / 8;
   const int64_t wg_per_xcd = (per_xcd + TPW - 1) / TPW;
