@@ -309,7 +309,8 @@ __device__ __forceinline__ int64_t sf128x4_offset(int64_t r, int64_t c, int64_t 
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+  // every pattern below has a source lane for every lane, so no lane keeps an old value
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
 }
 constexpr int DPP_XOR1 = 0xb1;         // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4e;         // quad_perm [2,3,0,1]

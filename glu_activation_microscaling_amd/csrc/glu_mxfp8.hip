@@ -394,14 +394,13 @@ __device__ __forceinline__ void lds_st8(uint8_t* p, uint32_t w0, uint32_t w1) {
 }
 __device__ __forceinline__ void lds_st4(uint8_t* p, uint32_t w) { *reinterpret_cast<uint32_t*>(p) = w; }
 
+// A[i][k] = H[i][k] with the sign bits cleared (packed BF16 magnitudes).
 template <class T, int FLAGS>
-__device__ __forceinline__ void stage_rows(const uint32_t (&H)[4][4], const Stage<T, FLAGS>& st,
-                                          int row0, int col, int lc) {
+__device__ __forceinline__ void stage_rows(const uint32_t (&H)[4][4], const uint32_t (&A)[4][4],
+                                          const Stage<T, FLAGS>& st, int row0, int col, int lc) {
   uint32_t m[4];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
-    m[i] = pkmax(pkmax(H[i][0] & 0x7fff7fffu, H[i][1] & 0x7fff7fffu),
-                 pkmax(H[i][2] & 0x7fff7fffu, H[i][3] & 0x7fff7fffu));
+  for (int i = 0; i < 4; i++) m[i] = pkmax(pkmax(A[i][0], A[i][1]), pkmax(A[i][2], A[i][3]));
   uint32_t R01 = pkmax(pair_lo(m[0], m[1]), pair_hi(m[0], m[1]));  // rows (0,1) packed
   uint32_t R23 = pkmax(pair_lo(m[2], m[3]), pair_hi(m[2], m[3]));  // rows (2,3) packed
   R01 = pkmax(R01, dpp<DPP_ROW_ROR8>(R01));
@@ -441,13 +440,12 @@ __device__ __forceinline__ void stage_rows(const uint32_t (&H)[4][4], const Stag
 }
 
 template <class T, int FLAGS>
-__device__ __forceinline__ void stage_cols(const uint32_t (&H)[4][4], const Stage<T, FLAGS>& st,
-                                          int row0, int col, int lr) {
+__device__ __forceinline__ void stage_cols(const uint32_t (&H)[4][4], const uint32_t (&A)[4][4],
+                                          const Stage<T, FLAGS>& st, int row0, int col, int lr) {
   uint32_t C[4];  // column block maxima, columns (2k, 2k+1) packed
 #pragma unroll
   for (int k = 0; k < 4; k++) {
-    uint32_t c = pkmax(pkmax(H[0][k] & 0x7fff7fffu, H[1][k] & 0x7fff7fffu),
-                       pkmax(H[2][k] & 0x7fff7fffu, H[3][k] & 0x7fff7fffu));
+    uint32_t c = pkmax(pkmax(A[0][k], A[1][k]), pkmax(A[2][k], A[3][k]));
     c = pkmax(c, dpp<DPP_XOR1>(c));
     c = pkmax(c, dpp<DPP_XOR2>(c));
     C[k] = pkmax(c, dpp<DPP_HALF_MIRROR>(c));
@@ -492,8 +490,13 @@ __device__ __forceinline__ void stage_cols(const uint32_t (&H)[4][4], const Stag
 template <class T, int FLAGS>
 __device__ __forceinline__ void stage_bf16(const uint32_t (&H)[4][4], const Stage<T, FLAGS>& st,
                                            int row0, int col, int lr, int lc) {
-  if constexpr ((FLAGS & ROWWISE) != 0) stage_rows<T, FLAGS>(H, st, row0, col, lc);
-  if constexpr ((FLAGS & COLWISE) != 0) stage_cols<T, FLAGS>(H, st, row0, col, lr);
+  uint32_t A[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int k = 0; k < 4; k++) A[i][k] = H[i][k] & 0x7fff7fffu;
+  if constexpr ((FLAGS & ROWWISE) != 0) stage_rows<T, FLAGS>(H, A, st, row0, col, lc);
+  if constexpr ((FLAGS & COLWISE) != 0) stage_cols<T, FLAGS>(H, A, st, row0, col, lr);
 }
 
 // The same rules on FP32 values (quantizer hook): magnitudes compared as FP32 bits, the
