@@ -17,7 +17,7 @@ from . import build as _build
 
 SWIGLU, GEGLU_TANH = 0, 1
 SPLIT, PAIRED = 0, 1
-ROWWISE, COLWISE = 1, 2
+ROWWISE, COLWISE, SF_SWIZZLED = 1, 2, 4
 SF_ROWMAJOR, SF_128x4 = 0, 1
 
 _lib = None
@@ -39,6 +39,7 @@ _SIGNATURES = {
     "orc_act": (ctypes.c_double, [_int, ctypes.c_double]),
     "orc_act_grad": (ctypes.c_double, [_int, ctypes.c_double]),
     "orc_sf128x4_offset": (_i64, [_i64, _i64, _i64]),
+    "orc_mx_sf_bytes": (_i64, [_i64, _i64, _int]),
     "orc_glu_fwd": (None, [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64]),
     "orc_glu_bwd": (None, [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _p, _p, _i64]),
     "orc_quant_mxfp8": (None, [_i64, _i64, _p, _int, _p, _p, _p, _p]),
@@ -205,15 +206,25 @@ def glu_bwd(kind, gate, up, dh, layout=SPLIT):
     return da, db
 
 
+def mx_sf_bytes(rows: int, nb: int, swizzled: bool) -> int:
+    return _load().orc_mx_sf_bytes(rows, nb, int(bool(swizzled)))
+
+
+def _mx_scales(rows, nb, swizzled):
+    return np.empty(mx_sf_bytes(rows, nb, True), np.uint8) if swizzled else np.empty((rows, nb), np.uint8)
+
+
 def _mx_outputs(M, N, flags):
-    row = (np.empty((M, N), np.uint8), np.empty((M, N // 32), np.uint8)) if flags & ROWWISE else (None, None)
-    col = (np.empty((N, M), np.uint8), np.empty((N, M // 32), np.uint8)) if flags & COLWISE else (None, None)
+    swz = bool(flags & SF_SWIZZLED)
+    row = (np.empty((M, N), np.uint8), _mx_scales(M, N // 32, swz)) if flags & ROWWISE else (None, None)
+    col = (np.empty((N, M), np.uint8), _mx_scales(N, M // 32, swz)) if flags & COLWISE else (None, None)
     return row[0], row[1], col[0], col[1]
 
 
 def quant_mxfp8(x, flags=ROWWISE):
     """x float32 [M, N] -> (q_row [M,N], s_row [M,N/32], q_col [N,M], s_col [N,M/32]);
-    the disabled direction comes back as None."""
+    the disabled direction comes back as None.  With SF_SWIZZLED in flags the scales are
+    flat zero-padded 128x4 arrays (mx_sf_bytes)."""
     x = _c(x, np.float32)
     M, N = x.shape
     out = _mx_outputs(M, N, flags)

@@ -39,7 +39,9 @@
  *   - NVFP4 scale = E4M3(amax / 6) rounded to nearest; codes = E2M1(x / S);
  *     S == 0 gives signed-zero codes; even element in the low nibble;
  *   - a block holding NaN or Inf gets a NaN scale (MX 0xFF, NV 0x7F) and NaN
- *     codes (MX 0x7F) or zero codes (NV).
+ *     codes (MX 0x7F) or zero codes (NV);
+ *   - MXFP8 scales may also be asked for in the same zero-padded 128x4 layout
+ *     (the GEMM-ready block-scale layout; no page fixes one for MXFP8).
  * Parity unpinned: the NaN/Inf block rule, the nibble order, and the 128x4
  * scale layout beyond its being a zero-padded permutation.  No page prints a
  * value for any of them.
@@ -58,7 +60,7 @@
 
 enum { ORC_SWIGLU = 0, ORC_GEGLU_TANH = 1 };
 enum { ORC_SPLIT = 0, ORC_PAIRED = 1 };
-enum { ORC_ROWWISE = 1, ORC_COLWISE = 2 };
+enum { ORC_ROWWISE = 1, ORC_COLWISE = 2, ORC_SF_SWIZZLED = 4 };
 enum { ORC_SF_ROWMAJOR = 0, ORC_SF_128x4 = 1 };
 
 int orc_num_threads(void) {
@@ -287,31 +289,50 @@ static void mx_block(const double* v, uint8_t* codes, uint8_t* scale) {
   for (int i = 0; i < 32; i++) codes[i] = orc_e4m3_from_f64(ldexp(v[i], -e)); /* exact */
 }
 
+/* Bytes of a [rows, nb] scale matrix: row-major, or the zero-padded 128x4 layout
+ * (reading: the GEMM-ready layout the pages name for block scales, also used for the
+ * MXFP8 scales when asked for; rows padded to a multiple of 128, columns to 4). */
+int64_t orc_mx_sf_bytes(int64_t rows, int64_t nb, int swizzled) {
+  if (!swizzled) return rows * nb;
+  return (rows + 127) / 128 * 128 * ((nb + 3) / 4 * 4);
+}
+
+int64_t orc_sf128x4_offset(int64_t r, int64_t c, int64_t scale_cols_padded);
+
+/* Position of scale (r, c) of a [rows, nb] scale matrix. */
+static int64_t sf_pos(int64_t r, int64_t c, int64_t nb, int swizzled) {
+  return swizzled ? orc_sf128x4_offset(r, c, (nb + 3) / 4 * 4) : r * nb + c;
+}
+
 /* X is a row-major [M, N] matrix of FP32 values (BF16 values widened exactly are
  * FP32 values).  Rowwise: blocks X[m, 32b .. 32b+31], codes [M, N], scales
  * [M, N/32].  Colwise: blocks X[32b .. 32b+31, j], codes stored transposed as
- * [N, M] (row j holds column j of X), scales [N, M/32]. */
+ * [N, M] (row j holds column j of X), scales [N, M/32].  With ORC_SF_SWIZZLED in
+ * flags both scale matrices use the zero-padded 128x4 layout instead. */
 void orc_quant_mxfp8(int64_t M, int64_t N, const float* X, int flags, uint8_t* q_row,
                      uint8_t* s_row, uint8_t* q_col, uint8_t* s_col) {
+  const int swz = (flags & ORC_SF_SWIZZLED) != 0;
   if (flags & ORC_ROWWISE) {
+    if (swz) memset(s_row, 0, (size_t)orc_mx_sf_bytes(M, N / 32, 1));
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; m++)
       for (int64_t b = 0; b < N / 32; b++) {
         double v[32];
         uint8_t c[32];
         for (int i = 0; i < 32; i++) v[i] = X[m * N + 32 * b + i];
-        mx_block(v, c, &s_row[m * (N / 32) + b]);
+        mx_block(v, c, &s_row[sf_pos(m, b, N / 32, swz)]);
         memcpy(&q_row[m * N + 32 * b], c, 32);
       }
   }
   if (flags & ORC_COLWISE) {
+    if (swz) memset(s_col, 0, (size_t)orc_mx_sf_bytes(N, M / 32, 1));
 #pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < N; j++)
       for (int64_t b = 0; b < M / 32; b++) {
         double v[32];
         uint8_t c[32];
         for (int i = 0; i < 32; i++) v[i] = X[(32 * b + i) * N + j];
-        mx_block(v, c, &s_col[j * (M / 32) + b]);
+        mx_block(v, c, &s_col[sf_pos(j, b, M / 32, swz)]);
         memcpy(&q_col[j * M + 32 * b], c, 32);
       }
   }

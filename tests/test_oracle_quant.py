@@ -176,6 +176,38 @@ def test_nv_128x4_equals_rowmajor_after_unswizzle():
     assert not np.any(s2[~seen])
 
 
+def _unswizzle_check(s_swz, s_rm):
+    rows, nb = s_rm.shape
+    cp = (nb + 3) // 4 * 4
+    assert s_swz.size == (rows + 127) // 128 * 128 * cp
+    seen = np.zeros(s_swz.size, bool)
+    for r in range(rows):
+        for c in range(nb):
+            o = oracle.sf128x4_offset(r, c, cp)
+            assert s_swz[o] == s_rm[r, c]
+            seen[o] = True
+    assert not np.any(s_swz[~seen])  # padding rows and columns are zero
+
+
+def test_mx_swizzled_scales_equal_rowmajor_after_unswizzle():
+    """The 128x4 MXFP8 scale option moves the same scale bytes (the layout function is pinned
+    above by hand-placed entries); codes are unchanged; padding is zero.  Shapes put partial
+    128-row and 4-column groups on both scale matrices."""
+    for M, N in [(160, 96), (96, 224), (32, 32)]:
+        X = _random_matrix(M, N, M + N)
+        rm = oracle.quant_mxfp8(X, oracle.ROWWISE | oracle.COLWISE)
+        sw = oracle.quant_mxfp8(X, oracle.ROWWISE | oracle.COLWISE | oracle.SF_SWIZZLED)
+        assert np.array_equal(rm[0], sw[0]) and np.array_equal(rm[2], sw[2])
+        _unswizzle_check(sw[1], rm[1])
+        _unswizzle_check(sw[3], rm[3])
+    gate, up, dh = si.glu_operands(64, 96, seed=31, outliers=True, with_dh=True)
+    gb, ub, db_ = si.to_bits(gate), si.to_bits(up), si.to_bits(dh)
+    rm = oracle.glu_bwd_mxfp8(oracle.SWIGLU, gb, ub, db_, flags=3)
+    sw = oracle.glu_bwd_mxfp8(oracle.SWIGLU, gb, ub, db_, flags=3 | oracle.SF_SWIZZLED)
+    _unswizzle_check(sw[1], rm[1])
+    _unswizzle_check(sw[3], rm[3])
+
+
 def test_fused_equals_glu_then_quantizer():
     gate, up, dh = si.glu_operands(64, 64, seed=25, outliers=True, with_dh=True)
     gb, ub, db_ = si.to_bits(gate), si.to_bits(up), si.to_bits(dh)
