@@ -34,8 +34,11 @@ MUTANTS = [
      [tf.test_rceil_golden]),
     ("RCEIL rounds down", "while (e < 127 && ldexp(448.0, e) < amax) e++;",
      "while (e < 127 && ldexp(448.0, e + 1) < amax) e++;", [tf.test_rceil_golden]),
-    ("colwise scales transposed", "&s_col[j * (M / 32) + b]", "&s_col[b * N + j]",
+    ("colwise scales transposed", "&s_col[sf_pos(j, b, M / 32, swz)]", "&s_col[sf_pos(b, j, N, swz)]",
      [tq.test_mx_colwise_is_rowwise_of_transpose]),
+    ("swizzled MX scales unpadded", "swizzled ? orc_sf128x4_offset(r, c, (nb + 3) / 4 * 4)",
+     "swizzled ? orc_sf128x4_offset(r, c, nb)",
+     [tq.test_mx_swizzled_scales_equal_rowmajor_after_unswizzle]),
     ("colwise codes transposed", "memcpy(&q_col[j * M + 32 * b], c, 32);",
      "for (int i = 0; i < 32; i++) q_col[(32 * b + i) * N + j] = c[i];",
      [tq.test_mx_golden_blocks_rowwise_and_colwise]),
