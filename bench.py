@@ -128,21 +128,25 @@ def sweep(torch, glu, si, iters):
         (128, 128, False, [("fwd", "row")]),
         (4096, 2048, False, [("fwd", "both"), ("bwd", "both")]),
         (16384, 7168, True, [("fwd", "row"), ("fwd", "col"), ("fwd", "both"),
-                             ("bwd", "row"), ("bwd", "col"), ("bwd", "both")]),
+                             ("bwd", "row"), ("bwd", "col"), ("bwd", "both"),
+                             ("fwd", "both_swizzled"), ("bwd", "both_swizzled")]),
         (131072, 8192, True, [("fwd", "row")]),
     ]:
         per = 6 * M * N
         sets = [si.normal_bf16_device([(M, N)] * 3, seed=100 + s, outliers=outl) for s in range(n_sets(per))]
         for d, mode in cases:
-            row, col = mode in ("row", "both"), mode in ("col", "both")
+            swz = mode.endswith("_swizzled")  # scales in the 128x4 layout
+            dirs = mode.removesuffix("_swizzled")
+            row, col = dirs in ("row", "both"), dirs in ("col", "both")
             bwd = d == "bwd"
-            out = glu._mx_buffers(M, 2 * N if bwd else N, row, col, "cuda", None)
+            out = glu._mx_buffers(M, 2 * N if bwd else N, row, col, "cuda", None, swz)
+            kw = dict(rowwise=row, colwise=col, swizzled=swz, out=out)
             if bwd:
-                fns = [lambda s=s: glu.glu_bwd_mxfp8(s[0], s[1], s[2], rowwise=row, colwise=col, out=out) for s in sets]
+                fns = [lambda s=s: glu.glu_bwd_mxfp8(s[0], s[1], s[2], **kw) for s in sets]
             else:
-                fns = [lambda s=s: glu.glu_fwd_mxfp8(s[0], s[1], rowwise=row, colwise=col, out=out) for s in sets]
+                fns = [lambda s=s: glu.glu_fwd_mxfp8(s[0], s[1], **kw) for s in sets]
             t = time_launches(torch, fns, iters)
-            rec(f"swiglu_mxfp8_{d}_{mode}_{M}x{N}", mx_bytes(M, N, bwd, 2 if mode == "both" else 1), t)
+            rec(f"swiglu_mxfp8_{d}_{mode}_{M}x{N}", mx_bytes(M, N, bwd, 2 if dirs == "both" else 1), t)
             del out, fns
         del sets
         torch.cuda.empty_cache()

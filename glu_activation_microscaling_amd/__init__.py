@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libglu_mx.so")
 ACT = {"swiglu": 0, "geglu": 1, "geglu_tanh": 1}
 LAYOUT = {"split": 0, "paired": 1}
 SF_LAYOUT = {"rowmajor": 0, "128x4": 1}
-ROWWISE, COLWISE = 1, 2
+ROWWISE, COLWISE, SF_SWIZZLED = 1, 2, 4
 
 STATUS = {
     0: "GLU_OK", 1: "GLU_ERR_NULL", 2: "GLU_ERR_SHAPE", 3: "GLU_ERR_ALIGN", 4: "GLU_ERR_STRIDE",
@@ -77,6 +77,8 @@ def lib():
         L.glu_status_string.restype = ctypes.c_char_p
         L.glu_nvfp4_sf_bytes.argtypes = [_i64, _i64, _int]
         L.glu_nvfp4_sf_bytes.restype = _i64
+        L.glu_mxfp8_sf_bytes.argtypes = [_i64, _i64, _int]
+        L.glu_mxfp8_sf_bytes.restype = _i64
         L.glu_version.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -159,42 +161,56 @@ def glu_bwd(gate, up, dh, *, act="swiglu", layout="split", out=None):
     return da, db
 
 
-def _mx_buffers(M, C, rowwise, colwise, dev, out):
+def mxfp8_sf_bytes(rows, cols, swizzled=False):
+    """Bytes of an MXFP8 scale buffer for a quantized [rows, cols] matrix."""
+    return lib().glu_mxfp8_sf_bytes(rows, cols, int(bool(swizzled)))
+
+
+def _mx_buffers(M, C, rowwise, colwise, dev, out, swizzled=False):
     if out is not None:
         return out
     u8 = dict(dtype=torch.uint8, device=dev)
     z = torch.empty((0,), **u8)
+
+    def scales(rows, cols):
+        if swizzled:
+            return torch.empty((mxfp8_sf_bytes(rows, cols, True),), **u8)
+        return torch.empty((rows, cols // 32), **u8)
+
     q_row = torch.empty((M, C), **u8) if rowwise else z
-    s_row = torch.empty((M, C // 32), **u8) if rowwise else z
+    s_row = scales(M, C) if rowwise else z
     q_col = torch.empty((C, M), **u8) if colwise else z
-    s_col = torch.empty((C, M // 32), **u8) if colwise else z
+    s_col = scales(C, M) if colwise else z
     return q_row, q_col, s_row, s_col
 
 
-def _flags(rowwise, colwise):
+def _flags(rowwise, colwise, swizzled=False):
     f = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
     if f == 0:
         raise ValueError("enable rowwise, colwise or both")
-    return f
+    return f | (SF_SWIZZLED if swizzled else 0)
 
 
-def glu_fwd_mxfp8(gate, up=None, *, act="swiglu", layout="split", rowwise=True, colwise=False, out=None):
-    """Fused forward + MXFP8: (q_row [M,N], q_col [N,M], s_row [M,N/32], s_col [N,M/32])."""
+def glu_fwd_mxfp8(gate, up=None, *, act="swiglu", layout="split", rowwise=True, colwise=False,
+                  swizzled=False, out=None):
+    """Fused forward + MXFP8: (q_row [M,N], q_col [N,M], s_row [M,N/32], s_col [N,M/32]);
+    swizzled=True gives both scale matrices as flat zero-padded 128x4 buffers."""
     M, N, ld = _operands(gate, up, layout)
-    f = _flags(rowwise, colwise)
-    q_row, q_col, s_row, s_col = _mx_buffers(M, N, rowwise, colwise, gate.device, out)
+    f = _flags(rowwise, colwise, swizzled)
+    q_row, q_col, s_row, s_col = _mx_buffers(M, N, rowwise, colwise, gate.device, out, swizzled)
     _call("glu_fwd_mxfp8", ACT[act], LAYOUT[layout], M, N, _ptr(gate), _ptr(up), ld, f,
           _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(gate))
     return q_row, q_col, s_row, s_col
 
 
-def glu_bwd_mxfp8(gate, up, dh, *, act="swiglu", rowwise=True, colwise=False, out=None):
+def glu_bwd_mxfp8(gate, up, dh, *, act="swiglu", rowwise=True, colwise=False, swizzled=False,
+                  out=None):
     """Fused backward + MXFP8 of [da | db] ([M, 2N]): (q_row [M,2N], q_col [2N,M],
-    s_row [M,2N/32], s_col [2N,M/32])."""
+    s_row [M,2N/32], s_col [2N,M/32]); swizzled=True as for glu_fwd_mxfp8."""
     M, N, ld = _operands(gate, up, "split")
     _, _, lddh = _rowmajor(dh, "dh", torch.bfloat16)
-    f = _flags(rowwise, colwise)
-    q_row, q_col, s_row, s_col = _mx_buffers(M, 2 * N, rowwise, colwise, gate.device, out)
+    f = _flags(rowwise, colwise, swizzled)
+    q_row, q_col, s_row, s_col = _mx_buffers(M, 2 * N, rowwise, colwise, gate.device, out, swizzled)
     _call("glu_bwd_mxfp8", ACT[act], 0, M, N, _ptr(gate), _ptr(up), ld, _ptr(dh), lddh, f,
           _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(gate))
     return q_row, q_col, s_row, s_col
@@ -224,11 +240,11 @@ def glu_fwd_nvfp4(x, up=None, *, act="geglu", layout="paired", sf_layout="rowmaj
     return q, sf
 
 
-def glu_quant_mxfp8_f32(x, *, rowwise=True, colwise=False, out=None):
+def glu_quant_mxfp8_f32(x, *, rowwise=True, colwise=False, swizzled=False, out=None):
     """The MXFP8 quantizer alone on an FP32 [M, N] matrix."""
     M, N, ld = _rowmajor(x, "x", torch.float32)
-    f = _flags(rowwise, colwise)
-    q_row, q_col, s_row, s_col = _mx_buffers(M, N, rowwise, colwise, x.device, out)
+    f = _flags(rowwise, colwise, swizzled)
+    q_row, q_col, s_row, s_col = _mx_buffers(M, N, rowwise, colwise, x.device, out, swizzled)
     _call("glu_quant_mxfp8_f32", M, N, _ptr(x), ld, f, _ptr(q_row), _ptr(s_row), _ptr(q_col),
           _ptr(s_col), _stream(x))
     return q_row, q_col, s_row, s_col

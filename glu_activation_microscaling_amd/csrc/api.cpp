@@ -84,7 +84,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool valid_act(int act) { return act == glu::SWIGLU || act == glu::GEGLU_TANH; }
 bool valid_layout(int l) { return l == glu::SPLIT || l == glu::PAIRED; }
-bool valid_flags(int f) { return f == glu::ROWWISE || f == glu::COLWISE || f == (glu::ROWWISE | glu::COLWISE); }
+// MXFP8 flags: one or both directions, optionally the 128x4 scale layout.
+bool valid_flags(int f) {
+  const int dir = f & ~glu::SF_SWIZZLED;
+  return dir == glu::ROWWISE || dir == glu::COLWISE || dir == (glu::ROWWISE | glu::COLWISE);
+}
 
 // Shared checks on the BF16 operands.
 glu_status check_inputs(int act, int layout, int64_t N, const void* gate, const void* up,
@@ -95,6 +99,13 @@ glu_status check_inputs(int act, int layout, int64_t N, const void* gate, const 
   if (layout == glu::PAIRED && up != nullptr) return GLU_ERR_ARG;
   if (ld_in < (layout == glu::PAIRED ? 2 * N : N)) return GLU_ERR_STRIDE;
   return GLU_OK;
+}
+
+// A [rows, nb] MXFP8 scale matrix: row-major, or the zero-padded 128x4 layout.
+Operand mx_scales(const void* p, int64_t rows, int64_t nb, int flags) {
+  const int64_t bytes = glu_mxfp8_sf_bytes(rows, 32 * nb, (flags & glu::SF_SWIZZLED) ? 1 : 0);
+  if (bytes < 0) return Operand{(uintptr_t)p, 1, 0, 0, 1, -1};  // extent overflows
+  return mat(p, 1, bytes, bytes, 1);
 }
 
 bool any_overflow(std::initializer_list<Operand> ops) {
@@ -150,6 +161,15 @@ const char* glu_status_string(glu_status s) {
     case GLU_ERR_HIP: return "HIP launch failed";
   }
   return "unknown status";
+}
+
+int64_t glu_mxfp8_sf_bytes(int64_t rows, int64_t cols, int swizzled) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0 || (swizzled != 0 && swizzled != 1)) return -1;
+  const int64_t nb = cols / 32;
+  const int64_t rp = swizzled ? (rows + 127) / 128 * 128 : rows;
+  const int64_t cp = swizzled ? (nb + 3) / 4 * 4 : nb;
+  int64_t r;
+  return __builtin_mul_overflow(rp, cp, &r) ? -1 : r;
 }
 
 int64_t glu_nvfp4_sf_bytes(int64_t M, int64_t H, int sf_layout) {
@@ -230,8 +250,8 @@ glu_status glu_check_fwd_mxfp8(int act, int layout, int64_t M, int64_t N, const 
     return GLU_ERR_ALIGN;
   const int64_t in_cols = layout == glu::PAIRED ? 2 * N : N;
   const Operand G = mat(gate, M, in_cols, ld_in, 2), U = mat(up, M, N, ld_in, 2),
-                QR = mat(q_row, M, N, N, 1), SR = mat(s_row, M, N / 32, N / 32, 1),
-                QC = mat(q_col, N, M, M, 1), SC = mat(s_col, N, M / 32, M / 32, 1);
+                QR = mat(q_row, M, N, N, 1), SR = mx_scales(s_row, M, N / 32, flags),
+                QC = mat(q_col, N, M, M, 1), SC = mx_scales(s_col, N, M / 32, flags);
   if (any_overflow({G, U, QR, SR, QC, SC})) return GLU_ERR_SHAPE;
   if (((M + 31) / 32) * ((N + 63) / 64) > kMaxTiles) return GLU_ERR_SHAPE;
   return check_no_overlap({QR, SR, QC, SC}, {G, U});
@@ -261,8 +281,8 @@ glu_status glu_check_bwd_mxfp8(int act, int layout, int64_t M, int64_t N, const 
   if (__builtin_mul_overflow(N, (int64_t)2, &N2)) return GLU_ERR_SHAPE;
   const Operand G = mat(gate, M, N, ld_in, 2), U = mat(up, M, N, ld_in, 2),
                 D = mat(dh, M, N, ld_dh, 2), QR = mat(q_row, M, N2, N2, 1),
-                SR = mat(s_row, M, N2 / 32, N2 / 32, 1), QC = mat(q_col, N2, M, M, 1),
-                SC = mat(s_col, N2, M / 32, M / 32, 1);
+                SR = mx_scales(s_row, M, N2 / 32, flags), QC = mat(q_col, N2, M, M, 1),
+                SC = mx_scales(s_col, N2, M / 32, flags);
   if (any_overflow({G, U, D, QR, SR, QC, SC})) return GLU_ERR_SHAPE;
   if (((M + 31) / 32) * ((N + 63) / 64) > kMaxTiles) return GLU_ERR_SHAPE;
   return check_no_overlap({QR, SR, QC, SC}, {G, U, D});
@@ -306,8 +326,8 @@ glu_status glu_check_quant_mxfp8_f32(int64_t M, int64_t N, const float* x, int64
       !aligned16(s_col))
     return GLU_ERR_ALIGN;
   const Operand X = mat(x, M, N, ld_x, 4), QR = mat(q_row, M, N, N, 1),
-                SR = mat(s_row, M, N / 32, N / 32, 1), QC = mat(q_col, N, M, M, 1),
-                SC = mat(s_col, N, M / 32, M / 32, 1);
+                SR = mx_scales(s_row, M, N / 32, flags), QC = mat(q_col, N, M, M, 1),
+                SC = mx_scales(s_col, N, M / 32, flags);
   if (any_overflow({X, QR, SR, QC, SC})) return GLU_ERR_SHAPE;
   if (((M + 31) / 32) * ((N + 63) / 64) > kMaxTiles) return GLU_ERR_SHAPE;
   return check_no_overlap({QR, SR, QC, SC}, {X});

@@ -556,6 +556,70 @@ __device__ __forceinline__ void stage_f32(const float (&v)[4][8], const Stage<T,
   }
 }
 
+// Scale words in the zero-padded 128x4 layout (GLU_SF_SWIZZLED).  The scale matrix of a
+// direction is [rows, nb] (rowwise: [M, ldq/32]; colwise: [ldq, M/32]), padded to
+// Rp = ceil(rows/128)*128 and Cp = ceil(nb/4)*4; scale (r, c) sits at sf128x4_offset(r, c, Cp).
+// A tile's 4 consecutive blocks of one row (or column) of the quantized matrix are one aligned
+// 4-byte group there.  Offsets are taken from the start of the tile's first 128-row band of the
+// scale matrix, so they stay small.  Padding bytes are written as zeros: blocks outside the
+// matrix were staged as zero scales, and the launch adds tiles where the padding reaches past
+// the last tile (see launch).  In the backward, a run of da's last scale columns that would
+// reach into db's is written byte by byte, only da's bytes, and so are db's runs when its
+// first scale column is not a multiple of 4.
+template <class T, int FLAGS>
+__device__ __forceinline__ void write_row_scales_128x4(const Stage<T, FLAGS>& st, const MxArgs& a,
+                                                       int64_t r0, int64_t c0, int64_t coloff,
+                                                       int64_t ldq, int tid) {
+  constexpr int TM = T::TM, NB = T::TN / 32;
+  const int64_t nbt = ldq / 32, cp = (nbt + 3) / 4 * 4, rp = (a.M + 127) / 128 * 128;
+  const int64_t part_end = (coloff + a.N) / 32;  // blocks of this part end here
+  const bool last = coloff + a.N == ldq;          // padding columns follow this part
+  const int64_t band0 = r0 / 128 * (cp / 4) * 512;
+  const auto sout = rsrc(a.s_row + band0);
+  const int row = tid < TM ? tid : 0;
+  const int64_t gr = r0 + row;
+  const bool row_ok = tid < TM && gr < rp;
+  // db's first block is 4-aligned only when N % 128 == 0; a misaligned run of 4 blocks spans
+  // two groups of the layout, so it goes byte by byte
+  const bool aligned = ((coloff / 32) & 3) == 0;
+#pragma unroll
+  for (int g = 0; g < NB / 4; g++) {
+    const int64_t b = (coloff + c0) / 32 + 4 * g;
+    const uint8_t* src = st.rs + row * NB + 4 * g;
+    if (aligned && (b + 4 <= part_end || (last && b < cp))) {
+      const uint32_t off = (uint32_t)(sf128x4_offset(gr, b, cp) - band0);
+      __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t*>(src), sout,
+                                            row_ok ? off : kOob, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int64_t bj = b + j;
+        const bool ok = row_ok && (bj < part_end || (last && bj < cp));
+        const uint32_t off = (uint32_t)(sf128x4_offset(gr, bj, cp) - band0);
+        __builtin_amdgcn_raw_buffer_store_b8(src[j], sout, ok ? off : kOob, 0, 0);
+      }
+    }
+  }
+}
+
+template <class T, int FLAGS>
+__device__ __forceinline__ void write_col_scales_128x4(const Stage<T, FLAGS>& st, const MxArgs& a,
+                                                       int64_t r0, int64_t c0, int64_t coloff,
+                                                       int64_t ldq, int tid) {
+  constexpr int TN = T::TN;
+  static_assert(T::TM == 128, "one 4-byte group of colwise scales per tile column");
+  const int64_t cp = (a.M / 32 + 3) / 4 * 4, rp = (ldq + 127) / 128 * 128;
+  const bool last = coloff + a.N == ldq;
+  const int64_t band0 = (coloff + c0) / 128 * (cp / 4) * 512;
+  const auto sout = rsrc(a.s_col + band0);
+  const int col = tid < TN ? tid : 0;
+  const int64_t gc = coloff + c0 + col;  // row of the colwise scale matrix
+  const bool ok = tid < TN && (c0 + col < a.N || (last && gc < rp));
+  const uint32_t off = (uint32_t)(sf128x4_offset(gc, r0 / 32, cp) - band0);
+  __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t*>(st.cs + col * 4), sout,
+                                        ok ? off : kOob, 0, 0);
+}
+
 // Writes a staged part to global memory: the part is the [M, N] matrix at column offset
 // `coloff` of the quantized matrix, whose rows hold ldq codes; the tile starts at (r0, c0).
 // Stores are raw buffer stores through descriptors based at the tile's first byte (scalar
@@ -566,7 +630,8 @@ __device__ __forceinline__ void stage_f32(const float (&v)[4][8], const Stage<T,
 // 4-byte aligned and in range, else byte by byte.
 template <class T, int FLAGS, bool NT>
 __device__ __forceinline__ void write_rows(const Stage<T, FLAGS>& st, const MxArgs& a, int64_t r0,
-                                          int64_t c0, int64_t coloff, int64_t ldq, int tid) {
+                                          int64_t c0, int64_t coloff, int64_t ldq, int tid,
+                                          bool swz) {
   constexpr int AUX = NT ? 2 : 0;
   const int64_t M = a.M, N = a.N;
   constexpr int TM = T::TM, TN = T::TN, NTHREADS = T::NTHREADS, RSEG = T::RSEG, CSEG = T::CSEG;
@@ -585,6 +650,10 @@ __device__ __forceinline__ void write_rows(const Stage<T, FLAGS>& st, const MxAr
       const u32x4 v = *reinterpret_cast<const u32x4*>(st.rq + row * TN + 16 * (seg ^ ((row >> 2) & (RSEG - 1))));
       const uint32_t off = seg_ok && row < rows ? (uint32_t)row * pitch + 16u * seg : kOob;
       __builtin_amdgcn_raw_buffer_store_b128(v, out, off, 0, AUX);
+    }
+    if (swz) {
+      write_row_scales_128x4<T, FLAGS>(st, a, r0, c0, coloff, ldq, tid);
+      return;
     }
     // scale words: thread `row` < TM writes the TN/32 scales of tile row `row`
     const int64_t nb = ldq / 32;
@@ -618,7 +687,8 @@ __device__ __forceinline__ void write_rows(const Stage<T, FLAGS>& st, const MxAr
 
 template <class T, int FLAGS, bool NT>
 __device__ __forceinline__ void write_cols(const Stage<T, FLAGS>& st, const MxArgs& a, int64_t r0,
-                                          int64_t c0, int64_t coloff, int64_t ldq, int tid) {
+                                          int64_t c0, int64_t coloff, int64_t ldq, int tid,
+                                          bool swz) {
   constexpr int AUX = NT ? 2 : 0;
   const int64_t M = a.M, N = a.N;
   constexpr int TM = T::TM, TN = T::TN, NTHREADS = T::NTHREADS, RSEG = T::RSEG, CSEG = T::CSEG;
@@ -640,6 +710,10 @@ __device__ __forceinline__ void write_cols(const Stage<T, FLAGS>& st, const MxAr
       __builtin_amdgcn_raw_buffer_store_b128(v, out, off, 0, AUX);
     }
     // scale words: thread `col` < TN writes the TM/32 scales of tile column `col`
+    if (swz) {
+      write_col_scales_128x4<T, FLAGS>(st, a, r0, c0, coloff, ldq, tid);
+      return;
+    }
     const int64_t nb = M / 32;
     const auto sout = rsrc(a.s_col + (coloff + c0) * nb + r0 / 32);
     const int col = tid < TN ? tid : 0;
@@ -661,8 +735,9 @@ __device__ __forceinline__ void write_cols(const Stage<T, FLAGS>& st, const MxAr
 template <class T, int FLAGS, bool NT>
 __device__ __forceinline__ void write_out(const Stage<T, FLAGS>& st, const MxArgs& a, int64_t r0,
                                           int64_t c0, int64_t coloff, int64_t ldq, int tid) {
-  write_rows<T, FLAGS, NT>(st, a, r0, c0, coloff, ldq, tid);
-  write_cols<T, FLAGS, NT>(st, a, r0, c0, coloff, ldq, tid);
+  const bool swz = (a.flags & SF_SWIZZLED) != 0;
+  write_rows<T, FLAGS, NT>(st, a, r0, c0, coloff, ldq, tid, swz);
+  write_cols<T, FLAGS, NT>(st, a, r0, c0, coloff, ldq, tid, swz);
 }
 
 // The wave's piece of tile (r0, c0).
@@ -769,7 +844,25 @@ template <int ACT, int LAYOUT, int FLAGS, int MODE>
 hipError_t launch(const MxArgs& a, hipStream_t s) {
   constexpr int TPW = tiles_per_workgroup<MODE>();
   using T = TileOf<FLAGS, MODE>;
-  const int64_t tiles_m = (a.M + T::TM - 1) / T::TM, tiles_n = (a.N + T::TN - 1) / T::TN;
+  int64_t tiles_m = (a.M + T::TM - 1) / T::TM, tiles_n = (a.N + T::TN - 1) / T::TN;
+  if (a.flags & SF_SWIZZLED) {
+    // tiles past the matrix (zero inputs, no codes written) cover the scale padding:
+    // rowwise padding rows up to a multiple of 128 and padding scale columns up to a multiple
+    // of 4 after the last part; colwise padding rows (columns of the quantized matrix) up to a
+    // multiple of 128 after the last part
+    const int64_t ldq = (MODE == MODE_BWD ? 2 : 1) * a.N, last = ldq - a.N;
+    const int64_t rp = (a.M + 127) / 128 * 128, wp = (ldq + 127) / 128 * 128;
+    if (FLAGS & ROWWISE) {
+      tiles_m = (rp + T::TM - 1) / T::TM;
+      const int64_t cpad = (ldq / 32 + 3) / 4 * 4 * 32;  // padded scale columns, in elements
+      const int64_t need = (cpad - last + T::TN - 1) / T::TN;
+      if (need > tiles_n) tiles_n = need;
+    }
+    if (FLAGS & COLWISE) {
+      const int64_t need = (wp - last + T::TN - 1) / T::TN;
+      if (need > tiles_n) tiles_n = need;
+    }
+  }
   const int64_t ntiles = tiles_m * tiles_n, per_xcd = (ntiles + 7) / 8;
   const int64_t wg_per_xcd = (per_xcd + TPW - 1) / TPW;
   return launch_kernel(k_mxfp8<ACT, LAYOUT, FLAGS, MODE, TPW>, dim3((unsigned)(8 * wg_per_xcd)),
@@ -779,7 +872,7 @@ hipError_t launch(const MxArgs& a, hipStream_t s) {
 
 template <int ACT, int LAYOUT, int MODE>
 hipError_t by_flags(const MxArgs& a, hipStream_t s) {
-  switch (a.flags) {
+  switch (a.flags & (ROWWISE | COLWISE)) {
     case ROWWISE: return launch<ACT, LAYOUT, ROWWISE, MODE>(a, s);
     case COLWISE: return launch<ACT, LAYOUT, COLWISE, MODE>(a, s);
     default: return launch<ACT, LAYOUT, ROWWISE | COLWISE, MODE>(a, s);

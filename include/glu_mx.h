@@ -77,8 +77,13 @@ enum { GLU_SWIGLU = 0, GLU_GEGLU_TANH = 1 };
  *               gate_j and column 2j+1 is up_j ([NV] Supported contract, weight layout). */
 enum { GLU_SPLIT = 0, GLU_PAIRED = 1 };
 
-/* MXFP8 direction flags; both = GLU_ROWWISE | GLU_COLWISE. */
-enum { GLU_ROWWISE = 1, GLU_COLWISE = 2 };
+/* MXFP8 flags: the directions (both = GLU_ROWWISE | GLU_COLWISE), optionally ORed with
+ * GLU_SF_SWIZZLED, which writes both E8M0 scale matrices in the zero-padded 128x4 layout
+ * described for GLU_SF_128x4 below (a [rows, nb] scale matrix then takes Rp*Cp bytes with
+ * Rp = ceil(rows/128)*128 and Cp = ceil(nb/4)*4; see glu_mxfp8_sf_bytes).  No page fixes a
+ * layout for MXFP8 scales; this is the GEMM-ready block-scale layout of [NV] Supported
+ * contract, offered as an option. */
+enum { GLU_ROWWISE = 1, GLU_COLWISE = 2, GLU_SF_SWIZZLED = 4 };
 
 /* NVFP4 scale-factor layout.
  *   GLU_SF_ROWMAJOR: [M, H/16] bytes.
@@ -119,6 +124,7 @@ glu_status glu_bwd(int act, int layout, int64_t M, int64_t N, const uint16_t* ga
  * (RCEIL); codes = E4M3(h * 2^-e), nearest even.  A block holding NaN or Inf gets scale
  * 0xFF and codes 0x7F.
  *   rowwise (flags & GLU_ROWWISE): q_row [M, N] codes, s_row [M, N/32] scales.
+ *   (With GLU_SF_SWIZZLED, s_row and s_col hold the same scales in the 128x4 layout.)
  *   colwise (flags & GLU_COLWISE): q_col [N, M] codes (row j holds column j of h, i.e.
  *                                  the column-major [M, N]), s_col [N, M/32] scales.
  * A disabled direction's two pointers must be NULL.  Needs N % 32 == 0, and M % 32 == 0
@@ -191,6 +197,12 @@ glu_status glu_check_quant_nvfp4_f32(int64_t M, int64_t H, const float* x, int64
 /* Bytes of the scale buffer glu_fwd_nvfp4 / glu_quant_nvfp4_f32 write for this layout
  * (M*H/16 row-major, Rp*Cp for 128x4), or -1 for bad arguments. */
 int64_t glu_nvfp4_sf_bytes(int64_t M, int64_t H, int sf_layout);
+
+/* Bytes of one MXFP8 scale buffer covering a quantized [rows, cols] matrix (cols % 32 == 0):
+ * rows*cols/32 row-major (swizzled = 0) or Rp*Cp in the 128x4 layout (swizzled = 1), or -1
+ * for bad arguments.  Rowwise scales: rows = M, cols = N (2N for the backward).  Colwise
+ * scales: rows = N (2N), cols = M. */
+int64_t glu_mxfp8_sf_bytes(int64_t rows, int64_t cols, int swizzled);
 
 /* Static text for a status code (never NULL). */
 const char* glu_status_string(glu_status status);

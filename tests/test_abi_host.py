@@ -147,6 +147,22 @@ def mxb(**kw):
                                  P(a["qc"]), P(a["sc"]))
 
 
+def test_mxfp8_swizzled_scale_flag_and_sizes():
+    SWZ = 4
+    assert mxf(flags=3 | SWZ) == OK and mxf(flags=1 | SWZ, qc=0, sc=0) == OK
+    assert mxf(flags=SWZ) == ARG and mxf(flags=8) == ARG and mxf(flags=3 | 8) == ARG
+    # padded scale buffers: [M, N/32] -> ceil(M/128)*128 x ceil(N/128)*4 bytes
+    f = L.glu_mxfp8_sf_bytes
+    f.restype = ctypes.c_int64
+    assert f(130, 224, 1) == 256 * 8 and f(130, 224, 0) == 130 * 7
+    assert f(128, 128, 1) == 128 * 4 and f(1, 32, 1) == 128 * 4
+    assert f(1, 33, 1) == -1 and f(-1, 32, 0) == -1 and f(1, 32, 2) == -1
+    # the padded extent counts for overlap: 64 x 128 both ways, s_row takes 128 * 4 bytes
+    assert mxf(flags=3 | SWZ, sr=D0, sc=D0 + 512) == OK
+    assert mxf(flags=3 | SWZ, sr=D0, sc=D0 + 256) == OVERLAP
+    assert mxf(flags=3, sr=D0, sc=D0 + 256) == OK  # row-major s_row is 64 * 4 bytes
+
+
 def test_bwd_mxfp8_checks():
     assert mxb() == OK
     assert mxb(layout=1, up=0) == UNSUP
@@ -205,7 +221,7 @@ def test_entry_points_fail_before_any_hip_call():
     assert L.glu_fwd_mxfp8(0, 0, 64, 40, P(A0), P(B0), 40, 1, P(C0), P(D0), P(0), P(0), P(0)) == SHAPE
     assert L.glu_bwd_mxfp8(0, 1, 64, 64, P(A0), P(0), 128, P(C0), 64, 1, P(D0), P(E0), P(0), P(0), P(0)) == UNSUP
     assert L.glu_fwd_nvfp4(1, 1, 8, 24, P(A0), P(0), 48, P(C0), P(D0), 0, P(0)) == SHAPE
-    assert L.glu_quant_mxfp8_f32(32, 32, P(A0), 32, 7, P(B0), P(C0), P(D0), P(E0), P(0)) == ARG
+    assert L.glu_quant_mxfp8_f32(32, 32, P(A0), 32, 8, P(B0), P(C0), P(D0), P(E0), P(0)) == ARG
     assert L.glu_quant_nvfp4_f32(32, 32, P(A0 + 4), 32, P(B0), P(C0), 0, P(0)) == ALIGN
 
 

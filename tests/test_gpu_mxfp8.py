@@ -179,6 +179,38 @@ def test_partial_tiles_every_direction(gpu, M, N):
             assert np.array_equal(u8(out[1]), ob[2]) and np.array_equal(u8(out[3]), ob[3])
 
 
+@pytest.mark.parametrize("M,N", [(352, 480), (160, 224), (256, 96), (130, 4160)])
+def test_swizzled_scales_match_oracle(gpu, M, N):
+    """GLU_SF_SWIZZLED: both scale matrices in the zero-padded 128x4 layout, forward, backward
+    and the FP32 hook, bit for bit against the oracle (whose padding is zero; the device
+    buffers start uninitialized, so every padding byte must be written).  N = 224 starts db's
+    scales off a 4-column boundary and leaves padding past the last colwise tile; M = 130
+    (rowwise only) pads 126 rows."""
+    gate, up, dh = si.glu_operands(M, N, seed=M + 3 * N, outliers=True, with_dh=True)
+    gd, ud, dd = gate.cuda(), up.cuda(), dh.cuda()
+    h = bits(gpu.glu_fwd(gd, ud))
+    da, db = gpu.glu_bwd(gd, ud, dd)
+    X = np.concatenate([bits(da), bits(db)], axis=1)
+    for row, col in FLAGS:
+        if col and M % 32:
+            continue
+        f = _flags(row, col) | oracle.SF_SWIZZLED
+        for got, want in ((gpu.glu_fwd_mxfp8(gd, ud, rowwise=row, colwise=col, swizzled=True), _q(h, f)),
+                          (gpu.glu_bwd_mxfp8(gd, ud, dd, rowwise=row, colwise=col, swizzled=True), _q(X, f))):
+            if row:
+                assert np.array_equal(u8(got[0]), want[0]) and np.array_equal(u8(got[2]), want[1])
+            if col:
+                assert np.array_equal(u8(got[1]), want[2]) and np.array_equal(u8(got[3]), want[3])
+    x = si.from_bits(h).float().numpy()
+    f = oracle.ROWWISE | (oracle.COLWISE if M % 32 == 0 else 0) | oracle.SF_SWIZZLED
+    got = gpu.glu_quant_mxfp8_f32(torch.from_numpy(x).cuda(), rowwise=True, colwise=bool(f & 2),
+                                  swizzled=True)
+    want = oracle.quant_mxfp8(x, f)
+    assert np.array_equal(u8(got[2]), want[1])
+    if f & 2:
+        assert np.array_equal(u8(got[3]), want[3])
+
+
 def test_row_slices_are_batch_invariant(gpu):
     gate, up = si.glu_operands(256, 256, seed=9, outliers=True)
     gd, ud = gate.cuda(), up.cuda()
