@@ -15,7 +15,7 @@ import numpy as np
 
 from . import build as _build
 
-SWIGLU, GEGLU_TANH = 0, 1
+SWIGLU, GEGLU_TANH, GEGLU_ERF, RELU2 = 0, 1, 2, 3
 SPLIT, PAIRED = 0, 1
 ROWWISE, COLWISE, SF_SWIZZLED = 1, 2, 4
 SF_ROWMAJOR, SF_128x4 = 0, 1

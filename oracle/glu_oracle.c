@@ -33,6 +33,9 @@
  * function that uses it):
  *   - the quantizer consumes the BF16-rounded activation, rounded once;
  *   - GELU is the tanh approximation with sqrt(2/pi) and 0.044715;
+ *   - two further activations through the same path (the [MX] page's Known
+ *     limitations plan more than SiLU; none is named): GeGLU with the exact,
+ *     erf-based GELU x * Phi(x), and ReLU^2 GLU, max(x, 0)^2 * up;
  *   - RCEIL: the scale is the smallest power of two 2^e, e in [-127, 127], with
  *     448 * 2^e >= amax (an all-zero block takes e = -127);
  *   - E4M3 saturates to +-448; E2M1 saturates to +-6;
@@ -58,7 +61,7 @@
 #error "the oracle must be built without fast-math"
 #endif
 
-enum { ORC_SWIGLU = 0, ORC_GEGLU_TANH = 1 };
+enum { ORC_SWIGLU = 0, ORC_GEGLU_TANH = 1, ORC_GEGLU_ERF = 2, ORC_RELU2 = 3 };
 enum { ORC_SPLIT = 0, ORC_PAIRED = 1 };
 enum { ORC_ROWWISE = 1, ORC_COLWISE = 2, ORC_SF_SWIZZLED = 4 };
 enum { ORC_SF_ROWMAJOR = 0, ORC_SF_128x4 = 1 };
@@ -178,7 +181,8 @@ int orc_mx_scale_exponent(double amax) {
 
 /* ------------------------------------------------------------------------- */
 /* Activations ([MX] Summary: swiglu = silu(gate) * up; [NV] Summary and [GE]     */
-/* Summary: GeGLU = gelu(gate) * up, tanh approximation by reading)            */
+/* Summary: GeGLU = gelu(gate) * up, tanh approximation by reading; [MX] Known    */
+/* limitations: more activations planned, here erf-GELU and ReLU^2 by reading)  */
 /* ------------------------------------------------------------------------- */
 
 static const double GELU_K0 = 0.79788456080286535588; /* sqrt(2/pi) */
@@ -187,23 +191,42 @@ static const double GELU_K1 = 0.044715;
 /* logistic function; 1/(1+exp(-z)) is accurate in both tails in binary64 */
 static double logistic(double z) { return 1.0 / (1.0 + exp(-z)); }
 
+/* Standard normal CDF and density: Phi(x) = erfc(-x / sqrt 2) / 2 (erfc keeps its
+ * relative accuracy for x << 0, where 1 + erf(x / sqrt 2) cancels), phi(x) =
+ * exp(-x^2 / 2) / sqrt(2 pi). */
+static const double SQRT1_2 = 0.70710678118654752440;    /* 1/sqrt(2) */
+static const double INV_SQRT_2PI = 0.39894228040143267794; /* 1/sqrt(2 pi) */
+static double normal_cdf(double x) { return 0.5 * erfc(-x * SQRT1_2); }
+static double normal_pdf(double x) { return INV_SQRT_2PI * exp(-0.5 * x * x); }
+
+/* ReLU^2: max(x, 0)^2, with NaN kept NaN (a plain max would drop it). */
+static double relu(double x) { return x > 0.0 ? x : (x <= 0.0 ? 0.0 : x); }
+
 /* act(x):  silu(x) = x * sigma(x);
- *          gelu_tanh(x) = x/2 * (1 + tanh(k0 (x + k1 x^3))).
+ *          gelu_tanh(x) = x/2 * (1 + tanh(k0 (x + k1 x^3)));
+ *          gelu_erf(x) = x * Phi(x);
+ *          relu2(x) = max(x, 0)^2.
  * 1 + tanh(u) is evaluated as 2 * sigma(2u), the same quantity written without
  * the cancellation that 1 + tanh(u) suffers for u << 0. */
 double orc_act(int act, double x) {
   if (act == ORC_SWIGLU) return x * logistic(x);
+  if (act == ORC_GEGLU_ERF) return x * normal_cdf(x);
+  if (act == ORC_RELU2) return relu(x) * relu(x);
   double u = GELU_K0 * (x + GELU_K1 * x * x * x);
   double one_plus_t = 2.0 * logistic(2.0 * u);
   return 0.5 * x * one_plus_t;
 }
 
 /* act'(x):  silu'(x) = sigma(x) (1 + x (1 - sigma(x)));
- *           gelu_tanh'(x) = (1 + t)/2 + x/2 (1 - t^2) k0 (1 + 3 k1 x^2).
+ *           gelu_tanh'(x) = (1 + t)/2 + x/2 (1 - t^2) k0 (1 + 3 k1 x^2);
+ *           gelu_erf'(x) = Phi(x) + x phi(x);
+ *           relu2'(x) = 2 max(x, 0)  (0 at the kink x = 0, where both sides agree).
  * 1 - sigma(x) is sigma(-x); 1 - t^2 = (1 + t)(1 - t) with 1 -+ t = 2 sigma(-+2u)
  * for the same reason as above. */
 double orc_act_grad(int act, double x) {
   if (act == ORC_SWIGLU) return logistic(x) * (1.0 + x * logistic(-x));
+  if (act == ORC_GEGLU_ERF) return normal_cdf(x) + x * normal_pdf(x);
+  if (act == ORC_RELU2) return 2.0 * relu(x);
   double u = GELU_K0 * (x + GELU_K1 * x * x * x);
   double one_plus_t = 2.0 * logistic(2.0 * u);
   double one_minus_t = 2.0 * logistic(-2.0 * u);

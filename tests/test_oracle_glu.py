@@ -1,9 +1,11 @@
 """Pins for the oracle's activations and GLU forward/backward (CPU only).
 
 Independent references: mpmath at 80 significant digits using the textbook formulas
-(silu = x/(1+e^-x); gelu_tanh = x/2 (1 + tanh(sqrt(2/pi)(x + 0.044715 x^3)))), mpmath's
-numerical differentiation for the derivatives, torch float64 functional and autograd,
-closed forms at special points, and the reflection identity act(-x) = act(x) - x.
+(silu = x/(1+e^-x); gelu_tanh = x/2 (1 + tanh(sqrt(2/pi)(x + 0.044715 x^3)));
+gelu_erf = x/2 (1 + erf(x/sqrt 2)); relu2 = max(x, 0)^2), mpmath's numerical
+differentiation for the derivatives, torch float64 functional and autograd, closed forms
+at special points, the reflection identity act(-x) = act(x) - x of the three GELU/SiLU
+forms, and the Mills-ratio asymptotic series for the erf-GELU tail.
 """
 import math
 
@@ -17,15 +19,30 @@ import oracle
 import synthetic_inputs as si
 
 mp.mp.dps = 80
-ACTS = [oracle.SWIGLU, oracle.GEGLU_TANH]
+ACTS = [oracle.SWIGLU, oracle.GEGLU_TANH, oracle.GEGLU_ERF, oracle.RELU2]
+GELU_LIKE = [oracle.SWIGLU, oracle.GEGLU_TANH, oracle.GEGLU_ERF]   # act(x) = x * F(x), F(-x) = 1 - F(x)
 
 
 def mp_act(kind, x):
     x = mp.mpf(x)
     if kind == oracle.SWIGLU:
         return x / (1 + mp.exp(-x))
+    if kind == oracle.GEGLU_ERF:   # 1 + erf(x / sqrt 2) written as erfc(-x / sqrt 2)
+        return x / 2 * mp.erfc(-x / mp.sqrt(2))
+    if kind == oracle.RELU2:
+        return x * x if x > 0 else mp.mpf(0)
     u = mp.sqrt(2 / mp.pi) * (x + mp.mpf("0.044715") * x ** 3)
     return x / 2 * (1 + mp.tanh(u))
+
+
+def torch_act(kind, x):
+    if kind == oracle.SWIGLU:
+        return F.silu(x)
+    if kind == oracle.GEGLU_TANH:
+        return F.gelu(x, approximate="tanh")
+    if kind == oracle.GEGLU_ERF:
+        return F.gelu(x, approximate="none")
+    return torch.relu(x) ** 2
 
 
 def mp_act_grad(kind, x):
@@ -43,8 +60,8 @@ def test_act_against_mpmath(kind):
     got = oracle.act(kind, SAMPLE_X)
     for x, g in zip(SAMPLE_X, got):
         ref = mp_act(kind, x)
-        if ref == 0:
-            assert g == 0
+        if abs(ref) < mp.mpf("1e-300"):   # zero, or below the binary64 range
+            assert abs(g) < 1e-300
             continue
         rel = abs((mp.mpf(g) - ref) / ref)
         assert rel < 1e-13, (kind, x, g, ref)
@@ -53,6 +70,8 @@ def test_act_against_mpmath(kind):
 @pytest.mark.parametrize("kind", ACTS)
 def test_act_grad_against_mpmath(kind):
     xs = SAMPLE_X[np.abs(SAMPLE_X) < 40]
+    if kind == oracle.RELU2:
+        xs = xs[xs != 0]   # numerical differentiation straddles the kink
     got = oracle.act_grad(kind, xs)
     for x, g in zip(xs, got):
         ref = mp_act_grad(kind, x)
@@ -60,7 +79,16 @@ def test_act_grad_against_mpmath(kind):
 
 
 def test_act_special_values():
-    S, G = oracle.SWIGLU, oracle.GEGLU_TANH
+    S, G, E, R = oracle.SWIGLU, oracle.GEGLU_TANH, oracle.GEGLU_ERF, oracle.RELU2
+    # erf-GELU: Phi(1) = 0.841344746068542948..., Phi(-1) = 1 - Phi(1), phi(1) = e^{-1/2}/sqrt(2 pi)
+    assert oracle.act(E, [0.0])[0] == 0.0 and oracle.act_grad(E, [0.0])[0] == 0.5
+    assert abs(oracle.act(E, [1.0])[0] - 0.8413447460685429) < 1e-15
+    assert abs(oracle.act(E, [-1.0])[0] + 0.15865525393145707) < 1e-15
+    assert abs(oracle.act_grad(E, [1.0])[0] - (0.8413447460685429 + 0.24197072451914337)) < 1e-15
+    # ReLU^2 at the kink and either side; NaN stays NaN
+    assert list(oracle.act(R, [-3.0, -0.0, 0.0, 1.5, 3.0])) == [0.0, 0.0, 0.0, 2.25, 9.0]
+    assert list(oracle.act_grad(R, [-3.0, 0.0, 1.5, 3.0])) == [0.0, 0.0, 3.0, 6.0]
+    assert np.isnan(oracle.act(R, [np.nan])[0]) and np.isnan(oracle.act_grad(R, [np.nan])[0])
     assert oracle.act(S, [0.0])[0] == 0.0 and oracle.act(G, [0.0])[0] == 0.0
     assert oracle.act_grad(S, [0.0])[0] == 0.5 and oracle.act_grad(G, [0.0])[0] == 0.5
     assert abs(oracle.act(S, [1.0])[0] - 0.7310585786300049) < 1e-15
@@ -73,31 +101,36 @@ def test_act_special_values():
     assert abs(oracle.act(S, [x0])[0] - (x0 + 1)) < 1e-15
 
 
-@pytest.mark.parametrize("kind", ACTS)
+@pytest.mark.parametrize("kind", GELU_LIKE)
 def test_act_reflection(kind):
-    """silu(-x) = silu(x) - x and gelu_tanh(-x) = gelu_tanh(x) - x (sigma(-z) = 1 - sigma(z))."""
+    """silu(-x) = silu(x) - x, and the same for both GELUs (sigma(-z) = 1 - sigma(z),
+    Phi(-x) = 1 - Phi(x))."""
     x = np.linspace(-8, 8, 1601)
     a, b = oracle.act(kind, -x), oracle.act(kind, x) - x
     assert np.allclose(a, b, rtol=1e-12, atol=1e-14)
 
 
+# torch evaluates both GELUs through 1 + tanh or 1 + erf, which loses relative accuracy
+# for x << 0; there the comparison stops at x = -4
+_TORCH_CANCELS = (oracle.GEGLU_TANH, oracle.GEGLU_ERF)
+
+
 @pytest.mark.parametrize("kind", ACTS)
 def test_act_against_torch_float64(kind):
     x = torch.linspace(-20, 20, 40001, dtype=torch.float64)
-    ref = F.silu(x) if kind == oracle.SWIGLU else F.gelu(x, approximate="tanh")
+    ref = torch_act(kind, x)
     got = torch.from_numpy(oracle.act(kind, x.numpy()))
-    # torch evaluates gelu through 1 + tanh, which loses relative accuracy for x << 0
-    mask = x > -4 if kind == oracle.GEGLU_TANH else torch.ones_like(x, dtype=torch.bool)
+    mask = x > -4 if kind in _TORCH_CANCELS else torch.ones_like(x, dtype=torch.bool)
     assert torch.allclose(got[mask], ref[mask], rtol=1e-13, atol=1e-15)
 
 
 @pytest.mark.parametrize("kind", ACTS)
 def test_act_grad_against_autograd(kind):
     x = torch.linspace(-20, 20, 4001, dtype=torch.float64, requires_grad=True)
-    y = F.silu(x) if kind == oracle.SWIGLU else F.gelu(x, approximate="tanh")
+    y = torch_act(kind, x)
     (g,) = torch.autograd.grad(y.sum(), x)
     got = torch.from_numpy(oracle.act_grad(kind, x.detach().numpy()))
-    mask = x.detach() > -4 if kind == oracle.GEGLU_TANH else torch.ones(x.shape, dtype=torch.bool)
+    mask = x.detach() > -4 if kind in _TORCH_CANCELS else torch.ones(x.shape, dtype=torch.bool)
     assert torch.allclose(got[mask], g[mask], rtol=1e-12, atol=1e-14)
 
 
@@ -105,8 +138,44 @@ def test_act_grad_central_difference():
     eps = 2.0 ** -20
     x = np.linspace(-6, 6, 121)
     for kind in ACTS:
-        fd = (oracle.act(kind, x + eps) - oracle.act(kind, x - eps)) / (2 * eps)
-        assert np.allclose(oracle.act_grad(kind, x), fd, rtol=1e-8, atol=1e-9)
+        xs = x[x != 0] if kind == oracle.RELU2 else x
+        fd = (oracle.act(kind, xs + eps) - oracle.act(kind, xs - eps)) / (2 * eps)
+        assert np.allclose(oracle.act_grad(kind, xs), fd, rtol=1e-8, atol=1e-9)
+
+
+def test_gelu_erf_tail_mills_ratio():
+    """For x << 0, Phi(x) = phi(x)/|x| (1 - 1/x^2 + 3/x^4 - 15/x^6 + ... + (-1)^k (2k-1)!!/x^2k)
+    (the asymptotic series of the Mills ratio); with 20 terms at |x| >= 14 the truncation
+    error is below 1e-20 relative.  Covers the range where Phi(x) is below the FP32 normal
+    range."""
+    for x in [-14.0, -16.0, -20.0, -25.0, -30.0, -37.0]:
+        phi = math.exp(-0.5 * x * x) / math.sqrt(2 * math.pi)
+        s, term = 0.0, 1.0
+        for k in range(20):
+            s += term
+            term *= -(2 * k + 1) / (x * x)
+        want_act = x * phi / abs(x) * s
+        want_grad = phi / abs(x) * s + x * phi
+        assert abs(oracle.act(oracle.GEGLU_ERF, [x])[0] / want_act - 1) < 1e-13, x
+        assert abs(oracle.act_grad(oracle.GEGLU_ERF, [x])[0] / want_grad - 1) < 1e-12, x
+
+
+def test_relu2_glu_is_exact():
+    """relu2(g) * u of BF16 operands has at most 24 significant bits (BF16 values are
+    m * 2^e with m < 256), so it is exact in binary64 and the oracle's BF16 output is the
+    rounding of the exact rational product, computed here with Fractions."""
+    from fractions import Fraction
+    gate, up = si.glu_operands(32, 64, seed=21)
+    gb, ub = si.to_bits(gate), si.to_bits(up)
+    h = oracle.glu_fwd(oracle.RELU2, gb, ub).ravel()
+    g, u = oracle.bf16_to_f64(gb).ravel(), oracle.bf16_to_f64(ub).ravel()
+    for i in range(g.size):
+        if g[i] <= 0:
+            assert int(h[i]) & 0x7FFF == 0, i
+            continue
+        exact = Fraction(g[i]) ** 2 * Fraction(u[i])
+        assert Fraction(float(exact)) == exact
+        assert int(h[i]) == int(oracle.bf16_from_f64([float(exact)])[0]), i
 
 
 # ---- GLU forward / backward ----------------------------------------------------------
@@ -129,8 +198,7 @@ def test_glu_fwd_matches_float64_reference(kind):
     gate, up = si.glu_operands(64, 96, seed=11)
     h = oracle.glu_fwd(kind, si.to_bits(gate), si.to_bits(up))
     g64, u64 = gate.double(), up.double()
-    a = F.silu(g64) if kind == oracle.SWIGLU else F.gelu(g64, approximate="tanh")
-    assert _bf16_nearest_ok(h, a * u64)
+    assert _bf16_nearest_ok(h, torch_act(kind, g64) * u64)
 
 
 @pytest.mark.parametrize("kind", ACTS)
@@ -138,8 +206,7 @@ def test_glu_bwd_matches_autograd(kind):
     gate, up, dh = si.glu_operands(48, 80, seed=12, with_dh=True)
     g64 = gate.double().requires_grad_(True)
     u64 = up.double().requires_grad_(True)
-    a = F.silu(g64) if kind == oracle.SWIGLU else F.gelu(g64, approximate="tanh")
-    (a * u64).backward(dh.double())
+    (torch_act(kind, g64) * u64).backward(dh.double())
     da, db = oracle.glu_bwd(kind, si.to_bits(gate), si.to_bits(up), si.to_bits(dh))
     assert _bf16_nearest_ok(da, g64.grad)
     assert _bf16_nearest_ok(db, u64.grad)
@@ -162,7 +229,7 @@ def test_glu_bwd_identities(kind):
     assert not np.any(da1 & 0x7FFF)
 
 
-@pytest.mark.parametrize("kind", ACTS)
+@pytest.mark.parametrize("kind", [oracle.SWIGLU, oracle.GEGLU_TANH])
 def test_glu_tail_closed_form(kind):
     """For z << 0 the logistic is e^z to 1e-30 relative, so act(x) = x e^{z} in closed
     form; with up = 1 the BF16 output is the rounding of that product (tiny but nonzero

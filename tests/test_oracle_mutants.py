@@ -16,7 +16,7 @@ import test_oracle_formats as tf
 import test_oracle_glu as tg
 import test_oracle_quant as tq
 
-S, G = oracle.SWIGLU, oracle.GEGLU_TANH
+S, G, E, R = oracle.SWIGLU, oracle.GEGLU_TANH, oracle.GEGLU_ERF, oracle.RELU2
 
 # (name, text to find, replacement, pins that should notice)
 MUTANTS = [
@@ -28,6 +28,17 @@ MUTANTS = [
      [lambda: tg.test_act_grad_against_mpmath(G)]),
     ("gelu' drops a factor", "0.5 * x * (one_plus_t * one_minus_t)", "0.5 * x * (one_plus_t)",
      [lambda: tg.test_act_grad_against_autograd(G)]),
+    ("erf-GELU CDF sign", "0.5 * erfc(-x * SQRT1_2)", "0.5 * erfc(x * SQRT1_2)",
+     [lambda: tg.test_act_against_mpmath(E)]),
+    ("erf-GELU' drops x", "normal_cdf(x) + x * normal_pdf(x)", "normal_cdf(x) + normal_pdf(x)",
+     [lambda: tg.test_act_grad_against_autograd(E)]),
+    ("erf-GELU density exponent", "exp(-0.5 * x * x)", "exp(-x * x)",
+     [lambda: tg.test_act_grad_against_mpmath(E)]),
+    ("relu2' drops the 2", "return 2.0 * relu(x);", "return relu(x);",
+     [lambda: tg.test_act_grad_against_autograd(R)]),
+    ("relu2 is plain relu", "return relu(x) * relu(x);", "return relu(x);",
+     [tg.test_relu2_glu_is_exact]),
+    ("relu drops NaN", "(x <= 0.0 ? 0.0 : x)", "0.0", [tg.test_act_special_values]),
     ("ties away from zero", "return (lo % 2 == 0) ? lo : hi;", "return hi;",
      [tf.test_e4m3_golden, tf.test_e2m1_golden, tf.test_bf16_overflow_and_specials]),
     ("RCEIL on equality", "ldexp(448.0, e) < amax", "ldexp(448.0, e) <= amax",

@@ -211,7 +211,7 @@ def test_mx_swizzled_scales_equal_rowmajor_after_unswizzle():
 def test_fused_equals_glu_then_quantizer():
     gate, up, dh = si.glu_operands(64, 64, seed=25, outliers=True, with_dh=True)
     gb, ub, db_ = si.to_bits(gate), si.to_bits(up), si.to_bits(dh)
-    for kind in (oracle.SWIGLU, oracle.GEGLU_TANH):
+    for kind in (oracle.SWIGLU, oracle.GEGLU_TANH, oracle.GEGLU_ERF, oracle.RELU2):
         h = oracle.glu_fwd(kind, gb, ub)
         hf = si.from_bits(h).float().numpy()
         a = oracle.glu_fwd_mxfp8(kind, gb, ub, flags=3)
