@@ -33,8 +33,8 @@
  * function that uses it):
  *   - the quantizer consumes the BF16-rounded activation, rounded once;
  *   - GELU is the tanh approximation with sqrt(2/pi) and 0.044715;
- *   - two further activations through the same path (the [MX] page's Known
- *     limitations plan more than SiLU; none is named): GeGLU with the exact,
+ *   - two further activations through the same path (the [MX] page's Follow-ups
+ *     plan more than SiLU; none is named): GeGLU with the exact,
  *     erf-based GELU x * Phi(x), and ReLU^2 GLU, max(x, 0)^2 * up;
  *   - RCEIL: the scale is the smallest power of two 2^e, e in [-127, 127], with
  *     448 * 2^e >= amax (an all-zero block takes e = -127);
@@ -181,8 +181,8 @@ int orc_mx_scale_exponent(double amax) {
 
 /* ------------------------------------------------------------------------- */
 /* Activations ([MX] Summary: swiglu = silu(gate) * up; [NV] Summary and [GE]     */
-/* Summary: GeGLU = gelu(gate) * up, tanh approximation by reading; [MX] Known    */
-/* limitations: more activations planned, here erf-GELU and ReLU^2 by reading)  */
+/* Summary: GeGLU = gelu(gate) * up, tanh approximation by reading; [MX]         */
+/* Follow-ups: more activations planned, here erf-GELU and ReLU^2 by reading)    */
 /* ------------------------------------------------------------------------- */
 
 static const double GELU_K0 = 0.79788456080286535588; /* sqrt(2/pi) */
@@ -222,16 +222,24 @@ double orc_act(int act, double x) {
  *           gelu_erf'(x) = Phi(x) + x phi(x);
  *           relu2'(x) = 2 max(x, 0)  (0 at the kink x = 0, where both sides agree).
  * 1 - sigma(x) is sigma(-x); 1 - t^2 = (1 + t)(1 - t) with 1 -+ t = 2 sigma(-+2u)
- * for the same reason as above. */
+ * for the same reason as above.  gelu_tanh' is taken in the factored form
+ * (1 + t)/2 * (1 + x (1 - t) k0 (1 + 3 k1 x^2)), the same value, so that where it
+ * underflows (x << 0) the zero keeps the sign of the exact, negative, derivative
+ * instead of the +0 that a sum of two underflowed terms gives; gelu_erf' returns -0
+ * there for the same reason. */
 double orc_act_grad(int act, double x) {
   if (act == ORC_SWIGLU) return logistic(x) * (1.0 + x * logistic(-x));
-  if (act == ORC_GEGLU_ERF) return normal_cdf(x) + x * normal_pdf(x);
+  if (act == ORC_GEGLU_ERF) {
+    double d = normal_cdf(x) + x * normal_pdf(x);
+    /* both terms underflow for x << 0, where the exact derivative is negative */
+    return (d == 0.0 && x < 0.0 && isfinite(x)) ? -0.0 : d;
+  }
   if (act == ORC_RELU2) return 2.0 * relu(x);
   double u = GELU_K0 * (x + GELU_K1 * x * x * x);
   double one_plus_t = 2.0 * logistic(2.0 * u);
   double one_minus_t = 2.0 * logistic(-2.0 * u);
-  return 0.5 * one_plus_t +
-         0.5 * x * (one_plus_t * one_minus_t) * GELU_K0 * (1.0 + 3.0 * GELU_K1 * x * x);
+  return 0.5 * one_plus_t *
+         (1.0 + x * one_minus_t * GELU_K0 * (1.0 + 3.0 * GELU_K1 * x * x));
 }
 
 /* ------------------------------------------------------------------------- */

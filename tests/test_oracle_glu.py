@@ -102,6 +102,17 @@ def test_act_special_values():
 
 
 @pytest.mark.parametrize("kind", GELU_LIKE)
+def test_act_and_grad_negative_in_the_tail(kind):
+    """For x below the minimum of act (x0 ~ -1.28 SiLU, ~ -0.75 GELUs) act(x) < 0 and
+    act'(x) < 0 exactly, so a result that underflows must be -0, not +0 (an E4M3 code keeps
+    the sign of zero)."""
+    xs = [-5.0, -40.0, -200.0, -1000.0, -1e30]
+    assert np.all(np.signbit(oracle.act(kind, xs)))
+    assert np.all(np.signbit(oracle.act_grad(kind, xs)))
+    assert np.isnan(oracle.act_grad(kind, [-np.inf])[0])
+
+
+@pytest.mark.parametrize("kind", GELU_LIKE)
 def test_act_reflection(kind):
     """silu(-x) = silu(x) - x, and the same for both GELUs (sigma(-z) = 1 - sigma(z),
     Phi(-x) = 1 - Phi(x))."""

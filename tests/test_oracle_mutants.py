@@ -26,8 +26,13 @@ MUTANTS = [
      [lambda: tg.test_act_grad_against_mpmath(S)]),
     ("gelu' drops the 3", "3.0 * GELU_K1", "GELU_K1",
      [lambda: tg.test_act_grad_against_mpmath(G)]),
-    ("gelu' drops a factor", "0.5 * x * (one_plus_t * one_minus_t)", "0.5 * x * (one_plus_t)",
+    ("gelu' drops a factor", "(1.0 + x * one_minus_t * GELU_K0", "(1.0 + x * GELU_K0",
      [lambda: tg.test_act_grad_against_autograd(G)]),
+    ("gelu' as a sum of terms", "return 0.5 * one_plus_t *\n         (1.0 + x * one_minus_t",
+     "return 0.5 * one_plus_t + 0.5 * one_plus_t *\n         (x * one_minus_t",
+     [lambda: tg.test_act_and_grad_negative_in_the_tail(G)]),
+    ("erf-GELU' loses the sign of zero", "(d == 0.0 && x < 0.0 && isfinite(x)) ? -0.0 : d", "d",
+     [lambda: tg.test_act_and_grad_negative_in_the_tail(E)]),
     ("erf-GELU CDF sign", "0.5 * erfc(-x * SQRT1_2)", "0.5 * erfc(x * SQRT1_2)",
      [lambda: tg.test_act_against_mpmath(E)]),
     ("erf-GELU' drops x", "normal_cdf(x) + x * normal_pdf(x)", "normal_cdf(x) + normal_pdf(x)",
