@@ -13,7 +13,8 @@ Also reported on the same JSON line:
                   its duration measured with HIP events on the launch stream;
   cpu_baseline  - the CPU oracle on a bounded row sample of the same workload;
   sweep         - every workload shape of the pages (MXFP8 SwiGLU fwd/bwd per direction,
-                  GeGLU BF16 fwd/bwd, GeGLU NVFP4), median of cold launches.
+                  GeGLU BF16 fwd/bwd, GeGLU NVFP4), median of cold launches, plus the
+                  other activations (tanh-GeGLU, erf-GeGLU, ReLU^2) at one shape of each.
 Only one GPU is supported; --gpus above 1 exits with a message.
 """
 import argparse
@@ -123,30 +124,32 @@ def sweep(torch, glu, si, iters):
     dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     rec("device_copy_1GiB", 2 << 30, time_launches(torch, [lambda x=x: dst.copy_(x) for x in src], iters))
     del src, dst
-    # MXFP8 SwiGLU shapes
+    # MXFP8 SwiGLU shapes, and the other activations at [16384, 7168]
+    others = [(d, "both", a) for a in ("geglu", "geglu_erf", "relu2") for d in ("fwd", "bwd")]
     for M, N, outl, cases in [
         (128, 128, False, [("fwd", "row")]),
         (4096, 2048, False, [("fwd", "both"), ("bwd", "both")]),
         (16384, 7168, True, [("fwd", "row"), ("fwd", "col"), ("fwd", "both"),
                              ("bwd", "row"), ("bwd", "col"), ("bwd", "both"),
-                             ("fwd", "both_swizzled"), ("bwd", "both_swizzled")]),
+                             ("fwd", "both_swizzled"), ("bwd", "both_swizzled"), *others]),
         (131072, 8192, True, [("fwd", "row")]),
     ]:
         per = 6 * M * N
         sets = [si.normal_bf16_device([(M, N)] * 3, seed=100 + s, outliers=outl) for s in range(n_sets(per))]
-        for d, mode in cases:
+        for d, mode, *act in cases:
+            act = act[0] if act else "swiglu"
             swz = mode.endswith("_swizzled")  # scales in the 128x4 layout
             dirs = mode.removesuffix("_swizzled")
             row, col = dirs in ("row", "both"), dirs in ("col", "both")
             bwd = d == "bwd"
             out = glu._mx_buffers(M, 2 * N if bwd else N, row, col, "cuda", None, swz)
-            kw = dict(rowwise=row, colwise=col, swizzled=swz, out=out)
+            kw = dict(act=act, rowwise=row, colwise=col, swizzled=swz, out=out)
             if bwd:
                 fns = [lambda s=s: glu.glu_bwd_mxfp8(s[0], s[1], s[2], **kw) for s in sets]
             else:
                 fns = [lambda s=s: glu.glu_fwd_mxfp8(s[0], s[1], **kw) for s in sets]
             t = time_launches(torch, fns, iters)
-            rec(f"swiglu_mxfp8_{d}_{mode}_{M}x{N}", mx_bytes(M, N, bwd, 2 if dirs == "both" else 1), t)
+            rec(f"{act}_mxfp8_{d}_{mode}_{M}x{N}", mx_bytes(M, N, bwd, 2 if dirs == "both" else 1), t)
             del out, fns
         del sets
         torch.cuda.empty_cache()
@@ -163,6 +166,19 @@ def sweep(torch, glu, si, iters):
             rec(f"geglu_bf16_bwd_{R}x{W}", bf16_bytes(R, W, True), t)
             del sets, h, da, db
         torch.cuda.empty_cache()
+    # the other activations, BF16 at [8192, 14336]
+    R, W = 8192, 14336
+    sets = [si.normal_bf16_device([(R, W)] * 3, seed=R + W + s) for s in range(n_sets(6 * R * W))]
+    h = torch.empty(R, W, dtype=torch.bfloat16, device="cuda")
+    da, db = torch.empty_like(h), torch.empty_like(h)
+    for act in ("swiglu", "geglu_erf", "relu2"):
+        t = time_launches(torch, [lambda s=s: glu.glu_fwd(s[0], s[1], act=act, out=h) for s in sets], iters)
+        rec(f"{act}_bf16_fwd_{R}x{W}", bf16_bytes(R, W, False), t)
+        t = time_launches(torch, [lambda s=s: glu.glu_bwd(s[0], s[1], s[2], act=act, out=(da, db))
+                                  for s in sets], iters)
+        rec(f"{act}_bf16_bwd_{R}x{W}", bf16_bytes(R, W, True), t)
+    del sets, h, da, db
+    torch.cuda.empty_cache()
     # GeGLU NVFP4
     H = 16384
     for M in (784, 816, 880, 968):
@@ -171,6 +187,11 @@ def sweep(torch, glu, si, iters):
         t = time_launches(torch, [lambda x=x: glu.glu_fwd_nvfp4(x, act="geglu", layout="paired",
                                                                  sf_layout="128x4", out=out) for x in sets], iters)
         rec(f"geglu_nvfp4_fwd_{M}x{H}", nv_bytes(M, H), t)
+        if M == 968:   # the other activations at the largest shape
+            for act in ("swiglu", "geglu_erf", "relu2"):
+                t = time_launches(torch, [lambda x=x: glu.glu_fwd_nvfp4(x, act=act, layout="paired",
+                                                                         sf_layout="128x4", out=out) for x in sets], iters)
+                rec(f"{act}_nvfp4_fwd_{M}x{H}", nv_bytes(M, H), t)
         del sets, out
     return res
 

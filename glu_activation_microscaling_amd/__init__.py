@@ -24,7 +24,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libglu_mx.so")
 
-ACT = {"swiglu": 0, "geglu": 1, "geglu_tanh": 1}
+ACT = {"swiglu": 0, "geglu": 1, "geglu_tanh": 1, "geglu_erf": 2, "relu2": 3}
 LAYOUT = {"split": 0, "paired": 1}
 SF_LAYOUT = {"rowmajor": 0, "128x4": 1}
 ROWWISE, COLWISE, SF_SWIZZLED = 1, 2, 4

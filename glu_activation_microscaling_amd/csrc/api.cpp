@@ -82,7 +82,7 @@ bool overlaps(const Operand& A, const Operand& B) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-bool valid_act(int act) { return act == glu::SWIGLU || act == glu::GEGLU_TANH; }
+bool valid_act(int act) { return act >= glu::SWIGLU && act <= glu::RELU2; }
 bool valid_layout(int l) { return l == glu::SPLIT || l == glu::PAIRED; }
 // MXFP8 flags: one or both directions, optionally the 128x4 scale layout.
 bool valid_flags(int f) {

@@ -106,22 +106,24 @@ __global__ __launch_bounds__(BF_THREADS) void k_glu_fwd_bf16(BF16Args a, int64_t
     for (int v = 0; v < BF_VEC; v++) {
       const int64_t j = j0 + ((int64_t)v * BF_THREADS + threadIdx.x) * 8;
       if (j + 8 <= cols) {
-        float h[8], zmin = 0.0f;
+        float h[8];
+        bool tail = false;
 #pragma unroll
-        for (int k = 0; k < 8; k++) h[k] = glu_fwd_elem<ACT>(g[v][k], u[v][k], zmin);
-        if (zmin < TAIL_ZL2) {
+        for (int k = 0; k < 8; k++) h[k] = glu_fwd_elem<ACT>(g[v][k], u[v][k], tail);
+        if (tail) {
 #pragma unroll
           for (int k = 0; k < 8; k++)
-            if (zl2<ACT>(g[v][k]) < TAIL_ZL2) h[k] = glu_fwd_tail<ACT>(g[v][k], u[v][k]);
+            if (fwd_tail_needed<ACT>(g[v][k], u[v][k])) h[k] = glu_fwd_tail<ACT>(g[v][k], u[v][k]);
         }
         st16(hrow + j, pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]),
              pack_bf16(h[6], h[7]));
       } else if (j < cols) {
         for (int64_t jj = j; jj < cols; jj++) {
-          float gg, uu, zmin = 0.0f;
+          float gg, uu;
+          bool tail = false;
           load1<LAYOUT>(grow, urow, jj, gg, uu);
-          float h = glu_fwd_elem<ACT>(gg, uu, zmin);
-          if (zmin < TAIL_ZL2) h = glu_fwd_tail<ACT>(gg, uu);
+          float h = glu_fwd_elem<ACT>(gg, uu, tail);
+          if (tail) h = glu_fwd_tail<ACT>(gg, uu);
           hrow[jj] = (uint16_t)bf16_rne(h);
         }
       }
@@ -160,13 +162,15 @@ __global__ __launch_bounds__(BF_THREADS) void k_glu_bwd_bf16(BF16Args a, int64_t
     for (int v = 0; v < BF_VEC; v++) {
       const int64_t j = j0 + ((int64_t)v * BF_THREADS + threadIdx.x) * 8;
       if (j + 8 <= cols) {
-        float da[8], db[8], zmin = 0.0f;
+        float da[8], db[8];
+        bool tail = false;
 #pragma unroll
-        for (int k = 0; k < 8; k++) glu_bwd_elem<ACT>(g[v][k], u[v][k], d[v][k], da[k], db[k], zmin);
-        if (zmin < TAIL_ZL2) {
+        for (int k = 0; k < 8; k++) glu_bwd_elem<ACT>(g[v][k], u[v][k], d[v][k], da[k], db[k], tail);
+        if (tail) {
 #pragma unroll
           for (int k = 0; k < 8; k++)
-            if (zl2<ACT>(g[v][k]) < TAIL_ZL2) glu_bwd_tail<ACT>(g[v][k], u[v][k], d[v][k], da[k], db[k]);
+            if (bwd_tail_needed<ACT>(g[v][k], u[v][k], d[v][k]))
+              glu_bwd_tail<ACT>(g[v][k], u[v][k], d[v][k], da[k], db[k]);
         }
         if constexpr (LAYOUT == SPLIT) {
           st16(arow + j, pack_bf16(da[0], da[1]), pack_bf16(da[2], da[3]), pack_bf16(da[4], da[5]),
@@ -181,11 +185,12 @@ __global__ __launch_bounds__(BF_THREADS) void k_glu_bwd_bf16(BF16Args a, int64_t
         }
       } else if (j < cols) {
         for (int64_t jj = j; jj < cols; jj++) {
-          float gg, uu, zmin = 0.0f, da, db;
+          float gg, uu, da, db;
+          bool tail = false;
           load1<LAYOUT>(grow, urow, jj, gg, uu);
           float dd = ld_bf(drow + jj);
-          glu_bwd_elem<ACT>(gg, uu, dd, da, db, zmin);
-          if (zmin < TAIL_ZL2) glu_bwd_tail<ACT>(gg, uu, dd, da, db);
+          glu_bwd_elem<ACT>(gg, uu, dd, da, db, tail);
+          if (tail) glu_bwd_tail<ACT>(gg, uu, dd, da, db);
           if constexpr (LAYOUT == SPLIT) {
             arow[jj] = (uint16_t)bf16_rne(da);
             brow[jj] = (uint16_t)bf16_rne(db);
@@ -214,10 +219,10 @@ hipError_t launch(const BF16Args& a, hipStream_t s) {
 
 template <bool BWD>
 hipError_t dispatch(const BF16Args& a, hipStream_t s) {
-  if (a.act == SWIGLU)
-    return a.layout == SPLIT ? launch<BWD, SWIGLU, SPLIT>(a, s) : launch<BWD, SWIGLU, PAIRED>(a, s);
-  return a.layout == SPLIT ? launch<BWD, GEGLU_TANH, SPLIT>(a, s)
-                           : launch<BWD, GEGLU_TANH, PAIRED>(a, s);
+  return with_act(a.act, [&](auto A) {
+    constexpr int ACT = decltype(A)::value;
+    return a.layout == SPLIT ? launch<BWD, ACT, SPLIT>(a, s) : launch<BWD, ACT, PAIRED>(a, s);
+  });
 }
 
 }  // namespace

@@ -39,11 +39,18 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 __device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(bf16_rne(f) << 16); }
 
 // ---------------------------------------------------------------------------------
-// Activations.  act(x) = x * sigma(z(x)) with z = x (SiLU) or z = 2 k0 (x + k1 x^3)
-// (tanh-GELU: x/2 (1 + tanh(u)) = x sigma(2u)).  act'(x) = sigma(z) (1 + x sigma(-z) z'(x)).
-// The fast path uses the hardware exp2 and reciprocal and is accurate while
-// z * log2(e) >= TAIL_ZL2; below that e^z leaves the FP32 normal range and the caller
-// recomputes the element on the tail path, which is rare and wave-divergent.
+// Activations, act(g) applied to the gate and multiplied by up:
+//   SWIGLU       silu(x) = x sigma(x);
+//   GEGLU_TANH   x/2 (1 + tanh(u)), u = k0 (x + k1 x^3), written as x sigma(2u);
+//   GEGLU_ERF    x Phi(x), Phi the standard normal CDF (the exact GELU);
+//   RELU2        max(x, 0)^2.
+// For the first two act(x) = x sigma(z(x)) and act'(x) = sigma(z) (1 + x sigma(-z) z'(x)).
+// Each activation has a fast FP32 path and a rare FP64 tail path for the elements where the
+// fast path could lose accuracy; fwd_tail_needed / bwd_tail_needed say which, and the kernels
+// recompute those elements (wave-divergent, rare for real data):
+//   sigmoid forms: z log2(e) < -125, where e^z leaves the FP32 normal range;
+//   erf-GELU:      x < -12.5, where Phi(x) nears the bottom of the FP32 normal range;
+//   ReLU^2:        an intermediate product that is not an FP32 normal number (see relu).
 // ---------------------------------------------------------------------------------
 
 constexpr float LOG2E = 1.44269504088896340736f;
@@ -54,8 +61,11 @@ constexpr float GEGLU_C1 = (float)(2.0 * GELU_K0 * GELU_K1 * 1.44269504088896340
 constexpr float GEGLU_D0 = (float)(2.0 * GELU_K0);                                     // z'(x) = D0 + D1 x^2
 constexpr float GEGLU_D1 = (float)(6.0 * GELU_K0 * GELU_K1);
 constexpr float TAIL_ZL2 = -125.0f;
+constexpr double SQRT1_2 = 0.70710678118654752440;       // 1/sqrt(2)
+constexpr double INV_SQRT_2PI = 0.39894228040143267794;  // 1/sqrt(2 pi)
+constexpr float ERF_TAIL_X = -12.5f;
 
-// z(x) * log2(e)
+// z(x) * log2(e) of the sigmoid forms
 template <int ACT>
 __device__ __forceinline__ float zl2(float x) {
   if constexpr (ACT == SWIGLU) {
@@ -63,6 +73,21 @@ __device__ __forceinline__ float zl2(float x) {
   } else {
     return x * __builtin_fmaf(x * x, GEGLU_C1, GEGLU_C0);
   }
+}
+
+// Wave-level trigger of the tail path from raw BF16 gate bit patterns: m16 is their maximum
+// as unsigned 16-bit numbers, under which negative values order by magnitude above 0x8000
+// and non-negative ones stay below.  True when some gate value is below G, where every
+// g >= G takes the fast path: SwiGLU G = -80 (zl2 >= -115.5), tanh-GeGLU G = -9.5
+// (zl2 >= -110.2), erf-GeGLU G = -12.5 (the bound itself).  Negative NaNs trigger it too
+// (harmless: both paths return NaN).
+// ReLU^2's tail depends on all operands, so it has no trigger of this kind.
+template <int ACT>
+constexpr bool tail_from_gate_bits() { return ACT != RELU2; }
+template <int ACT>
+__device__ __forceinline__ bool tail_possible(uint32_t m16) {
+  static_assert(tail_from_gate_bits<ACT>());
+  return m16 > (ACT == SWIGLU ? 0xC2A0u : ACT == GEGLU_TANH ? 0xC118u : 0xC148u);  // -80, -9.5, -12.5
 }
 
 // e^-z = 2^-zl and sigma(z) = 1 / (1 + e^-z) from zl = z log2(e); accurate for
@@ -82,69 +107,212 @@ __device__ __forceinline__ float dz(float x) {
   }
 }
 
-// Tail path, z log2(e) = zl < TAIL_ZL2: e^z = 2^zl is below the FP32 normal range, so it
-// is formed in FP64 as exp2(f) * 2^n with n = floor(zl), f = zl - n (exact), and the
-// products are taken in FP64 (no intermediate overflow or underflow).  There 1 + e^z == 1,
-// so sigma(z) = e^z and sigma(-z) = 1.  zl is clamped where e^z is 0 in FP64 anyway.
+// Tail path of the sigmoid forms, z log2(e) = zl < TAIL_ZL2: e^z = 2^zl is below the FP32
+// normal range, so it is formed in FP64 as exp2(f) * 2^n with n = floor(zl), f = zl - n
+// (exact), and the products are taken in FP64 (no intermediate overflow or underflow).
+// There 1 + e^z == 1, so sigma(z) = e^z and sigma(-z) = 1.  zl is clamped where e^z is 0
+// in FP64 anyway.
 __device__ __forceinline__ double exp2_tail(float zl) {
   const float zc = __builtin_fmaxf(zl, -1100.0f);
   const float n = __builtin_floorf(zc);
   return __builtin_ldexp((double)__builtin_amdgcn_exp2f(zc - n), (int)n);
 }
 
-// Forward: act(g) * u in FP32 (the caller rounds it to BF16).  Accurate for
-// zl2(g) >= TAIL_ZL2; zmin tracks the smallest zl2 so the caller can switch to the tail.
+// erf-GELU.  Phi(x) = erfc(-x / sqrt 2) / 2 and phi(x) = exp(-x^2 / 2) / sqrt(2 pi);
+// act'(x) = Phi(x) + x phi(x).
+//
+// FP32 fast path (x >= -12.5; below that the FP64 tail): with z = |x| / sqrt 2,
+//   erfc(z) = t e^(-z^2 + Q(t)),  t = 1 / (1 + z/2),
+// Q a degree-9 polynomial fitted to ln(erfc(z)/t) + z^2 for |x| <= 12.75 (max error
+// 4.3e-8; gen_erfc_poly.py prints the coefficients), and Phi = erfc(z)/2 for x < 0,
+// 1 - erfc(z)/2 otherwise.  x is clamped to +-12.75: beyond it Phi is 1 in FP32 (x > 0) or
+// the tail path applies (x < 0).  z^2 = x^2 / 2 is exact for a BF16 x, and e^(-z^2 + q) is
+// formed as 2^n 2^f with the product z^2 log2(e) carried to about 40 bits (log2 e split so
+// that its 8-bit head times the 16-bit z^2 is exact), so the large exponent costs no
+// accuracy.
+constexpr float ERFC_Q[10] = {
+    -1.265415668e+00f, 9.979900122e-01f, 3.920583725e-01f, 9.132201783e-03f,
+    7.507857680e-02f,  -2.174440175e-01f, -5.322819948e-01f, 1.034772754e+00f,
+    -6.294651031e-01f, 1.355749071e-01f};
+constexpr float ERF_X_CLAMP = 12.75f;
+constexpr float LOG2E_HI = 1.4453125f;  // log2(e) to 8 significant bits (0x3FB90000)
+constexpr float LOG2E_LO = (float)(1.44269504088896340736 - 1.4453125);
+
+// e^(-w + q) for 0 <= w <= 82 with at most 16 significant bits, |q| <= 2.
+__device__ __forceinline__ float exp_neg_w_plus(float w, float q) {
+  const float yh = -w * LOG2E_HI;  // exact
+  const float n = __builtin_rintf(yh);
+  const float f = __builtin_fmaf(-w, LOG2E_LO, __builtin_fmaf(q, LOG2E, yh - n));
+  return __builtin_ldexpf(__builtin_amdgcn_exp2f(f), (int)n);
+}
+
+struct ErfParts {
+  float xc, w, t, q;  // clamped x, z^2 = xc^2 / 2, t, Q(t)
+};
+__device__ __forceinline__ ErfParts erf_parts(float x) {
+  ErfParts p;
+  p.xc = __builtin_amdgcn_fmed3f(x, -ERF_X_CLAMP, ERF_X_CLAMP);
+  p.w = (0.5f * p.xc) * p.xc;
+  p.t = __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_fabsf(p.xc), (float)(0.5 * SQRT1_2), 1.0f));
+  float q = ERFC_Q[9];
+#pragma unroll
+  for (int i = 8; i >= 0; i--) q = __builtin_fmaf(q, p.t, ERFC_Q[i]);
+  p.q = q;
+  return p;
+}
+// Phi from erfc(|x| / sqrt 2)
+__device__ __forceinline__ float phi_from_erfc(float xc, float e) {
+  return xc < 0.0f ? 0.5f * e : __builtin_fmaf(-0.5f, e, 1.0f);
+}
+__device__ __forceinline__ float phi_cdf(float x) {
+  const ErfParts p = erf_parts(x);
+  return phi_from_erfc(p.xc, p.t * exp_neg_w_plus(p.w, p.q));
+}
+// Phi(x) and phi(x) together, sharing e^(-z^2); phi is 0 beyond the clamp (so that x phi(x)
+// is 0 for large finite x and NaN for infinite x, as in x e^(-x^2/2)).
+__device__ __forceinline__ void phi_cdf_pdf(float x, float& cdf, float& pdf) {
+  const ErfParts p = erf_parts(x);
+  const float ew = exp_neg_w_plus(p.w, 0.0f);
+  cdf = phi_from_erfc(p.xc, (p.t * __builtin_amdgcn_exp2f(p.q * LOG2E)) * ew);
+  pdf = __builtin_fabsf(x) <= ERF_X_CLAMP ? (float)INV_SQRT_2PI * ew : 0.0f;
+}
+
+// FP64 tail, x < -12.5 (z = |x|/sqrt 2 > 8.8): Phi(x) = phi(x) S(v) / |x| with the asymptotic
+// series of the Mills ratio, S = 1 - v + 3v^2 - 15v^3 + 105v^4 - 945v^5 + 10395v^6,
+// v = 1/x^2 (truncation error below 1e-10 relative at x = -12.5, smaller beyond).  FP64 is
+// there for the range (phi(x) leaves FP32 near x = -13.5); e^(-x^2/2) = 2^y is formed as
+// exp2(f) 2^n with n = floor(y), f = y - n, and is 0 where it is below the FP64 range.
+__device__ __forceinline__ void phi_tail64(float x, double& cdf, double& grad) {
+  const double xd = (double)x;
+  const double r = 1.0 / __builtin_fabs(xd), v = r * r;
+  double pdf, sv = 10395.0;
+  sv = __builtin_fma(sv, v, -945.0);
+  sv = __builtin_fma(sv, v, 105.0);
+  sv = __builtin_fma(sv, v, -15.0);
+  sv = __builtin_fma(sv, v, 3.0);
+  sv = __builtin_fma(sv, v, -1.0);
+  sv = __builtin_fma(sv, v, 1.0);
+  const double y = __builtin_fmax(-0.5 * xd * xd * 1.44269504088896340736, -1100.0);
+  const double n = __builtin_floor(y);
+  pdf = INV_SQRT_2PI * __builtin_ldexp((double)__builtin_amdgcn_exp2f((float)(y - n)), (int)n);
+  cdf = (pdf * sv) * r;
+  grad = pdf * (sv * r + xd);  // Phi + x phi, negative (or -0 where phi underflows)
+}
+
+// ReLU^2.  r = max(x, 0) with NaN kept NaN.  A product of two BF16 values has at most 16
+// significant bits and one of three at most 24, so in FP32 each is exact while it is a
+// normal number, and the last product is the correctly rounded exact value whatever its
+// range.  The fast path forms h = (r r) u, db = (dh r) r, da = ((dh + dh) u) r; an element
+// whose first product (r r, dh r or (dh + dh) u) is not a normal FP32 number (over- or
+// underflow, a zero that is not exact, or NaN) goes to the FP64 tail, where every product is
+// exact.
+__device__ __forceinline__ float relu(float x) { return x <= 0.0f ? 0.0f : x; }
+__device__ __forceinline__ bool fp32_normal(float x) {
+  return __builtin_amdgcn_classf(x, 0x108);  // -normal | +normal
+}
+
 template <int ACT>
-__device__ __forceinline__ float glu_fwd_fast(float g, float u) {
-  return (g * sigmoid_from(exp_neg(zl2<ACT>(g)))) * u;
+__device__ __forceinline__ bool fwd_tail_needed(float g, float u) {
+  if constexpr (ACT == RELU2) {
+    const float r = relu(g);
+    return r != 0.0f && !fp32_normal(r * r);
+  } else if constexpr (ACT == GEGLU_ERF) {
+    return g < ERF_TAIL_X;
+  } else {
+    return zl2<ACT>(g) < TAIL_ZL2;
+  }
 }
 template <int ACT>
-__device__ __forceinline__ float glu_fwd_elem(float g, float u, float& zmin) {
-  zmin = __builtin_fminf(zmin, zl2<ACT>(g));
+__device__ __forceinline__ bool bwd_tail_needed(float g, float u, float d) {
+  if constexpr (ACT == RELU2) {
+    const float r = relu(g);
+    return !fp32_normal((d + d) * u) || (r != 0.0f && !fp32_normal(d * r));
+  } else {
+    return fwd_tail_needed<ACT>(g, u);
+  }
+}
+
+// Forward: act(g) * u in FP32 (the caller rounds it to BF16); the tail elements are
+// recomputed by glu_fwd_tail.
+template <int ACT>
+__device__ __forceinline__ float glu_fwd_fast(float g, float u) {
+  if constexpr (ACT == GEGLU_ERF) {
+    return (g * phi_cdf(g)) * u;
+  } else if constexpr (ACT == RELU2) {
+    const float r = relu(g);
+    return (r * r) * u;
+  } else {
+    return (g * sigmoid_from(exp_neg(zl2<ACT>(g)))) * u;
+  }
+}
+template <int ACT>
+__device__ __forceinline__ float glu_fwd_elem(float g, float u, bool& tail) {
+  tail |= fwd_tail_needed<ACT>(g, u);
   return glu_fwd_fast<ACT>(g, u);
 }
 
 template <int ACT>
 __device__ __forceinline__ float glu_fwd_tail(float g, float u) {
-  return (float)((double)g * exp2_tail(zl2<ACT>(g)) * (double)u);
+  if constexpr (ACT == GEGLU_ERF) {
+    double cdf, grad;
+    phi_tail64(g, cdf, grad);
+    return (float)((double)g * cdf * (double)u);
+  } else if constexpr (ACT == RELU2) {
+    const double r = (double)relu(g);
+    return (float)((r * r) * (double)u);
+  } else {
+    return (float)((double)g * exp2_tail(zl2<ACT>(g)) * (double)u);
+  }
 }
 
-// Backward: da = dh u act'(g), db = dh act(g), FP32 before rounding, as
-// q = dh sigma(z), db = q g, da = (q u)(1 + (g sigma(-z)) z'(g)).  g sigma(-z) is taken
+// Backward: da = dh u act'(g), db = dh act(g), FP32 before rounding.  Sigmoid forms:
+// q = dh sigma(z), db = q g, da = (q u)(1 + (g sigma(-z)) z'(g)); g sigma(-z) is taken
 // before z'(g): for large g, z'(g) g overflows while sigma(-z) is 0.
 template <int ACT>
 __device__ __forceinline__ void glu_bwd_fast(float g, float u, float d, float& da, float& db) {
-  const float e = exp_neg(zl2<ACT>(g));
-  const float sp = sigmoid_from(e);  // sigma(z)
-  const float q = d * sp;
-  db = q * g;
-  const float sn = e * sp;           // sigma(-z)
-  const float s = ACT == SWIGLU ? __builtin_fmaf(g, sn, 1.0f) : __builtin_fmaf(g * sn, dz<ACT>(g), 1.0f);
-  da = (q * u) * s;
+  if constexpr (ACT == GEGLU_ERF) {
+    float p, pd;
+    phi_cdf_pdf(g, p, pd);
+    db = d * (g * p);
+    da = (d * u) * __builtin_fmaf(g, pd, p);
+  } else if constexpr (ACT == RELU2) {
+    const float r = relu(g);
+    db = (d * r) * r;
+    da = ((d + d) * u) * r;
+  } else {
+    const float e = exp_neg(zl2<ACT>(g));
+    const float sp = sigmoid_from(e);  // sigma(z)
+    const float q = d * sp;
+    db = q * g;
+    const float sn = e * sp;           // sigma(-z)
+    const float s = ACT == SWIGLU ? __builtin_fmaf(g, sn, 1.0f) : __builtin_fmaf(g * sn, dz<ACT>(g), 1.0f);
+    da = (q * u) * s;
+  }
 }
 template <int ACT>
 __device__ __forceinline__ void glu_bwd_elem(float g, float u, float d, float& da, float& db,
-                                             float& zmin) {
-  zmin = __builtin_fminf(zmin, zl2<ACT>(g));
+                                             bool& tail) {
+  tail |= bwd_tail_needed<ACT>(g, u, d);
   glu_bwd_fast<ACT>(g, u, d, da, db);
-}
-
-// Wave-level trigger of the tail path from raw BF16 gate bit patterns: m16 is their maximum
-// as unsigned 16-bit numbers, under which negative values order by magnitude above 0x8000
-// and non-negative ones stay below.  True when some gate value is below G with
-// zl2(g) >= TAIL_ZL2 for every g >= G: SwiGLU G = -80 (zl2 >= -115.5), GeGLU G = -9.5
-// (zl2 >= -110.2).  Negative NaNs trigger it too (harmless: both paths return NaN).
-template <int ACT>
-__device__ __forceinline__ bool tail_possible(uint32_t m16) {
-  return m16 > (ACT == SWIGLU ? 0xC2A0u : 0xC118u);  // BF16 -80, -9.5
 }
 
 template <int ACT>
 __device__ __forceinline__ void glu_bwd_tail(float g, float u, float d, float& da, float& db) {
-  const double t = exp2_tail(zl2<ACT>(g));
   const double gd = (double)g;
-  da = (float)((double)d * (double)u * t * (1.0 + gd * (double)dz<ACT>(g)));
-  db = (float)((double)d * gd * t);
+  if constexpr (ACT == GEGLU_ERF) {
+    double cdf, grad;
+    phi_tail64(g, cdf, grad);
+    db = (float)((double)d * (gd * cdf));
+    da = (float)((double)d * (double)u * grad);
+  } else if constexpr (ACT == RELU2) {
+    const double r = (double)relu(g), dd = (double)d;
+    db = (float)(dd * (r * r));
+    da = (float)((dd * (double)u) * (2.0 * r));
+  } else {
+    const double t = exp2_tail(zl2<ACT>(g));
+    da = (float)((double)d * (double)u * t * (1.0 + gd * (double)dz<ACT>(g)));
+    db = (float)((double)d * gd * t);
+  }
 }
 
 // ---------------------------------------------------------------------------------

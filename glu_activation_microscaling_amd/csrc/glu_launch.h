@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <tuple>
+#include <type_traits>
 
 #include "glu_common.h"
 
@@ -76,6 +77,18 @@ template <typename... KArgs, typename... Ts>
 hipError_t launch_kernel(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
                          Ts&&... ts) {
   return launch_kernel_shm(k, grid, block, 0, s, static_cast<Ts&&>(ts)...);
+}
+
+// Calls f(std::integral_constant<int, ACT>) for the run-time activation code (validated by
+// the caller), so a launcher names each template instance once for every activation.
+template <typename F>
+hipError_t with_act(int act, F&& f) {
+  switch (act) {
+    case SWIGLU: return f(std::integral_constant<int, SWIGLU>{});
+    case GEGLU_TANH: return f(std::integral_constant<int, GEGLU_TANH>{});
+    case GEGLU_ERF: return f(std::integral_constant<int, GEGLU_ERF>{});
+    default: return f(std::integral_constant<int, RELU2>{});
+  }
 }
 
 // Workgroups of a grid-stride launch over `units` work items: enough waves to fill the

@@ -317,23 +317,28 @@ __device__ __forceinline__ void compute(TileVals<MODE>& r, const TileOps<LAYOUT,
 #pragma unroll
       for (int c = 0; c < 8; c++) r.v[i][c] = __uint_as_float(o.x[i][c]);
   } else if constexpr (MODE == MODE_FWD) {
-    const bool tail = tail_possible<ACT>(gate_max16<LAYOUT>(o.in));
+    bool tail = false;
+    if constexpr (tail_from_gate_bits<ACT>()) tail = tail_possible<ACT>(gate_max16<LAYOUT>(o.in));
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       float gg[8], u[8], h[8];
       unpack_gu<LAYOUT>(o.in[i], gg, u);
 #pragma unroll
-      for (int c = 0; c < 8; c++) h[c] = glu_fwd_fast<ACT>(gg[c], u[c]);
-      if (tail) {  // rare: some e^z may be below the FP32 normal range
+      for (int c = 0; c < 8; c++) {
+        h[c] = glu_fwd_fast<ACT>(gg[c], u[c]);
+        if constexpr (!tail_from_gate_bits<ACT>()) tail |= fwd_tail_needed<ACT>(gg[c], u[c]);
+      }
+      if (tail) {  // rare: some element may need the FP64 tail path
 #pragma unroll
         for (int c = 0; c < 8; c++)
-          if (zl2<ACT>(gg[c]) < TAIL_ZL2) h[c] = glu_fwd_tail<ACT>(gg[c], u[c]);
+          if (fwd_tail_needed<ACT>(gg[c], u[c])) h[c] = glu_fwd_tail<ACT>(gg[c], u[c]);
       }
 #pragma unroll
       for (int k = 0; k < 4; k++) r.h[0][i][k] = pack_bf16(h[2 * k], h[2 * k + 1]);
     }
   } else {
-    const bool tail = tail_possible<ACT>(gate_max16<SPLIT>(o.in));
+    bool tail = false;
+    if constexpr (tail_from_gate_bits<ACT>()) tail = tail_possible<ACT>(gate_max16<SPLIT>(o.in));
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       float gg[8], u[8], d[8], da[8], db[8];
@@ -342,11 +347,12 @@ __device__ __forceinline__ void compute(TileVals<MODE>& r, const TileOps<LAYOUT,
       for (int c = 0; c < 8; c++) {
         d[c] = (c & 1) ? bf_hi(o.d[i][c >> 1]) : bf_lo(o.d[i][c >> 1]);
         glu_bwd_fast<ACT>(gg[c], u[c], d[c], da[c], db[c]);
+        if constexpr (!tail_from_gate_bits<ACT>()) tail |= bwd_tail_needed<ACT>(gg[c], u[c], d[c]);
       }
-      if (tail) {  // rare: some e^z may be below the FP32 normal range
+      if (tail) {  // rare: some element may need the FP64 tail path
 #pragma unroll
         for (int c = 0; c < 8; c++)
-          if (zl2<ACT>(gg[c]) < TAIL_ZL2) glu_bwd_tail<ACT>(gg[c], u[c], d[c], da[c], db[c]);
+          if (bwd_tail_needed<ACT>(gg[c], u[c], d[c])) glu_bwd_tail<ACT>(gg[c], u[c], d[c], da[c], db[c]);
       }
 #pragma unroll
       for (int k = 0; k < 4; k++) {
@@ -882,16 +888,17 @@ hipError_t by_flags(const MxArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_glu_fwd_mxfp8(const MxArgs& a, hipStream_t s) {
-  if (a.act == SWIGLU)
-    return a.layout == SPLIT ? by_flags<SWIGLU, SPLIT, MODE_FWD>(a, s)
-                             : by_flags<SWIGLU, PAIRED, MODE_FWD>(a, s);
-  return a.layout == SPLIT ? by_flags<GEGLU_TANH, SPLIT, MODE_FWD>(a, s)
-                           : by_flags<GEGLU_TANH, PAIRED, MODE_FWD>(a, s);
+  return with_act(a.act, [&](auto A) {
+    constexpr int ACT = decltype(A)::value;
+    return a.layout == SPLIT ? by_flags<ACT, SPLIT, MODE_FWD>(a, s) : by_flags<ACT, PAIRED, MODE_FWD>(a, s);
+  });
 }
 
 hipError_t launch_glu_bwd_mxfp8(const MxArgs& a, hipStream_t s) {
-  return a.act == SWIGLU ? by_flags<SWIGLU, SPLIT, MODE_BWD>(a, s)
-                         : by_flags<GEGLU_TANH, SPLIT, MODE_BWD>(a, s);
+  return with_act(a.act, [&](auto A) {
+    constexpr int ACT = decltype(A)::value;
+    return by_flags<ACT, SPLIT, MODE_BWD>(a, s);
+  });
 }
 
 hipError_t launch_quant_mxfp8_f32(const MxArgs& a, hipStream_t s) {

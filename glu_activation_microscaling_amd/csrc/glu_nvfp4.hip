@@ -96,13 +96,13 @@ __device__ __forceinline__ void values(const Raw8& r, float v[8]) {
         u[2 * k + 1] = bf_hi(r.B.w[k]);
       }
     }
-    float zmin = 0.0f;
+    bool tail = false;
 #pragma unroll
-    for (int k = 0; k < 8; k++) v[k] = glu_fwd_elem<ACT>(g[k], u[k], zmin);
-    if (zmin < TAIL_ZL2) {
+    for (int k = 0; k < 8; k++) v[k] = glu_fwd_elem<ACT>(g[k], u[k], tail);
+    if (tail) {
 #pragma unroll
       for (int k = 0; k < 8; k++)
-        if (zl2<ACT>(g[k]) < TAIL_ZL2) v[k] = glu_fwd_tail<ACT>(g[k], u[k]);
+        if (fwd_tail_needed<ACT>(g[k], u[k])) v[k] = glu_fwd_tail<ACT>(g[k], u[k]);
     }
 #pragma unroll
     for (int k = 0; k < 4; k++) {
@@ -202,10 +202,10 @@ hipError_t launch(const NvArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_glu_fwd_nvfp4(const NvArgs& a, hipStream_t s) {
-  if (a.act == SWIGLU)
-    return a.layout == PAIRED ? launch<SWIGLU, PAIRED, false>(a, s) : launch<SWIGLU, SPLIT, false>(a, s);
-  return a.layout == PAIRED ? launch<GEGLU_TANH, PAIRED, false>(a, s)
-                            : launch<GEGLU_TANH, SPLIT, false>(a, s);
+  return with_act(a.act, [&](auto A) {
+    constexpr int ACT = decltype(A)::value;
+    return a.layout == PAIRED ? launch<ACT, PAIRED, false>(a, s) : launch<ACT, SPLIT, false>(a, s);
+  });
 }
 
 hipError_t launch_quant_nvfp4_f32(const NvArgs& a, hipStream_t s) {

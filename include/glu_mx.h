@@ -9,7 +9,10 @@
  *   - NVFP4: E2M1 codes packed two per byte with one E4M3 scale per 16 elements and a
  *     global scale of 1.
  * Activations: SwiGLU, act = silu(x) = x * sigmoid(x); GeGLU, act = gelu_tanh(x) =
- * x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3))).
+ * x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3))); GeGLU with the exact GELU,
+ * act = x * Phi(x) (Phi the standard normal CDF); ReLU^2, act = max(x, 0)^2.  The last two
+ * go beyond the pages, which plan more activations than SiLU ([MX] Follow-ups)
+ * without naming them.
  *
  * Sources, cited by page title and section:
  *   [MX] "Add swiglu + MXFP8 fused CuTe DSL kernel": Summary (swiglu fused with the
@@ -66,8 +69,8 @@ typedef enum glu_status {
   GLU_ERR_HIP = 8          /* the HIP runtime refused the launch */
 } glu_status;
 
-/* Activation. */
-enum { GLU_SWIGLU = 0, GLU_GEGLU_TANH = 1 };
+/* Activation (every entry point takes all four). */
+enum { GLU_SWIGLU = 0, GLU_GEGLU_TANH = 1, GLU_GEGLU_ERF = 2, GLU_RELU2 = 3 };
 
 /* Operand layout.
  *   GLU_SPLIT : gate and up are two [M, N] matrices sharing the row stride ld_in.  The

@@ -65,7 +65,8 @@ def fwd(**kw):
 
 def test_fwd_checks():
     assert fwd() == OK
-    assert fwd(act=2) == ARG and fwd(layout=5) == ARG
+    assert fwd(act=2) == OK and fwd(act=3) == OK      # erf-GELU, ReLU^2
+    assert fwd(act=4) == ARG and fwd(act=-1) == ARG and fwd(layout=5) == ARG
     assert fwd(M=-1) == SHAPE and fwd(N=-3) == SHAPE
     assert fwd(M=0, gate=0, up=0, h=0) == OK and fwd(N=0, gate=0) == OK
     assert fwd(gate=0) == NULL and fwd(up=0) == NULL and fwd(h=0) == NULL

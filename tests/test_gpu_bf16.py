@@ -1,6 +1,7 @@
 """GPU parity of glu_fwd / glu_bwd (BF16 outputs) against the oracle, rule 2 (<= 1 BF16 ulp).
 
-Covers every finite BF16 gate value for both activations, the FP32 exp underflow tail,
+Covers every finite BF16 gate value for all four activations, the FP64 tail paths (exp
+underflow of the sigmoid forms, the erf-GELU tail) and ReLU^2 at extreme exponents,
 the three operand layouts (split, concatenated [gate | up], paired), strided rows, ragged
 and contiguous widths, in-place backward, and the full-size GeGLU sweep (sampled rows,
 compared in the launch configuration the benchmark uses).
@@ -15,7 +16,8 @@ from conftest import bits
 from parity import check_rule2
 
 pytestmark = pytest.mark.gpu
-ACTS = [("swiglu", oracle.SWIGLU), ("geglu", oracle.GEGLU_TANH)]
+ACTS = [("swiglu", oracle.SWIGLU), ("geglu", oracle.GEGLU_TANH), ("geglu_erf", oracle.GEGLU_ERF),
+        ("relu2", oracle.RELU2)]
 
 
 def _dev(*ts):
@@ -45,10 +47,15 @@ def test_every_bf16_gate_value(gpu, name, kind):
     check_rule2(bits(db), ob, f"{name} db")
 
 
-@pytest.mark.parametrize("name,kind", ACTS)
+TAIL_RANGE = {oracle.SWIGLU: (-104.0, -80.0), oracle.GEGLU_TANH: (-11.0, -9.0),
+              oracle.GEGLU_ERF: (-40.0, -11.0)}
+
+
+@pytest.mark.parametrize("name,kind", ACTS[:3])
 def test_exp_underflow_tail(gpu, name, kind):
-    """Gates where e^z leaves the FP32 normal range (the FP64 tail path) and large ups."""
-    lo, hi = (-104.0, -80.0) if kind == oracle.SWIGLU else (-11.0, -9.0)
+    """Gates on both sides of the switch to the FP64 tail path (e^z below the FP32 normal
+    range; Phi(x) near it for erf-GELU), with large ups."""
+    lo, hi = TAIL_RANGE[kind]
     gen = torch.Generator().manual_seed(7)
     g = (torch.rand(64, 256, generator=gen) * (hi - lo) + lo).to(torch.bfloat16)
     up = (torch.randn(64, 256, generator=gen) * torch.exp2(torch.randint(-10, 60, (64, 256), generator=gen))).to(torch.bfloat16)
@@ -59,6 +66,29 @@ def test_exp_underflow_tail(gpu, name, kind):
     oa, ob = oracle.glu_bwd(kind, bits(g), bits(up), bits(dh))
     check_rule2(bits(da), oa, "tail da")
     check_rule2(bits(db), ob, "tail db")
+
+
+def test_relu2_extreme_exponents(gpu):
+    """ReLU^2 where g^2 alone overflows or underflows FP32 while g^2 u (and dh u g, dh g^2)
+    is in range: the kernels' FP64 products must give the correctly rounded exact value."""
+    gen = torch.Generator().manual_seed(8)
+    shape = (64, 256)
+
+    def pow2(e):
+        return torch.exp2(e.clamp(-125, 125).double())
+
+    eg = torch.randint(-75, 76, shape, generator=gen)
+    g = (torch.rand(shape, generator=gen, dtype=torch.float64) + 0.5) * pow2(eg)
+    g = torch.where(torch.rand(shape, generator=gen) < 0.1, -g, g)
+    u = torch.randn(shape, generator=gen, dtype=torch.float64) * pow2(-2 * eg + torch.randint(-4, 5, shape, generator=gen))
+    d = torch.randn(shape, generator=gen, dtype=torch.float64) * pow2(-eg + torch.randint(-4, 5, shape, generator=gen))
+    g, u, d = (t.to(torch.bfloat16) for t in (g, u, d))
+    gd, ud, dd = _dev(g, u, d)
+    check_rule2(bits(gpu.glu_fwd(gd, ud, act="relu2")), oracle.glu_fwd(oracle.RELU2, bits(g), bits(u)), "fwd")
+    da, db = gpu.glu_bwd(gd, ud, dd, act="relu2")
+    oa, ob = oracle.glu_bwd(oracle.RELU2, bits(g), bits(u), bits(d))
+    check_rule2(bits(da), oa, "da")
+    check_rule2(bits(db), ob, "db")
 
 
 @pytest.mark.parametrize("name,kind", ACTS)

@@ -18,7 +18,8 @@ from parity import check_rule3_mx
 
 pytestmark = pytest.mark.gpu
 FLAGS = [(True, False), (False, True), (True, True)]
-ACTS = [("swiglu", oracle.SWIGLU), ("geglu", oracle.GEGLU_TANH)]
+ACTS = [("swiglu", oracle.SWIGLU), ("geglu", oracle.GEGLU_TANH), ("geglu_erf", oracle.GEGLU_ERF),
+        ("relu2", oracle.RELU2)]
 
 
 def _flags(row, col):
@@ -251,6 +252,22 @@ def test_config_mid_swiglu_fwd_bwd_both(gpu):
     oa, ob = oracle.glu_bwd(oracle.SWIGLU, gb, ub, db_)
     _rule3_rows(np.concatenate([oa, ob], 1), out,
                 oracle.glu_bwd_mxfp8(oracle.SWIGLU, gb, ub, db_, flags=3), "4096x2048 bwd")
+
+
+@pytest.mark.parametrize("name,kind", ACTS[1:])
+def test_other_activations_fwd_bwd_both(gpu, name, kind):
+    """Rule 3 end to end for the other activations at a shape with ragged tiles in both
+    directions."""
+    gate, up, dh = si.glu_operands(352, 480, seed=kind, outliers=True, with_dh=True)
+    gb, ub, db_ = bits(gate), bits(up), bits(dh)
+    gd, ud, dd = gate.cuda(), up.cuda(), dh.cuda()
+    out = gpu.glu_fwd_mxfp8(gd, ud, act=name, rowwise=True, colwise=True)
+    _rule3_rows(oracle.glu_fwd(kind, gb, ub), out,
+                oracle.glu_fwd_mxfp8(kind, gb, ub, flags=3), f"{name} fwd")
+    out = gpu.glu_bwd_mxfp8(gd, ud, dd, act=name, rowwise=True, colwise=True)
+    oa, ob = oracle.glu_bwd(kind, gb, ub, db_)
+    _rule3_rows(np.concatenate([oa, ob], 1), out,
+                oracle.glu_bwd_mxfp8(kind, gb, ub, db_, flags=3), f"{name} bwd")
 
 
 def _slabs(M, n, seed):

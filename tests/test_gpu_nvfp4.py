@@ -74,7 +74,8 @@ def test_hook_nonfinite_blocks(gpu):
     _hook(gpu, x)
 
 
-@pytest.mark.parametrize("act,kind", [("geglu", oracle.GEGLU_TANH), ("swiglu", oracle.SWIGLU)])
+@pytest.mark.parametrize("act,kind", [("geglu", oracle.GEGLU_TANH), ("swiglu", oracle.SWIGLU),
+                                      ("geglu_erf", oracle.GEGLU_ERF), ("relu2", oracle.RELU2)])
 @pytest.mark.parametrize("layout", ["paired", "split"])
 def test_fused_equals_quantized_glu_fwd(gpu, act, kind, layout):
     M, H = 130, 1024
