@@ -47,6 +47,7 @@ _SIGNATURES = {
     "orc_glu_fwd_mxfp8": (_int, [_int, _int, _i64, _i64, _p, _p, _i64, _int, _p, _p, _p, _p]),
     "orc_glu_bwd_mxfp8": (_int, [_int, _i64, _i64, _p, _p, _i64, _p, _i64, _int, _p, _p, _p, _p]),
     "orc_glu_fwd_nvfp4": (_int, [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int]),
+    "orc_glu_bwd_nvfp4": (_int, [_int, _i64, _i64, _p, _p, _i64, _p, _i64, _p, _p, _int]),
     "orc_bf16_from_f64_array": (None, [_p, _i64, _p]),
     "orc_e4m3_from_f64_array": (None, [_p, _i64, _p]),
     "orc_e2m1_from_f64_array": (None, [_p, _i64, _p]),
@@ -268,6 +269,19 @@ def glu_fwd_nvfp4(kind, gate, up=None, layout=PAIRED, sf_layout=SF_ROWMAJOR):
     q = np.empty((M, H // 2), np.uint8)
     sf = np.empty(sf128x4_bytes(M, H) if sf_layout == SF_128x4 else (M, H // 16), np.uint8)
     rc = _load().orc_glu_fwd_nvfp4(kind, layout, M, H, _ptr(gate), _ptr(up), ld, _ptr(q), _ptr(sf), sf_layout)
+    if rc != 0:
+        raise MemoryError("oracle ran out of host memory")
+    return q, sf
+
+
+def glu_bwd_nvfp4(kind, gate, up, dh, sf_layout=SF_ROWMAJOR):
+    """[da | db] ([M, 2N]) as NVFP4: q [M, N] packed E2M1, scales [M, 2N/16] or 128x4."""
+    gate, up, M, N, ld = _operands(SPLIT, gate, up)
+    dh = _c(dh, np.uint16)
+    q = np.empty((M, N), np.uint8)
+    sf = np.empty(sf128x4_bytes(M, 2 * N) if sf_layout == SF_128x4 else (M, 2 * N // 16), np.uint8)
+    rc = _load().orc_glu_bwd_nvfp4(kind, M, N, _ptr(gate), _ptr(up), ld, _ptr(dh), N, _ptr(q), _ptr(sf),
+                                   sf_layout)
     if rc != 0:
         raise MemoryError("oracle ran out of host memory")
     return q, sf

@@ -44,7 +44,9 @@
  *   - a block holding NaN or Inf gets a NaN scale (MX 0xFF, NV 0x7F) and NaN
  *     codes (MX 0x7F) or zero codes (NV);
  *   - MXFP8 scales may also be asked for in the same zero-padded 128x4 layout
- *     (the GEMM-ready block-scale layout; no page fixes one for MXFP8).
+ *     (the GEMM-ready block-scale layout; no page fixes one for MXFP8);
+ *   - an NVFP4 backward quantizes [da | db] as one [M, 2N] matrix in 16-element
+ *     row blocks, the MXFP8 backward's placement (no page defines one).
  * Parity unpinned: the NaN/Inf block rule, the nibble order, and the 128x4
  * scale layout beyond its being a zero-padded permutation.  No page prints a
  * value for any of them.
@@ -482,6 +484,23 @@ int orc_glu_fwd_nvfp4(int act, int layout, int64_t M, int64_t H, const uint16_t*
   free(h);
   if (!x) return -1;
   orc_quant_nvfp4(M, H, x, q, sf, sf_layout);
+  free(x);
+  return 0;
+}
+
+/* Backward with NVFP4 output: [da | db], [M, 2N], quantized in 16-element row blocks as
+ * the forward's h is (the MXFP8 backward's placement, [MX] API, carried over to NVFP4;
+ * no page defines an NVFP4 backward). */
+int orc_glu_bwd_nvfp4(int act, int64_t M, int64_t N, const uint16_t* gate,
+                      const uint16_t* up, int64_t ld, const uint16_t* dh, int64_t lddh,
+                      uint8_t* q, uint8_t* sf, int sf_layout) {
+  uint16_t* d = (uint16_t*)malloc((size_t)(M * 2 * N) * sizeof(uint16_t));
+  if (!d) return -1;
+  orc_glu_bwd(act, ORC_SPLIT, M, N, gate, up, ld, dh, lddh, d, d + N, 2 * N);
+  float* x = widen_bf16(d, M * 2 * N);
+  free(d);
+  if (!x) return -1;
+  orc_quant_nvfp4(M, 2 * N, x, q, sf, sf_layout);
   free(x);
   return 0;
 }

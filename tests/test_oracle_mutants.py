@@ -67,6 +67,10 @@ MUTANTS = [
      [lambda: tg.test_glu_bwd_matches_autograd(S)]),
     ("paired columns swapped", "*g = orc_bf16_to_f64(gate[m * ld + 2 * j]);", "*g = orc_bf16_to_f64(gate[m * ld + 2 * j + 1]);",
      [tg.test_layouts_agree]),
+    ("NV backward halves swapped",
+     "orc_glu_bwd(act, ORC_SPLIT, M, N, gate, up, ld, dh, lddh, d, d + N, 2 * N);\n  float* x = widen_bf16(d, M * 2 * N);\n  free(d);\n  if (!x) return -1;\n  orc_quant_nvfp4",
+     "orc_glu_bwd(act, ORC_SPLIT, M, N, gate, up, ld, dh, lddh, d + N, d, 2 * N);\n  float* x = widen_bf16(d, M * 2 * N);\n  free(d);\n  if (!x) return -1;\n  orc_quant_nvfp4",
+     [tq.test_nv_backward_is_da_then_db]),
     ("NV scale divisor", "amax / 6.0", "amax / 4.0", [tq.test_nv_golden_blocks]),
     ("MX scale direction", "ldexp(v[i], -e)", "ldexp(v[i], e)", [tq.test_mx_golden_blocks_rowwise_and_colwise]),
     ("bf16 subnormal exponent", "ldexp((double)m, -133)", "ldexp((double)m, -134)",

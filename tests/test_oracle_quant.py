@@ -208,6 +208,26 @@ def test_mx_swizzled_scales_equal_rowmajor_after_unswizzle():
     _unswizzle_check(sw[3], rm[3])
 
 
+def test_nv_backward_is_da_then_db():
+    """The NVFP4 backward quantizes [da | db]: its left half (codes and scales) is the
+    quantizer applied to da alone, its right half to db alone (16-element blocks never
+    straddle the two when N % 16 == 0); the 128x4 option moves the same scale bytes."""
+    M, N = 150, 80
+    gate, up, dh = si.glu_operands(M, N, seed=33, outliers=True, with_dh=True)
+    gb, ub, db_ = si.to_bits(gate), si.to_bits(up), si.to_bits(dh)
+    for kind in (oracle.SWIGLU, oracle.GEGLU_TANH):
+        q, sf = oracle.glu_bwd_nvfp4(kind, gb, ub, db_)
+        assert q.shape == (M, N) and sf.shape == (M, 2 * N // 16)
+        da, dbb = oracle.glu_bwd(kind, gb, ub, db_)
+        qa, sa = oracle.quant_nvfp4(si.from_bits(da).float().numpy())
+        qb, sb = oracle.quant_nvfp4(si.from_bits(dbb).float().numpy())
+        assert np.array_equal(q[:, :N // 2], qa) and np.array_equal(q[:, N // 2:], qb)
+        assert np.array_equal(sf[:, :N // 16], sa) and np.array_equal(sf[:, N // 16:], sb)
+        q2, sf2 = oracle.glu_bwd_nvfp4(kind, gb, ub, db_, sf_layout=oracle.SF_128x4)
+        assert np.array_equal(q, q2)
+        _unswizzle_check(sf2, sf)
+
+
 def test_fused_equals_glu_then_quantizer():
     gate, up, dh = si.glu_operands(64, 64, seed=25, outliers=True, with_dh=True)
     gb, ub, db_ = si.to_bits(gate), si.to_bits(up), si.to_bits(dh)
