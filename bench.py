@@ -14,7 +14,8 @@ Also reported on the same JSON line:
   cpu_baseline  - the CPU oracle on a bounded row sample of the same workload;
   sweep         - every workload shape of the pages (MXFP8 SwiGLU fwd/bwd per direction,
                   GeGLU BF16 fwd/bwd, GeGLU NVFP4), median of cold launches, plus the
-                  other activations (tanh-GeGLU, erf-GeGLU, ReLU^2) at one shape of each.
+                  other activations (tanh-GeGLU, erf-GeGLU, ReLU^2) at one shape of each
+                  and the NVFP4 backward.
 Only one GPU is supported; --gpus above 1 exits with a message.
 """
 import argparse
@@ -83,6 +84,12 @@ def bf16_bytes(M, N, bwd):
 def nv_bytes(M, H):
     E = M * H
     return 4 * E + E // 2 + E // 16
+
+
+def nv_bwd_bytes(M, N):
+    """Read gate, up, dh; write [da | db] as packed E2M1 plus one E4M3 scale per 16."""
+    E = M * N
+    return 6 * E + 2 * (E // 2 + E // 16)
 
 
 def _events(torch, n):
@@ -193,6 +200,16 @@ def sweep(torch, glu, si, iters):
                                                                          sf_layout="128x4", out=out) for x in sets], iters)
                 rec(f"{act}_nvfp4_fwd_{M}x{H}", nv_bytes(M, H), t)
         del sets, out
+    # NVFP4 backward ([da | db] quantized), the workload's shape and the MXFP8 training shape
+    for M, N in ((968, 16384), (16384, 7168)):
+        sets = [si.normal_bf16_device([(M, N)] * 3, seed=M + N + s) for s in range(n_sets(6 * M * N))]
+        out = glu._nv_buffers(M, 2 * N, "128x4", "cuda", None)
+        for act in ("swiglu", "geglu"):
+            t = time_launches(torch, [lambda s=s: glu.glu_bwd_nvfp4(s[0], s[1], s[2], act=act, sf_layout="128x4",
+                                                                     out=out) for s in sets], iters)
+            rec(f"{act}_nvfp4_bwd_{M}x{N}", nv_bwd_bytes(M, N), t)
+        del sets, out
+        torch.cuda.empty_cache()
     return res
 
 

@@ -11,6 +11,7 @@ Entry points (C names in include/glu_mx.h):
   glu_fwd_mxfp8(gate, up=None, rowwise=, colwise=, ...)     -> (q_row, q_col, s_row, s_col)
   glu_bwd_mxfp8(gate, up, dh, rowwise=, colwise=, ...)      -> (q_row, q_col, s_row, s_col)
   glu_fwd_nvfp4(x, up=None, layout="paired", sf_layout=...) -> (q, sf)
+  glu_bwd_nvfp4(gate, up, dh, sf_layout=...)                -> (q, sf) of [da | db]
   glu_quant_mxfp8_f32(x, rowwise=, colwise=)                -> (q_row, q_col, s_row, s_col)
   glu_quant_nvfp4_f32(x, sf_layout=)                        -> (q, sf)
 A disabled MXFP8 direction comes back as zero-sized tensors (fixed arity), as in the
@@ -41,6 +42,7 @@ _SIGNATURES = {
     "glu_fwd_mxfp8": [_int, _int, _i64, _i64, _p, _p, _i64, _int, _p, _p, _p, _p, _p],
     "glu_bwd_mxfp8": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _int, _p, _p, _p, _p, _p],
     "glu_fwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int, _p],
+    "glu_bwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _p, _p, _int, _p],
     "glu_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p, _p],
     "glu_quant_nvfp4_f32": [_i64, _i64, _p, _i64, _p, _p, _int, _p],
     "glu_check_fwd": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64],
@@ -48,6 +50,7 @@ _SIGNATURES = {
     "glu_check_fwd_mxfp8": [_int, _int, _i64, _i64, _p, _p, _i64, _int, _p, _p, _p, _p],
     "glu_check_bwd_mxfp8": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _int, _p, _p, _p, _p],
     "glu_check_fwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int],
+    "glu_check_bwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _p, _p, _int],
     "glu_check_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p],
     "glu_check_quant_nvfp4_f32": [_i64, _i64, _p, _i64, _p, _p, _int],
 }
@@ -108,6 +111,30 @@ def _rowmajor(t, name, dtype):
     return t.size(0), t.size(1), t.stride(0)
 
 
+def _shaped(t, name, M, N):
+    """A BF16 [M, N] operand or output with unit column stride; returns its row stride."""
+    Mt, Nt, ld = _rowmajor(t, name, torch.bfloat16)
+    if (Mt, Nt) != (M, N):
+        raise ValueError(f"{name} must be [{M}, {N}], got [{Mt}, {Nt}]")
+    return ld
+
+
+def _byte_buffer(t, name, numel):
+    """A caller-supplied code or scale buffer: contiguous uint8 on the GPU, numel bytes."""
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must be torch.uint8, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} bytes, got {t.numel()}")
+
+
+def _dh(dh, M, N):
+    return _shaped(dh, "dh", M, N)
+
+
 def _operands(gate, up, layout):
     M, C, ld = _rowmajor(gate, "gate", torch.bfloat16)
     if layout == "paired":
@@ -130,7 +157,7 @@ def glu_fwd(gate, up=None, *, act="swiglu", layout="split", out=None):
     """h = bf16(act(gate) * up), [M, N]."""
     M, N, ld = _operands(gate, up, layout)
     h = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=gate.device)
-    _, _, ldh = _rowmajor(h, "out", torch.bfloat16)
+    ldh = _shaped(h, "out", M, N)
     _call("glu_fwd", ACT[act], LAYOUT[layout], M, N, _ptr(gate), _ptr(up), ld, _ptr(h), ldh,
           _stream(gate))
     return h
@@ -140,11 +167,11 @@ def glu_bwd(gate, up, dh, *, act="swiglu", layout="split", out=None):
     """Split: (da, db) each [M, N].  Paired: one interleaved [M, 2N] gradient.
     out: (da, db) for split or a single tensor for paired; may alias (gate, up) in place."""
     M, N, ld = _operands(gate, up, layout)
-    _, _, lddh = _rowmajor(dh, "dh", torch.bfloat16)
+    lddh = _dh(dh, M, N)
     dev = gate.device
     if layout == "paired":
         d = out if out is not None else torch.empty((M, 2 * N), dtype=torch.bfloat16, device=dev)
-        _, _, ldo = _rowmajor(d, "out", torch.bfloat16)
+        ldo = _shaped(d, "out", M, 2 * N)
         _call("glu_bwd", ACT[act], 1, M, N, _ptr(gate), None, ld, _ptr(dh), lddh, _ptr(d), None,
               ldo, _stream(gate))
         return d
@@ -152,8 +179,8 @@ def glu_bwd(gate, up, dh, *, act="swiglu", layout="split", out=None):
         out = (torch.empty((M, N), dtype=torch.bfloat16, device=dev),
                torch.empty((M, N), dtype=torch.bfloat16, device=dev))
     da, db = out
-    _, _, ldo = _rowmajor(da, "da", torch.bfloat16)
-    _, _, ldb = _rowmajor(db, "db", torch.bfloat16)
+    ldo = _shaped(da, "da", M, N)
+    ldb = _shaped(db, "db", M, N)
     if ldb != ldo and M > 1:
         raise ValueError("da and db must share a row stride")
     _call("glu_bwd", ACT[act], 0, M, N, _ptr(gate), _ptr(up), ld, _ptr(dh), lddh, _ptr(da),
@@ -167,7 +194,17 @@ def mxfp8_sf_bytes(rows, cols, swizzled=False):
 
 
 def _mx_buffers(M, C, rowwise, colwise, dev, out, swizzled=False):
+    def sbytes(rows, cols):
+        return mxfp8_sf_bytes(rows, cols, True) if swizzled else rows * (cols // 32)
+
     if out is not None:
+        q_row, q_col, s_row, s_col = out
+        if rowwise:
+            _byte_buffer(q_row, "q_row", M * C)
+            _byte_buffer(s_row, "s_row", sbytes(M, C))
+        if colwise:
+            _byte_buffer(q_col, "q_col", C * M)
+            _byte_buffer(s_col, "s_col", sbytes(C, M))
         return out
     u8 = dict(dtype=torch.uint8, device=dev)
     z = torch.empty((0,), **u8)
@@ -208,7 +245,7 @@ def glu_bwd_mxfp8(gate, up, dh, *, act="swiglu", rowwise=True, colwise=False, sw
     """Fused backward + MXFP8 of [da | db] ([M, 2N]): (q_row [M,2N], q_col [2N,M],
     s_row [M,2N/32], s_col [2N,M/32]); swizzled=True as for glu_fwd_mxfp8."""
     M, N, ld = _operands(gate, up, "split")
-    _, _, lddh = _rowmajor(dh, "dh", torch.bfloat16)
+    lddh = _dh(dh, M, N)
     f = _flags(rowwise, colwise, swizzled)
     q_row, q_col, s_row, s_col = _mx_buffers(M, 2 * N, rowwise, colwise, gate.device, out, swizzled)
     _call("glu_bwd_mxfp8", ACT[act], 0, M, N, _ptr(gate), _ptr(up), ld, _ptr(dh), lddh, f,
@@ -222,6 +259,8 @@ def nvfp4_sf_bytes(M, H, sf_layout="rowmajor"):
 
 def _nv_buffers(M, H, sf_layout, dev, out):
     if out is not None:
+        _byte_buffer(out[0], "q", M * (H // 2))
+        _byte_buffer(out[1], "sf", nvfp4_sf_bytes(M, H, sf_layout))
         return out
     q = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
     if sf_layout == "rowmajor":
@@ -237,6 +276,17 @@ def glu_fwd_nvfp4(x, up=None, *, act="geglu", layout="paired", sf_layout="rowmaj
     q, sf = _nv_buffers(M, H, sf_layout, x.device, out)
     _call("glu_fwd_nvfp4", ACT[act], LAYOUT[layout], M, H, _ptr(x), _ptr(up), ld, _ptr(q), _ptr(sf),
           SF_LAYOUT[sf_layout], _stream(x))
+    return q, sf
+
+
+def glu_bwd_nvfp4(gate, up, dh, *, act="swiglu", sf_layout="rowmajor", out=None):
+    """Fused backward + NVFP4 (global scale 1) of [da | db] ([M, 2N]): (q [M, N] packed E2M1,
+    sf scales of [M, 2N/16])."""
+    M, N, ld = _operands(gate, up, "split")
+    lddh = _dh(dh, M, N)
+    q, sf = _nv_buffers(M, 2 * N, sf_layout, gate.device, out)
+    _call("glu_bwd_nvfp4", ACT[act], 0, M, N, _ptr(gate), _ptr(up), ld, _ptr(dh), lddh, _ptr(q),
+          _ptr(sf), SF_LAYOUT[sf_layout], _stream(gate))
     return q, sf
 
 

@@ -31,6 +31,10 @@ constexpr int64_t kMaxMxPitchBytes = (int64_t)1 << 25;
 // width; colwise: M): the kernels address 128 output rows from a per-tile base with 32-bit
 // offsets that must stay below 2^31.
 constexpr int64_t kMaxMxOutPitch = (int64_t)1 << 24;
+// Largest operand width (columns) of an NVFP4 launch: the kernels address one row from a
+// per-row base with 32-bit offsets (FP32 hook loads 4 bytes per column; 128x4 scales of the
+// backward's [M, 2N] reach 16 bytes per column) that must stay below 2^31.
+constexpr int64_t kMaxNvWidth = (int64_t)1 << 26;
 
 // Output pitches of an MXFP8 launch whose quantized matrix is [M, width].
 glu_status check_mx_pitch(int flags, int64_t M, int64_t width) {
@@ -298,7 +302,7 @@ glu_status glu_check_fwd_nvfp4(int act, int layout, int64_t M, int64_t H, const 
   glu_status st = check_inputs(act, layout, H, gate, up, ld_in);
   if (st != GLU_OK) return st;
   if (q == nullptr || sf == nullptr) return GLU_ERR_NULL;
-  if (H % 16 != 0) return GLU_ERR_SHAPE;
+  if (H % 16 != 0 || H > kMaxNvWidth) return GLU_ERR_SHAPE;
   if (ld_in % 8 != 0) return GLU_ERR_STRIDE;
   if (!aligned16(gate) || !aligned16(up) || !aligned16(q) || !aligned16(sf)) return GLU_ERR_ALIGN;
   const int64_t sfb = glu_nvfp4_sf_bytes(M, H, sf_layout);
@@ -308,6 +312,32 @@ glu_status glu_check_fwd_nvfp4(int act, int layout, int64_t M, int64_t H, const 
                 Q = mat(q, M, H / 2, H / 2, 1), S = mat(sf, 1, sfb, sfb, 1);
   if (any_overflow({G, U, Q, S})) return GLU_ERR_SHAPE;
   return check_no_overlap({Q, S}, {G, U});
+}
+
+glu_status glu_check_bwd_nvfp4(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                               const uint16_t* up, int64_t ld_in, const uint16_t* dh,
+                               int64_t ld_dh, uint8_t* q, uint8_t* sf, int sf_layout) {
+  if (!valid_act(act) || !valid_layout(layout)) return GLU_ERR_ARG;
+  if (sf_layout != glu::SF_ROWMAJOR && sf_layout != glu::SF_128x4) return GLU_ERR_ARG;
+  if (M < 0 || N < 0) return GLU_ERR_SHAPE;
+  if (layout == glu::PAIRED) return GLU_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return GLU_OK;
+  glu_status st = check_inputs(act, layout, N, gate, up, ld_in);
+  if (st != GLU_OK) return st;
+  if (dh == nullptr || q == nullptr || sf == nullptr) return GLU_ERR_NULL;
+  if (N % 16 != 0 || N > kMaxNvWidth) return GLU_ERR_SHAPE;
+  if (ld_dh < N) return GLU_ERR_STRIDE;
+  if (ld_in % 8 != 0 || ld_dh % 8 != 0) return GLU_ERR_STRIDE;
+  if (!aligned16(gate) || !aligned16(up) || !aligned16(dh) || !aligned16(q) || !aligned16(sf))
+    return GLU_ERR_ALIGN;
+  int64_t N2;
+  if (__builtin_mul_overflow(N, (int64_t)2, &N2)) return GLU_ERR_SHAPE;
+  const int64_t sfb = glu_nvfp4_sf_bytes(M, N2, sf_layout);
+  if (sfb < 0) return GLU_ERR_SHAPE;
+  const Operand G = mat(gate, M, N, ld_in, 2), U = mat(up, M, N, ld_in, 2),
+                D = mat(dh, M, N, ld_dh, 2), Q = mat(q, M, N, N, 1), S = mat(sf, 1, sfb, sfb, 1);
+  if (any_overflow({G, U, D, Q, S})) return GLU_ERR_SHAPE;
+  return check_no_overlap({Q, S}, {G, U, D});
 }
 
 glu_status glu_check_quant_mxfp8_f32(int64_t M, int64_t N, const float* x, int64_t ld_x,
@@ -339,7 +369,7 @@ glu_status glu_check_quant_nvfp4_f32(int64_t M, int64_t H, const float* x, int64
   if (M < 0 || H < 0) return GLU_ERR_SHAPE;
   if (M == 0 || H == 0) return GLU_OK;
   if (x == nullptr || q == nullptr || sf == nullptr) return GLU_ERR_NULL;
-  if (H % 16 != 0) return GLU_ERR_SHAPE;
+  if (H % 16 != 0 || H > kMaxNvWidth) return GLU_ERR_SHAPE;
   if (ld_x < H || ld_x % 4 != 0) return GLU_ERR_STRIDE;
   if (!aligned16(x) || !aligned16(q) || !aligned16(sf)) return GLU_ERR_ALIGN;
   const int64_t sfb = glu_nvfp4_sf_bytes(M, H, sf_layout);
@@ -419,8 +449,18 @@ glu_status glu_fwd_nvfp4(int act, int layout, int64_t M, int64_t H, const uint16
                          int sf_layout, void* stream) {
   glu_status st = glu_check_fwd_nvfp4(act, layout, M, H, gate, up, ld_in, q, sf, sf_layout);
   if (st != GLU_OK || M == 0 || H == 0) return st;
-  NvArgs a{act, layout, sf_layout, M, H, gate, up, ld_in, q, sf};
+  NvArgs a{act, layout, sf_layout, M, H, gate, up, ld_in, q, sf, nullptr, 0};
   return status_of(glu::launch_glu_fwd_nvfp4(a, (hipStream_t)stream));
+}
+
+glu_status glu_bwd_nvfp4(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                         const uint16_t* up, int64_t ld_in, const uint16_t* dh, int64_t ld_dh,
+                         uint8_t* q, uint8_t* sf, int sf_layout, void* stream) {
+  glu_status st =
+      glu_check_bwd_nvfp4(act, layout, M, N, gate, up, ld_in, dh, ld_dh, q, sf, sf_layout);
+  if (st != GLU_OK || M == 0 || N == 0) return st;
+  NvArgs a{act, layout, sf_layout, M, N, gate, up, ld_in, q, sf, dh, ld_dh};
+  return status_of(glu::launch_glu_bwd_nvfp4(a, (hipStream_t)stream));
 }
 
 glu_status glu_quant_mxfp8_f32(int64_t M, int64_t N, const float* x, int64_t ld_x, int flags,
@@ -437,7 +477,7 @@ glu_status glu_quant_nvfp4_f32(int64_t M, int64_t H, const float* x, int64_t ld_
                                uint8_t* sf, int sf_layout, void* stream) {
   glu_status st = glu_check_quant_nvfp4_f32(M, H, x, ld_x, q, sf, sf_layout);
   if (st != GLU_OK || M == 0 || H == 0) return st;
-  NvArgs a{glu::SWIGLU, glu::SPLIT, sf_layout, M, H, x, nullptr, ld_x, q, sf};
+  NvArgs a{glu::SWIGLU, glu::SPLIT, sf_layout, M, H, x, nullptr, ld_x, q, sf, nullptr, 0};
   return status_of(glu::launch_quant_nvfp4_f32(a, (hipStream_t)stream));
 }
 

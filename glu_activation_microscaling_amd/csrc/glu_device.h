@@ -427,6 +427,15 @@ __device__ __forceinline__ uint32_t nv_scale_code(float amax) {
   return c;
 }
 
+// The same decision for a BF16-valued amax (every block maximum of the fused paths): the
+// FP32 product amax * fl(1/6), clamped to 448, rounds to the same E4M3 code as amax / 6
+// does, for every finite BF16 amax (an exhaustive check over all of them), so the hardware
+// convert decides it directly.
+__device__ __forceinline__ uint32_t nv_scale_code_bf16(float amax) {
+  const float y = __builtin_fminf(amax * (1.0f / 6.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xffu;
+}
+
 // E2M1 decision thresholds at scale S: S * {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5}, each exact
 // in FP32.  S == 0 maps every magnitude to code 0 (thresholds at +Inf).
 struct E2m1Thresholds {
@@ -490,5 +499,38 @@ __device__ __forceinline__ uint32_t swz_xor16(uint32_t v) {
 }
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// ---------------------------------------------------------------------------------
+// Packed 16-bit helpers (two BF16 bit patterns per 32-bit word).
+// ---------------------------------------------------------------------------------
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t w) { return __builtin_bit_cast(u16x2, w); }
+__device__ __forceinline__ uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ uint32_t pkmax(uint32_t a, uint32_t b) {
+  return as_u32(__builtin_elementwise_max(as_u16x2(a), as_u16x2(b)));
+}
+__device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xffffu; }
+__device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
+// (a.lo, b.lo) and (a.hi, b.hi) as packed pairs
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// ---------------------------------------------------------------------------------
+// Raw buffer access.  A descriptor's base is a wave-uniform address (computed on the scalar
+// unit); lanes pass 32-bit byte offsets.  An offset of kOob or more is outside the
+// descriptor's range: the hardware returns zeros for such a load and drops such a store.
+// ---------------------------------------------------------------------------------
+
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+  // gfx9 descriptor word 3: 32-bit data format, raw (stride 0) addressing
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(kOob - 1),
+                                           0x00020000);
+}
 
 }  // namespace glu

@@ -43,12 +43,14 @@ struct MxArgs {
 
 struct NvArgs {
   int act, layout, sf_layout;
-  int64_t M, H;
+  int64_t M, H;              // operand shape; the quantized matrix is [M, H] (fwd) or [M, 2H] (bwd)
   const void* src;           // gate (BF16) or x (FP32, quantizer hook)
   const uint16_t* up;
   int64_t ld_in;
   uint8_t* q;
   uint8_t* sf;
+  const uint16_t* dh;        // backward only
+  int64_t ld_dh;
 };
 
 hipError_t launch_glu_fwd_bf16(const BF16Args& a, hipStream_t s);
@@ -57,6 +59,7 @@ hipError_t launch_glu_fwd_mxfp8(const MxArgs& a, hipStream_t s);
 hipError_t launch_glu_bwd_mxfp8(const MxArgs& a, hipStream_t s);
 hipError_t launch_quant_mxfp8_f32(const MxArgs& a, hipStream_t s);
 hipError_t launch_glu_fwd_nvfp4(const NvArgs& a, hipStream_t s);
+hipError_t launch_glu_bwd_nvfp4(const NvArgs& a, hipStream_t s);
 hipError_t launch_quant_nvfp4_f32(const NvArgs& a, hipStream_t s);
 
 // Launches kernel k and returns the launch status of this call alone (the HIP error

@@ -143,28 +143,12 @@ __device__ __forceinline__ void tile_of(uint32_t t, uint32_t tiles_m, uint32_t t
   }
 }
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ u16x2 as_u16x2(uint32_t w) { return __builtin_bit_cast(u16x2, w); }
-__device__ __forceinline__ uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
-__device__ __forceinline__ uint32_t pkmax(uint32_t a, uint32_t b) {
-  return as_u32(__builtin_elementwise_max(as_u16x2(a), as_u16x2(b)));
-}
 // Packed E8M0 RCEIL scale bytes from packed BF16 magnitudes A = E << 7 | m of finite block
 // maxima: e + 127 = E - 8 + (m > 0x60), i.e. ((A + 0x1F) >> 7) - 8 saturated at 0.
 __device__ __forceinline__ uint32_t pk_scale_bytes(uint32_t A) {
   const u16x2 t = (as_u16x2(A) + (u16x2){0x1f, 0x1f}) >> (u16x2){7, 7};
   return as_u32(__builtin_elementwise_sub_sat(t, (u16x2){8, 8}));
 }
-__device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xffffu; }
-__device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
-// (a.lo, b.lo) and (a.hi, b.hi) as packed pairs
-__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
 // Raw operand words of 8 consecutive outputs: SPLIT gives gate and up words (each a BF16
 // pair of adjacent columns); PAIRED gives 8 words, each a (gate, up) BF16 pair.
@@ -198,13 +182,6 @@ __device__ __forceinline__ void unpack_gu(const GU<LAYOUT>& r, float g[8], float
 // passes kOob as its offset; the hardware's range check turns that load into zeros, so every
 // path through a tile issues the same loads, with no branch and no select.  Row pitches are
 // limited (by the host checks) so that 32 rows of offsets stay below kOob.
-constexpr uint32_t kOob = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
-  // gfx9 descriptor word 3: 32-bit data format, raw (stride 0) addressing
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(kOob - 1),
-                                           0x00020000);
-}
 
 __device__ __forceinline__ void bld16(uint32_t (&w)[4], __amdgpu_buffer_rsrc_t r, uint32_t off) {
   const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, GLU_MX_NT_LOADS ? 2 : 0);

@@ -3,13 +3,23 @@
 // E2M1 values, E4M3 scales in the 128x4 layout, pairwise-interleaved gate/up columns), and
 // the FP32 quantizer hook running the same quantize-and-store stage.
 //
-// Work decomposition (wave64): a workgroup of 4 waves covers 2048 consecutive outputs of one
-// row; each lane computes 8 consecutive outputs (one 32-byte load of interleaved gate/up
-// pairs, or 16 bytes each of gate and up).  A 16-element block is a lane pair, so the block
+// The backward quantizes [dGate | dUp] the same way (a reading: no page defines an NVFP4
+// backward; the placement is that of the MXFP8 backward, "Add swiglu + MXFP8 fused CuTe DSL
+// kernel", API).
+//
+// Work decomposition (wave64): a workgroup of 4 waves covers 2048 consecutive operand
+// columns of one row per group (2 groups per workgroup; the backward 2 or 4); each lane takes 8
+// consecutive columns (one 32-byte load of interleaved gate/up pairs, or 16 bytes each of
+// gate and up, and of dh in the backward).  A 16-element block is a lane pair, so the block
 // amax is one DPP quad_perm exchange.  Each lane stores its 8 E2M1 codes as one 4-byte word
-// (a wave writes 256 contiguous bytes); the even lane of a pair stores the scale byte.
-// With the 128x4 layout the grid also covers the padding rows up to a multiple of 128, and
-// the lane holding the last block of a row zero-fills the padding scale columns.
+// (a wave writes 256 contiguous bytes).  With the 128x4 layout the four scales of a lane
+// octet (4 consecutive blocks) leave as one 4-byte word; the grid also covers the padding
+// rows up to a multiple of 128, which get zero scales.
+//
+// The row is uniform in a workgroup, so every row-dependent address is formed once on the
+// scalar unit as a buffer descriptor base; lanes add 32-bit offsets, and a lane outside the
+// matrix passes kOob (loads return zeros, stores are dropped), so every path issues the same
+// memory instructions.  The host keeps the operand width below 2^28 columns.
 #include "glu_device.h"
 #include "glu_launch.h"
 
@@ -17,11 +27,10 @@ namespace glu {
 namespace {
 
 constexpr int NV_THREADS = 256;
-constexpr int64_t NV_TILE = 2048;  // outputs per workgroup and group
+constexpr int64_t NV_TILE = 2048;  // operand columns per workgroup and group
 #ifndef GLU_NV_GROUPS              // build-time override, for measurements
-#define GLU_NV_GROUPS 1
+#define GLU_NV_GROUPS 2
 #endif
-constexpr int NV_GROUPS = GLU_NV_GROUPS;  // groups of 8 outputs per lane
 
 // Build-time tuning (fixed defaults; alternatives are compiled only to measure them):
 //   GLU_NV_NT_LOADS / GLU_NV_NT_STORES: non-temporal (streaming) loads / code stores.
@@ -32,171 +41,321 @@ constexpr int NV_GROUPS = GLU_NV_GROUPS;  // groups of 8 outputs per lane
 #define GLU_NV_NT_STORES 0
 #endif
 
-typedef unsigned int nu32x4 __attribute__((ext_vector_type(4)));
+enum { NV_FWD = 0, NV_BWD = 1, NV_F32 = 2 };
+
 
 struct Words4 {
   uint32_t w[4];
 };
-__device__ __forceinline__ Words4 ld16(const void* p) {
-  nu32x4 v;
-  if constexpr (GLU_NV_NT_LOADS) v = __builtin_nontemporal_load(reinterpret_cast<const nu32x4*>(p));
-  else v = *reinterpret_cast<const nu32x4*>(p);
-  return Words4{{v.x, v.y, v.z, v.w}};
-}
-__device__ __forceinline__ void st4(uint8_t* p, uint32_t w) {
-  if constexpr (GLU_NV_NT_STORES) __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(p));
-  else *reinterpret_cast<uint32_t*>(p) = w;
+__device__ __forceinline__ Words4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, GLU_NV_NT_LOADS ? 2 : 0);
+  return Words4{{x.x, x.y, x.z, x.w}};
 }
 
-// Raw operand words of a lane's 8 outputs: interleaved (gate, up) pairs, gate and up
-// vectors, or FP32 values.
+// Raw operand words of a lane's 8 columns: interleaved (gate, up) pairs (A, B), gate and up
+// vectors (A, B) and dh (C) in the backward, or FP32 values (A, B).
 struct Raw8 {
-  Words4 A, B;
+  Words4 A, B, C;
 };
 
-template <int LAYOUT, bool F32>
-__device__ __forceinline__ Raw8 load_raw(const NvArgs& a, int64_t row, int64_t j) {
-  if constexpr (F32) {
-    const float* p = static_cast<const float*>(a.src) + row * a.ld_in + j;
-    return Raw8{ld16(p), ld16(p + 4)};
-  } else if constexpr (LAYOUT == PAIRED) {
-    const uint16_t* p = static_cast<const uint16_t*>(a.src) + row * a.ld_in + 2 * j;
-    return Raw8{ld16(p), ld16(p + 8)};
+// Row-dependent descriptors of one tile row.
+struct RowIn {
+  __amdgpu_buffer_rsrc_t a, b, d;
+};
+
+template <int LAYOUT, int MODE>
+__device__ __forceinline__ RowIn row_in(const NvArgs& a, int64_t row) {
+  RowIn r;
+  if constexpr (MODE == NV_F32) {
+    r.a = rsrc(static_cast<const float*>(a.src) + row * a.ld_in);
   } else {
-    return Raw8{ld16(static_cast<const uint16_t*>(a.src) + row * a.ld_in + j),
-                ld16(a.up + row * a.ld_in + j)};
+    r.a = rsrc(static_cast<const uint16_t*>(a.src) + row * a.ld_in);
+    if constexpr (LAYOUT == SPLIT) r.b = rsrc(a.up + row * a.ld_in);
+    if constexpr (MODE == NV_BWD) r.d = rsrc(a.dh + row * a.ld_dh);
+  }
+  return r;
+}
+
+// Loads of column j (every lane issues them; off-matrix lanes pass kOob).
+template <int LAYOUT, int MODE>
+__device__ __forceinline__ Raw8 load_raw(const RowIn& r, uint32_t j, bool live) {
+  Raw8 x;
+  if constexpr (MODE == NV_F32 || LAYOUT == PAIRED) {  // 32 contiguous bytes per lane
+    const uint32_t off = live ? 4u * j : kOob;
+    x.A = bld16(r.a, off);
+    x.B = bld16(r.a, live ? off + 16u : kOob);
+  } else {
+    const uint32_t off = live ? 2u * j : kOob;
+    x.A = bld16(r.a, off);
+    x.B = bld16(r.b, off);
+    if constexpr (MODE == NV_BWD) x.C = bld16(r.d, off);
+  }
+  return x;
+}
+
+// Largest raw gate bit pattern (unsigned 16-bit) of the lane's 8 gates, the argument of
+// tail_possible: paired words hold (gate, up) with the gate in the low half.
+template <int LAYOUT>
+__device__ __forceinline__ uint32_t gate_max16(const Raw8& r) {
+  if constexpr (LAYOUT == PAIRED) {
+    uint32_t m = pkmax(pkmax(pkmax(r.A.w[0], r.A.w[1]), pkmax(r.A.w[2], r.A.w[3])),
+                       pkmax(pkmax(r.B.w[0], r.B.w[1]), pkmax(r.B.w[2], r.B.w[3])));
+    return lo16(m);
+  } else {
+    const uint32_t m = pkmax(pkmax(r.A.w[0], r.A.w[1]), pkmax(r.A.w[2], r.A.w[3]));
+    return umax(lo16(m), hi16(m));
   }
 }
 
-// The lane's 8 values to quantize: the FP32 inputs, or the GLU outputs rounded to BF16.
-template <int ACT, int LAYOUT, bool F32>
-__device__ __forceinline__ void values(const Raw8& r, float v[8]) {
-  if constexpr (F32) {
+// The lane's GLU results as packed BF16 pairs (4 words = 8 columns): h (forward), or da in
+// p and db in q (backward).
+template <int ACT, int LAYOUT, int MODE>
+__device__ __forceinline__ void glu_values(const Raw8& r, uint32_t p[4], uint32_t q[4]) {
+  float g[8], u[8];
+  if constexpr (LAYOUT == PAIRED) {
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-      v[k] = __uint_as_float(r.A.w[k]);
-      v[4 + k] = __uint_as_float(r.B.w[k]);
+      g[k] = bf_lo(r.A.w[k]);
+      u[k] = bf_hi(r.A.w[k]);
+      g[4 + k] = bf_lo(r.B.w[k]);
+      u[4 + k] = bf_hi(r.B.w[k]);
     }
   } else {
-    float g[8], u[8];
-    if constexpr (LAYOUT == PAIRED) {
 #pragma unroll
-      for (int k = 0; k < 4; k++) {
-        g[k] = bf_lo(r.A.w[k]);
-        u[k] = bf_hi(r.A.w[k]);
-        g[4 + k] = bf_lo(r.B.w[k]);
-        u[4 + k] = bf_hi(r.B.w[k]);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; k++) {
-        g[2 * k] = bf_lo(r.A.w[k]);
-        g[2 * k + 1] = bf_hi(r.A.w[k]);
-        u[2 * k] = bf_lo(r.B.w[k]);
-        u[2 * k + 1] = bf_hi(r.B.w[k]);
-      }
+    for (int k = 0; k < 4; k++) {
+      g[2 * k] = bf_lo(r.A.w[k]);
+      g[2 * k + 1] = bf_hi(r.A.w[k]);
+      u[2 * k] = bf_lo(r.B.w[k]);
+      u[2 * k + 1] = bf_hi(r.B.w[k]);
     }
-    bool tail = false;
+  }
+  bool tail = false;
+  if constexpr (tail_from_gate_bits<ACT>()) tail = tail_possible<ACT>(gate_max16<LAYOUT>(r));
+  if constexpr (MODE == NV_BWD) {
+    float d[8], da[8], db[8];
 #pragma unroll
-    for (int k = 0; k < 8; k++) v[k] = glu_fwd_elem<ACT>(g[k], u[k], tail);
-    if (tail) {
+    for (int k = 0; k < 4; k++) {
+      d[2 * k] = bf_lo(r.C.w[k]);
+      d[2 * k + 1] = bf_hi(r.C.w[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      glu_bwd_fast<ACT>(g[k], u[k], d[k], da[k], db[k]);
+      if constexpr (!tail_from_gate_bits<ACT>()) tail |= bwd_tail_needed<ACT>(g[k], u[k], d[k]);
+    }
+    if (tail) {  // rare: some element may need the FP64 tail path
 #pragma unroll
       for (int k = 0; k < 8; k++)
-        if (fwd_tail_needed<ACT>(g[k], u[k])) v[k] = glu_fwd_tail<ACT>(g[k], u[k]);
+        if (bwd_tail_needed<ACT>(g[k], u[k], d[k])) glu_bwd_tail<ACT>(g[k], u[k], d[k], da[k], db[k]);
     }
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-      const uint32_t p = pack_bf16(v[2 * k], v[2 * k + 1]);
-      v[2 * k] = bf_lo(p);
-      v[2 * k + 1] = bf_hi(p);
+      p[k] = pack_bf16(da[2 * k], da[2 * k + 1]);
+      q[k] = pack_bf16(db[2 * k], db[2 * k + 1]);
+    }
+  } else {
+    float h[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      h[k] = glu_fwd_fast<ACT>(g[k], u[k]);
+      if constexpr (!tail_from_gate_bits<ACT>()) tail |= fwd_tail_needed<ACT>(g[k], u[k]);
+    }
+    if (tail) {  // rare: some element may need the FP64 tail path
+#pragma unroll
+      for (int k = 0; k < 8; k++)
+        if (fwd_tail_needed<ACT>(g[k], u[k])) h[k] = glu_fwd_tail<ACT>(g[k], u[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) p[k] = pack_bf16(h[2 * k], h[2 * k + 1]);
+  }
+}
+
+// Output geometry of the quantized matrix: codes are q_pitch bytes per row, scales
+// scale_cols per row (scale_cols_padded in the 128x4 layout).
+struct NvOut {
+  int64_t q_pitch, scale_cols, scale_cols_padded;
+};
+
+// Scale and code descriptors of one output row.  128x4: the row's scales sit at
+// base + (c / 4) * 512 + c % 4 from base = ((row / 128) * (Cp / 4)) * 512 + (row % 32) * 16 +
+// ((row % 128) / 32) * 4.
+template <int SFL>
+__device__ __forceinline__ void row_out(const NvArgs& a, const NvOut& o, int64_t row,
+                                        __amdgpu_buffer_rsrc_t& qr, __amdgpu_buffer_rsrc_t& sr) {
+  qr = rsrc(a.q + row * o.q_pitch);
+  if constexpr (SFL == SF_ROWMAJOR)
+    sr = rsrc(a.sf + row * o.scale_cols);
+  else
+    sr = rsrc(a.sf + (row >> 7) * (o.scale_cols_padded >> 2) * 512 + (row & 31) * 16 +
+              ((row & 127) >> 5) * 4);
+}
+
+template <int N>
+__device__ __forceinline__ uint32_t row_shl(uint32_t v) {
+  // lane i of a 16-lane row reads lane i + N; lanes without a source read 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x100 + N, 0xf, 0xf, true);
+}
+
+// Block scale, codes and stores for the lane's 8 BF16 results (packed in p) at output column
+// jq.  Every lane of the wave calls it (the block amax is a lane-pair exchange, the 128x4
+// scale word a lane-octet gather).  WORD_SCALES: 128x4 scales leave as 4-byte words (needs
+// jq's block index to be a multiple of 4 at every lane octet, true when the column offset of
+// this part is a multiple of 64).
+template <int SFL, bool WORD_SCALES>
+__device__ __forceinline__ void quant_store_bf16(const uint32_t p[4], __amdgpu_buffer_rsrc_t qr,
+                                                 __amdgpu_buffer_rsrc_t sr, uint32_t jq,
+                                                 bool in_row, bool live, int lane,
+                                                 uint32_t scale_cols, uint32_t scale_cols_padded) {
+  const uint32_t M = 0x7fff7fffu;
+  const uint32_t m2 = pkmax(pkmax(p[0] & M, p[1] & M), pkmax(p[2] & M, p[3] & M));
+  uint32_t m = umax(lo16(m2), hi16(m2));
+  m = umax(m, dpp<DPP_XOR1>(m));  // BF16 magnitude bits of the block amax
+  const bool nonfinite = m >= 0x7f80u;
+  const uint32_t sc = nonfinite ? 0x7fu : nv_scale_code_bf16(__uint_as_float(m << 16));
+
+  const float S = e4m3_value(nonfinite ? 0u : sc);
+  const float R = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
+  uint32_t word = 0;
+  word = fp4x2<0>(word, e2m1_operand(bf_lo(p[0]), R), e2m1_operand(bf_hi(p[0]), R));
+  word = fp4x2<1>(word, e2m1_operand(bf_lo(p[1]), R), e2m1_operand(bf_hi(p[1]), R));
+  word = fp4x2<2>(word, e2m1_operand(bf_lo(p[2]), R), e2m1_operand(bf_hi(p[2]), R));
+  word = fp4x2<3>(word, e2m1_operand(bf_lo(p[3]), R), e2m1_operand(bf_hi(p[3]), R));
+  if (nonfinite) word = 0;
+  __builtin_amdgcn_raw_buffer_store_b32(word, qr, live ? jq / 2 : kOob, 0, GLU_NV_NT_STORES ? 2 : 0);
+
+  const uint32_t blk = jq / 16;
+  const uint32_t byte = live ? sc : 0u;  // padding rows and columns hold 0
+  if constexpr (SFL == SF_128x4 && WORD_SCALES) {
+    // lane 8k + 2i holds block 4k' + i of the octet: gather the four into lane 8k
+    uint32_t w = byte | (row_shl<2>(byte) << 8);
+    w |= row_shl<4>(w) << 16;
+    // only octets that start inside this part write (in the backward, the da part's octets
+    // past column H would otherwise land on db's scales); an octet reaching past the last
+    // block fills padding columns with zeros
+    const bool lead = (lane & 7) == 0 && in_row;
+    __builtin_amdgcn_raw_buffer_store_b32(w, sr, lead ? (blk >> 2) * 512u : kOob, 0, 0);
+  } else {
+    const bool even = (lane & 1) == 0 && in_row;
+    if constexpr (SFL == SF_ROWMAJOR) {
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, sr, even ? blk : kOob, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, sr, even ? (blk >> 2) * 512u + (blk & 3) : kOob, 0, 0);
+      // the lane holding the last block zero-fills the padding scale columns
+      if (even && blk == scale_cols - 1)
+        for (uint32_t c = scale_cols; c < scale_cols_padded; c++)
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)0, sr, (c >> 2) * 512u + (c & 3), 0, 0);
     }
   }
 }
 
-// A workgroup covers NV_GROUPS * 2048 consecutive outputs of one row: lane l takes 8 outputs
-// at l * 8 + g * 2048 for each group g, and issues the loads of all its groups first.
-template <int ACT, int LAYOUT, int SFL, bool F32>
+// FP32 hook: any FP32 value, exact scale decision and threshold comparisons; byte scales.
+template <int SFL>
+__device__ __forceinline__ void quant_store_f32(const float v[8], __amdgpu_buffer_rsrc_t qr,
+                                                __amdgpu_buffer_rsrc_t sr, uint32_t jq,
+                                                bool in_row, bool live, int lane,
+                                                uint32_t scale_cols, uint32_t scale_cols_padded) {
+  uint32_t m = __float_as_uint(v[0]) & 0x7fffffffu;
+#pragma unroll
+  for (int k = 1; k < 8; k++) m = umax(m, __float_as_uint(v[k]) & 0x7fffffffu);
+  m = umax(m, dpp<DPP_XOR1>(m));
+  const bool nonfinite = m >= 0x7f800000u;
+  const uint32_t sc = nonfinite ? 0x7fu : nv_scale_code(__uint_as_float(m));
+  const E2m1Thresholds T = e2m1_thresholds(e4m3_value(nonfinite ? 0u : sc));
+  uint32_t word = 0;
+#pragma unroll
+  for (int k = 0; k < 8; k++) word |= e2m1_code(v[k], T) << (4 * k);
+  if (nonfinite) word = 0;
+  __builtin_amdgcn_raw_buffer_store_b32(word, qr, live ? jq / 2 : kOob, 0, 0);
+  const uint32_t blk = jq / 16;
+  const uint32_t byte = live ? sc : 0u;
+  const bool even = (lane & 1) == 0 && in_row;
+  if constexpr (SFL == SF_ROWMAJOR) {
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, sr, even ? blk : kOob, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, sr, even ? (blk >> 2) * 512u + (blk & 3) : kOob, 0, 0);
+    if (even && blk == scale_cols - 1)
+      for (uint32_t c = scale_cols; c < scale_cols_padded; c++)
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)0, sr, (c >> 2) * 512u + (c & 3), 0, 0);
+  }
+}
+
+// A workgroup covers NV_GROUPS * 2048 consecutive operand columns of one row (a.H wide):
+// lane l takes 8 columns at l * 8 + g * 2048 for each group g, and issues the loads of all
+// its groups first.  Forward: the quantized matrix is h, [M, H].  Backward: it is
+// [da | db], [M, 2H]; the lane's da results go to column j, its db results to column H + j.
+// WORD_SCALES as for quant_store_bf16 (the backward needs H % 64 == 0 for it).
+template <int ACT, int LAYOUT, int SFL, int MODE, bool WORD_SCALES, int NV_GROUPS>
 __global__ __launch_bounds__(NV_THREADS) void k_nvfp4(NvArgs a, int64_t tiles_per_row,
-                                                      int64_t ntiles, int64_t scale_cols,
-                                                      int64_t scale_cols_padded) {
+                                                      int64_t ntiles, NvOut o) {
   const int lane = threadIdx.x & 63;
+  const uint32_t H = (uint32_t)a.H;
+  const uint32_t nb = (uint32_t)o.scale_cols, cp = (uint32_t)o.scale_cols_padded;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t row = t / tiles_per_row;
-    const int64_t j0 = (t - row * tiles_per_row) * (NV_TILE * NV_GROUPS) + (int64_t)threadIdx.x * 8;
+    const uint32_t j0 = (uint32_t)(t - row * tiles_per_row) * (uint32_t)(NV_TILE * NV_GROUPS) + threadIdx.x * 8u;
+    const bool row_ok = row < a.M;
+    const RowIn in = row_in<LAYOUT, MODE>(a, row_ok ? row : 0);
     Raw8 raw[NV_GROUPS];
 #pragma unroll
     for (int gi = 0; gi < NV_GROUPS; gi++) {
-      const int64_t j = j0 + gi * NV_TILE;
-      if (j < a.H && row < a.M) raw[gi] = load_raw<LAYOUT, F32>(a, row, j);
+      const uint32_t j = j0 + gi * (uint32_t)NV_TILE;
+      raw[gi] = load_raw<LAYOUT, MODE>(in, j, j < H && row_ok);
     }
+    __amdgpu_buffer_rsrc_t qr, sr;
+    row_out<SFL>(a, o, row, qr, sr);
 #pragma unroll
     for (int gi = 0; gi < NV_GROUPS; gi++) {
-      const int64_t j = j0 + gi * NV_TILE;
-      const bool in_row = j < a.H;  // pairs of lanes agree (H % 16 == 0)
-      const bool live = in_row && row < a.M;
-      float v[8];
-      if (live) {
-        values<ACT, LAYOUT, F32>(raw[gi], v);
+      const uint32_t j = j0 + gi * (uint32_t)NV_TILE;
+      const bool in_row = j < H;  // pairs (octets) of lanes agree: H % 16 == 0
+      const bool live = in_row && row_ok;
+      if constexpr (MODE == NV_F32) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          v[k] = __uint_as_float(raw[gi].A.w[k]);
+          v[4 + k] = __uint_as_float(raw[gi].B.w[k]);
+        }
+        quant_store_f32<SFL>(v, qr, sr, j, in_row, live, lane, nb, cp);
       } else {
-#pragma unroll
-        for (int k = 0; k < 8; k++) v[k] = 0.0f;
-      }
-
-      // block amax over the lane pair (all lanes take part in the exchange)
-      uint32_t m = __float_as_uint(v[0]) & 0x7fffffffu;
-#pragma unroll
-      for (int k = 1; k < 8; k++) m = umax(m, __float_as_uint(v[k]) & 0x7fffffffu);
-      m = umax(m, dpp<DPP_XOR1>(m));
-
-      const bool nonfinite = m >= 0x7f800000u;
-      const uint32_t sc = nonfinite ? 0x7fu : nv_scale_code(__uint_as_float(m));
-
-      if (live) {
-        uint32_t word = 0;
-        const float S = e4m3_value(nonfinite ? 0u : sc);
-        if constexpr (F32) {
-          // any FP32 value: exact threshold comparisons
-          const E2m1Thresholds T = e2m1_thresholds(S);
-#pragma unroll
-          for (int k = 0; k < 8; k++) word |= e2m1_code(v[k], T) << (4 * k);
-        } else {
-          // BF16 values: scaled operand + hardware convert
-          const float R = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
-          word = fp4x2<0>(word, e2m1_operand(v[0], R), e2m1_operand(v[1], R));
-          word = fp4x2<1>(word, e2m1_operand(v[2], R), e2m1_operand(v[3], R));
-          word = fp4x2<2>(word, e2m1_operand(v[4], R), e2m1_operand(v[5], R));
-          word = fp4x2<3>(word, e2m1_operand(v[6], R), e2m1_operand(v[7], R));
-        }
-        if (nonfinite) word = 0;
-        st4(a.q + row * (a.H / 2) + j / 2, word);
-      }
-      if (in_row && (lane & 1) == 0) {
-        const int64_t blk = j / 16;
-        const uint8_t byte = row < a.M ? (uint8_t)sc : (uint8_t)0;  // padding rows hold 0
-        if constexpr (SFL == SF_ROWMAJOR) {
-          a.sf[row * scale_cols + blk] = byte;
-        } else {
-          a.sf[sf128x4_offset(row, blk, scale_cols_padded)] = byte;
-          if (blk == scale_cols - 1)
-            for (int64_t c = scale_cols; c < scale_cols_padded; c++)
-              a.sf[sf128x4_offset(row, c, scale_cols_padded)] = 0;
-        }
+        uint32_t p[4], q[4];
+        glu_values<ACT, LAYOUT, MODE>(raw[gi], p, q);
+        // backward: with H % 64 != 0 the last da octet would reach into db's blocks
+        quant_store_bf16<SFL, WORD_SCALES>(p, qr, sr, j, in_row, live, lane, nb, cp);
+        if constexpr (MODE == NV_BWD)
+          quant_store_bf16<SFL, WORD_SCALES>(q, qr, sr, H + j, in_row, live, lane, nb, cp);
       }
     }
   }
 }
 
-template <int ACT, int LAYOUT, bool F32>
-hipError_t launch(const NvArgs& a, hipStream_t s) {
-  const int64_t nb = a.H / 16;
-  const int64_t cp = (nb + 3) / 4 * 4;
+template <int ACT, int LAYOUT, int MODE, int G>
+hipError_t launch_g(const NvArgs& a, hipStream_t s) {
+  const int64_t width = MODE == NV_BWD ? 2 * a.H : a.H;  // of the quantized matrix
+  const int64_t nb = width / 16;
+  const NvOut o{width / 2, nb, (nb + 3) / 4 * 4};
   const int64_t rows = a.sf_layout == SF_128x4 ? (a.M + 127) / 128 * 128 : a.M;
-  const int64_t tpr = (a.H + NV_TILE * NV_GROUPS - 1) / (NV_TILE * NV_GROUPS);
+  const int64_t tpr = (a.H + NV_TILE * G - 1) / (NV_TILE * G);
   const int64_t ntiles = rows * tpr;
   const dim3 grid(grid_for(ntiles, (int64_t)1 << 20)), block(NV_THREADS);
-  if (a.sf_layout == SF_128x4)
-    return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_128x4, F32>, grid, block, s, a, tpr, ntiles, nb, cp);
-  return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_ROWMAJOR, F32>, grid, block, s, a, tpr, ntiles, nb, cp);
+  const bool word = MODE != NV_BWD || a.H % 64 == 0;  // db's blocks start on a 4-block boundary
+  if (a.sf_layout == SF_128x4) {
+    if (word) return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_128x4, MODE, true, G>, grid, block, s, a, tpr, ntiles, o);
+    return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_128x4, MODE, false, G>, grid, block, s, a, tpr, ntiles, o);
+  }
+  return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_ROWMAJOR, MODE, true, G>, grid, block, s, a, tpr, ntiles, o);
+}
+
+// Groups per lane.  The backward takes 4 (more loads in flight per wave) when that still
+// leaves at least 16 workgroups per CU, else 2.
+template <int ACT, int LAYOUT, int MODE>
+hipError_t launch(const NvArgs& a, hipStream_t s) {
+  if constexpr (MODE == NV_BWD) {
+    const int64_t tiles4 = a.M * ((a.H + NV_TILE * 4 - 1) / (NV_TILE * 4));
+    if (tiles4 >= 16 * 256) return launch_g<ACT, LAYOUT, MODE, 4>(a, s);
+    return launch_g<ACT, LAYOUT, MODE, 2>(a, s);
+  } else {
+    return launch_g<ACT, LAYOUT, MODE, GLU_NV_GROUPS>(a, s);
+  }
 }
 
 }  // namespace
@@ -204,12 +363,19 @@ hipError_t launch(const NvArgs& a, hipStream_t s) {
 hipError_t launch_glu_fwd_nvfp4(const NvArgs& a, hipStream_t s) {
   return with_act(a.act, [&](auto A) {
     constexpr int ACT = decltype(A)::value;
-    return a.layout == PAIRED ? launch<ACT, PAIRED, false>(a, s) : launch<ACT, SPLIT, false>(a, s);
+    return a.layout == PAIRED ? launch<ACT, PAIRED, NV_FWD>(a, s) : launch<ACT, SPLIT, NV_FWD>(a, s);
+  });
+}
+
+hipError_t launch_glu_bwd_nvfp4(const NvArgs& a, hipStream_t s) {
+  return with_act(a.act, [&](auto A) {
+    constexpr int ACT = decltype(A)::value;
+    return launch<ACT, SPLIT, NV_BWD>(a, s);
   });
 }
 
 hipError_t launch_quant_nvfp4_f32(const NvArgs& a, hipStream_t s) {
-  return launch<SWIGLU, SPLIT, true>(a, s);
+  return launch<SWIGLU, SPLIT, NV_F32>(a, s);
 }
 
 }  // namespace glu

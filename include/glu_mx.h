@@ -155,16 +155,30 @@ glu_status glu_bwd_mxfp8(int act, int layout, int64_t M, int64_t N, const uint16
  * +-6; S == 0 gives signed-zero codes.  A block holding NaN or Inf gets scale 0x7F and
  * zero codes.  q is [M, H/2] bytes with element 2k in the low nibble of byte k; sf is
  * GLU_SF_ROWMAJOR [M, H/16] or GLU_SF_128x4 (see above).
- * Needs H % 16 == 0 and ld_in % 8 == 0. */
+ * Needs H % 16 == 0 and H <= 2^26 (GLU_ERR_SHAPE), ld_in % 8 == 0 (GLU_ERR_STRIDE). */
 glu_status glu_fwd_nvfp4(int act, int layout, int64_t M, int64_t H, const uint16_t* gate,
                          const uint16_t* up, int64_t ld_in, uint8_t* q, uint8_t* sf,
                          int sf_layout, void* stream);
 
+/* ---- Fused backward + NVFP4, global scale 1 (no page defines an NVFP4 backward: the
+ * placement is glu_bwd_mxfp8's, [MX] API; the block arithmetic is glu_fwd_nvfp4's, [NV]
+ * Supported contract).  The quantized matrix is X = [da | db], [M, 2N], with da, db as in
+ * glu_bwd and never written; 16-element row blocks never straddle da and db.  q is
+ * [M, N] bytes (2N codes per row, element 2k in the low nibble of byte k); sf is
+ * GLU_SF_ROWMAJOR [M, 2N/16] or GLU_SF_128x4 over [M, 2N/16] (glu_nvfp4_sf_bytes(M, 2N)).
+ * Only GLU_SPLIT is implemented (GLU_PAIRED -> GLU_ERR_UNSUPPORTED).  Needs N % 16 == 0
+ * and N <= 2^26 (GLU_ERR_SHAPE); ld_in, ld_dh multiples of 8 with ld_dh >= N
+ * (GLU_ERR_STRIDE). */
+glu_status glu_bwd_nvfp4(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                         const uint16_t* up, int64_t ld_in, const uint16_t* dh,
+                         int64_t ld_dh, uint8_t* q, uint8_t* sf, int sf_layout,
+                         void* stream);
+
 /* ---- Quantizer test hooks: the same device quantizer code, fed FP32 values
  * x is an FP32 [M, N] matrix with row stride ld_x (a multiple of 4; at most 2^23 for the
  * MXFP8 hook, whose output pitches are bounded as for glu_fwd_mxfp8).  Outputs and rules
- * exactly as glu_fwd_mxfp8 / glu_fwd_nvfp4 with x in place of h; every FP32 input is
- * quantized exactly (no intermediate rounding). */
+ * exactly as glu_fwd_mxfp8 / glu_fwd_nvfp4 with x in place of h (the NVFP4 hook also needs
+ * H <= 2^26); every FP32 input is quantized exactly (no intermediate rounding). */
 glu_status glu_quant_mxfp8_f32(int64_t M, int64_t N, const float* x, int64_t ld_x, int flags,
                                uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
                                uint8_t* s_col, void* stream);
@@ -191,6 +205,10 @@ glu_status glu_check_bwd_mxfp8(int act, int layout, int64_t M, int64_t N,
 glu_status glu_check_fwd_nvfp4(int act, int layout, int64_t M, int64_t H,
                                const uint16_t* gate, const uint16_t* up, int64_t ld_in,
                                uint8_t* q, uint8_t* sf, int sf_layout);
+glu_status glu_check_bwd_nvfp4(int act, int layout, int64_t M, int64_t N,
+                               const uint16_t* gate, const uint16_t* up, int64_t ld_in,
+                               const uint16_t* dh, int64_t ld_dh, uint8_t* q, uint8_t* sf,
+                               int sf_layout);
 glu_status glu_check_quant_mxfp8_f32(int64_t M, int64_t N, const float* x, int64_t ld_x,
                                      int flags, uint8_t* q_row, uint8_t* s_row,
                                      uint8_t* q_col, uint8_t* s_col);

@@ -189,6 +189,7 @@ def test_fwd_nvfp4_checks():
     assert nv() == OK and nv(sfl=1) == OK
     assert nv(sfl=2) == ARG
     assert nv(H=264, ld=528) == SHAPE                     # H % 16
+    assert nv(M=1, H=1 << 26, ld=1 << 27) == OK and nv(M=1, H=(1 << 26) + 16, ld=(1 << 27) + 32) == SHAPE
     assert nv(ld=516) == STRIDE and nv(ld=511) == STRIDE and nv(ld=520) == OK
     assert nv(q=0) == NULL and nv(sf=0) == NULL
     assert nv(layout=0, up=B0, ld=256) == OK
@@ -198,6 +199,30 @@ def test_fwd_nvfp4_checks():
     assert L.glu_nvfp4_sf_bytes(968, 16384, 1) == 1024 * 1024
     assert L.glu_nvfp4_sf_bytes(1, 80, 1) == 128 * 8
     assert L.glu_nvfp4_sf_bytes(1, 81, 0) == -1
+
+
+def nvb(**kw):
+    a = dict(act=0, layout=0, M=100, N=256, gate=A0, up=B0, ld=256, dh=C0, lddh=256, q=D0, sf=E0, sfl=0)
+    a.update(kw)
+    return L.glu_check_bwd_nvfp4(a["act"], a["layout"], a["M"], a["N"], P(a["gate"]), P(a["up"]),
+                                 a["ld"], P(a["dh"]), a["lddh"], P(a["q"]), P(a["sf"]), a["sfl"])
+
+
+def test_bwd_nvfp4_checks():
+    assert nvb() == OK and nvb(sfl=1) == OK and nvb(act=3) == OK
+    assert nvb(sfl=2) == ARG and nvb(act=4) == ARG
+    assert nvb(layout=1, up=0) == UNSUP
+    assert nvb(M=0) == OK and nvb(N=0) == OK and nvb(M=-1) == SHAPE
+    assert nvb(N=264, ld=264, lddh=264) == SHAPE                       # N % 16
+    assert nvb(dh=0) == NULL and nvb(q=0) == NULL and nvb(sf=0) == NULL and nvb(up=0) == NULL
+    assert nvb(lddh=248) == STRIDE and nvb(lddh=260) == STRIDE and nvb(ld=252) == STRIDE
+    assert nvb(dh=C0 + 8) == ALIGN and nvb(q=D0 + 4) == ALIGN
+    assert nvb(q=C0 + 64) == OVERLAP                                    # codes over dh
+    assert nvb(sf=D0 + 100 * 256 - 16) == OVERLAP                       # scales over the codes' end
+    assert nvb(sf=D0 + 100 * 256) == OK                                 # q is [M, N] bytes
+    assert nvb(N=1 << 62, ld=1 << 62, lddh=1 << 62) == SHAPE            # 2N overflows
+    assert nvb(M=1, N=1 << 26, ld=1 << 26, lddh=1 << 26) == OK
+    assert nvb(M=1, N=(1 << 26) + 16, ld=(1 << 26) + 16, lddh=(1 << 26) + 16) == SHAPE
 
 
 def test_quant_hook_checks():
@@ -222,6 +247,8 @@ def test_entry_points_fail_before_any_hip_call():
     assert L.glu_fwd_mxfp8(0, 0, 64, 40, P(A0), P(B0), 40, 1, P(C0), P(D0), P(0), P(0), P(0)) == SHAPE
     assert L.glu_bwd_mxfp8(0, 1, 64, 64, P(A0), P(0), 128, P(C0), 64, 1, P(D0), P(E0), P(0), P(0), P(0)) == UNSUP
     assert L.glu_fwd_nvfp4(1, 1, 8, 24, P(A0), P(0), 48, P(C0), P(D0), 0, P(0)) == SHAPE
+    assert L.glu_bwd_nvfp4(0, 0, 8, 24, P(A0), P(B0), 24, P(C0), 24, P(D0), P(E0), 0, P(0)) == SHAPE
+    assert L.glu_bwd_nvfp4(0, 0, 0, 32, P(0), P(0), 32, P(0), 32, P(0), P(0), 0, P(0)) == OK
     assert L.glu_quant_mxfp8_f32(32, 32, P(A0), 32, 8, P(B0), P(C0), P(D0), P(E0), P(0)) == ARG
     assert L.glu_quant_nvfp4_f32(32, 32, P(A0 + 4), 32, P(B0), P(C0), 0, P(0)) == ALIGN
 

@@ -5,6 +5,9 @@ tie-dense, all-BF16 and non-finite inputs, in both scale layouts; the fused kern
 the oracle quantizer applied to the GPU's own BF16 glu_fwd output.
 Rule 3: the GeGLU NVFP4 workload ([M, 32768] interleaved, M in {784, 816, 880, 968}) end to
 end against the oracle, plus the zero padding of the 128x4 scale layout.
+Backward ([da | db] as one [M, 2N] NVFP4 matrix): rule 1 against the oracle quantizer on the
+GPU's own glu_bwd output for every activation and both scale layouts, rule 3 end to end,
+ragged widths and rows, and the binding's refusal of mis-shaped buffers.
 """
 import numpy as np
 import pytest
@@ -112,3 +115,106 @@ def test_config_geglu_nvfp4(gpu, M):
             pad = np.array([oracle.sf128x4_offset(r, c, cp) for r in range(M, rp) for c in range(0, nb, 31)], dtype=np.int64)
             if pad.size:
                 assert not np.any(s[pad]), "128x4 padding rows must be zero"
+
+
+ACTS = [("swiglu", oracle.SWIGLU), ("geglu", oracle.GEGLU_TANH), ("geglu_erf", oracle.GEGLU_ERF),
+        ("relu2", oracle.RELU2)]
+
+
+@pytest.mark.parametrize("act,kind", ACTS)
+@pytest.mark.parametrize("M,N", [(130, 1024), (5, 48), (37, 2064), (4096, 96)])
+def test_fused_bwd_equals_quantized_glu_bwd(gpu, act, kind, M, N):
+    """Small launches take 2 column groups per lane, [4096, 96] takes 4."""
+    gate, up, dh = si.glu_operands(M, N, seed=M + N + kind, outliers=True, with_dh=True)
+    gd, ud, dd = gate.cuda(), up.cuda(), dh.cuda()
+    da, db = gpu.glu_bwd(gd, ud, dd, act=act)
+    X = si.from_bits(np.concatenate([bits(da), bits(db)], axis=1)).float().numpy()
+    for name, code in SFL:
+        q, sf = gpu.glu_bwd_nvfp4(gd, ud, dd, act=act, sf_layout=name)
+        oq, osf = oracle.quant_nvfp4(X, code)
+        assert np.array_equal(u8(sf).ravel(), osf.ravel()), f"scales ({name})"
+        assert np.array_equal(u8(q), oq), f"codes ({name})"
+
+
+@pytest.mark.parametrize("act,kind", ACTS)
+def test_bwd_rule3_against_oracle(gpu, act, kind):
+    M, N = 512, 4096
+    gate, up, dh = si.glu_operands(M, N, seed=40 + kind, outliers=True, with_dh=True)
+    gb, ub, db_ = bits(gate), bits(up), bits(dh)
+    q, sf = gpu.glu_bwd_nvfp4(gate.cuda(), up.cuda(), dh.cuda(), act=act)
+    oq, osf = oracle.glu_bwd_nvfp4(kind, gb, ub, db_)
+    oa, ob = oracle.glu_bwd(kind, gb, ub, db_)
+    check_rule3_nv(np.concatenate([oa, ob], 1), u8(q), u8(sf), oq, osf, f"{act} bwd")
+
+
+def test_bwd_strided_operands(gpu):
+    """gate/up rows inside a wider [gate | up] matrix, dh with a padded row stride."""
+    M, N = 64, 512
+    gate, up, dh = si.glu_operands(M, N, seed=44, with_dh=True)
+    cat = torch.cat([gate, up], 1).cuda()
+    dpad = torch.zeros(M, N + 64, dtype=torch.bfloat16, device="cuda")
+    dpad[:, :N] = dh.cuda()
+    q, sf = gpu.glu_bwd_nvfp4(cat[:, :N], cat[:, N:], dpad[:, :N])
+    oq, osf = oracle.glu_bwd_nvfp4(oracle.SWIGLU, bits(gate), bits(up), bits(dh))
+    oa, ob = oracle.glu_bwd(oracle.SWIGLU, bits(gate), bits(up), bits(dh))
+    check_rule3_nv(np.concatenate([oa, ob], 1), u8(q), u8(sf), oq, osf, "strided bwd")
+
+
+def test_binding_rejects_misshaped_buffers(gpu):
+    """Buffers that do not match the operands raise before any launch."""
+    gate, up, dh = (t.cuda() for t in si.glu_operands(32, 64, seed=45, with_dh=True))
+    with pytest.raises(ValueError):
+        gpu.glu_bwd_nvfp4(gate, up, dh[:16])
+    q = torch.empty((32, 64), dtype=torch.uint8, device="cuda")
+    sf = torch.empty((32, 8), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        gpu.glu_bwd_nvfp4(gate, up, dh, out=(q[:16], sf))
+    with pytest.raises(ValueError):
+        gpu.glu_bwd_nvfp4(gate, up, dh, out=(q, sf[:, :4]))
+    with pytest.raises(ValueError):
+        gpu.glu_fwd(gate, up, out=torch.empty((16, 64), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        gpu.glu_bwd(gate, up, dh[:, :32])
+    qr = torch.empty((32, 32), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        gpu.glu_fwd_mxfp8(gate, up, rowwise=True, out=(qr, torch.empty(0), torch.empty((32, 2)), torch.empty(0)))
+    gpu.glu_bwd_nvfp4(gate, up, dh, out=(q, sf))   # the right shapes are accepted
+
+
+def test_every_bf16_block_amax(gpu):
+    """The fused path's scale decision for every normal BF16 block maximum: gate = 32 makes
+    silu(32) * up round to exactly 32 * up in FP32, so up = a / 32 puts h = a at the head of
+    a block, followed by 15 smaller random values (mixed signs)."""
+    b = np.arange(0x0380, 0x7F80, dtype=np.uint32)   # a / 32 stays a normal BF16 number
+    a = (b << 16).view(np.float32)
+    rng = np.random.default_rng(46)
+    n = a.size
+    blocks = np.empty((n, 16), np.float32)
+    blocks[:, 0] = a
+    blocks[:, 1:] = a[:, None] * rng.uniform(-0.99, 0.99, (n, 15)).astype(np.float32)
+    pad = (-n) % 16
+    blocks = np.concatenate([blocks, np.ones((pad, 16), np.float32)])
+    up = torch.from_numpy(blocks.reshape(-1, 256) / np.float32(32.0)).to(torch.bfloat16)
+    gate = torch.full_like(up, 32.0)
+    gd, ud = gate.cuda(), up.cuda()
+    h = bits(gpu.glu_fwd(gd, ud, act="swiglu"))
+    assert np.array_equal(h.reshape(-1, 16)[:n, 0], b.astype(np.uint16)), "h = a at each block head"
+    hf = si.from_bits(h).float().numpy()
+    for name, code in SFL:
+        q, sf = gpu.glu_fwd_nvfp4(gd, ud, act="swiglu", layout="split", sf_layout=name)
+        oq, osf = oracle.quant_nvfp4(hf, code)
+        assert np.array_equal(u8(sf).ravel(), osf.ravel()), f"scales ({name})"
+        assert np.array_equal(u8(q), oq), f"codes ({name})"
+
+
+def test_bwd_four_groups_ragged_tile(gpu):
+    """[4160, 8208]: 4 column groups per lane, with a second tile holding 16 live columns."""
+    M, N = 4160, 8208
+    g, u, d = si.normal_bf16_device([(M, N)] * 3, seed=47, outliers=True)
+    da, db = gpu.glu_bwd(g, u, d)
+    X = si.from_bits(np.concatenate([bits(da), bits(db)], axis=1)).float().numpy()
+    for name, code in SFL:
+        q, sf = gpu.glu_bwd_nvfp4(g, u, d, sf_layout=name)
+        oq, osf = oracle.quant_nvfp4(X, code)
+        assert np.array_equal(u8(sf).ravel(), osf.ravel()), f"scales ({name})"
+        assert np.array_equal(u8(q), oq), f"codes ({name})"
