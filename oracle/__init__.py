@@ -48,6 +48,10 @@ _SIGNATURES = {
     "orc_glu_bwd_mxfp8": (_int, [_int, _i64, _i64, _p, _p, _i64, _p, _i64, _int, _p, _p, _p, _p]),
     "orc_glu_fwd_nvfp4": (_int, [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int]),
     "orc_glu_bwd_nvfp4": (_int, [_int, _i64, _i64, _p, _p, _i64, _p, _i64, _p, _p, _int]),
+    "orc_nvfp4_global_scale": (ctypes.c_float, [ctypes.c_float]),
+    "orc_quant_nvfp4_gs": (None, [_i64, _i64, _p, ctypes.c_float, _p, _p, _int]),
+    "orc_glu_amax": (ctypes.c_float, [_int, _int, _i64, _i64, _p, _p, _i64, _p]),
+    "orc_glu_fwd_nvfp4_gs": (_int, [_int, _int, _i64, _i64, _p, _p, _i64, ctypes.c_float, _p, _p, _int]),
     "orc_bf16_from_f64_array": (None, [_p, _i64, _p]),
     "orc_e4m3_from_f64_array": (None, [_p, _i64, _p]),
     "orc_e2m1_from_f64_array": (None, [_p, _i64, _p]),
@@ -282,6 +286,42 @@ def glu_bwd_nvfp4(kind, gate, up, dh, sf_layout=SF_ROWMAJOR):
     sf = np.empty(sf128x4_bytes(M, 2 * N) if sf_layout == SF_128x4 else (M, 2 * N // 16), np.uint8)
     rc = _load().orc_glu_bwd_nvfp4(kind, M, N, _ptr(gate), _ptr(up), ld, _ptr(dh), N, _ptr(q), _ptr(sf),
                                    sf_layout)
+    if rc != 0:
+        raise MemoryError("oracle ran out of host memory")
+    return q, sf
+
+
+# ---- two-level NVFP4 (global scale from the tensor's amax) ----------------------
+
+def nvfp4_global_scale(amax):
+    return float(_load().orc_nvfp4_global_scale(float(amax)))
+
+
+def quant_nvfp4_gs(x, amax, sf_layout=SF_ROWMAJOR):
+    """x float32 [M, H], FP32 amax -> (q [M, H/2] packed E2M1, sf E4M3 scales)."""
+    x = _c(x, np.float32)
+    M, H = x.shape
+    q = np.empty((M, H // 2), np.uint8)
+    sf = np.empty(sf128x4_bytes(M, H) if sf_layout == SF_128x4 else (M, H // 16), np.uint8)
+    _load().orc_quant_nvfp4_gs(M, H, _ptr(x), float(amax), _ptr(q), _ptr(sf), sf_layout)
+    return q, sf
+
+
+def glu_amax(kind, gate, up=None, layout=SPLIT):
+    gate, up, M, N, ld = _operands(layout, gate, up)
+    ok = ctypes.c_int(0)
+    a = _load().orc_glu_amax(kind, layout, M, N, _ptr(gate), _ptr(up), ld, ctypes.byref(ok))
+    if ok.value != 0:
+        raise MemoryError("oracle ran out of host memory")
+    return float(a)
+
+
+def glu_fwd_nvfp4_gs(kind, gate, up=None, amax=None, layout=PAIRED, sf_layout=SF_ROWMAJOR):
+    gate, up, M, H, ld = _operands(layout, gate, up)
+    q = np.empty((M, H // 2), np.uint8)
+    sf = np.empty(sf128x4_bytes(M, H) if sf_layout == SF_128x4 else (M, H // 16), np.uint8)
+    rc = _load().orc_glu_fwd_nvfp4_gs(kind, layout, M, H, _ptr(gate), _ptr(up), ld, float(amax), _ptr(q),
+                                      _ptr(sf), sf_layout)
     if rc != 0:
         raise MemoryError("oracle ran out of host memory")
     return q, sf

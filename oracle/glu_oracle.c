@@ -46,7 +46,10 @@
  *   - MXFP8 scales may also be asked for in the same zero-padded 128x4 layout
  *     (the GEMM-ready block-scale layout; no page fixes one for MXFP8);
  *   - an NVFP4 backward quantizes [da | db] as one [M, 2N] matrix in 16-element
- *     row blocks, the MXFP8 backward's placement (no page defines one).
+ *     row blocks, the MXFP8 backward's placement (no page defines one);
+ *   - two-level NVFP4 (a global scale from the tensor's amax, relaxing [NV]'s global
+ *     scale 1) is defined by IEEE FP32 operations: s = 2688 / amax, block scale
+ *     E4M3(bamax * fl(s / 6)), codes E2M1(x * fl(s / S)).
  * Parity unpinned: the NaN/Inf block rule, the nibble order, and the 128x4
  * scale layout beyond its being a zero-padded permutation.  No page prints a
  * value for any of them.
@@ -431,6 +434,66 @@ void orc_quant_nvfp4(int64_t M, int64_t H, const float* X, uint8_t* q, uint8_t* 
 }
 
 /* ------------------------------------------------------------------------- */
+/* NVFP4 with a global scale (two-level scaling).  [NV] Supported contract fixes */
+/* global scale 1; this is the relaxation real recipes use, by reading: every   */
+/* step below is one IEEE FP32 operation, as the kernels take it.               */
+/* ------------------------------------------------------------------------- */
+
+/* Global encode scale: 448 * 6 / amax in FP32, so that the block holding the tensor's
+ * amax gets (about) the largest E4M3 scale; 1 when amax is zero, negative or not finite. */
+float orc_nvfp4_global_scale(float amax) {
+  if (!(amax > 0.0f) || !isfinite(amax)) return 1.0f;
+  return 2688.0f / amax;
+}
+
+/* One block of 16 FP32 values at global encode scale s (k = fl(s / 6)):
+ *   scale code = E4M3(fl(bamax * k)), nearest even, saturating at 448;
+ *   codes      = E2M1(fl(x * r)), r = fl(s / S) with S the scale code's value (r = 0
+ *                when S = 0, giving signed zeros), nearest even, saturating at 6;
+ * a block holding NaN or Inf gets scale 0x7F and zero codes, as with global scale 1. */
+static void nv_block_gs(const float* v, float s, float k, uint8_t* codes, uint8_t* scale) {
+  float amax = 0.0f;
+  for (int i = 0; i < 16; i++) {
+    if (!isfinite(v[i])) {
+      *scale = 0x7F;
+      memset(codes, 0, 16);
+      return;
+    }
+    if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+  }
+  const float d = amax * k;
+  const uint8_t sc = orc_e4m3_from_f64((double)d);
+  const float S = (float)orc_e4m3_to_f64(sc);
+  const float r = S == 0.0f ? 0.0f : s / S;
+  *scale = sc;
+  for (int i = 0; i < 16; i++) {
+    const float y = v[i] * r;
+    codes[i] = orc_e2m1_from_f64((double)y);
+  }
+}
+
+/* As orc_quant_nvfp4, with the global encode scale of `amax`. */
+void orc_quant_nvfp4_gs(int64_t M, int64_t H, const float* X, float amax, uint8_t* q,
+                        uint8_t* sf, int sf_layout) {
+  const float s = orc_nvfp4_global_scale(amax);
+  const float k = s / 6.0f;
+  int64_t nb = H / 16;
+  int64_t cols_padded = (nb + 3) / 4 * 4;
+  int64_t rows_padded = (M + 127) / 128 * 128;
+  if (sf_layout == ORC_SF_128x4) memset(sf, 0, (size_t)(rows_padded * cols_padded));
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; m++)
+    for (int64_t b = 0; b < nb; b++) {
+      uint8_t c[16], sc;
+      nv_block_gs(&X[m * H + 16 * b], s, k, c, &sc);
+      for (int j = 0; j < 8; j++)
+        q[m * (H / 2) + 8 * b + j] = (uint8_t)(c[2 * j] | (c[2 * j + 1] << 4));
+      if (sf_layout == ORC_SF_128x4) sf[orc_sf128x4_offset(m, b, cols_padded)] = sc;
+      else sf[m * nb + b] = sc;
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* Fused paths = GLU (one BF16 rounding) followed by the quantizer             */
 /* ([MX] Numerics and tests: equal to the activation then the quantizers)      */
 /* ------------------------------------------------------------------------- */
@@ -501,6 +564,41 @@ int orc_glu_bwd_nvfp4(int act, int64_t M, int64_t N, const uint16_t* gate,
   free(d);
   if (!x) return -1;
   orc_quant_nvfp4(M, 2 * N, x, q, sf, sf_layout);
+  free(x);
+  return 0;
+}
+
+/* Largest |h| of h = bf16(act(gate) * up) over [M, N]: NaN if some h is NaN.  The amax
+ * pass of two-level NVFP4 scaling.  Returns -1 in *ok if host memory ran out. */
+float orc_glu_amax(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                   const uint16_t* up, int64_t ld, int* ok) {
+  uint16_t* h = (uint16_t*)malloc((size_t)(M * N) * sizeof(uint16_t));
+  *ok = h ? 0 : -1;
+  if (!h) return 0.0f;
+  orc_glu_fwd(act, layout, M, N, gate, up, ld, h, N);
+  float amax = 0.0f;
+  int nan = 0;
+  for (int64_t i = 0; i < M * N; i++) {
+    const float a = fabsf((float)orc_bf16_to_f64(h[i]));
+    if (isnan(a)) nan = 1;
+    else if (a > amax) amax = a;
+  }
+  free(h);
+  return nan ? NAN : amax;
+}
+
+/* Fused forward with two-level NVFP4 scaling: h as orc_glu_fwd, quantized with the global
+ * encode scale of the given amax (normally orc_glu_amax of the same operands). */
+int orc_glu_fwd_nvfp4_gs(int act, int layout, int64_t M, int64_t H, const uint16_t* gate,
+                         const uint16_t* up, int64_t ld, float amax, uint8_t* q, uint8_t* sf,
+                         int sf_layout) {
+  uint16_t* h = (uint16_t*)malloc((size_t)(M * H) * sizeof(uint16_t));
+  if (!h) return -1;
+  orc_glu_fwd(act, layout, M, H, gate, up, ld, h, H);
+  float* x = widen_bf16(h, M * H);
+  free(h);
+  if (!x) return -1;
+  orc_quant_nvfp4_gs(M, H, x, amax, q, sf, sf_layout);
   free(x);
   return 0;
 }

@@ -247,3 +247,101 @@ def test_fused_equals_glu_then_quantizer():
         a = oracle.glu_fwd_nvfp4(kind, paired, None)
         b = oracle.quant_nvfp4(hf)
         assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+# ---- two-level NVFP4 (global scale from the tensor's amax) -------------------------
+
+def _e4m3_table():
+    """Magnitudes of E4M3 codes 0..126 from the format definition (bias 7, 3 mantissa bits,
+    subnormals m * 2^-9; 0x7F is NaN)."""
+    return np.array([(c & 7) * 2.0 ** -9 if c >> 3 == 0 else (1 + (c & 7) / 8) * 2.0 ** ((c >> 3) - 7)
+                     for c in range(0x7F)])
+
+
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _nearest_even(y, table):
+    """Brute force: the code of the nearest magnitude, ties to the even code (saturates)."""
+    d = np.abs(table - abs(float(y)))
+    c = np.nonzero(d == d.min())[0]
+    return int(c[0]) if c.size == 1 or c[0] % 2 == 0 else int(c[1])
+
+
+def _nv_gs_block_ref(v, s):
+    """The two-level reading restated with numpy FP32 operations and brute-force rounding."""
+    f32 = np.float32
+    v = v.astype(np.float32)
+    k = f32(f32(s) / f32(6.0))
+    d = f32(np.abs(v).max() * k)
+    sc = _nearest_even(d, _e4m3_table())
+    S = f32(_e4m3_table()[sc])
+    r = f32(0.0) if S == 0 else f32(f32(s) / S)
+    codes = []
+    for x in v:
+        y = f32(x * r)
+        codes.append((8 if np.signbit(y) else 0) | _nearest_even(y, _E2M1))
+    return sc, codes
+
+
+def test_nv_global_scale_closed_forms():
+    gs = oracle.nvfp4_global_scale
+    assert gs(2688.0) == 1.0 and gs(1.0) == 2688.0 and gs(3.0) == 896.0 and gs(0.5) == 5376.0
+    assert gs(0.0) == 1.0 and gs(-2.0) == 1.0 and gs(float("inf")) == 1.0 and gs(float("nan")) == 1.0
+    assert gs(7.0) == float(np.float32(2688.0) / np.float32(7.0))
+
+
+def test_nv_gs_blocks_against_brute_force():
+    """Random blocks (several magnitudes, ties planted) at the true amax, at amax x 8 (small
+    scales) and at amax / 8 (saturating scales and codes)."""
+    rng = np.random.default_rng(48)
+    X = (rng.standard_normal((24, 64)) * np.exp2(rng.integers(-20, 20, (24, 1)))).astype(np.float32)
+    X[3, :16] = np.float32(0.75) * np.arange(16, dtype=np.float32)   # multiples of a tie step
+    X[5, 16:32] = 0.0
+    amax = float(np.abs(X).max())
+    for a in (amax, amax * 8, amax / 8, 1.0):
+        q, sf = oracle.quant_nvfp4_gs(X, a)
+        s = oracle.nvfp4_global_scale(a)
+        codes = np.empty((24, 64), np.uint8)
+        codes[:, 0::2], codes[:, 1::2] = q & 0xF, q >> 4
+        for r in range(24):
+            for b in range(4):
+                sc, c = _nv_gs_block_ref(X[r, 16 * b:16 * b + 16], s)
+                assert sf[r, b] == sc, (a, r, b)
+                assert list(codes[r, 16 * b:16 * b + 16]) == c, (a, r, b)
+
+
+def test_nv_gs_power_of_two_invariance_and_top_scale():
+    """Scaling the data and amax by 2^j changes nothing (every step is exact in 2^j); with a
+    power-of-two amax the block holding it gets the top scale 448 (code 0x7E)."""
+    rng = np.random.default_rng(49)
+    X = rng.standard_normal((16, 128)).astype(np.float32)
+    X[0, 5] = 8.0
+    X = np.clip(X, -7.9, 7.9)
+    X[0, 5] = 8.0
+    base = oracle.quant_nvfp4_gs(X, 8.0)
+    assert base[1][0, 0] == 0x7E
+    for j in (-12, -3, 5, 30):
+        q, sf = oracle.quant_nvfp4_gs(X * np.float32(2.0 ** j), 8.0 * 2.0 ** j)
+        assert np.array_equal(q, base[0]) and np.array_equal(sf, base[1]), j
+    q, sf = oracle.quant_nvfp4_gs(X, 8.0, oracle.SF_128x4)
+    assert np.array_equal(q, base[0])
+    _unswizzle_check(sf, base[1])
+
+
+def test_glu_amax_and_fused_gs():
+    """glu_amax is the largest |h| of the BF16 forward (NaN dominates); the fused two-level
+    forward is the quantizer applied to that forward."""
+    gate, up = si.glu_operands(40, 96, seed=50, outliers=True)
+    gb, ub = si.to_bits(gate), si.to_bits(up)
+    h = oracle.bf16_to_f64(oracle.glu_fwd(oracle.GEGLU_TANH, gb, ub))
+    a = oracle.glu_amax(oracle.GEGLU_TANH, gb, ub)
+    assert a == np.abs(h).max()
+    x = h.astype(np.float32)
+    for code in (oracle.SF_ROWMAJOR, oracle.SF_128x4):
+        got = oracle.glu_fwd_nvfp4_gs(oracle.GEGLU_TANH, gb, ub, amax=a, layout=oracle.SPLIT, sf_layout=code)
+        want = oracle.quant_nvfp4_gs(x, a, code)
+        assert all(np.array_equal(p, w) for p, w in zip(got, want))
+    gb2 = gb.copy()
+    gb2[7, 9] = 0x7FC0   # NaN gate
+    assert np.isnan(oracle.glu_amax(oracle.GEGLU_TANH, gb2, ub))
