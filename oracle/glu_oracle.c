@@ -48,8 +48,8 @@
  *   - an NVFP4 backward quantizes [da | db] as one [M, 2N] matrix in 16-element
  *     row blocks, the MXFP8 backward's placement (no page defines one);
  *   - two-level NVFP4 (a global scale from the tensor's amax, relaxing [NV]'s global
- *     scale 1) is defined by IEEE FP32 operations: s = 2688 / amax, block scale
- *     E4M3(bamax * fl(s / 6)), codes E2M1(x * fl(s / S)).
+ *     scale 1) is defined by IEEE FP32 operations: s = 2688 / amax (capped at
+ *     2^100), block scale E4M3(bamax * fl(s / 6)), codes E2M1(x * fl(s / S)).
  * Parity unpinned: the NaN/Inf block rule, the nibble order, and the 128x4
  * scale layout beyond its being a zero-padded permutation.  No page prints a
  * value for any of them.
@@ -440,10 +440,13 @@ void orc_quant_nvfp4(int64_t M, int64_t H, const float* X, uint8_t* q, uint8_t* 
 /* ------------------------------------------------------------------------- */
 
 /* Global encode scale: 448 * 6 / amax in FP32, so that the block holding the tensor's
- * amax gets (about) the largest E4M3 scale; 1 when amax is zero, negative or not finite. */
+ * amax gets (about) the largest E4M3 scale; 1 when amax is zero, negative or not finite.
+ * Capped at 2^100 (amax below about 2^-89): then s / S and x * s / S stay finite for
+ * every E4M3 scale S >= 2^-9 and every x up to amax. */
 float orc_nvfp4_global_scale(float amax) {
   if (!(amax > 0.0f) || !isfinite(amax)) return 1.0f;
-  return 2688.0f / amax;
+  const float s = 2688.0f / amax;
+  return s < 0x1p100f ? s : 0x1p100f;
 }
 
 /* One block of 16 FP32 values at global encode scale s (k = fl(s / 6)):

@@ -289,6 +289,8 @@ def test_nv_global_scale_closed_forms():
     assert gs(2688.0) == 1.0 and gs(1.0) == 2688.0 and gs(3.0) == 896.0 and gs(0.5) == 5376.0
     assert gs(0.0) == 1.0 and gs(-2.0) == 1.0 and gs(float("inf")) == 1.0 and gs(float("nan")) == 1.0
     assert gs(7.0) == float(np.float32(2688.0) / np.float32(7.0))
+    assert gs(2.0 ** -90) == 2.0 ** 100 and gs(2.0 ** -120) == 2.0 ** 100      # capped
+    assert gs(2.0 ** -80) == 2688.0 * 2.0 ** 80
 
 
 def test_nv_gs_blocks_against_brute_force():
