@@ -71,7 +71,7 @@ MUTANTS = [
      "orc_glu_bwd(act, ORC_SPLIT, M, N, gate, up, ld, dh, lddh, d, d + N, 2 * N);\n  float* x = widen_bf16(d, M * 2 * N);\n  free(d);\n  if (!x) return -1;\n  orc_quant_nvfp4",
      "orc_glu_bwd(act, ORC_SPLIT, M, N, gate, up, ld, dh, lddh, d + N, d, 2 * N);\n  float* x = widen_bf16(d, M * 2 * N);\n  free(d);\n  if (!x) return -1;\n  orc_quant_nvfp4",
      [tq.test_nv_backward_is_da_then_db]),
-    ("NV global scale drops the 6", "return 2688.0f / amax;", "return 448.0f / amax;",
+    ("NV global scale drops the 6", "const float s = 2688.0f / amax;", "const float s = 448.0f / amax;",
      [tq.test_nv_global_scale_closed_forms]),
     ("NV two-level block scale ignores the 6", "const float d = amax * k;", "const float d = amax * s;",
      [tq.test_nv_gs_blocks_against_brute_force]),
