@@ -14,8 +14,8 @@ Also reported on the same JSON line:
   cpu_baseline  - the CPU oracle on a bounded row sample of the same workload;
   sweep         - every workload shape of the pages (MXFP8 SwiGLU fwd/bwd per direction,
                   GeGLU BF16 fwd/bwd, GeGLU NVFP4), median of cold launches, plus the
-                  other activations (tanh-GeGLU, erf-GeGLU, ReLU^2) at one shape of each
-                  and the NVFP4 backward.
+                  other activations (tanh-GeGLU, erf-GeGLU, ReLU^2) at one shape of each,
+                  the NVFP4 backward, and two-level NVFP4 (amax pass + forward).
 Only one GPU is supported; --gpus above 1 exits with a message.
 """
 import argparse
@@ -200,6 +200,19 @@ def sweep(torch, glu, si, iters):
                                                                          sf_layout="128x4", out=out) for x in sets], iters)
                 rec(f"{act}_nvfp4_fwd_{M}x{H}", nv_bytes(M, H), t)
         del sets, out
+    # two-level NVFP4: the amax pass and the forward with the global scale
+    for M, H in ((968, 16384), (16384, 7168)):
+        sets = [si.normal_bf16_device([(M, 2 * H)], seed=M + s)[0] for s in range(n_sets(4 * M * H))]
+        out = glu._nv_buffers(M, H, "128x4", "cuda", None)
+        amax = torch.empty((1,), dtype=torch.float32, device="cuda")
+        t = time_launches(torch, [lambda x=x: glu.glu_amax(x, act="geglu", layout="paired", out=amax)
+                                  for x in sets], iters)
+        rec(f"geglu_amax_{M}x{H}", 4 * M * H, t)
+        t = time_launches(torch, [lambda x=x: glu.glu_fwd_nvfp4_gs(x, amax=amax, act="geglu", layout="paired",
+                                                                    sf_layout="128x4", out=out) for x in sets], iters)
+        rec(f"geglu_nvfp4_gs_fwd_{M}x{H}", nv_bytes(M, H), t)
+        del sets, out
+        torch.cuda.empty_cache()
     # NVFP4 backward ([da | db] quantized), the workload's shape and the MXFP8 training shape
     for M, N in ((968, 16384), (16384, 7168)):
         sets = [si.normal_bf16_device([(M, N)] * 3, seed=M + N + s) for s in range(n_sets(6 * M * N))]
@@ -244,6 +257,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch one 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--nvfp4-only", action="store_true",
+                    help="only launch the NVFP4 forward and backward at [16384, 7168] three times "
+                         "each and print no JSON (a target for profiler counter passes)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path needs no collective and runs one "
@@ -260,6 +276,17 @@ def main():
     glu.lib()  # fail loudly when the HIP library is missing
 
     M, N = 16384, 7168
+    if args.nvfp4_only:
+        g, u, d = si.normal_bf16_device([(M, N)] * 3, seed=1, outliers=True)
+        x = torch.stack([g, u], 2).reshape(M, 2 * N).contiguous()
+        of = glu._nv_buffers(M, N, "128x4", "cuda", None)
+        ob = glu._nv_buffers(M, 2 * N, "128x4", "cuda", None)
+        for _ in range(3):
+            glu.glu_fwd_nvfp4(x, act="swiglu", layout="paired", sf_layout="128x4", out=of)
+            glu.glu_bwd_nvfp4(g, u, d, act="swiglu", sf_layout="128x4", out=ob)
+        torch.cuda.synchronize()
+        print("[bench] nvfp4 launches done", file=sys.stderr, flush=True)
+        return
     sets = [si.normal_bf16_device([(M, N)] * 3, seed=s, outliers=True) for s in range(2)]
     fo = glu._mx_buffers(M, N, True, True, "cuda", None)
     bo = glu._mx_buffers(M, 2 * N, True, True, "cuda", None)

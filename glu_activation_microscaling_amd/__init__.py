@@ -12,6 +12,8 @@ Entry points (C names in include/glu_mx.h):
   glu_bwd_mxfp8(gate, up, dh, rowwise=, colwise=, ...)      -> (q_row, q_col, s_row, s_col)
   glu_fwd_nvfp4(x, up=None, layout="paired", sf_layout=...) -> (q, sf)
   glu_bwd_nvfp4(gate, up, dh, sf_layout=...)                -> (q, sf) of [da | db]
+  glu_amax(gate, up=None, layout=...)                        -> amax, float32 [1] on the GPU
+  glu_fwd_nvfp4_gs(x, up=None, amax=, layout=, sf_layout=)   -> (q, sf), two-level scaling
   glu_quant_mxfp8_f32(x, rowwise=, colwise=)                -> (q_row, q_col, s_row, s_col)
   glu_quant_nvfp4_f32(x, sf_layout=)                        -> (q, sf)
 A disabled MXFP8 direction comes back as zero-sized tensors (fixed arity), as in the
@@ -43,6 +45,8 @@ _SIGNATURES = {
     "glu_bwd_mxfp8": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _int, _p, _p, _p, _p, _p],
     "glu_fwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int, _p],
     "glu_bwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _p, _p, _int, _p],
+    "glu_amax": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p],
+    "glu_fwd_nvfp4_gs": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _p, _int, _p],
     "glu_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p, _p],
     "glu_quant_nvfp4_f32": [_i64, _i64, _p, _i64, _p, _p, _int, _p],
     "glu_check_fwd": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64],
@@ -51,6 +55,8 @@ _SIGNATURES = {
     "glu_check_bwd_mxfp8": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _int, _p, _p, _p, _p],
     "glu_check_fwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int],
     "glu_check_bwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _p, _p, _int],
+    "glu_check_amax": [_int, _int, _i64, _i64, _p, _p, _i64, _p],
+    "glu_check_fwd_nvfp4_gs": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _p, _int],
     "glu_check_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p],
     "glu_check_quant_nvfp4_f32": [_i64, _i64, _p, _i64, _p, _p, _int],
 }
@@ -276,6 +282,28 @@ def glu_fwd_nvfp4(x, up=None, *, act="geglu", layout="paired", sf_layout="rowmaj
     q, sf = _nv_buffers(M, H, sf_layout, x.device, out)
     _call("glu_fwd_nvfp4", ACT[act], LAYOUT[layout], M, H, _ptr(x), _ptr(up), ld, _ptr(q), _ptr(sf),
           SF_LAYOUT[sf_layout], _stream(x))
+    return q, sf
+
+
+def glu_amax(gate, up=None, *, act="swiglu", layout="split", out=None):
+    """Largest |h| of h = bf16(act(gate) * up), as a float32 [1] GPU tensor (no host sync)."""
+    M, N, ld = _operands(gate, up, layout)
+    a = out if out is not None else torch.empty((1,), dtype=torch.float32, device=gate.device)
+    if a.dtype != torch.float32 or not a.is_cuda or a.numel() < 1:
+        raise ValueError("out must be a float32 GPU tensor with at least one element")
+    _call("glu_amax", ACT[act], LAYOUT[layout], M, N, _ptr(gate), _ptr(up), ld, _ptr(a), _stream(gate))
+    return a
+
+
+def glu_fwd_nvfp4_gs(x, up=None, *, amax, act="geglu", layout="paired", sf_layout="rowmajor", out=None):
+    """Fused forward + two-level NVFP4: global encode scale from the float32 GPU tensor amax
+    (its first element, e.g. glu_amax's output): (q [M, H/2] packed E2M1, sf scales)."""
+    M, H, ld = _operands(x, up, layout)
+    if amax.dtype != torch.float32 or not amax.is_cuda or amax.numel() < 1:
+        raise ValueError("amax must be a float32 GPU tensor")
+    q, sf = _nv_buffers(M, H, sf_layout, x.device, out)
+    _call("glu_fwd_nvfp4_gs", ACT[act], LAYOUT[layout], M, H, _ptr(x), _ptr(up), ld, _ptr(amax), _ptr(q),
+          _ptr(sf), SF_LAYOUT[sf_layout], _stream(x))
     return q, sf
 
 

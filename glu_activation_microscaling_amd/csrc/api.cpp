@@ -314,6 +314,38 @@ glu_status glu_check_fwd_nvfp4(int act, int layout, int64_t M, int64_t H, const 
   return check_no_overlap({Q, S}, {G, U});
 }
 
+glu_status glu_check_amax(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                          const uint16_t* up, int64_t ld_in, float* amax) {
+  if (!valid_act(act) || !valid_layout(layout)) return GLU_ERR_ARG;
+  if (M < 0 || N < 0) return GLU_ERR_SHAPE;
+  if (amax == nullptr) return GLU_ERR_NULL;
+  if (((uintptr_t)amax & 3u) != 0) return GLU_ERR_ALIGN;
+  if (M == 0 || N == 0) return GLU_OK;
+  glu_status st = check_inputs(act, layout, N, gate, up, ld_in);
+  if (st != GLU_OK) return st;
+  if (N % 16 != 0 || N > kMaxNvWidth) return GLU_ERR_SHAPE;
+  if (ld_in % 8 != 0) return GLU_ERR_STRIDE;
+  if (!aligned16(gate) || !aligned16(up)) return GLU_ERR_ALIGN;
+  const int64_t in_cols = layout == glu::PAIRED ? 2 * N : N;
+  const Operand G = mat(gate, M, in_cols, ld_in, 2), U = mat(up, M, N, ld_in, 2),
+                A = mat(amax, 1, 1, 1, 4);
+  if (any_overflow({G, U})) return GLU_ERR_SHAPE;
+  return check_no_overlap({A}, {G, U});
+}
+
+glu_status glu_check_fwd_nvfp4_gs(int act, int layout, int64_t M, int64_t H,
+                                  const uint16_t* gate, const uint16_t* up, int64_t ld_in,
+                                  const float* amax, uint8_t* q, uint8_t* sf, int sf_layout) {
+  glu_status st = glu_check_fwd_nvfp4(act, layout, M, H, gate, up, ld_in, q, sf, sf_layout);
+  if (st != GLU_OK || M == 0 || H == 0) return st;
+  if (amax == nullptr) return GLU_ERR_NULL;
+  if (((uintptr_t)amax & 3u) != 0) return GLU_ERR_ALIGN;
+  const int64_t sfb = glu_nvfp4_sf_bytes(M, H, sf_layout);
+  const Operand A = mat(amax, 1, 1, 1, 4), Q = mat(q, M, H / 2, H / 2, 1),
+                S = mat(sf, 1, sfb, sfb, 1);
+  return check_no_overlap({Q, S}, {A});
+}
+
 glu_status glu_check_bwd_nvfp4(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
                                const uint16_t* up, int64_t ld_in, const uint16_t* dh,
                                int64_t ld_dh, uint8_t* q, uint8_t* sf, int sf_layout) {
@@ -449,8 +481,27 @@ glu_status glu_fwd_nvfp4(int act, int layout, int64_t M, int64_t H, const uint16
                          int sf_layout, void* stream) {
   glu_status st = glu_check_fwd_nvfp4(act, layout, M, H, gate, up, ld_in, q, sf, sf_layout);
   if (st != GLU_OK || M == 0 || H == 0) return st;
-  NvArgs a{act, layout, sf_layout, M, H, gate, up, ld_in, q, sf, nullptr, 0};
+  NvArgs a{act, layout, sf_layout, M, H, gate, up, ld_in, q, sf, nullptr, 0, nullptr, nullptr};
   return status_of(glu::launch_glu_fwd_nvfp4(a, (hipStream_t)stream));
+}
+
+glu_status glu_amax(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                    const uint16_t* up, int64_t ld_in, float* amax, void* stream) {
+  glu_status st = glu_check_amax(act, layout, M, N, gate, up, ld_in, amax);
+  if (st != GLU_OK) return st;
+  NvArgs a{act, layout, glu::SF_ROWMAJOR, M, N, gate, up, ld_in, nullptr, nullptr,
+           nullptr, 0, nullptr, amax};
+  return status_of(glu::launch_glu_amax(a, (hipStream_t)stream));
+}
+
+glu_status glu_fwd_nvfp4_gs(int act, int layout, int64_t M, int64_t H, const uint16_t* gate,
+                            const uint16_t* up, int64_t ld_in, const float* amax, uint8_t* q,
+                            uint8_t* sf, int sf_layout, void* stream) {
+  glu_status st =
+      glu_check_fwd_nvfp4_gs(act, layout, M, H, gate, up, ld_in, amax, q, sf, sf_layout);
+  if (st != GLU_OK || M == 0 || H == 0) return st;
+  NvArgs a{act, layout, sf_layout, M, H, gate, up, ld_in, q, sf, nullptr, 0, amax, nullptr};
+  return status_of(glu::launch_glu_fwd_nvfp4_gs(a, (hipStream_t)stream));
 }
 
 glu_status glu_bwd_nvfp4(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
@@ -459,7 +510,7 @@ glu_status glu_bwd_nvfp4(int act, int layout, int64_t M, int64_t N, const uint16
   glu_status st =
       glu_check_bwd_nvfp4(act, layout, M, N, gate, up, ld_in, dh, ld_dh, q, sf, sf_layout);
   if (st != GLU_OK || M == 0 || N == 0) return st;
-  NvArgs a{act, layout, sf_layout, M, N, gate, up, ld_in, q, sf, dh, ld_dh};
+  NvArgs a{act, layout, sf_layout, M, N, gate, up, ld_in, q, sf, dh, ld_dh, nullptr, nullptr};
   return status_of(glu::launch_glu_bwd_nvfp4(a, (hipStream_t)stream));
 }
 
@@ -477,7 +528,7 @@ glu_status glu_quant_nvfp4_f32(int64_t M, int64_t H, const float* x, int64_t ld_
                                uint8_t* sf, int sf_layout, void* stream) {
   glu_status st = glu_check_quant_nvfp4_f32(M, H, x, ld_x, q, sf, sf_layout);
   if (st != GLU_OK || M == 0 || H == 0) return st;
-  NvArgs a{glu::SWIGLU, glu::SPLIT, sf_layout, M, H, x, nullptr, ld_x, q, sf, nullptr, 0};
+  NvArgs a{glu::SWIGLU, glu::SPLIT, sf_layout, M, H, x, nullptr, ld_x, q, sf, nullptr, 0, nullptr, nullptr};
   return status_of(glu::launch_quant_nvfp4_f32(a, (hipStream_t)stream));
 }
 

@@ -51,6 +51,8 @@ struct NvArgs {
   uint8_t* sf;
   const uint16_t* dh;        // backward only
   int64_t ld_dh;
+  const float* amax;         // two-level forward: the tensor amax (device memory)
+  float* amax_out;           // amax pass: where it goes (device memory)
 };
 
 hipError_t launch_glu_fwd_bf16(const BF16Args& a, hipStream_t s);
@@ -60,6 +62,8 @@ hipError_t launch_glu_bwd_mxfp8(const MxArgs& a, hipStream_t s);
 hipError_t launch_quant_mxfp8_f32(const MxArgs& a, hipStream_t s);
 hipError_t launch_glu_fwd_nvfp4(const NvArgs& a, hipStream_t s);
 hipError_t launch_glu_bwd_nvfp4(const NvArgs& a, hipStream_t s);
+hipError_t launch_glu_fwd_nvfp4_gs(const NvArgs& a, hipStream_t s);
+hipError_t launch_glu_amax(const NvArgs& a, hipStream_t s);
 hipError_t launch_quant_nvfp4_f32(const NvArgs& a, hipStream_t s);
 
 // Launches kernel k and returns the launch status of this call alone (the HIP error

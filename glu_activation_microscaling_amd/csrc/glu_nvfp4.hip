@@ -34,6 +34,10 @@ constexpr int64_t NV_TILE = 2048;  // operand columns per workgroup and group
 
 // Build-time tuning (fixed defaults; alternatives are compiled only to measure them):
 //   GLU_NV_NT_LOADS / GLU_NV_NT_STORES: non-temporal (streaming) loads / code stores.
+//   GLU_AMAX_WGS: workgroups of the amax pass (each folds its maximum in with one atomic).
+#ifndef GLU_AMAX_WGS
+#define GLU_AMAX_WGS 1024
+#endif
 #ifndef GLU_NV_NT_LOADS
 #define GLU_NV_NT_LOADS 0
 #endif
@@ -41,7 +45,7 @@ constexpr int64_t NV_TILE = 2048;  // operand columns per workgroup and group
 #define GLU_NV_NT_STORES 0
 #endif
 
-enum { NV_FWD = 0, NV_BWD = 1, NV_F32 = 2 };
+enum { NV_FWD = 0, NV_BWD = 1, NV_F32 = 2, NV_FWD_GS = 3 };
 
 
 struct Words4 {
@@ -170,6 +174,22 @@ __device__ __forceinline__ void glu_values(const Raw8& r, uint32_t p[4], uint32_
   }
 }
 
+// Two-level NVFP4 (global scale from the tensor amax): s = fl(2688 / amax), capped at 2^100,
+// 1 for an amax that is zero, negative or not finite; k = fl(s / 6).  Every step is one
+// IEEE FP32 operation (the divisions are correctly rounded).
+struct GlobalScale {
+  float s = 1.0f, k = 1.0f / 6.0f;
+};
+__device__ __forceinline__ GlobalScale global_scale(float amax) {
+  GlobalScale g;
+  if (amax > 0.0f && __builtin_isfinite(amax)) {
+    const float s = 2688.0f / amax;
+    g.s = s < 0x1p100f ? s : 0x1p100f;
+  }
+  g.k = g.s / 6.0f;
+  return g;
+}
+
 // Output geometry of the quantized matrix: codes are q_pitch bytes per row, scales
 // scale_cols per row (scale_cols_padded in the 128x4 layout).
 struct NvOut {
@@ -201,25 +221,39 @@ __device__ __forceinline__ uint32_t row_shl(uint32_t v) {
 // scale word a lane-octet gather).  WORD_SCALES: 128x4 scales leave as 4-byte words (needs
 // jq's block index to be a multiple of 4 at every lane octet, true when the column offset of
 // this part is a multiple of 64).
-template <int SFL, bool WORD_SCALES>
+template <int SFL, bool WORD_SCALES, bool GS = false>
 __device__ __forceinline__ void quant_store_bf16(const uint32_t p[4], __amdgpu_buffer_rsrc_t qr,
                                                  __amdgpu_buffer_rsrc_t sr, uint32_t jq,
                                                  bool in_row, bool live, int lane,
-                                                 uint32_t scale_cols, uint32_t scale_cols_padded) {
+                                                 uint32_t scale_cols, uint32_t scale_cols_padded,
+                                                 const GlobalScale& gs = GlobalScale{}) {
   const uint32_t M = 0x7fff7fffu;
   const uint32_t m2 = pkmax(pkmax(p[0] & M, p[1] & M), pkmax(p[2] & M, p[3] & M));
   uint32_t m = umax(lo16(m2), hi16(m2));
   m = umax(m, dpp<DPP_XOR1>(m));  // BF16 magnitude bits of the block amax
   const bool nonfinite = m >= 0x7f80u;
-  const uint32_t sc = nonfinite ? 0x7fu : nv_scale_code_bf16(__uint_as_float(m << 16));
-
-  const float S = e4m3_value(nonfinite ? 0u : sc);
-  const float R = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
-  uint32_t word = 0;
-  word = fp4x2<0>(word, e2m1_operand(bf_lo(p[0]), R), e2m1_operand(bf_hi(p[0]), R));
-  word = fp4x2<1>(word, e2m1_operand(bf_lo(p[1]), R), e2m1_operand(bf_hi(p[1]), R));
-  word = fp4x2<2>(word, e2m1_operand(bf_lo(p[2]), R), e2m1_operand(bf_hi(p[2]), R));
-  word = fp4x2<3>(word, e2m1_operand(bf_lo(p[3]), R), e2m1_operand(bf_hi(p[3]), R));
+  uint32_t word = 0, sc;
+  if constexpr (GS) {
+    // two-level: E4M3(fl(bamax * k)), saturating at 448; codes E2M1(fl(x * fl(s / S)))
+    const float d = __builtin_fminf(__uint_as_float(m << 16) * gs.k, 448.0f);
+    sc = nonfinite ? 0x7fu : (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(d, 0.0f, 0, false) & 0xffu;
+    const float S = e4m3_value(nonfinite ? 0u : sc);
+    const float r = S > 0.0f ? gs.s / S : 0.0f;  // IEEE division
+    // |x * r| beyond 8 saturates to 6 either way; the clamp keeps the convert's input finite
+    auto y = [&](float x) { return __builtin_amdgcn_fmed3f(x * r, -8.0f, 8.0f); };
+    word = fp4x2<0>(word, y(bf_lo(p[0])), y(bf_hi(p[0])));
+    word = fp4x2<1>(word, y(bf_lo(p[1])), y(bf_hi(p[1])));
+    word = fp4x2<2>(word, y(bf_lo(p[2])), y(bf_hi(p[2])));
+    word = fp4x2<3>(word, y(bf_lo(p[3])), y(bf_hi(p[3])));
+  } else {
+    sc = nonfinite ? 0x7fu : nv_scale_code_bf16(__uint_as_float(m << 16));
+    const float S = e4m3_value(nonfinite ? 0u : sc);
+    const float R = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
+    word = fp4x2<0>(word, e2m1_operand(bf_lo(p[0]), R), e2m1_operand(bf_hi(p[0]), R));
+    word = fp4x2<1>(word, e2m1_operand(bf_lo(p[1]), R), e2m1_operand(bf_hi(p[1]), R));
+    word = fp4x2<2>(word, e2m1_operand(bf_lo(p[2]), R), e2m1_operand(bf_hi(p[2]), R));
+    word = fp4x2<3>(word, e2m1_operand(bf_lo(p[3]), R), e2m1_operand(bf_hi(p[3]), R));
+  }
   if (nonfinite) word = 0;
   __builtin_amdgcn_raw_buffer_store_b32(word, qr, live ? jq / 2 : kOob, 0, GLU_NV_NT_STORES ? 2 : 0);
 
@@ -290,6 +324,8 @@ __global__ __launch_bounds__(NV_THREADS) void k_nvfp4(NvArgs a, int64_t tiles_pe
   const int lane = threadIdx.x & 63;
   const uint32_t H = (uint32_t)a.H;
   const uint32_t nb = (uint32_t)o.scale_cols, cp = (uint32_t)o.scale_cols_padded;
+  GlobalScale gs;
+  if constexpr (MODE == NV_FWD_GS) gs = global_scale(*a.amax);
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t row = t / tiles_per_row;
     const uint32_t j0 = (uint32_t)(t - row * tiles_per_row) * (uint32_t)(NV_TILE * NV_GROUPS) + threadIdx.x * 8u;
@@ -316,6 +352,10 @@ __global__ __launch_bounds__(NV_THREADS) void k_nvfp4(NvArgs a, int64_t tiles_pe
           v[4 + k] = __uint_as_float(raw[gi].B.w[k]);
         }
         quant_store_f32<SFL>(v, qr, sr, j, in_row, live, lane, nb, cp);
+      } else if constexpr (MODE == NV_FWD_GS) {
+        uint32_t p[4], q[4];
+        glu_values<ACT, LAYOUT, NV_FWD>(raw[gi], p, q);
+        quant_store_bf16<SFL, WORD_SCALES, true>(p, qr, sr, j, in_row, live, lane, nb, cp, gs);
       } else {
         uint32_t p[4], q[4];
         glu_values<ACT, LAYOUT, MODE>(raw[gi], p, q);
@@ -358,7 +398,80 @@ hipError_t launch(const NvArgs& a, hipStream_t s) {
   }
 }
 
+// Amax pass of two-level NVFP4: the largest |h| over the matrix, h = bf16(act(gate) * up)
+// (NaN if some h is NaN), as FP32 bits in *a.amax_out.  Workgroups stride over the same
+// tiles as k_nvfp4 (2 groups per lane) keeping a running maximum of BF16 magnitude bits
+// (NaN patterns order above Inf), reduce it over the workgroup, and fold it into the output
+// with at most one unsigned atomic max per workgroup; k_zero_u32 clears the output first (on
+// the same stream).  Non-negative FP32 values order like their bit patterns.
+__global__ void k_zero_u32(uint32_t* p) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0u;
+}
+
+template <int ACT, int LAYOUT>
+__global__ __launch_bounds__(NV_THREADS) void k_glu_amax(NvArgs a, int64_t tiles_per_row,
+                                                         int64_t ntiles) {
+  constexpr int G = 2;
+  const uint32_t H = (uint32_t)a.H;
+  uint32_t m = 0;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t row = t / tiles_per_row;
+    const uint32_t j0 = (uint32_t)(t - row * tiles_per_row) * (uint32_t)(NV_TILE * G) + threadIdx.x * 8u;
+    const RowIn in = row_in<LAYOUT, NV_FWD>(a, row);
+    Raw8 raw[G];
+#pragma unroll
+    for (int gi = 0; gi < G; gi++) {
+      const uint32_t j = j0 + gi * (uint32_t)NV_TILE;
+      raw[gi] = load_raw<LAYOUT, NV_FWD>(in, j, j < H);
+    }
+#pragma unroll
+    for (int gi = 0; gi < G; gi++) {
+      // lanes past the row read zeros, and every activation gives h = 0 for them
+      uint32_t p[4], q[4];
+      glu_values<ACT, LAYOUT, NV_FWD>(raw[gi], p, q);
+      const uint32_t M = 0x7fff7fffu;
+      const uint32_t m2 = pkmax(pkmax(p[0] & M, p[1] & M), pkmax(p[2] & M, p[3] & M));
+      m = umax(m, umax(lo16(m2), hi16(m2)));
+    }
+  }
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, k));
+  __shared__ uint32_t wave_max[NV_THREADS / 64];
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t w = wave_max[0];
+#pragma unroll
+    for (int i = 1; i < NV_THREADS / 64; i++) w = umax(w, wave_max[i]);
+    // the running value only grows, so a workgroup whose maximum is not above it skips the
+    // atomic (an older, smaller value read here only costs a redundant atomic)
+    unsigned int* out = reinterpret_cast<unsigned int*>(a.amax_out);
+    if ((w << 16) > __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(out, w << 16);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_glu_amax(const NvArgs& a, hipStream_t s) {
+  hipError_t e = launch_kernel(k_zero_u32, dim3(1), dim3(64), s, reinterpret_cast<uint32_t*>(a.amax_out));
+  if (e != hipSuccess || a.M == 0 || a.H == 0) return e;
+  const int64_t tpr = (a.H + NV_TILE * 2 - 1) / (NV_TILE * 2);
+  const int64_t ntiles = a.M * tpr;
+  const dim3 grid(grid_for(ntiles, GLU_AMAX_WGS)), block(NV_THREADS);
+  return with_act(a.act, [&](auto A) {
+    constexpr int ACT = decltype(A)::value;
+    return a.layout == PAIRED ? launch_kernel(k_glu_amax<ACT, PAIRED>, grid, block, s, a, tpr, ntiles)
+                              : launch_kernel(k_glu_amax<ACT, SPLIT>, grid, block, s, a, tpr, ntiles);
+  });
+}
+
+hipError_t launch_glu_fwd_nvfp4_gs(const NvArgs& a, hipStream_t s) {
+  return with_act(a.act, [&](auto A) {
+    constexpr int ACT = decltype(A)::value;
+    return a.layout == PAIRED ? launch<ACT, PAIRED, NV_FWD_GS>(a, s) : launch<ACT, SPLIT, NV_FWD_GS>(a, s);
+  });
+}
 
 hipError_t launch_glu_fwd_nvfp4(const NvArgs& a, hipStream_t s) {
   return with_act(a.act, [&](auto A) {

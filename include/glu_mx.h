@@ -160,6 +160,32 @@ glu_status glu_fwd_nvfp4(int act, int layout, int64_t M, int64_t H, const uint16
                          const uint16_t* up, int64_t ld_in, uint8_t* q, uint8_t* sf,
                          int sf_layout, void* stream);
 
+/* ---- Two-level NVFP4: a global scale from the tensor's amax.  [NV] Supported contract
+ * fixes global scale 1; real recipes relax it, which no page defines.  By reading, every
+ * step is one IEEE FP32 operation:
+ *   s = 2688 / amax (448 * 6), capped at 2^100; s = 1 when amax is zero, negative, NaN or
+ *       infinite;
+ *   block scale code = E4M3(bamax * fl(s / 6)), nearest even, saturating at 448;
+ *   codes = E2M1(x * fl(s / S)), S = the scale code's value (0 when S == 0), nearest even,
+ *       saturating at 6; dequantized x ~ code * S / s.
+ * A block holding NaN or Inf gets scale 0x7F and zero codes. */
+
+/* Amax pass: *amax = the largest |h| over h = bf16(act(gate) * up), [M, N] (NaN when some h
+ * is NaN, 0 for an empty matrix); h is never written.  amax is device memory (4-byte
+ * aligned), written on `stream` by kernels (no host synchronization).  Operands as for
+ * glu_fwd_nvfp4: N % 16 == 0 and N <= 2^26 (GLU_ERR_SHAPE), ld_in % 8 == 0 (GLU_ERR_STRIDE),
+ * 16-byte aligned (GLU_ERR_ALIGN). */
+glu_status glu_amax(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                    const uint16_t* up, int64_t ld_in, float* amax, void* stream);
+
+/* Fused forward + two-level NVFP4: as glu_fwd_nvfp4, with the global encode scale of the
+ * FP32 value at device pointer amax (normally glu_amax's output on the same stream, or an
+ * amax kept from an earlier step).  The scale s itself is not stored: the consumer derives
+ * it from the same amax. */
+glu_status glu_fwd_nvfp4_gs(int act, int layout, int64_t M, int64_t H, const uint16_t* gate,
+                            const uint16_t* up, int64_t ld_in, const float* amax, uint8_t* q,
+                            uint8_t* sf, int sf_layout, void* stream);
+
 /* ---- Fused backward + NVFP4, global scale 1 (no page defines an NVFP4 backward: the
  * placement is glu_bwd_mxfp8's, [MX] API; the block arithmetic is glu_fwd_nvfp4's, [NV]
  * Supported contract).  The quantized matrix is X = [da | db], [M, 2N], with da, db as in
@@ -205,6 +231,11 @@ glu_status glu_check_bwd_mxfp8(int act, int layout, int64_t M, int64_t N,
 glu_status glu_check_fwd_nvfp4(int act, int layout, int64_t M, int64_t H,
                                const uint16_t* gate, const uint16_t* up, int64_t ld_in,
                                uint8_t* q, uint8_t* sf, int sf_layout);
+glu_status glu_check_amax(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
+                          const uint16_t* up, int64_t ld_in, float* amax);
+glu_status glu_check_fwd_nvfp4_gs(int act, int layout, int64_t M, int64_t H,
+                                  const uint16_t* gate, const uint16_t* up, int64_t ld_in,
+                                  const float* amax, uint8_t* q, uint8_t* sf, int sf_layout);
 glu_status glu_check_bwd_nvfp4(int act, int layout, int64_t M, int64_t N,
                                const uint16_t* gate, const uint16_t* up, int64_t ld_in,
                                const uint16_t* dh, int64_t ld_dh, uint8_t* q, uint8_t* sf,

@@ -135,6 +135,17 @@ def check_rule3_mx(h_bits, q_g, s_g, q_o, s_o, what=""):
                   0xFF, what)
 
 
+def check_rule3_nv_gs(h_bits, q_g, s_g, q_o, s_o, s, what=""):
+    """As check_rule3_nv for two-level scaling with global encode scale s: block scales decide
+    on amax * fl(s/6), codes on x * s / S, and dequantize as code * S / s."""
+    k = float(np.float32(np.float32(s) / np.float32(6.0)))
+    return _rule3(h_bits, _unpack_nibbles(q_g), s_g, _unpack_nibbles(q_o), s_o, 16, E2M1_VAL, E2M1_RANK,
+                  lambda c: E4M3_VAL[np.asarray(c, dtype=np.int64)] / s,
+                  E4M3_RANK,
+                  lambda a, b: 0.5 * (E4M3_VAL[int(a)] + E4M3_VAL[int(b)]) / k,
+                  0x7F, what)
+
+
 def check_rule3_nv(h_bits, q_g, s_g, q_o, s_o, what=""):
     """h_bits [M, H] BF16; q packed [M, H/2]; s row-major [M, H/16]."""
     return _rule3(h_bits, _unpack_nibbles(q_g), s_g, _unpack_nibbles(q_o), s_o, 16, E2M1_VAL, E2M1_RANK,

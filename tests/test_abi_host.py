@@ -225,6 +225,24 @@ def test_bwd_nvfp4_checks():
     assert nvb(M=1, N=(1 << 26) + 16, ld=(1 << 26) + 16, lddh=(1 << 26) + 16) == SHAPE
 
 
+def test_amax_and_two_level_checks():
+    am = L.glu_check_amax
+    assert am(0, 0, 64, 128, P(A0), P(B0), 128, P(C0)) == OK
+    assert am(0, 1, 64, 128, P(A0), P(0), 256, P(C0)) == OK
+    assert am(0, 0, 64, 128, P(A0), P(B0), 128, P(0)) == NULL
+    assert am(0, 0, 64, 128, P(A0), P(B0), 128, P(C0 + 2)) == ALIGN
+    assert am(0, 0, 0, 128, P(0), P(0), 128, P(C0)) == OK        # empty: still writes 0
+    assert am(0, 0, 64, 120, P(A0), P(B0), 120, P(C0)) == SHAPE   # N % 16
+    assert am(0, 0, 64, 128, P(A0), P(B0), 128, P(A0 + 64)) == OVERLAP
+    assert am(5, 0, 64, 128, P(A0), P(B0), 128, P(C0)) == ARG
+    gs = L.glu_check_fwd_nvfp4_gs
+    assert gs(1, 1, 100, 256, P(A0), P(0), 512, P(E0), P(C0), P(D0), 0) == OK
+    assert gs(1, 1, 100, 256, P(A0), P(0), 512, P(0), P(C0), P(D0), 0) == NULL
+    assert gs(1, 1, 100, 256, P(A0), P(0), 512, P(E0 + 1), P(C0), P(D0), 0) == ALIGN
+    assert gs(1, 1, 100, 256, P(A0), P(0), 512, P(C0 + 64), P(C0), P(D0), 0) == OVERLAP
+    assert gs(1, 1, 100, 264, P(A0), P(0), 528, P(E0), P(C0), P(D0), 0) == SHAPE
+
+
 def test_quant_hook_checks():
     q = L.glu_check_quant_mxfp8_f32
     assert q(64, 64, P(A0), 64, 3, P(B0), P(C0), P(D0), P(E0)) == OK
@@ -249,6 +267,8 @@ def test_entry_points_fail_before_any_hip_call():
     assert L.glu_fwd_nvfp4(1, 1, 8, 24, P(A0), P(0), 48, P(C0), P(D0), 0, P(0)) == SHAPE
     assert L.glu_bwd_nvfp4(0, 0, 8, 24, P(A0), P(B0), 24, P(C0), 24, P(D0), P(E0), 0, P(0)) == SHAPE
     assert L.glu_bwd_nvfp4(0, 0, 0, 32, P(0), P(0), 32, P(0), 32, P(0), P(0), 0, P(0)) == OK
+    assert L.glu_amax(0, 0, 4, 32, P(A0), P(B0), 32, P(0), P(0)) == NULL
+    assert L.glu_fwd_nvfp4_gs(1, 1, 0, 32, P(0), P(0), 64, P(0), P(0), P(0), 0, P(0)) == OK
     assert L.glu_quant_mxfp8_f32(32, 32, P(A0), 32, 8, P(B0), P(C0), P(D0), P(E0), P(0)) == ARG
     assert L.glu_quant_nvfp4_f32(32, 32, P(A0 + 4), 32, P(B0), P(C0), 0, P(0)) == ALIGN
 

@@ -16,7 +16,7 @@ import torch
 import oracle
 import synthetic_inputs as si
 from conftest import bits, u8
-from parity import check_rule3_nv
+from parity import check_rule3_nv, check_rule3_nv_gs
 
 pytestmark = pytest.mark.gpu
 SFL = [("rowmajor", oracle.SF_ROWMAJOR), ("128x4", oracle.SF_128x4)]
@@ -218,3 +218,65 @@ def test_bwd_four_groups_ragged_tile(gpu):
         oq, osf = oracle.quant_nvfp4(X, code)
         assert np.array_equal(u8(sf).ravel(), osf.ravel()), f"scales ({name})"
         assert np.array_equal(u8(q), oq), f"codes ({name})"
+
+
+# ---- two-level NVFP4 (global scale from the tensor amax) ----------------------------
+
+@pytest.mark.parametrize("act,kind", ACTS)
+@pytest.mark.parametrize("layout", ["split", "paired"])
+def test_amax_and_two_level_equal_oracle_quantizer(gpu, act, kind, layout):
+    """glu_amax equals the oracle's largest |h|; the two-level fused forward equals the oracle
+    quantizer applied to the GPU's own BF16 forward at that amax (rule 1)."""
+    M, H = 130, 2064
+    gate, up = si.glu_operands(M, H, seed=51 + kind, outliers=True)
+    gd, ud = gate.cuda(), up.cuda()
+    args = (torch.stack([gd, ud], 2).reshape(M, 2 * H).contiguous(), None) if layout == "paired" else (gd, ud)
+    a = gpu.glu_amax(*args, act=act, layout=layout)
+    h = bits(gpu.glu_fwd(*args, act=act, layout=layout))
+    assert float(a.item()) == oracle.glu_amax(kind, bits(gate), bits(up))
+    hf = si.from_bits(h).float().numpy()
+    for name, code in SFL:
+        q, sf = gpu.glu_fwd_nvfp4_gs(*args, amax=a, act=act, layout=layout, sf_layout=name)
+        oq, osf = oracle.quant_nvfp4_gs(hf, float(a.item()), code)
+        assert np.array_equal(u8(sf).ravel(), osf.ravel()), f"scales ({name})"
+        assert np.array_equal(u8(q), oq), f"codes ({name})"
+
+
+@pytest.mark.parametrize("M", [784, 968])
+def test_two_level_config_geglu(gpu, M):
+    """The GeGLU NVFP4 workload with two-level scaling, end to end against the oracle at the
+    oracle's amax (rule 3), and the GPU amax equal to the oracle's."""
+    H = 16384
+    x = si.paired_operand(M, H, seed=1)
+    xb = bits(x)
+    xd = x.cuda()
+    amax = oracle.glu_amax(oracle.GEGLU_TANH, xb, None, layout=oracle.PAIRED)
+    assert float(gpu.glu_amax(xd, act="geglu", layout="paired").item()) == amax
+    ad = torch.tensor([amax], dtype=torch.float32, device="cuda")
+    q, sf = gpu.glu_fwd_nvfp4_gs(xd, amax=ad, act="geglu", layout="paired")
+    oq, osf = oracle.glu_fwd_nvfp4_gs(oracle.GEGLU_TANH, xb, None, amax=amax)
+    h = oracle.glu_fwd(oracle.GEGLU_TANH, xb, None, layout=oracle.PAIRED)
+    check_rule3_nv_gs(h, u8(q), u8(sf), oq, osf, oracle.nvfp4_global_scale(amax), f"two-level M={M}")
+
+
+@pytest.mark.parametrize("amax", [0.0, 1e-30, 2.0 ** -100, 0.25, 3.0e38, float("inf"), float("nan")])
+def test_two_level_degenerate_amax(gpu, amax):
+    """Any amax, including ones far from the data's (saturating scales and codes), zero, tiny
+    (capped global scale) and non-finite (global scale 1), quantizes as the oracle does."""
+    M, H = 64, 512
+    gate, up = si.glu_operands(M, H, seed=52, outliers=True)
+    gd, ud = gate.cuda(), up.cuda()
+    hf = si.from_bits(bits(gpu.glu_fwd(gd, ud, act="swiglu"))).float().numpy()
+    ad = torch.tensor([amax], dtype=torch.float32, device="cuda")
+    q, sf = gpu.glu_fwd_nvfp4_gs(gd, ud, amax=ad, act="swiglu", layout="split")
+    oq, osf = oracle.quant_nvfp4_gs(hf, amax)
+    assert np.array_equal(u8(sf), osf) and np.array_equal(u8(q), oq)
+
+
+def test_amax_nan_and_empty(gpu):
+    gate, up = (t.cuda() for t in si.glu_operands(32, 64, seed=53))
+    gate[5, 7] = float("nan")
+    assert np.isnan(gpu.glu_amax(gate, up).item())
+    e = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    a = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+    assert gpu.glu_amax(e, e, out=a).item() == 0.0
