@@ -47,6 +47,8 @@
  *     (the GEMM-ready block-scale layout; no page fixes one for MXFP8);
  *   - an NVFP4 backward quantizes [da | db] as one [M, 2N] matrix in 16-element
  *     row blocks, the MXFP8 backward's placement (no page defines one);
+ *   - the GEMM epilogue form takes MXFP8 operands (E8M0 scales per 32 along K, the
+ *     block scaling gfx950's matrix cores take) and W = [W_gate | W_up];
  *   - two-level NVFP4 (a global scale from the tensor's amax, relaxing [NV]'s global
  *     scale 1) is defined by IEEE FP32 operations: s = 2688 / amax (capped at
  *     2^100), block scale E4M3(bamax * fl(s / 6)), codes E2M1(x * fl(s / S)).
@@ -602,6 +604,70 @@ int orc_glu_fwd_nvfp4_gs(int act, int layout, int64_t M, int64_t H, const uint16
   free(h);
   if (!x) return -1;
   orc_quant_nvfp4_gs(M, H, x, amax, q, sf, sf_layout);
+  free(x);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Merged gate/up MXFP8 GEMM with the GLU (and its quantizer) as the epilogue:  */
+/* the placement of [NV] Summary (the fold follows the merged GEMM), in the     */
+/* MXFP8 form of [MX] Performance's fused-w13 MoE composite; [MX] API fixes the */
+/* [gate | up] packing of what a fused w13 projection produces.                */
+/* ------------------------------------------------------------------------- */
+
+/* E8M0 scale byte -> 2^(b - 127); 0xFF is NaN. */
+static double e8m0(uint8_t b) { return b == 0xFF ? NAN : ldexp(1.0, (int)b - 127); }
+
+/* Y = X W^T in binary64: X is [M, K] E4M3 codes with E8M0 scales [M, K/32] (32-element
+ * blocks along K), W is [N2, K] codes with scales [N2, K/32].  Every product of two decoded
+ * values is exact in binary64; the sum runs over k in order. */
+void orc_mx_gemm_nt(int64_t M, int64_t N2, int64_t K, const uint8_t* Xq, const uint8_t* Xs,
+                    const uint8_t* Wq, const uint8_t* Ws, double* Y) {
+  const int64_t kb = K / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; m++)
+    for (int64_t n = 0; n < N2; n++) {
+      double acc = 0.0;
+      for (int64_t b = 0; b < kb; b++) {
+        const double sx = e8m0(Xs[m * kb + b]), sw = e8m0(Ws[n * kb + b]);
+        double blk = 0.0;
+        for (int64_t k = 32 * b; k < 32 * b + 32; k++)
+          blk += orc_e4m3_to_f64(Xq[m * K + k]) * orc_e4m3_to_f64(Wq[n * K + k]);
+        acc += blk * sx * sw;
+      }
+      Y[m * N2 + n] = acc;
+    }
+}
+
+/* h = bf16(act(Y[:, j]) * Y[:, N + j]) with Y = X W^T, W = [W_gate | W_up] ([2N, K] rows:
+ * gate then up).  One rounding, from binary64. */
+int orc_glu_gemm(int act, int64_t M, int64_t N, int64_t K, const uint8_t* Xq, const uint8_t* Xs,
+                 const uint8_t* Wq, const uint8_t* Ws, uint16_t* h) {
+  double* Y = (double*)malloc((size_t)(M * 2 * N) * sizeof(double));
+  if (!Y) return -1;
+  orc_mx_gemm_nt(M, 2 * N, K, Xq, Xs, Wq, Ws, Y);
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; m++)
+    for (int64_t j = 0; j < N; j++)
+      h[m * N + j] = orc_bf16_from_f64(orc_act(act, Y[m * 2 * N + j]) * Y[m * 2 * N + N + j]);
+  free(Y);
+  return 0;
+}
+
+/* The same with h quantized to MXFP8 rowwise (1x32 blocks along N). */
+int orc_glu_gemm_mxfp8(int act, int64_t M, int64_t N, int64_t K, const uint8_t* Xq,
+                       const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws, uint8_t* q_row,
+                       uint8_t* s_row) {
+  uint16_t* h = (uint16_t*)malloc((size_t)(M * N) * sizeof(uint16_t));
+  if (!h) return -1;
+  if (orc_glu_gemm(act, M, N, K, Xq, Xs, Wq, Ws, h) != 0) {
+    free(h);
+    return -1;
+  }
+  float* x = widen_bf16(h, M * N);
+  free(h);
+  if (!x) return -1;
+  orc_quant_mxfp8(M, N, x, ORC_ROWWISE, q_row, s_row, NULL, NULL);
   free(x);
   return 0;
 }

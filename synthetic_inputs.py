@@ -13,6 +13,10 @@ Workloads (shapes and value distributions of the pages' benchmarks):
                     W in {4096, 11008, 14336, 18944, 29568, 8193}.
   * geglu_nvfp4   : one BF16 [M, 32768] ~ N(0, 1) matrix, columns interleaved
                     gate0, up0, gate1, up1, ... for M in {784, 816, 880, 968}.
+  * mx_operand    : an MXFP8 GEMM operand [rows, K]: E4M3 codes of N(0, 1) * 64 draws
+                    (torch's float8_e4m3fn cast, clamped to +-448) and E8M0 block scales
+                    (one per 32 along K) drawn uniformly from 2^-9 .. 2^-5, the range a
+                    block of N(0, 1) data quantized to E4M3 takes.
 Draw order within one call: gate, up, dh (then the outlier masks, in the same order).
 """
 import numpy as np
@@ -92,3 +96,15 @@ def normal_bf16_device(shapes, seed=0, device="cuda", outliers=False):
         out.append(t.to(torch.bfloat16))
         del t
     return out
+
+
+def mx_operand(rows, K, seed=0, device="cpu"):
+    """(codes uint8 [rows, K], scales uint8 [rows, K / 32]) as torch tensors: E4M3 codes of
+    N(0, 1) * 64 draws (torch's float8_e4m3fn cast of the clamped draw) and E8M0 scale bytes
+    drawn uniformly from 118 .. 122 (2^-9 .. 2^-5).  Drawn on the host generator, then
+    moved."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    v = (torch.randn((rows, K), generator=g, dtype=torch.float32) * 64.0).clamp(-448.0, 448.0)
+    codes = v.to(torch.float8_e4m3fn).view(torch.uint8)
+    scales = torch.randint(118, 123, (rows, K // 32), generator=g, dtype=torch.uint8)
+    return codes.to(device), scales.to(device)

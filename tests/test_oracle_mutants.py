@@ -77,6 +77,12 @@ MUTANTS = [
      [tq.test_nv_gs_blocks_against_brute_force]),
     ("NV two-level codes inverted", "const float r = S == 0.0f ? 0.0f : s / S;",
      "const float r = S == 0.0f ? 0.0f : S / s;", [tq.test_nv_gs_blocks_against_brute_force]),
+    ("GEMM scale bias", "ldexp(1.0, (int)b - 127)", "ldexp(1.0, (int)b - 126)",
+     [tq.test_mx_gemm_closed_forms]),
+    ("GEMM epilogue gate and up swapped", "orc_act(act, Y[m * 2 * N + j]) * Y[m * 2 * N + N + j]",
+     "orc_act(act, Y[m * 2 * N + N + j]) * Y[m * 2 * N + j]", [tq.test_glu_gemm_is_glu_of_the_gemm]),
+    ("GEMM drops a block's scale", "acc += blk * sx * sw;", "acc += blk * sx;",
+     [tq.test_mx_gemm_matches_numpy_on_dequantized_operands]),
     ("NV scale divisor", "amax / 6.0", "amax / 4.0", [tq.test_nv_golden_blocks]),
     ("MX scale direction", "ldexp(v[i], -e)", "ldexp(v[i], e)", [tq.test_mx_golden_blocks_rowwise_and_colwise]),
     ("bf16 subnormal exponent", "ldexp((double)m, -133)", "ldexp((double)m, -134)",

@@ -347,3 +347,46 @@ def test_glu_amax_and_fused_gs():
     gb2 = gb.copy()
     gb2[7, 9] = 0x7FC0   # NaN gate
     assert np.isnan(oracle.glu_amax(oracle.GEGLU_TANH, gb2, ub))
+
+
+# ---- merged gate/up MXFP8 GEMM with the GLU epilogue ----------------------------------
+
+def _dequant_rows(q, s):
+    v = oracle.e4m3_to_f64(np.asarray(q)).reshape(q.shape)
+    return v * np.repeat(np.exp2(np.asarray(s, np.float64) - 127.0), 32, axis=1)
+
+
+def test_mx_gemm_matches_numpy_on_dequantized_operands():
+    """The oracle's loop equals numpy's matmul of the dequantized operands (a library
+    routine), to binary64 summation-order error."""
+    Xq, Xs = (t.numpy() for t in si.mx_operand(48, 256, seed=57))
+    Wq, Ws = (t.numpy() for t in si.mx_operand(80, 256, seed=58))
+    Y = oracle.mx_gemm_nt(Xq, Xs, Wq, Ws)
+    ref = _dequant_rows(Xq, Xs) @ _dequant_rows(Wq, Ws).T
+    assert np.allclose(Y, ref, rtol=1e-12, atol=0)
+
+
+def test_mx_gemm_closed_forms():
+    """E4M3 0x38 = 1, 0x40 = 2: a 32-long dot product of ones and twos is 64; each E8M0
+    step of either operand's scale doubles it; blocks with different scales add."""
+    one = np.full((1, 64), 0x38, np.uint8)
+    two = np.full((1, 64), 0x40, np.uint8)
+    s = np.array([[127, 127]], np.uint8)
+    assert oracle.mx_gemm_nt(one, s, two, s)[0, 0] == 128.0
+    assert oracle.mx_gemm_nt(one, np.array([[130, 127]], np.uint8), two, s)[0, 0] == 64.0 * 8 + 64.0
+    assert oracle.mx_gemm_nt(one, s, two, np.array([[127, 120]], np.uint8))[0, 0] == 64.0 + 64.0 / 128
+
+
+def test_glu_gemm_is_glu_of_the_gemm():
+    """h = bf16(act(Y_gate) * Y_up) with W = [W_gate | W_up]; the MXFP8 form is the rowwise
+    quantizer of that h."""
+    Xq, Xs = (t.numpy() for t in si.mx_operand(40, 128, seed=59))
+    Wq, Ws = (t.numpy() for t in si.mx_operand(2 * 96, 128, seed=60))
+    Y = oracle.mx_gemm_nt(Xq, Xs, Wq, Ws)
+    for kind in (oracle.SWIGLU, oracle.GEGLU_TANH):
+        h = oracle.glu_gemm(kind, Xq, Xs, Wq, Ws)
+        want = oracle.bf16_from_f64(oracle.act(kind, Y[:, :96]) * Y[:, 96:])
+        assert np.array_equal(h, want)
+        q, sc = oracle.glu_gemm_mxfp8(kind, Xq, Xs, Wq, Ws)
+        o = oracle.quant_mxfp8(si.from_bits(h).float().numpy(), oracle.ROWWISE)
+        assert np.array_equal(q, o[0]) and np.array_equal(sc, o[1])
