@@ -15,7 +15,8 @@ Also reported on the same JSON line:
   sweep         - every workload shape of the pages (MXFP8 SwiGLU fwd/bwd per direction,
                   GeGLU BF16 fwd/bwd, GeGLU NVFP4), median of cold launches, plus the
                   other activations (tanh-GeGLU, erf-GeGLU, ReLU^2) at one shape of each,
-                  the NVFP4 backward, and two-level NVFP4 (amax pass + forward).
+                  the NVFP4 backward, two-level NVFP4 (amax pass + forward), and the
+                  merged MXFP8 GEMM with the GLU epilogue (TFLOP/s against the FP8 peak).
 Only one GPU is supported; --gpus above 1 exits with a message.
 """
 import argparse
@@ -31,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused GLU+MX-quant fwd/bwd achieved HBM GB/s and % of peak, M×N sweep"
 PEAK_GBPS = 8000.0  # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 matrix cores
 # The MXFP8 page's fused GB200 times for this exact workload (forward both 143.36 us,
 # backward both 219.14 us at (16384, 7168)), combined under the same byte model.
 PAGES_STEP_GBPS = (711_983_104 + 1_189_085_184) / ((143.36 + 219.14) * 1e-6) / 1e9
@@ -221,6 +223,23 @@ def sweep(torch, glu, si, iters):
             t = time_launches(torch, [lambda s=s: glu.glu_bwd_nvfp4(s[0], s[1], s[2], act=act, sf_layout="128x4",
                                                                      out=out) for s in sets], iters)
             rec(f"{act}_nvfp4_bwd_{M}x{N}", nv_bwd_bytes(M, N), t)
+        del sets, out
+        torch.cuda.empty_cache()
+    # merged gate/up MXFP8 GEMM with the GLU and MXFP8 rowwise epilogue: the NVFP4 page's
+    # projection (M tokens, K = 2048, merged 2N = 32768) in MXFP8 form, and the MXFP8 page's
+    # [16384, 7168] activation produced from K = 2048
+    for M, N, K in ((968, 16384, 2048), (16384, 7168, 2048)):
+        per = M * K + 2 * N * K
+        sets = [si.mx_operand(M, K, seed=M + s, device="cuda") + si.mx_operand(2 * N, K, seed=N + s, device="cuda")
+                for s in range(min(4, n_sets(per)))]
+        out = (torch.empty((M, N), dtype=torch.uint8, device="cuda"),
+               torch.empty((M, N // 32), dtype=torch.uint8, device="cuda"))
+        for act in ("swiglu", "geglu"):
+            t = time_launches(torch, [lambda s=s: glu.glu_gemm_mxfp8(*s, act=act, out=out) for s in sets], iters)
+            tf = 2.0 * M * K * 2 * N / t["median_us"] / 1e6
+            print(f"[bench] {act}_gemm_mxfp8_{M}x{N}x{K}: {t['median_us']:.2f} us", file=sys.stderr, flush=True)
+            res[f"{act}_gemm_mxfp8_{M}x{N}x{K}"] = dict(flops=2 * M * K * 2 * N, us=round(t["median_us"], 2),
+                                                         tflops=round(tf, 1), frac=round(tf / PEAK_FP8_TFLOPS, 4))
         del sets, out
         torch.cuda.empty_cache()
     return res

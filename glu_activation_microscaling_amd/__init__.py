@@ -14,6 +14,9 @@ Entry points (C names in include/glu_mx.h):
   glu_bwd_nvfp4(gate, up, dh, sf_layout=...)                -> (q, sf) of [da | db]
   glu_amax(gate, up=None, layout=...)                        -> amax, float32 [1] on the GPU
   glu_fwd_nvfp4_gs(x, up=None, amax=, layout=, sf_layout=)   -> (q, sf), two-level scaling
+  glu_gemm(xq, xs, wq, ws, act=)                             -> h of the merged MXFP8 GEMM
+  glu_gemm_mxfp8(xq, xs, wq, ws, act=)                       -> (q_row, s_row) of that h
+  mx_gemm_f32(xq, xs, wq, ws)                                -> the GEMM alone (test hook)
   glu_quant_mxfp8_f32(x, rowwise=, colwise=)                -> (q_row, q_col, s_row, s_col)
   glu_quant_nvfp4_f32(x, sf_layout=)                        -> (q, sf)
 A disabled MXFP8 direction comes back as zero-sized tensors (fixed arity), as in the
@@ -46,6 +49,9 @@ _SIGNATURES = {
     "glu_fwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int, _p],
     "glu_bwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _p, _p, _int, _p],
     "glu_amax": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p],
+    "glu_gemm": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _p],
+    "glu_gemm_mxfp8": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p],
+    "glu_mx_gemm_f32": [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p],
     "glu_fwd_nvfp4_gs": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _p, _int, _p],
     "glu_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p, _p],
     "glu_quant_nvfp4_f32": [_i64, _i64, _p, _i64, _p, _p, _int, _p],
@@ -56,6 +62,9 @@ _SIGNATURES = {
     "glu_check_fwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int],
     "glu_check_bwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _p, _p, _int],
     "glu_check_amax": [_int, _int, _i64, _i64, _p, _p, _i64, _p],
+    "glu_check_gemm": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64],
+    "glu_check_gemm_mxfp8": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p],
+    "glu_check_mx_gemm_f32": [_i64, _i64, _i64, _p, _p, _p, _p, _p],
     "glu_check_fwd_nvfp4_gs": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _p, _int],
     "glu_check_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p],
     "glu_check_quant_nvfp4_f32": [_i64, _i64, _p, _i64, _p, _p, _int],
@@ -305,6 +314,53 @@ def glu_fwd_nvfp4_gs(x, up=None, *, amax, act="geglu", layout="paired", sf_layou
     _call("glu_fwd_nvfp4_gs", ACT[act], LAYOUT[layout], M, H, _ptr(x), _ptr(up), ld, _ptr(amax), _ptr(q),
           _ptr(sf), SF_LAYOUT[sf_layout], _stream(x))
     return q, sf
+
+
+def _gemm_operands(xq, xs, wq, ws):
+    """MXFP8 operands of the merged gate/up GEMM: xq [M, K], xs [M, K/32], wq [2N, K],
+    ws [2N, K/32], contiguous uint8 on the GPU; returns (M, N, K)."""
+    for t, name in ((xq, "xq"), (xs, "xs"), (wq, "wq"), (ws, "ws")):
+        if t.dtype != torch.uint8 or not t.is_cuda or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 2-D torch.uint8 GPU tensor")
+    M, K = xq.shape
+    N2 = wq.shape[0]
+    if wq.shape[1] != K or tuple(xs.shape) != (M, K // 32) or tuple(ws.shape) != (N2, K // 32) or N2 % 2:
+        raise ValueError("operand shapes: xq [M, K], xs [M, K/32], wq [2N, K], ws [2N, K/32]")
+    return M, N2 // 2, K
+
+
+def glu_gemm(xq, xs, wq, ws, *, act="swiglu", out=None):
+    """h = bf16(act(Y_gate) * Y_up), Y = X W^T of MXFP8 operands, W = [W_gate | W_up]: [M, N]."""
+    M, N, K = _gemm_operands(xq, xs, wq, ws)
+    h = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    ldh = _shaped(h, "out", M, N)
+    _call("glu_gemm", ACT[act], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(h), ldh, _stream(xq))
+    return h
+
+
+def glu_gemm_mxfp8(xq, xs, wq, ws, *, act="swiglu", out=None):
+    """The same h quantized MXFP8 rowwise: (q_row [M, N], s_row [M, N/32])."""
+    M, N, K = _gemm_operands(xq, xs, wq, ws)
+    if out is not None:
+        q, sc = out
+        _byte_buffer(q, "q_row", M * N)
+        _byte_buffer(sc, "s_row", M * (N // 32))
+    else:
+        q = torch.empty((M, N), dtype=torch.uint8, device=xq.device)
+        sc = torch.empty((M, N // 32), dtype=torch.uint8, device=xq.device)
+    _call("glu_gemm_mxfp8", ACT[act], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(q), _ptr(sc),
+          _stream(xq))
+    return q, sc
+
+
+def mx_gemm_f32(xq, xs, wq, ws, *, out=None):
+    """Test hook: the merged GEMM's FP32 result Y = X W^T, [M, 2N], as the fused kernels form it."""
+    M, N, K = _gemm_operands(xq, xs, wq, ws)
+    y = out if out is not None else torch.empty((M, 2 * N), dtype=torch.float32, device=xq.device)
+    if y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous() or tuple(y.shape) != (M, 2 * N):
+        raise ValueError(f"out must be a contiguous float32 [{M}, {2 * N}] GPU tensor")
+    _call("glu_mx_gemm_f32", M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y), _stream(xq))
+    return y
 
 
 def glu_bwd_nvfp4(gate, up, dh, *, act="swiglu", sf_layout="rowmajor", out=None):

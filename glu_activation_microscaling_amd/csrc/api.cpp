@@ -20,6 +20,7 @@ namespace {
 using glu::BF16Args;
 using glu::MxArgs;
 using glu::NvArgs;
+using glu::GemmArgs;
 
 // Upper bound on MXFP8 tiles per launch (counted with the smallest tile, 32 x 64), so the
 // tile index and the workgroup count stay within 32 bits.
@@ -35,6 +36,8 @@ constexpr int64_t kMaxMxOutPitch = (int64_t)1 << 24;
 // per-row base with 32-bit offsets (FP32 hook loads 4 bytes per column; 128x4 scales of the
 // backward's [M, 2N] reach 16 bytes per column) that must stay below 2^31.
 constexpr int64_t kMaxNvWidth = (int64_t)1 << 26;
+// Bytes an operand or output of the GEMM kernels may span (32-bit offsets from its base).
+constexpr int64_t kOffsetLimit = (int64_t)1 << 31;
 
 // Output pitches of an MXFP8 launch whose quantized matrix is [M, width].
 glu_status check_mx_pitch(int flags, int64_t M, int64_t width) {
@@ -346,6 +349,69 @@ glu_status glu_check_fwd_nvfp4_gs(int act, int layout, int64_t M, int64_t H,
   return check_no_overlap({Q, S}, {A});
 }
 
+// Operands of the merged gate/up MXFP8 GEMM.  The kernels address each operand from its base
+// with 32-bit byte offsets, so every operand and output extent stays below 2^31 bytes.
+glu_status check_gemm_inputs(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                             const uint8_t* xs, const uint8_t* wq, const uint8_t* ws) {
+  if (xq == nullptr || xs == nullptr || wq == nullptr || ws == nullptr) return GLU_ERR_NULL;
+  if (K <= 0 || K % 128 != 0 || N % 128 != 0) return GLU_ERR_SHAPE;
+  int64_t xb, wb;
+  if (__builtin_mul_overflow(M, K, &xb) || __builtin_mul_overflow(2 * N, K, &wb)) return GLU_ERR_SHAPE;
+  if (xb >= kOffsetLimit || wb >= kOffsetLimit) return GLU_ERR_SHAPE;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws)) return GLU_ERR_ALIGN;
+  return GLU_OK;
+}
+
+glu_status glu_check_gemm(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                          const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, uint16_t* h,
+                          int64_t ld_h) {
+  if (!valid_act(act)) return GLU_ERR_ARG;
+  if (M < 0 || N < 0 || K < 0) return GLU_ERR_SHAPE;
+  if (M == 0 || N == 0) return GLU_OK;
+  glu_status st = check_gemm_inputs(M, N, K, xq, xs, wq, ws);
+  if (st != GLU_OK) return st;
+  if (h == nullptr) return GLU_ERR_NULL;
+  if (ld_h < N) return GLU_ERR_STRIDE;
+  if (!aligned16(h) || ld_h % 8 != 0) return GLU_ERR_ALIGN;
+  const Operand X = mat(xq, M, K, K, 1), XS = mat(xs, M, K / 32, K / 32, 1),
+                W = mat(wq, 2 * N, K, K, 1), WS = mat(ws, 2 * N, K / 32, K / 32, 1),
+                Hh = mat(h, M, N, ld_h, 2);
+  if (any_overflow({Hh}) || Hh.bytes >= kOffsetLimit) return GLU_ERR_SHAPE;
+  return check_no_overlap({Hh}, {X, XS, W, WS});
+}
+
+glu_status glu_check_gemm_mxfp8(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                                uint8_t* q_row, uint8_t* s_row) {
+  if (!valid_act(act)) return GLU_ERR_ARG;
+  if (M < 0 || N < 0 || K < 0) return GLU_ERR_SHAPE;
+  if (M == 0 || N == 0) return GLU_OK;
+  glu_status st = check_gemm_inputs(M, N, K, xq, xs, wq, ws);
+  if (st != GLU_OK) return st;
+  if (q_row == nullptr || s_row == nullptr) return GLU_ERR_NULL;
+  if (!aligned16(q_row) || !aligned16(s_row)) return GLU_ERR_ALIGN;
+  const Operand X = mat(xq, M, K, K, 1), XS = mat(xs, M, K / 32, K / 32, 1),
+                W = mat(wq, 2 * N, K, K, 1), WS = mat(ws, 2 * N, K / 32, K / 32, 1),
+                Q = mat(q_row, M, N, N, 1), S = mat(s_row, M, N / 32, N / 32, 1);
+  if (any_overflow({Q, S}) || Q.bytes >= kOffsetLimit) return GLU_ERR_SHAPE;
+  return check_no_overlap({Q, S}, {X, XS, W, WS});
+}
+
+glu_status glu_check_mx_gemm_f32(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                 const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, float* y) {
+  if (M < 0 || N < 0 || K < 0) return GLU_ERR_SHAPE;
+  if (M == 0 || N == 0) return GLU_OK;
+  glu_status st = check_gemm_inputs(M, N, K, xq, xs, wq, ws);
+  if (st != GLU_OK) return st;
+  if (y == nullptr) return GLU_ERR_NULL;
+  if (!aligned16(y)) return GLU_ERR_ALIGN;
+  const Operand X = mat(xq, M, K, K, 1), XS = mat(xs, M, K / 32, K / 32, 1),
+                W = mat(wq, 2 * N, K, K, 1), WS = mat(ws, 2 * N, K / 32, K / 32, 1),
+                Y = mat(y, M, 2 * N, 2 * N, 4);
+  if (any_overflow({Y}) || Y.bytes >= kOffsetLimit) return GLU_ERR_SHAPE;
+  return check_no_overlap({Y}, {X, XS, W, WS});
+}
+
 glu_status glu_check_bwd_nvfp4(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
                                const uint16_t* up, int64_t ld_in, const uint16_t* dh,
                                int64_t ld_dh, uint8_t* q, uint8_t* sf, int sf_layout) {
@@ -502,6 +568,33 @@ glu_status glu_fwd_nvfp4_gs(int act, int layout, int64_t M, int64_t H, const uin
   if (st != GLU_OK || M == 0 || H == 0) return st;
   NvArgs a{act, layout, sf_layout, M, H, gate, up, ld_in, q, sf, nullptr, 0, amax, nullptr};
   return status_of(glu::launch_glu_fwd_nvfp4_gs(a, (hipStream_t)stream));
+}
+
+glu_status glu_gemm(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                    const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, uint16_t* h,
+                    int64_t ld_h, void* stream) {
+  glu_status st = glu_check_gemm(act, M, N, K, xq, xs, wq, ws, h, ld_h);
+  if (st != GLU_OK || M == 0 || N == 0) return st;
+  GemmArgs a{act, M, N, K, xq, xs, wq, ws, h, ld_h, nullptr, nullptr, nullptr};
+  return status_of(glu::launch_glu_gemm(a, (hipStream_t)stream));
+}
+
+glu_status glu_gemm_mxfp8(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                          const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                          uint8_t* q_row, uint8_t* s_row, void* stream) {
+  glu_status st = glu_check_gemm_mxfp8(act, M, N, K, xq, xs, wq, ws, q_row, s_row);
+  if (st != GLU_OK || M == 0 || N == 0) return st;
+  GemmArgs a{act, M, N, K, xq, xs, wq, ws, nullptr, 0, q_row, s_row, nullptr};
+  return status_of(glu::launch_glu_gemm_mxfp8(a, (hipStream_t)stream));
+}
+
+glu_status glu_mx_gemm_f32(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                           const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, float* y,
+                           void* stream) {
+  glu_status st = glu_check_mx_gemm_f32(M, N, K, xq, xs, wq, ws, y);
+  if (st != GLU_OK || M == 0 || N == 0) return st;
+  GemmArgs a{glu::SWIGLU, M, N, K, xq, xs, wq, ws, nullptr, 0, nullptr, nullptr, y};
+  return status_of(glu::launch_mx_gemm_f32(a, (hipStream_t)stream));
 }
 
 glu_status glu_bwd_nvfp4(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,

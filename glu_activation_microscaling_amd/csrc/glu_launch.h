@@ -55,6 +55,20 @@ struct NvArgs {
   float* amax_out;           // amax pass: where it goes (device memory)
 };
 
+struct GemmArgs {
+  int act;
+  int64_t M, N, K;           // X [M, K], W [2N, K]; the output has N columns
+  const uint8_t* xq;         // E4M3 codes [M, K]
+  const uint8_t* xs;         // E8M0 scales [M, K/32]
+  const uint8_t* wq;         // [W_gate | W_up] codes [2N, K]
+  const uint8_t* ws;         // scales [2N, K/32]
+  uint16_t* h;               // BF16 h [M, N], row stride ld_h
+  int64_t ld_h;
+  uint8_t* q_row;            // MXFP8 rowwise codes [M, N]
+  uint8_t* s_row;            // scales [M, N/32]
+  float* y;                  // test hook: the pre-activation [M, 2N]
+};
+
 hipError_t launch_glu_fwd_bf16(const BF16Args& a, hipStream_t s);
 hipError_t launch_glu_bwd_bf16(const BF16Args& a, hipStream_t s);
 hipError_t launch_glu_fwd_mxfp8(const MxArgs& a, hipStream_t s);
@@ -64,6 +78,9 @@ hipError_t launch_glu_fwd_nvfp4(const NvArgs& a, hipStream_t s);
 hipError_t launch_glu_bwd_nvfp4(const NvArgs& a, hipStream_t s);
 hipError_t launch_glu_fwd_nvfp4_gs(const NvArgs& a, hipStream_t s);
 hipError_t launch_glu_amax(const NvArgs& a, hipStream_t s);
+hipError_t launch_glu_gemm(const GemmArgs& a, hipStream_t s);
+hipError_t launch_glu_gemm_mxfp8(const GemmArgs& a, hipStream_t s);
+hipError_t launch_mx_gemm_f32(const GemmArgs& a, hipStream_t s);
 hipError_t launch_quant_nvfp4_f32(const NvArgs& a, hipStream_t s);
 
 // Launches kernel k and returns the launch status of this call alone (the HIP error

@@ -186,6 +186,32 @@ glu_status glu_fwd_nvfp4_gs(int act, int layout, int64_t M, int64_t H, const uin
                             const uint16_t* up, int64_t ld_in, const float* amax, uint8_t* q,
                             uint8_t* sf, int sf_layout, void* stream);
 
+/* ---- Merged gate/up MXFP8 GEMM with the GLU as its epilogue ([NV] Summary: the fold
+ * follows the merged GEMM; [MX] Performance: the fused-w13 MoE composite under an MXFP8
+ * recipe; [MX] API: a fused w13 projection packs [gate | up]).  The pre-activation is never
+ * written.
+ *   Y = X W^T: xq [M, K] E4M3 codes, xs [M, K/32] E8M0 scales (32-element blocks along K),
+ *   wq [2N, K] = [W_gate | W_up] codes, ws [2N, K/32] scales; all row-major, K contiguous.
+ *   h = bf16(act(Y[:, j]) * Y[:, N + j]), Y accumulated in FP32 by the matrix cores.
+ * The matrix cores add the products of each 8-element K chunk in a 14-bit fixed-point
+ * window anchored at the chunk's largest product (smaller bits are dropped), then add the
+ * chunk sums into FP32 one at a time.  Y thus differs from the exact product sum by at most
+ * sum over chunks of 2^-10 * (largest |x_k w_k| of the chunk), plus (K/8) * 2^-23 * sum |x_k w_k|.
+ * Each row of h depends only on that row of X and on W, bit for bit.
+ * Needs K % 128 == 0, K > 0, N % 128 == 0 (GLU_ERR_SHAPE); every operand and output below
+ * 2^31 bytes (GLU_ERR_SHAPE); 16-byte aligned pointers (GLU_ERR_ALIGN). */
+glu_status glu_gemm(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                    const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, uint16_t* h,
+                    int64_t ld_h, void* stream);
+/* The same h quantized MXFP8 rowwise (as glu_fwd_mxfp8): q_row [M, N], s_row [M, N/32]. */
+glu_status glu_gemm_mxfp8(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                          const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                          uint8_t* q_row, uint8_t* s_row, void* stream);
+/* Test hook: the FP32 GEMM alone, y [M, 2N], formed exactly as the fused kernels form it. */
+glu_status glu_mx_gemm_f32(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                           const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, float* y,
+                           void* stream);
+
 /* ---- Fused backward + NVFP4, global scale 1 (no page defines an NVFP4 backward: the
  * placement is glu_bwd_mxfp8's, [MX] API; the block arithmetic is glu_fwd_nvfp4's, [NV]
  * Supported contract).  The quantized matrix is X = [da | db], [M, 2N], with da, db as in
@@ -236,6 +262,15 @@ glu_status glu_check_amax(int act, int layout, int64_t M, int64_t N, const uint1
 glu_status glu_check_fwd_nvfp4_gs(int act, int layout, int64_t M, int64_t H,
                                   const uint16_t* gate, const uint16_t* up, int64_t ld_in,
                                   const float* amax, uint8_t* q, uint8_t* sf, int sf_layout);
+glu_status glu_check_gemm(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                          const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, uint16_t* h,
+                          int64_t ld_h);
+glu_status glu_check_gemm_mxfp8(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                                uint8_t* q_row, uint8_t* s_row);
+glu_status glu_check_mx_gemm_f32(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                 const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                                 float* y);
 glu_status glu_check_bwd_nvfp4(int act, int layout, int64_t M, int64_t N,
                                const uint16_t* gate, const uint16_t* up, int64_t ld_in,
                                const uint16_t* dh, int64_t ld_dh, uint8_t* q, uint8_t* sf,

@@ -256,6 +256,40 @@ def test_quant_hook_checks():
     assert n(64, 72, P(A0), 72, P(B0), P(C0), 0) == SHAPE
 
 
+def test_gemm_checks():
+    g = lambda **kw: _gemm(L.glu_check_gemm, **kw)
+    assert g() == OK and g(act=3) == OK and g(act=4) == ARG
+    assert g(M=0) == OK and g(M=-1) == SHAPE and g(K=0) == SHAPE
+    assert g(K=96) == SHAPE and g(N=64, ldh=64) == SHAPE              # K % 128, N % 128
+    assert g(xq=0) == NULL and g(ws=0) == NULL and g(h=0) == NULL
+    assert g(xs=B0 + 4) == ALIGN and g(h=E0 + 2) == ALIGN and g(ldh=136) == OK
+    assert g(ldh=120) == STRIDE and g(ldh=132) == ALIGN
+    assert g(h=A0 + 64) == OVERLAP                                    # h over X
+    # 32-bit offsets: X, W and h each below 2^31 bytes (an FP32 [M, 2N] would not be)
+    assert g(M=1 << 24, K=128, ldh=128) == SHAPE
+    assert g(M=1 << 22, K=128, ldh=128, h=F0 * 64) == OK
+    assert g(M=1 << 22, K=128, ldh=512, h=F0 * 64) == SHAPE
+    assert g(N=1 << 23, K=128, ldh=1 << 23, M=1) == SHAPE             # W is 2N x K
+    q = lambda **kw: _gemm(L.glu_check_gemm_mxfp8, **kw)
+    assert q() == OK and q(q=0) == NULL and q(s=E0 + 1) == ALIGN and q(act=7) == ARG
+    assert q(s=D0 + 64 * 128 - 16) == OVERLAP and q(s=D0 + 64 * 128) == OK
+    y = lambda **kw: _gemm(L.glu_check_mx_gemm_f32, **kw)
+    assert y() == OK and y(y=0) == NULL and y(y=D0 + 4) == ALIGN
+    assert y(M=1 << 20, K=128, N=256, y=F0 * 64) == SHAPE             # y is M x 2N x 4 bytes
+    assert y(M=(1 << 20) - 8, K=128, N=256, y=F0 * 64) == OK
+
+
+def _gemm(fn, act=0, M=64, N=128, K=256, xq=A0, xs=B0, wq=C0, ws=A0 // 2, h=E0, ldh=128,
+          q=D0, s=E0, y=D0):
+    """Fake operands: X [M, K] at A0, its scales at B0, W [2N, K] at C0, W's scales at A0/2."""
+    ops = [P(xq), P(xs), P(wq), P(ws)]
+    if fn is L.glu_check_gemm:
+        return fn(act, M, N, K, *ops, P(h), ldh)
+    if fn is L.glu_check_gemm_mxfp8:
+        return fn(act, M, N, K, *ops, P(q), P(s))
+    return fn(M, N, K, *ops, P(y))
+
+
 def test_entry_points_fail_before_any_hip_call():
     """Rejected arguments and empty problems return without touching HIP, so these calls
     are safe on a machine with no GPU."""
@@ -271,6 +305,9 @@ def test_entry_points_fail_before_any_hip_call():
     assert L.glu_fwd_nvfp4_gs(1, 1, 0, 32, P(0), P(0), 64, P(0), P(0), P(0), 0, P(0)) == OK
     assert L.glu_quant_mxfp8_f32(32, 32, P(A0), 32, 8, P(B0), P(C0), P(D0), P(E0), P(0)) == ARG
     assert L.glu_quant_nvfp4_f32(32, 32, P(A0 + 4), 32, P(B0), P(C0), 0, P(0)) == ALIGN
+    assert L.glu_gemm(0, 8, 64, 128, P(A0), P(B0), P(C0), P(D0), P(E0), 64, P(0)) == SHAPE
+    assert L.glu_gemm_mxfp8(0, 0, 128, 128, P(0), P(0), P(0), P(0), P(0), P(0), P(0)) == OK
+    assert L.glu_mx_gemm_f32(8, 128, 100, P(A0), P(B0), P(C0), P(D0), P(E0), P(0)) == SHAPE
 
 
 def test_binding_refuses_cpu_tensors():
