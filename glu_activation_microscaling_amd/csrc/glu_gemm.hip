@@ -17,12 +17,30 @@
 // sign), and the chunk sums are added to the FP32 accumulator one at a time with FP32
 // rounding.
 //
-// Work decomposition: a workgroup of 4 waves owns 128 rows x 128 output columns, i.e. 128 gate
-// and 128 up rows of W; each wave a 64 x 64 quarter, holding the gate and up accumulators of
-// the same (row, column) positions (4 x 4 tiles of 16 x 16 each, in the accumulation
-// registers), so the GLU is applied in registers.  Operands are read straight into the
-// matrix-core layout with 16-byte raw buffer loads (rows past M read zeros), two K steps of
-// 128 in flight: one step's loads are issued before the previous step's products.
+// Work decomposition: a workgroup of 8 waves (two per SIMD, so one wave's LDS reads overlap
+// the other's matrix instructions) owns 256 rows x 128 output columns, i.e. 128 gate and 128
+// up rows of W.  Each wave holds a 64 x 64 block: the gate and the up accumulators of the
+// same (row, column) positions (4 x 4 tiles of 16 x 16 each), so the GLU is applied in
+// registers.
+//
+// Operand staging: each 128-byte K step of the workgroup's 256 X rows and 256 W rows
+// (64 KiB) is copied into LDS by direct-to-LDS buffer loads, which place lane l's 16 bytes at
+// 16 l of a 1 KiB block.  Each group of 8 lanes fetches one row's whole 128-byte line, and
+// lane l puts global chunk (l % 8) ^ ((row / 2) % 8) at chunk l % 8 of the row, so the
+// fragment reads (row r, chunks g and g + 4 per lane) hit distinct LDS banks.  Two stages
+// alternate: the loads of step t + 1 are issued right after the barrier of step t and have
+// step t's matrix work to arrive.  The E8M0 scales come in groups of 4 K steps (16 bytes a
+// row, 4 lanes a row) into a ring of two groups.  Rows past M read zeros.
+//
+// Epilogue: per 16-row slice, the GLU in FP32 for all elements, one wave-wide branch for
+// the rare tail elements, BF16 pairs by the hardware converter, then (MXFP8) the block amax
+// over the 16 lanes of a DPP row and the scaled E4M3 converter.  A transpose within each
+// 16-lane row group (ds_bpermute) gives each lane 4 consecutive columns, stored at once.
+//
+// Tile order: workgroups are spread over the 8 XCDs in turn, so workgroup b is given tile
+// (b mod 8) * (tiles / 8) + b / 8, which keeps each XCD on a contiguous run of tiles, and
+// tiles run down groups of 8 row tiles before moving to the next column tile, so the
+// workgroups resident on one XCD share X and W in its L2.
 #include "glu_device.h"
 #include "glu_launch.h"
 
@@ -31,60 +49,133 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
-constexpr int GM_THREADS = 256;
-#ifndef GLU_GEMM_WN                                   // build-time override, for measurements
-#define GLU_GEMM_WN 4
-#endif
-constexpr int WM = 4, WN = GLU_GEMM_WN;               // 16x16 tiles per wave: rows, columns
-constexpr int GM_BM = 2 * 16 * WM, GM_BN = 2 * 16 * WN, GM_BK = 128;  // workgroup tile, K step
+constexpr int GM_THREADS = 512;
+constexpr int WM = 4, WN = 4;                         // 16x16 tiles per wave: rows, columns
+constexpr int GM_BM = 4 * 16 * WM, GM_BN = 2 * 16 * WN, GM_BK = 128;  // workgroup tile, K step
 static_assert(WN % 2 == 0, "an MXFP8 block is two 16-column tiles");
+constexpr int GROUP_M = 8;                            // row tiles per group of the tile order
+
+// LDS stage: 16 X slices, then 16 W slices (gate 0..7, up 8..15), 2 KiB each.
+constexpr uint32_t X_SLICES = GM_BM / 16, W_SLICES = 2 * GM_BN / 16;
+constexpr uint32_t W_OFF = X_SLICES * 2048u;
+constexpr uint32_t STAGE = W_OFF + W_SLICES * 2048u;
+constexpr int STAGES = 2;
+// Scale ring: 2 groups of 4 K steps; a group holds 16 bytes (4 steps x 4 blocks) per row,
+// X rows 0..255 then W rows 256..511.
+constexpr uint32_t SC_ROWS = GM_BM + 2 * GM_BN, SC_GROUP = 16u * SC_ROWS, SC_OFF = STAGES * STAGE;
+static_assert(SC_OFF + 2 * SC_GROUP <= 160u * 1024u, "LDS");
+constexpr int OP_LOADS = 2 * 2 + 2 * 2;               // per wave and K step: X, W
+constexpr int SC_LOADS = SC_ROWS / 16 / 8;            // per wave and group: 16 rows each
 
 enum { GEMM_H = 0, GEMM_MXFP8 = 1, GEMM_F32 = 2 };
 
-// One lane's 32 bytes of a 16-row operand slice at K step k0: chunks g and g + 4.
-__device__ __forceinline__ v8i frag(__amdgpu_buffer_rsrc_t r, uint32_t row_off, bool ok,
-                                    uint32_t k0, uint32_t g) {
-  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, ok ? row_off + k0 + 16u * g : kOob, 0, 0);
-  const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, ok ? row_off + k0 + 64u + 16u * g : kOob, 0, 0);
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 4, off, 0, 0, 0);
+}
+
+// s_waitcnt on the vector-memory counter alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Barrier that also orders the workgroup's LDS accesses (no wait on global memory).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ v8i frag(const uint8_t* blk, uint32_t oa, uint32_t ob) {
+  const u32x4 a = *(const u32x4*)(blk + oa);
+  const u32x4 b = *(const u32x4*)(blk + ob);
   return (v8i){(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
-// The lane's scale byte: block g of the K step, from the row's 4 scale bytes of the step.
-__device__ __forceinline__ int scale_of(__amdgpu_buffer_rsrc_t r, uint32_t srow_off, bool ok,
-                                        uint32_t kb0, uint32_t g) {
-  const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, ok ? srow_off + kb0 : kOob, 0, 0);
-  return (int)((w >> (8u * g)) & 0xffu);
-}
-
 template <int ACT, int OUT>
-__global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t tiles_n) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t g = (uint32_t)lane >> 4, r = (uint32_t)lane & 15u;
-  const uint32_t tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+__global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t tiles_m, uint32_t tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SC_OFF + 2 * SC_GROUP];
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t g = lane >> 4, r = lane & 15u;
+
+  // tile of this workgroup: XCD-contiguous runs, grouped row-tile order
+  const uint32_t tiles = tiles_m * tiles_n, per_xcd = tiles / 8u, b = blockIdx.x;
+  const uint32_t t = b < 8u * per_xcd ? (b % 8u) * per_xcd + b / 8u : b;
+  const uint32_t in_group = GROUP_M * tiles_n, first_m = (t / in_group) * GROUP_M;
+  const uint32_t gm = min(tiles_m - first_m, (uint32_t)GROUP_M);
+  const uint32_t tm = first_m + (t % in_group) % gm, tn = (t % in_group) / gm;
+
   const uint32_t row0 = tm * GM_BM + (wave >> 1) * (16 * WM);  // the wave's first row
   const uint32_t col0 = tn * GM_BN + (wave & 1) * (16 * WN);   // its first output column
-  const uint32_t K = (uint32_t)a.K, KB = K / 32u, N = (uint32_t)a.N;
+  const uint32_t K = (uint32_t)a.K, KB = K / 32u, N = (uint32_t)a.N, M = (uint32_t)a.M;
+  const uint32_t T = K / GM_BK;                                 // K steps
 
+  // Load assignment (per wave, the same count every step): X slices 2w, 2w + 1 and W slices
+  // 2w, 2w + 1, two loads of 8 rows each.  Lane l of load h of a slice: slice row
+  // 8 h + l / 8, LDS chunk l % 8 <- global chunk (l % 8) ^ ((slice row / 2) % 8).
   const auto rx = rsrc(a.xq), rxs = rsrc(a.xs), rw = rsrc(a.wq), rws = rsrc(a.ws);
-  uint32_t xo[WM], xso[WM];
-  bool xok[WM];
+  uint32_t xoff[2], woff[2];
+  const uint32_t lrow = lane >> 3;                                   // + 8 h
+  uint32_t lchunk[2];
 #pragma unroll
-  for (int i = 0; i < WM; i++) {
-    const uint32_t row = row0 + 16u * i + r;
-    xok[i] = row < (uint32_t)a.M;
-    xo[i] = row * K;
-    xso[i] = row * KB;
+  for (int h = 0; h < 2; h++) lchunk[h] = 16u * ((lane & 7u) ^ (((8u * h + lrow) >> 1) & 7u));
+  bool xokh[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const uint32_t row = tm * GM_BM + 16u * (2u * wave + i) + lrow;
+    xoff[i] = row * K;
+#pragma unroll
+    for (int h = 0; h < 2; h++) xokh[i][h] = row + 8u * h < M;
   }
-  uint32_t wo[2][WN], wso[2][WN];  // [gate, up][tile]: W rows col0 + 16 j + r and N + ...
 #pragma unroll
-  for (int h = 0; h < 2; h++)
+  for (int i = 0; i < 2; i++) {
+    const uint32_t sl = 2u * wave + i;                           // 0..7 gate, 8..15 up
+    const uint32_t wrow = (sl < 8u ? 0u : N - 8u * 16u) + tn * GM_BN + 16u * sl + lrow;
+    woff[i] = wrow * K;
+  }
+  // scale load i of a group: rows 16 q .. 16 q + 15, q = SC_LOADS w + i; lane l reads the
+  // word of step 4 j + l % 4 of row 16 q + l / 4
+  uint32_t soff[SC_LOADS];
+  bool sok[SC_LOADS], sx[SC_LOADS];
 #pragma unroll
-    for (int j = 0; j < WN; j++) {
-      const uint32_t wrow = h * N + col0 + 16u * j + r;
-      wo[h][j] = wrow * K;
-      wso[h][j] = wrow * KB;
+  for (int i = 0; i < SC_LOADS; i++) {
+    const uint32_t row = 16u * (SC_LOADS * wave + i) + (lane >> 2);
+    if (row < (uint32_t)GM_BM) {
+      const uint32_t grow = tm * GM_BM + row;
+      sx[i] = true; sok[i] = grow < M; soff[i] = grow * KB + 4u * (lane & 3u);
+    } else {
+      const uint32_t wr = row - GM_BM;
+      const uint32_t wrow = (wr < (uint32_t)GM_BN ? 0u : N - GM_BN) + tn * GM_BN + wr;
+      sx[i] = false; sok[i] = true; soff[i] = wrow * KB + 4u * (lane & 3u);
     }
+  }
+  auto issue_scales = [&](uint32_t grp) {
+    uint8_t* sc = smem + SC_OFF + (grp & 1u) * SC_GROUP;
+    const bool live = 4u * grp + (lane & 3u) < T;
+#pragma unroll
+    for (int i = 0; i < SC_LOADS; i++)
+      dma4(sx[i] ? rxs : rws, sok[i] && live ? soff[i] + 16u * grp : kOob, sc + 256u * (SC_LOADS * wave + i));
+  };
+  auto issue = [&](uint32_t step, uint32_t stage) {
+    uint8_t* st = smem + stage * STAGE;
+    const uint32_t k0 = step * GM_BK;
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+        dma16(rx, xokh[i][h] ? xoff[i] + 8u * h * K + k0 + lchunk[h] : kOob, st + (2u * (2u * wave + i) + h) * 1024u);
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+        dma16(rw, woff[i] + 8u * h * K + k0 + lchunk[h], st + W_OFF + (2u * (2u * wave + i) + h) * 1024u);
+  };
 
   v4f acc[2][WM][WN];
 #pragma unroll
@@ -94,30 +185,33 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
 #pragma unroll
       for (int j = 0; j < WN; j++) acc[h][i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Operand fragments of one K step (the lane's part of the matrix-core layout).
-  struct Step {
+  const uint32_t fo_a = 128u * r + 16u * (g ^ ((r >> 1) & 7u));
+  const uint32_t fo_b = 128u * r + 16u * ((g + 4u) ^ ((r >> 1) & 7u));
+  issue_scales(0);
+  issue(0, 0);
+  for (uint32_t step = 0; step < T; step++) {
+    wait_vm<0>();
+    lds_barrier();   // every wave's loads of this step have landed; step - 1's stage is free
+    if (step % 4u == 0u && step + 4u < T) issue_scales(step / 4u + 1u);
+    if (step + 1u < T) issue(step + 1u, (step + 1u) % STAGES);
+    const uint8_t* st = smem + (step % STAGES) * STAGE;
+    const uint8_t* sc = smem + SC_OFF + ((step / 4u) & 1u) * SC_GROUP + 4u * (step % 4u) + g;
     v8i xa[WM], wb[2][WN];
     int xs[WM], ws[2][WN];
-  };
-  // Loads of the K step at k0; past K every load reads zeros (and zero scales), which add
-  // nothing, so the two-step loop below needs no tail.
-  auto load = [&](Step& st, uint32_t k0) {
-    const bool in = k0 < K;
-    const uint32_t kb0 = k0 / 32u;
 #pragma unroll
     for (int i = 0; i < WM; i++) {
-      st.xa[i] = frag(rx, xo[i], xok[i] && in, k0, g);
-      st.xs[i] = scale_of(rxs, xso[i], xok[i] && in, kb0, g);
+      const uint32_t sl = (wave >> 1) * WM + i;
+      xa[i] = frag(st + 2048u * sl, fo_a, fo_b);
+      xs[i] = sc[16u * (16u * sl + r)];
     }
 #pragma unroll
     for (int h = 0; h < 2; h++)
 #pragma unroll
       for (int j = 0; j < WN; j++) {
-        st.wb[h][j] = frag(rw, wo[h][j], in, k0, g);
-        st.ws[h][j] = scale_of(rws, wso[h][j], in, kb0, g);
+        const uint32_t sl = 8u * h + (wave & 1) * WN + j;
+        wb[h][j] = frag(st + W_OFF + 2048u * sl, fo_a, fo_b);
+        ws[h][j] = sc[16u * (GM_BM + 16u * sl + r)];
       }
-  };
-  auto mma = [&](const Step& st) {
 #pragma unroll
     for (int h = 0; h < 2; h++)
 #pragma unroll
@@ -125,17 +219,7 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
 #pragma unroll
         for (int j = 0; j < WN; j++)
           acc[h][i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              st.xa[i], st.wb[h][j], acc[h][i][j], 0, 0, 0, st.xs[i], 0, st.ws[h][j]);
-  };
-  // Two register buffers: the loads of one K step are in flight while the other's products
-  // issue.
-  Step s0, s1;
-  load(s0, 0);
-  for (uint32_t k0 = 0; k0 < K; k0 += 2 * GM_BK) {
-    load(s1, k0 + GM_BK);
-    mma(s0);
-    load(s0, k0 + 2 * GM_BK);
-    mma(s1);
+              xa[i], wb[h][j], acc[h][i][j], 0, 0, 0, xs[i], 0, ws[h][j]);
   }
 
   // Epilogue.  acc[h][i][j][e] is Y at row row0 + 16 i + 4 g + e, column col0 + 16 j + r of
@@ -157,65 +241,81 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
                                                   row < (uint32_t)a.M ? 4u * (row * 2u * N + col) : kOob, 0, 0);
           }
   } else {
-    // h = bf16(act(gate) * up); the tail path covers gates whose activation leaves FP32
-    uint32_t hb[WM][WN][4];
+    // h = bf16(act(gate) * up), one 16-row slice i at a time (so that the slice's
+    // accumulators die as it is written): the fast form for every element, then the tail
+    // form where the fast one leaves FP32 (one branch per slice for the whole wave, rarely
+    // taken).  The BF16 pair P[e][b] holds tiles 2b (low half) and 2b + 1 of row
+    // 16 i + 4 g + e.  Stores: within each 16-lane row group the pairs are transposed so that
+    // lane r holds columns col0 + 4r .. 4r + 3 (lane 4 (r % 4) + k holds column 4r + k in
+    // tile r / 4), and each lane writes them with one store.
+    static_assert(WN == 4, "two BF16 pairs per row and lane");
+    auto gather = [&](uint32_t v, uint32_t k) {
+      return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(4u * (16u * g + 4u * (r & 3u) + k)), (int)v);
+    };
+    const uint32_t sel = r >> 2;   // the source tile of this lane's columns
+    const auto rh = rsrc(a.h), rq = rsrc(a.q_row), rs = rsrc(a.s_row);
+    const uint32_t NB = N / 32u;
 #pragma unroll
-    for (int i = 0; i < WM; i++)
+    for (int i = 0; i < WM; i++) {
+      float hv[WN][4];
+      bool tail = false;
 #pragma unroll
       for (int j = 0; j < WN; j++)
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const float gv = acc[0][i][j][e], uv = acc[1][i][j][e];
-          float hv = glu_fwd_fast<ACT>(gv, uv);
-          if (fwd_tail_needed<ACT>(gv, uv)) hv = glu_fwd_tail<ACT>(gv, uv);
-          hb[i][j][e] = bf16_rne(hv);
-        }
-    if constexpr (OUT == GEMM_H) {
-      const auto rh = rsrc(a.h);
-#pragma unroll
-      for (int i = 0; i < WM; i++)
+        for (int e = 0; e < 4; e++) hv[j][e] = glu_fwd_elem<ACT>(acc[0][i][j][e], acc[1][i][j][e], tail);
+      if (tail) {
 #pragma unroll
         for (int j = 0; j < WN; j++)
 #pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const uint32_t row = row0 + 16u * i + 4u * g + (uint32_t)e;
-            const uint32_t col = col0 + 16u * j + r;
-            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hb[i][j][e], rh,
-                                                  row < (uint32_t)a.M ? 2u * (row * (uint32_t)a.ld_h + col) : kOob, 0, 0);
+          for (int e = 0; e < 4; e++)
+            if (fwd_tail_needed<ACT>(acc[0][i][j][e], acc[1][i][j][e]))
+              hv[j][e] = glu_fwd_tail<ACT>(acc[0][i][j][e], acc[1][i][j][e]);
+      }
+      uint32_t P[4][2];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        P[e][0] = pack_bf16(hv[0][e], hv[1][e]);
+        P[e][1] = pack_bf16(hv[2][e], hv[3][e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const uint32_t row = row0 + 16u * i + 4u * g + (uint32_t)e;
+        const bool ok = row < M;
+        if constexpr (OUT == GEMM_H) {
+          uint32_t v[4];
+#pragma unroll
+          for (int k = 0; k < 4; k++) {
+            const uint32_t w0 = gather(P[e][0], k), w1 = gather(P[e][1], k);
+            v[k] = ((sel < 2u ? w0 : w1) >> (16u * (sel & 1u))) & 0xffffu;
           }
-    } else {
-      // MXFP8 rowwise: the wave's columns of a row form WN / 2 blocks of 32 (tiles 2b and
-      // 2b + 1); a row's values sit in the 16 lanes of one DPP row (columns r and 16 + r)
-      const auto rq = rsrc(a.q_row), rs = rsrc(a.s_row);
-      const uint32_t NB = N / 32u;
+          __builtin_amdgcn_raw_buffer_store_b64((v2u){v[0] | (v[1] << 16), v[2] | (v[3] << 16)}, rh,
+                                                ok ? 2u * (row * (uint32_t)a.ld_h + col0 + 4u * r) : kOob, 0, 0);
+        } else {
+          // MXFP8 rowwise: the wave's 64 columns of a row are two blocks of 32 (pair b holds
+          // block b's two elements of this lane); a row sits in the 16 lanes of one DPP row
+          uint32_t codes = 0, sbs = 0;
 #pragma unroll
-      for (int i = 0; i < WM; i++)
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const uint32_t row = row0 + 16u * i + 4u * g + (uint32_t)e;
-          const bool ok = row < (uint32_t)a.M;
-#pragma unroll
-          for (int b = 0; b < WN / 2; b++) {
-            uint32_t m = umax(hb[i][2 * b][e] & 0x7fffu, hb[i][2 * b + 1][e] & 0x7fffu);
+          for (int b = 0; b < 2; b++) {
+            const uint32_t p = P[e][b];
+            uint32_t m = umax(p & 0x7fffu, (p >> 16) & 0x7fffu);
             m = umax(m, dpp<DPP_XOR1>(m));
             m = umax(m, dpp<DPP_XOR2>(m));
             m = umax(m, dpp<0x124>(m));  // row_ror:4
             m = umax(m, dpp<DPP_ROW_ROR8>(m));
             const bool nonfinite = m >= 0x7f80u;
             const uint32_t sb = nonfinite ? 0xffu : mx_scale_byte(m << 16);
-            const float inv = nonfinite ? 1.0f : mx_inv_scale(sb);
-#pragma unroll
-            for (int t = 0; t < 2; t++) {
-              const int j = 2 * b + t;
-              const uint32_t code = nonfinite
-                  ? 0x7fu
-                  : fp8x2<false>(0u, __uint_as_float(hb[i][j][e] << 16) * inv, 0.0f) & 0xffu;
-              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, rq, ok ? row * N + col0 + 16u * j + r : kOob, 0, 0);
-            }
-            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, rs,
-                                                 ok && r == 0 ? row * NB + (col0 + 32u * b) / 32u : kOob, 0, 0);
+            sbs |= sb << (8 * b);
+            const uint32_t c = b == 0 ? fp8x2_scaled<false>(0u, p, e8m0_value(sb))
+                                      : fp8x2_scaled<true>(0u, p, e8m0_value(sb));
+            codes |= nonfinite ? 0x7f7fu << (16 * b) : c;
           }
+          uint32_t v = 0;
+#pragma unroll
+          for (int k = 0; k < 4; k++) v |= ((gather(codes, k) >> (8u * sel)) & 0xffu) << (8 * k);
+          __builtin_amdgcn_raw_buffer_store_b32(v, rq, ok ? row * N + col0 + 4u * r : kOob, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sbs, rs, ok && r == 0 ? row * NB + col0 / 32u : kOob, 0, 0);
         }
+      }
     }
   }
 }
@@ -225,11 +325,11 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
   const uint32_t tiles_m = (uint32_t)((a.M + GM_BM - 1) / GM_BM), tiles_n = (uint32_t)(a.N / GM_BN);
   const dim3 grid(tiles_m * tiles_n), block(GM_THREADS);
   if constexpr (OUT == GEMM_F32) {
-    return launch_kernel(k_glu_gemm<SWIGLU, GEMM_F32>, grid, block, s, a, tiles_n);
+    return launch_kernel(k_glu_gemm<SWIGLU, GEMM_F32>, grid, block, s, a, tiles_m, tiles_n);
   } else {
     return with_act(a.act, [&](auto A) {
       constexpr int ACT = decltype(A)::value;
-      return launch_kernel(k_glu_gemm<ACT, OUT>, grid, block, s, a, tiles_n);
+      return launch_kernel(k_glu_gemm<ACT, OUT>, grid, block, s, a, tiles_m, tiles_n);
     });
   }
 }

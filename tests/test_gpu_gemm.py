@@ -43,7 +43,8 @@ def _dequant(q, s):
     return v * np.repeat(np.exp2(s.numpy().astype(np.float64) - 127.0), 32, axis=1)
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 128, 512), (200, 128, 256), (128, 256, 2048), (37, 128, 128), (96, 384, 384)])
+@pytest.mark.parametrize("M,N,K", [(256, 128, 512), (200, 128, 256), (128, 256, 2048), (37, 128, 128),
+                                   (96, 384, 384), (64, 128, 640), (300, 256, 1152)])
 def test_gemm_within_the_accumulation_bound(gpu, M, N, K):
     ops = _operands(M, N, K, seed=M + N + K)
     y = gpu.mx_gemm_f32(*(t.cuda() for t in ops)).cpu().numpy().astype(np.float64)
