@@ -127,3 +127,30 @@ def test_gemm_end_to_end_against_the_exact_oracle(gpu):
     ho = oracle.glu_gemm(oracle.SWIGLU, *(t.numpy() for t in ops))
     same = float((h == ho).mean())
     assert same > 0.5, f"only {same:.3f} of h identical to the exact oracle"
+
+
+@pytest.mark.parametrize("act,kind", [ACTS[0], ACTS[2]])
+def test_nan_codes_and_scales(gpu, act, kind):
+    """The MX encodings' NaNs (E4M3 codes 0x7F and 0xFF, E8M0 scale byte 0xFF) make every
+    product they enter NaN, as the oracle reads the formats: a NaN in X poisons a row of Y,
+    a NaN in W a column.  h is NaN wherever its gate or up value is, and its MXFP8 blocks
+    holding NaN get scale 0xFF and NaN codes."""
+    M, N, K = 64, 128, 256
+    xq, xs, wq, ws = _operands(M, N, K, seed=90)
+    xq[3, 5] = 0x7F          # NaN code: row 3
+    xs[7, 2] = 0xFF          # NaN scale of K block 2: row 7
+    wq[11, 200] = 0xFF       # NaN code (sign set): gate column 11
+    ws[N + 40, 1] = 0xFF     # NaN scale: up column 40
+    ops = (xq, xs, wq, ws)
+    dev = [t.cuda() for t in ops]
+    y = gpu.mx_gemm_f32(*dev).cpu().numpy().astype(np.float64)
+    exact = oracle.mx_gemm_nt(*(t.numpy() for t in ops))
+    assert np.array_equal(np.isnan(y), np.isnan(exact))
+    assert np.isnan(exact[[3, 7]]).all() and np.isnan(exact[:, [11, N + 40]]).all()
+    assert np.isnan(exact).sum() == 2 * 2 * N + 2 * M - 4
+    h = bits(gpu.glu_gemm(*dev, act=act))
+    check_rule2(h, oracle.bf16_from_f64(oracle.act(kind, y[:, :N]) * y[:, N:]), f"{act} NaN epilogue")
+    q, sc = gpu.glu_gemm_mxfp8(*dev, act=act)
+    o = oracle.quant_mxfp8(si.from_bits(h).float().numpy(), oracle.ROWWISE)
+    assert np.array_equal(u8(sc), o[1]) and np.array_equal(u8(q), o[0])
+    assert (u8(sc)[[3, 7]] == 0xFF).all() and (u8(sc)[:, [0, 1]] == 0xFF).all()
