@@ -13,6 +13,8 @@ that torch.compile keeps whole; these ops do the same for the MI355X kernels:
   torch.ops.glu_mx.glu_backward_nvfp4(gate, up, dh, act, sf_layout)    -> (q, sf)
   torch.ops.glu_mx.glu_amax(gate, up, act, layout)                     -> amax [1]
   torch.ops.glu_mx.glu_nvfp4_gs(x, up, amax, act, layout, sf_layout)   -> (q, sf)
+  torch.ops.glu_mx.glu_gemm(xq, xs, wq, ws, act)                       -> h
+  torch.ops.glu_mx.glu_gemm_mxfp8(xq, xs, wq, ws, act)                 -> (q_row, s_row)
 
 Each real implementation is the binding function of the same name (argument marshalling;
 the HIP kernels compute everything).  Each fake implementation gives the output shapes and
@@ -30,7 +32,8 @@ from torch import Tensor
 
 from . import (glu_amax as _amax, glu_bwd as _bwd, glu_bwd_mxfp8 as _bwd_mx,
                glu_bwd_nvfp4 as _bwd_nv, glu_fwd as _fwd, glu_fwd_mxfp8 as _fwd_mx,
-               glu_fwd_nvfp4 as _fwd_nv, glu_fwd_nvfp4_gs as _fwd_nv_gs)
+               glu_fwd_nvfp4 as _fwd_nv, glu_fwd_nvfp4_gs as _fwd_nv_gs, glu_gemm as _gemm,
+               glu_gemm_mxfp8 as _gemm_mx)
 
 _LIB = "glu_mx"
 
@@ -187,3 +190,28 @@ def _(x, up, amax, act="geglu", layout="paired", sf_layout="rowmajor"):
     M, H = x.shape[0], _width(x, layout)
     return (x.new_empty((M, H // 2), dtype=torch.uint8),
             x.new_empty(_nv_scale_shape(M, H, sf_layout), dtype=torch.uint8))
+
+
+# ---- merged gate/up MXFP8 GEMM with the GLU epilogue --------------------------------
+# xq [M, K] E4M3 codes, xs [M, K/32] E8M0 scales, wq [2N, K] = [W_gate | W_up], ws [2N, K/32]
+
+@torch.library.custom_op(f"{_LIB}::glu_gemm", mutates_args=())
+def glu_gemm(xq: Tensor, xs: Tensor, wq: Tensor, ws: Tensor, act: str = "swiglu") -> Tensor:
+    return _gemm(xq, xs, wq, ws, act=act)
+
+
+@glu_gemm.register_fake
+def _(xq, xs, wq, ws, act="swiglu"):
+    return xq.new_empty((xq.shape[0], wq.shape[0] // 2), dtype=torch.bfloat16)
+
+
+@torch.library.custom_op(f"{_LIB}::glu_gemm_mxfp8", mutates_args=())
+def glu_gemm_mxfp8(xq: Tensor, xs: Tensor, wq: Tensor, ws: Tensor,
+                   act: str = "swiglu") -> Tuple[Tensor, Tensor]:
+    return _gemm_mx(xq, xs, wq, ws, act=act)
+
+
+@glu_gemm_mxfp8.register_fake
+def _(xq, xs, wq, ws, act="swiglu"):
+    M, N = xq.shape[0], wq.shape[0] // 2
+    return xq.new_empty((M, N), dtype=torch.uint8), xq.new_empty((M, N // 32), dtype=torch.uint8)

@@ -38,6 +38,15 @@ def test_ops_equal_the_binding(gpu):
     assert torch.equal(a, gpu.glu_amax(p, act="geglu", layout="paired"))
     assert _same(ops.glu_nvfp4_gs(p, e, a, "geglu", "paired", "rowmajor"),
                  gpu.glu_fwd_nvfp4_gs(p, amax=a, act="geglu", layout="paired"))
+    mx = _mx_operands(96, 128, 256, 65)
+    assert _same([ops.glu_gemm(*mx, "geglu")], [gpu.glu_gemm(*mx, act="geglu")])
+    assert _same(ops.glu_gemm_mxfp8(*mx, "swiglu"), gpu.glu_gemm_mxfp8(*mx))
+
+
+def _mx_operands(M, N, K, seed):
+    xq, xs = si.mx_operand(M, K, seed=seed, device="cuda")
+    wq, ws = si.mx_operand(2 * N, K, seed=seed + 1, device="cuda")
+    return xq, xs, wq, ws
 
 
 @pytest.mark.parametrize("layout", ["split", "paired"])
@@ -76,6 +85,9 @@ def test_opcheck(gpu):
     torch.library.opcheck(ops.glu_backward_nvfp4, (g.detach(), u, d, "swiglu", "128x4"))
     torch.library.opcheck(ops.glu_amax, (g.detach(), u, "swiglu", "split"))
     torch.library.opcheck(ops.glu_nvfp4, (g.detach(), u, "geglu", "split", "rowmajor"))
+    mx = _mx_operands(64, 128, 256, 66)
+    torch.library.opcheck(ops.glu_gemm, (*mx, "swiglu"))
+    torch.library.opcheck(ops.glu_gemm_mxfp8, (*mx, "geglu"))
 
 
 def test_compile_fullgraph_matches_eager(gpu):

@@ -43,6 +43,13 @@ def test_fake_shapes_match_the_entry_points():
         assert a.shape == (1,) and a.dtype == torch.float32
         q, sf = ops.glu_nvfp4_gs(g, u, a, "geglu", "split", "128x4")
         assert q.dtype == torch.uint8 and sf.numel() == glu.nvfp4_sf_bytes(M, N, "128x4")
+        K, u8 = 256, dict(dtype=torch.uint8, device="cuda")
+        xq, xs = torch.empty((M, K), **u8), torch.empty((M, K // 32), **u8)
+        wq, ws = torch.empty((2 * 128, K), **u8), torch.empty((2 * 128, K // 32), **u8)
+        h = ops.glu_gemm(xq, xs, wq, ws, "geglu")
+        assert h.shape == (M, 128) and h.dtype == torch.bfloat16
+        q, sr = ops.glu_gemm_mxfp8(xq, xs, wq, ws, "swiglu")
+        assert q.shape == (M, 128) and sr.shape == (M, 4) and q.dtype == sr.dtype == torch.uint8
 
 
 def test_graph_capture_keeps_each_op_whole():
