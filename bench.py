@@ -225,7 +225,8 @@ def sweep(torch, glu, si, iters):
             rec(f"{act}_nvfp4_bwd_{M}x{N}", nv_bwd_bytes(M, N), t)
         del sets, out
         torch.cuda.empty_cache()
-    # merged gate/up MXFP8 GEMM with the GLU and MXFP8 rowwise epilogue: the NVFP4 page's
+    # merged gate/up MXFP8 GEMM with the GLU and MXFP8 rowwise (or NVFP4, 128x4 scales)
+    # epilogue: the NVFP4 page's
     # projection (M tokens, K = 2048, merged 2N = 32768) in MXFP8 form, and the MXFP8 page's
     # [16384, 7168] activation produced from K = 2048
     for M, N, K in ((968, 16384, 2048), (16384, 7168, 2048)):
@@ -234,13 +235,20 @@ def sweep(torch, glu, si, iters):
                 for s in range(min(4, n_sets(per)))]
         out = (torch.empty((M, N), dtype=torch.uint8, device="cuda"),
                torch.empty((M, N // 32), dtype=torch.uint8, device="cuda"))
-        for act in ("swiglu", "geglu"):
-            t = time_launches(torch, [lambda s=s: glu.glu_gemm_mxfp8(*s, act=act, out=out) for s in sets], iters)
+        nv_out = glu._nv_buffers(M, N, "128x4", "cuda", None)
+        cases = [("swiglu", "mxfp8"), ("geglu", "mxfp8"), ("geglu", "nvfp4")]
+        for act, fmt in cases:
+            if fmt == "mxfp8":
+                fns = [lambda s=s: glu.glu_gemm_mxfp8(*s, act=act, out=out) for s in sets]
+            else:
+                fns = [lambda s=s: glu.glu_gemm_nvfp4(*s, act=act, sf_layout="128x4", out=nv_out) for s in sets]
+            t = time_launches(torch, fns, iters)
             tf = 2.0 * M * K * 2 * N / t["median_us"] / 1e6
-            print(f"[bench] {act}_gemm_mxfp8_{M}x{N}x{K}: {t['median_us']:.2f} us", file=sys.stderr, flush=True)
-            res[f"{act}_gemm_mxfp8_{M}x{N}x{K}"] = dict(flops=2 * M * K * 2 * N, us=round(t["median_us"], 2),
-                                                         tflops=round(tf, 1), frac=round(tf / PEAK_FP8_TFLOPS, 4))
-        del sets, out
+            name = f"{act}_gemm_{fmt}_{M}x{N}x{K}"
+            print(f"[bench] {name}: {t['median_us']:.2f} us", file=sys.stderr, flush=True)
+            res[name] = dict(flops=2 * M * K * 2 * N, us=round(t["median_us"], 2), tflops=round(tf, 1),
+                             frac=round(tf / PEAK_FP8_TFLOPS, 4))
+        del sets, out, nv_out
         torch.cuda.empty_cache()
     return res
 

@@ -16,6 +16,7 @@ Entry points (C names in include/glu_mx.h):
   glu_fwd_nvfp4_gs(x, up=None, amax=, layout=, sf_layout=)   -> (q, sf), two-level scaling
   glu_gemm(xq, xs, wq, ws, act=)                             -> h of the merged MXFP8 GEMM
   glu_gemm_mxfp8(xq, xs, wq, ws, act=)                       -> (q_row, s_row) of that h
+  glu_gemm_nvfp4(xq, xs, wq, ws, act=, sf_layout=)            -> (q, sf) of that h, NVFP4
   mx_gemm_f32(xq, xs, wq, ws)                                -> the GEMM alone (test hook)
   glu_quant_mxfp8_f32(x, rowwise=, colwise=)                -> (q_row, q_col, s_row, s_col)
   glu_quant_nvfp4_f32(x, sf_layout=)                        -> (q, sf)
@@ -51,6 +52,7 @@ _SIGNATURES = {
     "glu_amax": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p],
     "glu_gemm": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _p],
     "glu_gemm_mxfp8": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p],
+    "glu_gemm_nvfp4": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _int, _p],
     "glu_mx_gemm_f32": [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p],
     "glu_fwd_nvfp4_gs": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _p, _int, _p],
     "glu_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p, _p],
@@ -64,6 +66,7 @@ _SIGNATURES = {
     "glu_check_amax": [_int, _int, _i64, _i64, _p, _p, _i64, _p],
     "glu_check_gemm": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64],
     "glu_check_gemm_mxfp8": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p],
+    "glu_check_gemm_nvfp4": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _int],
     "glu_check_mx_gemm_f32": [_i64, _i64, _i64, _p, _p, _p, _p, _p],
     "glu_check_fwd_nvfp4_gs": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _p, _int],
     "glu_check_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p],
@@ -351,6 +354,15 @@ def glu_gemm_mxfp8(xq, xs, wq, ws, *, act="swiglu", out=None):
     _call("glu_gemm_mxfp8", ACT[act], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(q), _ptr(sc),
           _stream(xq))
     return q, sc
+
+
+def glu_gemm_nvfp4(xq, xs, wq, ws, *, act="geglu", sf_layout="rowmajor", out=None):
+    """The same h quantized NVFP4, global scale 1: (q [M, N/2] packed E2M1, sf scales)."""
+    M, N, K = _gemm_operands(xq, xs, wq, ws)
+    q, sf = _nv_buffers(M, N, sf_layout, xq.device, out)
+    _call("glu_gemm_nvfp4", ACT[act], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(q), _ptr(sf),
+          SF_LAYOUT[sf_layout], _stream(xq))
+    return q, sf
 
 
 def mx_gemm_f32(xq, xs, wq, ws, *, out=None):

@@ -397,6 +397,26 @@ glu_status glu_check_gemm_mxfp8(int act, int64_t M, int64_t N, int64_t K, const 
   return check_no_overlap({Q, S}, {X, XS, W, WS});
 }
 
+glu_status glu_check_gemm_nvfp4(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                                uint8_t* q, uint8_t* sf, int sf_layout) {
+  if (!valid_act(act)) return GLU_ERR_ARG;
+  if (sf_layout != glu::SF_ROWMAJOR && sf_layout != glu::SF_128x4) return GLU_ERR_ARG;
+  if (M < 0 || N < 0 || K < 0) return GLU_ERR_SHAPE;
+  if (M == 0 || N == 0) return GLU_OK;
+  glu_status st = check_gemm_inputs(M, N, K, xq, xs, wq, ws);
+  if (st != GLU_OK) return st;
+  if (q == nullptr || sf == nullptr) return GLU_ERR_NULL;
+  if (!aligned16(q) || !aligned16(sf)) return GLU_ERR_ALIGN;
+  const int64_t sfb = glu_nvfp4_sf_bytes(M, N, sf_layout);
+  if (sfb < 0) return GLU_ERR_SHAPE;
+  const Operand X = mat(xq, M, K, K, 1), XS = mat(xs, M, K / 32, K / 32, 1),
+                W = mat(wq, 2 * N, K, K, 1), WS = mat(ws, 2 * N, K / 32, K / 32, 1),
+                Q = mat(q, M, N / 2, N / 2, 1), S = mat(sf, 1, sfb, sfb, 1);
+  if (any_overflow({Q, S}) || Q.bytes >= kOffsetLimit || S.bytes >= kOffsetLimit) return GLU_ERR_SHAPE;
+  return check_no_overlap({Q, S}, {X, XS, W, WS});
+}
+
 glu_status glu_check_mx_gemm_f32(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
                                  const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, float* y) {
   if (M < 0 || N < 0 || K < 0) return GLU_ERR_SHAPE;
@@ -586,6 +606,15 @@ glu_status glu_gemm_mxfp8(int act, int64_t M, int64_t N, int64_t K, const uint8_
   if (st != GLU_OK || M == 0 || N == 0) return st;
   GemmArgs a{act, M, N, K, xq, xs, wq, ws, nullptr, 0, q_row, s_row, nullptr};
   return status_of(glu::launch_glu_gemm_mxfp8(a, (hipStream_t)stream));
+}
+
+glu_status glu_gemm_nvfp4(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                          const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, uint8_t* q,
+                          uint8_t* sf, int sf_layout, void* stream) {
+  glu_status st = glu_check_gemm_nvfp4(act, M, N, K, xq, xs, wq, ws, q, sf, sf_layout);
+  if (st != GLU_OK || M == 0 || N == 0) return st;
+  GemmArgs a{act, M, N, K, xq, xs, wq, ws, nullptr, 0, q, sf, nullptr};
+  return status_of(glu::launch_glu_gemm_nvfp4(a, sf_layout, (hipStream_t)stream));
 }
 
 glu_status glu_mx_gemm_f32(int64_t M, int64_t N, int64_t K, const uint8_t* xq,

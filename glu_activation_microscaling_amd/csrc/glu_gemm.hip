@@ -67,10 +67,9 @@ constexpr int STAGES = 2;
 // X rows 0..255 then W rows 256..511.
 constexpr uint32_t SC_ROWS = GM_BM + 2 * GM_BN, SC_GROUP = 16u * SC_ROWS, SC_OFF = STAGES * STAGE;
 static_assert(SC_OFF + 2 * SC_GROUP <= 160u * 1024u, "LDS");
-constexpr int OP_LOADS = 2 * 2 + 2 * 2;               // per wave and K step: X, W
 constexpr int SC_LOADS = SC_ROWS / 16 / 8;            // per wave and group: 16 rows each
 
-enum { GEMM_H = 0, GEMM_MXFP8 = 1, GEMM_F32 = 2 };
+enum { GEMM_H = 0, GEMM_MXFP8 = 1, GEMM_F32 = 2, GEMM_NV_ROWMAJOR = 3, GEMM_NV_128x4 = 4 };
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, off, 0, 0, 0);
@@ -290,6 +289,48 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
           }
           __builtin_amdgcn_raw_buffer_store_b64((v2u){v[0] | (v[1] << 16), v[2] | (v[3] << 16)}, rh,
                                                 ok ? 2u * (row * (uint32_t)a.ld_h + col0 + 4u * r) : kOob, 0, 0);
+        } else if constexpr (OUT == GEMM_NV_ROWMAJOR || OUT == GEMM_NV_128x4) {
+          // NVFP4 (global scale 1): a 16-column block is one tile j; its amax runs over the
+          // 16 lanes of a DPP row, two blocks at a time on packed 16-bit magnitudes
+          uint32_t m2[2];
+#pragma unroll
+          for (int b = 0; b < 2; b++) {
+            uint32_t m = P[e][b] & 0x7fff7fffu;
+            m = pkmax(m, dpp<DPP_XOR1>(m));
+            m = pkmax(m, dpp<DPP_XOR2>(m));
+            m = pkmax(m, dpp<0x124>(m));  // row_ror:4
+            m2[b] = pkmax(m, dpp<DPP_ROW_ROR8>(m));
+          }
+          uint32_t word = 0, sbs = 0;
+          float y[4];
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const uint32_t mj = (j & 1) ? hi16(m2[j >> 1]) : lo16(m2[j >> 1]);
+            const bool nonfinite = mj >= 0x7f80u;
+            const uint32_t sc = nonfinite ? 0x7fu : nv_scale_code_bf16(__uint_as_float(mj << 16));
+            const float S = e4m3_value(nonfinite ? 0u : sc);
+            const float R = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
+            const float x = (j & 1) ? bf_hi(P[e][j >> 1]) : bf_lo(P[e][j >> 1]);
+            y[j] = nonfinite ? 0.0f : e2m1_operand(x, R);
+            sbs |= sc << (8 * j);
+          }
+          // (a block holding NaN or Inf gets scale 0x7F and zero codes)
+          word = fp4x2<0>(word, y[0], y[1]);
+          word = fp4x2<1>(word, y[2], y[3]);
+          uint32_t v = 0;
+#pragma unroll
+          for (int k = 0; k < 4; k++) v |= ((gather(word, k) >> (4u * sel)) & 0xfu) << (4 * k);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, rq, ok ? row * (N / 2u) + (col0 + 4u * r) / 2u : kOob, 0, 0);
+          // the row's four scale bytes of this wave, blocks col0 / 16 .. + 3, as one word
+          if constexpr (OUT == GEMM_NV_ROWMAJOR) {
+            __builtin_amdgcn_raw_buffer_store_b32(sbs, rs, ok && r == 0 ? row * (N / 16u) + col0 / 16u : kOob, 0, 0);
+          } else {
+            // 128x4: rows padded to 128 with zero scales (N / 16 is a multiple of 4)
+            const uint32_t off = (row >> 7) * (N / 64u) * 512u + (row & 31u) * 16u + ((row & 127u) >> 5) * 4u +
+                                 (col0 / 64u) * 512u;
+            const bool pad_ok = row < ((M + 127u) & ~127u);
+            __builtin_amdgcn_raw_buffer_store_b32(ok ? sbs : 0u, rs, pad_ok && r == 0 ? off : kOob, 0, 0);
+          }
         } else {
           // MXFP8 rowwise: the wave's 64 columns of a row are two blocks of 32 (pair b holds
           // block b's two elements of this lane); a row sits in the 16 lanes of one DPP row
@@ -339,5 +380,8 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_glu_gemm(const GemmArgs& a, hipStream_t s) { return launch<GEMM_H>(a, s); }
 hipError_t launch_glu_gemm_mxfp8(const GemmArgs& a, hipStream_t s) { return launch<GEMM_MXFP8>(a, s); }
 hipError_t launch_mx_gemm_f32(const GemmArgs& a, hipStream_t s) { return launch<GEMM_F32>(a, s); }
+hipError_t launch_glu_gemm_nvfp4(const GemmArgs& a, int sf_layout, hipStream_t s) {
+  return sf_layout == SF_128x4 ? launch<GEMM_NV_128x4>(a, s) : launch<GEMM_NV_ROWMAJOR>(a, s);
+}
 
 }  // namespace glu

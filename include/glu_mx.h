@@ -207,6 +207,16 @@ glu_status glu_gemm(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
 glu_status glu_gemm_mxfp8(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
                           const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
                           uint8_t* q_row, uint8_t* s_row, void* stream);
+/* The same h quantized NVFP4 with global scale 1, as glu_fwd_nvfp4 quantizes its output
+ * ([NV] Summary: the merged GEMM's GeGLU result leaves as packed NVFP4 and scales for the
+ * down projection; the operands stay MXFP8, the form gfx950's block-scaled matrix
+ * instruction takes): q [M, N/2] packed E2M1 (even column in the low nibble), sf E4M3
+ * scales of 16-column blocks in sf_layout (GLU_SF_ROWMAJOR [M, N/16], or GLU_SF_128x4 with
+ * rows padded to 128 and zero padding; glu_nvfp4_sf_bytes(M, N, sf_layout) bytes).
+ * Requirements and errors as glu_gemm; an unknown sf_layout is GLU_ERR_ARG. */
+glu_status glu_gemm_nvfp4(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                          const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, uint8_t* q,
+                          uint8_t* sf, int sf_layout, void* stream);
 /* Test hook: the FP32 GEMM alone, y [M, 2N], formed exactly as the fused kernels form it. */
 glu_status glu_mx_gemm_f32(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
                            const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, float* y,
@@ -268,6 +278,9 @@ glu_status glu_check_gemm(int act, int64_t M, int64_t N, int64_t K, const uint8_
 glu_status glu_check_gemm_mxfp8(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
                                 const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
                                 uint8_t* q_row, uint8_t* s_row);
+glu_status glu_check_gemm_nvfp4(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                                uint8_t* q, uint8_t* sf, int sf_layout);
 glu_status glu_check_mx_gemm_f32(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
                                  const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
                                  float* y);

@@ -273,6 +273,17 @@ def test_gemm_checks():
     q = lambda **kw: _gemm(L.glu_check_gemm_mxfp8, **kw)
     assert q() == OK and q(q=0) == NULL and q(s=E0 + 1) == ALIGN and q(act=7) == ARG
     assert q(s=D0 + 64 * 128 - 16) == OVERLAP and q(s=D0 + 64 * 128) == OK
+    nv = L.glu_check_gemm_nvfp4
+    assert nv(0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(E0), 0) == OK
+    assert nv(0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(E0), 1) == OK
+    assert nv(0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(E0), 2) == ARG
+    assert nv(0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(0), P(E0), 0) == NULL
+    assert nv(0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(E0 + 8), 0) == ALIGN
+    # q is [M, N/2] = 4096 bytes; the 128x4 scales of 64 rows take 128 * 8 bytes
+    assert nv(0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(D0 + 4096 - 16), 0) == OVERLAP
+    assert nv(0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(D0 + 4096), 1) == OK
+    assert nv(0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(E0 + 1024 - 16), P(E0), 1) == OVERLAP
+    assert nv(0, 64, 96, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(E0), 0) == SHAPE
     y = lambda **kw: _gemm(L.glu_check_mx_gemm_f32, **kw)
     assert y() == OK and y(y=0) == NULL and y(y=D0 + 4) == ALIGN
     assert y(M=1 << 20, K=128, N=256, y=F0 * 64) == SHAPE             # y is M x 2N x 4 bytes

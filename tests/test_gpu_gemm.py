@@ -13,8 +13,8 @@ Parity is taken in three steps:
     that bound;
   * the GLU epilogue (glu_gemm) against the oracle's GLU of the device's own Y (rule 2,
     within 1 BF16 ulp);
-  * the quantizing epilogue (glu_gemm_mxfp8) against the oracle quantizer of the device's
-    own h (rule 1, bit-exact).
+  * the quantizing epilogues (glu_gemm_mxfp8, glu_gemm_nvfp4) against the oracle quantizers
+    of the device's own h (rule 1, bit-exact).
 """
 import numpy as np
 import pytest
@@ -107,6 +107,24 @@ def test_glu_epilogue_and_quantizer(gpu, act, kind):
     assert np.array_equal(u8(sc), o[1]) and np.array_equal(u8(q), o[0])
 
 
+@pytest.mark.parametrize("act,kind", [ACTS[0], ACTS[1], ACTS[3]])
+@pytest.mark.parametrize("M", [160, 300])
+@pytest.mark.parametrize("sf_layout", ["rowmajor", "128x4"])
+def test_nvfp4_epilogue(gpu, act, kind, M, sf_layout):
+    """NVFP4 (global scale 1) of the device's own h, bit-exact; 128x4 padding rows are zero
+    (the outputs start as 0xAB so that a missing write shows)."""
+    N, K = 256, 256
+    ops = [t.cuda() for t in _operands(M, N, K, seed=100 + M + kind)]
+    h = bits(gpu.glu_gemm(*ops, act=act))
+    sfl = oracle.SF_128x4 if sf_layout == "128x4" else oracle.SF_ROWMAJOR
+    o = oracle.quant_nvfp4(si.from_bits(h).float().numpy(), sfl)
+    q = torch.full((M, N // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    sf = torch.full((gpu.nvfp4_sf_bytes(M, N, sf_layout),), 0xAB, dtype=torch.uint8, device="cuda")
+    gpu.glu_gemm_nvfp4(*ops, act=act, sf_layout=sf_layout, out=(q, sf))
+    assert np.array_equal(u8(q), o[0])
+    assert np.array_equal(u8(sf).ravel(), np.asarray(o[1]).ravel())
+
+
 def test_gemm_deterministic_and_row_batch_invariant(gpu):
     M, N, K = 256, 128, 256
     xq, xs, wq, ws = (t.cuda() for t in _operands(M, N, K, seed=80))
@@ -154,3 +172,7 @@ def test_nan_codes_and_scales(gpu, act, kind):
     o = oracle.quant_mxfp8(si.from_bits(h).float().numpy(), oracle.ROWWISE)
     assert np.array_equal(u8(sc), o[1]) and np.array_equal(u8(q), o[0])
     assert (u8(sc)[[3, 7]] == 0xFF).all() and (u8(sc)[:, [0, 1]] == 0xFF).all()
+    qn, sn = gpu.glu_gemm_nvfp4(*dev, act=act)
+    on = oracle.quant_nvfp4(si.from_bits(h).float().numpy(), oracle.SF_ROWMAJOR)
+    assert np.array_equal(u8(qn), on[0]) and np.array_equal(u8(sn), on[1])
+    assert (u8(sn)[[3, 7]] == 0x7F).all() and (u8(sn)[:, [0, 2]] == 0x7F).all()

@@ -41,6 +41,7 @@ def test_ops_equal_the_binding(gpu):
     mx = _mx_operands(96, 128, 256, 65)
     assert _same([ops.glu_gemm(*mx, "geglu")], [gpu.glu_gemm(*mx, act="geglu")])
     assert _same(ops.glu_gemm_mxfp8(*mx, "swiglu"), gpu.glu_gemm_mxfp8(*mx))
+    assert _same(ops.glu_gemm_nvfp4(*mx, "geglu", "128x4"), gpu.glu_gemm_nvfp4(*mx, sf_layout="128x4"))
 
 
 def _mx_operands(M, N, K, seed):
@@ -88,6 +89,7 @@ def test_opcheck(gpu):
     mx = _mx_operands(64, 128, 256, 66)
     torch.library.opcheck(ops.glu_gemm, (*mx, "swiglu"))
     torch.library.opcheck(ops.glu_gemm_mxfp8, (*mx, "geglu"))
+    torch.library.opcheck(ops.glu_gemm_nvfp4, (*mx, "geglu", "rowmajor"))
 
 
 def test_compile_fullgraph_matches_eager(gpu):

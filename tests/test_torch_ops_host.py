@@ -50,6 +50,8 @@ def test_fake_shapes_match_the_entry_points():
         assert h.shape == (M, 128) and h.dtype == torch.bfloat16
         q, sr = ops.glu_gemm_mxfp8(xq, xs, wq, ws, "swiglu")
         assert q.shape == (M, 128) and sr.shape == (M, 4) and q.dtype == sr.dtype == torch.uint8
+        q, sf = ops.glu_gemm_nvfp4(xq, xs, wq, ws, "geglu", "128x4")
+        assert q.shape == (M, 64) and sf.numel() == glu.nvfp4_sf_bytes(M, 128, "128x4")
 
 
 def test_graph_capture_keeps_each_op_whole():
