@@ -287,6 +287,10 @@ def main():
     ap.add_argument("--nvfp4-only", action="store_true",
                     help="only launch the NVFP4 forward and backward at [16384, 7168] three times "
                          "each and print no JSON (a target for profiler counter passes)")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="only launch the merged MXFP8 GEMM with the SwiGLU + MXFP8 epilogue at "
+                         "8192 x 2048 x 7168 and 16384 x 7168 x 2048, three times each, and print "
+                         "no JSON (a target for profiler counter passes)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path needs no collective and runs one "
@@ -313,6 +317,14 @@ def main():
             glu.glu_bwd_nvfp4(g, u, d, act="swiglu", sf_layout="128x4", out=ob)
         torch.cuda.synchronize()
         print("[bench] nvfp4 launches done", file=sys.stderr, flush=True)
+        return
+    if args.gemm_only:
+        for gm, gn, gk in ((8192, 2048, 7168), (16384, 7168, 2048)):
+            ops = si.mx_operand(gm, gk, seed=3, device="cuda") + si.mx_operand(2 * gn, gk, seed=4, device="cuda")
+            for _ in range(3):
+                glu.glu_gemm_mxfp8(*ops, act="swiglu")
+        torch.cuda.synchronize()
+        print("[bench] gemm launches done", file=sys.stderr, flush=True)
         return
     sets = [si.normal_bf16_device([(M, N)] * 3, seed=s, outliers=True) for s in range(2)]
     fo = glu._mx_buffers(M, N, True, True, "cuda", None)
