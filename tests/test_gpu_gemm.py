@@ -38,9 +38,7 @@ def _operands(M, N, K, seed):
     return xq, xs, wq, ws
 
 
-def _dequant(q, s):
-    v = oracle.e4m3_to_f64(q.numpy()).reshape(tuple(q.shape))
-    return v * np.repeat(np.exp2(s.numpy().astype(np.float64) - 127.0), 32, axis=1)
+_E4M3 = oracle.e4m3_to_f64(np.arange(256, dtype=np.uint8))   # the oracle's value of every code
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 128, 512), (200, 128, 256), (128, 256, 2048), (37, 128, 128),
@@ -50,18 +48,27 @@ def test_gemm_within_the_accumulation_bound(gpu, M, N, K):
     y = gpu.mx_gemm_f32(*(t.cuda() for t in ops)).cpu().numpy().astype(np.float64)
     exact = oracle.mx_gemm_nt(*(t.numpy() for t in ops))
     err = np.abs(y - exact)
-    bound = _accumulation_bound(_dequant(ops[0], ops[1]), _dequant(ops[2], ops[3]))
+    bound = _accumulation_bound(*(t.numpy() for t in ops))
     assert np.all(err <= bound), f"worst {float((err / bound).max()):.3g} of the bound"
 
 
-def _accumulation_bound(x, w):
-    """The elementwise bound above, for dequantized X [M, K] and W [2N, K]."""
-    ax, aw = np.abs(x), np.abs(w)
-    K = x.shape[1]
-    chunk_max = np.zeros((x.shape[0], w.shape[0]))
+def _accumulation_bound(xq, xs, wq, ws):
+    """The elementwise bound above, from the codes and scales of X [M, K] and W [2N, K]
+    (dequantized one 8-element K chunk at a time)."""
+    xq, xs, wq, ws = (np.asarray(t) for t in (xq, xs, wq, ws))
+    K = xq.shape[1]
+    xsc, wsc = np.exp2(xs.astype(np.float64) - 127.0), np.exp2(ws.astype(np.float64) - 127.0)
+    chunk_max = np.zeros((xq.shape[0], wq.shape[0]))
+    total = np.zeros_like(chunk_max)
     for c in range(0, K, 8):
-        chunk_max += (ax[:, None, c:c + 8] * aw[None, :, c:c + 8]).max(axis=2)
-    return 8 * WINDOW * chunk_max + (K / 8) * ROUND * (ax @ aw.T)
+        ax = np.abs(_E4M3[xq[:, c:c + 8]]) * xsc[:, c // 32, None]   # [M, 8]
+        aw = np.abs(_E4M3[wq[:, c:c + 8]]) * wsc[:, c // 32, None]   # [2N, 8]
+        m = np.outer(ax[:, 0], aw[:, 0])
+        for k in range(1, 8):
+            np.maximum(m, np.outer(ax[:, k], aw[:, k]), out=m)
+        chunk_max += m
+        total += ax @ aw.T
+    return 8 * WINDOW * chunk_max + (K / 8) * ROUND * total
 
 
 def _e4m3_code(v):
@@ -176,3 +183,31 @@ def test_nan_codes_and_scales(gpu, act, kind):
     on = oracle.quant_nvfp4(si.from_bits(h).float().numpy(), oracle.SF_ROWMAJOR)
     assert np.array_equal(u8(qn), on[0]) and np.array_equal(u8(sn), on[1])
     assert (u8(sn)[[3, 7]] == 0x7F).all() and (u8(sn)[:, [0, 2]] == 0x7F).all()
+
+
+@pytest.mark.parametrize("M,N,K", [(968, 16384, 2048), (16384, 7168, 2048)])
+def test_full_size_sampled_rows(gpu, M, N, K):
+    """The bench's GEMM shapes, launched whole as the bench launches them; a sample of rows
+    (first, last, and spread between) is checked in the three parity steps: the FP32 GEMM
+    within the accumulation bound of the exact one, h by rule 2 against the GLU of the
+    device's Y, and the MXFP8 and NVFP4 outputs bit-exact against the oracle quantizers of
+    the device's h."""
+    xq, xs, wq, ws = _operands(M, N, K, seed=7)
+    dev = [t.cuda() for t in (xq, xs, wq, ws)]
+    rows = np.unique(np.r_[0, 1, 255, 256, M - 1, np.linspace(0, M - 1, 11).astype(int)])
+    ridx = torch.as_tensor(rows, device="cuda")
+    y = gpu.mx_gemm_f32(*dev).index_select(0, ridx).cpu().numpy().astype(np.float64)
+    h = bits(gpu.glu_gemm(*dev, act="swiglu").index_select(0, ridx))
+    qm, sm = (t.index_select(0, ridx) for t in gpu.glu_gemm_mxfp8(*dev, act="swiglu"))
+    qn, sn = (t.index_select(0, ridx) for t in gpu.glu_gemm_nvfp4(*dev, act="swiglu"))
+    torch.cuda.synchronize()
+    x_r, xs_r = xq[rows], xs[rows]
+    exact = oracle.mx_gemm_nt(x_r.numpy(), xs_r.numpy(), wq.numpy(), ws.numpy())
+    bound = _accumulation_bound(x_r.numpy(), xs_r.numpy(), wq.numpy(), ws.numpy())
+    assert np.all(np.abs(y - exact) <= bound)
+    check_rule2(h, oracle.bf16_from_f64(oracle.act(oracle.SWIGLU, y[:, :N]) * y[:, N:]), "full-size epilogue")
+    hf = si.from_bits(h).float().numpy()
+    om = oracle.quant_mxfp8(hf, oracle.ROWWISE)
+    assert np.array_equal(u8(qm), om[0]) and np.array_equal(u8(sm), om[1])
+    on = oracle.quant_nvfp4(hf, oracle.SF_ROWMAJOR)
+    assert np.array_equal(u8(qn), on[0]) and np.array_equal(u8(sn), on[1])
