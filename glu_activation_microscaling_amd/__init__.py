@@ -17,6 +17,7 @@ Entry points (C names in include/glu_mx.h):
   glu_gemm(xq, xs, wq, ws, act=)                             -> h of the merged MXFP8 GEMM
   glu_gemm_mxfp8(xq, xs, wq, ws, act=)                       -> (q_row, s_row) of that h
   glu_gemm_nvfp4(xq, xs, wq, ws, act=, sf_layout=)            -> (q, sf) of that h, NVFP4
+  glu_gemm_nvfp4_gs(xq, xs, wq, ws, amax=, act=, sf_layout=)  -> (q, sf), two-level NVFP4
   mx_gemm_f32(xq, xs, wq, ws)                                -> the GEMM alone (test hook)
   glu_quant_mxfp8_f32(x, rowwise=, colwise=)                -> (q_row, q_col, s_row, s_col)
   glu_quant_nvfp4_f32(x, sf_layout=)                        -> (q, sf)
@@ -53,6 +54,7 @@ _SIGNATURES = {
     "glu_gemm": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _p],
     "glu_gemm_mxfp8": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p],
     "glu_gemm_nvfp4": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _int, _p],
+    "glu_gemm_nvfp4_gs": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _int, _p],
     "glu_mx_gemm_f32": [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p],
     "glu_fwd_nvfp4_gs": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _p, _int, _p],
     "glu_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p, _p],
@@ -67,6 +69,7 @@ _SIGNATURES = {
     "glu_check_gemm": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64],
     "glu_check_gemm_mxfp8": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p],
     "glu_check_gemm_nvfp4": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _int],
+    "glu_check_gemm_nvfp4_gs": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _int],
     "glu_check_mx_gemm_f32": [_i64, _i64, _i64, _p, _p, _p, _p, _p],
     "glu_check_fwd_nvfp4_gs": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _p, _int],
     "glu_check_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p],
@@ -362,6 +365,18 @@ def glu_gemm_nvfp4(xq, xs, wq, ws, *, act="geglu", sf_layout="rowmajor", out=Non
     q, sf = _nv_buffers(M, N, sf_layout, xq.device, out)
     _call("glu_gemm_nvfp4", ACT[act], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(q), _ptr(sf),
           SF_LAYOUT[sf_layout], _stream(xq))
+    return q, sf
+
+
+def glu_gemm_nvfp4_gs(xq, xs, wq, ws, *, amax, act="geglu", sf_layout="rowmajor", out=None):
+    """The same h quantized two-level NVFP4, the global scale from `amax` (a float32 [1] GPU
+    tensor, e.g. kept from an earlier step): (q [M, N/2] packed E2M1, sf scales)."""
+    M, N, K = _gemm_operands(xq, xs, wq, ws)
+    if amax.dtype != torch.float32 or not amax.is_cuda or amax.numel() != 1:
+        raise ValueError("amax must be a float32 GPU tensor with one element")
+    q, sf = _nv_buffers(M, N, sf_layout, xq.device, out)
+    _call("glu_gemm_nvfp4_gs", ACT[act], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(amax), _ptr(q),
+          _ptr(sf), SF_LAYOUT[sf_layout], _stream(xq))
     return q, sf
 
 

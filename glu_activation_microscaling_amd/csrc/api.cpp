@@ -614,7 +614,29 @@ glu_status glu_gemm_nvfp4(int act, int64_t M, int64_t N, int64_t K, const uint8_
   glu_status st = glu_check_gemm_nvfp4(act, M, N, K, xq, xs, wq, ws, q, sf, sf_layout);
   if (st != GLU_OK || M == 0 || N == 0) return st;
   GemmArgs a{act, M, N, K, xq, xs, wq, ws, nullptr, 0, q, sf, nullptr};
-  return status_of(glu::launch_glu_gemm_nvfp4(a, sf_layout, (hipStream_t)stream));
+  return status_of(glu::launch_glu_gemm_nvfp4(a, sf_layout, false, (hipStream_t)stream));
+}
+
+glu_status glu_check_gemm_nvfp4_gs(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                   const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                                   const float* amax, uint8_t* q, uint8_t* sf, int sf_layout) {
+  glu_status st = glu_check_gemm_nvfp4(act, M, N, K, xq, xs, wq, ws, q, sf, sf_layout);
+  if (st != GLU_OK || M == 0 || N == 0) return st;
+  if (amax == nullptr) return GLU_ERR_NULL;
+  if ((uintptr_t)amax % 4 != 0) return GLU_ERR_ALIGN;
+  const int64_t sfb = glu_nvfp4_sf_bytes(M, N, sf_layout);
+  const Operand A = mat(amax, 1, 1, 1, 4), Q = mat(q, M, N / 2, N / 2, 1), S = mat(sf, 1, sfb, sfb, 1);
+  return check_no_overlap({Q, S}, {A});
+}
+
+glu_status glu_gemm_nvfp4_gs(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                             const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                             const float* amax, uint8_t* q, uint8_t* sf, int sf_layout,
+                             void* stream) {
+  glu_status st = glu_check_gemm_nvfp4_gs(act, M, N, K, xq, xs, wq, ws, amax, q, sf, sf_layout);
+  if (st != GLU_OK || M == 0 || N == 0) return st;
+  GemmArgs a{act, M, N, K, xq, xs, wq, ws, nullptr, 0, q, sf, nullptr, amax};
+  return status_of(glu::launch_glu_gemm_nvfp4(a, sf_layout, true, (hipStream_t)stream));
 }
 
 glu_status glu_mx_gemm_f32(int64_t M, int64_t N, int64_t K, const uint8_t* xq,

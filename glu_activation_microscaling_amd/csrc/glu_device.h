@@ -436,6 +436,22 @@ __device__ __forceinline__ uint32_t nv_scale_code_bf16(float amax) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xffu;
 }
 
+// Two-level NVFP4 (global scale from the tensor amax): s = fl(2688 / amax), capped at 2^100,
+// 1 for an amax that is zero, negative or not finite; k = fl(s / 6).  Every step is one
+// IEEE FP32 operation (the divisions are correctly rounded).
+struct GlobalScale {
+  float s = 1.0f, k = 1.0f / 6.0f;
+};
+__device__ __forceinline__ GlobalScale global_scale(float amax) {
+  GlobalScale g;
+  if (amax > 0.0f && __builtin_isfinite(amax)) {
+    const float s = 2688.0f / amax;
+    g.s = s < 0x1p100f ? s : 0x1p100f;
+  }
+  g.k = g.s / 6.0f;
+  return g;
+}
+
 // E2M1 decision thresholds at scale S: S * {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5}, each exact
 // in FP32.  S == 0 maps every magnitude to code 0 (thresholds at +Inf).
 struct E2m1Thresholds {

@@ -69,7 +69,12 @@ constexpr uint32_t SC_ROWS = GM_BM + 2 * GM_BN, SC_GROUP = 16u * SC_ROWS, SC_OFF
 static_assert(SC_OFF + 2 * SC_GROUP <= 160u * 1024u, "LDS");
 constexpr int SC_LOADS = SC_ROWS / 16 / 8;            // per wave and group: 16 rows each
 
-enum { GEMM_H = 0, GEMM_MXFP8 = 1, GEMM_F32 = 2, GEMM_NV_ROWMAJOR = 3, GEMM_NV_128x4 = 4 };
+enum {
+  GEMM_H = 0, GEMM_MXFP8 = 1, GEMM_F32 = 2,
+  GEMM_NV_ROWMAJOR = 3, GEMM_NV_128x4 = 4,         // NVFP4, global scale 1
+  GEMM_NV_GS_ROWMAJOR = 5, GEMM_NV_GS_128x4 = 6    // NVFP4, two-level (global scale from *amax)
+};
+constexpr bool is_nv(int out) { return out >= GEMM_NV_ROWMAJOR; }
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, off, 0, 0, 0);
@@ -253,6 +258,8 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
     };
     const uint32_t sel = r >> 2;   // the source tile of this lane's columns
     const auto rh = rsrc(a.h), rq = rsrc(a.q_row), rs = rsrc(a.s_row);
+    GlobalScale gs;
+    if constexpr (OUT >= GEMM_NV_GS_ROWMAJOR) gs = global_scale(*a.amax);
     const uint32_t NB = N / 32u;
 #pragma unroll
     for (int i = 0; i < WM; i++) {
@@ -289,9 +296,9 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
           }
           __builtin_amdgcn_raw_buffer_store_b64((v2u){v[0] | (v[1] << 16), v[2] | (v[3] << 16)}, rh,
                                                 ok ? 2u * (row * (uint32_t)a.ld_h + col0 + 4u * r) : kOob, 0, 0);
-        } else if constexpr (OUT == GEMM_NV_ROWMAJOR || OUT == GEMM_NV_128x4) {
-          // NVFP4 (global scale 1): a 16-column block is one tile j; its amax runs over the
-          // 16 lanes of a DPP row, two blocks at a time on packed 16-bit magnitudes
+        } else if constexpr (is_nv(OUT)) {
+          // NVFP4: a 16-column block is one tile j; its amax runs over the 16 lanes of a DPP
+          // row, two blocks at a time on packed 16-bit magnitudes
           uint32_t m2[2];
 #pragma unroll
           for (int b = 0; b < 2; b++) {
@@ -307,11 +314,22 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
           for (int j = 0; j < 4; j++) {
             const uint32_t mj = (j & 1) ? hi16(m2[j >> 1]) : lo16(m2[j >> 1]);
             const bool nonfinite = mj >= 0x7f80u;
-            const uint32_t sc = nonfinite ? 0x7fu : nv_scale_code_bf16(__uint_as_float(mj << 16));
-            const float S = e4m3_value(nonfinite ? 0u : sc);
-            const float R = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
             const float x = (j & 1) ? bf_hi(P[e][j >> 1]) : bf_lo(P[e][j >> 1]);
-            y[j] = nonfinite ? 0.0f : e2m1_operand(x, R);
+            uint32_t sc;
+            if constexpr (OUT >= GEMM_NV_GS_ROWMAJOR) {
+              // two-level: E4M3(fl(bamax * k)), saturating at 448; codes E2M1(fl(x * fl(s / S)))
+              const float d = __builtin_fminf(__uint_as_float(mj << 16) * gs.k, 448.0f);
+              sc = nonfinite ? 0x7fu : (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(d, 0.0f, 0, false) & 0xffu;
+              const float S = e4m3_value(nonfinite ? 0u : sc);
+              const float rs = S > 0.0f ? gs.s / S : 0.0f;   // IEEE division
+              // |x * rs| beyond 8 saturates to 6 either way; the clamp keeps the input finite
+              y[j] = nonfinite ? 0.0f : __builtin_amdgcn_fmed3f(x * rs, -8.0f, 8.0f);
+            } else {
+              sc = nonfinite ? 0x7fu : nv_scale_code_bf16(__uint_as_float(mj << 16));
+              const float S = e4m3_value(nonfinite ? 0u : sc);
+              const float R = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
+              y[j] = nonfinite ? 0.0f : e2m1_operand(x, R);
+            }
             sbs |= sc << (8 * j);
           }
           // (a block holding NaN or Inf gets scale 0x7F and zero codes)
@@ -322,7 +340,7 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
           for (int k = 0; k < 4; k++) v |= ((gather(word, k) >> (4u * sel)) & 0xfu) << (4 * k);
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, rq, ok ? row * (N / 2u) + (col0 + 4u * r) / 2u : kOob, 0, 0);
           // the row's four scale bytes of this wave, blocks col0 / 16 .. + 3, as one word
-          if constexpr (OUT == GEMM_NV_ROWMAJOR) {
+          if constexpr (OUT == GEMM_NV_ROWMAJOR || OUT == GEMM_NV_GS_ROWMAJOR) {
             __builtin_amdgcn_raw_buffer_store_b32(sbs, rs, ok && r == 0 ? row * (N / 16u) + col0 / 16u : kOob, 0, 0);
           } else {
             // 128x4: rows padded to 128 with zero scales (N / 16 is a multiple of 4)
@@ -380,7 +398,9 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_glu_gemm(const GemmArgs& a, hipStream_t s) { return launch<GEMM_H>(a, s); }
 hipError_t launch_glu_gemm_mxfp8(const GemmArgs& a, hipStream_t s) { return launch<GEMM_MXFP8>(a, s); }
 hipError_t launch_mx_gemm_f32(const GemmArgs& a, hipStream_t s) { return launch<GEMM_F32>(a, s); }
-hipError_t launch_glu_gemm_nvfp4(const GemmArgs& a, int sf_layout, hipStream_t s) {
+hipError_t launch_glu_gemm_nvfp4(const GemmArgs& a, int sf_layout, bool two_level, hipStream_t s) {
+  if (two_level)
+    return sf_layout == SF_128x4 ? launch<GEMM_NV_GS_128x4>(a, s) : launch<GEMM_NV_GS_ROWMAJOR>(a, s);
   return sf_layout == SF_128x4 ? launch<GEMM_NV_128x4>(a, s) : launch<GEMM_NV_ROWMAJOR>(a, s);
 }
 

@@ -67,6 +67,7 @@ struct GemmArgs {
   uint8_t* q_row;            // MXFP8 rowwise codes [M, N] (NVFP4: packed E2M1 [M, N/2])
   uint8_t* s_row;            // scales [M, N/32] (NVFP4: E4M3, row-major or 128x4)
   float* y;                  // test hook: the pre-activation [M, 2N]
+  const float* amax = nullptr;  // two-level NVFP4: the amax the global scale comes from
 };
 
 hipError_t launch_glu_fwd_bf16(const BF16Args& a, hipStream_t s);
@@ -82,7 +83,7 @@ hipError_t launch_glu_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_glu_gemm_mxfp8(const GemmArgs& a, hipStream_t s);
 hipError_t launch_mx_gemm_f32(const GemmArgs& a, hipStream_t s);
 // NVFP4 epilogue: codes into q_row ([M, N/2] packed E2M1), E4M3 scales into s_row
-hipError_t launch_glu_gemm_nvfp4(const GemmArgs& a, int sf_layout, hipStream_t s);
+hipError_t launch_glu_gemm_nvfp4(const GemmArgs& a, int sf_layout, bool two_level, hipStream_t s);
 hipError_t launch_quant_nvfp4_f32(const NvArgs& a, hipStream_t s);
 
 // Launches kernel k and returns the launch status of this call alone (the HIP error

@@ -174,22 +174,6 @@ __device__ __forceinline__ void glu_values(const Raw8& r, uint32_t p[4], uint32_
   }
 }
 
-// Two-level NVFP4 (global scale from the tensor amax): s = fl(2688 / amax), capped at 2^100,
-// 1 for an amax that is zero, negative or not finite; k = fl(s / 6).  Every step is one
-// IEEE FP32 operation (the divisions are correctly rounded).
-struct GlobalScale {
-  float s = 1.0f, k = 1.0f / 6.0f;
-};
-__device__ __forceinline__ GlobalScale global_scale(float amax) {
-  GlobalScale g;
-  if (amax > 0.0f && __builtin_isfinite(amax)) {
-    const float s = 2688.0f / amax;
-    g.s = s < 0x1p100f ? s : 0x1p100f;
-  }
-  g.k = g.s / 6.0f;
-  return g;
-}
-
 // Output geometry of the quantized matrix: codes are q_pitch bytes per row, scales
 // scale_cols per row (scale_cols_padded in the 128x4 layout).
 struct NvOut {

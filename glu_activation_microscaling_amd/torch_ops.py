@@ -16,6 +16,7 @@ that torch.compile keeps whole; these ops do the same for the MI355X kernels:
   torch.ops.glu_mx.glu_gemm(xq, xs, wq, ws, act)                       -> h
   torch.ops.glu_mx.glu_gemm_mxfp8(xq, xs, wq, ws, act)                 -> (q_row, s_row)
   torch.ops.glu_mx.glu_gemm_nvfp4(xq, xs, wq, ws, act, sf_layout)      -> (q, sf)
+  torch.ops.glu_mx.glu_gemm_nvfp4_gs(xq, xs, wq, ws, amax, act, sf_layout) -> (q, sf)
 
 Each real implementation is the binding function of the same name (argument marshalling;
 the HIP kernels compute everything).  Each fake implementation gives the output shapes and
@@ -34,7 +35,8 @@ from torch import Tensor
 from . import (glu_amax as _amax, glu_bwd as _bwd, glu_bwd_mxfp8 as _bwd_mx,
                glu_bwd_nvfp4 as _bwd_nv, glu_fwd as _fwd, glu_fwd_mxfp8 as _fwd_mx,
                glu_fwd_nvfp4 as _fwd_nv, glu_fwd_nvfp4_gs as _fwd_nv_gs, glu_gemm as _gemm,
-               glu_gemm_mxfp8 as _gemm_mx, glu_gemm_nvfp4 as _gemm_nv)
+               glu_gemm_mxfp8 as _gemm_mx, glu_gemm_nvfp4 as _gemm_nv,
+               glu_gemm_nvfp4_gs as _gemm_nv_gs)
 
 _LIB = "glu_mx"
 
@@ -226,6 +228,19 @@ def glu_gemm_nvfp4(xq: Tensor, xs: Tensor, wq: Tensor, ws: Tensor, act: str = "g
 
 @glu_gemm_nvfp4.register_fake
 def _(xq, xs, wq, ws, act="geglu", sf_layout="rowmajor"):
+    M, N = xq.shape[0], wq.shape[0] // 2
+    return (xq.new_empty((M, N // 2), dtype=torch.uint8),
+            xq.new_empty(_nv_scale_shape(M, N, sf_layout), dtype=torch.uint8))
+
+
+@torch.library.custom_op(f"{_LIB}::glu_gemm_nvfp4_gs", mutates_args=())
+def glu_gemm_nvfp4_gs(xq: Tensor, xs: Tensor, wq: Tensor, ws: Tensor, amax: Tensor,
+                      act: str = "geglu", sf_layout: str = "rowmajor") -> Tuple[Tensor, Tensor]:
+    return _gemm_nv_gs(xq, xs, wq, ws, amax=amax, act=act, sf_layout=sf_layout)
+
+
+@glu_gemm_nvfp4_gs.register_fake
+def _(xq, xs, wq, ws, amax, act="geglu", sf_layout="rowmajor"):
     M, N = xq.shape[0], wq.shape[0] // 2
     return (xq.new_empty((M, N // 2), dtype=torch.uint8),
             xq.new_empty(_nv_scale_shape(M, N, sf_layout), dtype=torch.uint8))

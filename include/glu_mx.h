@@ -217,6 +217,15 @@ glu_status glu_gemm_mxfp8(int act, int64_t M, int64_t N, int64_t K, const uint8_
 glu_status glu_gemm_nvfp4(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
                           const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, uint8_t* q,
                           uint8_t* sf, int sf_layout, void* stream);
+/* The same NVFP4 output with two-level scaling (as glu_fwd_nvfp4_gs): the global encode scale
+ * comes from the FP32 value at device pointer amax, which a GEMM epilogue cannot know before
+ * h exists, so it is the caller's (an amax kept from an earlier step, i.e. delayed scaling, or
+ * glu_amax of an h computed earlier).  amax: 4-byte aligned (GLU_ERR_ALIGN), not NULL
+ * (GLU_ERR_NULL), not overlapping the outputs (GLU_ERR_OVERLAP).  Otherwise as glu_gemm_nvfp4. */
+glu_status glu_gemm_nvfp4_gs(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                             const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                             const float* amax, uint8_t* q, uint8_t* sf, int sf_layout,
+                             void* stream);
 /* Test hook: the FP32 GEMM alone, y [M, 2N], formed exactly as the fused kernels form it. */
 glu_status glu_mx_gemm_f32(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
                            const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, float* y,
@@ -281,6 +290,9 @@ glu_status glu_check_gemm_mxfp8(int act, int64_t M, int64_t N, int64_t K, const 
 glu_status glu_check_gemm_nvfp4(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
                                 const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
                                 uint8_t* q, uint8_t* sf, int sf_layout);
+glu_status glu_check_gemm_nvfp4_gs(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                   const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                                   const float* amax, uint8_t* q, uint8_t* sf, int sf_layout);
 glu_status glu_check_mx_gemm_f32(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
                                  const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
                                  float* y);

@@ -284,6 +284,13 @@ def test_gemm_checks():
     assert nv(0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(D0 + 4096), 1) == OK
     assert nv(0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(E0 + 1024 - 16), P(E0), 1) == OVERLAP
     assert nv(0, 64, 96, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(E0), 0) == SHAPE
+    gs = L.glu_check_gemm_nvfp4_gs
+    base = (0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2))
+    assert gs(*base, P(F0), P(D0), P(E0), 1) == OK
+    assert gs(*base, P(0), P(D0), P(E0), 1) == NULL
+    assert gs(*base, P(F0 + 2), P(D0), P(E0), 1) == ALIGN
+    assert gs(*base, P(D0 + 64), P(D0), P(E0), 1) == OVERLAP          # amax inside the codes
+    assert gs(*base, P(F0), P(D0), P(E0), 3) == ARG
     y = lambda **kw: _gemm(L.glu_check_mx_gemm_f32, **kw)
     assert y() == OK and y(y=0) == NULL and y(y=D0 + 4) == ALIGN
     assert y(M=1 << 20, K=128, N=256, y=F0 * 64) == SHAPE             # y is M x 2N x 4 bytes

@@ -132,6 +132,26 @@ def test_nvfp4_epilogue(gpu, act, kind, M, sf_layout):
     assert np.array_equal(u8(sf).ravel(), np.asarray(o[1]).ravel())
 
 
+@pytest.mark.parametrize("sf_layout", ["rowmajor", "128x4"])
+def test_two_level_nvfp4_epilogue(gpu, sf_layout):
+    """Two-level NVFP4 of the device's own h, bit-exact against the oracle's, for amax values
+    chosen as a delayed-scaling caller would pass them (the amax of h itself, an older and
+    larger one, a smaller one that saturates blocks) and for the degenerate ones (zero,
+    negative, infinite: global scale 1; tiny: the 2^100 cap)."""
+    M, N, K = 160, 256, 256
+    ops = [t.cuda() for t in _operands(M, N, K, seed=110)]
+    h = bits(gpu.glu_gemm(*ops, act="geglu"))
+    hf = si.from_bits(h).float().numpy()
+    sfl = oracle.SF_128x4 if sf_layout == "128x4" else oracle.SF_ROWMAJOR
+    top = float(np.abs(hf).max())
+    for amax in (top, 3.0 * top, top / 16, 0.0, -1.0, float("inf"), 1e-35):
+        a = torch.tensor([amax], dtype=torch.float32, device="cuda")
+        q, sf = gpu.glu_gemm_nvfp4_gs(*ops, amax=a, act="geglu", sf_layout=sf_layout)
+        o = oracle.quant_nvfp4_gs(hf, np.float32(amax), sfl)
+        assert np.array_equal(u8(q), o[0]), amax
+        assert np.array_equal(u8(sf).ravel(), np.asarray(o[1]).ravel()), amax
+
+
 def test_gemm_deterministic_and_row_batch_invariant(gpu):
     M, N, K = 256, 128, 256
     xq, xs, wq, ws = (t.cuda() for t in _operands(M, N, K, seed=80))

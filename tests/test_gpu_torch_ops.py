@@ -42,6 +42,8 @@ def test_ops_equal_the_binding(gpu):
     assert _same([ops.glu_gemm(*mx, "geglu")], [gpu.glu_gemm(*mx, act="geglu")])
     assert _same(ops.glu_gemm_mxfp8(*mx, "swiglu"), gpu.glu_gemm_mxfp8(*mx))
     assert _same(ops.glu_gemm_nvfp4(*mx, "geglu", "128x4"), gpu.glu_gemm_nvfp4(*mx, sf_layout="128x4"))
+    am = torch.tensor([3.0], dtype=torch.float32, device="cuda")
+    assert _same(ops.glu_gemm_nvfp4_gs(*mx, am, "geglu", "rowmajor"), gpu.glu_gemm_nvfp4_gs(*mx, amax=am))
 
 
 def _mx_operands(M, N, K, seed):

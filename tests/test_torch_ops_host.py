@@ -52,6 +52,9 @@ def test_fake_shapes_match_the_entry_points():
         assert q.shape == (M, 128) and sr.shape == (M, 4) and q.dtype == sr.dtype == torch.uint8
         q, sf = ops.glu_gemm_nvfp4(xq, xs, wq, ws, "geglu", "128x4")
         assert q.shape == (M, 64) and sf.numel() == glu.nvfp4_sf_bytes(M, 128, "128x4")
+        am = torch.empty((1,), dtype=torch.float32, device="cuda")
+        q, sf = ops.glu_gemm_nvfp4_gs(xq, xs, wq, ws, am, "geglu", "rowmajor")
+        assert q.shape == (M, 64) and sf.shape == (M, 8)
 
 
 def test_graph_capture_keeps_each_op_whole():
