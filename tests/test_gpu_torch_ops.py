@@ -97,11 +97,14 @@ def test_opcheck(gpu):
 def test_compile_fullgraph_matches_eager(gpu):
     g, u, d = _operands(128, 256, 64)
 
+    mx = _mx_operands(128, 128, 256, 67)
+
     def step(g, u, d):
         h = ops.glu(g, u, "swiglu", "split")
         fq = ops.glu_mxfp8(g, u, "swiglu", "split", True, True, False)
         bq = ops.glu_backward_mxfp8(g, u, d, "swiglu", True, True, False)
-        return (h,) + tuple(fq) + tuple(bq)
+        gq = ops.glu_gemm_mxfp8(*mx, "swiglu")
+        return (h,) + tuple(fq) + tuple(bq) + tuple(gq)
 
     eager = step(g, u, d)
     compiled = torch.compile(step, fullgraph=True, backend="aot_eager")(g, u, d)
