@@ -32,10 +32,11 @@
 // step t's matrix work to arrive.  The E8M0 scales come in groups of 4 K steps (16 bytes a
 // row, 4 lanes a row) into a ring of two groups.  Rows past M read zeros.
 //
-// Epilogue: per 16-row slice, the GLU in FP32 for all elements, one wave-wide branch for
-// the rare tail elements, BF16 pairs by the hardware converter, then (MXFP8) the block amax
-// over the 16 lanes of a DPP row and the scaled E4M3 converter.  A transpose within each
-// 16-lane row group (ds_bpermute) gives each lane 4 consecutive columns, stored at once.
+// Epilogue: the products are formed as W X^T, so each 16 x 16 result is a transposed tile of
+// Y and a lane holds 4 consecutive columns of one row.  Per 16-row slice: the GLU in FP32 for
+// all elements, one wave-wide branch for the rare tail elements, BF16 pairs by the hardware
+// converter; then the block amax in the lane and over the row's 4 lanes (two exchanges), the
+// block scale, the hardware converters, and one store per lane and tile.
 //
 // Tile order: workgroups are spread over the 8 XCDs in turn, so workgroup b is given tile
 // (b mod 8) * (tiles / 8) + b / 8, which keeps each XCD on a contiguous run of tiles, and
@@ -223,11 +224,14 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
 #pragma unroll
         for (int j = 0; j < WN; j++)
           acc[h][i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              xa[i], wb[h][j], acc[h][i][j], 0, 0, 0, xs[i], 0, ws[h][j]);
+              wb[h][j], xa[i], acc[h][i][j], 0, 0, 0, ws[h][j], 0, xs[i]);
   }
 
-  // Epilogue.  acc[h][i][j][e] is Y at row row0 + 16 i + 4 g + e, column col0 + 16 j + r of
-  // the gate (h = 0) or up (h = 1) half.
+  // Epilogue.  The products are formed as W X^T (W the first operand), so each 16 x 16 result
+  // is a transposed tile of Y: acc[h][i][j][e] is Y at row row0 + 16 i + r and column
+  // col0 + 16 j + 4 g + e of the gate (h = 0) or up (h = 1) half.  A lane thus holds 4
+  // consecutive columns of one row per tile, and a row's 16 columns of a tile sit in the 4
+  // lanes r, 16 + r, 32 + r, 48 + r.
   if constexpr (OUT == GEMM_F32) {
     // test hook: the pre-activation itself, [M, 2N] FP32
     const auto ry = rsrc(a.y);
@@ -236,33 +240,35 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
 #pragma unroll
       for (int i = 0; i < WM; i++)
 #pragma unroll
-        for (int j = 0; j < WN; j++)
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const uint32_t row = row0 + 16u * i + 4u * g + (uint32_t)e;
-            const uint32_t col = h * N + col0 + 16u * j + r;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[h][i][j][e]), ry,
-                                                  row < (uint32_t)a.M ? 4u * (row * 2u * N + col) : kOob, 0, 0);
-          }
+        for (int j = 0; j < WN; j++) {
+          const uint32_t row = row0 + 16u * i + r;
+          const uint32_t col = h * N + col0 + 16u * j + 4u * g;
+          const v4f v = acc[h][i][j];
+          __builtin_amdgcn_raw_buffer_store_b128((u32x4){__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                         __float_as_uint(v[2]), __float_as_uint(v[3])},
+                                                 ry, row < M ? 4u * (row * 2u * N + col) : kOob, 0, 0);
+        }
   } else {
     // h = bf16(act(gate) * up), one 16-row slice i at a time (so that the slice's
     // accumulators die as it is written): the fast form for every element, then the tail
     // form where the fast one leaves FP32 (one branch per slice for the whole wave, rarely
-    // taken).  The BF16 pair P[e][b] holds tiles 2b (low half) and 2b + 1 of row
-    // 16 i + 4 g + e.  Stores: within each 16-lane row group the pairs are transposed so that
-    // lane r holds columns col0 + 4r .. 4r + 3 (lane 4 (r % 4) + k holds column 4r + k in
-    // tile r / 4), and each lane writes them with one store.
-    static_assert(WN == 4, "two BF16 pairs per row and lane");
-    auto gather = [&](uint32_t v, uint32_t k) {
-      return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(4u * (16u * g + 4u * (r & 3u) + k)), (int)v);
+    // taken).  P[j][0] holds columns 4g, 4g + 1 of tile j as a BF16 pair, P[j][1] 4g + 2, 4g + 3.
+    auto xor32 = [&](uint32_t v) {   // the value of lane l ^ 32
+      return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(4u * (lane ^ 32u)), (int)v);
     };
-    const uint32_t sel = r >> 2;   // the source tile of this lane's columns
+    // the packed maxima of the lane's row over its 4 lanes g
+    auto row_max = [&](uint32_t m) {
+      m = pkmax(m, swz_xor16(m));
+      return pkmax(m, xor32(m));
+    };
     const auto rh = rsrc(a.h), rq = rsrc(a.q_row), rs = rsrc(a.s_row);
     GlobalScale gs;
     if constexpr (OUT >= GEMM_NV_GS_ROWMAJOR) gs = global_scale(*a.amax);
     const uint32_t NB = N / 32u;
 #pragma unroll
     for (int i = 0; i < WM; i++) {
+      const uint32_t row = row0 + 16u * i + r;
+      const bool ok = row < M;
       float hv[WN][4];
       bool tail = false;
 #pragma unroll
@@ -277,102 +283,98 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
             if (fwd_tail_needed<ACT>(acc[0][i][j][e], acc[1][i][j][e]))
               hv[j][e] = glu_fwd_tail<ACT>(acc[0][i][j][e], acc[1][i][j][e]);
       }
-      uint32_t P[4][2];
+      uint32_t P[WN][2];
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        P[e][0] = pack_bf16(hv[0][e], hv[1][e]);
-        P[e][1] = pack_bf16(hv[2][e], hv[3][e]);
+      for (int j = 0; j < WN; j++) {
+        P[j][0] = pack_bf16(hv[j][0], hv[j][1]);
+        P[j][1] = pack_bf16(hv[j][2], hv[j][3]);
       }
+      const uint32_t cl = col0 + 4u * g;   // the lane's first column in tile 0
+      if constexpr (OUT == GEMM_H) {
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const uint32_t row = row0 + 16u * i + 4u * g + (uint32_t)e;
-        const bool ok = row < M;
-        if constexpr (OUT == GEMM_H) {
-          uint32_t v[4];
+        for (int j = 0; j < WN; j++)
+          __builtin_amdgcn_raw_buffer_store_b64((v2u){P[j][0], P[j][1]}, rh,
+                                                ok ? 2u * (row * (uint32_t)a.ld_h + cl + 16u * j) : kOob, 0, 0);
+      } else if constexpr (OUT == GEMM_MXFP8) {
+        // MXFP8 rowwise: the wave's 64 columns of a row are two blocks of 32 (tiles 2b and
+        // 2b + 1); block amax in the lane (packed), then over the row's 4 lanes, both blocks
+        // at once (block 0 in the low half)
+        static_assert(WN == 4, "two MXFP8 blocks per row and wave");
+        uint32_t mb[2];
 #pragma unroll
-          for (int k = 0; k < 4; k++) {
-            const uint32_t w0 = gather(P[e][0], k), w1 = gather(P[e][1], k);
-            v[k] = ((sel < 2u ? w0 : w1) >> (16u * (sel & 1u))) & 0xffffu;
+        for (int b = 0; b < 2; b++) {
+          const uint32_t t = pkmax(pkmax(P[2 * b][0] & 0x7fff7fffu, P[2 * b][1] & 0x7fff7fffu),
+                                   pkmax(P[2 * b + 1][0] & 0x7fff7fffu, P[2 * b + 1][1] & 0x7fff7fffu));
+          mb[b] = umax(lo16(t), hi16(t));
+        }
+        const uint32_t mm = row_max(mb[0] | (mb[1] << 16));
+        uint32_t sbs = 0;
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+          const uint32_t m = b ? hi16(mm) : lo16(mm);
+          const bool nonfinite = m >= 0x7f80u;
+          const uint32_t sb = nonfinite ? 0xffu : mx_scale_byte(m << 16);
+          sbs |= sb << (8 * b);
+          const float sc = e8m0_value(sb);
+#pragma unroll
+          for (int t = 0; t < 2; t++) {
+            const int j = 2 * b + t;
+            uint32_t c = fp8x2_scaled<false>(0u, P[j][0], sc);
+            c = fp8x2_scaled<true>(c, P[j][1], sc);
+            __builtin_amdgcn_raw_buffer_store_b32(nonfinite ? 0x7f7f7f7fu : c, rq,
+                                                  ok ? row * N + cl + 16u * j : kOob, 0, 0);
           }
-          __builtin_amdgcn_raw_buffer_store_b64((v2u){v[0] | (v[1] << 16), v[2] | (v[3] << 16)}, rh,
-                                                ok ? 2u * (row * (uint32_t)a.ld_h + col0 + 4u * r) : kOob, 0, 0);
-        } else if constexpr (is_nv(OUT)) {
-          // NVFP4: a 16-column block is one tile j; its amax runs over the 16 lanes of a DPP
-          // row, two blocks at a time on packed 16-bit magnitudes
-          uint32_t m2[2];
+        }
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sbs, rs, ok && g == 0 ? row * NB + col0 / 32u : kOob, 0, 0);
+      } else {
+        // NVFP4: a 16-column block is one tile j; its amax in the lane, then over the row's 4
+        // lanes, two blocks at a time (packed)
+        uint32_t mt[WN];
 #pragma unroll
-          for (int b = 0; b < 2; b++) {
-            uint32_t m = P[e][b] & 0x7fff7fffu;
-            m = pkmax(m, dpp<DPP_XOR1>(m));
-            m = pkmax(m, dpp<DPP_XOR2>(m));
-            m = pkmax(m, dpp<0x124>(m));  // row_ror:4
-            m2[b] = pkmax(m, dpp<DPP_ROW_ROR8>(m));
-          }
-          uint32_t word = 0, sbs = 0;
+        for (int j = 0; j < WN; j++) {
+          const uint32_t t = pkmax(P[j][0] & 0x7fff7fffu, P[j][1] & 0x7fff7fffu);
+          mt[j] = umax(lo16(t), hi16(t));
+        }
+        const uint32_t m01 = row_max(mt[0] | (mt[1] << 16)), m23 = row_max(mt[2] | (mt[3] << 16));
+        uint32_t sbs = 0;
+#pragma unroll
+        for (int j = 0; j < WN; j++) {
+          const uint32_t mj = j == 0 ? lo16(m01) : j == 1 ? hi16(m01) : j == 2 ? lo16(m23) : hi16(m23);
+          const bool nonfinite = mj >= 0x7f80u;
           float y[4];
+          const float x[4] = {bf_lo(P[j][0]), bf_hi(P[j][0]), bf_lo(P[j][1]), bf_hi(P[j][1])};
+          uint32_t sc;
+          if constexpr (OUT >= GEMM_NV_GS_ROWMAJOR) {
+            // two-level: E4M3(fl(bamax * k)), saturating at 448; codes E2M1(fl(x * fl(s / S)))
+            const float d = __builtin_fminf(__uint_as_float(mj << 16) * gs.k, 448.0f);
+            sc = nonfinite ? 0x7fu : (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(d, 0.0f, 0, false) & 0xffu;
+            const float S = e4m3_value(nonfinite ? 0u : sc);
+            const float rs_ = S > 0.0f ? gs.s / S : 0.0f;   // IEEE division
+            // |x * rs_| beyond 8 saturates to 6 either way; the clamp keeps the input finite
 #pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const uint32_t mj = (j & 1) ? hi16(m2[j >> 1]) : lo16(m2[j >> 1]);
-            const bool nonfinite = mj >= 0x7f80u;
-            const float x = (j & 1) ? bf_hi(P[e][j >> 1]) : bf_lo(P[e][j >> 1]);
-            uint32_t sc;
-            if constexpr (OUT >= GEMM_NV_GS_ROWMAJOR) {
-              // two-level: E4M3(fl(bamax * k)), saturating at 448; codes E2M1(fl(x * fl(s / S)))
-              const float d = __builtin_fminf(__uint_as_float(mj << 16) * gs.k, 448.0f);
-              sc = nonfinite ? 0x7fu : (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(d, 0.0f, 0, false) & 0xffu;
-              const float S = e4m3_value(nonfinite ? 0u : sc);
-              const float rs = S > 0.0f ? gs.s / S : 0.0f;   // IEEE division
-              // |x * rs| beyond 8 saturates to 6 either way; the clamp keeps the input finite
-              y[j] = nonfinite ? 0.0f : __builtin_amdgcn_fmed3f(x * rs, -8.0f, 8.0f);
-            } else {
-              sc = nonfinite ? 0x7fu : nv_scale_code_bf16(__uint_as_float(mj << 16));
-              const float S = e4m3_value(nonfinite ? 0u : sc);
-              const float R = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
-              y[j] = nonfinite ? 0.0f : e2m1_operand(x, R);
-            }
-            sbs |= sc << (8 * j);
-          }
-          // (a block holding NaN or Inf gets scale 0x7F and zero codes)
-          word = fp4x2<0>(word, y[0], y[1]);
-          word = fp4x2<1>(word, y[2], y[3]);
-          uint32_t v = 0;
-#pragma unroll
-          for (int k = 0; k < 4; k++) v |= ((gather(word, k) >> (4u * sel)) & 0xfu) << (4 * k);
-          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, rq, ok ? row * (N / 2u) + (col0 + 4u * r) / 2u : kOob, 0, 0);
-          // the row's four scale bytes of this wave, blocks col0 / 16 .. + 3, as one word
-          if constexpr (OUT == GEMM_NV_ROWMAJOR || OUT == GEMM_NV_GS_ROWMAJOR) {
-            __builtin_amdgcn_raw_buffer_store_b32(sbs, rs, ok && r == 0 ? row * (N / 16u) + col0 / 16u : kOob, 0, 0);
+            for (int e = 0; e < 4; e++) y[e] = nonfinite ? 0.0f : __builtin_amdgcn_fmed3f(x[e] * rs_, -8.0f, 8.0f);
           } else {
-            // 128x4: rows padded to 128 with zero scales (N / 16 is a multiple of 4)
-            const uint32_t off = (row >> 7) * (N / 64u) * 512u + (row & 31u) * 16u + ((row & 127u) >> 5) * 4u +
-                                 (col0 / 64u) * 512u;
-            const bool pad_ok = row < ((M + 127u) & ~127u);
-            __builtin_amdgcn_raw_buffer_store_b32(ok ? sbs : 0u, rs, pad_ok && r == 0 ? off : kOob, 0, 0);
+            sc = nonfinite ? 0x7fu : nv_scale_code_bf16(__uint_as_float(mj << 16));
+            const float S = e4m3_value(nonfinite ? 0u : sc);
+            const float R = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; e++) y[e] = nonfinite ? 0.0f : e2m1_operand(x[e], R);
           }
+          sbs |= sc << (8 * j);
+          // (a block holding NaN or Inf gets scale 0x7F and zero codes)
+          uint32_t word = fp4x2<0>(0u, y[0], y[1]);
+          word = fp4x2<1>(word, y[2], y[3]);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)word, rq, ok ? (row * N + cl + 16u * j) / 2u : kOob, 0, 0);
+        }
+        // the row's four scale bytes of this wave, blocks col0 / 16 .. + 3, as one word
+        if constexpr (OUT == GEMM_NV_ROWMAJOR || OUT == GEMM_NV_GS_ROWMAJOR) {
+          __builtin_amdgcn_raw_buffer_store_b32(sbs, rs, ok && g == 0 ? row * (N / 16u) + col0 / 16u : kOob, 0, 0);
         } else {
-          // MXFP8 rowwise: the wave's 64 columns of a row are two blocks of 32 (pair b holds
-          // block b's two elements of this lane); a row sits in the 16 lanes of one DPP row
-          uint32_t codes = 0, sbs = 0;
-#pragma unroll
-          for (int b = 0; b < 2; b++) {
-            const uint32_t p = P[e][b];
-            uint32_t m = umax(p & 0x7fffu, (p >> 16) & 0x7fffu);
-            m = umax(m, dpp<DPP_XOR1>(m));
-            m = umax(m, dpp<DPP_XOR2>(m));
-            m = umax(m, dpp<0x124>(m));  // row_ror:4
-            m = umax(m, dpp<DPP_ROW_ROR8>(m));
-            const bool nonfinite = m >= 0x7f80u;
-            const uint32_t sb = nonfinite ? 0xffu : mx_scale_byte(m << 16);
-            sbs |= sb << (8 * b);
-            const uint32_t c = b == 0 ? fp8x2_scaled<false>(0u, p, e8m0_value(sb))
-                                      : fp8x2_scaled<true>(0u, p, e8m0_value(sb));
-            codes |= nonfinite ? 0x7f7fu << (16 * b) : c;
-          }
-          uint32_t v = 0;
-#pragma unroll
-          for (int k = 0; k < 4; k++) v |= ((gather(codes, k) >> (8u * sel)) & 0xffu) << (8 * k);
-          __builtin_amdgcn_raw_buffer_store_b32(v, rq, ok ? row * N + col0 + 4u * r : kOob, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sbs, rs, ok && r == 0 ? row * NB + col0 / 32u : kOob, 0, 0);
+          // 128x4: rows padded to 128 with zero scales (N / 16 is a multiple of 4)
+          const uint32_t off = (row >> 7) * (N / 64u) * 512u + (row & 31u) * 16u + ((row & 127u) >> 5) * 4u +
+                               (col0 / 64u) * 512u;
+          const bool pad_ok = row < ((M + 127u) & ~127u);
+          __builtin_amdgcn_raw_buffer_store_b32(ok ? sbs : 0u, rs, pad_ok && g == 0 ? off : kOob, 0, 0);
         }
       }
     }
