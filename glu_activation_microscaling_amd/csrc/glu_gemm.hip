@@ -77,11 +77,13 @@ enum {
 };
 constexpr bool is_nv(int out) { return out >= GEMM_NV_ROWMAJOR; }
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, off, 0, 0, 0);
+// Direct-to-LDS loads: lane l's bytes go to lds + size * l.  voffset is the lane's part,
+// soffset the wave-uniform part (an out-of-range voffset stays out of range with it added).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voff, soff, 0, 0);
 }
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 4, off, 0, 0, 0);
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 4, voff, soff, 0, 0);
 }
 
 // s_waitcnt on the vector-memory counter alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
@@ -165,8 +167,18 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
     const bool live = 4u * grp + (lane & 3u) < T;
 #pragma unroll
     for (int i = 0; i < SC_LOADS; i++)
-      dma4(sx[i] ? rxs : rws, sok[i] && live ? soff[i] + 16u * grp : kOob, sc + 256u * (SC_LOADS * wave + i));
+      dma4(sx[i] ? rxs : rws, sok[i] && live ? soff[i] : kOob, 16u * grp, sc + 256u * (SC_LOADS * wave + i));
   };
+  // the lanes' parts of the operand loads (rows past M out of range); the K offset is added
+  // as the instruction's scalar offset
+  uint32_t vx[2][2], vw[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      vx[i][h] = xokh[i][h] ? xoff[i] + 8u * h * K + lchunk[h] : kOob;
+      vw[i][h] = woff[i] + 8u * h * K + lchunk[h];
+    }
   auto issue = [&](uint32_t step, uint32_t stage) {
     uint8_t* st = smem + stage * STAGE;
     const uint32_t k0 = step * GM_BK;
@@ -174,12 +186,12 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
     for (int i = 0; i < 2; i++)
 #pragma unroll
       for (int h = 0; h < 2; h++)
-        dma16(rx, xokh[i][h] ? xoff[i] + 8u * h * K + k0 + lchunk[h] : kOob, st + (2u * (2u * wave + i) + h) * 1024u);
+        dma16(rx, vx[i][h], k0, st + (2u * (2u * wave + i) + h) * 1024u);
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
       for (int h = 0; h < 2; h++)
-        dma16(rw, woff[i] + 8u * h * K + k0 + lchunk[h], st + W_OFF + (2u * (2u * wave + i) + h) * 1024u);
+        dma16(rw, vw[i][h], k0, st + W_OFF + (2u * (2u * wave + i) + h) * 1024u);
   };
 
   v4f acc[2][WM][WN];
@@ -190,32 +202,36 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
 #pragma unroll
       for (int j = 0; j < WN; j++) acc[h][i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
+  // The lane's fragment bases (row r, chunks g and g + 4 at their swizzled positions) in
+  // the wave's first X slice and first gate slice; the slices, the stage and the up half are
+  // compile-time offsets from these.
   const uint32_t fo_a = 128u * r + 16u * (g ^ ((r >> 1) & 7u));
   const uint32_t fo_b = 128u * r + 16u * ((g + 4u) ^ ((r >> 1) & 7u));
-  issue_scales(0);
-  issue(0, 0);
-  for (uint32_t step = 0; step < T; step++) {
+  const uint32_t xb_a = fo_a + 2048u * ((wave >> 1) * WM), xb_b = fo_b + 2048u * ((wave >> 1) * WM);
+  const uint32_t wb_a = fo_a + W_OFF + 2048u * ((wave & 1) * WN), wb_b = fo_b + W_OFF + 2048u * ((wave & 1) * WN);
+  const uint32_t sc_x = 16u * (16u * ((wave >> 1) * WM) + r) + g;             // scale bytes
+  const uint32_t sc_w = 16u * (GM_BM + 16u * ((wave & 1) * WN) + r) + g;
+  auto run_step = [&](uint32_t step, auto STG) {
+    constexpr uint32_t stage = decltype(STG)::value;
     wait_vm<0>();
     lds_barrier();   // every wave's loads of this step have landed; step - 1's stage is free
     if (step % 4u == 0u && step + 4u < T) issue_scales(step / 4u + 1u);
-    if (step + 1u < T) issue(step + 1u, (step + 1u) % STAGES);
-    const uint8_t* st = smem + (step % STAGES) * STAGE;
-    const uint8_t* sc = smem + SC_OFF + ((step / 4u) & 1u) * SC_GROUP + 4u * (step % 4u) + g;
+    if (step + 1u < T) issue(step + 1u, 1u - stage);
+    const uint8_t* st = smem + stage * STAGE;
+    const uint32_t sq = SC_OFF + ((step / 4u) & 1u) * SC_GROUP + 4u * (step % 4u);
     v8i xa[WM], wb[2][WN];
     int xs[WM], ws[2][WN];
 #pragma unroll
     for (int i = 0; i < WM; i++) {
-      const uint32_t sl = (wave >> 1) * WM + i;
-      xa[i] = frag(st + 2048u * sl, fo_a, fo_b);
-      xs[i] = sc[16u * (16u * sl + r)];
+      xa[i] = frag(st, xb_a + 2048u * i, xb_b + 2048u * i);
+      xs[i] = smem[sq + sc_x + 256u * i];
     }
 #pragma unroll
     for (int h = 0; h < 2; h++)
 #pragma unroll
       for (int j = 0; j < WN; j++) {
-        const uint32_t sl = 8u * h + (wave & 1) * WN + j;
-        wb[h][j] = frag(st + W_OFF + 2048u * sl, fo_a, fo_b);
-        ws[h][j] = sc[16u * (GM_BM + 16u * sl + r)];
+        wb[h][j] = frag(st, wb_a + 2048u * (8u * h + j), wb_b + 2048u * (8u * h + j));
+        ws[h][j] = smem[sq + sc_w + 256u * (8u * h + j)];
       }
 #pragma unroll
     for (int h = 0; h < 2; h++)
@@ -225,6 +241,13 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
         for (int j = 0; j < WN; j++)
           acc[h][i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               wb[h][j], xa[i], acc[h][i][j], 0, 0, 0, ws[h][j], 0, xs[i]);
+  };
+  static_assert(STAGES == 2, "two steps per iteration, one per stage");
+  issue_scales(0);
+  issue(0, 0);
+  for (uint32_t step = 0; step < T; step += 2) {
+    run_step(step, std::integral_constant<uint32_t, 0>{});
+    if (step + 1u < T) run_step(step + 1u, std::integral_constant<uint32_t, 1>{});
   }
 
   // Epilogue.  The products are formed as W X^T (W the first operand), so each 16 x 16 result
