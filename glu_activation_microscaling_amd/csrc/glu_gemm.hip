@@ -1,5 +1,5 @@
-// Merged gate/up MXFP8 GEMM with the GLU as its epilogue (and optionally the MXFP8 rowwise
-// quantizer after it): "feat(phyai-kernel): add Thor NVFP4 GeGLU kernel for pi0.5" (Summary:
+// Merged gate/up MXFP8 GEMM with the GLU as its epilogue (and optionally the MXFP8 rowwise or
+// the NVFP4 quantizer after it): "feat(phyai-kernel): add Thor NVFP4 GeGLU kernel for pi0.5" (Summary:
 // the GeGLU fold follows the merged gate/up GEMM), in the MXFP8 form of "Add swiglu + MXFP8
 // fused CuTe DSL kernel" (Performance: the fused-w13 MoE composite under an MXFP8 recipe;
 // API: a fused w13 projection packs [gate | up]).  The pre-activation never reaches memory.
@@ -30,7 +30,10 @@
 // fragment reads (row r, chunks g and g + 4 per lane) hit distinct LDS banks.  Two stages
 // alternate: the loads of step t + 1 are issued right after the barrier of step t and have
 // step t's matrix work to arrive.  The E8M0 scales come in groups of 4 K steps (16 bytes a
-// row, 4 lanes a row) into a ring of two groups.  Rows past M read zeros.
+// row, 4 lanes a row) into a ring of two groups.  Rows past M read zeros.  The loop body runs
+// two steps with the stage as a compile-time constant, so every fragment read is a lane base
+// register plus an immediate offset and each load's K offset rides in the scalar offset: the
+// loop carries almost no VALU work (a wave64 VALU instruction occupies its SIMD 4 cycles).
 //
 // Epilogue: the products are formed as W X^T, so each 16 x 16 result is a transposed tile of
 // Y and a lane holds 4 consecutive columns of one row.  Per 16-row slice: the GLU in FP32 for
