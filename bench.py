@@ -248,6 +248,28 @@ def sweep(torch, glu, si, iters):
             print(f"[bench] {name}: {t['median_us']:.2f} us", file=sys.stderr, flush=True)
             res[name] = dict(flops=2 * M * K * 2 * N, us=round(t["median_us"], 2), tflops=round(tf, 1),
                              frac=round(tf / PEAK_FP8_TFLOPS, 4))
+        # context, not part of the path: the platform library's GEMM alone (torch._scaled_mm,
+        # BF16 output, no activation, no quantizer) on the same codes, with the same E8M0 block
+        # scales and with one tensor-wide scale
+        one = torch.ones((), device="cuda")
+        lib = {"blockwise": lambda s: torch._scaled_mm(
+                   s[0].view(torch.float8_e4m3fn), s[2].view(torch.float8_e4m3fn).t(),
+                   scale_a=s[1].view(torch.float8_e8m0fnu), scale_b=s[3].view(torch.float8_e8m0fnu),
+                   out_dtype=torch.bfloat16),
+               "tensorwise": lambda s: torch._scaled_mm(
+                   s[0].view(torch.float8_e4m3fn), s[2].view(torch.float8_e4m3fn).t(),
+                   scale_a=one, scale_b=one, out_dtype=torch.bfloat16)}
+        for kind, fn in lib.items():
+            name = f"library_fp8_gemm_{kind}_{M}x{2 * N}x{K}"
+            try:
+                t = time_launches(torch, [lambda s=s: fn(s) for s in sets], iters)
+            except RuntimeError as e:  # a shape or scaling the library does not take
+                print(f"[bench] {name}: not supported ({str(e).splitlines()[0][:80]})", file=sys.stderr, flush=True)
+                continue
+            tf = 2.0 * M * K * 2 * N / t["median_us"] / 1e6
+            print(f"[bench] {name}: {t['median_us']:.2f} us", file=sys.stderr, flush=True)
+            res[name] = dict(flops=2 * M * K * 2 * N, us=round(t["median_us"], 2), tflops=round(tf, 1),
+                             frac=round(tf / PEAK_FP8_TFLOPS, 4))
         del sets, out, nv_out
         torch.cuda.empty_cache()
     return res
