@@ -42,7 +42,8 @@ _E4M3 = oracle.e4m3_to_f64(np.arange(256, dtype=np.uint8))   # the oracle's valu
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 128, 512), (200, 128, 256), (128, 256, 2048), (37, 128, 128),
-                                   (96, 384, 384), (64, 128, 640), (300, 256, 1152)])
+                                   (96, 384, 384), (64, 128, 640), (300, 256, 1152), (1, 128, 128),
+                                   (1, 256, 384)])
 def test_gemm_within_the_accumulation_bound(gpu, M, N, K):
     ops = _operands(M, N, K, seed=M + N + K)
     y = gpu.mx_gemm_f32(*(t.cuda() for t in ops)).cpu().numpy().astype(np.float64)
@@ -160,6 +161,21 @@ def test_gemm_deterministic_and_row_batch_invariant(gpu):
     c = gpu.glu_gemm(xq[100:200].contiguous(), xs[100:200].contiguous(), wq, ws)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(a[100:200].view(torch.int16), c.view(torch.int16))
+
+
+def test_gemm_zero_rows(gpu):
+    """M = 0 is a valid empty product: every entry point returns empty outputs and leaves the
+    caller's buffers untouched."""
+    N, K = 128, 256
+    _, _, wq, ws = (t.cuda() for t in _operands(4, N, K, seed=82))
+    xq = torch.empty((0, K), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((0, K // 32), dtype=torch.uint8, device="cuda")
+    assert gpu.glu_gemm(xq, xs, wq, ws).shape == (0, N)
+    q, s = gpu.glu_gemm_mxfp8(xq, xs, wq, ws)
+    assert q.shape == (0, N) and s.shape == (0, N // 32)
+    q, s = gpu.glu_gemm_nvfp4(xq, xs, wq, ws, sf_layout="rowmajor")
+    assert q.shape == (0, N // 2) and s.numel() == 0
+    torch.cuda.synchronize()
 
 
 def test_gemm_end_to_end_against_the_exact_oracle(gpu):
