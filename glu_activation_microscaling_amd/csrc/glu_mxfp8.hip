@@ -31,7 +31,8 @@ namespace {
 
 // Build-time tuning (fixed defaults; alternatives are compiled only to measure them):
 //   GLU_MX_NT_LOADS: non-temporal (streaming) operand loads.
-//   GLU_MX_NT_STORES: -1 per kernel (below); 0 / 1 non-temporal code stores off / on.
+//   GLU_MX_NT_STORES: -1 by the size of the codes written (below); 0 / 1 non-temporal
+//   code stores off / on.
 #ifndef GLU_MX_NT_LOADS
 #define GLU_MX_NT_LOADS 1
 #endif
@@ -83,13 +84,18 @@ template <int FLAGS, int MODE>
 using TileOf = Tile<FLAGS == ROWWISE ? GLU_MX_ROW_WM : 4,
                     FLAGS == ROWWISE ? GLU_MX_ROW_WN(MODE) : GLU_MX_COL_WN>;
 
-// Non-temporal code stores: measured faster only for the backward quantized both ways
-// (234 vs 267 us at [16384, 7168] in the blocked tile order); slower for the forward both
-// ways (138 vs 126 us).
-template <int MODE, int FLAGS>
-constexpr bool nt_stores() {
-  return GLU_MX_NT_STORES < 0 ? MODE == MODE_BWD && FLAGS == (ROWWISE | COLWISE)
-                               : GLU_MX_NT_STORES == 1;
+// Non-temporal code stores, chosen per launch from the size of the codes written.  Ordinary
+// stores are absorbed by the 256 MB last-level cache and drain after the kernel when the codes
+// fit there; when they do not, non-temporal stores are faster.  Measured (MXFP8 SwiGLU):
+//   [16384, 7168]  forward rowwise (117 MB)   101.5 vs 106.9 us  (ordinary faster)
+//                  forward both (235 MB)      125.9 vs 136.5 us  (ordinary faster)
+//                  backward rowwise (235 MB)  157.8 vs 163.2 us  (ordinary faster)
+//                  backward both (470 MB)     234 vs 267 us      (non-temporal faster)
+//   [131072, 8192] forward rowwise (1.07 GB)  896.4 vs 982.5 us  (non-temporal faster)
+//                  forward both (2.1 GB)      1211 vs 1368 us    (non-temporal faster)
+constexpr int64_t kNtStoreBytes = 256ll << 20;
+bool nt_stores(int64_t code_bytes) {
+  return GLU_MX_NT_STORES < 0 ? code_bytes > kNtStoreBytes : GLU_MX_NT_STORES == 1;
 }
 
 // Order of the tiles; each XCD takes a contiguous run of it.
@@ -749,7 +755,7 @@ __device__ __forceinline__ TileGeom wave_geom(const MxArgs& a, int64_t r0, int64
 #endif
 template <int ACT, int LAYOUT, int FLAGS, int MODE, int TPW>
 __global__ __launch_bounds__((TileOf<FLAGS, MODE>::NTHREADS)) GLU_MX_KATTR void k_mxfp8(
-    MxArgs a, uint32_t tiles_m, uint32_t tiles_n, uint32_t ntiles, uint32_t per_xcd) {
+    MxArgs a, uint32_t tiles_m, uint32_t tiles_n, uint32_t ntiles, uint32_t per_xcd, uint32_t nt) {
   using T = TileOf<FLAGS, MODE>;
   using St = Stage<T, FLAGS>;
   constexpr int TM = T::TM, TN = T::TN;
@@ -766,13 +772,17 @@ __global__ __launch_bounds__((TileOf<FLAGS, MODE>::NTHREADS)) GLU_MX_KATTR void 
   const int lr = lane & 7, lc = lane >> 3;
   const int row0 = 32 * wm + 4 * lr, col = 64 * wn + 8 * lc;
   const int64_t ldq = PARTS * a.N;
-  constexpr bool NT = nt_stores<MODE, FLAGS>();
   constexpr int ORDER = tile_order<FLAGS>();
   constexpr int PIPE = GLU_MX_PIPE;
 
   uint32_t tm, tn;
   tile_of<T, ORDER>(beg, tiles_m, tiles_n, tm, tn);
   int64_t r0 = (int64_t)tm * TM, c0 = (int64_t)tn * TN;
+  // one store form per launch (nt is uniform): both are instantiated, a scalar branch picks
+  auto write_part = [&](const St& S, int64_t coloff) {
+    if (nt != 0u) write_out<T, FLAGS, true>(S, a, r0, c0, coloff, ldq, tid);
+    else write_out<T, FLAGS, false>(S, a, r0, c0, coloff, ldq, tid);
+  };
   TileOps<LAYOUT, MODE> o;
   load_ops<LAYOUT, MODE>(o, a, wave_geom(a, r0, c0, wm, wn, lc), lr, lc);
   TileVals<MODE> R;
@@ -786,7 +796,7 @@ __global__ __launch_bounds__((TileOf<FLAGS, MODE>::NTHREADS)) GLU_MX_KATTR void 
     } else if constexpr (PIPE == 1 && MODE == MODE_BWD) {
       stage_bf16<T, FLAGS>(R.h[0], A, row0, col, lr, lc);
       __syncthreads();
-      write_out<T, FLAGS, NT>(A, a, r0, c0, 0, ldq, tid);
+      write_part(A, 0);
       stage_bf16<T, FLAGS>(R.h[1], B, row0, col, lr, lc);
     } else {
       stage_bf16<T, FLAGS>(R.h[0], A, row0, col, lr, lc);
@@ -810,10 +820,10 @@ __global__ __launch_bounds__((TileOf<FLAGS, MODE>::NTHREADS)) GLU_MX_KATTR void 
     }
     __syncthreads();
     if constexpr (PIPE == 1 && MODE == MODE_BWD) {
-      write_out<T, FLAGS, NT>(B, a, r0, c0, a.N, ldq, tid);
+      write_part(B, a.N);
     } else {
-      write_out<T, FLAGS, NT>(A, a, r0, c0, 0, ldq, tid);
-      if constexpr (MODE == MODE_BWD) write_out<T, FLAGS, NT>(B, a, r0, c0, a.N, ldq, tid);
+      write_part(A, 0);
+      if constexpr (MODE == MODE_BWD) write_part(B, a.N);
     }
     if (TPW == 1 || !more) break;
     __syncthreads();  // the stage is read out before it is refilled
@@ -848,9 +858,11 @@ hipError_t launch(const MxArgs& a, hipStream_t s) {
   }
   const int64_t ntiles = tiles_m * tiles_n, per_xcd = (ntiles + 7) / 8;
   const int64_t wg_per_xcd = (per_xcd + TPW - 1) / TPW;
+  const int64_t code_bytes = (((FLAGS & ROWWISE) ? 1 : 0) + ((FLAGS & COLWISE) ? 1 : 0)) *
+                             a.M * (MODE == MODE_BWD ? 2 : 1) * a.N;
   return launch_kernel(k_mxfp8<ACT, LAYOUT, FLAGS, MODE, TPW>, dim3((unsigned)(8 * wg_per_xcd)),
                        dim3(T::NTHREADS), s, a, (uint32_t)tiles_m, (uint32_t)tiles_n, (uint32_t)ntiles,
-                       (uint32_t)per_xcd);
+                       (uint32_t)per_xcd, (uint32_t)nt_stores(code_bytes));
 }
 
 template <int ACT, int LAYOUT, int MODE>
