@@ -833,76 +833,30 @@ __global__ __launch_bounds__((TileOf<FLAGS, MODE>::NTHREADS)) GLU_MX_KATTR void 
   }
 }
 
-// Rowwise-only forward without LDS.  A wave owns one row and 512 columns of it (a unit); lane
-// l holds columns 8l..8l+7, so a 32-column block is the lane quad 4b..4b+3 (amax over two
-// DPP steps), its 32 codes are the 8-byte stores of those 4 lanes, and 16 lanes together
-// store one whole 128-byte line straight from their registers.  One 16-byte load per operand
-// per lane: the simplest streaming shape measured fastest for this byte mix (4 bytes read, 1
-// written per element).  Units run along the rows; each XCD takes a contiguous run of them.
-// The arithmetic is that of the tiled kernel (the same device functions, the same NaN/Inf
-// block rule), so the two produce identical bytes.
-#ifndef GLU_MX_ROW_FWD  // build-time switch, for measurements: 0 sends rowwise forwards to k_mxfp8
+// Rowwise-only launches without LDS (forward, and the backward's [da | db]).  A wave owns one
+// row and 512 columns of it (a unit); lane l holds columns 8l..8l+7, so a 32-column block is
+// the lane quad 4b..4b+3 (amax over two DPP steps), its 32 codes are the 8-byte stores of those
+// 4 lanes, and 16 lanes together store one whole 128-byte line straight from their registers.
+// One 16-byte load per operand per lane: the simplest streaming shape measured fastest for
+// these byte mixes.  Units run along the rows; each XCD takes a contiguous run of them.  The
+// arithmetic is that of the tiled kernel (the same device functions, the same NaN/Inf block
+// rule), so the two produce identical bytes.
+#ifndef GLU_MX_ROW_FWD  // build-time switch, for measurements: 0 sends these launches to k_mxfp8
 #define GLU_MX_ROW_FWD 1
 #endif
+// Measured against the tiled kernel (us, SwiGLU, one box):
+//   forward rowwise   [16384, 7168] 103.6 -> 101.1   [131072, 8192] 893.9 -> 855.5
+//   backward rowwise  [16384, 7168] 157.5 -> 148.2   [65536, 8192]  728.7 -> 691.7
+//                     [4096, 2048]   17.5 -> 16.4    [8192, 8192]    99.7 -> 93.8
 constexpr int RF_WAVES = 4;    // waves per workgroup, one unit each
 constexpr int RF_COLS = 512;   // columns per unit
 
-template <int ACT, int LAYOUT>
-__global__ __launch_bounds__(64 * RF_WAVES) void k_mxfp8_row_fwd(MxArgs a, uint32_t segs, uint32_t units,
-                                                                 uint32_t wg_per_xcd, uint32_t nt,
-                                                                 uint32_t word_scales) {
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t wg = (blockIdx.x & 7u) * wg_per_xcd + (blockIdx.x >> 3);
-  const uint32_t unit = wg * RF_WAVES + w;
-  if (unit >= units) return;  // the whole wave; no barrier follows
-  const uint32_t row = unit / segs, seg = unit - row * segs;
-  const int64_t c0 = (int64_t)seg * RF_COLS;
-  const bool ok = c0 + 8 * (int64_t)lane < a.N;  // N % 32 == 0: a block's 4 lanes agree
-
-  GU<LAYOUT> in;
-  const uint16_t* gate = static_cast<const uint16_t*>(a.src);
-  if constexpr (LAYOUT == SPLIT) {
-    const int64_t base = (int64_t)row * a.ld_in + c0;
-    const uint32_t off = ok ? 16u * lane : kOob;
-    bld16(in.a, rsrc(gate + base), off);
-    bld16(in.b, rsrc(a.up + base), off);
-  } else {
-    const auto r = rsrc(gate + (int64_t)row * a.ld_in + 2 * c0);
-    uint32_t w0[4], w1[4];
-    bld16(w0, r, ok ? 32u * lane : kOob);
-    bld16(w1, r, ok ? 32u * lane + 16u : kOob);
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      in.a[k] = w0[k];
-      in.a[4 + k] = w1[k];
-    }
-  }
-
-  float g[8], u[8], h[8];
-  unpack_gu<LAYOUT>(in, g, u);
-  bool tail = false;
-  if constexpr (tail_from_gate_bits<ACT>()) {
-    uint32_t m = in.a[0];
-#pragma unroll
-    for (int k = 1; k < (LAYOUT == SPLIT ? 4 : 8); k++) m = pkmax(m, in.a[k]);
-    tail = tail_possible<ACT>(LAYOUT == SPLIT ? umax(lo16(m), hi16(m)) : lo16(m));
-  }
-#pragma unroll
-  for (int c = 0; c < 8; c++) {
-    h[c] = glu_fwd_fast<ACT>(g[c], u[c]);
-    if constexpr (!tail_from_gate_bits<ACT>()) tail |= fwd_tail_needed<ACT>(g[c], u[c]);
-  }
-  if (tail) {  // rare: some element may need the FP64 tail path
-#pragma unroll
-    for (int c = 0; c < 8; c++)
-      if (fwd_tail_needed<ACT>(g[c], u[c])) h[c] = glu_fwd_tail<ACT>(g[c], u[c]);
-  }
-  uint32_t H[4];
-#pragma unroll
-  for (int k = 0; k < 4; k++) H[k] = pack_bf16(h[2 * k], h[2 * k + 1]);
-
-  // block amax of BF16 magnitudes over the lane quad, E8M0 scale, E4M3 codes
+// Quantizes the lane's 8 BF16 values H (columns 2k, 2k+1 in word k) of one part and stores
+// its codes at byte 8 lane of rq and the unit's scales at rs: lane 4b holds block b's byte,
+// and lane 16k gathers blocks 4k..4k+3 into one word (aligned, as N % 128 == 0).
+__device__ __forceinline__ void row_quant_store(const uint32_t (&H)[4], __amdgpu_buffer_rsrc_t rq,
+                                                __amdgpu_buffer_rsrc_t rs, uint32_t lane, bool ok,
+                                                uint32_t nt) {
   uint32_t m = pkmax(pkmax(H[0] & 0x7fff7fffu, H[1] & 0x7fff7fffu), pkmax(H[2] & 0x7fff7fffu, H[3] & 0x7fff7fffu));
   m = umax(lo16(m), hi16(m));
   m = umax(m, dpp<DPP_XOR1>(m));
@@ -917,34 +871,117 @@ __global__ __launch_bounds__(64 * RF_WAVES) void k_mxfp8_row_fwd(MxArgs a, uint3
     w0 = w1 = 0x7f7f7f7fu;
     sb = 0xffu;
   }
-
-  const auto rq = rsrc(a.q_row + (int64_t)row * a.N + c0);
   const uint32_t qo = ok ? 8u * lane : kOob;
   if (nt != 0u) __builtin_amdgcn_raw_buffer_store_b64((u32x2){w0, w1}, rq, qo, 0, 2);
   else __builtin_amdgcn_raw_buffer_store_b64((u32x2){w0, w1}, rq, qo, 0, 0);
-  // the unit's 16 scale bytes: lane 4b holds block b's; with N % 128 == 0 lane 16k gathers
-  // blocks 4k..4k+3 into one aligned word, else each quad leader stores its byte
-  const auto rs = rsrc(a.s_row + (int64_t)row * (a.N / 32) + (int64_t)seg * (RF_COLS / 32));
-  if (word_scales != 0u) {
-    const uint32_t s1 = __shfl_down(sb, 4, 16), s2 = __shfl_down(sb, 8, 16), s3 = __shfl_down(sb, 12, 16);
-    const uint32_t word = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
-    __builtin_amdgcn_raw_buffer_store_b32(word, rs, ok && (lane & 15u) == 0u ? lane / 4u : kOob, 0, 0);
+  const uint32_t s1 = __shfl_down(sb, 4, 16), s2 = __shfl_down(sb, 8, 16), s3 = __shfl_down(sb, 12, 16);
+  const uint32_t word = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
+  __builtin_amdgcn_raw_buffer_store_b32(word, rs, ok && (lane & 15u) == 0u ? lane / 4u : kOob, 0, 0);
+}
+
+template <int ACT, int LAYOUT, int MODE>
+__global__ __launch_bounds__(64 * RF_WAVES) void k_mxfp8_row(MxArgs a, uint32_t segs, uint32_t units,
+                                                             uint32_t wg_per_xcd, uint32_t nt) {
+  static_assert(MODE == MODE_FWD || LAYOUT == SPLIT, "the backward takes split operands");
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t wg = (blockIdx.x & 7u) * wg_per_xcd + (blockIdx.x >> 3);
+  const uint32_t unit = wg * RF_WAVES + w;
+  if (unit >= units) return;  // the whole wave; no barrier follows
+  const uint32_t row = unit / segs, seg = unit - row * segs;
+  const int64_t c0 = (int64_t)seg * RF_COLS;
+  const bool ok = c0 + 8 * (int64_t)lane < a.N;  // N % 128 == 0: a scale word's 16 lanes agree
+
+  GU<LAYOUT> in;
+  uint32_t dw[4];
+  const uint16_t* gate = static_cast<const uint16_t*>(a.src);
+  if constexpr (LAYOUT == SPLIT) {
+    const int64_t base = (int64_t)row * a.ld_in + c0;
+    const uint32_t off = ok ? 16u * lane : kOob;
+    bld16(in.a, rsrc(gate + base), off);
+    bld16(in.b, rsrc(a.up + base), off);
+    if constexpr (MODE == MODE_BWD) bld16(dw, rsrc(a.dh + (int64_t)row * a.ld_dh + c0), off);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, rs, ok && (lane & 3u) == 0u ? lane / 4u : kOob, 0, 0);
+    const auto r = rsrc(gate + (int64_t)row * a.ld_in + 2 * c0);
+    uint32_t w0[4], w1[4];
+    bld16(w0, r, ok ? 32u * lane : kOob);
+    bld16(w1, r, ok ? 32u * lane + 16u : kOob);
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      in.a[k] = w0[k];
+      in.a[4 + k] = w1[k];
+    }
+  }
+
+  float g[8], u[8];
+  unpack_gu<LAYOUT>(in, g, u);
+  bool tail = false;
+  if constexpr (tail_from_gate_bits<ACT>()) {
+    uint32_t m = in.a[0];
+#pragma unroll
+    for (int k = 1; k < (LAYOUT == SPLIT ? 4 : 8); k++) m = pkmax(m, in.a[k]);
+    tail = tail_possible<ACT>(LAYOUT == SPLIT ? umax(lo16(m), hi16(m)) : lo16(m));
+  }
+  const int64_t ldq = (MODE == MODE_BWD ? 2 : 1) * a.N;
+  const auto rq = rsrc(a.q_row + (int64_t)row * ldq + c0);
+  const auto rs = rsrc(a.s_row + (int64_t)row * (ldq / 32) + (int64_t)seg * (RF_COLS / 32));
+  if constexpr (MODE == MODE_FWD) {
+    float h[8];
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      h[c] = glu_fwd_fast<ACT>(g[c], u[c]);
+      if constexpr (!tail_from_gate_bits<ACT>()) tail |= fwd_tail_needed<ACT>(g[c], u[c]);
+    }
+    if (tail) {  // rare: some element may need the FP64 tail path
+#pragma unroll
+      for (int c = 0; c < 8; c++)
+        if (fwd_tail_needed<ACT>(g[c], u[c])) h[c] = glu_fwd_tail<ACT>(g[c], u[c]);
+    }
+    uint32_t H[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) H[k] = pack_bf16(h[2 * k], h[2 * k + 1]);
+    row_quant_store(H, rq, rs, lane, ok, nt);
+  } else {
+    float d[8], da[8], db[8];
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      d[c] = (c & 1) ? bf_hi(dw[c >> 1]) : bf_lo(dw[c >> 1]);
+      glu_bwd_fast<ACT>(g[c], u[c], d[c], da[c], db[c]);
+      if constexpr (!tail_from_gate_bits<ACT>()) tail |= bwd_tail_needed<ACT>(g[c], u[c], d[c]);
+    }
+    if (tail) {  // rare: some element may need the FP64 tail path
+#pragma unroll
+      for (int c = 0; c < 8; c++)
+        if (bwd_tail_needed<ACT>(g[c], u[c], d[c])) glu_bwd_tail<ACT>(g[c], u[c], d[c], da[c], db[c]);
+    }
+    uint32_t A[4], B[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      A[k] = pack_bf16(da[2 * k], da[2 * k + 1]);
+      B[k] = pack_bf16(db[2 * k], db[2 * k + 1]);
+    }
+    row_quant_store(A, rq, rs, lane, ok, nt);
+    // db: N columns further along the row; its scales N / 32 bytes further
+    row_quant_store(B, rsrc(a.q_row + (int64_t)row * ldq + a.N + c0),
+                    rsrc(a.s_row + (int64_t)row * (ldq / 32) + a.N / 32 + (int64_t)seg * (RF_COLS / 32)), lane, ok,
+                    nt);
   }
 }
 
-// Launches the rowwise forward above when it applies (row-major scales, units numbered in 32
-// bits); returns false to leave the launch to k_mxfp8.
-template <int ACT, int LAYOUT>
-bool launch_row_fwd(const MxArgs& a, hipStream_t s, hipError_t& err) {
-  if (!GLU_MX_ROW_FWD || a.flags != ROWWISE) return false;
+// Launches the rowwise kernel above when it applies: row-major scales, N % 128 == 0 (whole
+// scale words; at [1000, 4000], whose scales would leave byte by byte, the tiled kernel was
+// faster: 11.7 vs 13.1 us forward), units numbered in 32 bits.  Returns false to leave the
+// launch to k_mxfp8.
+template <int ACT, int LAYOUT, int MODE>
+bool launch_row(const MxArgs& a, hipStream_t s, hipError_t& err) {
+  if (!GLU_MX_ROW_FWD || a.flags != ROWWISE || a.N % 128 != 0) return false;
   const int64_t segs = (a.N + RF_COLS - 1) / RF_COLS, units = a.M * segs;
   if (units >= (int64_t)1 << 31) return false;
   const int64_t wgs = (units + RF_WAVES - 1) / RF_WAVES, wg_per_xcd = (wgs + 7) / 8;
-  err = launch_kernel(k_mxfp8_row_fwd<ACT, LAYOUT>, dim3((unsigned)(8 * wg_per_xcd)), dim3(64 * RF_WAVES), s, a,
-                      (uint32_t)segs, (uint32_t)units, (uint32_t)wg_per_xcd,
-                      (uint32_t)nt_stores(a.M * a.N), (uint32_t)(a.N % 128 == 0));
+  const int64_t parts = MODE == MODE_BWD ? 2 : 1;
+  err = launch_kernel(k_mxfp8_row<ACT, LAYOUT, MODE>, dim3((unsigned)(8 * wg_per_xcd)), dim3(64 * RF_WAVES), s,
+                      a, (uint32_t)segs, (uint32_t)units, (uint32_t)wg_per_xcd,
+                      (uint32_t)nt_stores(parts * a.M * a.N));
   return true;
 }
 
@@ -995,7 +1032,7 @@ hipError_t launch_glu_fwd_mxfp8(const MxArgs& a, hipStream_t s) {
   return with_act(a.act, [&](auto A) {
     constexpr int ACT = decltype(A)::value;
     hipError_t err = hipSuccess;
-    if (a.layout == SPLIT ? launch_row_fwd<ACT, SPLIT>(a, s, err) : launch_row_fwd<ACT, PAIRED>(a, s, err))
+    if (a.layout == SPLIT ? launch_row<ACT, SPLIT, MODE_FWD>(a, s, err) : launch_row<ACT, PAIRED, MODE_FWD>(a, s, err))
       return err;
     return a.layout == SPLIT ? by_flags<ACT, SPLIT, MODE_FWD>(a, s) : by_flags<ACT, PAIRED, MODE_FWD>(a, s);
   });
@@ -1004,6 +1041,8 @@ hipError_t launch_glu_fwd_mxfp8(const MxArgs& a, hipStream_t s) {
 hipError_t launch_glu_bwd_mxfp8(const MxArgs& a, hipStream_t s) {
   return with_act(a.act, [&](auto A) {
     constexpr int ACT = decltype(A)::value;
+    hipError_t err = hipSuccess;
+    if (launch_row<ACT, SPLIT, MODE_BWD>(a, s, err)) return err;
     return by_flags<ACT, SPLIT, MODE_BWD>(a, s);
   });
 }

@@ -114,8 +114,8 @@ def test_fused_fwd_equals_quantized_glu_fwd(gpu, name, kind, layout):
 
 
 @pytest.mark.parametrize("name,kind", ACTS)
-def test_fused_bwd_equals_quantized_glu_bwd(gpu, name, kind):
-    M, N = 96, 160
+@pytest.mark.parametrize("M,N", [(96, 160), (96, 640)])
+def test_fused_bwd_equals_quantized_glu_bwd(gpu, name, kind, M, N):
     gate, up, dh = si.glu_operands(M, N, seed=6, outliers=True, with_dh=True)
     gd, ud, dd = gate.cuda(), up.cuda(), dh.cuda()
     da, db = gpu.glu_bwd(gd, ud, dd, act=name)
@@ -127,6 +127,36 @@ def test_fused_bwd_equals_quantized_glu_bwd(gpu, name, kind):
             assert np.array_equal(u8(qr), o[0]) and np.array_equal(u8(sr), o[1])
         if col:
             assert np.array_equal(u8(qc), o[2]) and np.array_equal(u8(sc), o[3])
+
+
+@pytest.mark.parametrize("layout", ["split", "paired"])
+def test_rowwise_nonfinite_blocks(gpu, layout):
+    """NaN and Inf operands in rowwise-only launches at a width with two 512-column pieces per
+    row (the second one partial): the blocks they reach get scale 0xFF and codes 0x7F, the
+    others quantize as usual; forward and backward against the oracle quantizer of the
+    device's own h, da, db."""
+    M, N = 64, 640
+    gate, up, dh = si.glu_operands(M, N, seed=7, outliers=True, with_dh=True)
+    gate[3, 5] = float("nan")
+    up[10, 600] = float("inf")
+    gate[40, 130] = float("-inf")
+    dh[20, 100] = float("inf")
+    gd, ud, dd = gate.cuda(), up.cuda(), dh.cuda()
+    if layout == "paired":
+        args, lay = (torch.stack([gd, ud], 2).reshape(M, 2 * N).contiguous(), None), "paired"
+    else:
+        args, lay = (gd, ud), "split"
+    h = bits(gpu.glu_fwd(*args, layout=lay))
+    qr, _, sr, _ = gpu.glu_fwd_mxfp8(*args, layout=lay, rowwise=True)
+    o = _q(h, oracle.ROWWISE)
+    assert (u8(sr) == 0xFF).any()
+    assert np.array_equal(u8(qr), o[0]) and np.array_equal(u8(sr), o[1])
+    if layout == "split":
+        da, db = gpu.glu_bwd(gd, ud, dd)
+        qr, _, sr, _ = gpu.glu_bwd_mxfp8(gd, ud, dd, rowwise=True)
+        o = _q(np.concatenate([bits(da), bits(db)], axis=1), oracle.ROWWISE)
+        assert (u8(sr) == 0xFF).any()
+        assert np.array_equal(u8(qr), o[0]) and np.array_equal(u8(sr), o[1])
 
 
 def test_both_equals_row_and_col(gpu):
