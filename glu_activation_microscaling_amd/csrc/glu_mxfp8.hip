@@ -23,6 +23,9 @@
 //   tiles run concurrently to keep HBM busy.
 //   Each XCD takes a contiguous run of a tile order chosen per direction (below), so tiles
 //   that share output lines and scale sectors run on one XCD at about the same time.
+//   Rowwise-only launches with row-major scales and N % 128 == 0 go to a second kernel,
+//   k_mxfp8_row, which needs no LDS: one row per wave, one 16-byte load per operand per lane
+//   (further below).
 #include "glu_device.h"
 #include "glu_launch.h"
 
@@ -67,10 +70,11 @@ struct Tile {
                 "shapes the swizzles and scale words fit");
 };
 
-// Tile per kernel, from interleaved measurements at [16384, 7168].  Rowwise only: a band of
-// 32 rows, 512 columns wide in the forward (102 vs 110 us with 64 x 128; 984 vs 1043 us at
-// [131072, 8192]) and 256 wide in the backward (158 vs 169 us), so each workgroup reads and
-// writes long runs of its rows.  With colwise output, 128 x 128.
+// Tile per kernel, from interleaved measurements at [16384, 7168].  Rowwise only (the launches
+// k_mxfp8_row does not take): a band of 32 rows, 512 columns wide in the forward (102 vs 110 us
+// with 64 x 128; 984 vs 1043 us at [131072, 8192]) and 256 wide in the backward (158 vs 169
+// us), so each workgroup reads and writes long runs of its rows.  With colwise output,
+// 128 x 128.
 #ifndef GLU_MX_ROW_WM  // build-time override of the rowwise-only tile, for measurements
 #define GLU_MX_ROW_WM 1
 #define GLU_MX_ROW_WN(MODE) ((MODE) == 1 ? 4 : 8)
@@ -841,8 +845,8 @@ __global__ __launch_bounds__((TileOf<FLAGS, MODE>::NTHREADS)) GLU_MX_KATTR void 
 // these byte mixes.  Units run along the rows; each XCD takes a contiguous run of them.  The
 // arithmetic is that of the tiled kernel (the same device functions, the same NaN/Inf block
 // rule), so the two produce identical bytes.
-#ifndef GLU_MX_ROW_FWD  // build-time switch, for measurements: 0 sends these launches to k_mxfp8
-#define GLU_MX_ROW_FWD 1
+#ifndef GLU_MX_ROW_KERNEL  // build-time switch, for measurements: 0 sends these launches to k_mxfp8
+#define GLU_MX_ROW_KERNEL 1
 #endif
 // Measured against the tiled kernel (us, SwiGLU, one box):
 //   forward rowwise   [16384, 7168] 103.6 -> 101.1   [131072, 8192] 893.9 -> 855.5
@@ -974,7 +978,7 @@ __global__ __launch_bounds__(64 * RF_WAVES) void k_mxfp8_row(MxArgs a, uint32_t 
 // launch to k_mxfp8.
 template <int ACT, int LAYOUT, int MODE>
 bool launch_row(const MxArgs& a, hipStream_t s, hipError_t& err) {
-  if (!GLU_MX_ROW_FWD || a.flags != ROWWISE || a.N % 128 != 0) return false;
+  if (!GLU_MX_ROW_KERNEL || a.flags != ROWWISE || a.N % 128 != 0) return false;
   const int64_t segs = (a.N + RF_COLS - 1) / RF_COLS, units = a.M * segs;
   if (units >= (int64_t)1 << 31) return false;
   const int64_t wgs = (units + RF_WAVES - 1) / RF_WAVES, wg_per_xcd = (wgs + 7) / 8;
