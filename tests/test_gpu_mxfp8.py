@@ -326,6 +326,26 @@ def test_config_large_swiglu_outliers_sampled(gpu):
         _rule3_rows(np.concatenate([oa, ob], 1), sl, o, f"bwd slab {s}")
 
 
+def test_rowwise_bwd_streaming_stores_sampled(gpu):
+    """Rowwise-only backward whose codes (2 x 16384 x 8192 bytes) exceed 256 MiB, so they
+    leave as non-temporal stores: sampled rows of [da | db] bit-exact against the oracle
+    quantizer of the device's own BF16 gradients, and end to end (rule 3) against the
+    oracle's backward."""
+    M, N = 16384, 8192
+    g, u, d = si.normal_bf16_device([(M, N)] * 3, seed=11, outliers=True)
+    qr, _, sr, _ = gpu.glu_bwd_mxfp8(g, u, d, rowwise=True)
+    da, db = gpu.glu_bwd(g, u, d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = torch.tensor(sorted({0, M - 1, *rng.integers(0, M, 24).tolist()}), device="cuda")
+    o = _q(np.concatenate([bits(da[rows]), bits(db[rows])], axis=1), oracle.ROWWISE)
+    assert np.array_equal(u8(qr[rows]), o[0]) and np.array_equal(u8(sr[rows]), o[1])
+    gb, ub, dbits = bits(g[rows]), bits(u[rows]), bits(d[rows])
+    oe = oracle.glu_bwd_mxfp8(oracle.SWIGLU, gb, ub, dbits, flags=1)
+    x = np.concatenate(oracle.glu_bwd(oracle.SWIGLU, gb, ub, dbits), axis=1)
+    check_rule3_mx(x, u8(qr[rows]), u8(sr[rows]), oe[0], oe[1], "bwd 16384x8192")
+
+
 def test_config_xlarge_swiglu_fwd_rowwise_sampled(gpu):
     M, N = 131072, 8192
     g, u = si.normal_bf16_device([(M, N)] * 2, seed=0, outliers=True)
