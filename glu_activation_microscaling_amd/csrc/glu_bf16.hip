@@ -6,6 +6,8 @@
 // (gate, up and dh loads, h or da/db stores), computes in FP32 and rounds once to BF16.
 // Contiguous operands are processed as a single flat row, so any width (8193 included)
 // runs the vector path everywhere except for the last < 8 elements.
+#include <type_traits>
+
 #include "glu_device.h"
 #include "glu_launch.h"
 
@@ -13,18 +15,31 @@ namespace glu {
 namespace {
 
 constexpr int BF_THREADS = 256;
-constexpr int BF_VEC = 2;                                          // vectors per thread
-constexpr int64_t BF_CHUNK = (int64_t)BF_THREADS * BF_VEC * 8;     // elements per tile
+template <int VEC>  // 16-byte vectors per operand per thread
+constexpr int64_t bf_chunk() { return (int64_t)BF_THREADS * VEC * 8; }  // elements per tile
 
 // Build-time tuning (fixed defaults; alternatives are compiled only to measure them):
-//   GLU_BF16_NT_LOADS / GLU_BF16_NT_STORES: non-temporal (streaming) loads / stores.  Both
-//   on: [8192, 14336] GeGLU forward 122 vs 130 us, backward 193 vs 206 us (6.1 TB/s).
+//   GLU_BF16_NT_LOADS: non-temporal (streaming) loads ([8192, 14336] GeGLU forward 122 vs
+//   130 us, backward 193 vs 206 us, with non-temporal stores).
+//   GLU_BF16_NT_STORES: -1 chooses per launch (below); 0 / 1 non-temporal stores off / on.
 #ifndef GLU_BF16_NT_LOADS
 #define GLU_BF16_NT_LOADS 1
 #endif
 #ifndef GLU_BF16_NT_STORES
-#define GLU_BF16_NT_STORES 1
+#define GLU_BF16_NT_STORES -1
 #endif
+// Per launch, by the bytes it writes against the 256 MiB last-level cache, and by direction
+// (same-box A/B with cold inputs, GeGLU, us):
+//   stores: non-temporal above 256 MiB, ordinary below (the cache absorbs them);
+//   16-byte vectors per operand per thread: one, except two for a backward above 256 MiB.
+//     up to 256 MiB, one vs two:  [1024, 29568] forward 33.9 vs 38.5, backward 50.4 vs 55.7;
+//                                 [8192, 4096] 36.9 vs 40.1 and 57.1 vs 60.2;
+//                                 [8192, 14336] forward 107.9 vs 118.3;
+//     above, one vs two:          forward [8192, 18944] 154.1 vs 160.3, [16384, 14336] 231.1
+//                                 vs 236.7; backward [8192, 14336] 203.6 vs 198.0, [8192,
+//                                 29568] 411.6 vs 403.5.
+//   With two vectors, ordinary and non-temporal stores measured the same below 256 MiB.
+constexpr int64_t kBf16NtStoreBytes = 256ll << 20;
 
 typedef unsigned int bu32x4 __attribute__((ext_vector_type(4)));
 
@@ -38,10 +53,10 @@ __device__ __forceinline__ Uint4 ld16(const uint16_t* p) {
   else v = *reinterpret_cast<const bu32x4*>(p);
   return Uint4{{v.x, v.y, v.z, v.w}};
 }
-__device__ __forceinline__ void st16(uint16_t* p, uint32_t a, uint32_t b, uint32_t c,
+__device__ __forceinline__ void st16(uint32_t nt, uint16_t* p, uint32_t a, uint32_t b, uint32_t c,
                                      uint32_t d) {
   const bu32x4 v = {a, b, c, d};
-  if constexpr (GLU_BF16_NT_STORES) __builtin_nontemporal_store(v, reinterpret_cast<bu32x4*>(p));
+  if (nt != 0u) __builtin_nontemporal_store(v, reinterpret_cast<bu32x4*>(p));
   else *reinterpret_cast<bu32x4*>(p) = v;
 }
 __device__ __forceinline__ float ld_bf(const uint16_t* p) {
@@ -85,13 +100,13 @@ __device__ __forceinline__ void load1(const uint16_t* gate_row, const uint16_t* 
   }
 }
 
-template <int ACT, int LAYOUT>
+template <int ACT, int LAYOUT, int BF_VEC>
 __global__ __launch_bounds__(BF_THREADS) void k_glu_fwd_bf16(BF16Args a, int64_t cols,
                                                              int64_t tiles_per_row,
-                                                             int64_t ntiles) {
+                                                             int64_t ntiles, uint32_t nt) {
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t row = t / tiles_per_row;
-    const int64_t j0 = (t - row * tiles_per_row) * BF_CHUNK;
+    const int64_t j0 = (t - row * tiles_per_row) * bf_chunk<BF_VEC>();
     const uint16_t* grow = a.gate + row * a.ld_in;
     const uint16_t* urow = (LAYOUT == SPLIT) ? a.up + row * a.ld_in : nullptr;
     uint16_t* hrow = a.out0 + row * a.ld_out;
@@ -115,7 +130,7 @@ __global__ __launch_bounds__(BF_THREADS) void k_glu_fwd_bf16(BF16Args a, int64_t
           for (int k = 0; k < 8; k++)
             if (fwd_tail_needed<ACT>(g[v][k], u[v][k])) h[k] = glu_fwd_tail<ACT>(g[v][k], u[v][k]);
         }
-        st16(hrow + j, pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]),
+        st16(nt, hrow + j, pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]),
              pack_bf16(h[6], h[7]));
       } else if (j < cols) {
         for (int64_t jj = j; jj < cols; jj++) {
@@ -131,13 +146,13 @@ __global__ __launch_bounds__(BF_THREADS) void k_glu_fwd_bf16(BF16Args a, int64_t
   }
 }
 
-template <int ACT, int LAYOUT>
+template <int ACT, int LAYOUT, int BF_VEC>
 __global__ __launch_bounds__(BF_THREADS) void k_glu_bwd_bf16(BF16Args a, int64_t cols,
                                                              int64_t tiles_per_row,
-                                                             int64_t ntiles) {
+                                                             int64_t ntiles, uint32_t nt) {
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t row = t / tiles_per_row;
-    const int64_t j0 = (t - row * tiles_per_row) * BF_CHUNK;
+    const int64_t j0 = (t - row * tiles_per_row) * bf_chunk<BF_VEC>();
     const uint16_t* grow = a.gate + row * a.ld_in;
     const uint16_t* urow = (LAYOUT == SPLIT) ? a.up + row * a.ld_in : nullptr;
     const uint16_t* drow = a.dh + row * a.ld_dh;
@@ -173,14 +188,14 @@ __global__ __launch_bounds__(BF_THREADS) void k_glu_bwd_bf16(BF16Args a, int64_t
               glu_bwd_tail<ACT>(g[v][k], u[v][k], d[v][k], da[k], db[k]);
         }
         if constexpr (LAYOUT == SPLIT) {
-          st16(arow + j, pack_bf16(da[0], da[1]), pack_bf16(da[2], da[3]), pack_bf16(da[4], da[5]),
+          st16(nt, arow + j, pack_bf16(da[0], da[1]), pack_bf16(da[2], da[3]), pack_bf16(da[4], da[5]),
                pack_bf16(da[6], da[7]));
-          st16(brow + j, pack_bf16(db[0], db[1]), pack_bf16(db[2], db[3]), pack_bf16(db[4], db[5]),
+          st16(nt, brow + j, pack_bf16(db[0], db[1]), pack_bf16(db[2], db[3]), pack_bf16(db[4], db[5]),
                pack_bf16(db[6], db[7]));
         } else {
-          st16(arow + 2 * j, pack_bf16(da[0], db[0]), pack_bf16(da[1], db[1]), pack_bf16(da[2], db[2]),
+          st16(nt, arow + 2 * j, pack_bf16(da[0], db[0]), pack_bf16(da[1], db[1]), pack_bf16(da[2], db[2]),
                pack_bf16(da[3], db[3]));
-          st16(arow + 2 * j + 8, pack_bf16(da[4], db[4]), pack_bf16(da[5], db[5]),
+          st16(nt, arow + 2 * j + 8, pack_bf16(da[4], db[4]), pack_bf16(da[5], db[5]),
                pack_bf16(da[6], db[6]), pack_bf16(da[7], db[7]));
         }
       } else if (j < cols) {
@@ -208,13 +223,20 @@ template <bool BWD, int ACT, int LAYOUT>
 hipError_t launch(const BF16Args& a, hipStream_t s) {
   const int64_t rows = a.flat ? 1 : a.M;
   const int64_t cols = a.flat ? a.M * a.N : a.N;
-  const int64_t tpr = (cols + BF_CHUNK - 1) / BF_CHUNK;
-  const int64_t ntiles = rows * tpr;
-  const dim3 grid(grid_for(ntiles, (int64_t)1 << 20)), block(BF_THREADS);
-  if constexpr (BWD)
-    return launch_kernel(k_glu_bwd_bf16<ACT, LAYOUT>, grid, block, s, a, cols, tpr, ntiles);
-  else
-    return launch_kernel(k_glu_fwd_bf16<ACT, LAYOUT>, grid, block, s, a, cols, tpr, ntiles);
+  const bool large = (BWD ? 2 : 1) * 2 * a.M * a.N > kBf16NtStoreBytes;
+  const uint32_t nt = GLU_BF16_NT_STORES < 0 ? large : GLU_BF16_NT_STORES == 1;
+  auto go = [&](auto V) {
+    constexpr int VEC = decltype(V)::value;
+    const int64_t tpr = (cols + bf_chunk<VEC>() - 1) / bf_chunk<VEC>();
+    const int64_t ntiles = rows * tpr;
+    const dim3 grid(grid_for(ntiles, (int64_t)1 << 20)), block(BF_THREADS);
+    if constexpr (BWD)
+      return launch_kernel(k_glu_bwd_bf16<ACT, LAYOUT, VEC>, grid, block, s, a, cols, tpr, ntiles, nt);
+    else
+      return launch_kernel(k_glu_fwd_bf16<ACT, LAYOUT, VEC>, grid, block, s, a, cols, tpr, ntiles, nt);
+  };
+  if (BWD && large) return go(std::integral_constant<int, 2>{});
+  return go(std::integral_constant<int, 1>{});
 }
 
 template <bool BWD>
