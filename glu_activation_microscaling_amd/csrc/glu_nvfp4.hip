@@ -38,8 +38,8 @@ constexpr int64_t NV_TILE = 2048;  // operand columns per workgroup and group
 #ifndef GLU_AMAX_WGS
 #define GLU_AMAX_WGS 1024
 #endif
-#ifndef GLU_NV_NT_LOADS
-#define GLU_NV_NT_LOADS 0
+#ifndef GLU_NV_NT_LOADS  // -1: per direction (below)
+#define GLU_NV_NT_LOADS -1
 #endif
 #ifndef GLU_NV_NT_STORES
 #define GLU_NV_NT_STORES 0
@@ -51,8 +51,14 @@ enum { NV_FWD = 0, NV_BWD = 1, NV_F32 = 2, NV_FWD_GS = 3 };
 struct Words4 {
   uint32_t w[4];
 };
+// Non-temporal operand loads for the backward only: same-box A/B with cold inputs, SwiGLU
+// backward [16384, 7168] 156.5 vs 166.2 us; GeGLU forward 122.8 vs 110.6 us there and 19.6 vs
+// 19.0 us at [968, 16384] (slower).
+template <bool BWD>
+constexpr bool nv_nt_loads() { return GLU_NV_NT_LOADS < 0 ? BWD : GLU_NV_NT_LOADS == 1; }
+template <bool NT>
 __device__ __forceinline__ Words4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, GLU_NV_NT_LOADS ? 2 : 0);
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0);
   return Words4{{x.x, x.y, x.z, x.w}};
 }
 
@@ -86,13 +92,13 @@ __device__ __forceinline__ Raw8 load_raw(const RowIn& r, uint32_t j, bool live) 
   Raw8 x;
   if constexpr (MODE == NV_F32 || LAYOUT == PAIRED) {  // 32 contiguous bytes per lane
     const uint32_t off = live ? 4u * j : kOob;
-    x.A = bld16(r.a, off);
-    x.B = bld16(r.a, live ? off + 16u : kOob);
+    x.A = bld16<nv_nt_loads<MODE == NV_BWD>()>(r.a, off);
+    x.B = bld16<nv_nt_loads<MODE == NV_BWD>()>(r.a, live ? off + 16u : kOob);
   } else {
     const uint32_t off = live ? 2u * j : kOob;
-    x.A = bld16(r.a, off);
-    x.B = bld16(r.b, off);
-    if constexpr (MODE == NV_BWD) x.C = bld16(r.d, off);
+    x.A = bld16<nv_nt_loads<MODE == NV_BWD>()>(r.a, off);
+    x.B = bld16<nv_nt_loads<MODE == NV_BWD>()>(r.b, off);
+    if constexpr (MODE == NV_BWD) x.C = bld16<nv_nt_loads<MODE == NV_BWD>()>(r.d, off);
   }
   return x;
 }
