@@ -21,8 +21,11 @@
 //   data would leave as 32-byte (colwise) and 64-byte (rowwise) pieces and single scale
 //   bytes: several times more L2 write requests, which measured as the limit once enough
 //   tiles run concurrently to keep HBM busy.
-//   Each XCD takes a contiguous run of a tile order chosen per direction (below), so tiles
-//   that share output lines and scale sectors run on one XCD at about the same time.
+//   Straight from the registers, 32- and 64-byte pieces also measured 20-60% slower than
+//   whole lines in a skeleton with the same loads and no arithmetic.
+//   Tiles follow an order chosen per direction (below); a launch that writes scale words of
+//   both directions gives each XCD a contiguous run of it, so tiles that share scale sectors
+//   run on one XCD at about the same time.
 //   Rowwise-only launches with row-major scales and N % 128 == 0 go to a second kernel,
 //   k_mxfp8_row, which needs no LDS: one row per wave, one 16-byte load per operand per lane
 //   (further below).
@@ -31,27 +34,6 @@
 
 namespace glu {
 namespace {
-
-// Build-time tuning (fixed defaults; alternatives are compiled only to measure them):
-//   GLU_MX_NT_LOADS: non-temporal (streaming) operand loads.
-//   GLU_MX_NT_STORES: -1 by the size of the codes written (below); 0 / 1 non-temporal
-//   code stores off / on.
-#ifndef GLU_MX_NT_LOADS
-#define GLU_MX_NT_LOADS 1
-#endif
-#ifndef GLU_MX_NT_STORES
-#define GLU_MX_NT_STORES -1
-#endif
-//   GLU_MX_TILE_ORDER: -1 per direction (below), else the order 0, 1 or 2 for every kernel.
-#ifndef GLU_MX_TILE_ORDER
-#define GLU_MX_TILE_ORDER -1
-#endif
-//   GLU_MX_TPW: if set, the tiles per workgroup of every kernel (else per kernel, below).
-//   GLU_MX_PIPE: 0 stages everything, then writes everything out; 1 (the backward) writes da
-//   out while staging db.
-#ifndef GLU_MX_PIPE
-#define GLU_MX_PIPE 1
-#endif
 
 enum { MODE_FWD = 0, MODE_BWD = 1, MODE_F32 = 2 };
 
@@ -74,35 +56,43 @@ struct Tile {
 // k_mxfp8_row does not take): a band of 32 rows, 512 columns wide in the forward (102 vs 110 us
 // with 64 x 128; 984 vs 1043 us at [131072, 8192]) and 256 wide in the backward (158 vs 169
 // us), so each workgroup reads and writes long runs of its rows.  With colwise output,
-// 128 x 128.
-#ifndef GLU_MX_ROW_WM  // build-time override of the rowwise-only tile, for measurements
-#define GLU_MX_ROW_WM 1
-#define GLU_MX_ROW_WN(MODE) ((MODE) == 1 ? 4 : 8)
-#else
-#define GLU_MX_ROW_WN(MODE) GLU_MX_ROW_WN_
-#endif
-#ifndef GLU_MX_COL_WN  // build-time override of the colwise tiles' width, for measurements
-#define GLU_MX_COL_WN 2
-#endif
+// 128 x 128 (128 x 64 and 128 x 256 were slower).
 template <int FLAGS, int MODE>
-using TileOf = Tile<FLAGS == ROWWISE ? GLU_MX_ROW_WM : 4,
-                    FLAGS == ROWWISE ? GLU_MX_ROW_WN(MODE) : GLU_MX_COL_WN>;
+using TileOf = Tile<FLAGS == ROWWISE ? 1 : 4, FLAGS == ROWWISE ? (MODE == MODE_BWD ? 4 : 8) : 2>;
 
-// Non-temporal code stores, chosen per launch from the size of the codes written.  Ordinary
-// stores are absorbed by the 256 MB last-level cache and drain after the kernel when the codes
-// fit there; when they do not, non-temporal stores are faster.  Measured (MXFP8 SwiGLU):
-//   [16384, 7168]  forward rowwise (117 MB)   101.5 vs 106.9 us  (ordinary faster)
-//                  forward both (235 MB)      125.9 vs 136.5 us  (ordinary faster)
-//                  backward rowwise (235 MB)  157.8 vs 163.2 us  (ordinary faster)
-//                  backward both (470 MB)     234 vs 267 us      (non-temporal faster)
-//   [131072, 8192] forward rowwise (1.07 GB)  896.4 vs 982.5 us  (non-temporal faster)
-//                  forward both (2.1 GB)      1211 vs 1368 us    (non-temporal faster)
+// Where a launch's code stores go, and how its workgroups map to tiles; both are uniform
+// kernel arguments chosen per launch from measurements (SwiGLU, cold inputs, us).
+//   Non-temporal code stores.  Ordinary stores are absorbed by the 256 MB last-level cache
+//   and drain after the kernel while the codes fit there:
+//     tiled kernel, [16384, 7168]: forward both (235 MB) 126.2 ordinary vs 137.0
+//     non-temporal, backward both (470 MB) 234 vs 267 the other way, backward rowwise
+//     (235 MB, k_mxfp8_row) 146.7 vs 152.4, [131072, 8192] forward both (2.1 GB) 1368 vs 1211;
+//   so the size decides, at 256 MiB.  Two launches stream their codes whatever the size:
+//     forward rowwise (k_mxfp8_row): [16384, 7168] 95.7 non-temporal vs 101.8 ordinary,
+//     [131072, 8192] 843.6 vs 857.2;
+//     forward colwise only: [16384, 7168] 105.1 vs 107.0.
+//   Tile mapping.  Workgroups are dealt to the XCDs round-robin by id.  Consecutive ids on
+//   consecutive positions of the tile order keep the whole chip on one region of the
+//   operands, as a streaming copy does, which is faster for pure streams; a contiguous run of
+//   the order per XCD instead keeps the tiles that share scale words on one L2, which the
+//   launches writing rowwise and colwise scale words together need:
+//     forward colwise only, [16384, 7168]: 105.1 round-robin vs 109.8 per-XCD runs;
+//     forward both: 127.7 per-XCD runs vs 134.0; backward both 229.2 vs 234.6.
 constexpr int64_t kNtStoreBytes = 256ll << 20;
-bool nt_stores(int64_t code_bytes) {
-  return GLU_MX_NT_STORES < 0 ? code_bytes > kNtStoreBytes : GLU_MX_NT_STORES == 1;
+struct LaunchPolicy {
+  uint32_t nt;        // non-temporal code stores
+  uint32_t xcd_runs;  // each XCD takes a contiguous run of the tile (unit) order
+};
+// row_kernel: the launch goes to k_mxfp8_row (rowwise only, further below).
+LaunchPolicy launch_policy(int flags, int mode, int64_t code_bytes, bool row_kernel) {
+  const bool streamed = mode == MODE_FWD && (row_kernel || (flags & (ROWWISE | COLWISE)) == COLWISE);
+  LaunchPolicy p;
+  p.nt = streamed || code_bytes > kNtStoreBytes;
+  p.xcd_runs = !streamed;
+  return p;
 }
 
-// Order of the tiles; each XCD takes a contiguous run of it.
+// Order of the tiles:
 //   0 (colwise only): along M first, so consecutive tiles continue the same rows of the
 //     transposed [N, M] output and fill its scale rows word after word.
 //   1 (rowwise only): along N first, so consecutive tiles continue the same input and output
@@ -113,22 +103,11 @@ bool nt_stores(int64_t code_bytes) {
 //     concurrent tiles, so both scale streams leave L2 as whole sectors (orders 0 and 1 leave
 //     one of them as single words: 6% slower at [16384, 7168]; blocks of 4 x 4 or 16 x 16
 //     128 x 128 tiles were 8% and 2% slower than 8 x 8).
-// Tiles per workgroup: with more than one, the next tile's loads overlap the current tile's
-// write-out.  One is fastest: the prefetch buffer costs more in occupancy than it gains
-// (backward both 248 vs 234 us at [16384, 7168] with two).
-template <int MODE>
-constexpr int tiles_per_workgroup() {
-#ifdef GLU_MX_TPW
-  return GLU_MX_TPW;
-#else
-  return 1;
-#endif
-}
-
+// One tile per workgroup: a workgroup that prefetched its next tile during the write-out was
+// slower (forward both 179 vs 128 us, backward both 288 vs 227 us at [16384, 7168]).
 template <int FLAGS>
 constexpr int tile_order() {
-  return GLU_MX_TILE_ORDER >= 0 ? GLU_MX_TILE_ORDER
-                                : FLAGS == ROWWISE ? 1 : FLAGS == COLWISE ? 0 : 2;
+  return FLAGS == ROWWISE ? 1 : FLAGS == COLWISE ? 0 : 2;
 }
 
 template <class T, int ORDER>
@@ -194,7 +173,7 @@ __device__ __forceinline__ void unpack_gu(const GU<LAYOUT>& r, float g[8], float
 // limited (by the host checks) so that 32 rows of offsets stay below kOob.
 
 __device__ __forceinline__ void bld16(uint32_t (&w)[4], __amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, GLU_MX_NT_LOADS ? 2 : 0);
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);  // non-temporal
   w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
 }
 
@@ -744,96 +723,59 @@ __device__ __forceinline__ TileGeom wave_geom(const MxArgs& a, int64_t r0, int64
   return g;
 }
 
-// A workgroup takes `TPW` consecutive tiles of the tile order.  Workgroup id b runs on XCD
-// b % 8 (workgroups are dealt to the XCDs round-robin); XCD x owns positions
-// [x * per_xcd, (x + 1) * per_xcd) of the order, and workgroup b the TPW positions from
-// x * per_xcd + (b / 8) * TPW.  While a tile is staged and written out, the loads of the next
-// one are already in flight.  The loop is entered with the first tile computed, so the wait
-// for a prefetched tile follows the write-out on every path; the write-out's stores are
-// unconditional (out-of-range ones are dropped by the buffer range check), so that wait
-// counts them and does not drain them.
-#ifdef GLU_MX_WPE  // build-time override, for measurements
-#define GLU_MX_KATTR __attribute__((amdgpu_waves_per_eu(GLU_MX_WPE, 8)))
-#else
-#define GLU_MX_KATTR
-#endif
-template <int ACT, int LAYOUT, int FLAGS, int MODE, int TPW>
-__global__ __launch_bounds__((TileOf<FLAGS, MODE>::NTHREADS)) GLU_MX_KATTR void k_mxfp8(
-    MxArgs a, uint32_t tiles_m, uint32_t tiles_n, uint32_t ntiles, uint32_t per_xcd, uint32_t nt) {
+// A workgroup owns one tile of the tile order.  Workgroup id b runs on XCD b % 8 (workgroups
+// are dealt to the XCDs round-robin).  With xcd_runs, XCD x owns positions
+// [x * per_xcd, (x + 1) * per_xcd) of the order and workgroup b takes x * per_xcd + b / 8;
+// otherwise workgroup b takes position b.
+template <int ACT, int LAYOUT, int FLAGS, int MODE>
+__global__ __launch_bounds__((TileOf<FLAGS, MODE>::NTHREADS)) void k_mxfp8(
+    MxArgs a, uint32_t tiles_m, uint32_t tiles_n, uint32_t ntiles, uint32_t per_xcd, LaunchPolicy pol) {
   using T = TileOf<FLAGS, MODE>;
   using St = Stage<T, FLAGS>;
   constexpr int TM = T::TM, TN = T::TN;
   constexpr int PARTS = MODE == MODE_BWD ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint8_t lds[PARTS * St::BYTES];
-  const uint32_t xcd = blockIdx.x & 7;
-  const uint32_t beg = xcd * per_xcd + (blockIdx.x >> 3) * TPW;
-  const uint32_t end = xcd * per_xcd + per_xcd < ntiles ? xcd * per_xcd + per_xcd : ntiles;
-  if (beg >= end) return;  // the whole workgroup
-  const uint32_t count = end - beg < (uint32_t)TPW ? end - beg : (uint32_t)TPW;
+  uint32_t t = blockIdx.x;
+  if (pol.xcd_runs != 0u) {
+    const uint32_t xcd = blockIdx.x & 7;
+    t = xcd * per_xcd + (blockIdx.x >> 3);
+    if (t >= xcd * per_xcd + per_xcd) return;  // the whole workgroup
+  }
+  if (t >= ntiles) return;  // the whole workgroup
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int wm = w % T::WM, wn = w / T::WM;
   const int lr = lane & 7, lc = lane >> 3;
   const int row0 = 32 * wm + 4 * lr, col = 64 * wn + 8 * lc;
   const int64_t ldq = PARTS * a.N;
-  constexpr int ORDER = tile_order<FLAGS>();
-  constexpr int PIPE = GLU_MX_PIPE;
 
   uint32_t tm, tn;
-  tile_of<T, ORDER>(beg, tiles_m, tiles_n, tm, tn);
-  int64_t r0 = (int64_t)tm * TM, c0 = (int64_t)tn * TN;
-  // one store form per launch (nt is uniform): both are instantiated, a scalar branch picks
+  tile_of<T, tile_order<FLAGS>()>(t, tiles_m, tiles_n, tm, tn);
+  const int64_t r0 = (int64_t)tm * TM, c0 = (int64_t)tn * TN;
+  // one store form per launch (pol.nt is uniform): both are instantiated, a scalar branch picks
   auto write_part = [&](const St& S, int64_t coloff) {
-    if (nt != 0u) write_out<T, FLAGS, true>(S, a, r0, c0, coloff, ldq, tid);
+    if (pol.nt != 0u) write_out<T, FLAGS, true>(S, a, r0, c0, coloff, ldq, tid);
     else write_out<T, FLAGS, false>(S, a, r0, c0, coloff, ldq, tid);
   };
   TileOps<LAYOUT, MODE> o;
   load_ops<LAYOUT, MODE>(o, a, wave_geom(a, r0, c0, wm, wn, lc), lr, lc);
   TileVals<MODE> R;
   compute<ACT, LAYOUT, MODE>(R, o);
-  for (uint32_t k = 1;; k++) {
-    // The backward stages da, and writes it out while db is staged (PIPE 1: 227 vs 234 us
-    // at [16384, 7168]; splitting the rowwise and colwise pieces too gained nothing).
-    const St A(lds), B(lds + St::BYTES);
-    if constexpr (MODE == MODE_F32) {
-      stage_f32<T, FLAGS>(R.v, A, row0, col, lr, lc);
-    } else if constexpr (PIPE == 1 && MODE == MODE_BWD) {
-      stage_bf16<T, FLAGS>(R.h[0], A, row0, col, lr, lc);
-      __syncthreads();
-      write_part(A, 0);
-      stage_bf16<T, FLAGS>(R.h[1], B, row0, col, lr, lc);
-    } else {
-      stage_bf16<T, FLAGS>(R.h[0], A, row0, col, lr, lc);
-      if constexpr (MODE == MODE_BWD) stage_bf16<T, FLAGS>(R.h[1], B, row0, col, lr, lc);
-    }
-    const bool more = k < count;
-    int64_t r1 = 0, c1 = 0;
-    if constexpr (TPW > 1) {
-      // prefetch the next tile (past the last one, a tile outside the matrix) once this
-      // tile's results are staged, so the operand registers overlap only the write-out
-      TileGeom gn;
-      if (more) {
-        tile_of<T, ORDER>(beg + k, tiles_m, tiles_n, tm, tn);
-        r1 = (int64_t)tm * TM;
-        c1 = (int64_t)tn * TN;
-        gn = wave_geom(a, r1, c1, wm, wn, lc);
-      } else {
-        gn = TileGeom{a.M, 0, 0, false};
-      }
-      load_ops<LAYOUT, MODE>(o, a, gn, lr, lc);
-    }
+  const St A(lds), B(lds + St::BYTES);
+  if constexpr (MODE == MODE_BWD) {
+    // da is staged and written out while db is staged (227 vs 234 us at [16384, 7168] against
+    // staging both first; splitting the rowwise and colwise pieces too gained nothing)
+    stage_bf16<T, FLAGS>(R.h[0], A, row0, col, lr, lc);
     __syncthreads();
-    if constexpr (PIPE == 1 && MODE == MODE_BWD) {
-      write_part(B, a.N);
-    } else {
-      write_part(A, 0);
-      if constexpr (MODE == MODE_BWD) write_part(B, a.N);
-    }
-    if (TPW == 1 || !more) break;
-    __syncthreads();  // the stage is read out before it is refilled
-    compute<ACT, LAYOUT, MODE>(R, o);
-    r0 = r1;
-    c0 = c1;
+    write_part(A, 0);
+    stage_bf16<T, FLAGS>(R.h[1], B, row0, col, lr, lc);
+    __syncthreads();
+    write_part(B, a.N);
+  } else {
+    if constexpr (MODE == MODE_F32) stage_f32<T, FLAGS>(R.v, A, row0, col, lr, lc);
+    else stage_bf16<T, FLAGS>(R.h[0], A, row0, col, lr, lc);
+    __syncthreads();
+    write_part(A, 0);
   }
 }
 
@@ -842,12 +784,10 @@ __global__ __launch_bounds__((TileOf<FLAGS, MODE>::NTHREADS)) GLU_MX_KATTR void 
 // the lane quad 4b..4b+3 (amax over two DPP steps), its 32 codes are the 8-byte stores of those
 // 4 lanes, and 16 lanes together store one whole 128-byte line straight from their registers.
 // One 16-byte load per operand per lane: the simplest streaming shape measured fastest for
-// these byte mixes.  Units run along the rows; each XCD takes a contiguous run of them.  The
-// arithmetic is that of the tiled kernel (the same device functions, the same NaN/Inf block
-// rule), so the two produce identical bytes.
-#ifndef GLU_MX_ROW_KERNEL  // build-time switch, for measurements: 0 sends these launches to k_mxfp8
-#define GLU_MX_ROW_KERNEL 1
-#endif
+// these byte mixes.  Units run along the rows, mapped to workgroups as the launch policy says
+// (round-robin over the XCDs in the forward, per-XCD runs in the backward).  The arithmetic is
+// that of the tiled kernel (the same device functions, the same NaN/Inf block rule), so the
+// two produce identical bytes.
 // Measured against the tiled kernel (us, SwiGLU, one box):
 //   forward rowwise   [16384, 7168] 103.6 -> 101.1   [131072, 8192] 893.9 -> 855.5
 //   backward rowwise  [16384, 7168] 157.5 -> 148.2   [65536, 8192]  728.7 -> 691.7
@@ -885,11 +825,11 @@ __device__ __forceinline__ void row_quant_store(const uint32_t (&H)[4], __amdgpu
 
 template <int ACT, int LAYOUT, int MODE>
 __global__ __launch_bounds__(64 * RF_WAVES) void k_mxfp8_row(MxArgs a, uint32_t segs, uint32_t units,
-                                                             uint32_t wg_per_xcd, uint32_t nt) {
+                                                             uint32_t wg_per_xcd, LaunchPolicy pol) {
   static_assert(MODE == MODE_FWD || LAYOUT == SPLIT, "the backward takes split operands");
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t wg = (blockIdx.x & 7u) * wg_per_xcd + (blockIdx.x >> 3);
+  const uint32_t wg = pol.xcd_runs != 0u ? (blockIdx.x & 7u) * wg_per_xcd + (blockIdx.x >> 3) : blockIdx.x;
   const uint32_t unit = wg * RF_WAVES + w;
   if (unit >= units) return;  // the whole wave; no barrier follows
   const uint32_t row = unit / segs, seg = unit - row * segs;
@@ -944,7 +884,7 @@ __global__ __launch_bounds__(64 * RF_WAVES) void k_mxfp8_row(MxArgs a, uint32_t 
     uint32_t H[4];
 #pragma unroll
     for (int k = 0; k < 4; k++) H[k] = pack_bf16(h[2 * k], h[2 * k + 1]);
-    row_quant_store(H, rq, rs, lane, ok, nt);
+    row_quant_store(H, rq, rs, lane, ok, pol.nt);
   } else {
     float d[8], da[8], db[8];
 #pragma unroll
@@ -964,11 +904,11 @@ __global__ __launch_bounds__(64 * RF_WAVES) void k_mxfp8_row(MxArgs a, uint32_t 
       A[k] = pack_bf16(da[2 * k], da[2 * k + 1]);
       B[k] = pack_bf16(db[2 * k], db[2 * k + 1]);
     }
-    row_quant_store(A, rq, rs, lane, ok, nt);
+    row_quant_store(A, rq, rs, lane, ok, pol.nt);
     // db: N columns further along the row; its scales N / 32 bytes further
     row_quant_store(B, rsrc(a.q_row + (int64_t)row * ldq + a.N + c0),
                     rsrc(a.s_row + (int64_t)row * (ldq / 32) + a.N / 32 + (int64_t)seg * (RF_COLS / 32)), lane, ok,
-                    nt);
+                    pol.nt);
   }
 }
 
@@ -978,20 +918,19 @@ __global__ __launch_bounds__(64 * RF_WAVES) void k_mxfp8_row(MxArgs a, uint32_t 
 // launch to k_mxfp8.
 template <int ACT, int LAYOUT, int MODE>
 bool launch_row(const MxArgs& a, hipStream_t s, hipError_t& err) {
-  if (!GLU_MX_ROW_KERNEL || a.flags != ROWWISE || a.N % 128 != 0) return false;
+  if (a.flags != ROWWISE || a.N % 128 != 0) return false;
   const int64_t segs = (a.N + RF_COLS - 1) / RF_COLS, units = a.M * segs;
   if (units >= (int64_t)1 << 31) return false;
   const int64_t wgs = (units + RF_WAVES - 1) / RF_WAVES, wg_per_xcd = (wgs + 7) / 8;
   const int64_t parts = MODE == MODE_BWD ? 2 : 1;
   err = launch_kernel(k_mxfp8_row<ACT, LAYOUT, MODE>, dim3((unsigned)(8 * wg_per_xcd)), dim3(64 * RF_WAVES), s,
                       a, (uint32_t)segs, (uint32_t)units, (uint32_t)wg_per_xcd,
-                      (uint32_t)nt_stores(parts * a.M * a.N));
+                      launch_policy(a.flags, MODE, parts * a.M * a.N, true));
   return true;
 }
 
 template <int ACT, int LAYOUT, int FLAGS, int MODE>
 hipError_t launch(const MxArgs& a, hipStream_t s) {
-  constexpr int TPW = tiles_per_workgroup<MODE>();
   using T = TileOf<FLAGS, MODE>;
   int64_t tiles_m = (a.M + T::TM - 1) / T::TM, tiles_n = (a.N + T::TN - 1) / T::TN;
   if (a.flags & SF_SWIZZLED) {
@@ -1013,12 +952,14 @@ hipError_t launch(const MxArgs& a, hipStream_t s) {
     }
   }
   const int64_t ntiles = tiles_m * tiles_n, per_xcd = (ntiles + 7) / 8;
-  const int64_t wg_per_xcd = (per_xcd + TPW - 1) / TPW;
   const int64_t code_bytes = (((FLAGS & ROWWISE) ? 1 : 0) + ((FLAGS & COLWISE) ? 1 : 0)) *
                              a.M * (MODE == MODE_BWD ? 2 : 1) * a.N;
-  return launch_kernel(k_mxfp8<ACT, LAYOUT, FLAGS, MODE, TPW>, dim3((unsigned)(8 * wg_per_xcd)),
-                       dim3(T::NTHREADS), s, a, (uint32_t)tiles_m, (uint32_t)tiles_n, (uint32_t)ntiles,
-                       (uint32_t)per_xcd, (uint32_t)nt_stores(code_bytes));
+  const LaunchPolicy pol = launch_policy(FLAGS, MODE, code_bytes, false);
+  // per-XCD runs need 8 * per_xcd workgroups (the last XCD's run may be short); round-robin
+  // needs one per tile
+  const int64_t grid = pol.xcd_runs != 0u ? 8 * per_xcd : ntiles;
+  return launch_kernel(k_mxfp8<ACT, LAYOUT, FLAGS, MODE>, dim3((unsigned)grid), dim3(T::NTHREADS), s, a,
+                       (uint32_t)tiles_m, (uint32_t)tiles_n, (uint32_t)ntiles, (uint32_t)per_xcd, pol);
 }
 
 template <int ACT, int LAYOUT, int MODE>

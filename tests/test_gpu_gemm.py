@@ -178,16 +178,54 @@ def test_gemm_zero_rows(gpu):
     torch.cuda.synchronize()
 
 
-def test_gemm_end_to_end_against_the_exact_oracle(gpu):
-    """Against the oracle's exact h (binary64 GEMM, one rounding), the FP32 matrix-core sums
-    leave most h identical and the rest within the accumulation bound (carried through the
-    activation's slope)."""
-    M, N, K = 128, 128, 1024
-    ops = _operands(M, N, K, seed=81)
-    h = bits(gpu.glu_gemm(*(t.cuda() for t in ops), act="swiglu"))
-    ho = oracle.glu_gemm(oracle.SWIGLU, *(t.numpy() for t in ops))
+# Largest |act'(x)| over the reals for the three smooth activations (SiLU: 1.0998 at x = 2.40;
+# both GELUs: 1.1289 at x = 1.42 for the exact one, 1.1290 for the tanh form), rounded up.
+_SLOPE = {oracle.SWIGLU: 1.10, oracle.GEGLU_TANH: 1.13, oracle.GEGLU_ERF: 1.13}
+
+
+def _carried_bound(kind, y_gate, y_up, b_gate, b_up):
+    """Elementwise bound on |act(Yg') Yu' - act(Yg) Yu| when |Yg' - Yg| <= b_gate and
+    |Yu' - Yu| <= b_up:  L b_gate (|Yu| + b_up) + |act(Yg)| b_up, with L the largest |act'| on
+    [Yg - b_gate, Yg + b_gate] (a global constant for the smooth activations; 2 (|Yg| + b_gate)
+    for ReLU^2, whose derivative is 2 max(x, 0))."""
+    L = 2.0 * (np.abs(y_gate) + b_gate) if kind == oracle.RELU2 else _SLOPE[kind]
+    return L * b_gate * (np.abs(y_up) + b_up) + np.abs(oracle.act(kind, y_gate)) * b_up
+
+
+@pytest.mark.parametrize("act,kind", ACTS)
+@pytest.mark.parametrize("K", [128, 1024, 2048])
+def test_gemm_end_to_end_against_the_exact_oracle(gpu, act, kind, K):
+    """The fused h against the oracle's exact h (binary64 GEMM, one rounding), element by
+    element.  With Y' the device's FP32 GEMM and Y the exact one, |Y' - Y| <= B (the
+    accumulation bound above), carried through the GLU as D (_carried_bound).  The device h is
+    within one BF16 ulp (rule 2) of bf16(act(Yg') Yu'), i.e. within 1.5 ulp of act(Yg') Yu';
+    the oracle's h is within half an ulp of act(Yg) Yu.  So
+        |h_device - h_oracle| <= D + 2 ulp(max(|h_device|, |h_oracle|)),
+    asserted for every element; most elements are also identical."""
+    M, N = 128, 128
+    ops = _operands(M, N, K, seed=81 + K + kind)
+    h = bits(gpu.glu_gemm(*(t.cuda() for t in ops), act=act))
+    ops_np = [t.numpy() for t in ops]
+    ho = oracle.glu_gemm(kind, *ops_np)
+    y = oracle.mx_gemm_nt(*ops_np)
+    B = _accumulation_bound(*ops_np)
+    D = _carried_bound(kind, y[:, :N], y[:, N:], B[:, :N], B[:, N:])
+    hd, hv = _bf16_value(h), _bf16_value(ho)
+    ulp = _bf16_spacing(np.maximum(np.abs(hd), np.abs(hv)))
+    err = np.abs(hd - hv)
+    assert np.all(err <= D + 2 * ulp), f"worst {float(((err - 2 * ulp) / np.maximum(D, 1e-300)).max()):.3g} of the bound"
     same = float((h == ho).mean())
     assert same > 0.5, f"only {same:.3f} of h identical to the exact oracle"
+
+
+def _bf16_value(b):
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _bf16_spacing(a):
+    """Spacing of BF16 numbers at magnitude a (2^-133 below the normal range)."""
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.exp2(e - 7)
 
 
 @pytest.mark.parametrize("act,kind", [ACTS[0], ACTS[2]])

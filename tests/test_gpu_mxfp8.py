@@ -14,7 +14,8 @@ import torch
 import oracle
 import synthetic_inputs as si
 from conftest import bits, u8
-from parity import check_rule3_mx
+from parity import check_rule2, check_rule3_mx, rule3_mx
+from sweep_inputs import mxfp8_sweep_matrix
 
 pytestmark = pytest.mark.gpu
 FLAGS = [(True, False), (False, True), (True, True)]
@@ -300,30 +301,63 @@ def test_other_activations_fwd_bwd_both(gpu, name, kind):
                 oracle.glu_bwd_mxfp8(kind, gb, ub, db_, flags=3), f"{name} bwd")
 
 
-def _slabs(M, n, seed):
-    rng = np.random.default_rng(seed)
-    return sorted({0, M // 32 - 1, *rng.integers(0, M // 32, n).tolist()})
+def _full_rule3_mx(gb, ub, db_, out, flags, what, chunk=1024):
+    """Rule 3 over every output of a fused launch, against the oracle run on row chunks of the
+    same inputs (db_ None: forward).  out = (q_row, q_col, s_row, s_col) as host arrays, the
+    disabled direction's empty.  Chunks are checked in a small thread pool (the oracle runs
+    OpenMP inside each call, numpy releases the interpreter lock)."""
+    import concurrent.futures as cf
+    M = gb.shape[0]
+    qr, qc, sr, sc = out
+
+    def one(r0):
+        r = slice(r0, r0 + chunk)
+        acc_r, acc_c = rule3_mx(what + " rowwise"), rule3_mx(what + " colwise")
+        if db_ is None:
+            o = oracle.glu_fwd_mxfp8(oracle.SWIGLU, gb[r], ub[r], flags=flags)
+            h = oracle.glu_fwd(oracle.SWIGLU, gb[r], ub[r])
+        else:
+            o = oracle.glu_bwd_mxfp8(oracle.SWIGLU, gb[r], ub[r], db_[r], flags=flags)
+            h = np.concatenate(oracle.glu_bwd(oracle.SWIGLU, gb[r], ub[r], db_[r]), axis=1)
+        if flags & oracle.ROWWISE:
+            acc_r.add(h, qr[r], sr[r], o[0], o[1])
+        if flags & oracle.COLWISE:
+            acc_c.add(np.ascontiguousarray(h.T), qc[:, r], sc[:, r0 // 32:(r0 + chunk) // 32], o[2], o[3])
+        return acc_r, acc_c
+
+    tot_r, tot_c = rule3_mx(what + " rowwise"), rule3_mx(what + " colwise")
+    with cf.ThreadPoolExecutor(max_workers=4) as ex:
+        for acc_r, acc_c in ex.map(one, range(0, M, chunk)):
+            tot_r.merge(acc_r)
+            tot_c.merge(acc_c)
+    res = {}
+    if flags & oracle.ROWWISE:
+        res["rowwise"] = tot_r.finish()
+    if flags & oracle.COLWISE:
+        res["colwise"] = tot_c.finish()
+    return res
 
 
-def test_config_large_swiglu_outliers_sampled(gpu):
-    """[16384, 7168] with 0.1% x1000 outliers, fwd and bwd, both scalings: every output of
-    sampled 32-row slabs (whole rows, whole colwise blocks) against the oracle."""
+def _host(out):
+    return tuple(u8(t) for t in out)
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_config_large_swiglu_outliers_full(gpu, direction):
+    """[16384, 7168] with 0.1% x1000 outliers, both scalings: rule 3 on every code and scale
+    of the fused launch (as the benchmark launches it), forward or backward."""
     M, N = 16384, 7168
     g, u, d = si.normal_bf16_device([(M, N)] * 3, seed=0, outliers=True)
-    fwd = gpu.glu_fwd_mxfp8(g, u, rowwise=True, colwise=True)
-    bwd = gpu.glu_bwd_mxfp8(g, u, d, rowwise=True, colwise=True)
+    if direction == "fwd":
+        out = gpu.glu_fwd_mxfp8(g, u, rowwise=True, colwise=True)
+    else:
+        out = gpu.glu_bwd_mxfp8(g, u, d, rowwise=True, colwise=True)
     torch.cuda.synchronize()
-    for s in _slabs(M, 6, 1):
-        r = slice(32 * s, 32 * s + 32)
-        gb, ub, db_ = bits(g[r]), bits(u[r]), bits(d[r])
-        o = oracle.glu_fwd_mxfp8(oracle.SWIGLU, gb, ub, flags=3)
-        h = oracle.glu_fwd(oracle.SWIGLU, gb, ub)
-        sl = (fwd[0][r], fwd[1][:, r], fwd[2][r], fwd[3][:, s:s + 1])
-        _rule3_rows(h, sl, o, f"fwd slab {s}")
-        o = oracle.glu_bwd_mxfp8(oracle.SWIGLU, gb, ub, db_, flags=3)
-        oa, ob = oracle.glu_bwd(oracle.SWIGLU, gb, ub, db_)
-        sl = (bwd[0][r], bwd[1][:, r], bwd[2][r], bwd[3][:, s:s + 1])
-        _rule3_rows(np.concatenate([oa, ob], 1), sl, o, f"bwd slab {s}")
+    gb, ub = bits(g), bits(u)
+    db_ = bits(d) if direction == "bwd" else None
+    res = _full_rule3_mx(gb, ub, db_, _host(out), 3, f"{direction} 16384x7168")
+    assert res["rowwise"]["codes"] == (2 if direction == "bwd" else 1) * M * N
+    assert res["colwise"]["codes"] == (2 if direction == "bwd" else 1) * M * N
 
 
 def test_rowwise_bwd_streaming_stores_sampled(gpu):
@@ -346,13 +380,76 @@ def test_rowwise_bwd_streaming_stores_sampled(gpu):
     check_rule3_mx(x, u8(qr[rows]), u8(sr[rows]), oe[0], oe[1], "bwd 16384x8192")
 
 
-def test_config_xlarge_swiglu_fwd_rowwise_sampled(gpu):
+def test_config_xlarge_swiglu_fwd_rowwise_full(gpu):
+    """[131072, 8192] with the same outlier recipe, forward rowwise: rule 3 on every code and
+    scale (1.07e9 codes)."""
     M, N = 131072, 8192
     g, u = si.normal_bf16_device([(M, N)] * 2, seed=0, outliers=True)
     qr, _, sr, _ = gpu.glu_fwd_mxfp8(g, u, rowwise=True)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(2)
-    rows = torch.tensor(sorted({0, M - 1, *rng.integers(0, M, 30).tolist()}), device="cuda")
-    gb, ub = bits(g[rows]), bits(u[rows])
-    o = oracle.glu_fwd_mxfp8(oracle.SWIGLU, gb, ub, flags=1)
-    check_rule3_mx(oracle.glu_fwd(oracle.SWIGLU, gb, ub), u8(qr[rows]), u8(sr[rows]), o[0], o[1], "131072x8192")
+    gb, ub = bits(g), bits(u)
+    del g, u
+    empty = np.zeros((0, 0), np.uint8)
+    res = _full_rule3_mx(gb, ub, None, (u8(qr), empty, u8(sr), empty), 1, "fwd 131072x8192", chunk=2048)
+    assert res["rowwise"]["codes"] == M * N
+
+
+def test_int32_bound_paired_operand_2pow31(gpu):
+    """The largest legal shape of the 32-bit bound: an interleaved [131072, 16384] operand holds
+    2^31 elements (4 GiB), past every 32-bit element and byte index.  glu_fwd and the rowwise
+    fused forward take it whole; sampled rows, the last included, are checked against the
+    oracle: h within one BF16 ulp (rule 2), the codes and scales bit-exact against the oracle
+    quantizer of the device's own h (rule 1) and end to end (rule 3)."""
+    M, H = 131072, 8192
+    x = si.normal_bf16_device([(M, 2 * H)], seed=5)[0]
+    assert x.numel() == 2 ** 31
+    h = gpu.glu_fwd(x, None, layout="paired")
+    qr, _, sr, _ = gpu.glu_fwd_mxfp8(x, None, layout="paired", rowwise=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    rows = torch.tensor(sorted({0, 1, M // 2, M - 2, M - 1, *rng.integers(0, M, 27).tolist()}), device="cuda")
+    xr = bits(x[rows])
+    gb, ub = np.ascontiguousarray(xr[:, 0::2]), np.ascontiguousarray(xr[:, 1::2])
+    hb = bits(h[rows])
+    check_rule2(hb, oracle.glu_fwd(oracle.SWIGLU, gb, ub), "h at 2^31 elements")
+    o = _q(hb, oracle.ROWWISE)
+    assert np.array_equal(u8(qr[rows]), o[0]) and np.array_equal(u8(sr[rows]), o[1])
+    oe = oracle.glu_fwd_mxfp8(oracle.SWIGLU, gb, ub, flags=1)
+    check_rule3_mx(oracle.glu_fwd(oracle.SWIGLU, gb, ub), u8(qr[rows]), u8(sr[rows]), oe[0], oe[1], "2^31 paired")
+
+
+@pytest.mark.parametrize("transposed", [False, True])
+def test_every_bf16_value_under_every_scale_fused(gpu, transposed):
+    """Rule 1 through the fused kernels on the sweep matrix (every scale byte 0..247 with every
+    BF16 magnitude at that scale, every BF16 number as a block maximum, zero and subnormal
+    blocks): ReLU^2 with gate = 1 gives h = up exactly, and in the backward (up = 0.5)
+    da = db = dh exactly, so the quantizers see the sweep values themselves.  Forward rowwise
+    (the row kernel), colwise and both (the tiled kernel), backward rowwise and both; the
+    transposed matrix puts the blocks in columns.  Codes and scales are compared byte for byte
+    with the oracle quantizer of the device's own h, da, db, which are first checked to equal
+    the sweep values."""
+    X = mxfp8_sweep_matrix()
+    if transposed:
+        X = np.ascontiguousarray(X.T)
+    x = si.from_bits(X).cuda()
+    one = torch.ones_like(x)
+    h = bits(gpu.glu_fwd(one, x, act="relu2"))
+    assert np.array_equal(h, X), "h = up"
+    xf = si.from_bits(X).float().numpy()
+    for row, col in FLAGS:
+        qr, qc, sr, sc = gpu.glu_fwd_mxfp8(one, x, act="relu2", rowwise=row, colwise=col)
+        o = oracle.quant_mxfp8(xf, _flags(row, col))
+        if row:
+            assert np.array_equal(u8(sr), o[1]) and np.array_equal(u8(qr), o[0]), f"fwd rowwise ({row}, {col})"
+        if col:
+            assert np.array_equal(u8(sc), o[3]) and np.array_equal(u8(qc), o[2]), f"fwd colwise ({row}, {col})"
+    half = torch.full_like(x, 0.5)
+    da, db = gpu.glu_bwd(one, half, x, act="relu2")
+    assert np.array_equal(bits(da), X) and np.array_equal(bits(db), X), "da = db = dh"
+    xx = np.concatenate([xf, xf], axis=1)
+    for row, col in [(True, False), (True, True)]:
+        qr, qc, sr, sc = gpu.glu_bwd_mxfp8(one, half, x, act="relu2", rowwise=row, colwise=col)
+        o = oracle.quant_mxfp8(xx, _flags(row, col))
+        assert np.array_equal(u8(sr), o[1]) and np.array_equal(u8(qr), o[0]), f"bwd rowwise ({row}, {col})"
+        if col:
+            assert np.array_equal(u8(sc), o[3]) and np.array_equal(u8(qc), o[2]), "bwd colwise"

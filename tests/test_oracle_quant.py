@@ -390,3 +390,52 @@ def test_glu_gemm_is_glu_of_the_gemm():
         q, sc = oracle.glu_gemm_mxfp8(kind, Xq, Xs, Wq, Ws)
         o = oracle.quant_mxfp8(si.from_bits(h).float().numpy(), oracle.ROWWISE)
         assert np.array_equal(q, o[0]) and np.array_equal(sc, o[1])
+
+
+def test_two_level_at_unit_global_scale_against_single_level():
+    """An amax of 2688 (448 x 6) makes the global scale exactly 1, so two-level NVFP4 meets the
+    single-level quantizer, which is pinned on its own (hand-worked blocks, brute force).  Over
+    every positive finite E4M3 block scale S (a block whose maximum is 6 S) and every BF16
+    value x with |x| <= 6 S (both signs):
+      * the block scales agree everywhere (fl(amax * fl(1/6)) decides as amax / 6 does);
+      * the codes agree except at 42 (x, S) pairs (each with both signs), found in closed
+        form: S a normal E4M3 value with all three mantissa bits set (1.875 * 2^k, k = -6..7)
+        and |x| / S one of the E2M1 ties 1.25, 2.5, 5.  There fl(1/S) = fl(8/15) 2^-k lies
+        above 1/S, so fl(x * fl(1/S)) lands one FP32 ulp above the tie and rounds to the next
+        code up, where x / S itself rounds to the even code below.  (The subnormal 7 * 2^-9 has
+        fl(1/S) = fl(8/7) 2^6 below 1/S and no such pair.)"""
+    S_codes = np.arange(1, 0x7F, dtype=np.uint8)
+    S_vals = oracle.e4m3_to_f64(S_codes)
+    mags = np.arange(1, 0x7F80, dtype=np.uint32)
+    mvals = (mags << 16).view(np.float32).astype(np.float64)
+    rng = np.random.default_rng(77)
+    blocks, predicted = [], []
+    for code, S in zip(S_codes, S_vals):
+        body = np.concatenate([mags[mvals <= 6.0 * S]] * 2)
+        body = body | (rng.integers(0, 2, body.size, dtype=np.uint32) << 15)   # random signs
+        n = -(-body.size // 15)
+        body = np.resize(body, n * 15).reshape(n, 15)
+        head_bits = int(np.float32(6.0 * S).view(np.uint32) >> 16)
+        assert (head_bits << 16) == int(np.float32(6.0 * S).view(np.uint32))   # 6 S is a BF16 value
+        head = np.full((n, 1), head_bits, np.uint32) | (rng.integers(0, 2, (n, 1), dtype=np.uint32) << 15)
+        blk = np.concatenate([head, body], axis=1)
+        blocks.append(blk)
+        ratio = ((blk & 0x7FFF) << 16).view(np.float32).astype(np.float64) / S
+        predicted.append(((code & 7) == 7) & ((code >> 3) >= 1) & np.isin(ratio, (1.25, 2.5, 5.0)))
+    X = ((np.concatenate(blocks).astype(np.uint32)) << 16).view(np.float32)
+    pred = np.concatenate(predicted)
+    pad = (-X.shape[0]) % 8
+    X = np.concatenate([X, np.zeros((pad, 16), np.float32)]).reshape(-1, 128)
+    pred = np.concatenate([pred, np.zeros((pad, 16), bool)]).reshape(-1, 128)
+    q1, s1 = oracle.quant_nvfp4(X)
+    q2, s2 = oracle.quant_nvfp4_gs(X, np.float32(2688.0))
+    assert oracle.nvfp4_global_scale(2688.0) == 1.0
+    assert np.array_equal(s1, s2), "block scales"
+    c1 = np.empty(X.shape, np.uint8); c1[:, 0::2], c1[:, 1::2] = q1 & 0xF, q1 >> 4
+    c2 = np.empty(X.shape, np.uint8); c2[:, 0::2], c2[:, 1::2] = q2 & 0xF, q2 >> 4
+    differ = c1 != c2
+    assert np.array_equal(differ, pred), f"{int(differ.sum())} differing codes, {int(pred.sum())} predicted"
+    sblk = np.repeat(np.asarray(s1).reshape(X.shape[0], 8), 16, axis=1)     # each element's scale code
+    pairs = set(zip(((X.view(np.uint32)[pred] >> 16) & 0x7FFF).tolist(), sblk[pred].tolist()))
+    assert len(pairs) == 42
+    assert np.all((c2[differ] & 8) == (c1[differ] & 8)) and np.all((c2[differ] & 7) == (c1[differ] & 7) + 1)
