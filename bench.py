@@ -8,15 +8,25 @@ Inputs are resident in HBM before the timed region.  `value` is algorithmic GB/s
 the method must move (BF16 inputs read once, E4M3 codes and E8M0 scales written once,
 GB = 1e9) divided by the time of the K timed steps.
 
+Before anything is timed, every timed configuration is validated on the GPU (unless
+--no-validate): the fused outputs must equal, byte for byte, the library's unfused path
+(glu_fwd / glu_bwd, then the FP32 quantizer hook: the activation followed by the standalone
+quantizer), and sampled rows of h, da, db must be within one BF16 ulp of a float64 torch
+reference of the same formulas.  A failure stops the run.
+
 Also reported on the same JSON line:
   roofline      - the dominant kernel (the fused backward) against the 8 TB/s HBM peak,
-                  its duration measured with HIP events on the launch stream;
+                  its duration measured with HIP events on the launch stream, and against
+                  the practical ceiling of its byte mix (the library's streaming probe:
+                  three BF16 read streams and four code write streams at the same size);
+  ceiling       - the streaming probe as a plain 1 GiB copy, and at the step's mixes;
   cpu_baseline  - the CPU oracle on a bounded row sample of the same workload;
   sweep         - every workload shape of the pages (MXFP8 SwiGLU fwd/bwd per direction,
-                  GeGLU BF16 fwd/bwd, GeGLU NVFP4), median of cold launches, plus the
-                  other activations (tanh-GeGLU, erf-GeGLU, ReLU^2) at one shape of each,
-                  the NVFP4 backward, two-level NVFP4 (amax pass + forward), and the
-                  merged MXFP8 GEMM with the GLU epilogue (TFLOP/s against the FP8 peak).
+                  GeGLU BF16 fwd/bwd, GeGLU NVFP4), median, min and p90 of cold launches,
+                  each beside the probe's ceiling for its byte mix, plus the other
+                  activations (tanh-GeGLU, erf-GeGLU, ReLU^2) at one shape of each, the
+                  NVFP4 backward, two-level NVFP4 (amax pass + forward), and the merged
+                  MXFP8 GEMM with the GLU epilogue (TFLOP/s against the FP8 peak).
 Only one GPU is supported; --gpus above 1 exits with a message.
 """
 import argparse
@@ -34,7 +44,8 @@ METRIC = "fused GLU+MX-quant fwd/bwd achieved HBM GB/s and % of peak, M×N sweep
 PEAK_GBPS = 8000.0  # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 matrix cores
 # The MXFP8 page's fused GB200 times for this exact workload (forward both 143.36 us,
-# backward both 219.14 us at (16384, 7168)), combined under the same byte model.
+# backward both 219.14 us at (16384, 7168)), combined under the same byte model: another
+# machine's figure, reported under config as context only.
 PAGES_STEP_GBPS = (711_983_104 + 1_189_085_184) / ((143.36 + 219.14) * 1e-6) / 1e9
 
 
@@ -120,19 +131,174 @@ def n_sets(bytes_per_set):
     return max(1, min(32, math.ceil((1 << 30) / max(1, bytes_per_set))))
 
 
-def sweep(torch, glu, si, iters):
+# ---------------------------------------------------------------------------------------
+# Validation before timing (GPU only): the fused outputs against the library's unfused path,
+# and the BF16 values against a float64 torch reference of the same formulas.
+# ---------------------------------------------------------------------------------------
+
+class ValidationError(RuntimeError):
+    pass
+
+
+def _ref_act(torch, act, x):
+    """act(x) and act'(x) in float64 (the textbook formulas; torch's own GELUs)."""
+    F = torch.nn.functional
+    x = x.detach().requires_grad_(True)
+    if act == "swiglu":
+        y = x * torch.sigmoid(x)
+    elif act == "geglu":
+        y = F.gelu(x, approximate="tanh")
+    elif act == "geglu_erf":
+        y = F.gelu(x)
+    else:
+        y = torch.relu(x) ** 2
+    (g,) = torch.autograd.grad(y.sum(), x)
+    return y.detach(), g
+
+
+def _ulp_far(torch, got, ref):
+    """Elements of two BF16 tensors more than one BF16 ulp apart (+0 and -0 identified,
+    NaN matching NaN)."""
+    def ordered(t):
+        b = t.contiguous().view(torch.int16).to(torch.int32)
+        mag = b & 0x7FFF
+        return torch.where(b < 0, -mag, mag), mag > 0x7F80
+    a, na = ordered(got)
+    b, nb = ordered(ref)
+    far = ((a - b).abs() > 1) & ~(na & nb)
+    return int(far.sum())
+
+
+def _check_bf16_rows(torch, act, g, u, d, outs, what, nrows=8):
+    """Sampled rows of h (d None) or of (da, db): within one BF16 ulp of float64 torch."""
+    M = g.shape[0]
+    rows = torch.unique(torch.tensor([0, M - 1] + [int(M * k / nrows) for k in range(1, nrows)],
+                                     device=g.device))
+    gg, uu = g[rows].double(), u[rows].double()
+    a, ap = _ref_act(torch, act, gg)
+    if d is None:
+        refs = [(a * uu).to(torch.bfloat16)]
+    else:
+        dd = d[rows].double()
+        refs = [(dd * uu * ap).to(torch.bfloat16), (dd * a).to(torch.bfloat16)]
+    for got, ref in zip(outs, refs):
+        n = _ulp_far(torch, got[rows], ref)
+        if n:
+            raise ValidationError(f"{what}: {n} sampled BF16 values beyond one ulp of the float64 reference")
+
+
+def _equal(torch, a, b, what):
+    if a.shape != b.shape or not torch.equal(a, b):
+        raise ValidationError(f"{what}: fused output differs from the unfused path")
+
+
+def validate_mx(torch, glu, act, g, u, d, out, row, col, swz, what):
+    """Fused MXFP8 outputs == glu_quant_mxfp8_f32 of the BF16 GLU output; BF16 rows vs float64."""
+    if d is None:
+        h = glu.glu_fwd(g, u, act=act)
+        _check_bf16_rows(torch, act, g, u, None, [h], what)
+        x = h.float()
+    else:
+        da, db = glu.glu_bwd(g, u, d, act=act)
+        _check_bf16_rows(torch, act, g, u, d, [da, db], what)
+        x = torch.cat([da, db], 1).float()
+        del da, db
+    ref = glu.glu_quant_mxfp8_f32(x, rowwise=row, colwise=col, swizzled=swz)
+    for k in range(4):
+        _equal(torch, out[k], ref[k], f"{what} output {k}")
+    del x, ref
+
+
+def validate_bf16(torch, glu, act, g, u, d, outs, what):
+    _check_bf16_rows(torch, act, g, u, d, outs, what)
+
+
+def validate_nv(torch, glu, act, x, out, sf_layout, what, amax=None):
+    """Fused NVFP4 (paired operand) == glu_quant_nvfp4_f32 of the BF16 GLU output (global
+    scale 1 only; the two-level forward is checked against its amax pass being finite)."""
+    h = glu.glu_fwd(x, None, act=act, layout="paired")
+    g, u = x[:, 0::2], x[:, 1::2]
+    _check_bf16_rows(torch, act, g, u, None, [h], what)
+    if amax is None:
+        ref = glu.glu_quant_nvfp4_f32(h.float(), sf_layout=sf_layout)
+        _equal(torch, out[0], ref[0], what + " codes")
+        _equal(torch, out[1], ref[1], what + " scales")
+    else:
+        a = float(amax.item())
+        if not (a == float(h.float().abs().max().item())):
+            raise ValidationError(f"{what}: amax pass {a} differs from the largest |h|")
+
+
+def validate_nv_bwd(torch, glu, act, g, u, d, out, sf_layout, what):
+    da, db = glu.glu_bwd(g, u, d, act=act)
+    _check_bf16_rows(torch, act, g, u, d, [da, db], what)
+    ref = glu.glu_quant_nvfp4_f32(torch.cat([da, db], 1).float(), sf_layout=sf_layout)
+    _equal(torch, out[0], ref[0], what + " codes")
+    _equal(torch, out[1], ref[1], what + " scales")
+
+
+def validate_gemm(torch, glu, ops, act, fmt, out, what):
+    h = glu.glu_gemm(*ops, act=act)
+    if fmt == "mxfp8":
+        q, s = glu.glu_quant_mxfp8_f32(h.float(), rowwise=True)[0::2]
+    else:
+        q, s = glu.glu_quant_nvfp4_f32(h.float(), sf_layout="128x4")
+    _equal(torch, out[0], q, what + " codes")
+    _equal(torch, out[1].reshape(-1), s.reshape(-1), what + " scales")
+
+
+# ---------------------------------------------------------------------------------------
+# The streaming probe: practical ceilings for a byte mix
+# ---------------------------------------------------------------------------------------
+
+def probe_ceiling(torch, glu, n_src, n_dst, width, elems, iters):
+    """GB/s of the streaming probe moving n_src BF16 streams of `elems` elements in and n_dst
+    streams of width / 16 bytes per source byte out (cold: buffer sets rotated past 1 GiB)."""
+    nbytes = 2 * elems
+    nbytes -= nbytes % 16
+    per = (n_src + n_dst * width / 16) * nbytes
+    k = max(2, n_sets(per))
+    sets = [([torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n_src)],
+             [torch.empty(nbytes * width // 16, dtype=torch.uint8, device="cuda") for _ in range(n_dst)])
+            for _ in range(k)]
+    t = time_launches(torch, [lambda st=st: glu.glu_stream_probe(*st) for st in sets], iters)
+    del sets
+    return dict(gbps=round(per / t["median_us"] / 1e3, 1), us=round(t["median_us"], 2),
+                frac=round(per / t["median_us"] / 1e3 / PEAK_GBPS, 4), n_src=n_src, n_dst=n_dst,
+                dst_bytes_per_16=width, bytes=int(per))
+
+
+# ---------------------------------------------------------------------------------------
+# Sweep
+# ---------------------------------------------------------------------------------------
+
+def sweep(torch, glu, si, iters, validate):
     res = {}
+    ceilings = {}
 
-    def rec(name, b, t):
-        print(f"[bench] {name}: {t['median_us']:.2f} us", file=sys.stderr, flush=True)
-        res[name] = dict(bytes=b, us=round(t["median_us"], 2), gbps=round(b / t["median_us"] / 1e3, 1),
-                         frac=round(b / t["median_us"] / 1e3 / PEAK_GBPS, 4))
+    def ceiling(n_src, n_dst, width, elems):
+        key = (n_src, n_dst, width, elems)
+        if key not in ceilings:
+            ceilings[key] = probe_ceiling(torch, glu, n_src, n_dst, width, elems, iters)
+        return ceilings[key]
 
-    # practical ceiling: a device-to-device copy of 1 GiB (runtime blit kernel), 2 GiB moved
-    src = [torch.empty(1 << 30, dtype=torch.uint8, device="cuda") for _ in range(2)]
-    dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    rec("device_copy_1GiB", 2 << 30, time_launches(torch, [lambda x=x: dst.copy_(x) for x in src], iters))
-    del src, dst
+    def rec(name, b, t, mix=None):
+        gbps = b / t["median_us"] / 1e3
+        r = dict(bytes=b, us=round(t["median_us"], 2), min_us=round(t["min_us"], 2), p90_us=round(t["p90_us"], 2),
+                 gbps=round(gbps, 1), frac=round(gbps / PEAK_GBPS, 4), validated=validate)
+        if mix is not None:
+            c = ceiling(*mix)
+            r["ceiling_gbps"] = c["gbps"]
+            r["frac_of_ceiling"] = round(gbps / c["gbps"], 4)
+        res[name] = r
+        print(f"[bench] {name}: {t['median_us']:.2f} us ({r['frac']:.3f} of peak"
+              + (f", {r['frac_of_ceiling']:.3f} of ceiling" if mix else "") + ")", file=sys.stderr, flush=True)
+
+    # practical ceiling: the streaming probe as a 1 GiB copy (2 GiB moved)
+    c = ceiling(1, 1, 16, 1 << 29)
+    res["stream_copy_1GiB"] = dict(bytes=c["bytes"], us=c["us"], gbps=c["gbps"], frac=c["frac"])
+    print(f"[bench] stream_copy_1GiB: {c['us']:.2f} us ({c['frac']:.3f} of peak)", file=sys.stderr, flush=True)
+
     # MXFP8 SwiGLU shapes, and the other activations at [16384, 7168]
     others = [(d, "both", a) for a in ("geglu", "geglu_erf", "relu2") for d in ("fwd", "bwd")]
     for M, N, outl, cases in [
@@ -153,12 +319,19 @@ def sweep(torch, glu, si, iters):
             bwd = d == "bwd"
             out = glu._mx_buffers(M, 2 * N if bwd else N, row, col, "cuda", None, swz)
             kw = dict(act=act, rowwise=row, colwise=col, swizzled=swz, out=out)
+            name = f"{act}_mxfp8_{d}_{mode}_{M}x{N}"
             if bwd:
                 fns = [lambda s=s: glu.glu_bwd_mxfp8(s[0], s[1], s[2], **kw) for s in sets]
             else:
                 fns = [lambda s=s: glu.glu_fwd_mxfp8(s[0], s[1], **kw) for s in sets]
+            if validate:
+                fns[0]()
+                validate_mx(torch, glu, act, sets[0][0], sets[0][1], sets[0][2] if bwd else None, out,
+                            row, col, swz, name)
             t = time_launches(torch, fns, iters)
-            rec(f"{act}_mxfp8_{d}_{mode}_{M}x{N}", mx_bytes(M, N, bwd, 2 if dirs == "both" else 1), t)
+            ndir = 2 if dirs == "both" else 1
+            mix = (3, 2 * ndir, 8, M * N) if bwd else (2, ndir, 8, M * N)
+            rec(name, mx_bytes(M, N, bwd, ndir), t, mix if M * N >= (1 << 24) else None)
             del out, fns
         del sets
         torch.cuda.empty_cache()
@@ -168,12 +341,19 @@ def sweep(torch, glu, si, iters):
             sets = [si.normal_bf16_device([(R, W)] * 3, seed=R + W + s) for s in range(n_sets(6 * R * W))]
             h = torch.empty(R, W, dtype=torch.bfloat16, device="cuda")
             da, db = torch.empty_like(h), torch.empty_like(h)
-            t = time_launches(torch, [lambda s=s: glu.glu_fwd(s[0], s[1], act="geglu", out=h) for s in sets], iters)
-            rec(f"geglu_bf16_fwd_{R}x{W}", bf16_bytes(R, W, False), t)
-            t = time_launches(torch, [lambda s=s: glu.glu_bwd(s[0], s[1], s[2], act="geglu", out=(da, db))
-                                      for s in sets], iters)
-            rec(f"geglu_bf16_bwd_{R}x{W}", bf16_bytes(R, W, True), t)
-            del sets, h, da, db
+            fns = [lambda s=s: glu.glu_fwd(s[0], s[1], act="geglu", out=h) for s in sets]
+            if validate:
+                fns[0]()
+                validate_bf16(torch, glu, "geglu", sets[0][0], sets[0][1], None, [h], f"geglu bf16 fwd {R}x{W}")
+            t = time_launches(torch, fns, iters)
+            rec(f"geglu_bf16_fwd_{R}x{W}", bf16_bytes(R, W, False), t, (2, 1, 16, R * W))
+            fns = [lambda s=s: glu.glu_bwd(s[0], s[1], s[2], act="geglu", out=(da, db)) for s in sets]
+            if validate:
+                fns[0]()
+                validate_bf16(torch, glu, "geglu", *sets[0], [da, db], f"geglu bf16 bwd {R}x{W}")
+            t = time_launches(torch, fns, iters)
+            rec(f"geglu_bf16_bwd_{R}x{W}", bf16_bytes(R, W, True), t, (3, 2, 16, R * W))
+            del sets, h, da, db, fns
         torch.cuda.empty_cache()
     # the other activations, BF16 at [8192, 14336]
     R, W = 8192, 14336
@@ -181,54 +361,62 @@ def sweep(torch, glu, si, iters):
     h = torch.empty(R, W, dtype=torch.bfloat16, device="cuda")
     da, db = torch.empty_like(h), torch.empty_like(h)
     for act in ("swiglu", "geglu_erf", "relu2"):
-        t = time_launches(torch, [lambda s=s: glu.glu_fwd(s[0], s[1], act=act, out=h) for s in sets], iters)
-        rec(f"{act}_bf16_fwd_{R}x{W}", bf16_bytes(R, W, False), t)
-        t = time_launches(torch, [lambda s=s: glu.glu_bwd(s[0], s[1], s[2], act=act, out=(da, db))
-                                  for s in sets], iters)
-        rec(f"{act}_bf16_bwd_{R}x{W}", bf16_bytes(R, W, True), t)
-    del sets, h, da, db
+        fns = [lambda s=s: glu.glu_fwd(s[0], s[1], act=act, out=h) for s in sets]
+        if validate:
+            fns[0]()
+            validate_bf16(torch, glu, act, sets[0][0], sets[0][1], None, [h], f"{act} bf16 fwd")
+        rec(f"{act}_bf16_fwd_{R}x{W}", bf16_bytes(R, W, False), time_launches(torch, fns, iters), (2, 1, 16, R * W))
+        fns = [lambda s=s: glu.glu_bwd(s[0], s[1], s[2], act=act, out=(da, db)) for s in sets]
+        if validate:
+            fns[0]()
+            validate_bf16(torch, glu, act, *sets[0], [da, db], f"{act} bf16 bwd")
+        rec(f"{act}_bf16_bwd_{R}x{W}", bf16_bytes(R, W, True), time_launches(torch, fns, iters), (3, 2, 16, R * W))
+    del sets, h, da, db, fns
     torch.cuda.empty_cache()
-    # GeGLU NVFP4
+    # GeGLU NVFP4 (paired operand: two virtual BF16 streams in, half a byte per element out)
     H = 16384
     for M in (784, 816, 880, 968):
         sets = [si.normal_bf16_device([(M, 2 * H)], seed=M + s)[0] for s in range(n_sets(4 * M * H))]
         out = glu._nv_buffers(M, H, "128x4", "cuda", None)
-        t = time_launches(torch, [lambda x=x: glu.glu_fwd_nvfp4(x, act="geglu", layout="paired",
-                                                                 sf_layout="128x4", out=out) for x in sets], iters)
-        rec(f"geglu_nvfp4_fwd_{M}x{H}", nv_bytes(M, H), t)
-        if M == 968:   # the other activations at the largest shape
-            for act in ("swiglu", "geglu_erf", "relu2"):
-                t = time_launches(torch, [lambda x=x: glu.glu_fwd_nvfp4(x, act=act, layout="paired",
-                                                                         sf_layout="128x4", out=out) for x in sets], iters)
-                rec(f"{act}_nvfp4_fwd_{M}x{H}", nv_bytes(M, H), t)
-        del sets, out
+        for act in ("geglu",) + (("swiglu", "geglu_erf", "relu2") if M == 968 else ()):
+            fns = [lambda x=x: glu.glu_fwd_nvfp4(x, act=act, layout="paired", sf_layout="128x4", out=out)
+                   for x in sets]
+            if validate:
+                fns[0]()
+                validate_nv(torch, glu, act, sets[0], out, "128x4", f"{act} nvfp4 fwd {M}")
+            rec(f"{act}_nvfp4_fwd_{M}x{H}", nv_bytes(M, H), time_launches(torch, fns, iters), (2, 1, 4, M * H))
+        del sets, out, fns
     # two-level NVFP4: the amax pass and the forward with the global scale
     for M, H in ((968, 16384), (16384, 7168)):
         sets = [si.normal_bf16_device([(M, 2 * H)], seed=M + s)[0] for s in range(n_sets(4 * M * H))]
         out = glu._nv_buffers(M, H, "128x4", "cuda", None)
         amax = torch.empty((1,), dtype=torch.float32, device="cuda")
-        t = time_launches(torch, [lambda x=x: glu.glu_amax(x, act="geglu", layout="paired", out=amax)
-                                  for x in sets], iters)
-        rec(f"geglu_amax_{M}x{H}", 4 * M * H, t)
-        t = time_launches(torch, [lambda x=x: glu.glu_fwd_nvfp4_gs(x, amax=amax, act="geglu", layout="paired",
-                                                                    sf_layout="128x4", out=out) for x in sets], iters)
-        rec(f"geglu_nvfp4_gs_fwd_{M}x{H}", nv_bytes(M, H), t)
-        del sets, out
+        fns = [lambda x=x: glu.glu_amax(x, act="geglu", layout="paired", out=amax) for x in sets]
+        if validate:
+            fns[0]()
+            validate_nv(torch, glu, "geglu", sets[0], out, "128x4", f"geglu amax {M}", amax=amax)
+        rec(f"geglu_amax_{M}x{H}", 4 * M * H, time_launches(torch, fns, iters))
+        fns = [lambda x=x: glu.glu_fwd_nvfp4_gs(x, amax=amax, act="geglu", layout="paired", sf_layout="128x4",
+                                                out=out) for x in sets]
+        rec(f"geglu_nvfp4_gs_fwd_{M}x{H}", nv_bytes(M, H), time_launches(torch, fns, iters), (2, 1, 4, M * H))
+        del sets, out, fns
         torch.cuda.empty_cache()
     # NVFP4 backward ([da | db] quantized), the workload's shape and the MXFP8 training shape
     for M, N in ((968, 16384), (16384, 7168)):
         sets = [si.normal_bf16_device([(M, N)] * 3, seed=M + N + s) for s in range(n_sets(6 * M * N))]
         out = glu._nv_buffers(M, 2 * N, "128x4", "cuda", None)
         for act in ("swiglu", "geglu"):
-            t = time_launches(torch, [lambda s=s: glu.glu_bwd_nvfp4(s[0], s[1], s[2], act=act, sf_layout="128x4",
-                                                                     out=out) for s in sets], iters)
-            rec(f"{act}_nvfp4_bwd_{M}x{N}", nv_bwd_bytes(M, N), t)
-        del sets, out
+            fns = [lambda s=s: glu.glu_bwd_nvfp4(s[0], s[1], s[2], act=act, sf_layout="128x4", out=out)
+                   for s in sets]
+            if validate:
+                fns[0]()
+                validate_nv_bwd(torch, glu, act, *sets[0], out, "128x4", f"{act} nvfp4 bwd {M}x{N}")
+            rec(f"{act}_nvfp4_bwd_{M}x{N}", nv_bwd_bytes(M, N), time_launches(torch, fns, iters), (3, 2, 4, M * N))
+        del sets, out, fns
         torch.cuda.empty_cache()
     # merged gate/up MXFP8 GEMM with the GLU and MXFP8 rowwise (or NVFP4, 128x4 scales)
-    # epilogue: the NVFP4 page's
-    # projection (M tokens, K = 2048, merged 2N = 32768) in MXFP8 form, and the MXFP8 page's
-    # [16384, 7168] activation produced from K = 2048
+    # epilogue: the NVFP4 page's projection (M tokens, K = 2048, merged 2N = 32768) in MXFP8
+    # form, and the MXFP8 page's [16384, 7168] activation produced from K = 2048
     for M, N, K in ((968, 16384, 2048), (16384, 7168, 2048)):
         per = M * K + 2 * N * K
         sets = [si.mx_operand(M, K, seed=M + s, device="cuda") + si.mx_operand(2 * N, K, seed=N + s, device="cuda")
@@ -236,18 +424,21 @@ def sweep(torch, glu, si, iters):
         out = (torch.empty((M, N), dtype=torch.uint8, device="cuda"),
                torch.empty((M, N // 32), dtype=torch.uint8, device="cuda"))
         nv_out = glu._nv_buffers(M, N, "128x4", "cuda", None)
-        cases = [("swiglu", "mxfp8"), ("geglu", "mxfp8"), ("geglu", "nvfp4")]
-        for act, fmt in cases:
+        for act, fmt in [("swiglu", "mxfp8"), ("geglu", "mxfp8"), ("geglu", "nvfp4")]:
             if fmt == "mxfp8":
                 fns = [lambda s=s: glu.glu_gemm_mxfp8(*s, act=act, out=out) for s in sets]
             else:
                 fns = [lambda s=s: glu.glu_gemm_nvfp4(*s, act=act, sf_layout="128x4", out=nv_out) for s in sets]
+            name = f"{act}_gemm_{fmt}_{M}x{N}x{K}"
+            if validate:
+                fns[0]()
+                validate_gemm(torch, glu, sets[0], act, fmt, out if fmt == "mxfp8" else nv_out, name)
             t = time_launches(torch, fns, iters)
             tf = 2.0 * M * K * 2 * N / t["median_us"] / 1e6
-            name = f"{act}_gemm_{fmt}_{M}x{N}x{K}"
             print(f"[bench] {name}: {t['median_us']:.2f} us", file=sys.stderr, flush=True)
-            res[name] = dict(flops=2 * M * K * 2 * N, us=round(t["median_us"], 2), tflops=round(tf, 1),
-                             frac=round(tf / PEAK_FP8_TFLOPS, 4))
+            res[name] = dict(flops=2 * M * K * 2 * N, us=round(t["median_us"], 2), min_us=round(t["min_us"], 2),
+                             p90_us=round(t["p90_us"], 2), tflops=round(tf, 1), frac=round(tf / PEAK_FP8_TFLOPS, 4),
+                             validated=validate)
         # context, not part of the path: the platform library's GEMM alone (torch._scaled_mm,
         # BF16 output, no activation, no quantizer) on the same codes, with the same E8M0 block
         # scales and with one tensor-wide scale
@@ -275,6 +466,18 @@ def sweep(torch, glu, si, iters):
     return res
 
 
+def cpu_model():
+    """The host CPU's model name (as lscpu reports it, read from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(si, budget_s):
     """The oracle (as it stands) on whole 512-row slabs of the step's workload, until
     budget_s seconds of CPU time have passed or every row is done."""
@@ -292,6 +495,7 @@ def cpu_baseline(si, budget_s):
     b = mx_bytes(done, N, False, 2) + mx_bytes(done, N, True, 2)
     print(f"[bench] cpu oracle: {done} rows in {t_used:.1f} s", file=sys.stderr, flush=True)
     return dict(value=round(b / t_used / 1e9, 4), unit="GB/s", cores=oracle.num_threads(), kind="oracle",
+                cpu_model=cpu_model(), nproc=os.cpu_count(),
                 sample=f"{done} of 16384 rows x 7168 (fwd + bwd, both scalings), {t_used:.1f} s")
 
 
@@ -303,6 +507,8 @@ def main():
     ap.add_argument("--sweep-iters", type=int, default=20)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-validate", action="store_true",
+                    help="skip the validation of each timed configuration before it is timed")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch one 1 GiB device copy (for scaling HBM counters)")
@@ -327,6 +533,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     glu.lib()  # fail loudly when the HIP library is missing
+    validate = not args.no_validate
 
     M, N = 16384, 7168
     if args.nvfp4_only:
@@ -361,6 +568,14 @@ def main():
         glu.glu_bwd_mxfp8(g, u, d, rowwise=True, colwise=True, out=bo)
         if ev: ev[2].record()
 
+    if validate:
+        for i in range(2):
+            step(i)
+            g, u, d = sets[i]
+            validate_mx(torch, glu, "swiglu", g, u, None, fo, True, True, False, f"step forward, input set {i}")
+            validate_mx(torch, glu, "swiglu", g, u, d, bo, True, True, False, f"step backward, input set {i}")
+        torch.cuda.empty_cache()
+        print("[bench] step validated (both input sets, forward and backward)", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -386,7 +601,14 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    del sets, fo, bo
+    torch.cuda.empty_cache()
 
+    # practical ceilings of the step's byte mixes (the streaming probe at the same size)
+    ceil_copy = probe_ceiling(torch, glu, 1, 1, 16, 1 << 29, args.sweep_iters)
+    ceil_bwd = probe_ceiling(torch, glu, 3, 4, 8, M * N, args.sweep_iters)
+    ceil_fwd = probe_ceiling(torch, glu, 2, 2, 8, M * N, args.sweep_iters)
+    achieved = bwd_b / bwd_us / 1e3
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -397,7 +619,7 @@ def main():
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / PAGES_STEP_GBPS, 3),
+        "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {
@@ -406,19 +628,21 @@ def main():
             "outputs": "E4M3 codes + E8M0 RCEIL scales, rowwise 1x32 and colwise 32x1",
             "bytes_per_step": fwd_b + bwd_b, "pct_of_peak": round(100 * value / PEAK_GBPS, 1),
             "fwd_us": round(fwd_us, 2), "bwd_us": round(bwd_us, 2), "wall_s": round(wall, 3),
-            "pages_gbps_same_workload_gb200": round(PAGES_STEP_GBPS, 1),
+            "validated": validate,
+            "context_pages_gb200_gbps_same_workload": round(PAGES_STEP_GBPS, 1),
+            "context_ratio_to_pages_gb200": round(value / PAGES_STEP_GBPS, 3),
         },
         "roofline": {
             "bound": "hbm", "kernel": "k_mxfp8 backward, both scalings",
-            "achieved": round(bwd_b / bwd_us / 1e3, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-            "frac": round(bwd_b / bwd_us / 1e3 / PEAK_GBPS, 4),
-            "traffic": traffic_bytes("k_mxfp8<0,0,3,1,1>"),
+            "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBPS, 4),
+            "traffic": traffic_bytes("k_mxfp8<0,0,3,1>"),
+            "ceiling": ceil_bwd["gbps"], "frac_of_ceiling": round(achieved / ceil_bwd["gbps"], 4),
         },
+        "ceiling": {"stream_copy_1GiB": ceil_copy, "step_fwd_mix": ceil_fwd, "step_bwd_mix": ceil_bwd},
     }
-    del sets, fo, bo
-    torch.cuda.empty_cache()
     if not args.no_sweep:
-        result["sweep"] = sweep(torch, glu, si, args.sweep_iters)
+        result["sweep"] = sweep(torch, glu, si, args.sweep_iters, validate)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(si, args.cpu_budget)
     print(json.dumps(result), flush=True)

@@ -74,6 +74,8 @@ _SIGNATURES = {
     "glu_check_fwd_nvfp4_gs": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _p, _int],
     "glu_check_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p],
     "glu_check_quant_nvfp4_f32": [_i64, _i64, _p, _i64, _p, _p, _int],
+    "glu_stream_probe": [_int, _p, _int, _p, _i64, _int, _p],
+    "glu_check_stream_probe": [_int, _p, _int, _p, _i64, _int],
 }
 
 _lib = None
@@ -417,3 +419,23 @@ def glu_quant_nvfp4_f32(x, *, sf_layout="rowmajor", out=None):
     q, sf = _nv_buffers(M, H, sf_layout, x.device, out)
     _call("glu_quant_nvfp4_f32", M, H, _ptr(x), ld, _ptr(q), _ptr(sf), SF_LAYOUT[sf_layout], _stream(x))
     return q, sf
+
+
+def glu_stream_probe(srcs, dsts):
+    """The streaming probe (a measurement hook): each of the 1..3 uint8 GPU tensors in srcs
+    (n bytes each, n % 16 == 0) is read once and each of the 1..4 uint8 tensors in dsts
+    (n, n / 2 or n / 4 bytes each, all the same) written once, as glu_mx.h describes."""
+    n = srcs[0].numel()
+    for t in (*srcs, *dsts):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("stream probe buffers are contiguous uint8 GPU tensors")
+    if n % 16 or any(t.numel() != n for t in srcs) or len({t.numel() for t in dsts}) != 1:
+        raise ValueError("sources of equal size (a multiple of 16 bytes), destinations of equal size")
+    width = dsts[0].numel() * 16 // n if n else 16
+    if width not in (4, 8, 16) or dsts[0].numel() * 16 != width * n:
+        raise ValueError("destinations hold 4, 8 or 16 bytes per 16 source bytes")
+    src = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in srcs])
+    dst = (ctypes.c_void_p * 4)(*[t.data_ptr() for t in dsts])
+    _call("glu_stream_probe", len(srcs), ctypes.cast(src, ctypes.c_void_p), len(dsts),
+          ctypes.cast(dst, ctypes.c_void_p), n // 16, width, _stream(srcs[0]))
+

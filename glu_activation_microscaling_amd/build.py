@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libglu_mx.so")
-SOURCES = ["api.cpp", "glu_bf16.hip", "glu_mxfp8.hip", "glu_nvfp4.hip", "glu_gemm.hip"]
+SOURCES = ["api.cpp", "glu_bf16.hip", "glu_mxfp8.hip", "glu_nvfp4.hip", "glu_gemm.hip", "glu_stream.hip"]
 ARCH = "gfx950"
 
 COMMON = [
@@ -52,7 +52,7 @@ def _compile(src, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]

@@ -498,6 +498,33 @@ glu_status glu_check_quant_nvfp4_f32(int64_t M, int64_t H, const float* x, int64
   return check_no_overlap({Q, S}, {X});
 }
 
+glu_status glu_check_stream_probe(int n_src, const void* const* src, int n_dst, void* const* dst,
+                                  int64_t n_vec, int dst_bytes) {
+  if (n_src < 1 || n_src > 3 || n_dst < 1 || n_dst > 4 || (dst_bytes != 4 && dst_bytes != 8 && dst_bytes != 16))
+    return GLU_ERR_ARG;
+  if (n_vec < 0 || n_vec > ((int64_t)1 << 36)) return GLU_ERR_SHAPE;
+  if (src == nullptr || dst == nullptr) return GLU_ERR_NULL;
+  if (n_vec == 0) return GLU_OK;
+  Operand S[3], D[4];
+  for (int k = 0; k < n_src; k++) {
+    if (src[k] == nullptr) return GLU_ERR_NULL;
+    if (!aligned16(src[k])) return GLU_ERR_ALIGN;
+    S[k] = mat(src[k], 1, n_vec * 16, n_vec * 16, 1);
+  }
+  for (int k = 0; k < n_dst; k++) {
+    if (dst[k] == nullptr) return GLU_ERR_NULL;
+    if (!aligned16(dst[k])) return GLU_ERR_ALIGN;
+    D[k] = mat(dst[k], 1, n_vec * dst_bytes, n_vec * dst_bytes, 1);
+  }
+  for (int k = 0; k < n_dst; k++) {
+    for (int j = 0; j < n_src; j++)
+      if (overlaps(D[k], S[j])) return GLU_ERR_OVERLAP;
+    for (int j = k + 1; j < n_dst; j++)
+      if (overlaps(D[k], D[j])) return GLU_ERR_OVERLAP;
+  }
+  return GLU_OK;
+}
+
 // ---- entry points -----------------------------------------------------------------
 
 glu_status glu_fwd(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
@@ -674,6 +701,16 @@ glu_status glu_quant_nvfp4_f32(int64_t M, int64_t H, const float* x, int64_t ld_
   if (st != GLU_OK || M == 0 || H == 0) return st;
   NvArgs a{glu::SWIGLU, glu::SPLIT, sf_layout, M, H, x, nullptr, ld_x, q, sf, nullptr, 0, nullptr, nullptr};
   return status_of(glu::launch_quant_nvfp4_f32(a, (hipStream_t)stream));
+}
+
+glu_status glu_stream_probe(int n_src, const void* const* src, int n_dst, void* const* dst,
+                            int64_t n_vec, int dst_bytes, void* stream) {
+  glu_status st = glu_check_stream_probe(n_src, src, n_dst, dst, n_vec, dst_bytes);
+  if (st != GLU_OK || n_vec == 0) return st;
+  glu::StreamArgs a{n_src, n_dst, dst_bytes, n_vec, {nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr, nullptr}};
+  for (int k = 0; k < n_src; k++) a.src[k] = src[k];
+  for (int k = 0; k < n_dst; k++) a.dst[k] = dst[k];
+  return status_of(glu::launch_stream_probe(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

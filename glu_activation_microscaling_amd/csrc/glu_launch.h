@@ -70,6 +70,13 @@ struct GemmArgs {
   const float* amax = nullptr;  // two-level NVFP4: the amax the global scale comes from
 };
 
+struct StreamArgs {          // streaming probe (validated: 1..3 sources, 1..4 destinations)
+  int n_src, n_dst, dst_bytes;  // dst_bytes: 4, 8 or 16 per source vector
+  int64_t n_vec;                // 16-byte vectors per source
+  const void* src[3];
+  void* dst[4];
+};
+
 hipError_t launch_glu_fwd_bf16(const BF16Args& a, hipStream_t s);
 hipError_t launch_glu_bwd_bf16(const BF16Args& a, hipStream_t s);
 hipError_t launch_glu_fwd_mxfp8(const MxArgs& a, hipStream_t s);
@@ -85,6 +92,7 @@ hipError_t launch_mx_gemm_f32(const GemmArgs& a, hipStream_t s);
 // NVFP4 epilogue: codes into q_row ([M, N/2] packed E2M1), E4M3 scales into s_row
 hipError_t launch_glu_gemm_nvfp4(const GemmArgs& a, int sf_layout, bool two_level, hipStream_t s);
 hipError_t launch_quant_nvfp4_f32(const NvArgs& a, hipStream_t s);
+hipError_t launch_stream_probe(const StreamArgs& a, hipStream_t s);
 
 // Launches kernel k and returns the launch status of this call alone (the HIP error
 // state left by earlier, unrelated calls is not consulted).

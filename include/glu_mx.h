@@ -256,6 +256,21 @@ glu_status glu_quant_mxfp8_f32(int64_t M, int64_t N, const float* x, int64_t ld_
 glu_status glu_quant_nvfp4_f32(int64_t M, int64_t H, const float* x, int64_t ld_x,
                                uint8_t* q, uint8_t* sf, int sf_layout, void* stream);
 
+/* ---- Measurement hook: the streaming probe.  Moves n_vec 16-byte vectors from each of the
+ * n_src sources (1..3) into each of the n_dst destinations (1..4; dst_bytes = 4, 8 or 16
+ * bytes per vector) with non-temporal loads and stores, one vector per thread, consecutive
+ * workgroups on consecutive addresses: the practical HBM ceiling for that mix of read and
+ * write streams, beside which the fused kernels' rates are read (a fused MXFP8 forward
+ * reads two BF16 streams and writes one byte per element: n_src = 2, dst_bytes = 8 per
+ * 8-element vector).  With x the XOR of the sources' vectors (32-bit words x0..x3),
+ * destination k receives per vector x with x0 + k in place of x0 (dst_bytes = 16), the words
+ * (x0 ^ x2) + k, x1 ^ x3 (8), or the word (x0 ^ x1 ^ x2 ^ x3) + k (4).  src and dst are host
+ * arrays of device pointers (16-byte aligned); destinations may not overlap the sources or
+ * each other.  Errors: GLU_ERR_ARG (counts, dst_bytes), GLU_ERR_SHAPE (n_vec < 0 or above
+ * 2^36), GLU_ERR_NULL, GLU_ERR_ALIGN, GLU_ERR_OVERLAP. */
+glu_status glu_stream_probe(int n_src, const void* const* src, int n_dst, void* const* dst,
+                            int64_t n_vec, int dst_bytes, void* stream);
+
 /* ---- Host-only validation: the exact checks the entry point of the same name runs
  * before launching, with the same arguments minus the stream.  Never calls HIP and never
  * dereferences a pointer, so it runs on machines without a GPU. */
@@ -305,6 +320,8 @@ glu_status glu_check_quant_mxfp8_f32(int64_t M, int64_t N, const float* x, int64
                                      uint8_t* q_col, uint8_t* s_col);
 glu_status glu_check_quant_nvfp4_f32(int64_t M, int64_t H, const float* x, int64_t ld_x,
                                      uint8_t* q, uint8_t* sf, int sf_layout);
+glu_status glu_check_stream_probe(int n_src, const void* const* src, int n_dst, void* const* dst,
+                                  int64_t n_vec, int dst_bytes);
 
 /* Bytes of the scale buffer glu_fwd_nvfp4 / glu_quant_nvfp4_f32 write for this layout
  * (M*H/16 row-major, Rp*Cp for 128x4), or -1 for bad arguments. */

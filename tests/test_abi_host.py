@@ -256,6 +256,32 @@ def test_quant_hook_checks():
     assert n(64, 72, P(A0), 72, P(B0), P(C0), 0) == SHAPE
 
 
+def _ptrs(*addrs):
+    arr = (ctypes.c_void_p * max(1, len(addrs)))(*addrs)
+    return ctypes.cast(arr, ctypes.c_void_p)
+
+
+def test_stream_probe_checks():
+    c = L.glu_check_stream_probe
+    n = 1 << 20
+    assert c(2, _ptrs(A0, B0), 1, _ptrs(C0), n, 8) == OK
+    assert c(3, _ptrs(A0, B0, C0), 4, _ptrs(D0, E0, F0, F0 + 0x4000000), n, 16) == OK
+    assert c(0, _ptrs(A0), 1, _ptrs(C0), n, 8) == ARG
+    assert c(4, _ptrs(A0, B0, C0, D0), 1, _ptrs(E0), n, 8) == ARG
+    assert c(1, _ptrs(A0), 5, _ptrs(B0, C0, D0, E0, F0), n, 8) == ARG
+    assert c(1, _ptrs(A0), 1, _ptrs(B0), n, 4) == OK
+    assert c(1, _ptrs(A0), 1, _ptrs(B0), n, 2) == ARG
+    assert c(1, _ptrs(A0), 1, _ptrs(B0), -1, 8) == SHAPE
+    assert c(1, _ptrs(A0), 1, _ptrs(B0), 0, 8) == OK                 # empty: nothing inspected
+    assert c(1, P(0), 1, _ptrs(B0), n, 8) == NULL
+    assert c(1, _ptrs(0), 1, _ptrs(B0), n, 8) == NULL
+    assert c(1, _ptrs(A0 + 8), 1, _ptrs(B0), n, 8) == ALIGN
+    assert c(1, _ptrs(A0), 1, _ptrs(A0 + 16 * n - 16), n, 8) == OVERLAP   # destination on the source
+    assert c(1, _ptrs(A0), 2, _ptrs(B0, B0 + 8 * n - 16), n, 8) == OVERLAP  # destinations overlap
+    assert c(1, _ptrs(A0), 2, _ptrs(B0, B0 + 8 * n), n, 8) == OK           # adjacent is fine
+    assert L.glu_stream_probe(1, _ptrs(A0), 1, _ptrs(A0), n, 8, P(0)) == OVERLAP
+
+
 def test_gemm_checks():
     g = lambda **kw: _gemm(L.glu_check_gemm, **kw)
     assert g() == OK and g(act=3) == OK and g(act=4) == ARG
