@@ -9,6 +9,10 @@ Flags:
   -fno-fast-math                             the quantizer's decisions rely on IEEE FP32.
 Each translation unit is compiled in parallel; the result replaces the old library
 atomically.
+
+`python glu_activation_microscaling_amd/build.py --resources` prints the per-kernel resource
+table (VGPRs, AGPRs, SGPRs, scratch, spills, LDS, occupancy) that the compiler reports for
+these sources with these flags (-Rpass-analysis=kernel-resource-usage).
 """
 import concurrent.futures as cf
 import os
@@ -63,6 +67,47 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+_FIELDS = {"VGPRs": "vgpr", "AGPRs": "agpr", "TotalSGPRs": "sgpr", "ScratchSize [bytes/lane]": "scratch",
+           "VGPRs Spill": "vgpr_spill", "SGPRs Spill": "sgpr_spill", "LDS Size [bytes/block]": "lds",
+           "Occupancy [waves/SIMD]": "occupancy"}
+
+
+def resource_table():
+    """Markdown table of every kernel's resources as the compiler reports them."""
+    import re
+    rows = []
+    for src in SOURCES:
+        if not src.endswith(".hip"):
+            continue
+        cmd = [_hipcc(), *COMMON, "--cuda-device-only", "-c", "-x", "hip", os.path.join(CSRC, src),
+               "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        cur = None
+        for line in r.stderr.splitlines():
+            m = re.search(r"remark: Function Name: (\S+)", line)
+            if m:
+                cur = {"file": src, "name": m.group(1)}
+                rows.append(cur)
+                continue
+            m = re.search(r"remark:\s+(.+?): (\S+) \[-Rpass", line)
+            if m and cur is not None and m.group(1) in _FIELDS:
+                cur[_FIELDS[m.group(1)]] = m.group(2)
+    names = subprocess.run(["c++filt"], input="\n".join(r["name"] for r in rows), capture_output=True,
+                           text=True).stdout.splitlines()
+    out = ["| file | kernel | VGPRs | AGPRs | SGPRs | scratch B/lane | VGPR spill | SGPR spill | LDS B | waves/SIMD |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    for r, n in zip(rows, names):
+        n = n.replace("glu::(anonymous namespace)::", "").split("(")[0]
+        out.append(f"| {r['file']} | `{n}` | {r.get('vgpr')} | {r.get('agpr')} | {r.get('sgpr')} | {r.get('scratch')} | "
+                   f"{r.get('vgpr_spill')} | {r.get('sgpr_spill')} | {r.get('lds')} | {r.get('occupancy')} |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
-    print(LIB)
+    if "--resources" in sys.argv:
+        print(resource_table())
+    else:
+        build(verbose="-v" in sys.argv)
+        print(LIB)

@@ -18,16 +18,8 @@ constexpr int BF_THREADS = 256;
 template <int VEC>  // 16-byte vectors per operand per thread
 constexpr int64_t bf_chunk() { return (int64_t)BF_THREADS * VEC * 8; }  // elements per tile
 
-// Build-time tuning (fixed defaults; alternatives are compiled only to measure them):
-//   GLU_BF16_NT_LOADS: non-temporal (streaming) loads ([8192, 14336] GeGLU forward 122 vs
-//   130 us, backward 193 vs 206 us, with non-temporal stores).
-//   GLU_BF16_NT_STORES: -1 chooses per launch (below); 0 / 1 non-temporal stores off / on.
-#ifndef GLU_BF16_NT_LOADS
-#define GLU_BF16_NT_LOADS 1
-#endif
-#ifndef GLU_BF16_NT_STORES
-#define GLU_BF16_NT_STORES -1
-#endif
+// Loads are non-temporal (streaming): [8192, 14336] GeGLU forward 122 vs 130 us, backward 193
+// vs 206 us against ordinary loads (with non-temporal stores).
 // Per launch, by the bytes it writes against the 256 MiB last-level cache, and by direction
 // (same-box A/B with cold inputs, GeGLU, us):
 //   stores: non-temporal above 256 MiB, ordinary below (the cache absorbs them);
@@ -49,8 +41,7 @@ struct Uint4 {
 
 __device__ __forceinline__ Uint4 ld16(const uint16_t* p) {
   bu32x4 v;
-  if constexpr (GLU_BF16_NT_LOADS) v = __builtin_nontemporal_load(reinterpret_cast<const bu32x4*>(p));
-  else v = *reinterpret_cast<const bu32x4*>(p);
+  v = __builtin_nontemporal_load(reinterpret_cast<const bu32x4*>(p));
   return Uint4{{v.x, v.y, v.z, v.w}};
 }
 __device__ __forceinline__ void st16(uint32_t nt, uint16_t* p, uint32_t a, uint32_t b, uint32_t c,
@@ -224,7 +215,7 @@ hipError_t launch(const BF16Args& a, hipStream_t s) {
   const int64_t rows = a.flat ? 1 : a.M;
   const int64_t cols = a.flat ? a.M * a.N : a.N;
   const bool large = (BWD ? 2 : 1) * 2 * a.M * a.N > kBf16NtStoreBytes;
-  const uint32_t nt = GLU_BF16_NT_STORES < 0 ? large : GLU_BF16_NT_STORES == 1;
+  const uint32_t nt = large;
   auto go = [&](auto V) {
     constexpr int VEC = decltype(V)::value;
     const int64_t tpr = (cols + bf_chunk<VEC>() - 1) / bf_chunk<VEC>();

@@ -260,20 +260,25 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
   // lanes r, 16 + r, 32 + r, 48 + r.
   if constexpr (OUT == GEMM_F32) {
     // test hook: the pre-activation itself, [M, 2N] FP32
+    // one lane offset per 16-row slice; the gate/up half and the tile column are constants
+    // added to it, so no per-store address arithmetic is kept live across the stores
     const auto ry = rsrc(a.y);
+    const uint32_t pitch = 8u * N;  // bytes per row of y
+    const uint32_t base = (row0 + r) * pitch + 4u * (col0 + 4u * g);
 #pragma unroll
-    for (int h = 0; h < 2; h++)
+    for (int i = 0; i < WM; i++) {
+      const uint32_t oi = row0 + 16u * i + r < M ? base + 16u * i * pitch : kOob;
 #pragma unroll
-      for (int i = 0; i < WM; i++)
+      for (int h = 0; h < 2; h++)
 #pragma unroll
         for (int j = 0; j < WN; j++) {
-          const uint32_t row = row0 + 16u * i + r;
-          const uint32_t col = h * N + col0 + 16u * j + 4u * g;
           const v4f v = acc[h][i][j];
+          const uint32_t off = oi == kOob ? kOob : oi + 4u * N * h + 64u * j;
           __builtin_amdgcn_raw_buffer_store_b128((u32x4){__float_as_uint(v[0]), __float_as_uint(v[1]),
                                                          __float_as_uint(v[2]), __float_as_uint(v[3])},
-                                                 ry, row < M ? 4u * (row * 2u * N + col) : kOob, 0, 0);
+                                                 ry, off, 0, 0);
         }
+    }
   } else {
     // h = bf16(act(gate) * up), one 16-row slice i at a time (so that the slice's
     // accumulators die as it is written): the fast form for every element, then the tail

@@ -28,22 +28,11 @@ namespace {
 
 constexpr int NV_THREADS = 256;
 constexpr int64_t NV_TILE = 2048;  // operand columns per workgroup and group
-#ifndef GLU_NV_GROUPS              // build-time override, for measurements
-#define GLU_NV_GROUPS 2
-#endif
-
-// Build-time tuning (fixed defaults; alternatives are compiled only to measure them):
-//   GLU_NV_NT_LOADS / GLU_NV_NT_STORES: non-temporal (streaming) loads / code stores.
-//   GLU_AMAX_WGS: workgroups of the amax pass (each folds its maximum in with one atomic).
-#ifndef GLU_AMAX_WGS
-#define GLU_AMAX_WGS 1024
-#endif
-#ifndef GLU_NV_NT_LOADS  // -1: per direction (below)
-#define GLU_NV_NT_LOADS -1
-#endif
-#ifndef GLU_NV_NT_STORES
-#define GLU_NV_NT_STORES 0
-#endif
+constexpr int NV_FWD_GROUPS = 2;   // column groups per lane in the forward (one was slower)
+// Workgroups of the amax pass (each folds its maximum in with one atomic): a capped grid took
+// the pass from 97 to 88 us at [16384, 7168] and from 38 to 23 us at [968, 16384] against one
+// workgroup per tile, where fewer same-address atomics matter more than parallelism.
+constexpr int64_t kAmaxWorkgroups = 1024;
 
 enum { NV_FWD = 0, NV_BWD = 1, NV_F32 = 2, NV_FWD_GS = 3 };
 
@@ -55,7 +44,7 @@ struct Words4 {
 // backward [16384, 7168] 156.5 vs 166.2 us; GeGLU forward 122.8 vs 110.6 us there and 19.6 vs
 // 19.0 us at [968, 16384] (slower).
 template <bool BWD>
-constexpr bool nv_nt_loads() { return GLU_NV_NT_LOADS < 0 ? BWD : GLU_NV_NT_LOADS == 1; }
+constexpr bool nv_nt_loads() { return BWD; }
 template <bool NT>
 __device__ __forceinline__ Words4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0);
@@ -245,7 +234,7 @@ __device__ __forceinline__ void quant_store_bf16(const uint32_t p[4], __amdgpu_b
     word = fp4x2<3>(word, e2m1_operand(bf_lo(p[3]), R), e2m1_operand(bf_hi(p[3]), R));
   }
   if (nonfinite) word = 0;
-  __builtin_amdgcn_raw_buffer_store_b32(word, qr, live ? jq / 2 : kOob, 0, GLU_NV_NT_STORES ? 2 : 0);
+  __builtin_amdgcn_raw_buffer_store_b32(word, qr, live ? jq / 2 : kOob, 0, 0);
 
   const uint32_t blk = jq / 16;
   const uint32_t byte = live ? sc : 0u;  // padding rows and columns hold 0
@@ -384,7 +373,7 @@ hipError_t launch(const NvArgs& a, hipStream_t s) {
     if (tiles4 >= 16 * 256) return launch_g<ACT, LAYOUT, MODE, 4>(a, s);
     return launch_g<ACT, LAYOUT, MODE, 2>(a, s);
   } else {
-    return launch_g<ACT, LAYOUT, MODE, GLU_NV_GROUPS>(a, s);
+    return launch_g<ACT, LAYOUT, MODE, NV_FWD_GROUPS>(a, s);
   }
 }
 
@@ -448,7 +437,7 @@ hipError_t launch_glu_amax(const NvArgs& a, hipStream_t s) {
   if (e != hipSuccess || a.M == 0 || a.H == 0) return e;
   const int64_t tpr = (a.H + NV_TILE * 2 - 1) / (NV_TILE * 2);
   const int64_t ntiles = a.M * tpr;
-  const dim3 grid(grid_for(ntiles, GLU_AMAX_WGS)), block(NV_THREADS);
+  const dim3 grid(grid_for(ntiles, kAmaxWorkgroups)), block(NV_THREADS);
   return with_act(a.act, [&](auto A) {
     constexpr int ACT = decltype(A)::value;
     return a.layout == PAIRED ? launch_kernel(k_glu_amax<ACT, PAIRED>, grid, block, s, a, tpr, ntiles)
