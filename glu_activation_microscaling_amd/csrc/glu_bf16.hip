@@ -93,11 +93,11 @@ __device__ __forceinline__ void load1(const uint16_t* gate_row, const uint16_t* 
 
 template <int ACT, int LAYOUT, int BF_VEC>
 __global__ __launch_bounds__(BF_THREADS) void k_glu_fwd_bf16(BF16Args a, int64_t cols,
-                                                             int64_t tiles_per_row,
-                                                             int64_t ntiles, uint32_t nt) {
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int64_t row = t / tiles_per_row;
-    const int64_t j0 = (t - row * tiles_per_row) * bf_chunk<BF_VEC>();
+                                                             int64_t tiles_per_row, int64_t rows,
+                                                             uint32_t nt) {
+  for (int64_t row = blockIdx.y; row < rows; row += gridDim.y)
+  for (int64_t tc = blockIdx.x; tc < tiles_per_row; tc += gridDim.x) {
+    const int64_t j0 = tc * bf_chunk<BF_VEC>();
     const uint16_t* grow = a.gate + row * a.ld_in;
     const uint16_t* urow = (LAYOUT == SPLIT) ? a.up + row * a.ld_in : nullptr;
     uint16_t* hrow = a.out0 + row * a.ld_out;
@@ -139,11 +139,11 @@ __global__ __launch_bounds__(BF_THREADS) void k_glu_fwd_bf16(BF16Args a, int64_t
 
 template <int ACT, int LAYOUT, int BF_VEC>
 __global__ __launch_bounds__(BF_THREADS) void k_glu_bwd_bf16(BF16Args a, int64_t cols,
-                                                             int64_t tiles_per_row,
-                                                             int64_t ntiles, uint32_t nt) {
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int64_t row = t / tiles_per_row;
-    const int64_t j0 = (t - row * tiles_per_row) * bf_chunk<BF_VEC>();
+                                                             int64_t tiles_per_row, int64_t rows,
+                                                             uint32_t nt) {
+  for (int64_t row = blockIdx.y; row < rows; row += gridDim.y)
+  for (int64_t tc = blockIdx.x; tc < tiles_per_row; tc += gridDim.x) {
+    const int64_t j0 = tc * bf_chunk<BF_VEC>();
     const uint16_t* grow = a.gate + row * a.ld_in;
     const uint16_t* urow = (LAYOUT == SPLIT) ? a.up + row * a.ld_in : nullptr;
     const uint16_t* drow = a.dh + row * a.ld_dh;
@@ -219,12 +219,11 @@ hipError_t launch(const BF16Args& a, hipStream_t s) {
   auto go = [&](auto V) {
     constexpr int VEC = decltype(V)::value;
     const int64_t tpr = (cols + bf_chunk<VEC>() - 1) / bf_chunk<VEC>();
-    const int64_t ntiles = rows * tpr;
-    const dim3 grid(grid_for(ntiles, (int64_t)1 << 20)), block(BF_THREADS);
+    const dim3 grid = grid_2d(tpr, rows), block(BF_THREADS);
     if constexpr (BWD)
-      return launch_kernel(k_glu_bwd_bf16<ACT, LAYOUT, VEC>, grid, block, s, a, cols, tpr, ntiles, nt);
+      return launch_kernel(k_glu_bwd_bf16<ACT, LAYOUT, VEC>, grid, block, s, a, cols, tpr, rows, nt);
     else
-      return launch_kernel(k_glu_fwd_bf16<ACT, LAYOUT, VEC>, grid, block, s, a, cols, tpr, ntiles, nt);
+      return launch_kernel(k_glu_fwd_bf16<ACT, LAYOUT, VEC>, grid, block, s, a, cols, tpr, rows, nt);
   };
   if (BWD && large) return go(std::integral_constant<int, 2>{});
   return go(std::integral_constant<int, 1>{});

@@ -478,15 +478,19 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, const E2m1Thresholds& T) 
   return s | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
 }
 
-// E2M1 codes of x / S for inputs with at most 16 significant bits (every BF16 value):
-// y = x * rcp(S) is within 2^-22 of x / S, which for such x either is an E2M1 tie exactly
-// or lies at least 2^-8 (relative) away from every tie; rounding y to 16 significant bits
-// therefore restores the ties without moving any other value across one, and the
-// hardware E2M1 convert (nearest even, saturating at 6) then decides exactly.  R = 0 for
-// S = 0 gives signed zeros.
-__device__ __forceinline__ float e2m1_operand(float x, float R) {
-  const uint32_t b = __float_as_uint(x * R);
-  return __uint_as_float((b + 0x80u) & 0xffffff00u);
+// E2M1 codes of x / S for BF16-valued x and an E4M3 scale S, two at a time: y = x * R with R
+// within one FP32 ulp of 1 / S (the hardware reciprocal) is within 2^-22 of x / S, which for
+// such x either is an E2M1 tie exactly or lies at least 2^-8 (relative) away from every tie.
+// Rounding y to BF16 (8 significant bits, error at most 2^-9 relative) therefore restores the
+// ties without moving any other value onto or across one, and the hardware E2M1 convert of
+// the BF16 pair (nearest even, saturating at 6) decides exactly.  The whole domain (every
+// BF16 x, every finite E4M3 S, R = fl(1/S) and its two FP32 neighbours) is checked against
+// the exact quotient on the host.  R = 0 for S = 0 gives signed zeros.  The result goes into
+// nibbles 2 SEL and 2 SEL + 1 of `old`.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_of_quotients(uint32_t old, float x0, float x1, float R) {
+  const uint32_t y = pack_bf16(x0 * R, x1 * R);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(old, __builtin_bit_cast(v2bf16, y), 1.0f, SEL);
 }
 
 // Byte offset of NVFP4 scale (r, c) in the 128x4 layout; cp = padded scale columns.

@@ -372,9 +372,8 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
         for (int j = 0; j < WN; j++) {
           const uint32_t mj = j == 0 ? lo16(m01) : j == 1 ? hi16(m01) : j == 2 ? lo16(m23) : hi16(m23);
           const bool nonfinite = mj >= 0x7f80u;
-          float y[4];
           const float x[4] = {bf_lo(P[j][0]), bf_hi(P[j][0]), bf_lo(P[j][1]), bf_hi(P[j][1])};
-          uint32_t sc;
+          uint32_t sc, word;
           if constexpr (OUT >= GEMM_NV_GS_ROWMAJOR) {
             // two-level: E4M3(fl(bamax * k)), saturating at 448; codes E2M1(fl(x * fl(s / S)))
             const float d = __builtin_fminf(__uint_as_float(mj << 16) * gs.k, 448.0f);
@@ -382,19 +381,21 @@ __global__ __launch_bounds__(GM_THREADS) void k_glu_gemm(GemmArgs a, uint32_t ti
             const float S = e4m3_value(nonfinite ? 0u : sc);
             const float rs_ = S > 0.0f ? gs.s / S : 0.0f;   // IEEE division
             // |x * rs_| beyond 8 saturates to 6 either way; the clamp keeps the input finite
+            float y[4];
 #pragma unroll
             for (int e = 0; e < 4; e++) y[e] = nonfinite ? 0.0f : __builtin_amdgcn_fmed3f(x[e] * rs_, -8.0f, 8.0f);
+            word = fp4x2<0>(0u, y[0], y[1]);
+            word = fp4x2<1>(word, y[2], y[3]);
           } else {
             sc = nonfinite ? 0x7fu : nv_scale_code_bf16(__uint_as_float(mj << 16));
             const float S = e4m3_value(nonfinite ? 0u : sc);
             const float R = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; e++) y[e] = nonfinite ? 0.0f : e2m1_operand(x[e], R);
+            word = fp4x2_of_quotients<0>(0u, x[0], x[1], R);
+            word = fp4x2_of_quotients<1>(word, x[2], x[3], R);
+            if (nonfinite) word = 0u;
           }
           sbs |= sc << (8 * j);
           // (a block holding NaN or Inf gets scale 0x7F and zero codes)
-          uint32_t word = fp4x2<0>(0u, y[0], y[1]);
-          word = fp4x2<1>(word, y[2], y[3]);
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)word, rq, ok ? (row * N + cl + 16u * j) / 2u : kOob, 0, 0);
         }
         // the row's four scale bytes of this wave, blocks col0 / 16 .. + 3, as one word

@@ -133,4 +133,15 @@ inline unsigned grid_for(int64_t units, int64_t cap) {
   return (unsigned)(units < cap ? units : cap);
 }
 
+// Grid of a launch over `rows` rows of `tiles_per_row` tiles each: x walks the tiles of a row,
+// y the rows, each dimension with a grid-stride loop past its cap, so kernels find their tile
+// without dividing.  At most `cap` workgroups in all (x first).
+inline dim3 grid_2d(int64_t tiles_per_row, int64_t rows, int64_t cap = (int64_t)1 << 26) {
+  int64_t x = tiles_per_row < 1 ? 1 : (tiles_per_row < ((int64_t)1 << 20) ? tiles_per_row : (int64_t)1 << 20);
+  if (x > cap) x = cap;
+  int64_t y = rows < 1 ? 1 : (rows < 65535 ? rows : 65535);
+  if (x * y > cap) y = cap / x;
+  return dim3((unsigned)x, (unsigned)y);
+}
+
 }  // namespace glu

@@ -228,10 +228,10 @@ __device__ __forceinline__ void quant_store_bf16(const uint32_t p[4], __amdgpu_b
     sc = nonfinite ? 0x7fu : nv_scale_code_bf16(__uint_as_float(m << 16));
     const float S = e4m3_value(nonfinite ? 0u : sc);
     const float R = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
-    word = fp4x2<0>(word, e2m1_operand(bf_lo(p[0]), R), e2m1_operand(bf_hi(p[0]), R));
-    word = fp4x2<1>(word, e2m1_operand(bf_lo(p[1]), R), e2m1_operand(bf_hi(p[1]), R));
-    word = fp4x2<2>(word, e2m1_operand(bf_lo(p[2]), R), e2m1_operand(bf_hi(p[2]), R));
-    word = fp4x2<3>(word, e2m1_operand(bf_lo(p[3]), R), e2m1_operand(bf_hi(p[3]), R));
+    word = fp4x2_of_quotients<0>(word, bf_lo(p[0]), bf_hi(p[0]), R);
+    word = fp4x2_of_quotients<1>(word, bf_lo(p[1]), bf_hi(p[1]), R);
+    word = fp4x2_of_quotients<2>(word, bf_lo(p[2]), bf_hi(p[2]), R);
+    word = fp4x2_of_quotients<3>(word, bf_lo(p[3]), bf_hi(p[3]), R);
   }
   if (nonfinite) word = 0;
   __builtin_amdgcn_raw_buffer_store_b32(word, qr, live ? jq / 2 : kOob, 0, 0);
@@ -299,15 +299,15 @@ __device__ __forceinline__ void quant_store_f32(const float v[8], __amdgpu_buffe
 // WORD_SCALES as for quant_store_bf16 (the backward needs H % 64 == 0 for it).
 template <int ACT, int LAYOUT, int SFL, int MODE, bool WORD_SCALES, int NV_GROUPS>
 __global__ __launch_bounds__(NV_THREADS) void k_nvfp4(NvArgs a, int64_t tiles_per_row,
-                                                      int64_t ntiles, NvOut o) {
+                                                      int64_t rows, NvOut o) {
   const int lane = threadIdx.x & 63;
   const uint32_t H = (uint32_t)a.H;
   const uint32_t nb = (uint32_t)o.scale_cols, cp = (uint32_t)o.scale_cols_padded;
   GlobalScale gs;
   if constexpr (MODE == NV_FWD_GS) gs = global_scale(*a.amax);
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int64_t row = t / tiles_per_row;
-    const uint32_t j0 = (uint32_t)(t - row * tiles_per_row) * (uint32_t)(NV_TILE * NV_GROUPS) + threadIdx.x * 8u;
+  for (int64_t row = blockIdx.y; row < rows; row += gridDim.y)
+  for (int64_t tc = blockIdx.x; tc < tiles_per_row; tc += gridDim.x) {
+    const uint32_t j0 = (uint32_t)tc * (uint32_t)(NV_TILE * NV_GROUPS) + threadIdx.x * 8u;
     const bool row_ok = row < a.M;
     const RowIn in = row_in<LAYOUT, MODE>(a, row_ok ? row : 0);
     Raw8 raw[NV_GROUPS];
@@ -354,14 +354,13 @@ hipError_t launch_g(const NvArgs& a, hipStream_t s) {
   const NvOut o{width / 2, nb, (nb + 3) / 4 * 4};
   const int64_t rows = a.sf_layout == SF_128x4 ? (a.M + 127) / 128 * 128 : a.M;
   const int64_t tpr = (a.H + NV_TILE * G - 1) / (NV_TILE * G);
-  const int64_t ntiles = rows * tpr;
-  const dim3 grid(grid_for(ntiles, (int64_t)1 << 20)), block(NV_THREADS);
+  const dim3 grid = grid_2d(tpr, rows), block(NV_THREADS);
   const bool word = MODE != NV_BWD || a.H % 64 == 0;  // db's blocks start on a 4-block boundary
   if (a.sf_layout == SF_128x4) {
-    if (word) return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_128x4, MODE, true, G>, grid, block, s, a, tpr, ntiles, o);
-    return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_128x4, MODE, false, G>, grid, block, s, a, tpr, ntiles, o);
+    if (word) return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_128x4, MODE, true, G>, grid, block, s, a, tpr, rows, o);
+    return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_128x4, MODE, false, G>, grid, block, s, a, tpr, rows, o);
   }
-  return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_ROWMAJOR, MODE, true, G>, grid, block, s, a, tpr, ntiles, o);
+  return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_ROWMAJOR, MODE, true, G>, grid, block, s, a, tpr, rows, o);
 }
 
 // Groups per lane.  The backward takes 4 (more loads in flight per wave) when that still
@@ -388,14 +387,13 @@ __global__ void k_zero_u32(uint32_t* p) {
 }
 
 template <int ACT, int LAYOUT>
-__global__ __launch_bounds__(NV_THREADS) void k_glu_amax(NvArgs a, int64_t tiles_per_row,
-                                                         int64_t ntiles) {
+__global__ __launch_bounds__(NV_THREADS) void k_glu_amax(NvArgs a, int64_t tiles_per_row) {
   constexpr int G = 2;
   const uint32_t H = (uint32_t)a.H;
   uint32_t m = 0;
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int64_t row = t / tiles_per_row;
-    const uint32_t j0 = (uint32_t)(t - row * tiles_per_row) * (uint32_t)(NV_TILE * G) + threadIdx.x * 8u;
+  for (int64_t row = blockIdx.y; row < a.M; row += gridDim.y)
+  for (int64_t tc = blockIdx.x; tc < tiles_per_row; tc += gridDim.x) {
+    const uint32_t j0 = (uint32_t)tc * (uint32_t)(NV_TILE * G) + threadIdx.x * 8u;
     const RowIn in = row_in<LAYOUT, NV_FWD>(a, row);
     Raw8 raw[G];
 #pragma unroll
@@ -436,12 +434,11 @@ hipError_t launch_glu_amax(const NvArgs& a, hipStream_t s) {
   hipError_t e = launch_kernel(k_zero_u32, dim3(1), dim3(64), s, reinterpret_cast<uint32_t*>(a.amax_out));
   if (e != hipSuccess || a.M == 0 || a.H == 0) return e;
   const int64_t tpr = (a.H + NV_TILE * 2 - 1) / (NV_TILE * 2);
-  const int64_t ntiles = a.M * tpr;
-  const dim3 grid(grid_for(ntiles, kAmaxWorkgroups)), block(NV_THREADS);
+  const dim3 grid = grid_2d(tpr, a.M, kAmaxWorkgroups), block(NV_THREADS);
   return with_act(a.act, [&](auto A) {
     constexpr int ACT = decltype(A)::value;
-    return a.layout == PAIRED ? launch_kernel(k_glu_amax<ACT, PAIRED>, grid, block, s, a, tpr, ntiles)
-                              : launch_kernel(k_glu_amax<ACT, SPLIT>, grid, block, s, a, tpr, ntiles);
+    return a.layout == PAIRED ? launch_kernel(k_glu_amax<ACT, PAIRED>, grid, block, s, a, tpr)
+                              : launch_kernel(k_glu_amax<ACT, SPLIT>, grid, block, s, a, tpr);
   });
 }
 

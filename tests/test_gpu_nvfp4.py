@@ -280,3 +280,35 @@ def test_amax_nan_and_empty(gpu):
     e = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
     a = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
     assert gpu.glu_amax(e, e, out=a).item() == 0.0
+
+
+def test_every_bf16_value_under_every_scale_fused(gpu):
+    """Rule 1 through the fused NVFP4 forward for every BF16 value under every E4M3 block scale:
+    for each positive finite E4M3 value S a set of 16-element blocks has the maximum 6 S (so
+    the block scale is S) and runs through every BF16 magnitude up to 6 S with random signs.
+    ReLU^2 with gate = 1 makes h = up exactly; codes and scales (both layouts) equal the
+    oracle quantizer of the device's own h byte for byte."""
+    rng = np.random.default_rng(91)
+    mags = np.arange(1, 0x7F80, dtype=np.uint32)
+    mvals = (mags << 16).view(np.float32).astype(np.float64)
+    blocks = []
+    for S in oracle.e4m3_to_f64(np.arange(1, 0x7F, dtype=np.uint8)):
+        body = mags[mvals <= 6.0 * S]
+        body = body | (rng.integers(0, 2, body.size, dtype=np.uint32) << 15)
+        n = -(-body.size // 15)
+        body = np.resize(body, n * 15).reshape(n, 15)
+        head = np.full((n, 1), int(np.float32(6.0 * S).view(np.uint32) >> 16), np.uint32)
+        blocks.append(np.concatenate([head | (rng.integers(0, 2, (n, 1), dtype=np.uint32) << 15), body], axis=1))
+    X = np.concatenate(blocks).astype(np.uint16)
+    pad = (-X.shape[0]) % 64
+    X = np.concatenate([X, np.zeros((pad, 16), np.uint16)]).reshape(-1, 1024)
+    x = si.from_bits(X).cuda()
+    one = torch.ones_like(x)
+    h = bits(gpu.glu_fwd(one, x, act="relu2"))
+    assert np.array_equal(h, X), "h = up"
+    hf = si.from_bits(X).float().numpy()
+    for name, code in SFL:
+        q, sf = gpu.glu_fwd_nvfp4(one, x, act="relu2", layout="split", sf_layout=name)
+        oq, osf = oracle.quant_nvfp4(hf, code)
+        assert np.array_equal(u8(sf).ravel(), osf.ravel()), f"scales ({name})"
+        assert np.array_equal(u8(q), oq), f"codes ({name})"
