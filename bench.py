@@ -511,7 +511,11 @@ def main():
                     help="skip the validation of each timed configuration before it is timed")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also launch one 1 GiB device copy (for scaling HBM counters)")
+                    help="also launch the streaming probe as a 1 GiB copy (a kernel of known bytes, "
+                         "for scaling HBM counters)")
+    ap.add_argument("--bf16-only", action="store_true",
+                    help="only launch the GeGLU BF16 forward and backward at [8192, 14336] three times "
+                         "each and print no JSON (a target for profiler counter passes)")
     ap.add_argument("--nvfp4-only", action="store_true",
                     help="only launch the NVFP4 forward and backward at [16384, 7168] three times "
                          "each and print no JSON (a target for profiler counter passes)")
@@ -535,6 +539,13 @@ def main():
     glu.lib()  # fail loudly when the HIP library is missing
     validate = not args.no_validate
 
+    def calibrate():
+        """The streaming probe as a 1 GiB copy: a kernel of known bytes for counter scaling."""
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        glu.glu_stream_probe([src], [dst])
+        torch.cuda.synchronize()
+
     M, N = 16384, 7168
     if args.nvfp4_only:
         g, u, d = si.normal_bf16_device([(M, N)] * 3, seed=1, outliers=True)
@@ -545,7 +556,22 @@ def main():
             glu.glu_fwd_nvfp4(x, act="swiglu", layout="paired", sf_layout="128x4", out=of)
             glu.glu_bwd_nvfp4(g, u, d, act="swiglu", sf_layout="128x4", out=ob)
         torch.cuda.synchronize()
+        if args.copy_calibration:
+            calibrate()
         print("[bench] nvfp4 launches done", file=sys.stderr, flush=True)
+        return
+    if args.bf16_only:
+        R, W = 8192, 14336
+        g, u, d = si.normal_bf16_device([(R, W)] * 3, seed=2)
+        h = torch.empty(R, W, dtype=torch.bfloat16, device="cuda")
+        da, db = torch.empty_like(h), torch.empty_like(h)
+        for _ in range(3):
+            glu.glu_fwd(g, u, act="geglu", out=h)
+            glu.glu_bwd(g, u, d, act="geglu", out=(da, db))
+        torch.cuda.synchronize()
+        if args.copy_calibration:
+            calibrate()
+        print("[bench] bf16 launches done", file=sys.stderr, flush=True)
         return
     if args.gemm_only:
         for gm, gn, gk in ((8192, 2048, 7168), (16384, 7168, 2048)):
@@ -596,11 +622,7 @@ def main():
     value = (fwd_b + bwd_b) / (ms_per_step * 1e-3) / 1e9
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibrate()
     del sets, fo, bo
     torch.cuda.empty_cache()
 
