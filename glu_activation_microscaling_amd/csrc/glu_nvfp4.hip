@@ -19,7 +19,8 @@
 // The row is uniform in a workgroup, so every row-dependent address is formed once on the
 // scalar unit as a buffer descriptor base; lanes add 32-bit offsets, and a lane outside the
 // matrix passes kOob (loads return zeros, stores are dropped), so every path issues the same
-// memory instructions.  The host keeps the operand width below 2^28 columns.
+// memory instructions.  The host keeps the quantized width at most 2^26 columns, so every
+// lane offset stays below 2^28 bytes.
 #include "glu_device.h"
 #include "glu_launch.h"
 
