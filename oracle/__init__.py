@@ -52,9 +52,9 @@ _SIGNATURES = {
     "orc_quant_nvfp4_gs": (None, [_i64, _i64, _p, ctypes.c_float, _p, _p, _int]),
     "orc_glu_amax": (ctypes.c_float, [_int, _int, _i64, _i64, _p, _p, _i64, _p]),
     "orc_glu_fwd_nvfp4_gs": (_int, [_int, _int, _i64, _i64, _p, _p, _i64, ctypes.c_float, _p, _p, _int]),
-    "orc_mx_gemm_nt": (None, [_i64, _i64, _i64, _p, _p, _p, _p, _p]),
-    "orc_glu_gemm": (_int, [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
-    "orc_glu_gemm_mxfp8": (_int, [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p]),
+    "orc_mx_gemm_nt": (None, [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
+    "orc_glu_gemm": (_int, [_int, _int, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
+    "orc_glu_gemm_mxfp8": (_int, [_int, _int, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p]),
     "orc_bf16_from_f64_array": (None, [_p, _i64, _p]),
     "orc_e4m3_from_f64_array": (None, [_p, _i64, _p]),
     "orc_e2m1_from_f64_array": (None, [_p, _i64, _p]),
@@ -330,40 +330,50 @@ def glu_fwd_nvfp4_gs(kind, gate, up=None, amax=None, layout=PAIRED, sf_layout=SF
     return q, sf
 
 
-# ---- merged gate/up MXFP8 GEMM with the GLU epilogue ----------------------------------
+# ---- merged gate/up block-scaled GEMM with the GLU epilogue -----------------------------
 
-def _gemm_operands(Xq, Xs, Wq, Ws):
+FMT_E4M3, FMT_E2M1 = 0, 1   # operand codes: MXFP8 (one per byte) or MXFP4 (two per byte)
+
+
+def _gemm_operands(Xq, Xs, Wq, Ws, fmt):
     Xq, Xs, Wq, Ws = (_c(a, np.uint8) for a in (Xq, Xs, Wq, Ws))
-    M, K = Xq.shape
+    M, rb = Xq.shape
+    K = 2 * rb if fmt == FMT_E2M1 else rb
     N2 = Wq.shape[0]
-    if Wq.shape[1] != K or Xs.shape != (M, K // 32) or Ws.shape != (N2, K // 32) or K % 32:
+    if fmt not in (FMT_E4M3, FMT_E2M1) or Wq.shape[1] != rb or Xs.shape != (M, K // 32) \
+            or Ws.shape != (N2, K // 32) or K % 32:
         raise ValueError("operand shapes")
     return Xq, Xs, Wq, Ws, M, N2, K
 
 
-def mx_gemm_nt(Xq, Xs, Wq, Ws):
-    """Y = X W^T in float64 from MXFP8 codes and E8M0 scales (blocks of 32 along K)."""
-    Xq, Xs, Wq, Ws, M, N2, K = _gemm_operands(Xq, Xs, Wq, Ws)
+def mx_gemm_nt(Xq, Xs, Wq, Ws, fmt=FMT_E4M3):
+    """Y = X W^T in float64 from block-scaled codes (E4M3 codes [rows, K], or E2M1 codes packed
+    [rows, K/2] with element 2j in the low nibble) and E8M0 scales (blocks of 32 along K).
+    Y keeps W's row order."""
+    Xq, Xs, Wq, Ws, M, N2, K = _gemm_operands(Xq, Xs, Wq, Ws, fmt)
     Y = np.empty((M, N2), np.float64)
-    _load().orc_mx_gemm_nt(M, N2, K, _ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(Y))
+    _load().orc_mx_gemm_nt(fmt, M, N2, K, _ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(Y))
     return Y
 
 
-def glu_gemm(kind, Xq, Xs, Wq, Ws):
-    """BF16 bits of h = act(Y_gate) * Y_up, W = [W_gate | W_up]."""
-    Xq, Xs, Wq, Ws, M, N2, K = _gemm_operands(Xq, Xs, Wq, Ws)
+def glu_gemm(kind, Xq, Xs, Wq, Ws, fmt=FMT_E4M3, w_layout=SPLIT):
+    """BF16 bits of h = act(Y_gate) * Y_up; W = [W_gate | W_up] (SPLIT) or pairwise-interleaved
+    gate/up rows (PAIRED)."""
+    Xq, Xs, Wq, Ws, M, N2, K = _gemm_operands(Xq, Xs, Wq, Ws, fmt)
     h = np.empty((M, N2 // 2), np.uint16)
-    if _load().orc_glu_gemm(kind, M, N2 // 2, K, _ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(h)) != 0:
+    if _load().orc_glu_gemm(kind, fmt, w_layout, M, N2 // 2, K, _ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws),
+                            _ptr(h)) != 0:
         raise MemoryError("oracle ran out of host memory")
     return h
 
 
-def glu_gemm_mxfp8(kind, Xq, Xs, Wq, Ws):
+def glu_gemm_mxfp8(kind, Xq, Xs, Wq, Ws, fmt=FMT_E4M3, w_layout=SPLIT):
     """(q_row [M, N], s_row [M, N/32]): h of glu_gemm quantized MXFP8 rowwise."""
-    Xq, Xs, Wq, Ws, M, N2, K = _gemm_operands(Xq, Xs, Wq, Ws)
+    Xq, Xs, Wq, Ws, M, N2, K = _gemm_operands(Xq, Xs, Wq, Ws, fmt)
     N = N2 // 2
     q = np.empty((M, N), np.uint8)
     sc = np.empty((M, N // 32), np.uint8)
-    if _load().orc_glu_gemm_mxfp8(kind, M, N, K, _ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(q), _ptr(sc)) != 0:
+    if _load().orc_glu_gemm_mxfp8(kind, fmt, w_layout, M, N, K, _ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws),
+                                  _ptr(q), _ptr(sc)) != 0:
         raise MemoryError("oracle ran out of host memory")
     return q, sc

@@ -47,8 +47,12 @@
  *     (the GEMM-ready block-scale layout; no page fixes one for MXFP8);
  *   - an NVFP4 backward quantizes [da | db] as one [M, 2N] matrix in 16-element
  *     row blocks, the MXFP8 backward's placement (no page defines one);
- *   - the GEMM epilogue form takes MXFP8 operands (E8M0 scales per 32 along K, the
- *     block scaling gfx950's matrix cores take) and W = [W_gate | W_up];
+ *   - the GEMM epilogue form takes block-scaled operands with E8M0 scales per 32
+ *     along K (the block scaling gfx950's matrix cores take): E4M3 codes (MXFP8), or
+ *     E2M1 codes packed two per byte, even element in the low nibble (MXFP4, the
+ *     closest form of [NV]'s packed E2M1 operands); W = [W_gate | W_up] or, as [NV]
+ *     Supported contract's weight layout row fixes, pairwise-interleaved gate/up
+ *     rows (gate0, up0, gate1, up1, ...);
  *   - two-level NVFP4 (a global scale from the tensor's amax, relaxing [NV]'s global
  *     scale 1) is defined by IEEE FP32 operations: s = 2688 / amax (capped at
  *     2^100), block scale E4M3(bamax * fl(s / 6)), codes E2M1(x * fl(s / S)).
@@ -618,12 +622,25 @@ int orc_glu_fwd_nvfp4_gs(int act, int layout, int64_t M, int64_t H, const uint16
 /* E8M0 scale byte -> 2^(b - 127); 0xFF is NaN. */
 static double e8m0(uint8_t b) { return b == 0xFF ? NAN : ldexp(1.0, (int)b - 127); }
 
-/* Y = X W^T in binary64: X is [M, K] E4M3 codes with E8M0 scales [M, K/32] (32-element
- * blocks along K), W is [N2, K] codes with scales [N2, K/32].  Every product of two decoded
- * values is exact in binary64; the sum runs over k in order. */
-void orc_mx_gemm_nt(int64_t M, int64_t N2, int64_t K, const uint8_t* Xq, const uint8_t* Xs,
-                    const uint8_t* Wq, const uint8_t* Ws, double* Y) {
-  const int64_t kb = K / 32;
+enum { ORC_FMT_E4M3 = 0, ORC_FMT_E2M1 = 1 };
+
+/* Decoded code of element k of a GEMM operand row: E4M3 one per byte, or E2M1 two per byte
+ * with element 2j in the low nibble of byte j. */
+static double operand_code(int fmt, const uint8_t* row, int64_t k) {
+  if (fmt == ORC_FMT_E2M1) {
+    const uint8_t b = row[k / 2];
+    return orc_e2m1_to_f64((uint8_t)((k & 1) ? b >> 4 : b & 15));
+  }
+  return orc_e4m3_to_f64(row[k]);
+}
+
+/* Y = X W^T in binary64: X is [M, K] codes with E8M0 scales [M, K/32] (32-element blocks
+ * along K), W is [N2, K] codes with scales [N2, K/32]; codes in format fmt (a row of K
+ * elements takes K bytes for E4M3, K/2 for E2M1).  Every product of two decoded values is
+ * exact in binary64; the sum runs over k in order.  Y keeps W's row order. */
+void orc_mx_gemm_nt(int fmt, int64_t M, int64_t N2, int64_t K, const uint8_t* Xq,
+                    const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws, double* Y) {
+  const int64_t kb = K / 32, rb = fmt == ORC_FMT_E2M1 ? K / 2 : K;
 #pragma omp parallel for schedule(static)
   for (int64_t m = 0; m < M; m++)
     for (int64_t n = 0; n < N2; n++) {
@@ -632,35 +649,42 @@ void orc_mx_gemm_nt(int64_t M, int64_t N2, int64_t K, const uint8_t* Xq, const u
         const double sx = e8m0(Xs[m * kb + b]), sw = e8m0(Ws[n * kb + b]);
         double blk = 0.0;
         for (int64_t k = 32 * b; k < 32 * b + 32; k++)
-          blk += orc_e4m3_to_f64(Xq[m * K + k]) * orc_e4m3_to_f64(Wq[n * K + k]);
+          blk += operand_code(fmt, Xq + m * rb, k) * operand_code(fmt, Wq + n * rb, k);
         acc += blk * sx * sw;
       }
       Y[m * N2 + n] = acc;
     }
 }
 
-/* h = bf16(act(Y[:, j]) * Y[:, N + j]) with Y = X W^T, W = [W_gate | W_up] ([2N, K] rows:
- * gate then up).  One rounding, from binary64. */
-int orc_glu_gemm(int act, int64_t M, int64_t N, int64_t K, const uint8_t* Xq, const uint8_t* Xs,
-                 const uint8_t* Wq, const uint8_t* Ws, uint16_t* h) {
+/* Columns of Y = X W^T holding gate and up output j: W = [W_gate | W_up] puts them at j and
+ * N + j; pairwise-interleaved W rows at 2j and 2j + 1. */
+static int64_t gate_col(int w_layout, int64_t j) { return w_layout == ORC_PAIRED ? 2 * j : j; }
+static int64_t up_col(int w_layout, int64_t N, int64_t j) { return w_layout == ORC_PAIRED ? 2 * j + 1 : N + j; }
+
+/* h = bf16(act(Y_gate) * Y_up) with Y = X W^T, W [2N, K] in w_layout.  One rounding, from
+ * binary64. */
+int orc_glu_gemm(int act, int fmt, int w_layout, int64_t M, int64_t N, int64_t K,
+                 const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                 uint16_t* h) {
   double* Y = (double*)malloc((size_t)(M * 2 * N) * sizeof(double));
   if (!Y) return -1;
-  orc_mx_gemm_nt(M, 2 * N, K, Xq, Xs, Wq, Ws, Y);
+  orc_mx_gemm_nt(fmt, M, 2 * N, K, Xq, Xs, Wq, Ws, Y);
 #pragma omp parallel for schedule(static)
   for (int64_t m = 0; m < M; m++)
     for (int64_t j = 0; j < N; j++)
-      h[m * N + j] = orc_bf16_from_f64(orc_act(act, Y[m * 2 * N + j]) * Y[m * 2 * N + N + j]);
+      h[m * N + j] = orc_bf16_from_f64(orc_act(act, Y[m * 2 * N + gate_col(w_layout, j)]) *
+                                       Y[m * 2 * N + up_col(w_layout, N, j)]);
   free(Y);
   return 0;
 }
 
 /* The same with h quantized to MXFP8 rowwise (1x32 blocks along N). */
-int orc_glu_gemm_mxfp8(int act, int64_t M, int64_t N, int64_t K, const uint8_t* Xq,
-                       const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws, uint8_t* q_row,
-                       uint8_t* s_row) {
+int orc_glu_gemm_mxfp8(int act, int fmt, int w_layout, int64_t M, int64_t N, int64_t K,
+                       const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                       uint8_t* q_row, uint8_t* s_row) {
   uint16_t* h = (uint16_t*)malloc((size_t)(M * N) * sizeof(uint16_t));
   if (!h) return -1;
-  if (orc_glu_gemm(act, M, N, K, Xq, Xs, Wq, Ws, h) != 0) {
+  if (orc_glu_gemm(act, fmt, w_layout, M, N, K, Xq, Xs, Wq, Ws, h) != 0) {
     free(h);
     return -1;
   }

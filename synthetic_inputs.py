@@ -17,6 +17,11 @@ Workloads (shapes and value distributions of the pages' benchmarks):
                     (torch's float8_e4m3fn cast, clamped to +-448) and E8M0 block scales
                     (one per 32 along K) drawn uniformly from 2^-9 .. 2^-5, the range a
                     block of N(0, 1) data quantized to E4M3 takes.
+  * mxfp4_operand : an MXFP4 GEMM operand: E2M1 codes [rows, K] packed two per byte
+                    (element 2j in the low nibble), each code's magnitude drawn from the
+                    eight E2M1 magnitudes with the frequencies a block of N(0, 1) data
+                    scaled to a block maximum of 6 puts on them, a uniform sign, and E8M0
+                    block scales drawn uniformly from 2^-5 .. 2^-1.
 Draw order within one call: gate, up, dh (then the outlier masks, in the same order).
 """
 import numpy as np
@@ -108,3 +113,30 @@ def mx_operand(rows, K, seed=0, device="cpu"):
     codes = v.to(torch.float8_e4m3fn).view(torch.uint8)
     scales = torch.randint(118, 123, (rows, K // 32), generator=g, dtype=torch.uint8)
     return codes.to(device), scales.to(device)
+
+
+# Frequencies of the E2M1 magnitude codes 0..7 (0, 0.5, 1, 1.5, 2, 3, 4, 6) for N(0, 1) blocks
+# of 32 scaled so that the block maximum sits near 6 (a fixed table: the draw itself does no
+# rounding).
+_E2M1_MAG_FREQ = (0.10, 0.20, 0.19, 0.16, 0.13, 0.13, 0.06, 0.03)
+
+
+def mxfp4_operand(rows, K, seed=0, device="cpu"):
+    """(packed E2M1 codes uint8 [rows, K / 2], E8M0 scales uint8 [rows, K / 32]) as torch
+    tensors: per element a magnitude code drawn with _E2M1_MAG_FREQ and a uniform sign bit,
+    two codes per byte with element 2j in the low nibble; scale bytes uniform in 122 .. 126
+    (2^-5 .. 2^-1).  Drawn on the host generator, then moved."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    mag = torch.multinomial(torch.tensor(_E2M1_MAG_FREQ), rows * K, replacement=True, generator=g)
+    sign = torch.randint(0, 2, (rows * K,), generator=g)
+    codes = (mag | (sign << 3)).to(torch.uint8).reshape(rows, K // 2, 2)
+    packed = codes[:, :, 0] | (codes[:, :, 1] << 4)
+    scales = torch.randint(122, 127, (rows, K // 32), generator=g, dtype=torch.uint8)
+    return packed.contiguous().to(device), scales.to(device)
+
+
+def interleave_rows(w):
+    """[2N, ...] = [gate rows | up rows] -> pairwise-interleaved rows gate0, up0, gate1, up1,
+    ... (a permutation)."""
+    n = w.shape[0] // 2
+    return torch.stack([w[:n], w[n:]], dim=1).reshape(w.shape).contiguous()

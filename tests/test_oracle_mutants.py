@@ -79,8 +79,14 @@ MUTANTS = [
      "const float r = S == 0.0f ? 0.0f : S / s;", [tq.test_nv_gs_blocks_against_brute_force]),
     ("GEMM scale bias", "ldexp(1.0, (int)b - 127)", "ldexp(1.0, (int)b - 126)",
      [tq.test_mx_gemm_closed_forms]),
-    ("GEMM epilogue gate and up swapped", "orc_act(act, Y[m * 2 * N + j]) * Y[m * 2 * N + N + j]",
-     "orc_act(act, Y[m * 2 * N + N + j]) * Y[m * 2 * N + j]", [tq.test_glu_gemm_is_glu_of_the_gemm]),
+    ("GEMM epilogue gate column off by one", "return w_layout == ORC_PAIRED ? 2 * j : j;",
+     "return w_layout == ORC_PAIRED ? 2 * j : j + 1;", [tq.test_glu_gemm_is_glu_of_the_gemm]),
+    ("GEMM interleaved W: gate and up rows swapped", "return w_layout == ORC_PAIRED ? 2 * j + 1 : N + j;",
+     "return w_layout == ORC_PAIRED ? 2 * j : N + j;", [tq.test_glu_gemm_interleaved_w_rows]),
+    ("E2M1 operand row pitch", "rb = fmt == ORC_FMT_E2M1 ? K / 2 : K;", "rb = K;",
+     [tq.test_mx_gemm_e2m1_matches_numpy_on_dequantized_operands]),
+    ("E2M1 operand read as E4M3", "if (fmt == ORC_FMT_E2M1) {", "if (0) {",
+     [tq.test_mx_gemm_e2m1_closed_forms]),
     ("GEMM drops a block's scale", "acc += blk * sx * sw;", "acc += blk * sx;",
      [tq.test_mx_gemm_matches_numpy_on_dequantized_operands]),
     ("NV scale divisor", "amax / 6.0", "amax / 4.0", [tq.test_nv_golden_blocks]),

@@ -392,6 +392,63 @@ def test_glu_gemm_is_glu_of_the_gemm():
         assert np.array_equal(q, o[0]) and np.array_equal(sc, o[1])
 
 
+def _dequant_rows_e2m1(q, s):
+    """Packed E2M1 rows [R, K/2] (element 2j in the low nibble) with E8M0 scales -> float64
+    [R, K], decoded one nibble at a time with the E2M1 table (pinned in test_oracle_formats)."""
+    q = np.asarray(q)
+    codes = np.empty((q.shape[0], 2 * q.shape[1]), np.uint8)
+    codes[:, 0::2], codes[:, 1::2] = q & 0xF, q >> 4
+    v = oracle.e2m1_to_f64(codes).reshape(codes.shape)
+    return v * np.repeat(np.exp2(np.asarray(s, np.float64) - 127.0), 32, axis=1)
+
+
+def test_mx_gemm_e2m1_matches_numpy_on_dequantized_operands():
+    """MXFP4 operands: the oracle's loop equals numpy's matmul of the operands decoded nibble
+    by nibble (a library routine), to binary64 summation-order error."""
+    Xq, Xs = (t.numpy() for t in si.mxfp4_operand(48, 256, seed=61))
+    Wq, Ws = (t.numpy() for t in si.mxfp4_operand(80, 256, seed=62))
+    Y = oracle.mx_gemm_nt(Xq, Xs, Wq, Ws, fmt=oracle.FMT_E2M1)
+    ref = _dequant_rows_e2m1(Xq, Xs) @ _dequant_rows_e2m1(Wq, Ws).T
+    assert np.allclose(Y, ref, rtol=1e-12, atol=0)
+
+
+def test_mx_gemm_e2m1_closed_forms():
+    """E2M1 code 0x2 = 1 and 0x4 = 2, so byte 0x22 packs two ones and 0x44 two twos: a 32-long
+    dot product of ones and twos is 64, each E8M0 step doubles it, blocks add; 0xF = -6 and
+    0x7 = 6 in one byte cancel against a row of ones; one nonzero element lands in the block
+    of its own K position (element 33 is the high nibble of byte 16)."""
+    one, two = np.full((1, 32), 0x22, np.uint8), np.full((1, 32), 0x44, np.uint8)
+    s = np.array([[127, 127]], np.uint8)
+    f = oracle.FMT_E2M1
+    assert oracle.mx_gemm_nt(one, s, two, s, fmt=f)[0, 0] == 128.0
+    assert oracle.mx_gemm_nt(one, np.array([[130, 127]], np.uint8), two, s, fmt=f)[0, 0] == 64.0 * 8 + 64.0
+    assert oracle.mx_gemm_nt(one, s, two, np.array([[127, 120]], np.uint8), fmt=f)[0, 0] == 64.0 + 64.0 / 128
+    assert oracle.mx_gemm_nt(np.full((1, 32), 0x7F, np.uint8), s, one, s, fmt=f)[0, 0] == 0.0
+    x = np.zeros((1, 32), np.uint8)
+    x[0, 16] = 0x50                                      # element 33 = 3.0, in block 1
+    assert oracle.mx_gemm_nt(x, np.array([[127, 129]], np.uint8), one, s, fmt=f)[0, 0] == 12.0
+
+
+def test_glu_gemm_interleaved_w_rows():
+    """[NV] Supported contract, weight layout row: W rows gate0, up0, gate1, up1, ...  The GLU
+    GEMM on interleaved W equals the one on [W_gate | W_up] holding the same rows, and equals
+    the GLU of Y's even (gate) and odd (up) columns; MXFP8 and MXFP4 operands."""
+    for fmt, gen in ((oracle.FMT_E4M3, si.mx_operand), (oracle.FMT_E2M1, si.mxfp4_operand)):
+        Xq, Xs = (t.numpy() for t in gen(24, 128, seed=63))
+        Wq, Ws = gen(2 * 64, 128, seed=64)
+        Wp, Wps = si.interleave_rows(Wq).numpy(), si.interleave_rows(Ws).numpy()
+        Wq, Ws = Wq.numpy(), Ws.numpy()
+        assert not np.array_equal(Wp, Wq)
+        Yp = oracle.mx_gemm_nt(Xq, Xs, Wp, Wps, fmt=fmt)
+        for kind in (oracle.SWIGLU, oracle.GEGLU_TANH):
+            h = oracle.glu_gemm(kind, Xq, Xs, Wp, Wps, fmt=fmt, w_layout=oracle.PAIRED)
+            assert np.array_equal(h, oracle.glu_gemm(kind, Xq, Xs, Wq, Ws, fmt=fmt))
+            assert np.array_equal(h, oracle.bf16_from_f64(oracle.act(kind, Yp[:, 0::2]) * Yp[:, 1::2]))
+            q, sc = oracle.glu_gemm_mxfp8(kind, Xq, Xs, Wp, Wps, fmt=fmt, w_layout=oracle.PAIRED)
+            o = oracle.quant_mxfp8(si.from_bits(h).float().numpy(), oracle.ROWWISE)
+            assert np.array_equal(q, o[0]) and np.array_equal(sc, o[1])
+
+
 def test_two_level_at_unit_global_scale_against_single_level():
     """An amax of 2688 (448 x 6) makes the global scale exactly 1, so two-level NVFP4 meets the
     single-level quantizer, which is pinned on its own (hand-worked blocks, brute force).  Over
