@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused GLU+MX-quant fwd/bwd achieved HBM GB/s and % of peak, M×N sweep"
 PEAK_GBPS = 8000.0  # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 matrix cores
+PEAK_FP4_TFLOPS = 10100.0  # MI355X dense FP4 matrix cores
 # The MXFP8 page's fused GB200 times for this exact workload (forward both 143.36 us,
 # backward both 219.14 us at (16384, 7168)), combined under the same byte model: another
 # machine's figure, reported under config as context only.
@@ -237,8 +238,8 @@ def validate_nv_bwd(torch, glu, act, g, u, d, out, sf_layout, what):
     _equal(torch, out[1], ref[1], what + " scales")
 
 
-def validate_gemm(torch, glu, ops, act, fmt, out, what):
-    h = glu.glu_gemm(*ops, act=act)
+def validate_gemm(torch, glu, ops, act, fmt, out, what, **operand_kw):
+    h = glu.glu_gemm(*ops, act=act, **operand_kw)
     if fmt == "mxfp8":
         q, s = glu.glu_quant_mxfp8_f32(h.float(), rowwise=True)[0::2]
     else:
@@ -424,21 +425,31 @@ def sweep(torch, glu, si, iters, validate):
         out = (torch.empty((M, N), dtype=torch.uint8, device="cuda"),
                torch.empty((M, N // 32), dtype=torch.uint8, device="cuda"))
         nv_out = glu._nv_buffers(M, N, "128x4", "cuda", None)
-        for act, fmt in [("swiglu", "mxfp8"), ("geglu", "mxfp8"), ("geglu", "nvfp4")]:
+        # MXFP4 operands with interleaved W: the NVFP4 page's contract form (packed E2M1
+        # values, gate/up rows interleaved, NVFP4 output) on the block scaling gfx950 takes
+        sets4 = [si.mxfp4_operand(M, K, seed=M + s, device="cuda") +
+                 tuple(si.interleave_rows(t) for t in si.mxfp4_operand(2 * N, K, seed=N + s, device="cuda"))
+                 for s in range(min(4, n_sets(per // 2)))]
+        for act, fmt, opfmt in [("swiglu", "mxfp8", "mxfp8"), ("geglu", "mxfp8", "mxfp8"),
+                                ("geglu", "nvfp4", "mxfp8"), ("geglu", "nvfp4", "mxfp4")]:
+            kw = dict(fmt=opfmt, w_layout="paired") if opfmt == "mxfp4" else {}
+            src = sets4 if opfmt == "mxfp4" else sets
             if fmt == "mxfp8":
-                fns = [lambda s=s: glu.glu_gemm_mxfp8(*s, act=act, out=out) for s in sets]
+                fns = [lambda s=s: glu.glu_gemm_mxfp8(*s, act=act, out=out, **kw) for s in src]
             else:
-                fns = [lambda s=s: glu.glu_gemm_nvfp4(*s, act=act, sf_layout="128x4", out=nv_out) for s in sets]
-            name = f"{act}_gemm_{fmt}_{M}x{N}x{K}"
+                fns = [lambda s=s: glu.glu_gemm_nvfp4(*s, act=act, sf_layout="128x4", out=nv_out, **kw) for s in src]
+            name = f"{act}_gemm_{fmt}_{M}x{N}x{K}" if opfmt == "mxfp8" else \
+                f"{act}_gemm_{opfmt}_paired_{fmt}_{M}x{N}x{K}"
             if validate:
                 fns[0]()
-                validate_gemm(torch, glu, sets[0], act, fmt, out if fmt == "mxfp8" else nv_out, name)
+                validate_gemm(torch, glu, src[0], act, fmt, out if fmt == "mxfp8" else nv_out, name, **kw)
             t = time_launches(torch, fns, iters)
             tf = 2.0 * M * K * 2 * N / t["median_us"] / 1e6
+            peak = PEAK_FP4_TFLOPS if opfmt == "mxfp4" else PEAK_FP8_TFLOPS
             print(f"[bench] {name}: {t['median_us']:.2f} us", file=sys.stderr, flush=True)
             res[name] = dict(flops=2 * M * K * 2 * N, us=round(t["median_us"], 2), min_us=round(t["min_us"], 2),
-                             p90_us=round(t["p90_us"], 2), tflops=round(tf, 1), frac=round(tf / PEAK_FP8_TFLOPS, 4),
-                             validated=validate)
+                             p90_us=round(t["p90_us"], 2), tflops=round(tf, 1), frac=round(tf / peak, 4),
+                             peak_tflops=peak, validated=validate)
         # context, not part of the path: the platform library's GEMM alone (torch._scaled_mm,
         # BF16 output, no activation, no quantizer) on the same codes, with the same E8M0 block
         # scales and with one tensor-wide scale
@@ -461,7 +472,7 @@ def sweep(torch, glu, si, iters, validate):
             print(f"[bench] {name}: {t['median_us']:.2f} us", file=sys.stderr, flush=True)
             res[name] = dict(flops=2 * M * K * 2 * N, us=round(t["median_us"], 2), tflops=round(tf, 1),
                              frac=round(tf / PEAK_FP8_TFLOPS, 4))
-        del sets, out, nv_out
+        del sets, sets4, out, nv_out
         torch.cuda.empty_cache()
     return res
 
@@ -578,6 +589,9 @@ def main():
             ops = si.mx_operand(gm, gk, seed=3, device="cuda") + si.mx_operand(2 * gn, gk, seed=4, device="cuda")
             for _ in range(3):
                 glu.glu_gemm_mxfp8(*ops, act="swiglu")
+            ops4 = si.mxfp4_operand(gm, gk, seed=3, device="cuda") + si.mxfp4_operand(2 * gn, gk, seed=4, device="cuda")
+            for _ in range(3):
+                glu.glu_gemm_nvfp4(*ops4, act="geglu", sf_layout="128x4", fmt="mxfp4", w_layout="paired")
         torch.cuda.synchronize()
         print("[bench] gemm launches done", file=sys.stderr, flush=True)
         return

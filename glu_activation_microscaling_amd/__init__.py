@@ -14,11 +14,12 @@ Entry points (C names in include/glu_mx.h):
   glu_bwd_nvfp4(gate, up, dh, sf_layout=...)                -> (q, sf) of [da | db]
   glu_amax(gate, up=None, layout=...)                        -> amax, float32 [1] on the GPU
   glu_fwd_nvfp4_gs(x, up=None, amax=, layout=, sf_layout=)   -> (q, sf), two-level scaling
-  glu_gemm(xq, xs, wq, ws, act=)                             -> h of the merged MXFP8 GEMM
-  glu_gemm_mxfp8(xq, xs, wq, ws, act=)                       -> (q_row, s_row) of that h
-  glu_gemm_nvfp4(xq, xs, wq, ws, act=, sf_layout=)            -> (q, sf) of that h, NVFP4
-  glu_gemm_nvfp4_gs(xq, xs, wq, ws, amax=, act=, sf_layout=)  -> (q, sf), two-level NVFP4
-  mx_gemm_f32(xq, xs, wq, ws)                                -> the GEMM alone (test hook)
+  glu_gemm(xq, xs, wq, ws, act=, fmt=, w_layout=)            -> h of the merged block-scaled GEMM
+  glu_gemm_mxfp8(xq, xs, wq, ws, act=, fmt=, w_layout=)      -> (q_row, s_row) of that h
+  glu_gemm_nvfp4(..., act=, fmt=, w_layout=, sf_layout=)      -> (q, sf) of that h, NVFP4
+  glu_gemm_nvfp4_gs(..., amax=, act=, fmt=, w_layout=, sf_layout=) -> (q, sf), two-level NVFP4
+  mx_gemm_f32(xq, xs, wq, ws, fmt=, w_layout=)               -> the GEMM alone (test hook)
+  (fmt "mxfp8": E4M3 codes, or "mxfp4": packed E2M1 codes; w_layout "split" or "paired")
   glu_quant_mxfp8_f32(x, rowwise=, colwise=)                -> (q_row, q_col, s_row, s_col)
   glu_quant_nvfp4_f32(x, sf_layout=)                        -> (q, sf)
 A disabled MXFP8 direction comes back as zero-sized tensors (fixed arity), as in the
@@ -35,6 +36,8 @@ LIB_PATH = os.path.join(_HERE, "libglu_mx.so")
 ACT = {"swiglu": 0, "geglu": 1, "geglu_tanh": 1, "geglu_erf": 2, "relu2": 3}
 LAYOUT = {"split": 0, "paired": 1}
 SF_LAYOUT = {"rowmajor": 0, "128x4": 1}
+GEMM_FMT = {"mxfp8": 0, "mxfp4": 1}          # operand codes: E4M3 one per byte, E2M1 two per byte
+W_LAYOUT = {"split": 0, "paired": 1}         # [W_gate | W_up], or rows gate0, up0, gate1, ...
 ROWWISE, COLWISE, SF_SWIZZLED = 1, 2, 4
 
 STATUS = {
@@ -51,11 +54,11 @@ _SIGNATURES = {
     "glu_fwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int, _p],
     "glu_bwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _p, _p, _int, _p],
     "glu_amax": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p],
-    "glu_gemm": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _p],
-    "glu_gemm_mxfp8": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p],
-    "glu_gemm_nvfp4": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _int, _p],
-    "glu_gemm_nvfp4_gs": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _int, _p],
-    "glu_mx_gemm_f32": [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p],
+    "glu_gemm": [_int, _int, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _p],
+    "glu_gemm_mxfp8": [_int, _int, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p],
+    "glu_gemm_nvfp4": [_int, _int, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _int, _p],
+    "glu_gemm_nvfp4_gs": [_int, _int, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _int, _p],
+    "glu_mx_gemm_f32": [_int, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p],
     "glu_fwd_nvfp4_gs": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _p, _int, _p],
     "glu_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p, _p],
     "glu_quant_nvfp4_f32": [_i64, _i64, _p, _i64, _p, _p, _int, _p],
@@ -66,11 +69,11 @@ _SIGNATURES = {
     "glu_check_fwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int],
     "glu_check_bwd_nvfp4": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _i64, _p, _p, _int],
     "glu_check_amax": [_int, _int, _i64, _i64, _p, _p, _i64, _p],
-    "glu_check_gemm": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64],
-    "glu_check_gemm_mxfp8": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p],
-    "glu_check_gemm_nvfp4": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _int],
-    "glu_check_gemm_nvfp4_gs": [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _int],
-    "glu_check_mx_gemm_f32": [_i64, _i64, _i64, _p, _p, _p, _p, _p],
+    "glu_check_gemm": [_int, _int, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64],
+    "glu_check_gemm_mxfp8": [_int, _int, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p],
+    "glu_check_gemm_nvfp4": [_int, _int, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _int],
+    "glu_check_gemm_nvfp4_gs": [_int, _int, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _int],
+    "glu_check_mx_gemm_f32": [_int, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p],
     "glu_check_fwd_nvfp4_gs": [_int, _int, _i64, _i64, _p, _p, _i64, _p, _p, _p, _int],
     "glu_check_quant_mxfp8_f32": [_i64, _i64, _p, _i64, _int, _p, _p, _p, _p],
     "glu_check_quant_nvfp4_f32": [_i64, _i64, _p, _i64, _p, _p, _int],
@@ -324,31 +327,38 @@ def glu_fwd_nvfp4_gs(x, up=None, *, amax, act="geglu", layout="paired", sf_layou
     return q, sf
 
 
-def _gemm_operands(xq, xs, wq, ws):
-    """MXFP8 operands of the merged gate/up GEMM: xq [M, K], xs [M, K/32], wq [2N, K],
-    ws [2N, K/32], contiguous uint8 on the GPU; returns (M, N, K)."""
+def _gemm_operands(xq, xs, wq, ws, fmt):
+    """Block-scaled operands of the merged gate/up GEMM, contiguous uint8 on the GPU: codes
+    xq [M, K] and wq [2N, K] (mxfp8), or packed xq [M, K/2] and wq [2N, K/2] (mxfp4), and
+    E8M0 scales xs [M, K/32], ws [2N, K/32]; returns (fmt code, M, N, K)."""
+    if fmt not in GEMM_FMT:
+        raise ValueError(f"fmt must be one of {sorted(GEMM_FMT)}")
     for t, name in ((xq, "xq"), (xs, "xs"), (wq, "wq"), (ws, "ws")):
         if t.dtype != torch.uint8 or not t.is_cuda or t.dim() != 2 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous 2-D torch.uint8 GPU tensor")
-    M, K = xq.shape
+    M, rb = xq.shape
+    K = 2 * rb if fmt == "mxfp4" else rb
     N2 = wq.shape[0]
-    if wq.shape[1] != K or tuple(xs.shape) != (M, K // 32) or tuple(ws.shape) != (N2, K // 32) or N2 % 2:
-        raise ValueError("operand shapes: xq [M, K], xs [M, K/32], wq [2N, K], ws [2N, K/32]")
-    return M, N2 // 2, K
+    if wq.shape[1] != rb or tuple(xs.shape) != (M, K // 32) or tuple(ws.shape) != (N2, K // 32) or N2 % 2:
+        raise ValueError("operand shapes: xq [M, K], xs [M, K/32], wq [2N, K], ws [2N, K/32] "
+                         "(codes [rows, K/2] bytes for mxfp4)")
+    return GEMM_FMT[fmt], M, N2 // 2, K
 
 
-def glu_gemm(xq, xs, wq, ws, *, act="swiglu", out=None):
-    """h = bf16(act(Y_gate) * Y_up), Y = X W^T of MXFP8 operands, W = [W_gate | W_up]: [M, N]."""
-    M, N, K = _gemm_operands(xq, xs, wq, ws)
+def glu_gemm(xq, xs, wq, ws, *, act="swiglu", fmt="mxfp8", w_layout="split", out=None):
+    """h = bf16(act(Y_gate) * Y_up), Y = X W^T of block-scaled operands: [M, N].  W's rows are
+    [W_gate | W_up] (split) or gate0, up0, gate1, up1, ... (paired)."""
+    f, M, N, K = _gemm_operands(xq, xs, wq, ws, fmt)
     h = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     ldh = _shaped(h, "out", M, N)
-    _call("glu_gemm", ACT[act], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(h), ldh, _stream(xq))
+    _call("glu_gemm", ACT[act], f, W_LAYOUT[w_layout], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws),
+          _ptr(h), ldh, _stream(xq))
     return h
 
 
-def glu_gemm_mxfp8(xq, xs, wq, ws, *, act="swiglu", out=None):
+def glu_gemm_mxfp8(xq, xs, wq, ws, *, act="swiglu", fmt="mxfp8", w_layout="split", out=None):
     """The same h quantized MXFP8 rowwise: (q_row [M, N], s_row [M, N/32])."""
-    M, N, K = _gemm_operands(xq, xs, wq, ws)
+    f, M, N, K = _gemm_operands(xq, xs, wq, ws, fmt)
     if out is not None:
         q, sc = out
         _byte_buffer(q, "q_row", M * N)
@@ -356,39 +366,43 @@ def glu_gemm_mxfp8(xq, xs, wq, ws, *, act="swiglu", out=None):
     else:
         q = torch.empty((M, N), dtype=torch.uint8, device=xq.device)
         sc = torch.empty((M, N // 32), dtype=torch.uint8, device=xq.device)
-    _call("glu_gemm_mxfp8", ACT[act], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(q), _ptr(sc),
-          _stream(xq))
+    _call("glu_gemm_mxfp8", ACT[act], f, W_LAYOUT[w_layout], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws),
+          _ptr(q), _ptr(sc), _stream(xq))
     return q, sc
 
 
-def glu_gemm_nvfp4(xq, xs, wq, ws, *, act="geglu", sf_layout="rowmajor", out=None):
+def glu_gemm_nvfp4(xq, xs, wq, ws, *, act="geglu", fmt="mxfp8", w_layout="split", sf_layout="rowmajor",
+                   out=None):
     """The same h quantized NVFP4, global scale 1: (q [M, N/2] packed E2M1, sf scales)."""
-    M, N, K = _gemm_operands(xq, xs, wq, ws)
+    f, M, N, K = _gemm_operands(xq, xs, wq, ws, fmt)
     q, sf = _nv_buffers(M, N, sf_layout, xq.device, out)
-    _call("glu_gemm_nvfp4", ACT[act], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(q), _ptr(sf),
-          SF_LAYOUT[sf_layout], _stream(xq))
+    _call("glu_gemm_nvfp4", ACT[act], f, W_LAYOUT[w_layout], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws),
+          _ptr(q), _ptr(sf), SF_LAYOUT[sf_layout], _stream(xq))
     return q, sf
 
 
-def glu_gemm_nvfp4_gs(xq, xs, wq, ws, *, amax, act="geglu", sf_layout="rowmajor", out=None):
+def glu_gemm_nvfp4_gs(xq, xs, wq, ws, *, amax, act="geglu", fmt="mxfp8", w_layout="split",
+                      sf_layout="rowmajor", out=None):
     """The same h quantized two-level NVFP4, the global scale from `amax` (a float32 [1] GPU
     tensor, e.g. kept from an earlier step): (q [M, N/2] packed E2M1, sf scales)."""
-    M, N, K = _gemm_operands(xq, xs, wq, ws)
+    f, M, N, K = _gemm_operands(xq, xs, wq, ws, fmt)
     if amax.dtype != torch.float32 or not amax.is_cuda or amax.numel() != 1:
         raise ValueError("amax must be a float32 GPU tensor with one element")
     q, sf = _nv_buffers(M, N, sf_layout, xq.device, out)
-    _call("glu_gemm_nvfp4_gs", ACT[act], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(amax), _ptr(q),
-          _ptr(sf), SF_LAYOUT[sf_layout], _stream(xq))
+    _call("glu_gemm_nvfp4_gs", ACT[act], f, W_LAYOUT[w_layout], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq),
+          _ptr(ws), _ptr(amax), _ptr(q), _ptr(sf), SF_LAYOUT[sf_layout], _stream(xq))
     return q, sf
 
 
-def mx_gemm_f32(xq, xs, wq, ws, *, out=None):
-    """Test hook: the merged GEMM's FP32 result Y = X W^T, [M, 2N], as the fused kernels form it."""
-    M, N, K = _gemm_operands(xq, xs, wq, ws)
+def mx_gemm_f32(xq, xs, wq, ws, *, fmt="mxfp8", w_layout="split", out=None):
+    """Test hook: the merged GEMM's FP32 result as the fused kernels form it, [M, 2N] =
+    [Y_gate | Y_up] whatever w_layout."""
+    f, M, N, K = _gemm_operands(xq, xs, wq, ws, fmt)
     y = out if out is not None else torch.empty((M, 2 * N), dtype=torch.float32, device=xq.device)
     if y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous() or tuple(y.shape) != (M, 2 * N):
         raise ValueError(f"out must be a contiguous float32 [{M}, {2 * N}] GPU tensor")
-    _call("glu_mx_gemm_f32", M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y), _stream(xq))
+    _call("glu_mx_gemm_f32", f, W_LAYOUT[w_layout], M, N, K, _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y),
+          _stream(xq))
     return y
 
 

@@ -349,87 +349,96 @@ glu_status glu_check_fwd_nvfp4_gs(int act, int layout, int64_t M, int64_t H,
   return check_no_overlap({Q, S}, {A});
 }
 
-// Operands of the merged gate/up MXFP8 GEMM.  The kernels address each operand from its base
-// with 32-bit byte offsets, so every operand and output extent stays below 2^31 bytes.
-glu_status check_gemm_inputs(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
-                             const uint8_t* xs, const uint8_t* wq, const uint8_t* ws) {
+// Operands of the merged gate/up block-scaled GEMM.  The kernels address each operand from
+// its base with 32-bit byte offsets, so every operand and output extent stays below 2^31
+// bytes.  A K step is one 128-byte line of an operand row: 128 E4M3 or 256 E2M1 codes.
+struct GemmOperands {
+  Operand X, XS, W, WS;
+};
+bool valid_gemm_format(int fmt, int w_layout) {
+  return (fmt == glu::FMT_E4M3 || fmt == glu::FMT_E2M1) && (w_layout == glu::SPLIT || w_layout == glu::PAIRED);
+}
+glu_status check_gemm_inputs(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                             const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, GemmOperands* ops) {
   if (xq == nullptr || xs == nullptr || wq == nullptr || ws == nullptr) return GLU_ERR_NULL;
-  if (K <= 0 || K % 128 != 0 || N % 128 != 0) return GLU_ERR_SHAPE;
+  const int64_t kstep = fmt == glu::FMT_E2M1 ? 256 : 128;
+  if (K <= 0 || K % kstep != 0 || N % 128 != 0) return GLU_ERR_SHAPE;
+  const int64_t rb = fmt == glu::FMT_E2M1 ? K / 2 : K;   // bytes per operand row
   int64_t xb, wb;
-  if (__builtin_mul_overflow(M, K, &xb) || __builtin_mul_overflow(2 * N, K, &wb)) return GLU_ERR_SHAPE;
+  if (__builtin_mul_overflow(M, rb, &xb) || __builtin_mul_overflow(2 * N, rb, &wb)) return GLU_ERR_SHAPE;
   if (xb >= kOffsetLimit || wb >= kOffsetLimit) return GLU_ERR_SHAPE;
   if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws)) return GLU_ERR_ALIGN;
+  *ops = {mat(xq, M, rb, rb, 1), mat(xs, M, K / 32, K / 32, 1), mat(wq, 2 * N, rb, rb, 1),
+          mat(ws, 2 * N, K / 32, K / 32, 1)};
   return GLU_OK;
 }
 
-glu_status glu_check_gemm(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
-                          const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, uint16_t* h,
-                          int64_t ld_h) {
-  if (!valid_act(act)) return GLU_ERR_ARG;
+glu_status glu_check_gemm(int act, int fmt, int w_layout, int64_t M, int64_t N, int64_t K,
+                          const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
+                          const uint8_t* ws, uint16_t* h, int64_t ld_h) {
+  if (!valid_act(act) || !valid_gemm_format(fmt, w_layout)) return GLU_ERR_ARG;
   if (M < 0 || N < 0 || K < 0) return GLU_ERR_SHAPE;
   if (M == 0 || N == 0) return GLU_OK;
-  glu_status st = check_gemm_inputs(M, N, K, xq, xs, wq, ws);
+  GemmOperands o;
+  glu_status st = check_gemm_inputs(fmt, M, N, K, xq, xs, wq, ws, &o);
   if (st != GLU_OK) return st;
   if (h == nullptr) return GLU_ERR_NULL;
   if (ld_h < N) return GLU_ERR_STRIDE;
   if (!aligned16(h) || ld_h % 8 != 0) return GLU_ERR_ALIGN;
-  const Operand X = mat(xq, M, K, K, 1), XS = mat(xs, M, K / 32, K / 32, 1),
-                W = mat(wq, 2 * N, K, K, 1), WS = mat(ws, 2 * N, K / 32, K / 32, 1),
-                Hh = mat(h, M, N, ld_h, 2);
+  const Operand Hh = mat(h, M, N, ld_h, 2);
   if (any_overflow({Hh}) || Hh.bytes >= kOffsetLimit) return GLU_ERR_SHAPE;
-  return check_no_overlap({Hh}, {X, XS, W, WS});
+  return check_no_overlap({Hh}, {o.X, o.XS, o.W, o.WS});
 }
 
-glu_status glu_check_gemm_mxfp8(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
-                                const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
-                                uint8_t* q_row, uint8_t* s_row) {
-  if (!valid_act(act)) return GLU_ERR_ARG;
+glu_status glu_check_gemm_mxfp8(int act, int fmt, int w_layout, int64_t M, int64_t N, int64_t K,
+                                const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
+                                const uint8_t* ws, uint8_t* q_row, uint8_t* s_row) {
+  if (!valid_act(act) || !valid_gemm_format(fmt, w_layout)) return GLU_ERR_ARG;
   if (M < 0 || N < 0 || K < 0) return GLU_ERR_SHAPE;
   if (M == 0 || N == 0) return GLU_OK;
-  glu_status st = check_gemm_inputs(M, N, K, xq, xs, wq, ws);
+  GemmOperands o;
+  glu_status st = check_gemm_inputs(fmt, M, N, K, xq, xs, wq, ws, &o);
   if (st != GLU_OK) return st;
   if (q_row == nullptr || s_row == nullptr) return GLU_ERR_NULL;
   if (!aligned16(q_row) || !aligned16(s_row)) return GLU_ERR_ALIGN;
-  const Operand X = mat(xq, M, K, K, 1), XS = mat(xs, M, K / 32, K / 32, 1),
-                W = mat(wq, 2 * N, K, K, 1), WS = mat(ws, 2 * N, K / 32, K / 32, 1),
-                Q = mat(q_row, M, N, N, 1), S = mat(s_row, M, N / 32, N / 32, 1);
+  const Operand Q = mat(q_row, M, N, N, 1), S = mat(s_row, M, N / 32, N / 32, 1);
   if (any_overflow({Q, S}) || Q.bytes >= kOffsetLimit) return GLU_ERR_SHAPE;
-  return check_no_overlap({Q, S}, {X, XS, W, WS});
+  return check_no_overlap({Q, S}, {o.X, o.XS, o.W, o.WS});
 }
 
-glu_status glu_check_gemm_nvfp4(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
-                                const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
-                                uint8_t* q, uint8_t* sf, int sf_layout) {
-  if (!valid_act(act)) return GLU_ERR_ARG;
+glu_status glu_check_gemm_nvfp4(int act, int fmt, int w_layout, int64_t M, int64_t N, int64_t K,
+                                const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
+                                const uint8_t* ws, uint8_t* q, uint8_t* sf, int sf_layout) {
+  if (!valid_act(act) || !valid_gemm_format(fmt, w_layout)) return GLU_ERR_ARG;
   if (sf_layout != glu::SF_ROWMAJOR && sf_layout != glu::SF_128x4) return GLU_ERR_ARG;
   if (M < 0 || N < 0 || K < 0) return GLU_ERR_SHAPE;
   if (M == 0 || N == 0) return GLU_OK;
-  glu_status st = check_gemm_inputs(M, N, K, xq, xs, wq, ws);
+  GemmOperands o;
+  glu_status st = check_gemm_inputs(fmt, M, N, K, xq, xs, wq, ws, &o);
   if (st != GLU_OK) return st;
   if (q == nullptr || sf == nullptr) return GLU_ERR_NULL;
   if (!aligned16(q) || !aligned16(sf)) return GLU_ERR_ALIGN;
   const int64_t sfb = glu_nvfp4_sf_bytes(M, N, sf_layout);
   if (sfb < 0) return GLU_ERR_SHAPE;
-  const Operand X = mat(xq, M, K, K, 1), XS = mat(xs, M, K / 32, K / 32, 1),
-                W = mat(wq, 2 * N, K, K, 1), WS = mat(ws, 2 * N, K / 32, K / 32, 1),
-                Q = mat(q, M, N / 2, N / 2, 1), S = mat(sf, 1, sfb, sfb, 1);
+  const Operand Q = mat(q, M, N / 2, N / 2, 1), S = mat(sf, 1, sfb, sfb, 1);
   if (any_overflow({Q, S}) || Q.bytes >= kOffsetLimit || S.bytes >= kOffsetLimit) return GLU_ERR_SHAPE;
-  return check_no_overlap({Q, S}, {X, XS, W, WS});
+  return check_no_overlap({Q, S}, {o.X, o.XS, o.W, o.WS});
 }
 
-glu_status glu_check_mx_gemm_f32(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
-                                 const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, float* y) {
+glu_status glu_check_mx_gemm_f32(int fmt, int w_layout, int64_t M, int64_t N, int64_t K,
+                                 const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
+                                 const uint8_t* ws, float* y) {
+  if (!valid_gemm_format(fmt, w_layout)) return GLU_ERR_ARG;
   if (M < 0 || N < 0 || K < 0) return GLU_ERR_SHAPE;
   if (M == 0 || N == 0) return GLU_OK;
-  glu_status st = check_gemm_inputs(M, N, K, xq, xs, wq, ws);
+  GemmOperands o;
+  glu_status st = check_gemm_inputs(fmt, M, N, K, xq, xs, wq, ws, &o);
   if (st != GLU_OK) return st;
   if (y == nullptr) return GLU_ERR_NULL;
   if (!aligned16(y)) return GLU_ERR_ALIGN;
-  const Operand X = mat(xq, M, K, K, 1), XS = mat(xs, M, K / 32, K / 32, 1),
-                W = mat(wq, 2 * N, K, K, 1), WS = mat(ws, 2 * N, K / 32, K / 32, 1),
-                Y = mat(y, M, 2 * N, 2 * N, 4);
+  const Operand Y = mat(y, M, 2 * N, 2 * N, 4);
   if (any_overflow({Y}) || Y.bytes >= kOffsetLimit) return GLU_ERR_SHAPE;
-  return check_no_overlap({Y}, {X, XS, W, WS});
+  return check_no_overlap({Y}, {o.X, o.XS, o.W, o.WS});
 }
 
 glu_status glu_check_bwd_nvfp4(int act, int layout, int64_t M, int64_t N, const uint16_t* gate,
@@ -617,37 +626,38 @@ glu_status glu_fwd_nvfp4_gs(int act, int layout, int64_t M, int64_t H, const uin
   return status_of(glu::launch_glu_fwd_nvfp4_gs(a, (hipStream_t)stream));
 }
 
-glu_status glu_gemm(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
-                    const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, uint16_t* h,
-                    int64_t ld_h, void* stream) {
-  glu_status st = glu_check_gemm(act, M, N, K, xq, xs, wq, ws, h, ld_h);
+glu_status glu_gemm(int act, int fmt, int w_layout, int64_t M, int64_t N, int64_t K,
+                    const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                    uint16_t* h, int64_t ld_h, void* stream) {
+  glu_status st = glu_check_gemm(act, fmt, w_layout, M, N, K, xq, xs, wq, ws, h, ld_h);
   if (st != GLU_OK || M == 0 || N == 0) return st;
-  GemmArgs a{act, M, N, K, xq, xs, wq, ws, h, ld_h, nullptr, nullptr, nullptr};
+  GemmArgs a{act, fmt, w_layout, M, N, K, xq, xs, wq, ws, h, ld_h, nullptr, nullptr, nullptr};
   return status_of(glu::launch_glu_gemm(a, (hipStream_t)stream));
 }
 
-glu_status glu_gemm_mxfp8(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
-                          const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
-                          uint8_t* q_row, uint8_t* s_row, void* stream) {
-  glu_status st = glu_check_gemm_mxfp8(act, M, N, K, xq, xs, wq, ws, q_row, s_row);
+glu_status glu_gemm_mxfp8(int act, int fmt, int w_layout, int64_t M, int64_t N, int64_t K,
+                          const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
+                          const uint8_t* ws, uint8_t* q_row, uint8_t* s_row, void* stream) {
+  glu_status st = glu_check_gemm_mxfp8(act, fmt, w_layout, M, N, K, xq, xs, wq, ws, q_row, s_row);
   if (st != GLU_OK || M == 0 || N == 0) return st;
-  GemmArgs a{act, M, N, K, xq, xs, wq, ws, nullptr, 0, q_row, s_row, nullptr};
+  GemmArgs a{act, fmt, w_layout, M, N, K, xq, xs, wq, ws, nullptr, 0, q_row, s_row, nullptr};
   return status_of(glu::launch_glu_gemm_mxfp8(a, (hipStream_t)stream));
 }
 
-glu_status glu_gemm_nvfp4(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
-                          const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, uint8_t* q,
-                          uint8_t* sf, int sf_layout, void* stream) {
-  glu_status st = glu_check_gemm_nvfp4(act, M, N, K, xq, xs, wq, ws, q, sf, sf_layout);
+glu_status glu_gemm_nvfp4(int act, int fmt, int w_layout, int64_t M, int64_t N, int64_t K,
+                          const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
+                          const uint8_t* ws, uint8_t* q, uint8_t* sf, int sf_layout, void* stream) {
+  glu_status st = glu_check_gemm_nvfp4(act, fmt, w_layout, M, N, K, xq, xs, wq, ws, q, sf, sf_layout);
   if (st != GLU_OK || M == 0 || N == 0) return st;
-  GemmArgs a{act, M, N, K, xq, xs, wq, ws, nullptr, 0, q, sf, nullptr};
+  GemmArgs a{act, fmt, w_layout, M, N, K, xq, xs, wq, ws, nullptr, 0, q, sf, nullptr};
   return status_of(glu::launch_glu_gemm_nvfp4(a, sf_layout, false, (hipStream_t)stream));
 }
 
-glu_status glu_check_gemm_nvfp4_gs(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
-                                   const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
-                                   const float* amax, uint8_t* q, uint8_t* sf, int sf_layout) {
-  glu_status st = glu_check_gemm_nvfp4(act, M, N, K, xq, xs, wq, ws, q, sf, sf_layout);
+glu_status glu_check_gemm_nvfp4_gs(int act, int fmt, int w_layout, int64_t M, int64_t N,
+                                   int64_t K, const uint8_t* xq, const uint8_t* xs,
+                                   const uint8_t* wq, const uint8_t* ws, const float* amax,
+                                   uint8_t* q, uint8_t* sf, int sf_layout) {
+  glu_status st = glu_check_gemm_nvfp4(act, fmt, w_layout, M, N, K, xq, xs, wq, ws, q, sf, sf_layout);
   if (st != GLU_OK || M == 0 || N == 0) return st;
   if (amax == nullptr) return GLU_ERR_NULL;
   if ((uintptr_t)amax % 4 != 0) return GLU_ERR_ALIGN;
@@ -656,22 +666,23 @@ glu_status glu_check_gemm_nvfp4_gs(int act, int64_t M, int64_t N, int64_t K, con
   return check_no_overlap({Q, S}, {A});
 }
 
-glu_status glu_gemm_nvfp4_gs(int act, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
-                             const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
-                             const float* amax, uint8_t* q, uint8_t* sf, int sf_layout,
-                             void* stream) {
-  glu_status st = glu_check_gemm_nvfp4_gs(act, M, N, K, xq, xs, wq, ws, amax, q, sf, sf_layout);
+glu_status glu_gemm_nvfp4_gs(int act, int fmt, int w_layout, int64_t M, int64_t N, int64_t K,
+                             const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
+                             const uint8_t* ws, const float* amax, uint8_t* q, uint8_t* sf,
+                             int sf_layout, void* stream) {
+  glu_status st =
+      glu_check_gemm_nvfp4_gs(act, fmt, w_layout, M, N, K, xq, xs, wq, ws, amax, q, sf, sf_layout);
   if (st != GLU_OK || M == 0 || N == 0) return st;
-  GemmArgs a{act, M, N, K, xq, xs, wq, ws, nullptr, 0, q, sf, nullptr, amax};
+  GemmArgs a{act, fmt, w_layout, M, N, K, xq, xs, wq, ws, nullptr, 0, q, sf, nullptr, amax};
   return status_of(glu::launch_glu_gemm_nvfp4(a, sf_layout, true, (hipStream_t)stream));
 }
 
-glu_status glu_mx_gemm_f32(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
-                           const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, float* y,
-                           void* stream) {
-  glu_status st = glu_check_mx_gemm_f32(M, N, K, xq, xs, wq, ws, y);
+glu_status glu_mx_gemm_f32(int fmt, int w_layout, int64_t M, int64_t N, int64_t K,
+                           const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
+                           const uint8_t* ws, float* y, void* stream) {
+  glu_status st = glu_check_mx_gemm_f32(fmt, w_layout, M, N, K, xq, xs, wq, ws, y);
   if (st != GLU_OK || M == 0 || N == 0) return st;
-  GemmArgs a{glu::SWIGLU, M, N, K, xq, xs, wq, ws, nullptr, 0, nullptr, nullptr, y};
+  GemmArgs a{glu::SWIGLU, fmt, w_layout, M, N, K, xq, xs, wq, ws, nullptr, 0, nullptr, nullptr, y};
   return status_of(glu::launch_mx_gemm_f32(a, (hipStream_t)stream));
 }
 

@@ -57,16 +57,18 @@ struct NvArgs {
 
 struct GemmArgs {
   int act;
-  int64_t M, N, K;           // X [M, K], W [2N, K]; the output has N columns
-  const uint8_t* xq;         // E4M3 codes [M, K]
+  int fmt;                   // FMT_E4M3 (a code per byte) or FMT_E2M1 (two codes per byte)
+  int w_layout;              // SPLIT: W = [W_gate | W_up]; PAIRED: rows gate0, up0, gate1, ...
+  int64_t M, N, K;           // X [M, K], W [2N, K] elements; the output has N columns
+  const uint8_t* xq;         // codes [M, K] (E2M1: [M, K/2] bytes)
   const uint8_t* xs;         // E8M0 scales [M, K/32]
-  const uint8_t* wq;         // [W_gate | W_up] codes [2N, K]
-  const uint8_t* ws;         // scales [2N, K/32]
+  const uint8_t* wq;         // codes [2N, K] (E2M1: [2N, K/2] bytes), rows in w_layout
+  const uint8_t* ws;         // scales [2N, K/32], rows in w_layout
   uint16_t* h;               // BF16 h [M, N], row stride ld_h
   int64_t ld_h;
   uint8_t* q_row;            // MXFP8 rowwise codes [M, N] (NVFP4: packed E2M1 [M, N/2])
   uint8_t* s_row;            // scales [M, N/32] (NVFP4: E4M3, row-major or 128x4)
-  float* y;                  // test hook: the pre-activation [M, 2N]
+  float* y;                  // test hook: the pre-activation [M, 2N] = [Y_gate | Y_up]
   const float* amax = nullptr;  // two-level NVFP4: the amax the global scale comes from
 };
 

@@ -13,10 +13,10 @@ that torch.compile keeps whole; these ops do the same for the MI355X kernels:
   torch.ops.glu_mx.glu_backward_nvfp4(gate, up, dh, act, sf_layout)    -> (q, sf)
   torch.ops.glu_mx.glu_amax(gate, up, act, layout)                     -> amax [1]
   torch.ops.glu_mx.glu_nvfp4_gs(x, up, amax, act, layout, sf_layout)   -> (q, sf)
-  torch.ops.glu_mx.glu_gemm(xq, xs, wq, ws, act)                       -> h
-  torch.ops.glu_mx.glu_gemm_mxfp8(xq, xs, wq, ws, act)                 -> (q_row, s_row)
-  torch.ops.glu_mx.glu_gemm_nvfp4(xq, xs, wq, ws, act, sf_layout)      -> (q, sf)
-  torch.ops.glu_mx.glu_gemm_nvfp4_gs(xq, xs, wq, ws, amax, act, sf_layout) -> (q, sf)
+  torch.ops.glu_mx.glu_gemm(xq, xs, wq, ws, act, fmt, w_layout)        -> h
+  torch.ops.glu_mx.glu_gemm_mxfp8(xq, xs, wq, ws, act, fmt, w_layout)  -> (q_row, s_row)
+  torch.ops.glu_mx.glu_gemm_nvfp4(xq, xs, wq, ws, act, sf_layout, fmt, w_layout) -> (q, sf)
+  torch.ops.glu_mx.glu_gemm_nvfp4_gs(xq, xs, wq, ws, amax, act, sf_layout, fmt, w_layout) -> (q, sf)
 
 Each real implementation is the binding function of the same name (argument marshalling;
 the HIP kernels compute everything).  Each fake implementation gives the output shapes and
@@ -195,39 +195,43 @@ def _(x, up, amax, act="geglu", layout="paired", sf_layout="rowmajor"):
             x.new_empty(_nv_scale_shape(M, H, sf_layout), dtype=torch.uint8))
 
 
-# ---- merged gate/up MXFP8 GEMM with the GLU epilogue --------------------------------
-# xq [M, K] E4M3 codes, xs [M, K/32] E8M0 scales, wq [2N, K] = [W_gate | W_up], ws [2N, K/32]
+# ---- merged gate/up block-scaled GEMM with the GLU epilogue ---------------------------
+# xq [M, K] codes (fmt "mxfp8": E4M3, one per byte; "mxfp4": E2M1, [M, K/2] packed), xs [M, K/32]
+# E8M0 scales, wq [2N, K] (rows [W_gate | W_up], or gate0, up0, ... with w_layout "paired"),
+# ws [2N, K/32]
 
 @torch.library.custom_op(f"{_LIB}::glu_gemm", mutates_args=())
-def glu_gemm(xq: Tensor, xs: Tensor, wq: Tensor, ws: Tensor, act: str = "swiglu") -> Tensor:
-    return _gemm(xq, xs, wq, ws, act=act)
+def glu_gemm(xq: Tensor, xs: Tensor, wq: Tensor, ws: Tensor, act: str = "swiglu", fmt: str = "mxfp8",
+             w_layout: str = "split") -> Tensor:
+    return _gemm(xq, xs, wq, ws, act=act, fmt=fmt, w_layout=w_layout)
 
 
 @glu_gemm.register_fake
-def _(xq, xs, wq, ws, act="swiglu"):
+def _(xq, xs, wq, ws, act="swiglu", fmt="mxfp8", w_layout="split"):
     return xq.new_empty((xq.shape[0], wq.shape[0] // 2), dtype=torch.bfloat16)
 
 
 @torch.library.custom_op(f"{_LIB}::glu_gemm_mxfp8", mutates_args=())
-def glu_gemm_mxfp8(xq: Tensor, xs: Tensor, wq: Tensor, ws: Tensor,
-                   act: str = "swiglu") -> Tuple[Tensor, Tensor]:
-    return _gemm_mx(xq, xs, wq, ws, act=act)
+def glu_gemm_mxfp8(xq: Tensor, xs: Tensor, wq: Tensor, ws: Tensor, act: str = "swiglu",
+                   fmt: str = "mxfp8", w_layout: str = "split") -> Tuple[Tensor, Tensor]:
+    return _gemm_mx(xq, xs, wq, ws, act=act, fmt=fmt, w_layout=w_layout)
 
 
 @glu_gemm_mxfp8.register_fake
-def _(xq, xs, wq, ws, act="swiglu"):
+def _(xq, xs, wq, ws, act="swiglu", fmt="mxfp8", w_layout="split"):
     M, N = xq.shape[0], wq.shape[0] // 2
     return xq.new_empty((M, N), dtype=torch.uint8), xq.new_empty((M, N // 32), dtype=torch.uint8)
 
 
 @torch.library.custom_op(f"{_LIB}::glu_gemm_nvfp4", mutates_args=())
 def glu_gemm_nvfp4(xq: Tensor, xs: Tensor, wq: Tensor, ws: Tensor, act: str = "geglu",
-                   sf_layout: str = "rowmajor") -> Tuple[Tensor, Tensor]:
-    return _gemm_nv(xq, xs, wq, ws, act=act, sf_layout=sf_layout)
+                   sf_layout: str = "rowmajor", fmt: str = "mxfp8",
+                   w_layout: str = "split") -> Tuple[Tensor, Tensor]:
+    return _gemm_nv(xq, xs, wq, ws, act=act, sf_layout=sf_layout, fmt=fmt, w_layout=w_layout)
 
 
 @glu_gemm_nvfp4.register_fake
-def _(xq, xs, wq, ws, act="geglu", sf_layout="rowmajor"):
+def _(xq, xs, wq, ws, act="geglu", sf_layout="rowmajor", fmt="mxfp8", w_layout="split"):
     M, N = xq.shape[0], wq.shape[0] // 2
     return (xq.new_empty((M, N // 2), dtype=torch.uint8),
             xq.new_empty(_nv_scale_shape(M, N, sf_layout), dtype=torch.uint8))
@@ -235,12 +239,13 @@ def _(xq, xs, wq, ws, act="geglu", sf_layout="rowmajor"):
 
 @torch.library.custom_op(f"{_LIB}::glu_gemm_nvfp4_gs", mutates_args=())
 def glu_gemm_nvfp4_gs(xq: Tensor, xs: Tensor, wq: Tensor, ws: Tensor, amax: Tensor,
-                      act: str = "geglu", sf_layout: str = "rowmajor") -> Tuple[Tensor, Tensor]:
-    return _gemm_nv_gs(xq, xs, wq, ws, amax=amax, act=act, sf_layout=sf_layout)
+                      act: str = "geglu", sf_layout: str = "rowmajor", fmt: str = "mxfp8",
+                      w_layout: str = "split") -> Tuple[Tensor, Tensor]:
+    return _gemm_nv_gs(xq, xs, wq, ws, amax=amax, act=act, sf_layout=sf_layout, fmt=fmt, w_layout=w_layout)
 
 
 @glu_gemm_nvfp4_gs.register_fake
-def _(xq, xs, wq, ws, amax, act="geglu", sf_layout="rowmajor"):
+def _(xq, xs, wq, ws, amax, act="geglu", sf_layout="rowmajor", fmt="mxfp8", w_layout="split"):
     M, N = xq.shape[0], wq.shape[0] // 2
     return (xq.new_empty((M, N // 2), dtype=torch.uint8),
             xq.new_empty(_nv_scale_shape(M, N, sf_layout), dtype=torch.uint8))

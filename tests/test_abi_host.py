@@ -299,7 +299,7 @@ def test_gemm_checks():
     q = lambda **kw: _gemm(L.glu_check_gemm_mxfp8, **kw)
     assert q() == OK and q(q=0) == NULL and q(s=E0 + 1) == ALIGN and q(act=7) == ARG
     assert q(s=D0 + 64 * 128 - 16) == OVERLAP and q(s=D0 + 64 * 128) == OK
-    nv = L.glu_check_gemm_nvfp4
+    nv = lambda *a: L.glu_check_gemm_nvfp4(a[0], 0, 0, *a[1:])
     assert nv(0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(E0), 0) == OK
     assert nv(0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(E0), 1) == OK
     assert nv(0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(E0), 2) == ARG
@@ -311,7 +311,7 @@ def test_gemm_checks():
     assert nv(0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(E0 + 1024 - 16), P(E0), 1) == OVERLAP
     assert nv(0, 64, 96, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(E0), 0) == SHAPE
     gs = L.glu_check_gemm_nvfp4_gs
-    base = (0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2))
+    base = (0, 0, 0, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2))
     assert gs(*base, P(F0), P(D0), P(E0), 1) == OK
     assert gs(*base, P(0), P(D0), P(E0), 1) == NULL
     assert gs(*base, P(F0 + 2), P(D0), P(E0), 1) == ALIGN
@@ -323,15 +323,36 @@ def test_gemm_checks():
     assert y(M=(1 << 20) - 8, K=128, N=256, y=F0 * 64) == OK
 
 
-def _gemm(fn, act=0, M=64, N=128, K=256, xq=A0, xs=B0, wq=C0, ws=A0 // 2, h=E0, ldh=128,
+def test_gemm_operand_format_and_w_layout_checks():
+    """fmt: E4M3 (one code per byte) or E2M1 (two per byte, K % 256); w_layout: split or
+    interleaved rows.  E2M1 operand rows take K/2 bytes, so the extents used for the 32-bit
+    bound and the overlap checks halve."""
+    g = lambda **kw: _gemm(L.glu_check_gemm, **kw)
+    assert g(fmt=1) == OK and g(wl=1) == OK and g(fmt=1, wl=1) == OK
+    assert g(fmt=2) == ARG and g(fmt=-1) == ARG and g(wl=2) == ARG
+    assert g(fmt=1, K=128) == SHAPE and g(fmt=0, K=128) == OK and g(fmt=1, K=512) == OK
+    # h placed just past X: X is [64, 256] E4M3 = 16 KiB, or [64, 128] bytes = 8 KiB as E2M1
+    assert g(h=A0 + 8192) == OVERLAP and g(h=A0 + 8192, fmt=1) == OK
+    # W is [2N, K] elements: 2^31 bytes as E4M3 at 2N = 2^23, K = 256, half of it as E2M1
+    assert g(N=1 << 22, K=256, M=1, ldh=1 << 22, h=F0 * 64) == SHAPE
+    assert g(N=1 << 22, K=256, M=1, ldh=1 << 22, h=F0 * 64, fmt=1) == OK
+    y = lambda **kw: _gemm(L.glu_check_mx_gemm_f32, **kw)
+    assert y(fmt=1, wl=1) == OK and y(fmt=3) == ARG and y(wl=5) == ARG
+    q = lambda **kw: _gemm(L.glu_check_gemm_mxfp8, **kw)
+    assert q(fmt=1, wl=1) == OK and q(fmt=1, K=384) == SHAPE
+    assert L.glu_check_gemm_nvfp4(0, 1, 1, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(E0), 1) == OK
+    assert L.glu_check_gemm_nvfp4(0, 2, 1, 64, 128, 256, P(A0), P(B0), P(C0), P(A0 // 2), P(D0), P(E0), 1) == ARG
+
+
+def _gemm(fn, act=0, fmt=0, wl=0, M=64, N=128, K=256, xq=A0, xs=B0, wq=C0, ws=A0 // 2, h=E0, ldh=128,
           q=D0, s=E0, y=D0):
     """Fake operands: X [M, K] at A0, its scales at B0, W [2N, K] at C0, W's scales at A0/2."""
     ops = [P(xq), P(xs), P(wq), P(ws)]
     if fn is L.glu_check_gemm:
-        return fn(act, M, N, K, *ops, P(h), ldh)
+        return fn(act, fmt, wl, M, N, K, *ops, P(h), ldh)
     if fn is L.glu_check_gemm_mxfp8:
-        return fn(act, M, N, K, *ops, P(q), P(s))
-    return fn(M, N, K, *ops, P(y))
+        return fn(act, fmt, wl, M, N, K, *ops, P(q), P(s))
+    return fn(fmt, wl, M, N, K, *ops, P(y))
 
 
 def test_entry_points_fail_before_any_hip_call():
@@ -349,9 +370,13 @@ def test_entry_points_fail_before_any_hip_call():
     assert L.glu_fwd_nvfp4_gs(1, 1, 0, 32, P(0), P(0), 64, P(0), P(0), P(0), 0, P(0)) == OK
     assert L.glu_quant_mxfp8_f32(32, 32, P(A0), 32, 8, P(B0), P(C0), P(D0), P(E0), P(0)) == ARG
     assert L.glu_quant_nvfp4_f32(32, 32, P(A0 + 4), 32, P(B0), P(C0), 0, P(0)) == ALIGN
-    assert L.glu_gemm(0, 8, 64, 128, P(A0), P(B0), P(C0), P(D0), P(E0), 64, P(0)) == SHAPE
-    assert L.glu_gemm_mxfp8(0, 0, 128, 128, P(0), P(0), P(0), P(0), P(0), P(0), P(0)) == OK
-    assert L.glu_mx_gemm_f32(8, 128, 100, P(A0), P(B0), P(C0), P(D0), P(E0), P(0)) == SHAPE
+    assert L.glu_gemm(0, 0, 0, 8, 64, 128, P(A0), P(B0), P(C0), P(D0), P(E0), 64, P(0)) == SHAPE
+    assert L.glu_gemm(0, 1, 1, 8, 128, 128, P(A0), P(B0), P(C0), P(D0), P(E0), 128, P(0)) == SHAPE
+    assert L.glu_gemm_mxfp8(0, 0, 0, 0, 128, 128, P(0), P(0), P(0), P(0), P(0), P(0), P(0)) == OK
+    assert L.glu_gemm_nvfp4(0, 4, 0, 8, 128, 256, P(A0), P(B0), P(C0), P(D0), P(E0), P(F0), 0, P(0)) == ARG
+    assert L.glu_gemm_nvfp4_gs(0, 0, 0, 8, 128, 256, P(A0), P(B0), P(C0), P(D0), P(0), P(E0), P(F0), 0,
+                               P(0)) == NULL
+    assert L.glu_mx_gemm_f32(0, 0, 8, 128, 100, P(A0), P(B0), P(C0), P(D0), P(E0), P(0)) == SHAPE
 
 
 def test_binding_refuses_cpu_tensors():
