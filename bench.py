@@ -527,6 +527,8 @@ def main():
     ap.add_argument("--bf16-only", action="store_true",
                     help="only launch the GeGLU BF16 forward and backward at [8192, 14336] three times "
                          "each and print no JSON (a target for profiler counter passes)")
+    ap.add_argument("--nvfp4-contract-only", action="store_true",
+                    help="only launch the NVFP4 GeGLU forward at 968 x 16384 three times (for profiler passes)")
     ap.add_argument("--nvfp4-only", action="store_true",
                     help="only launch the NVFP4 forward and backward at [16384, 7168] three times "
                          "each and print no JSON (a target for profiler counter passes)")
@@ -570,6 +572,17 @@ def main():
         if args.copy_calibration:
             calibrate()
         print("[bench] nvfp4 launches done", file=sys.stderr, flush=True)
+        return
+    if args.nvfp4_contract_only:
+        # the NVFP4 page's contract shape: GeGLU of an interleaved [968, 32768] operand, 128x4 scales
+        x = si.normal_bf16_device([(968, 2 * 16384)], seed=5)[0]
+        of = glu._nv_buffers(968, 16384, "128x4", "cuda", None)
+        for _ in range(3):
+            glu.glu_fwd_nvfp4(x, act="geglu", layout="paired", sf_layout="128x4", out=of)
+        torch.cuda.synchronize()
+        if args.copy_calibration:
+            calibrate()
+        print("[bench] nvfp4 contract-shape launches done", file=sys.stderr, flush=True)
         return
     if args.bf16_only:
         R, W = 8192, 14336
