@@ -238,9 +238,11 @@ def validate_nv_bwd(torch, glu, act, g, u, d, out, sf_layout, what):
     _equal(torch, out[1], ref[1], what + " scales")
 
 
-def validate_gemm(torch, glu, ops, act, fmt, out, what, **operand_kw):
+def validate_gemm(torch, glu, ops, act, out_fmt, out, what, operand_kw):
+    """The fused quantized output equals the standalone quantizer of glu_gemm's h (operand_kw:
+    the operand format and W layout)."""
     h = glu.glu_gemm(*ops, act=act, **operand_kw)
-    if fmt == "mxfp8":
+    if out_fmt == "mxfp8":
         q, s = glu.glu_quant_mxfp8_f32(h.float(), rowwise=True)[0::2]
     else:
         q, s = glu.glu_quant_nvfp4_f32(h.float(), sf_layout="128x4")
@@ -442,7 +444,7 @@ def sweep(torch, glu, si, iters, validate):
                 f"{act}_gemm_{opfmt}_paired_{fmt}_{M}x{N}x{K}"
             if validate:
                 fns[0]()
-                validate_gemm(torch, glu, src[0], act, fmt, out if fmt == "mxfp8" else nv_out, name, **kw)
+                validate_gemm(torch, glu, src[0], act, fmt, out if fmt == "mxfp8" else nv_out, name, kw)
             t = time_launches(torch, fns, iters)
             tf = 2.0 * M * K * 2 * N / t["median_us"] / 1e6
             peak = PEAK_FP4_TFLOPS if opfmt == "mxfp4" else PEAK_FP8_TFLOPS
