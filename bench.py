@@ -112,7 +112,9 @@ def _events(torch, n):
 
 def time_launches(torch, fns, iters):
     """Median / min / p90 of per-launch durations (us), cycling through fns (one per input
-    set, so repeated launches do not re-read cached inputs)."""
+    set, so repeated launches do not re-read cached inputs: cold), and the median of the same
+    number of launches on the first set alone (warm: inputs left in the caches by the previous
+    launch, where they fit)."""
     for f in fns[: min(3, len(fns))]:
         f()
     torch.cuda.synchronize()
@@ -123,7 +125,14 @@ def time_launches(torch, fns, iters):
         ev[2 * i + 1].record()
     torch.cuda.synchronize()
     us = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(iters))
-    return dict(median_us=statistics.median(us), min_us=us[0], p90_us=us[int(0.9 * (len(us) - 1))])
+    for i in range(iters):
+        ev[2 * i].record()
+        fns[0]()
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    warm = statistics.median(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(iters))
+    return dict(median_us=statistics.median(us), min_us=us[0], p90_us=us[int(0.9 * (len(us) - 1))],
+                warm_median_us=warm)
 
 
 def n_sets(bytes_per_set):
@@ -288,7 +297,8 @@ def sweep(torch, glu, si, iters, validate):
     def rec(name, b, t, mix=None):
         gbps = b / t["median_us"] / 1e3
         r = dict(bytes=b, us=round(t["median_us"], 2), min_us=round(t["min_us"], 2), p90_us=round(t["p90_us"], 2),
-                 gbps=round(gbps, 1), frac=round(gbps / PEAK_GBPS, 4), validated=validate)
+                 gbps=round(gbps, 1), frac=round(gbps / PEAK_GBPS, 4), warm_us=round(t["warm_median_us"], 2),
+                 validated=validate)
         if mix is not None:
             c = ceiling(*mix)
             r["ceiling_gbps"] = c["gbps"]
@@ -450,8 +460,8 @@ def sweep(torch, glu, si, iters, validate):
             peak = PEAK_FP4_TFLOPS if opfmt == "mxfp4" else PEAK_FP8_TFLOPS
             print(f"[bench] {name}: {t['median_us']:.2f} us", file=sys.stderr, flush=True)
             res[name] = dict(flops=2 * M * K * 2 * N, us=round(t["median_us"], 2), min_us=round(t["min_us"], 2),
-                             p90_us=round(t["p90_us"], 2), tflops=round(tf, 1), frac=round(tf / peak, 4),
-                             peak_tflops=peak, validated=validate)
+                             p90_us=round(t["p90_us"], 2), warm_us=round(t["warm_median_us"], 2), tflops=round(tf, 1),
+                             frac=round(tf / peak, 4), peak_tflops=peak, validated=validate)
         # context, not part of the path: the platform library's GEMM alone (torch._scaled_mm,
         # BF16 output, no activation, no quantizer) on the same codes, with the same E8M0 block
         # scales and with one tensor-wide scale
