@@ -2,7 +2,7 @@
 
 erfc(z) = t * exp(-z^2 + Q(t)) with t = 1 / (1 + z/2) (the change of variable of the
 classic Chebyshev-fitted erfc of Press et al., Numerical Recipes, 6.2), here with Q a
-degree-9 polynomial fitted by least squares on Chebyshev nodes to ln(erfc(z)/t) + z^2 over
+degree-7 polynomial fitted by least squares on Chebyshev nodes to ln(erfc(z)/t) + z^2 over
 the range the kernels use, z in [0, 12.75/sqrt 2] (|x| <= 12.75 in x = -z sqrt 2).
 Q(0) tends to ln(1/(2 sqrt pi)) as z -> inf.  Run: python gen_erfc_poly.py
 """
@@ -12,7 +12,7 @@ import numpy as np
 mp.mp.dps = 40
 ZMAX = 12.75 / np.sqrt(2.0)
 TMIN = 1.0 / (1.0 + 0.5 * ZMAX)
-DEG = 9
+DEG = 7
 
 
 def q_exact(t):

@@ -123,17 +123,16 @@ __device__ __forceinline__ double exp2_tail(float zl) {
 //
 // FP32 fast path (x >= -12.5; below that the FP64 tail): with z = |x| / sqrt 2,
 //   erfc(z) = t e^(-z^2 + Q(t)),  t = 1 / (1 + z/2),
-// Q a degree-9 polynomial fitted to ln(erfc(z)/t) + z^2 for |x| <= 12.75 (max error
-// 4.3e-8; gen_erfc_poly.py prints the coefficients), and Phi = erfc(z)/2 for x < 0,
+// Q a degree-7 polynomial fitted to ln(erfc(z)/t) + z^2 for |x| <= 12.75 (max error
+// 7.0e-7; gen_erfc_poly.py prints the coefficients), and Phi = erfc(z)/2 for x < 0,
 // 1 - erfc(z)/2 otherwise.  x is clamped to +-12.75: beyond it Phi is 1 in FP32 (x > 0) or
 // the tail path applies (x < 0).  z^2 = x^2 / 2 is exact for a BF16 x, and e^(-z^2 + q) is
 // formed as 2^n 2^f with the product z^2 log2(e) carried to about 40 bits (log2 e split so
 // that its 8-bit head times the 16-bit z^2 is exact), so the large exponent costs no
 // accuracy.
-constexpr float ERFC_Q[10] = {
-    -1.265415668e+00f, 9.979900122e-01f, 3.920583725e-01f, 9.132201783e-03f,
-    7.507857680e-02f,  -2.174440175e-01f, -5.322819948e-01f, 1.034772754e+00f,
-    -6.294651031e-01f, 1.355749071e-01f};
+constexpr float ERFC_Q[8] = {-1.265515924e+00f, 9.991499186e-01f,  3.906860054e-01f,
+                             -2.971511893e-02f, 3.325169683e-01f,  -9.836239219e-01f,
+                             7.421878576e-01f,  -1.856864840e-01f};
 constexpr float ERF_X_CLAMP = 12.75f;
 constexpr float LOG2E_HI = 1.4453125f;  // log2(e) to 8 significant bits (0x3FB90000)
 constexpr float LOG2E_LO = (float)(1.44269504088896340736 - 1.4453125);
@@ -154,9 +153,9 @@ __device__ __forceinline__ ErfParts erf_parts(float x) {
   p.xc = __builtin_amdgcn_fmed3f(x, -ERF_X_CLAMP, ERF_X_CLAMP);
   p.w = (0.5f * p.xc) * p.xc;
   p.t = __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_fabsf(p.xc), (float)(0.5 * SQRT1_2), 1.0f));
-  float q = ERFC_Q[9];
+  float q = ERFC_Q[7];
 #pragma unroll
-  for (int i = 8; i >= 0; i--) q = __builtin_fmaf(q, p.t, ERFC_Q[i]);
+  for (int i = 6; i >= 0; i--) q = __builtin_fmaf(q, p.t, ERFC_Q[i]);
   p.q = q;
   return p;
 }
