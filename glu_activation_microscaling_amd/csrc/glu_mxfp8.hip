@@ -303,28 +303,53 @@ __device__ __forceinline__ void compute(TileVals<MODE>& r, const TileOps<LAYOUT,
       for (int k = 0; k < 4; k++) r.h[0][i][k] = pack_bf16(h[2 * k], h[2 * k + 1]);
     }
   } else {
+    // Each row is packed to BF16 right after its fast path, and the rare tail elements then
+    // overwrite their halves of the packed words (recomputed from the raw operand words), so
+    // no FP32 result outlives its row.  The empty asm keeps the compiler from sinking the
+    // packs of db past da's staging (it would hold 32 FP32 values instead of 16 words), and
+    // the scheduling barriers keep the halves and rows in order.  SwiGLU at [16384, 7168]:
+    // 102 -> 83 VGPRs and 228 -> 226 us (both), 100 -> 80 VGPRs and 174 -> 167 us (colwise
+    // only); without the barriers the same VGPRs and 232 and 170 us.
     bool tail = false;
     if constexpr (tail_from_gate_bits<ACT>()) tail = tail_possible<ACT>(gate_max16<SPLIT>(o.in));
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       float gg[8], u[8], d[8], da[8], db[8];
       unpack_gu<SPLIT>(o.in[i], gg, u);
+      bool rt = tail;
 #pragma unroll
-      for (int c = 0; c < 8; c++) {
-        d[c] = (c & 1) ? bf_hi(o.d[i][c >> 1]) : bf_lo(o.d[i][c >> 1]);
-        glu_bwd_fast<ACT>(gg[c], u[c], d[c], da[c], db[c]);
-        if constexpr (!tail_from_gate_bits<ACT>()) tail |= bwd_tail_needed<ACT>(gg[c], u[c], d[c]);
-      }
-      if (tail) {  // rare: some element may need the FP64 tail path
+      for (int half = 0; half < 2; half++) {  // 4 elements, then their 2 packed words
 #pragma unroll
-        for (int c = 0; c < 8; c++)
-          if (bwd_tail_needed<ACT>(gg[c], u[c], d[c])) glu_bwd_tail<ACT>(gg[c], u[c], d[c], da[c], db[c]);
-      }
+        for (int c = 4 * half; c < 4 * half + 4; c++) {
+          d[c] = (c & 1) ? bf_hi(o.d[i][c >> 1]) : bf_lo(o.d[i][c >> 1]);
+          glu_bwd_fast<ACT>(gg[c], u[c], d[c], da[c], db[c]);
+          if constexpr (!tail_from_gate_bits<ACT>()) rt |= bwd_tail_needed<ACT>(gg[c], u[c], d[c]);
+        }
 #pragma unroll
-      for (int k = 0; k < 4; k++) {
-        r.h[0][i][k] = pack_bf16(da[2 * k], da[2 * k + 1]);
-        r.h[1][i][k] = pack_bf16(db[2 * k], db[2 * k + 1]);
+        for (int k = 2 * half; k < 2 * half + 2; k++) {
+          r.h[0][i][k] = pack_bf16(da[2 * k], da[2 * k + 1]);
+          r.h[1][i][k] = pack_bf16(db[2 * k], db[2 * k + 1]);
+          asm volatile("" : "+v"(r.h[0][i][k]), "+v"(r.h[1][i][k]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      if (rt) {  // rare: some element may need the FP64 tail path
+#pragma unroll
+        for (int c = 0; c < 8; c++) {
+          const int k = c >> 1;
+          const float g1 = (c & 1) ? bf_hi(o.in[i].a[k]) : bf_lo(o.in[i].a[k]);
+          const float u1 = (c & 1) ? bf_hi(o.in[i].b[k]) : bf_lo(o.in[i].b[k]);
+          const float d1 = (c & 1) ? bf_hi(o.d[i][k]) : bf_lo(o.d[i][k]);
+          if (bwd_tail_needed<ACT>(g1, u1, d1)) {
+            float ta, tb;
+            glu_bwd_tail<ACT>(g1, u1, d1, ta, tb);
+            const uint32_t keep = (c & 1) ? 0x0000ffffu : 0xffff0000u;  // the other element's half
+            r.h[0][i][k] = (r.h[0][i][k] & keep) | (pack_bf16(ta, ta) & ~keep);
+            r.h[1][i][k] = (r.h[1][i][k] & keep) | (pack_bf16(tb, tb) & ~keep);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -734,7 +759,7 @@ __global__ __launch_bounds__((TileOf<FLAGS, MODE>::NTHREADS)) void k_mxfp8(
   using St = Stage<T, FLAGS>;
   constexpr int TM = T::TM, TN = T::TN;
   constexpr int PARTS = MODE == MODE_BWD ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[PARTS * St::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[St::BYTES];
   uint32_t t = blockIdx.x;
   if (pol.xcd_runs != 0u) {
     const uint32_t xcd = blockIdx.x & 7;
@@ -761,16 +786,17 @@ __global__ __launch_bounds__((TileOf<FLAGS, MODE>::NTHREADS)) void k_mxfp8(
   load_ops<LAYOUT, MODE>(o, a, wave_geom(a, r0, c0, wm, wn, lc), lr, lc);
   TileVals<MODE> R;
   compute<ACT, LAYOUT, MODE>(R, o);
-  const St A(lds), B(lds + St::BYTES);
+  const St A(lds);
   if constexpr (MODE == MODE_BWD) {
-    // da is staged and written out while db is staged (227 vs 234 us at [16384, 7168] against
-    // staging both first; splitting the rowwise and colwise pieces too gained nothing)
+    // da and db pass through one stage in turn: backward both [16384, 7168] 227 vs 229 us
+    // against a second stage that takes db while da is written out, at half the LDS
     stage_bf16<T, FLAGS>(R.h[0], A, row0, col, lr, lc);
     __syncthreads();
     write_part(A, 0);
-    stage_bf16<T, FLAGS>(R.h[1], B, row0, col, lr, lc);
     __syncthreads();
-    write_part(B, a.N);
+    stage_bf16<T, FLAGS>(R.h[1], A, row0, col, lr, lc);
+    __syncthreads();
+    write_part(A, a.N);
   } else {
     if constexpr (MODE == MODE_F32) stage_f32<T, FLAGS>(R.v, A, row0, col, lr, lc);
     else stage_bf16<T, FLAGS>(R.h[0], A, row0, col, lr, lc);
