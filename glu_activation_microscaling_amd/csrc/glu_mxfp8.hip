@@ -4,8 +4,9 @@
 //
 // Work decomposition (wave64):
 //   A workgroup owns a TM x TN tile of the quantized matrix (of each of da and db in the
-//   backward): 128 x 128 with 4 x 2 waves, or 64 x 128 with 2 x 2 waves when only rowwise
-//   codes are written.  A wave covers 32 rows x 64 columns: one 32-row colwise block row and
+//   backward): 128 x 128 with 4 x 2 waves, or, when only rowwise codes are written, a band
+//   of 32 rows 512 (forward) or 256 (backward) columns wide with 1 x 8 or 1 x 4 waves.  A
+//   wave covers 32 rows x 64 columns: one 32-row colwise block row and
 //   two 32-column rowwise blocks per row.  Lane = lr + 8*lc owns rows 4lr..4lr+3 and columns
 //   8lc..8lc+7 of the wave's piece: 16-byte loads per row and per operand, 32 elements per
 //   lane, kept after the activation as 16 packed BF16 pairs.
@@ -15,7 +16,8 @@
 //   xor 2, then row_half_mirror.  Maxima are taken on packed 16-bit magnitudes (two
 //   columns, or two rows, per instruction).
 //   Codes and scales are staged in LDS and leave, after one workgroup barrier, as 16-byte
-//   stores that fill whole 128-byte lines: a tile row of rowwise codes and a tile column of
+//   stores that fill whole 128-byte lines (the backward stages da, writes it out, then
+//   stages db in the same LDS): a tile row of rowwise codes and a tile column of
 //   colwise codes are 128 bytes each (colwise output always uses 128-row tiles), and the
 //   scales of a tile row (column) are one 4-byte word.  Straight from the registers the same
 //   data would leave as 32-byte (colwise) and 64-byte (rowwise) pieces and single scale
