@@ -22,6 +22,13 @@ Workloads (shapes and value distributions of the pages' benchmarks):
                     eight E2M1 magnitudes with the frequencies a block of N(0, 1) data
                     scaled to a block maximum of 6 puts on them, a uniform sign, and E8M0
                     block scales drawn uniformly from 2^-5 .. 2^-1.
+  * tail_operands : gate, up, dh BF16 [M, N] that send most elements down the kernels'
+                    FP64 tail path: gates uniform over a range that straddles the switch
+                    (SwiGLU -104 .. -78, tanh-GeGLU -11 .. -9, erf-GeGLU -40 .. -11) with
+                    N(0, 1) * 2^k ups (k uniform in -10 .. 59) and N(0, 1) * 1000 dh; for
+                    ReLU^2, gates of magnitude 2^e (e uniform in -75 .. 75, 10% negative)
+                    with ups near 2^-2e and dh near 2^-e, so g^2 or dh g leaves the FP32
+                    normal range while the results stay in it.
 Draw order within one call: gate, up, dh (then the outlier masks, in the same order).
 """
 import numpy as np
@@ -53,6 +60,32 @@ def glu_operands(M, N, seed=0, outliers=False, with_dh=False):
     """gate, up (and dh) BF16 [M, N] as torch CPU tensors."""
     n = 3 if with_dh else 2
     return normal_bf16([(M, N)] * n, seed=seed, outliers=outliers)
+
+
+# gate ranges of tail_operands that straddle the switch to the FP64 tail path
+TAIL_GATE_RANGE = {"swiglu": (-104.0, -78.0), "geglu": (-11.0, -9.0), "geglu_erf": (-40.0, -11.0)}
+
+
+def tail_operands(act, M, N, seed=0):
+    """gate, up, dh BF16 [M, N] CPU tensors for the tail path of activation `act`
+    ("swiglu", "geglu", "geglu_erf" or "relu2"); see the module docstring."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    shape = (M, N)
+    if act == "relu2":
+        def pow2(e):
+            return torch.exp2(e.clamp(-125, 125).double())
+        eg = torch.randint(-75, 76, shape, generator=g)
+        gate = (torch.rand(shape, generator=g, dtype=torch.float64) + 0.5) * pow2(eg)
+        gate = torch.where(torch.rand(shape, generator=g) < 0.1, -gate, gate)
+        up = torch.randn(shape, generator=g, dtype=torch.float64) * pow2(-2 * eg + torch.randint(-4, 5, shape, generator=g))
+        dh = torch.randn(shape, generator=g, dtype=torch.float64) * pow2(-eg + torch.randint(-4, 5, shape, generator=g))
+    else:
+        lo, hi = TAIL_GATE_RANGE[act]
+        gate = torch.rand(shape, generator=g, dtype=torch.float64) * (hi - lo) + lo
+        up = torch.randn(shape, generator=g, dtype=torch.float64) * torch.exp2(
+            torch.randint(-10, 60, shape, generator=g).double())
+        dh = torch.randn(shape, generator=g, dtype=torch.float64) * 1000
+    return [t.to(torch.bfloat16) for t in (gate, up, dh)]
 
 
 def paired_operand(M, H, seed=0):

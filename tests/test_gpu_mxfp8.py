@@ -4,7 +4,8 @@ Rule 1 (bit-exact when the quantizer sees identical FP32 values):
   * glu_quant_mxfp8_f32 on random, outlier, subnormal, tie-dense, all-BF16 and non-finite
     inputs equals oracle.quant_mxfp8 byte for byte, rowwise, colwise and both;
   * the fused kernels equal the oracle quantizer applied to the GPU's own BF16 glu_fwd /
-    glu_bwd output (the quantizer isolated end to end).
+    glu_bwd output (the quantizer isolated end to end), also with most elements on the
+    FP64 tail path (synthetic_inputs.tail_operands).
 Rule 3 (fused GPU vs oracle end to end) on the five workload shapes, full or sampled.
 """
 import numpy as np
@@ -128,6 +129,29 @@ def test_fused_bwd_equals_quantized_glu_bwd(gpu, name, kind, M, N):
             assert np.array_equal(u8(qr), o[0]) and np.array_equal(u8(sr), o[1])
         if col:
             assert np.array_equal(u8(qc), o[2]) and np.array_equal(u8(sc), o[3])
+
+
+@pytest.mark.parametrize("name,kind", ACTS)
+def test_fused_tail_paths_equal_quantized_glu(gpu, name, kind):
+    """The fused kernels patch the FP64 tail results into their packed BF16 words; with most
+    elements on the tail path, both directions and every scaling must still equal the oracle
+    quantizer applied to the GPU's own glu_fwd / glu_bwd output (whose tails the BF16 tests
+    hold to rule 2 against the oracle)."""
+    M, N = 128, 256
+    g, u, d = si.tail_operands(name, M, N, seed=11 + kind)
+    gd, ud, dd = g.cuda(), u.cuda(), d.cuda()
+    h = bits(gpu.glu_fwd(gd, ud, act=name))
+    da, db = gpu.glu_bwd(gd, ud, dd, act=name)
+    X = np.concatenate([bits(da), bits(db)], axis=1)
+    for row, col in FLAGS:
+        for what, got, ref in (("fwd", gpu.glu_fwd_mxfp8(gd, ud, act=name, rowwise=row, colwise=col), h),
+                               ("bwd", gpu.glu_bwd_mxfp8(gd, ud, dd, act=name, rowwise=row, colwise=col), X)):
+            qr, qc, sr, sc = got
+            o = _q(ref, _flags(row, col))
+            if row:
+                assert np.array_equal(u8(qr), o[0]) and np.array_equal(u8(sr), o[1]), f"{what} rowwise"
+            if col:
+                assert np.array_equal(u8(qc), o[2]) and np.array_equal(u8(sc), o[3]), f"{what} colwise"
 
 
 @pytest.mark.parametrize("layout", ["split", "paired"])

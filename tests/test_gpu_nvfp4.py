@@ -137,6 +137,29 @@ def test_fused_bwd_equals_quantized_glu_bwd(gpu, act, kind, M, N):
 
 
 @pytest.mark.parametrize("act,kind", ACTS)
+def test_fused_tail_paths_equal_quantized_glu(gpu, act, kind):
+    """Most elements on the FP64 tail path (si.tail_operands): the fused forward (paired and
+    split operands) and backward equal the oracle quantizer applied to the GPU's own
+    glu_fwd / glu_bwd output, in both scale layouts."""
+    M, N = 130, 1024
+    g, u, d = si.tail_operands(act, M, N, seed=21 + kind)
+    gd, ud, dd = g.cuda(), u.cuda(), d.cuda()
+    pair = torch.stack([gd, ud], 2).reshape(M, 2 * N).contiguous()
+    hf = si.from_bits(bits(gpu.glu_fwd(gd, ud, act=act))).float().numpy()
+    da, db = gpu.glu_bwd(gd, ud, dd, act=act)
+    X = si.from_bits(np.concatenate([bits(da), bits(db)], axis=1)).float().numpy()
+    for name, code in SFL:
+        oq, osf = oracle.quant_nvfp4(hf, code)
+        for args, layout in (((pair, None), "paired"), ((gd, ud), "split")):
+            q, sf = gpu.glu_fwd_nvfp4(*args, act=act, layout=layout, sf_layout=name)
+            assert np.array_equal(u8(q), oq) and np.array_equal(u8(sf).ravel(), osf.ravel()), f"fwd {layout} ({name})"
+        q, sf = gpu.glu_bwd_nvfp4(gd, ud, dd, act=act, sf_layout=name)
+        oq, osf = oracle.quant_nvfp4(X, code)
+        assert np.array_equal(u8(sf).ravel(), osf.ravel()), f"bwd scales ({name})"
+        assert np.array_equal(u8(q), oq), f"bwd codes ({name})"
+
+
+@pytest.mark.parametrize("act,kind", ACTS)
 def test_bwd_rule3_against_oracle(gpu, act, kind):
     M, N = 512, 4096
     gate, up, dh = si.glu_operands(M, N, seed=40 + kind, outliers=True, with_dh=True)
