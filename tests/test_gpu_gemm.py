@@ -115,6 +115,59 @@ def test_glu_epilogue_and_quantizer(gpu, act, kind):
     assert np.array_equal(u8(sc), o[1]) and np.array_equal(u8(q), o[0])
 
 
+def _tail_operands(act, M, N, K, seed):
+    """Operands whose exact Y puts the gate half across the activation's switch to the FP64
+    tail path.  X is all E4M3 1.0 (code 0x38, scale 2^0), so Y[i, j] = K * v_j * 2^e_j for a
+    gate row j holding one code v_j with scale byte 127 + e_j:
+      * SwiGLU: v in -[0.5, 1) (codes 0xB0..0xB7), e = 0 at K = 128: Y in -[64, 120];
+      * GeGLU (tanh, erf): the same codes with e = -3: Y in -[8, 15];
+      * ReLU^2: v in [0.5, 1) with e = 60 (Y^2 above the FP32 range) or e = -70 (Y^2 below
+        it), every fourth row negated, and up rows scaled by 2^-20 or 2^60 so that h stays in
+        range.
+    Up rows: random E4M3 codes N(0, 1) * 64 with scale bytes 118..122."""
+    g = torch.Generator().manual_seed(seed)
+    xq = torch.full((M, K), 0x38, dtype=torch.uint8)
+    xs = torch.full((M, K // 32), 127, dtype=torch.uint8)
+    wq, ws = si.mx_operand(2 * N, K, seed=seed + 1)
+    code = torch.randint(0, 8, (N,), generator=g, dtype=torch.uint8)
+    if act == "relu2":
+        big = torch.arange(N) % 2 == 0
+        gate_code = 0x30 + code
+        gate_code = torch.where(torch.arange(N) % 4 == 3, gate_code | 0x80, gate_code)
+        gate_scale = torch.where(big, torch.tensor(127 + 60), torch.tensor(127 - 70)).to(torch.uint8)
+        up_scale = torch.where(big, torch.tensor(127 - 20), torch.tensor(127 + 60)).to(torch.uint8)
+        ws[N:] = up_scale[:, None]
+    else:
+        gate_code = 0xB0 + code
+        gate_scale = torch.full((N,), 127 if act == "swiglu" else 124, dtype=torch.uint8)
+    wq[:N] = gate_code[:, None]
+    ws[:N] = gate_scale[:, None]
+    return xq, xs, wq, ws
+
+
+@pytest.mark.parametrize("act,kind", ACTS)
+def test_epilogue_tail_paths(gpu, act, kind):
+    """The epilogue's FP64 tail path: h within 1 BF16 ulp of the oracle's GLU of the device's
+    own Y (rule 2), and the MXFP8 and NVFP4 codes equal to the oracle quantizers of the device's
+    own h (rule 1)."""
+    M, N, K = 64, 128, 128
+    ops = [t.cuda() for t in _tail_operands(act, M, N, K, seed=300 + kind)]
+    y = gpu.mx_gemm_f32(*ops).cpu().numpy().astype(np.float64)
+    gate = y[:, :N]
+    if act == "swiglu":
+        assert (gate < -86.7).any() and (gate > -86.5).any(), "the gates straddle the switch"
+    h = gpu.glu_gemm(*ops, act=act)
+    want = oracle.bf16_from_f64(oracle.act(kind, gate) * y[:, N:])
+    check_rule2(bits(h), want, f"{act} tail epilogue")
+    hf = si.from_bits(bits(h)).float().numpy()
+    q, sc = gpu.glu_gemm_mxfp8(*ops, act=act)
+    o = oracle.quant_mxfp8(hf, oracle.ROWWISE)
+    assert np.array_equal(u8(sc), o[1]) and np.array_equal(u8(q), o[0])
+    q, sf = gpu.glu_gemm_nvfp4(*ops, act=act, sf_layout="128x4")
+    o = oracle.quant_nvfp4(hf, oracle.SF_128x4)
+    assert np.array_equal(u8(q), o[0]) and np.array_equal(u8(sf).ravel(), np.asarray(o[1]).ravel())
+
+
 @pytest.mark.parametrize("act,kind", ACTS)
 @pytest.mark.parametrize("M", [160, 300])
 @pytest.mark.parametrize("sf_layout", ["rowmajor", "128x4"])
