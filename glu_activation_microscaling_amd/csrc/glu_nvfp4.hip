@@ -333,12 +333,14 @@ __global__ __launch_bounds__(NV_THREADS) void k_nvfp4(NvArgs a, int64_t tiles_pe
         }
         quant_store_f32<SFL>(v, qr, sr, j, in_row, live, lane, nb, cp);
       } else if constexpr (MODE == NV_FWD_GS) {
-        uint32_t p[4], q[4];
-        glu_values<ACT, LAYOUT, NV_FWD>(raw[gi], p, q);
+        uint32_t p[4] = {0u, 0u, 0u, 0u}, q[4];
+        if (row_ok) glu_values<ACT, LAYOUT, NV_FWD>(raw[gi], p, q);
         quant_store_bf16<SFL, WORD_SCALES, true>(p, qr, sr, j, in_row, live, lane, nb, cp, gs);
       } else {
-        uint32_t p[4], q[4];
-        glu_values<ACT, LAYOUT, MODE>(raw[gi], p, q);
+        // rows past M (the 128x4 layout's padding rows) only store zero scales: the
+        // activation is skipped there (row_ok is uniform in the workgroup)
+        uint32_t p[4] = {0u, 0u, 0u, 0u}, q[4] = {0u, 0u, 0u, 0u};
+        if (row_ok) glu_values<ACT, LAYOUT, MODE>(raw[gi], p, q);
         // backward: with H % 64 != 0 the last da octet would reach into db's blocks
         quant_store_bf16<SFL, WORD_SCALES>(p, qr, sr, j, in_row, live, lane, nb, cp);
         if constexpr (MODE == NV_BWD)
