@@ -32,8 +32,10 @@ constexpr int64_t NV_TILE = 2048;  // operand columns per workgroup and group
 constexpr int NV_FWD_GROUPS = 2;   // column groups per lane in the forward (one was slower)
 // Workgroups of the amax pass (each folds its maximum in with one atomic): a capped grid took
 // the pass from 97 to 88 us at [16384, 7168] and from 38 to 23 us at [968, 16384] against one
-// workgroup per tile, where fewer same-address atomics matter more than parallelism.
-constexpr int64_t kAmaxWorkgroups = 1024;
+// workgroup per tile, where fewer same-address atomics matter more than parallelism.  With
+// the next row prefetched, 512 beat 1024 (968 rows 24.7 -> 20.9 us, 784 rows 24.7 -> 18.6,
+// [16384, 7168] 88.4 -> 85.5); 2048 took 40 us at 968 rows, 256 and 384 were slower than 512.
+constexpr int64_t kAmaxWorkgroups = 512;
 
 enum { NV_FWD = 0, NV_BWD = 1, NV_F32 = 2, NV_FWD_GS = 3 };
 
@@ -380,9 +382,11 @@ hipError_t launch(const NvArgs& a, hipStream_t s) {
 }
 
 // Amax pass of two-level NVFP4: the largest |h| over the matrix, h = bf16(act(gate) * up)
-// (NaN if some h is NaN), as FP32 bits in *a.amax_out.  Workgroups stride over the same
-// tiles as k_nvfp4 (2 groups per lane) keeping a running maximum of BF16 magnitude bits
-// (NaN patterns order above Inf), reduce it over the workgroup, and fold it into the output
+// (NaN if some h is NaN), as FP32 bits in *a.amax_out.  A capped grid of workgroups covers
+// the tiles of k_nvfp4 (2 groups per lane): each takes a column tile and walks its rows in a
+// grid stride with the next row's loads in flight, keeping a running maximum of BF16
+// magnitude bits (NaN patterns order above Inf), reduces it over the workgroup, and folds it
+// into the output
 // with at most one unsigned atomic max per workgroup; k_zero_u32 clears the output first (on
 // the same stream).  Non-negative FP32 values order like their bit patterns.
 __global__ void k_zero_u32(uint32_t* p) {
@@ -394,24 +398,34 @@ __global__ __launch_bounds__(NV_THREADS) void k_glu_amax(NvArgs a, int64_t tiles
   constexpr int G = 2;
   const uint32_t H = (uint32_t)a.H;
   uint32_t m = 0;
-  for (int64_t row = blockIdx.y; row < a.M; row += gridDim.y)
   for (int64_t tc = blockIdx.x; tc < tiles_per_row; tc += gridDim.x) {
     const uint32_t j0 = (uint32_t)tc * (uint32_t)(NV_TILE * G) + threadIdx.x * 8u;
-    const RowIn in = row_in<LAYOUT, NV_FWD>(a, row);
-    Raw8 raw[G];
+    // lanes past the row, and rows past M, read zeros (every activation gives h = 0 for them)
+    auto load_row = [&](int64_t row, Raw8 (&raw)[G]) {
+      const bool ok = row < a.M;
+      const RowIn in = row_in<LAYOUT, NV_FWD>(a, ok ? row : 0);
 #pragma unroll
-    for (int gi = 0; gi < G; gi++) {
-      const uint32_t j = j0 + gi * (uint32_t)NV_TILE;
-      raw[gi] = load_raw<LAYOUT, NV_FWD>(in, j, j < H);
-    }
+      for (int gi = 0; gi < G; gi++) {
+        const uint32_t j = j0 + gi * (uint32_t)NV_TILE;
+        raw[gi] = load_raw<LAYOUT, NV_FWD>(in, j, j < H && ok);
+      }
+    };
+    // the workgroup walks its rows with the next row's operands already in flight
+    Raw8 cur[G];
+    load_row(blockIdx.y, cur);
+    for (int64_t row = blockIdx.y; row < a.M; row += gridDim.y) {
+      Raw8 nxt[G];
+      load_row(row + gridDim.y, nxt);
 #pragma unroll
-    for (int gi = 0; gi < G; gi++) {
-      // lanes past the row read zeros, and every activation gives h = 0 for them
-      uint32_t p[4], q[4];
-      glu_values<ACT, LAYOUT, NV_FWD>(raw[gi], p, q);
-      const uint32_t M = 0x7fff7fffu;
-      const uint32_t m2 = pkmax(pkmax(p[0] & M, p[1] & M), pkmax(p[2] & M, p[3] & M));
-      m = umax(m, umax(lo16(m2), hi16(m2)));
+      for (int gi = 0; gi < G; gi++) {
+        uint32_t p[4], q[4];
+        glu_values<ACT, LAYOUT, NV_FWD>(cur[gi], p, q);
+        const uint32_t M = 0x7fff7fffu;
+        const uint32_t m2 = pkmax(pkmax(p[0] & M, p[1] & M), pkmax(p[2] & M, p[3] & M));
+        m = umax(m, umax(lo16(m2), hi16(m2)));
+      }
+#pragma unroll
+      for (int gi = 0; gi < G; gi++) cur[gi] = nxt[gi];
     }
   }
 #pragma unroll
