@@ -401,10 +401,12 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 // NVFP4: E4M3 scale of amax / 6 and E2M1 codes
 // ---------------------------------------------------------------------------------
 
-// Value of a non-negative finite E4M3 code.
+// Value of a non-negative finite E4M3 code (0 .. 0x7E): 2^(E - 7) (1 + m/8), or m 2^-9 for
+// E = 0.  gfx950's v_cvt_f32_fp8 decodes the OCP E4M3 format exactly (every code 0 .. 0xFF
+// from every byte position matched this definition on the device), in one instruction where
+// the field arithmetic took a branch between the two forms.
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
-  uint32_t E = c >> 3, m = c & 7u;
-  return E ? __uint_as_float(((E + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  return __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
 }
 
 // Nearest E4M3 code to amax / 6 (ties to even, saturating at 448), decided exactly: the
