@@ -19,19 +19,25 @@ template <int VEC>  // 16-byte vectors per operand per thread
 constexpr int64_t bf_chunk() { return (int64_t)BF_THREADS * VEC * 8; }  // elements per tile
 
 // Loads are non-temporal (streaming): [8192, 14336] GeGLU forward 122 vs 130 us, backward 193
-// vs 206 us against ordinary loads (with non-temporal stores).
+// vs 206 us against ordinary loads.
 // Per launch, by the bytes it writes against the 256 MiB last-level cache, and by direction
 // (same-box A/B with cold inputs, GeGLU, us):
-//   stores: non-temporal above 256 MiB, ordinary below (the cache absorbs them);
-//   16-byte vectors per operand per thread: one, except two for a backward above 256 MiB.
+//   stores: non-temporal above 256 MiB, ordinary below (the cache absorbs them).  Above:
+//     forward [8192, 18944] 149.6 vs 156.7 ordinary, [8192, 29568] 228.7 vs 239.3; backward
+//     [8192, 11008] 149.7 vs 157.0, [8192, 29568] 394.1 vs 408.3.  Below, non-temporal stores
+//     cost 5% (forward [8192, 14336] 114.9 vs 109.0).  The choice is a template parameter: a
+//     run-time branch between the two stores of one value to one address is merged into a
+//     single ordinary store, which drops the non-temporal hint.
+//   16-byte vectors per operand per thread: one, except two for a backward above 512 MiB.
 //     up to 256 MiB, one vs two:  [1024, 29568] forward 33.9 vs 38.5, backward 50.4 vs 55.7;
 //                                 [8192, 4096] 36.9 vs 40.1 and 57.1 vs 60.2;
 //                                 [8192, 14336] forward 107.9 vs 118.3;
-//     above, one vs two:          forward [8192, 18944] 154.1 vs 160.3, [16384, 14336] 231.1
-//                                 vs 236.7; backward [8192, 14336] 203.6 vs 198.0, [8192,
-//                                 29568] 411.6 vs 403.5.
-//   With two vectors, ordinary and non-temporal stores measured the same below 256 MiB.
+//     above, one vs two:          forward [8192, 18944] 149.0 vs 152.6, [8192, 29568] 231.6
+//                                 vs 233.2; backward [8192, 11008] (361 MB) 146.9 vs 149.7,
+//                                 [8192, 14336] 194.3 vs 194.8, [8192, 18944] (621 MB) 256.8
+//                                 vs 253.2, [8192, 29568] 400.5 vs 396.1.
 constexpr int64_t kBf16NtStoreBytes = 256ll << 20;
+constexpr int64_t kBf16TwoVecBwdBytes = 512ll << 20;
 
 typedef unsigned int bu32x4 __attribute__((ext_vector_type(4)));
 
@@ -44,10 +50,10 @@ __device__ __forceinline__ Uint4 ld16(const uint16_t* p) {
   v = __builtin_nontemporal_load(reinterpret_cast<const bu32x4*>(p));
   return Uint4{{v.x, v.y, v.z, v.w}};
 }
-__device__ __forceinline__ void st16(uint32_t nt, uint16_t* p, uint32_t a, uint32_t b, uint32_t c,
-                                     uint32_t d) {
+template <bool NT>
+__device__ __forceinline__ void st16(uint16_t* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const bu32x4 v = {a, b, c, d};
-  if (nt != 0u) __builtin_nontemporal_store(v, reinterpret_cast<bu32x4*>(p));
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<bu32x4*>(p));
   else *reinterpret_cast<bu32x4*>(p) = v;
 }
 __device__ __forceinline__ float ld_bf(const uint16_t* p) {
@@ -91,10 +97,9 @@ __device__ __forceinline__ void load1(const uint16_t* gate_row, const uint16_t* 
   }
 }
 
-template <int ACT, int LAYOUT, int BF_VEC>
+template <int ACT, int LAYOUT, int BF_VEC, bool NT>
 __global__ __launch_bounds__(BF_THREADS) void k_glu_fwd_bf16(BF16Args a, int64_t cols,
-                                                             int64_t tiles_per_row, int64_t rows,
-                                                             uint32_t nt) {
+                                                             int64_t tiles_per_row, int64_t rows) {
   for (int64_t row = blockIdx.y; row < rows; row += gridDim.y)
   for (int64_t tc = blockIdx.x; tc < tiles_per_row; tc += gridDim.x) {
     const int64_t j0 = tc * bf_chunk<BF_VEC>();
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(BF_THREADS) void k_glu_fwd_bf16(BF16Args a, int64_t
           for (int k = 0; k < 8; k++)
             if (fwd_tail_needed<ACT>(g[v][k], u[v][k])) h[k] = glu_fwd_tail<ACT>(g[v][k], u[v][k]);
         }
-        st16(nt, hrow + j, pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]),
+        st16<NT>(hrow + j, pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]),
              pack_bf16(h[6], h[7]));
       } else if (j < cols) {
         for (int64_t jj = j; jj < cols; jj++) {
@@ -137,10 +142,9 @@ __global__ __launch_bounds__(BF_THREADS) void k_glu_fwd_bf16(BF16Args a, int64_t
   }
 }
 
-template <int ACT, int LAYOUT, int BF_VEC>
+template <int ACT, int LAYOUT, int BF_VEC, bool NT>
 __global__ __launch_bounds__(BF_THREADS) void k_glu_bwd_bf16(BF16Args a, int64_t cols,
-                                                             int64_t tiles_per_row, int64_t rows,
-                                                             uint32_t nt) {
+                                                             int64_t tiles_per_row, int64_t rows) {
   for (int64_t row = blockIdx.y; row < rows; row += gridDim.y)
   for (int64_t tc = blockIdx.x; tc < tiles_per_row; tc += gridDim.x) {
     const int64_t j0 = tc * bf_chunk<BF_VEC>();
@@ -179,14 +183,14 @@ __global__ __launch_bounds__(BF_THREADS) void k_glu_bwd_bf16(BF16Args a, int64_t
               glu_bwd_tail<ACT>(g[v][k], u[v][k], d[v][k], da[k], db[k]);
         }
         if constexpr (LAYOUT == SPLIT) {
-          st16(nt, arow + j, pack_bf16(da[0], da[1]), pack_bf16(da[2], da[3]), pack_bf16(da[4], da[5]),
+          st16<NT>(arow + j, pack_bf16(da[0], da[1]), pack_bf16(da[2], da[3]), pack_bf16(da[4], da[5]),
                pack_bf16(da[6], da[7]));
-          st16(nt, brow + j, pack_bf16(db[0], db[1]), pack_bf16(db[2], db[3]), pack_bf16(db[4], db[5]),
+          st16<NT>(brow + j, pack_bf16(db[0], db[1]), pack_bf16(db[2], db[3]), pack_bf16(db[4], db[5]),
                pack_bf16(db[6], db[7]));
         } else {
-          st16(nt, arow + 2 * j, pack_bf16(da[0], db[0]), pack_bf16(da[1], db[1]), pack_bf16(da[2], db[2]),
+          st16<NT>(arow + 2 * j, pack_bf16(da[0], db[0]), pack_bf16(da[1], db[1]), pack_bf16(da[2], db[2]),
                pack_bf16(da[3], db[3]));
-          st16(nt, arow + 2 * j + 8, pack_bf16(da[4], db[4]), pack_bf16(da[5], db[5]),
+          st16<NT>(arow + 2 * j + 8, pack_bf16(da[4], db[4]), pack_bf16(da[5], db[5]),
                pack_bf16(da[6], db[6]), pack_bf16(da[7], db[7]));
         }
       } else if (j < cols) {
@@ -214,19 +218,21 @@ template <bool BWD, int ACT, int LAYOUT>
 hipError_t launch(const BF16Args& a, hipStream_t s) {
   const int64_t rows = a.flat ? 1 : a.M;
   const int64_t cols = a.flat ? a.M * a.N : a.N;
-  const bool large = (BWD ? 2 : 1) * 2 * a.M * a.N > kBf16NtStoreBytes;
-  const uint32_t nt = large;
-  auto go = [&](auto V) {
+  const int64_t written = (BWD ? 2 : 1) * 2 * a.M * a.N;
+  auto go = [&](auto V, auto NTC) {
     constexpr int VEC = decltype(V)::value;
+    constexpr bool NT = decltype(NTC)::value;
     const int64_t tpr = (cols + bf_chunk<VEC>() - 1) / bf_chunk<VEC>();
     const dim3 grid = grid_2d(tpr, rows), block(BF_THREADS);
     if constexpr (BWD)
-      return launch_kernel(k_glu_bwd_bf16<ACT, LAYOUT, VEC>, grid, block, s, a, cols, tpr, rows, nt);
+      return launch_kernel(k_glu_bwd_bf16<ACT, LAYOUT, VEC, NT>, grid, block, s, a, cols, tpr, rows);
     else
-      return launch_kernel(k_glu_fwd_bf16<ACT, LAYOUT, VEC>, grid, block, s, a, cols, tpr, rows, nt);
+      return launch_kernel(k_glu_fwd_bf16<ACT, LAYOUT, VEC, NT>, grid, block, s, a, cols, tpr, rows);
   };
-  if (BWD && large) return go(std::integral_constant<int, 2>{});
-  return go(std::integral_constant<int, 1>{});
+  if (written <= kBf16NtStoreBytes) return go(std::integral_constant<int, 1>{}, std::false_type{});
+  if constexpr (BWD)
+    if (written > kBf16TwoVecBwdBytes) return go(std::integral_constant<int, 2>{}, std::true_type{});
+  return go(std::integral_constant<int, 1>{}, std::true_type{});
 }
 
 template <bool BWD>
