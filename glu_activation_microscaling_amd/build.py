@@ -105,6 +105,16 @@ def resource_table():
     return "\n".join(out)
 
 
+def device_asm(src: str) -> str:
+    """gfx950 assembly of one kernel source, compiled with the library's flags (device code
+    only): what the code-generation tests inspect."""
+    cmd = [_hipcc(), *COMMON, "--cuda-device-only", "-S", "-x", "hip", os.path.join(CSRC, src), "-o", "-"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    return r.stdout
+
+
 if __name__ == "__main__":
     if "--resources" in sys.argv:
         print(resource_table())
