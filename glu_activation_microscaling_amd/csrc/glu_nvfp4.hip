@@ -27,9 +27,20 @@
 namespace glu {
 namespace {
 
-constexpr int NV_THREADS = 256;
-constexpr int64_t NV_TILE = 2048;  // operand columns per workgroup and group
-constexpr int NV_FWD_GROUPS = 2;   // column groups per lane in the forward (one was slower)
+// Quantizing kernels: a workgroup is one wave and a lane takes one group of 8 columns, so a
+// workgroup covers 512 operand columns of one row.  That divides every multiple of 512
+// exactly, where 256-thread workgroups with 2 (forward) or 4 (backward) groups per lane left
+// an eighth of the lanes idle at widths of 7168 columns.  Same-box A/B, cold inputs, us:
+//   forward  [16384, 7168] GeGLU 112.9 -> 97.1; [968, 16384] 17.0 -> 16.4; [784, 16384]
+//            14.8 -> 14.2;
+//   backward [16384, 7168] SwiGLU 155.7 -> 139.5, GeGLU 152.8 -> 141.0; [968, 16384] 24.6 ->
+//            23.8 (all bit-identical).  128 threads with one group was within 2% of it, and
+//            better only at [16384, 7168] forward (95.4); two groups per lane were slower.
+constexpr int NV_THREADS = 64;
+constexpr int64_t NV_TILE = 8 * NV_THREADS;  // operand columns per workgroup
+// The amax pass keeps 256-thread workgroups with two groups per lane (its grid is capped).
+constexpr int AMAX_THREADS = 256, AMAX_GROUPS = 2;
+constexpr int64_t AMAX_TILE = 8 * AMAX_THREADS;  // operand columns per workgroup and group
 // Workgroups of the amax pass (each folds its maximum in with one atomic): a capped grid took
 // the pass from 97 to 88 us at [16384, 7168] and from 38 to 23 us at [968, 16384] against one
 // workgroup per tile, where fewer same-address atomics matter more than parallelism.  With
@@ -295,12 +306,11 @@ __device__ __forceinline__ void quant_store_f32(const float v[8], __amdgpu_buffe
   }
 }
 
-// A workgroup covers NV_GROUPS * 2048 consecutive operand columns of one row (a.H wide):
-// lane l takes 8 columns at l * 8 + g * 2048 for each group g, and issues the loads of all
-// its groups first.  Forward: the quantized matrix is h, [M, H].  Backward: it is
+// A workgroup covers NV_TILE consecutive operand columns of one row (a.H wide): lane l takes
+// the 8 columns at l * 8.  Forward: the quantized matrix is h, [M, H].  Backward: it is
 // [da | db], [M, 2H]; the lane's da results go to column j, its db results to column H + j.
 // WORD_SCALES as for quant_store_bf16 (the backward needs H % 64 == 0 for it).
-template <int ACT, int LAYOUT, int SFL, int MODE, bool WORD_SCALES, int NV_GROUPS>
+template <int ACT, int LAYOUT, int SFL, int MODE, bool WORD_SCALES>
 __global__ __launch_bounds__(NV_THREADS) void k_nvfp4(NvArgs a, int64_t tiles_per_row,
                                                       int64_t rows, NvOut o) {
   const int lane = threadIdx.x & 63;
@@ -310,39 +320,32 @@ __global__ __launch_bounds__(NV_THREADS) void k_nvfp4(NvArgs a, int64_t tiles_pe
   if constexpr (MODE == NV_FWD_GS) gs = global_scale(*a.amax);
   for (int64_t row = blockIdx.y; row < rows; row += gridDim.y)
   for (int64_t tc = blockIdx.x; tc < tiles_per_row; tc += gridDim.x) {
-    const uint32_t j0 = (uint32_t)tc * (uint32_t)(NV_TILE * NV_GROUPS) + threadIdx.x * 8u;
+    const uint32_t j = (uint32_t)tc * (uint32_t)NV_TILE + threadIdx.x * 8u;
     const bool row_ok = row < a.M;
     const RowIn in = row_in<LAYOUT, MODE>(a, row_ok ? row : 0);
-    Raw8 raw[NV_GROUPS];
-#pragma unroll
-    for (int gi = 0; gi < NV_GROUPS; gi++) {
-      const uint32_t j = j0 + gi * (uint32_t)NV_TILE;
-      raw[gi] = load_raw<LAYOUT, MODE>(in, j, j < H && row_ok);
-    }
+    const Raw8 raw = load_raw<LAYOUT, MODE>(in, j, j < H && row_ok);
     __amdgpu_buffer_rsrc_t qr, sr;
     row_out<SFL>(a, o, row, qr, sr);
-#pragma unroll
-    for (int gi = 0; gi < NV_GROUPS; gi++) {
-      const uint32_t j = j0 + gi * (uint32_t)NV_TILE;
+    {
       const bool in_row = j < H;  // pairs (octets) of lanes agree: H % 16 == 0
       const bool live = in_row && row_ok;
       if constexpr (MODE == NV_F32) {
         float v[8];
 #pragma unroll
         for (int k = 0; k < 4; k++) {
-          v[k] = __uint_as_float(raw[gi].A.w[k]);
-          v[4 + k] = __uint_as_float(raw[gi].B.w[k]);
+          v[k] = __uint_as_float(raw.A.w[k]);
+          v[4 + k] = __uint_as_float(raw.B.w[k]);
         }
         quant_store_f32<SFL>(v, qr, sr, j, in_row, live, lane, nb, cp);
       } else if constexpr (MODE == NV_FWD_GS) {
         uint32_t p[4] = {0u, 0u, 0u, 0u}, q[4];
-        if (row_ok) glu_values<ACT, LAYOUT, NV_FWD>(raw[gi], p, q);
+        if (row_ok) glu_values<ACT, LAYOUT, NV_FWD>(raw, p, q);
         quant_store_bf16<SFL, WORD_SCALES, true>(p, qr, sr, j, in_row, live, lane, nb, cp, gs);
       } else {
         // rows past M (the 128x4 layout's padding rows) only store zero scales: the
         // activation is skipped there (row_ok is uniform in the workgroup)
         uint32_t p[4] = {0u, 0u, 0u, 0u}, q[4] = {0u, 0u, 0u, 0u};
-        if (row_ok) glu_values<ACT, LAYOUT, MODE>(raw[gi], p, q);
+        if (row_ok) glu_values<ACT, LAYOUT, MODE>(raw, p, q);
         // backward: with H % 64 != 0 the last da octet would reach into db's blocks
         quant_store_bf16<SFL, WORD_SCALES>(p, qr, sr, j, in_row, live, lane, nb, cp);
         if constexpr (MODE == NV_BWD)
@@ -352,61 +355,47 @@ __global__ __launch_bounds__(NV_THREADS) void k_nvfp4(NvArgs a, int64_t tiles_pe
   }
 }
 
-template <int ACT, int LAYOUT, int MODE, int G>
-hipError_t launch_g(const NvArgs& a, hipStream_t s) {
+template <int ACT, int LAYOUT, int MODE>
+hipError_t launch(const NvArgs& a, hipStream_t s) {
   const int64_t width = MODE == NV_BWD ? 2 * a.H : a.H;  // of the quantized matrix
   const int64_t nb = width / 16;
   const NvOut o{width / 2, nb, (nb + 3) / 4 * 4};
   const int64_t rows = a.sf_layout == SF_128x4 ? (a.M + 127) / 128 * 128 : a.M;
-  const int64_t tpr = (a.H + NV_TILE * G - 1) / (NV_TILE * G);
+  const int64_t tpr = (a.H + NV_TILE - 1) / NV_TILE;
   const dim3 grid = grid_2d(tpr, rows), block(NV_THREADS);
   const bool word = MODE != NV_BWD || a.H % 64 == 0;  // db's blocks start on a 4-block boundary
   if (a.sf_layout == SF_128x4) {
-    if (word) return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_128x4, MODE, true, G>, grid, block, s, a, tpr, rows, o);
-    return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_128x4, MODE, false, G>, grid, block, s, a, tpr, rows, o);
+    if (word) return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_128x4, MODE, true>, grid, block, s, a, tpr, rows, o);
+    return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_128x4, MODE, false>, grid, block, s, a, tpr, rows, o);
   }
-  return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_ROWMAJOR, MODE, true, G>, grid, block, s, a, tpr, rows, o);
-}
-
-// Groups per lane.  The backward takes 4 (more loads in flight per wave) when that still
-// leaves at least 16 workgroups per CU, else 2.
-template <int ACT, int LAYOUT, int MODE>
-hipError_t launch(const NvArgs& a, hipStream_t s) {
-  if constexpr (MODE == NV_BWD) {
-    const int64_t tiles4 = a.M * ((a.H + NV_TILE * 4 - 1) / (NV_TILE * 4));
-    if (tiles4 >= 16 * 256) return launch_g<ACT, LAYOUT, MODE, 4>(a, s);
-    return launch_g<ACT, LAYOUT, MODE, 2>(a, s);
-  } else {
-    return launch_g<ACT, LAYOUT, MODE, NV_FWD_GROUPS>(a, s);
-  }
+  return launch_kernel(k_nvfp4<ACT, LAYOUT, SF_ROWMAJOR, MODE, true>, grid, block, s, a, tpr, rows, o);
 }
 
 // Amax pass of two-level NVFP4: the largest |h| over the matrix, h = bf16(act(gate) * up)
-// (NaN if some h is NaN), as FP32 bits in *a.amax_out.  A capped grid of workgroups covers
-// the tiles of k_nvfp4 (2 groups per lane): each takes a column tile and walks its rows in a
-// grid stride with the next row's loads in flight, keeping a running maximum of BF16
-// magnitude bits (NaN patterns order above Inf), reduces it over the workgroup, and folds it
-// into the output
-// with at most one unsigned atomic max per workgroup; k_zero_u32 clears the output first (on
+// (NaN if some h is NaN), as FP32 bits in *a.amax_out.  A capped grid of 256-thread
+// workgroups (2 groups of 8 columns per lane) covers the operand: each takes a column tile
+// and walks its rows in a grid stride with the next row's loads in flight, keeping a running
+// maximum of BF16 magnitude bits (NaN patterns order above Inf), reduces it over the
+// workgroup, and folds it into the output with at most one unsigned atomic max per workgroup; k_zero_u32 clears the output first (on
 // the same stream).  Non-negative FP32 values order like their bit patterns.
 __global__ void k_zero_u32(uint32_t* p) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0u;
 }
 
 template <int ACT, int LAYOUT>
-__global__ __launch_bounds__(NV_THREADS) void k_glu_amax(NvArgs a, int64_t tiles_per_row) {
-  constexpr int G = 2;
+__global__ __launch_bounds__(AMAX_THREADS) void k_glu_amax(NvArgs a, int64_t tiles_per_row) {
+  constexpr int G = AMAX_GROUPS;
   const uint32_t H = (uint32_t)a.H;
   uint32_t m = 0;
   for (int64_t tc = blockIdx.x; tc < tiles_per_row; tc += gridDim.x) {
-    const uint32_t j0 = (uint32_t)tc * (uint32_t)(NV_TILE * G) + threadIdx.x * 8u;
+    const uint32_t j0 = (uint32_t)tc * (uint32_t)(AMAX_TILE * G) + threadIdx.x * 8u;
     // lanes past the row, and rows past M, read zeros (every activation gives h = 0 for them)
     auto load_row = [&](int64_t row, Raw8 (&raw)[G]) {
       const bool ok = row < a.M;
       const RowIn in = row_in<LAYOUT, NV_FWD>(a, ok ? row : 0);
 #pragma unroll
       for (int gi = 0; gi < G; gi++) {
-        const uint32_t j = j0 + gi * (uint32_t)NV_TILE;
+        const uint32_t j = j0 + gi * (uint32_t)AMAX_TILE;
         raw[gi] = load_raw<LAYOUT, NV_FWD>(in, j, j < H && ok);
       }
     };
@@ -430,13 +419,13 @@ __global__ __launch_bounds__(NV_THREADS) void k_glu_amax(NvArgs a, int64_t tiles
   }
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, k));
-  __shared__ uint32_t wave_max[NV_THREADS / 64];
+  __shared__ uint32_t wave_max[AMAX_THREADS / 64];
   if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t w = wave_max[0];
 #pragma unroll
-    for (int i = 1; i < NV_THREADS / 64; i++) w = umax(w, wave_max[i]);
+    for (int i = 1; i < AMAX_THREADS / 64; i++) w = umax(w, wave_max[i]);
     // the running value only grows, so a workgroup whose maximum is not above it skips the
     // atomic (an older, smaller value read here only costs a redundant atomic)
     unsigned int* out = reinterpret_cast<unsigned int*>(a.amax_out);
@@ -450,8 +439,8 @@ __global__ __launch_bounds__(NV_THREADS) void k_glu_amax(NvArgs a, int64_t tiles
 hipError_t launch_glu_amax(const NvArgs& a, hipStream_t s) {
   hipError_t e = launch_kernel(k_zero_u32, dim3(1), dim3(64), s, reinterpret_cast<uint32_t*>(a.amax_out));
   if (e != hipSuccess || a.M == 0 || a.H == 0) return e;
-  const int64_t tpr = (a.H + NV_TILE * 2 - 1) / (NV_TILE * 2);
-  const dim3 grid = grid_2d(tpr, a.M, kAmaxWorkgroups), block(NV_THREADS);
+  const int64_t tpr = (a.H + AMAX_TILE * AMAX_GROUPS - 1) / (AMAX_TILE * AMAX_GROUPS);
+  const dim3 grid = grid_2d(tpr, a.M, kAmaxWorkgroups), block(AMAX_THREADS);
   return with_act(a.act, [&](auto A) {
     constexpr int ACT = decltype(A)::value;
     return a.layout == PAIRED ? launch_kernel(k_glu_amax<ACT, PAIRED>, grid, block, s, a, tpr)
