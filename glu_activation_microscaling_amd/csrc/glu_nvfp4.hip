@@ -7,10 +7,9 @@
 // backward; the placement is that of the MXFP8 backward, "Add swiglu + MXFP8 fused CuTe DSL
 // kernel", API).
 //
-// Work decomposition (wave64): a workgroup of 4 waves covers 2048 consecutive operand
-// columns of one row per group (2 groups per workgroup; the backward 2 or 4); each lane takes 8
-// consecutive columns (one 32-byte load of interleaved gate/up pairs, or 16 bytes each of
-// gate and up, and of dh in the backward).  A 16-element block is a lane pair, so the block
+// Work decomposition (wave64): a workgroup is one wave and covers 512 consecutive operand
+// columns of one row; each lane takes 8 consecutive columns (one 32-byte load of interleaved
+// gate/up pairs, or 16 bytes each of gate and up, and of dh in the backward).  A 16-element block is a lane pair, so the block
 // amax is one DPP quad_perm exchange.  Each lane stores its 8 E2M1 codes as one 4-byte word
 // (a wave writes 256 contiguous bytes).  With the 128x4 layout the four scales of a lane
 // octet (4 consecutive blocks) leave as one 4-byte word; the grid also covers the padding
