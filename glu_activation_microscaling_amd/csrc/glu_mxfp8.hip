@@ -80,17 +80,22 @@ using TileOf = Tile<FLAGS == ROWWISE ? 1 : 4, FLAGS == ROWWISE ? (MODE == MODE_B
 //   launches writing rowwise and colwise scale words together need:
 //     forward colwise only, [16384, 7168]: 105.1 round-robin vs 109.8 per-XCD runs;
 //     forward both: 127.7 per-XCD runs vs 134.0; backward both 229.2 vs 234.6.
+//   With 128x4 scales a rowwise-only tile writes whole scale lines of its own, and
+//   round-robin is faster there: forward 99.0 vs 102.3, backward 150.4 vs 155.6; launches
+//   with both scalings keep per-XCD runs (forward 123.7 vs 128.4 round-robin, backward
+//   223.9 vs 226.0).
 constexpr int64_t kNtStoreBytes = 256ll << 20;
 struct LaunchPolicy {
   uint32_t nt;        // non-temporal code stores
   uint32_t xcd_runs;  // each XCD takes a contiguous run of the tile (unit) order
 };
-// row_kernel: the launch goes to k_mxfp8_row (rowwise only, further below).
-LaunchPolicy launch_policy(int flags, int mode, int64_t code_bytes, bool row_kernel) {
+// row_kernel: the launch goes to k_mxfp8_row (rowwise only, further below); swizzled: the
+// scales are written in the 128x4 layout.
+LaunchPolicy launch_policy(int flags, int mode, int64_t code_bytes, bool row_kernel, bool swizzled) {
   const bool streamed = mode == MODE_FWD && (row_kernel || (flags & (ROWWISE | COLWISE)) == COLWISE);
   LaunchPolicy p;
   p.nt = streamed || code_bytes > kNtStoreBytes;
-  p.xcd_runs = !streamed;
+  p.xcd_runs = !streamed && !(swizzled && (flags & (ROWWISE | COLWISE)) == ROWWISE);
   return p;
 }
 
@@ -953,7 +958,7 @@ bool launch_row(const MxArgs& a, hipStream_t s, hipError_t& err) {
   const int64_t parts = MODE == MODE_BWD ? 2 : 1;
   err = launch_kernel(k_mxfp8_row<ACT, LAYOUT, MODE>, dim3((unsigned)(8 * wg_per_xcd)), dim3(64 * RF_WAVES), s,
                       a, (uint32_t)segs, (uint32_t)units, (uint32_t)wg_per_xcd,
-                      launch_policy(a.flags, MODE, parts * a.M * a.N, true));
+                      launch_policy(a.flags, MODE, parts * a.M * a.N, true, (a.flags & SF_SWIZZLED) != 0));
   return true;
 }
 
@@ -982,7 +987,7 @@ hipError_t launch(const MxArgs& a, hipStream_t s) {
   const int64_t ntiles = tiles_m * tiles_n, per_xcd = (ntiles + 7) / 8;
   const int64_t code_bytes = (((FLAGS & ROWWISE) ? 1 : 0) + ((FLAGS & COLWISE) ? 1 : 0)) *
                              a.M * (MODE == MODE_BWD ? 2 : 1) * a.N;
-  const LaunchPolicy pol = launch_policy(FLAGS, MODE, code_bytes, false);
+  const LaunchPolicy pol = launch_policy(FLAGS, MODE, code_bytes, false, (a.flags & SF_SWIZZLED) != 0);
   // per-XCD runs need 8 * per_xcd workgroups (the last XCD's run may be short); round-robin
   // needs one per tile
   const int64_t grid = pol.xcd_runs != 0u ? 8 * per_xcd : ntiles;
