@@ -315,14 +315,23 @@ __global__ __launch_bounds__(NV_THREADS) void k_nvfp4(NvArgs a, int64_t tiles_pe
   const int lane = threadIdx.x & 63;
   const uint32_t H = (uint32_t)a.H;
   const uint32_t nb = (uint32_t)o.scale_cols, cp = (uint32_t)o.scale_cols_padded;
-  GlobalScale gs;
-  if constexpr (MODE == NV_FWD_GS) gs = global_scale(*a.amax);
   for (int64_t row = blockIdx.y; row < rows; row += gridDim.y)
   for (int64_t tc = blockIdx.x; tc < tiles_per_row; tc += gridDim.x) {
     const uint32_t j = (uint32_t)tc * (uint32_t)NV_TILE + threadIdx.x * 8u;
     const bool row_ok = row < a.M;
     const RowIn in = row_in<LAYOUT, MODE>(a, row_ok ? row : 0);
     const Raw8 raw = load_raw<LAYOUT, MODE>(in, j, j < H && row_ok);
+    // Two-level: the amax is loaded after the operand loads are issued (the scheduling barrier
+    // keeps it and the global scale's divisions below them), so its latency overlaps theirs.
+    // Loaded first, it held the operand loads back by a whole memory latency.  Same-box A/B,
+    // cold inputs, GeGLU, us: [968, 16384] 18.8 -> 17.3, [784, 16384] 16.4 -> 15.2,
+    // [16384, 7168] 101.6 -> 95.6 (bit-identical); a scalar load of the amax, which the
+    // compiler hoists with the divisions above the loop, was slower (19.3, 16.9, 104.7).
+    GlobalScale gs;
+    if constexpr (MODE == NV_FWD_GS) {
+      __builtin_amdgcn_sched_barrier(0);
+      gs = global_scale(*a.amax);
+    }
     __amdgpu_buffer_rsrc_t qr, sr;
     row_out<SFL>(a, o, row, qr, sr);
     {
